@@ -1,0 +1,279 @@
+/*
+ * nf4stream.h -- C ABI of the layer-streamed NF4 + LoRA hot path (MI355X, gfx950).
+ *
+ * Frozen decoder linears are stored as NF4 blockwise 4-bit weights with
+ * double-quantised absmax (block 64, nested block 256, about 0.516 bytes per
+ * parameter), dequantised on the GPU and contracted in bf16 with fp32
+ * accumulation, forward y = x.W'^T + s.(x.A^T).B^T and backward
+ * dx = dy.W' + du.A, with the rank-r LoRA gradients. Layer shards stream from
+ * pinned host memory into a pool of 2..8 device slots on a side stream.
+ *
+ * Sources (web pages on the Soup tool's stream_layers feature), cited by page
+ * title and section:
+ *   [G]  "Soup layer-streamed NF4 training measured" (gate walkthrough):
+ *        s1.3 resident-NF4 reference and the double-quant flag; s2.1 offline
+ *        per-tensor quantisation, per-call weight reconstruction from slot
+ *        bytes plus two shared tables, checkpointed layer body; s2.3
+ *        deterministic quantiser; s2.4 bytes per weight and the two constant
+ *        tables (asserted, never assumed); s2.5 zero-B adapter pitfall; s4.4
+ *        no weight gradient for the frozen base.
+ *   [E]  "Fine-Tune 8B Models on 4GB VRAM: Soup's Layer Streaming", section
+ *        "The Principle of Layer Streaming": 2-8 VRAM buffers, prefetch of
+ *        layer i+1 (forward) / i-1 (backward) on a dedicated stream, each
+ *        layer read twice per step; the slot-aliasing gradient bug of NF4
+ *        layers above ~165 MiB.
+ *
+ * Conventions for every function:
+ *   - Return 0 (NF4S_OK) or a negative NF4S_E* code; nf4s_last_error() gives a
+ *     thread-local message for the last failure. No exception crosses the ABI.
+ *   - All arguments are validated on the host before anything is enqueued; on
+ *     error nothing is launched and outputs are untouched. There is no
+ *     fallback path: an unsupported case is an error, never a slower variant.
+ *   - The caller owns every buffer, stream and event it passes. Device
+ *     pointers are device (HBM) addresses; "host_pinned" pointers must come
+ *     from hipHostMalloc (torch pin_memory). The library allocates no device
+ *     memory; scratch comes in through (ws, ws_bytes), sized by
+ *     nf4s_workspace_bytes(). Streams are hipStream_t passed as void*; 0 is the
+ *     null stream. Calls are asynchronous on the given stream and never
+ *     synchronise the device.
+ *   - bf16 tensors are uint16_t bit patterns, row-major, contiguous.
+ *   - Results do not depend on pointer values, on slot indices or on the
+ *     pool size: the launch configuration is a function of the shapes only.
+ */
+#ifndef NF4STREAM_H
+#define NF4STREAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define NF4S_OK 0
+#define NF4S_EINVAL -1      /* null pointer, bad enum, non-finite scale, r out of range */
+#define NF4S_ESHAPE -2      /* K_in % 64 != 0, odd element count, M/N <= 0, size overflow */
+#define NF4S_EALIGN -3      /* pointer not aligned (16 B for tensors, 256 B for shards/slots) */
+#define NF4S_ETABLE -4      /* descriptor's table hash differs from the library's tables */
+#define NF4S_EKEY -5        /* method / block / nested block / double-quant flag mismatch */
+#define NF4S_ESLOT -6       /* slot too small, pool size outside [2, 8], unknown layer */
+#define NF4S_ENOTPINNED -7  /* host source is not page-locked */
+#define NF4S_EHIP -8        /* a HIP runtime call failed (message kept) */
+#define NF4S_EWORKSPACE -9  /* workspace missing or smaller than nf4s_workspace_bytes() */
+
+/* ---- format ------------------------------------------------------------- */
+#define NF4S_METHOD_NF4 1
+#define NF4S_BLOCK 64
+#define NF4S_NESTED_BLOCK 256
+#define NF4S_SECTION_ALIGN 256
+#define NF4S_MAX_RANK 64
+
+#define NF4S_DTYPE_F32 0
+#define NF4S_DTYPE_BF16 1
+
+/*
+ * Where one quantised tensor W[n_out, k_in] lives inside a shard (a device or
+ * host byte buffer). [G] s2.1/s2.4: uint8 packed codes, 8-bit absmax codes,
+ * fp32 nested absmax, one fp32 offset. Offsets are bytes from the shard base
+ * and are multiples of NF4S_SECTION_ALIGN.
+ *   packed: uint8 [n_out*k_in/2], row-major, element 2j in the high nibble of
+ *           byte j;
+ *   q8:     uint8 [nb], nb = n_out*k_in/64, block b = elements [64b, 64b+64);
+ *   nested: float [nn], nn = ceil(nb/256), nested block j = blocks [256j, 256j+256);
+ *   offset: float [1], the mean of the fp32 absmax the q8 codes are centred on.
+ * table_hash is FNV-1a-64 over the fp32 bytes of the NF4 table then the nested
+ * table; a descriptor whose hash differs from nf4s_table_hash() is refused
+ * ([G] s2.4: a per-weight table would silently dequantise with wrong constants).
+ */
+typedef struct nf4s_tensor_desc {
+  int64_t n_out;
+  int64_t k_in;
+  int32_t method;        /* NF4S_METHOD_NF4 */
+  int32_t blocksize;     /* NF4S_BLOCK */
+  int32_t nested_block;  /* NF4S_NESTED_BLOCK */
+  int32_t double_quant;  /* 1 ([G] s1.3: the flag must agree between sharder and reader) */
+  uint64_t off_packed;
+  uint64_t off_q8;
+  uint64_t off_nested;
+  uint64_t off_offset;
+  uint64_t end;          /* first byte after this tensor's sections */
+  uint64_t table_hash;
+} nf4s_tensor_desc;
+
+/* Library identification and the last error of the calling thread. */
+const char* nf4s_version(void);
+const char* nf4s_last_error(void);
+
+/*
+ * Payload bytes of one tensor, [G] s2.4: N/2 + ceil(N/64) + 4*ceil(N/16384) + 4
+ * for N = n_out*k_in (about 0.516 bytes per parameter). Section padding is not
+ * included (see nf4s_tensor_layout). Returns 0 for invalid shapes.
+ */
+uint64_t nf4_shard_bytes(int64_t n_out, int64_t k_in);
+
+/*
+ * Fill *out with the section offsets of a tensor placed at byte `base` of a
+ * shard (base must be a multiple of 256); out->end is where the next tensor
+ * may start. Errors: ESHAPE (k_in % 64, n_out <= 0), EALIGN (base), EINVAL.
+ */
+int nf4s_tensor_layout(int64_t n_out, int64_t k_in, uint64_t base, nf4s_tensor_desc* out);
+
+/*
+ * Copy out the library's code tables ([G] s2.4: 16 fp32 NF4 levels and 256
+ * fp32 nested levels, ascending, shared by every tensor) and their hash.
+ * The NF4 levels are normal quantiles (QLoRA section 3); the nested table is
+ * the signed dynamic-tree map (8-bit Optimizers section 2). Either pointer may
+ * be NULL.
+ */
+int nf4_code_tables(float* c4_16, float* c8_256);
+uint64_t nf4s_table_hash(void);
+
+/*
+ * Scratch bytes an operation needs for the given shape (0 means none; ws may
+ * then be NULL). op: NF4S_OP_QUANTIZE (n_out, k_in), NF4S_OP_LINEAR_FWD and
+ * NF4S_OP_LINEAR_BWD and NF4S_OP_LORA_BWD (M, n_out, k_in). The value depends
+ * on shapes only.
+ */
+#define NF4S_OP_QUANTIZE 1
+#define NF4S_OP_LINEAR_FWD 2
+#define NF4S_OP_LINEAR_BWD 3
+#define NF4S_OP_LORA_BWD 4
+int nf4s_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, size_t* bytes);
+
+/*
+ * Offline NF4 double-quant of one tensor, [G] s2.1 (quantised once, one tensor
+ * at a time, written as packed bytes plus sidecars) and s2.3 (deterministic).
+ *   w_dev:     W[n_out, k_in] on the device, dtype NF4S_DTYPE_F32 or _BF16;
+ *   shard_dev: device buffer receiving the sections at desc's offsets
+ *              (desc from nf4s_tensor_layout, base 256-B aligned);
+ *   status_dev: nullable device int32, set to 1 if W held a non-finite value
+ *              (codes for such a tensor are meaningless), else left as is;
+ *   ws:        nf4s_workspace_bytes(NF4S_OP_QUANTIZE) bytes.
+ * Per 64-block: absmax, v = w/absmax (IEEE fp32 division), code = nearest NF4
+ * level (ties to the lower code; all-zero block -> level 0). Offset = mean of
+ * the absmax (exact sum, one fp64 division, rounded to fp32); nested absmax =
+ * max |absmax - offset| over 256 blocks; q8 = nearest nested level of
+ * (absmax - offset)/nested. Errors: EINVAL, ESHAPE, EALIGN, EKEY, EWORKSPACE.
+ */
+int nf4_quantize_shard(const void* w_dev, int dtype, int64_t n_out, int64_t k_in,
+                       void* shard_dev, const nf4s_tensor_desc* desc, int32_t* status_dev,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dequantise one tensor to bf16, [G] s2.1 (NF4 weight rebuilt per call from
+ * the streamed bytes and the two shared tables, bf16 compute):
+ *   a'[b] = fp32(fp32(C8[q8[b]] * nested[b/256]) + offset)  (two roundings)
+ *   W'[e] = bf16_rne(fp32(C4[code[e]] * a'[e/64]))
+ * w_bf16_dev: uint16 [n_out, k_in]. Errors: EINVAL, EALIGN, ETABLE, EKEY.
+ */
+int nf4_dequant(const void* shard_dev, const nf4s_tensor_desc* d, uint16_t* w_bf16_dev,
+                void* stream);
+
+/*
+ * Forward of a frozen NF4 linear with an optional LoRA adapter, [G] s2.1
+ * (matmul over the NF4 weight with bf16 compute; LoRA r16 on the target
+ * projections):  y = bf16( x.W'^T + scale * u.B^T ),  fp32 accumulation, W'
+ * dequantised tile by tile on chip (never written to HBM).
+ *   x:      bf16 [M, k_in];  y: bf16 [M, n_out];
+ *   lora_u: nullable fp32 [M, r] = x.A^T from lora_fwd;
+ *   lora_B: fp32 [n_out, r] (required iff lora_u is given); r in [1, 64];
+ *   ws:     nf4s_workspace_bytes(NF4S_OP_LINEAR_FWD, M, n_out, k_in) bytes.
+ * The LoRA term is contracted in bf16 on the matrix cores (u and scale*B
+ * rounded to bf16). Errors: EINVAL, ESHAPE, EALIGN, ETABLE, EKEY, EWORKSPACE.
+ */
+int streamed_linear_fwd(const void* shard_dev, const nf4s_tensor_desc* d, const uint16_t* x,
+                        int64_t M, uint16_t* y, const float* lora_u, const float* lora_B, int r,
+                        float scale, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward (input gradient only) of the same linear, [G] s4.4 (frozen base:
+ * dL/dx and no dL/dW) and [E] (dL/dx needs W again, hence the second read):
+ *   dx = bf16( dy.W' + du.A ),  fp32 accumulation.
+ *   dy: bf16 [M, n_out];  dx: bf16 [M, k_in];
+ *   lora_du: nullable fp32 [M, r] (= scale * dy.B, from lora_bwd);
+ *   lora_A:  fp32 [r, k_in] (required iff lora_du is given).
+ * Errors as streamed_linear_fwd.
+ */
+int streamed_linear_bwd(const void* shard_dev, const nf4s_tensor_desc* d, const uint16_t* dy,
+                        int64_t M, uint16_t* dx, const float* lora_du, const float* lora_A,
+                        int r, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * LoRA down-projection, u = x.A^T in fp32 ([G] s2.1, adapter on q/v):
+ *   x: bf16 [M, k_in]; A: fp32 [r, k_in]; u_out: fp32 [M, r].
+ * Deterministic (fixed reduction order). Errors: EINVAL, ESHAPE, EALIGN.
+ */
+int lora_fwd(const uint16_t* x, int64_t M, int64_t k_in, const float* A, int r, float* u_out,
+             void* stream);
+
+/*
+ * LoRA gradients for L with upstream dy ([G] s2.2 check 2: non-zero in every
+ * layer; s2.5: with B = 0, dA is structurally zero):
+ *   du_out = scale * dy.B        fp32 [M, r]
+ *   dB    (+)= scale * dy^T.u     fp32 [n_out, r]
+ *   dA    (+)= du^T.x             fp32 [r, k_in]
+ * x: bf16 [M, k_in]; dy: bf16 [M, n_out]; u: fp32 [M, r] (x.A^T);
+ * B: fp32 [n_out, r]. accumulate = 0 overwrites dA/dB, 1 adds to them.
+ * ws: nf4s_workspace_bytes(NF4S_OP_LORA_BWD, M, n_out, k_in) bytes.
+ * Reductions run in a fixed order, so results are bit-reproducible.
+ * Errors: EINVAL, ESHAPE, EALIGN, EWORKSPACE.
+ */
+int lora_bwd(const uint16_t* x, const uint16_t* dy, const float* u, int64_t M, int64_t k_in,
+             int64_t n_out, const float* B, int r, float scale, float* dA, float* dB,
+             float* du_out, int accumulate, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Enqueue one layer-shard copy host -> device slot on copy_stream, [E] (a
+ * dedicated stream prefetches the next layer while the current one computes):
+ * wait wait_slot_free (nullable; the event recorded after the slot's last
+ * reader), hipMemcpyAsync H2D, record record_ready (nullable).
+ * Errors: EINVAL, EALIGN (slot), ESLOT (bytes > slot_bytes), ENOTPINNED
+ * (host_pinned_src not page-locked: a pageable source would make the copy
+ * synchronous), EHIP.
+ */
+int layer_prefetch(void* slot_dev, size_t slot_bytes, const void* host_pinned_src, size_t bytes,
+                   void* copy_stream, void* wait_slot_free, void* record_ready);
+
+/* Events for layer_prefetch and cross-stream ordering (timing disabled). */
+int nf4s_event_create(void** event_out);
+int nf4s_event_destroy(void* event);
+int nf4s_event_record(void* event, void* stream);
+int nf4s_stream_wait_event(void* stream, void* event);
+
+/*
+ * Slot pool: n_slots device slots that layer shards stream through, [E]
+ * (2..8 buffers, default 2; forward prefetches i+1, backward i-1). The pool
+ * tracks which layer each slot holds and orders every overwrite after the
+ * slot's last reader with a per-slot free event, and every read after its copy
+ * with a per-slot ready event -- the ordering whose absence corrupted
+ * gradients but not the forward pass in the pages' slot-aliasing bug ([E],
+ * the NF4 layers above ~165 MiB). A layer still resident in a slot is not
+ * copied again.
+ *   nf4s_pool_create:   slots are caller-owned device buffers (256-B aligned,
+ *                       slot_bytes each); n_slots in [2, 8]; copy and compute
+ *                       are distinct streams.
+ *   nf4s_pool_set_layer: register layer `layer`'s pinned host shard.
+ *   nf4s_pool_prefetch: start copying `layer` into a slot no reader holds
+ *                       (no-op if resident or in flight). ESLOT if every
+ *                       slot is held.
+ *   nf4s_pool_acquire:  make `layer` resident (copying now if needed), make
+ *                       the compute stream wait for it, return its slot.
+ *   nf4s_pool_release:  record the slot's free event on the compute stream
+ *                       after the last kernel that reads it was enqueued.
+ *   nf4s_pool_stats:    copies issued and bytes copied so far.
+ */
+typedef struct nf4s_pool nf4s_pool;
+int nf4s_pool_create(int n_slots, void* const* slots, size_t slot_bytes, void* copy_stream,
+                     void* compute_stream, nf4s_pool** out);
+int nf4s_pool_destroy(nf4s_pool* pool);
+int nf4s_pool_set_layer(nf4s_pool* pool, int layer, const void* host_pinned_src, size_t bytes);
+int nf4s_pool_prefetch(nf4s_pool* pool, int layer);
+int nf4s_pool_acquire(nf4s_pool* pool, int layer, void** slot_dev_out);
+int nf4s_pool_release(nf4s_pool* pool, int layer);
+int nf4s_pool_stats(const nf4s_pool* pool, uint64_t* copies, uint64_t* bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NF4STREAM_H */

@@ -1,0 +1,235 @@
+"""Python binding of libnf4stream (the layer-streamed NF4 + LoRA hot path).
+
+Argument marshalling only: every function forwards to the C ABI declared in
+include/nf4stream.h with the same name, raises Nf4sError on a negative status,
+and computes nothing itself. Device pointers and streams are plain integers
+(``tensor.data_ptr()``, ``torch.cuda.Stream().cuda_stream``). There is no
+fallback: if the HIP library is missing, importing a function that needs it
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnf4stream.so")
+
+OK, EINVAL, ESHAPE, EALIGN, ETABLE, EKEY, ESLOT, ENOTPINNED, EHIP, EWORKSPACE = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9)
+DTYPE_F32, DTYPE_BF16 = 0, 1
+OP_QUANTIZE, OP_LINEAR_FWD, OP_LINEAR_BWD, OP_LORA_BWD = 1, 2, 3, 4
+METHOD_NF4 = 1
+
+EXPORTS = (
+    "nf4s_version", "nf4s_last_error", "nf4_shard_bytes", "nf4s_tensor_layout",
+    "nf4_code_tables", "nf4s_table_hash", "nf4s_workspace_bytes", "nf4_quantize_shard",
+    "nf4_dequant", "streamed_linear_fwd", "streamed_linear_bwd", "lora_fwd", "lora_bwd",
+    "layer_prefetch", "nf4s_event_create", "nf4s_event_destroy", "nf4s_event_record",
+    "nf4s_stream_wait_event", "nf4s_pool_create", "nf4s_pool_destroy", "nf4s_pool_set_layer",
+    "nf4s_pool_prefetch", "nf4s_pool_acquire", "nf4s_pool_release", "nf4s_pool_stats",
+)
+
+
+class Nf4sError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"nf4stream error {code}: {msg}")
+        self.code = code
+
+
+class TensorDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_out", ctypes.c_int64), ("k_in", ctypes.c_int64),
+        ("method", ctypes.c_int32), ("blocksize", ctypes.c_int32),
+        ("nested_block", ctypes.c_int32), ("double_quant", ctypes.c_int32),
+        ("off_packed", ctypes.c_uint64), ("off_q8", ctypes.c_uint64),
+        ("off_nested", ctypes.c_uint64), ("off_offset", ctypes.c_uint64),
+        ("end", ctypes.c_uint64), ("table_hash", ctypes.c_uint64),
+    ]
+
+    def copy(self):
+        d = TensorDesc()
+        ctypes.pointer(d)[0] = self
+        return d
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SIG = {
+    "nf4s_version": (ctypes.c_char_p, []),
+    "nf4s_last_error": (ctypes.c_char_p, []),
+    "nf4_shard_bytes": (ctypes.c_uint64, [_I64, _I64]),
+    "nf4s_tensor_layout": (ctypes.c_int, [_I64, _I64, ctypes.c_uint64, ctypes.POINTER(TensorDesc)]),
+    "nf4_code_tables": (ctypes.c_int, [_P, _P]),
+    "nf4s_table_hash": (ctypes.c_uint64, []),
+    "nf4s_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
+    "nf4_quantize_shard": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _P, ctypes.POINTER(TensorDesc),
+                                          _P, _P, ctypes.c_size_t, _P]),
+    "nf4_dequant": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _P]),
+    "streamed_linear_fwd": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P, _P,
+                                           ctypes.c_int, ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "streamed_linear_bwd": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P, _P,
+                                           ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "lora_fwd": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, _P, _P]),
+    "lora_bwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, ctypes.c_float,
+                                _P, _P, _P, ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "layer_prefetch": (ctypes.c_int, [_P, ctypes.c_size_t, _P, ctypes.c_size_t, _P, _P, _P]),
+    "nf4s_event_create": (ctypes.c_int, [ctypes.POINTER(_P)]),
+    "nf4s_event_destroy": (ctypes.c_int, [_P]),
+    "nf4s_event_record": (ctypes.c_int, [_P, _P]),
+    "nf4s_stream_wait_event": (ctypes.c_int, [_P, _P]),
+    "nf4s_pool_create": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(_P), ctypes.c_size_t, _P, _P,
+                                        ctypes.POINTER(_P)]),
+    "nf4s_pool_destroy": (ctypes.c_int, [_P]),
+    "nf4s_pool_set_layer": (ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_size_t]),
+    "nf4s_pool_prefetch": (ctypes.c_int, [_P, ctypes.c_int]),
+    "nf4s_pool_acquire": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_P)]),
+    "nf4s_pool_release": (ctypes.c_int, [_P, ctypes.c_int]),
+    "nf4s_pool_stats": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)]),
+}
+
+
+def lib():
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m layer_streamed_nf4_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIG.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != OK:
+        raise Nf4sError(rc, lib().nf4s_last_error().decode())
+    return rc
+
+
+def nf4s_version() -> str:
+    return lib().nf4s_version().decode()
+
+
+def nf4_shard_bytes(n_out: int, k_in: int) -> int:
+    return int(lib().nf4_shard_bytes(n_out, k_in))
+
+
+def nf4s_tensor_layout(n_out: int, k_in: int, base: int = 0) -> TensorDesc:
+    d = TensorDesc()
+    _check(lib().nf4s_tensor_layout(n_out, k_in, base, ctypes.byref(d)))
+    return d
+
+
+def nf4_code_tables():
+    c4 = np.zeros(16, np.float32)
+    c8 = np.zeros(256, np.float32)
+    _check(lib().nf4_code_tables(c4.ctypes.data, c8.ctypes.data))
+    return c4, c8
+
+
+def nf4s_table_hash() -> int:
+    return int(lib().nf4s_table_hash())
+
+
+def nf4s_workspace_bytes(op: int, M: int, n_out: int, k_in: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check(lib().nf4s_workspace_bytes(op, M, n_out, k_in, ctypes.byref(b)))
+    return int(b.value)
+
+
+def nf4_quantize_shard(w, dtype, n_out, k_in, shard, desc, status, ws, ws_bytes, stream=0):
+    _check(lib().nf4_quantize_shard(w, dtype, n_out, k_in, shard, ctypes.byref(desc), status, ws,
+                                    ws_bytes, stream))
+
+
+def nf4_dequant(shard, desc, w_bf16, stream=0):
+    _check(lib().nf4_dequant(shard, ctypes.byref(desc), w_bf16, stream))
+
+
+def streamed_linear_fwd(shard, desc, x, M, y, lora_u, lora_B, r, scale, ws, ws_bytes, stream=0):
+    _check(lib().streamed_linear_fwd(shard, ctypes.byref(desc), x, M, y, lora_u, lora_B, r, scale,
+                                     ws, ws_bytes, stream))
+
+
+def streamed_linear_bwd(shard, desc, dy, M, dx, lora_du, lora_A, r, ws, ws_bytes, stream=0):
+    _check(lib().streamed_linear_bwd(shard, ctypes.byref(desc), dy, M, dx, lora_du, lora_A, r, ws,
+                                     ws_bytes, stream))
+
+
+def lora_fwd(x, M, k_in, A, r, u_out, stream=0):
+    _check(lib().lora_fwd(x, M, k_in, A, r, u_out, stream))
+
+
+def lora_bwd(x, dy, u, M, k_in, n_out, B, r, scale, dA, dB, du_out, accumulate, ws, ws_bytes,
+             stream=0):
+    _check(lib().lora_bwd(x, dy, u, M, k_in, n_out, B, r, scale, dA, dB, du_out, accumulate, ws,
+                          ws_bytes, stream))
+
+
+def layer_prefetch(slot, slot_bytes, host_src, nbytes, copy_stream, wait_free=None, record_ready=None):
+    _check(lib().layer_prefetch(slot, slot_bytes, host_src, nbytes, copy_stream, wait_free,
+                                record_ready))
+
+
+def nf4s_event_create() -> int:
+    ev = _P()
+    _check(lib().nf4s_event_create(ctypes.byref(ev)))
+    return ev.value
+
+
+def nf4s_event_destroy(ev):
+    _check(lib().nf4s_event_destroy(ev))
+
+
+def nf4s_event_record(ev, stream):
+    _check(lib().nf4s_event_record(ev, stream))
+
+
+def nf4s_stream_wait_event(stream, ev):
+    _check(lib().nf4s_stream_wait_event(stream, ev))
+
+
+def nf4s_pool_create(slots, slot_bytes, copy_stream, compute_stream) -> int:
+    arr = (_P * len(slots))(*slots)
+    out = _P()
+    _check(lib().nf4s_pool_create(len(slots), arr, slot_bytes, copy_stream, compute_stream,
+                                  ctypes.byref(out)))
+    return out.value
+
+
+def nf4s_pool_destroy(pool):
+    _check(lib().nf4s_pool_destroy(pool))
+
+
+def nf4s_pool_set_layer(pool, layer, host_src, nbytes):
+    _check(lib().nf4s_pool_set_layer(pool, layer, host_src, nbytes))
+
+
+def nf4s_pool_prefetch(pool, layer):
+    _check(lib().nf4s_pool_prefetch(pool, layer))
+
+
+def nf4s_pool_acquire(pool, layer) -> int:
+    out = _P()
+    _check(lib().nf4s_pool_acquire(pool, layer, ctypes.byref(out)))
+    return out.value
+
+
+def nf4s_pool_release(pool, layer):
+    _check(lib().nf4s_pool_release(pool, layer))
+
+
+def nf4s_pool_stats(pool):
+    c = ctypes.c_uint64(0)
+    b = ctypes.c_uint64(0)
+    _check(lib().nf4s_pool_stats(pool, ctypes.byref(c), ctypes.byref(b)))
+    return int(c.value), int(b.value)

@@ -1,0 +1,495 @@
+// Host side of the C ABI: argument validation (before anything is enqueued),
+// descriptor and table-key checks, dispatch to the kernels, events, the
+// layer prefetch and the slot pool. No device memory is allocated here.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+using namespace nf4s;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(NF4S_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+// Shapes the kernels support: n_out a positive multiple of 8 (16-byte rows of
+// bf16 activations), k_in a positive multiple of 64 (whole NF4 blocks per row),
+// element count below 2^40.
+int check_shape(int64_t n_out, int64_t k_in) {
+  if (n_out <= 0 || k_in <= 0) return fail(NF4S_ESHAPE, "n_out=%lld k_in=%lld must be positive", (long long)n_out, (long long)k_in);
+  if (k_in % 64) return fail(NF4S_ESHAPE, "k_in=%lld is not a multiple of 64", (long long)k_in);
+  if (n_out % 8) return fail(NF4S_ESHAPE, "n_out=%lld is not a multiple of 8", (long long)n_out);
+  if (n_out > (1ll << 26) || k_in > (1ll << 26) || n_out * k_in > (1ll << 40))
+    return fail(NF4S_ESHAPE, "tensor too large");
+  return NF4S_OK;
+}
+
+int check_desc(const nf4s_tensor_desc* d) {
+  if (!d) return fail(NF4S_EINVAL, "descriptor is NULL");
+  int rc = check_shape(d->n_out, d->k_in);
+  if (rc) return rc;
+  if (d->method != NF4S_METHOD_NF4 || d->blocksize != NF4S_BLOCK ||
+      d->nested_block != NF4S_NESTED_BLOCK || d->double_quant != 1)
+    return fail(NF4S_EKEY,
+                "descriptor key mismatch: method=%d block=%d nested=%d double_quant=%d "
+                "(library: NF4, 64, 256, 1)",
+                d->method, d->blocksize, d->nested_block, d->double_quant);
+  if (d->table_hash != host_table_hash())
+    return fail(NF4S_ETABLE, "descriptor table hash %016llx differs from library tables %016llx",
+                (unsigned long long)d->table_hash, (unsigned long long)host_table_hash());
+  nf4s_tensor_desc ref;
+  const uint64_t base = d->off_packed;
+  if (base % NF4S_SECTION_ALIGN) return fail(NF4S_EALIGN, "packed section not 256-B aligned");
+  if (nf4s_tensor_layout(d->n_out, d->k_in, base, &ref)) return NF4S_ESHAPE;
+  if (ref.off_q8 != d->off_q8 || ref.off_nested != d->off_nested ||
+      ref.off_offset != d->off_offset || ref.end != d->end)
+    return fail(NF4S_EKEY, "descriptor section offsets do not follow the shard layout");
+  return NF4S_OK;
+}
+
+QPtrs resolve(const void* shard, const nf4s_tensor_desc* d) {
+  const uint8_t* b = static_cast<const uint8_t*>(shard);
+  QPtrs q;
+  q.packed = b + d->off_packed;
+  q.q8 = b + d->off_q8;
+  q.nested = reinterpret_cast<const float*>(b + d->off_nested);
+  q.offset = reinterpret_cast<const float*>(b + d->off_offset);
+  return q;
+}
+
+int check_ptr(const void* p, const char* name, uintptr_t align = 16) {
+  if (!p) return fail(NF4S_EINVAL, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(NF4S_EALIGN, "%s is not %u-byte aligned", name, (unsigned)align);
+  return NF4S_OK;
+}
+
+int check_rank(int r) {
+  if (r < 1 || r > NF4S_MAX_RANK) return fail(NF4S_EINVAL, "rank r=%d outside [1, %d]", r, NF4S_MAX_RANK);
+  return NF4S_OK;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return NF4S_OK;
+  if (!ws || have < need)
+    return fail(NF4S_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? have : 0);
+  if (!aligned(ws, 256)) return fail(NF4S_EALIGN, "workspace not 256-byte aligned");
+  return NF4S_OK;
+}
+
+int check_pinned(const void* p) {
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(NF4S_ENOTPINNED, "host source %p is not page-locked (%s)", p, hipGetErrorString(e));
+  }
+  if (attr.type != hipMemoryTypeHost)
+    return fail(NF4S_ENOTPINNED, "source %p is not page-locked host memory (type %d)", p, (int)attr.type);
+  return NF4S_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nf4s_version(void) { return "nf4stream 0.1 gfx950"; }
+const char* nf4s_last_error(void) { return g_err.c_str(); }
+
+uint64_t nf4_shard_bytes(int64_t n_out, int64_t k_in) {
+  if (n_out <= 0 || k_in <= 0) return 0;
+  const uint64_t n = (uint64_t)n_out * (uint64_t)k_in;
+  if (n % 2) return 0;
+  const uint64_t nb = (n + 63) / 64;
+  const uint64_t nn = (nb + 255) / 256;
+  return n / 2 + nb + 4 * nn + 4;
+}
+
+int nf4s_tensor_layout(int64_t n_out, int64_t k_in, uint64_t base, nf4s_tensor_desc* out) {
+  if (!out) return fail(NF4S_EINVAL, "out is NULL");
+  int rc = check_shape(n_out, k_in);
+  if (rc) return rc;
+  if (base % NF4S_SECTION_ALIGN) return fail(NF4S_EALIGN, "base %llu not 256-byte aligned", (unsigned long long)base);
+  const uint64_t n = (uint64_t)n_out * (uint64_t)k_in;
+  const uint64_t nb = n / 64;
+  const uint64_t nn = (nb + 255) / 256;
+  nf4s_tensor_desc d;
+  memset(&d, 0, sizeof d);
+  d.n_out = n_out;
+  d.k_in = k_in;
+  d.method = NF4S_METHOD_NF4;
+  d.blocksize = NF4S_BLOCK;
+  d.nested_block = NF4S_NESTED_BLOCK;
+  d.double_quant = 1;
+  d.off_packed = base;
+  d.off_q8 = round_up(d.off_packed + n / 2, NF4S_SECTION_ALIGN);
+  d.off_nested = round_up(d.off_q8 + nb, NF4S_SECTION_ALIGN);
+  d.off_offset = round_up(d.off_nested + 4 * nn, NF4S_SECTION_ALIGN);
+  d.end = round_up(d.off_offset + 4, NF4S_SECTION_ALIGN);
+  d.table_hash = host_table_hash();
+  *out = d;
+  return NF4S_OK;
+}
+
+int nf4_code_tables(float* c4_16, float* c8_256) {
+  const Tables& t = host_tables();
+  if (c4_16) memcpy(c4_16, t.c4, sizeof t.c4);
+  if (c8_256) memcpy(c8_256, t.c8, sizeof t.c8);
+  return NF4S_OK;
+}
+
+uint64_t nf4s_table_hash(void) { return host_table_hash(); }
+
+int nf4s_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, size_t* bytes) {
+  if (!bytes) return fail(NF4S_EINVAL, "bytes is NULL");
+  int rc = check_shape(n_out, k_in);
+  if (rc) return rc;
+  switch (op) {
+    case NF4S_OP_QUANTIZE:
+      *bytes = quantize_ws_bytes(n_out, k_in);
+      return NF4S_OK;
+    case NF4S_OP_LINEAR_FWD:
+    case NF4S_OP_LINEAR_BWD: {
+      if (M <= 0) return fail(NF4S_ESHAPE, "M=%lld must be positive", (long long)M);
+      const bool bwd = op == NF4S_OP_LINEAR_BWD;
+      *bytes = plan_gemm(M, bwd ? k_in : n_out, bwd ? n_out : k_in).ws_bytes;
+      return NF4S_OK;
+    }
+    case NF4S_OP_LORA_BWD:
+      if (M <= 0) return fail(NF4S_ESHAPE, "M=%lld must be positive", (long long)M);
+      *bytes = lora_bwd_ws_bytes(M, k_in, n_out);
+      return NF4S_OK;
+    default:
+      return fail(NF4S_EINVAL, "unknown op %d", op);
+  }
+}
+
+int nf4_quantize_shard(const void* w_dev, int dtype, int64_t n_out, int64_t k_in, void* shard_dev,
+                       const nf4s_tensor_desc* desc, int32_t* status_dev, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int rc;
+  if (dtype != NF4S_DTYPE_F32 && dtype != NF4S_DTYPE_BF16) return fail(NF4S_EINVAL, "dtype %d", dtype);
+  if ((rc = check_shape(n_out, k_in))) return rc;
+  if ((rc = check_desc(desc))) return rc;
+  if (desc->n_out != n_out || desc->k_in != k_in)
+    return fail(NF4S_ESHAPE, "descriptor shape %lldx%lld differs from %lldx%lld",
+                (long long)desc->n_out, (long long)desc->k_in, (long long)n_out, (long long)k_in);
+  if ((rc = check_ptr(w_dev, "w_dev"))) return rc;
+  if ((rc = check_ptr(shard_dev, "shard_dev", 256))) return rc;
+  if ((rc = check_ws(ws, ws_bytes, quantize_ws_bytes(n_out, k_in)))) return rc;
+  uint8_t* b = static_cast<uint8_t*>(shard_dev);
+  hipError_t e = launch_quantize(w_dev, dtype, n_out, k_in, b + desc->off_packed, b + desc->off_q8,
+                                 reinterpret_cast<float*>(b + desc->off_nested),
+                                 reinterpret_cast<float*>(b + desc->off_offset), status_dev, ws,
+                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "quantize launch");
+}
+
+int nf4_dequant(const void* shard_dev, const nf4s_tensor_desc* d, uint16_t* w_bf16_dev, void* stream) {
+  int rc;
+  if ((rc = check_desc(d))) return rc;
+  if ((rc = check_ptr(shard_dev, "shard_dev", 256))) return rc;
+  if ((rc = check_ptr(w_bf16_dev, "w_bf16_dev"))) return rc;
+  hipError_t e = launch_dequant(resolve(shard_dev, d), d->n_out, d->k_in, w_bf16_dev,
+                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "dequant launch");
+}
+
+static int linear_common(bool bwd, const void* shard_dev, const nf4s_tensor_desc* d,
+                         const uint16_t* a, int64_t M, uint16_t* out, const float* lora_l,
+                         const float* lora_r, int r, float scale, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int rc;
+  if ((rc = check_desc(d))) return rc;
+  if (M <= 0 || M > (1ll << 24)) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
+  if ((rc = check_ptr(shard_dev, "shard_dev", 256))) return rc;
+  if ((rc = check_ptr(a, bwd ? "dy" : "x"))) return rc;
+  if ((rc = check_ptr(out, bwd ? "dx" : "y"))) return rc;
+  if ((lora_l == nullptr) != (lora_r == nullptr))
+    return fail(NF4S_EINVAL, "LoRA operands must be given together");
+  if (lora_l) {
+    if ((rc = check_rank(r))) return rc;
+    if ((rc = check_ptr(lora_l, bwd ? "lora_du" : "lora_u", 4))) return rc;
+    if ((rc = check_ptr(lora_r, bwd ? "lora_A" : "lora_B", 4))) return rc;
+    if (!std::isfinite(scale)) return fail(NF4S_EINVAL, "scale is not finite");
+  }
+  const GemmPlan p = plan_gemm(M, bwd ? d->k_in : d->n_out, bwd ? d->n_out : d->k_in);
+  if ((rc = check_ws(ws, ws_bytes, p.ws_bytes))) return rc;
+  hipError_t e = launch_linear(bwd, resolve(shard_dev, d), d->n_out, d->k_in, a, M, out, lora_l,
+                               lora_r, lora_l ? r : 0, scale, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "linear launch");
+}
+
+int streamed_linear_fwd(const void* shard_dev, const nf4s_tensor_desc* d, const uint16_t* x,
+                        int64_t M, uint16_t* y, const float* lora_u, const float* lora_B, int r,
+                        float scale, void* ws, size_t ws_bytes, void* stream) {
+  return linear_common(false, shard_dev, d, x, M, y, lora_u, lora_B, r, scale, ws, ws_bytes, stream);
+}
+
+int streamed_linear_bwd(const void* shard_dev, const nf4s_tensor_desc* d, const uint16_t* dy,
+                        int64_t M, uint16_t* dx, const float* lora_du, const float* lora_A, int r,
+                        void* ws, size_t ws_bytes, void* stream) {
+  return linear_common(true, shard_dev, d, dy, M, dx, lora_du, lora_A, r, 1.0f, ws, ws_bytes, stream);
+}
+
+int lora_fwd(const uint16_t* x, int64_t M, int64_t k_in, const float* A, int r, float* u_out,
+             void* stream) {
+  int rc;
+  if (M <= 0 || k_in <= 0 || k_in % 64) return fail(NF4S_ESHAPE, "M=%lld k_in=%lld", (long long)M, (long long)k_in);
+  if ((rc = check_rank(r))) return rc;
+  if ((rc = check_ptr(x, "x"))) return rc;
+  if ((rc = check_ptr(A, "A", 4))) return rc;
+  if ((rc = check_ptr(u_out, "u_out", 4))) return rc;
+  hipError_t e = launch_lora_fwd(x, M, k_in, A, r, u_out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "lora_fwd launch");
+}
+
+int lora_bwd(const uint16_t* x, const uint16_t* dy, const float* u, int64_t M, int64_t k_in,
+             int64_t n_out, const float* B, int r, float scale, float* dA, float* dB,
+             float* du_out, int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if (M <= 0) return fail(NF4S_ESHAPE, "M=%lld must be positive", (long long)M);
+  if ((rc = check_shape(n_out, k_in))) return rc;
+  if ((rc = check_rank(r))) return rc;
+  if (!std::isfinite(scale)) return fail(NF4S_EINVAL, "scale is not finite");
+  if (accumulate != 0 && accumulate != 1) return fail(NF4S_EINVAL, "accumulate must be 0 or 1");
+  if ((rc = check_ptr(x, "x"))) return rc;
+  if ((rc = check_ptr(dy, "dy"))) return rc;
+  if ((rc = check_ptr(u, "u", 4))) return rc;
+  if ((rc = check_ptr(B, "B", 4))) return rc;
+  if ((rc = check_ptr(dA, "dA", 4))) return rc;
+  if ((rc = check_ptr(dB, "dB", 4))) return rc;
+  if ((rc = check_ptr(du_out, "du_out", 4))) return rc;
+  if ((rc = check_ws(ws, ws_bytes, lora_bwd_ws_bytes(M, k_in, n_out)))) return rc;
+  hipError_t e = launch_lora_bwd(x, dy, u, M, k_in, n_out, B, r, scale, dA, dB, du_out, accumulate,
+                                 ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "lora_bwd launch");
+}
+
+int layer_prefetch(void* slot_dev, size_t slot_bytes, const void* host_pinned_src, size_t bytes,
+                   void* copy_stream, void* wait_slot_free, void* record_ready) {
+  int rc;
+  if ((rc = check_ptr(slot_dev, "slot_dev", 256))) return rc;
+  if (!host_pinned_src) return fail(NF4S_EINVAL, "host source is NULL");
+  if (bytes == 0 || bytes > slot_bytes)
+    return fail(NF4S_ESLOT, "shard of %zu bytes does not fit a slot of %zu bytes", bytes, slot_bytes);
+  if ((rc = check_pinned(host_pinned_src))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(copy_stream);
+  hipError_t e;
+  if (wait_slot_free && (e = hipStreamWaitEvent(s, static_cast<hipEvent_t>(wait_slot_free), 0)) != hipSuccess)
+    return hip_fail(e, "hipStreamWaitEvent");
+  if ((e = hipMemcpyAsync(slot_dev, host_pinned_src, bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
+    return hip_fail(e, "hipMemcpyAsync");
+  if (record_ready && (e = hipEventRecord(static_cast<hipEvent_t>(record_ready), s)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord");
+  return NF4S_OK;
+}
+
+int nf4s_event_create(void** event_out) {
+  if (!event_out) return fail(NF4S_EINVAL, "event_out is NULL");
+  hipEvent_t ev;
+  hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+  if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+  *event_out = ev;
+  return NF4S_OK;
+}
+
+int nf4s_event_destroy(void* event) {
+  if (!event) return NF4S_OK;
+  hipError_t e = hipEventDestroy(static_cast<hipEvent_t>(event));
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "hipEventDestroy");
+}
+
+int nf4s_event_record(void* event, void* stream) {
+  if (!event) return fail(NF4S_EINVAL, "event is NULL");
+  hipError_t e = hipEventRecord(static_cast<hipEvent_t>(event), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "hipEventRecord");
+}
+
+int nf4s_stream_wait_event(void* stream, void* event) {
+  if (!event) return fail(NF4S_EINVAL, "event is NULL");
+  hipError_t e = hipStreamWaitEvent(static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(event), 0);
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "hipStreamWaitEvent");
+}
+
+}  // extern "C"
+
+// ---- slot pool -----------------------------------------------------------
+
+struct nf4s_pool {
+  struct Slot {
+    void* ptr = nullptr;
+    hipEvent_t ready = nullptr;  // recorded on the copy stream after the copy
+    hipEvent_t free = nullptr;   // recorded on the compute stream after the last reader
+    int layer = -1;              // layer held (or being copied), -1 = none
+    bool held = false;           // between acquire and release
+    bool free_recorded = false;  // a free event exists to wait on
+    uint64_t last_use = 0;
+  };
+  struct Layer {
+    const void* src = nullptr;
+    size_t bytes = 0;
+  };
+  int n = 0;
+  size_t slot_bytes = 0;
+  hipStream_t copy = nullptr, compute = nullptr;
+  Slot slots[8];
+  std::vector<Layer> layers;
+  uint64_t tick = 0, copies = 0, bytes = 0;
+};
+
+namespace {
+
+int pool_find(const nf4s_pool* p, int layer) {
+  for (int i = 0; i < p->n; ++i)
+    if (p->slots[i].layer == layer) return i;
+  return -1;
+}
+
+int pool_copy_into(nf4s_pool* p, int layer, int* slot_out) {
+  if (layer < 0 || layer >= (int)p->layers.size() || !p->layers[layer].src)
+    return fail(NF4S_ESLOT, "layer %d was not registered", layer);
+  // victim: the least recently used slot that no reader holds
+  int v = -1;
+  for (int i = 0; i < p->n; ++i) {
+    const auto& s = p->slots[i];
+    if (s.held) continue;
+    if (v < 0 || s.last_use < p->slots[v].last_use) v = i;
+  }
+  if (v < 0) return fail(NF4S_ESLOT, "every slot is held; release one before prefetching");
+  auto& s = p->slots[v];
+  const auto& L = p->layers[layer];
+  int rc = layer_prefetch(s.ptr, p->slot_bytes, L.src, L.bytes, p->copy,
+                          s.free_recorded ? s.free : nullptr, s.ready);
+  if (rc) return rc;
+  s.layer = layer;
+  s.last_use = ++p->tick;
+  p->copies += 1;
+  p->bytes += L.bytes;
+  *slot_out = v;
+  return NF4S_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nf4s_pool_create(int n_slots, void* const* slots, size_t slot_bytes, void* copy_stream,
+                     void* compute_stream, nf4s_pool** out) {
+  if (!out || !slots) return fail(NF4S_EINVAL, "NULL argument");
+  if (n_slots < 2 || n_slots > 8) return fail(NF4S_ESLOT, "pool size %d outside [2, 8]", n_slots);
+  if (copy_stream == compute_stream)
+    return fail(NF4S_EINVAL, "copy and compute streams must differ (the copy overlaps compute)");
+  for (int i = 0; i < n_slots; ++i) {
+    int rc = check_ptr(slots[i], "slot", 256);
+    if (rc) return rc;
+  }
+  nf4s_pool* p = new nf4s_pool();
+  p->n = n_slots;
+  p->slot_bytes = slot_bytes;
+  p->copy = static_cast<hipStream_t>(copy_stream);
+  p->compute = static_cast<hipStream_t>(compute_stream);
+  for (int i = 0; i < n_slots; ++i) {
+    p->slots[i].ptr = slots[i];
+    hipError_t e1 = hipEventCreateWithFlags(&p->slots[i].ready, hipEventDisableTiming);
+    hipError_t e2 = hipEventCreateWithFlags(&p->slots[i].free, hipEventDisableTiming);
+    if (e1 != hipSuccess || e2 != hipSuccess) {
+      nf4s_pool_destroy(p);
+      return hip_fail(e1 != hipSuccess ? e1 : e2, "hipEventCreateWithFlags");
+    }
+  }
+  *out = p;
+  return NF4S_OK;
+}
+
+int nf4s_pool_destroy(nf4s_pool* p) {
+  if (!p) return NF4S_OK;
+  for (int i = 0; i < p->n; ++i) {
+    if (p->slots[i].ready) (void)hipEventDestroy(p->slots[i].ready);
+    if (p->slots[i].free) (void)hipEventDestroy(p->slots[i].free);
+  }
+  delete p;
+  return NF4S_OK;
+}
+
+int nf4s_pool_set_layer(nf4s_pool* p, int layer, const void* src, size_t bytes) {
+  if (!p || !src) return fail(NF4S_EINVAL, "NULL argument");
+  if (layer < 0 || layer > (1 << 20)) return fail(NF4S_ESLOT, "layer index %d", layer);
+  if (bytes == 0 || bytes > p->slot_bytes)
+    return fail(NF4S_ESLOT, "shard of %zu bytes does not fit a slot of %zu bytes", bytes, p->slot_bytes);
+  int rc = check_pinned(src);
+  if (rc) return rc;
+  if ((int)p->layers.size() <= layer) p->layers.resize(layer + 1);
+  p->layers[layer].src = src;
+  p->layers[layer].bytes = bytes;
+  // a re-registered layer is stale wherever it is resident
+  const int i = pool_find(p, layer);
+  if (i >= 0 && !p->slots[i].held) p->slots[i].layer = -1;
+  return NF4S_OK;
+}
+
+int nf4s_pool_prefetch(nf4s_pool* p, int layer) {
+  if (!p) return fail(NF4S_EINVAL, "pool is NULL");
+  if (pool_find(p, layer) >= 0) return NF4S_OK;
+  int slot;
+  return pool_copy_into(p, layer, &slot);
+}
+
+int nf4s_pool_acquire(nf4s_pool* p, int layer, void** slot_dev_out) {
+  if (!p || !slot_dev_out) return fail(NF4S_EINVAL, "NULL argument");
+  int i = pool_find(p, layer);
+  if (i < 0) {
+    int rc = pool_copy_into(p, layer, &i);
+    if (rc) return rc;
+  }
+  auto& s = p->slots[i];
+  if (s.held) return fail(NF4S_ESLOT, "layer %d is already acquired", layer);
+  hipError_t e = hipStreamWaitEvent(p->compute, s.ready, 0);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  s.held = true;
+  s.last_use = ++p->tick;
+  *slot_dev_out = s.ptr;
+  return NF4S_OK;
+}
+
+int nf4s_pool_release(nf4s_pool* p, int layer) {
+  if (!p) return fail(NF4S_EINVAL, "pool is NULL");
+  const int i = pool_find(p, layer);
+  if (i < 0 || !p->slots[i].held) return fail(NF4S_ESLOT, "layer %d is not acquired", layer);
+  auto& s = p->slots[i];
+  hipError_t e = hipEventRecord(s.free, p->compute);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  s.free_recorded = true;
+  s.held = false;
+  return NF4S_OK;
+}
+
+int nf4s_pool_stats(const nf4s_pool* p, uint64_t* copies, uint64_t* bytes) {
+  if (!p) return fail(NF4S_EINVAL, "pool is NULL");
+  if (copies) *copies = p->copies;
+  if (bytes) *bytes = p->bytes;
+  return NF4S_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,237 @@
+"""The streamed linear-stack training step over the C ABI.
+
+Orchestration only: every byte of arithmetic runs in libnf4stream's kernels and
+the slot bookkeeping lives in its native pool; this module decides the order of
+calls. torch provides device memory, pinned host memory and streams.
+
+A layer is the seven frozen projections q, k, v, o, gate, up, down of a
+llama-style decoder at their real shapes (gate walkthrough "Soup layer-streamed
+NF4 training measured", section 4.4 counts exactly their 2 forward + 2
+recompute + 2 dL/dx FLOPs per weight and token). A step is a forward sweep over
+layers 0..L-1 and a backward sweep over L-1..0 that recomputes each layer before
+differentiating it (English article "Fine-Tune 8B Models on 4GB VRAM",
+"The Principle of Layer Streaming": streaming forces checkpointing, so every
+layer is read twice per step; the forward prefetches i+1 and the backward
+i-1 on a dedicated stream while layer i computes).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+from . import (DTYPE_F32, OP_LINEAR_BWD, OP_LINEAR_FWD, OP_LORA_BWD, OP_QUANTIZE, lora_bwd,
+               lora_fwd, nf4_quantize_shard, nf4s_pool_acquire, nf4s_pool_create,
+               nf4s_pool_destroy, nf4s_pool_prefetch, nf4s_pool_release, nf4s_pool_set_layer,
+               nf4s_pool_stats, nf4s_tensor_layout, nf4s_workspace_bytes, streamed_linear_bwd,
+               streamed_linear_fwd)
+
+PROJ = ("q", "k", "v", "o", "gate", "up", "down")
+ALIGN = 256
+
+
+def _round_up(x, a=ALIGN):
+    return (x + a - 1) // a * a
+
+
+def stream_handle(s: torch.cuda.Stream) -> int:
+    return s.cuda_stream
+
+
+@dataclass
+class LayerLayout:
+    """Byte layout of one layer shard: the seven tensors back to back."""
+    shapes: dict
+    descs: dict = field(default_factory=dict)
+    nbytes: int = 0
+
+    def __post_init__(self):
+        base = 0
+        for p in PROJ:
+            d = nf4s_tensor_layout(*self.shapes[p], base)
+            self.descs[p] = d
+            base = d.end
+        self.nbytes = _round_up(base)
+
+
+class ShardSet:
+    """Layer shards quantised on the device and parked in pinned host memory.
+
+    weight_fn(layer, proj) returns the fp32 weight [n_out, k_in] on the device.
+    The quantiser runs once per tensor, offline (gate walkthrough, section 2.1).
+    """
+
+    def __init__(self, shapes, n_layers, weight_fn, device="cuda", pinned=True, keep_device=False):
+        self.layout = LayerLayout(shapes)
+        self.n_layers = n_layers
+        self.shapes = shapes
+        nb = self.layout.nbytes
+        ws_bytes = max(nf4s_workspace_bytes(OP_QUANTIZE, 0, *shapes[p]) for p in PROJ)
+        ws = torch.empty(_round_up(ws_bytes), dtype=torch.uint8, device=device)
+        status = torch.zeros(1, dtype=torch.int32, device=device)
+        stage = torch.empty(nb, dtype=torch.uint8, device=device)
+        s = torch.cuda.current_stream().cuda_stream
+        self.host = []
+        self.device = []
+        for i in range(n_layers):
+            for p in PROJ:
+                w = weight_fn(i, p).contiguous()
+                assert w.dtype == torch.float32 and tuple(w.shape) == tuple(shapes[p])
+                nf4_quantize_shard(w.data_ptr(), DTYPE_F32, *shapes[p], stage.data_ptr(),
+                                   self.layout.descs[p], status.data_ptr(), ws.data_ptr(),
+                                   ws.numel(), s)
+                del w
+            if pinned:
+                h = torch.empty(nb, dtype=torch.uint8, pin_memory=True)
+                h.copy_(stage)
+                self.host.append(h)
+            if keep_device:
+                self.device.append(stage.clone())
+        torch.cuda.synchronize()
+        if int(status.item()) != 0:
+            raise ValueError("non-finite weight in a quantised tensor")
+
+    def to_device(self):
+        """Resident copies of every layer shard (the resident-NF4 reference)."""
+        if not self.device:
+            self.device = [h.to("cuda") for h in self.host]
+        return self.device
+
+
+class LinearStack:
+    """Runs the linear-stack step streamed (slot pool) or resident.
+
+    lora[i][p] = (A fp32 [r, k_in], B fp32 [n_out, r]) device tensors for the
+    target projections. inputs(i, p) / grads(i, p) return bf16-bit tensors
+    (int16 storage) x [M, k_in] and dy [M, n_out].
+    """
+
+    def __init__(self, shards: ShardSet, M, targets, lora, r=16, alpha=32, n_slots=2,
+                 mode="streamed", keep_outputs=True):
+        assert mode in ("streamed", "resident")
+        self.sh = shards
+        self.M = M
+        self.targets = tuple(targets)
+        self.lora = lora
+        self.r = r
+        self.scale = alpha / r
+        self.mode = mode
+        self.keep = keep_outputs
+        dev = "cuda"
+        shapes = shards.shapes
+        self.compute = torch.cuda.Stream()
+        self.copy = torch.cuda.Stream()
+        ws = 0
+        for p in PROJ:
+            n, k = shapes[p]
+            ws = max(ws, nf4s_workspace_bytes(OP_LINEAR_FWD, M, n, k),
+                     nf4s_workspace_bytes(OP_LINEAR_BWD, M, n, k),
+                     nf4s_workspace_bytes(OP_LORA_BWD, M, n, k))
+        self.ws = torch.empty(_round_up(max(ws, ALIGN)), dtype=torch.uint8, device=dev)
+        # u = x . A^T per target, produced by the (re)computed forward of a layer
+        # and consumed by that layer's backward
+        self.u = {p: torch.empty((M, r), dtype=torch.float32, device=dev) for p in self.targets}
+        self.du = torch.empty((M, r), dtype=torch.float32, device=dev)
+        self.pool = None
+        if mode == "streamed":
+            nb = shards.layout.nbytes
+            self.slots = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(n_slots)]
+            self.pool = nf4s_pool_create([s.data_ptr() for s in self.slots], nb,
+                                         self.copy.cuda_stream, self.compute.cuda_stream)
+            for i, h in enumerate(shards.host):
+                nf4s_pool_set_layer(self.pool, i, h.data_ptr(), nb)
+        else:
+            self.resident = shards.to_device()
+        self.y = {}
+        self.dx = {}
+        self.grads = {}
+
+    def close(self):
+        if self.pool is not None:
+            torch.cuda.synchronize()
+            nf4s_pool_destroy(self.pool)
+            self.pool = None
+
+    def stats(self):
+        return nf4s_pool_stats(self.pool) if self.pool is not None else (0, 0)
+
+    # -- one layer -----------------------------------------------------------------
+    def _out(self, store, key, shape, dtype):
+        t = store.get(key)
+        if t is None:
+            t = torch.empty(shape, dtype=dtype, device="cuda")
+            store[key] = t
+        return t
+
+    def _layer_fwd(self, i, base, inputs, store_key):
+        s = self.compute.cuda_stream
+        shapes = self.sh.shapes
+        for p in PROJ:
+            n, k = shapes[p]
+            x = inputs(i, p)
+            y = self._out(self.y, (store_key(i), p), (self.M, n), torch.int16)
+            if p in self.targets:
+                A, B = self.lora[i][p]
+                u = self.u[p]
+                lora_fwd(x.data_ptr(), self.M, k, A.data_ptr(), self.r, u.data_ptr(), s)
+                streamed_linear_fwd(base, self.sh.layout.descs[p], x.data_ptr(), self.M, y.data_ptr(),
+                                    u.data_ptr(), B.data_ptr(), self.r, self.scale,
+                                    self.ws.data_ptr(), self.ws.numel(), s)
+            else:
+                streamed_linear_fwd(base, self.sh.layout.descs[p], x.data_ptr(), self.M, y.data_ptr(),
+                                    None, None, 0, 0.0, self.ws.data_ptr(), self.ws.numel(), s)
+
+    def _layer_bwd(self, i, base, inputs, grads):
+        s = self.compute.cuda_stream
+        shapes = self.sh.shapes
+        key = i if self.keep else 0
+        for p in PROJ:
+            n, k = shapes[p]
+            x = inputs(i, p)
+            dy = grads(i, p)
+            dx = self._out(self.dx, (key, p), (self.M, k), torch.int16)
+            if p in self.targets:
+                A, B = self.lora[i][p]
+                dA = self._out(self.grads, (i, p, "dA"), (self.r, k), torch.float32)
+                dB = self._out(self.grads, (i, p, "dB"), (n, self.r), torch.float32)
+                # u = x . A^T from this layer's recompute
+                lora_bwd(x.data_ptr(), dy.data_ptr(), self.u[p].data_ptr(), self.M, k, n, B.data_ptr(),
+                         self.r, self.scale, dA.data_ptr(), dB.data_ptr(), self.du.data_ptr(), 0,
+                         self.ws.data_ptr(), self.ws.numel(), s)
+                streamed_linear_bwd(base, self.sh.layout.descs[p], dy.data_ptr(), self.M, dx.data_ptr(),
+                                    self.du.data_ptr(), A.data_ptr(), self.r, self.ws.data_ptr(),
+                                    self.ws.numel(), s)
+            else:
+                streamed_linear_bwd(base, self.sh.layout.descs[p], dy.data_ptr(), self.M, dx.data_ptr(),
+                                    None, None, 0, self.ws.data_ptr(), self.ws.numel(), s)
+
+    # -- the step ------------------------------------------------------------------
+    def step(self, inputs, grads):
+        """Forward sweep then backward sweep with recompute. Kernels are queued
+        on the compute stream, copies on the copy stream; returns at once."""
+        L = self.sh.n_layers
+        fkey = (lambda i: ("f", i)) if self.keep else (lambda i: ("f", 0))
+        rkey = (lambda i: ("r", i)) if self.keep else (lambda i: ("f", 0))
+        self.compute.wait_stream(torch.cuda.current_stream())
+        for i in range(L):
+            base = self._acquire(i, nxt=i + 1 if i + 1 < L else None)
+            self._layer_fwd(i, base, inputs, fkey)
+            self._release(i)
+        for i in range(L - 1, -1, -1):
+            base = self._acquire(i, nxt=i - 1 if i > 0 else None)
+            self._layer_fwd(i, base, inputs, rkey)      # recompute
+            self._layer_bwd(i, base, inputs, grads)
+            self._release(i)
+        torch.cuda.current_stream().wait_stream(self.compute)
+
+    def _acquire(self, i, nxt):
+        if self.pool is None:
+            return self.resident[i].data_ptr()
+        base = nf4s_pool_acquire(self.pool, i)
+        if nxt is not None:
+            nf4s_pool_prefetch(self.pool, nxt)
+        return base
+
+    def _release(self, i):
+        if self.pool is not None:
+            nf4s_pool_release(self.pool, i)

@@ -1,0 +1,180 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, reports the same code tables and byte accounting as the
+oracle, and refuses bad arguments on the host before launching anything.
+
+The oracle is imported only to compare constants; no value flows from the
+library into the oracle.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import layer_streamed_nf4_amd as L
+from oracle import nf4, tables
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "nf4stream.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_library_exports_every_declared_function():
+    names = _header_functions()
+    assert len(names) >= 20
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTS)
+
+
+def test_tables_match_oracle_bit_for_bit():
+    c4, c8 = L.nf4_code_tables()
+    assert c4.view(np.uint32).tolist() == tables.nf4_table().view(np.uint32).tolist()
+    assert c8.view(np.uint32).tolist() == tables.dynamic_table().view(np.uint32).tolist()
+    assert L.nf4s_table_hash() == tables.table_hash(tables.nf4_table(), tables.dynamic_table())
+
+
+@pytest.mark.parametrize("shape", [(576, 576), (192, 576), (1536, 576), (576, 1536),
+                                   (4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336),
+                                   (27648, 5120), (8, 64)])
+def test_shard_bytes_match_oracle(shape):
+    assert L.nf4_shard_bytes(*shape) == nf4.payload_bytes(*shape)
+
+
+def test_tensor_layout_sections():
+    d = L.nf4s_tensor_layout(576, 576, 512)
+    assert d.off_packed == 512
+    for off in (d.off_q8, d.off_nested, d.off_offset, d.end):
+        assert off % 256 == 0
+    assert d.off_q8 >= d.off_packed + 576 * 576 // 2
+    assert d.off_nested >= d.off_q8 + 5184
+    assert d.off_offset >= d.off_nested + 21 * 4
+    assert d.end >= d.off_offset + 4
+    assert (d.method, d.blocksize, d.nested_block, d.double_quant) == (1, 64, 256, 1)
+
+
+@pytest.mark.parametrize("n_out,k_in", [(576, 100), (0, 64), (7, 64), (64, -64)])
+def test_layout_rejects_bad_shapes(n_out, k_in):
+    with pytest.raises(L.Nf4sError) as e:
+        L.nf4s_tensor_layout(n_out, k_in)
+    assert e.value.code == L.ESHAPE
+
+
+def test_layout_rejects_misaligned_base():
+    with pytest.raises(L.Nf4sError) as e:
+        L.nf4s_tensor_layout(64, 64, 100)
+    assert e.value.code == L.EALIGN
+
+
+def test_workspace_queries_depend_on_shape_only():
+    a = L.nf4s_workspace_bytes(L.OP_LINEAR_FWD, 512, 4096, 4096)
+    b = L.nf4s_workspace_bytes(L.OP_LINEAR_FWD, 512, 4096, 4096)
+    assert a == b and a % 4 == 0
+    assert L.nf4s_workspace_bytes(L.OP_QUANTIZE, 0, 576, 576) == 5184 * 4
+    with pytest.raises(L.Nf4sError) as e:
+        L.nf4s_workspace_bytes(99, 1, 64, 64)
+    assert e.value.code == L.EINVAL
+
+
+FAKE = 1 << 40  # a 256-byte aligned address that is never dereferenced
+
+
+def _desc(n=64, k=64):
+    return L.nf4s_tensor_layout(n, k)
+
+
+def test_descriptor_key_mismatches_are_refused():
+    d = _desc()
+    d.double_quant = 0      # the sharder/reader double-quant flag disagreement
+    with pytest.raises(L.Nf4sError) as e:
+        L.nf4_dequant(FAKE, d, FAKE)
+    assert e.value.code == L.EKEY
+    d = _desc()
+    d.blocksize = 32
+    with pytest.raises(L.Nf4sError) as e:
+        L.streamed_linear_fwd(FAKE, d, FAKE, 16, FAKE, None, None, 0, 0.0, None, 0)
+    assert e.value.code == L.EKEY
+    d = _desc()
+    d.table_hash ^= 1
+    with pytest.raises(L.Nf4sError) as e:
+        L.streamed_linear_bwd(FAKE, d, FAKE, 16, FAKE, None, None, 0, None, 0)
+    assert e.value.code == L.ETABLE
+    d = _desc()
+    d.off_q8 += 256
+    with pytest.raises(L.Nf4sError) as e:
+        L.nf4_dequant(FAKE, d, FAKE)
+    assert e.value.code == L.EKEY
+
+
+def test_pointer_and_argument_errors():
+    d = _desc()
+    with pytest.raises(L.Nf4sError) as e:
+        L.nf4_dequant(None, d, FAKE)
+    assert e.value.code == L.EINVAL
+    with pytest.raises(L.Nf4sError) as e:
+        L.nf4_dequant(FAKE + 16, d, FAKE)        # shard base must be 256-B aligned
+    assert e.value.code == L.EALIGN
+    with pytest.raises(L.Nf4sError) as e:
+        L.streamed_linear_fwd(FAKE, d, FAKE + 2, 16, FAKE, None, None, 0, 0.0, None, 0)
+    assert e.value.code == L.EALIGN
+    with pytest.raises(L.Nf4sError) as e:     # LoRA operands come together
+        L.streamed_linear_fwd(FAKE, d, FAKE, 16, FAKE, FAKE, None, 16, 2.0, None, 0)
+    assert e.value.code == L.EINVAL
+    with pytest.raises(L.Nf4sError) as e:     # rank out of range
+        L.streamed_linear_fwd(FAKE, d, FAKE, 16, FAKE, FAKE, FAKE, 65, 2.0, None, 0)
+    assert e.value.code == L.EINVAL
+    with pytest.raises(L.Nf4sError) as e:
+        L.streamed_linear_fwd(FAKE, d, FAKE, 0, FAKE, None, None, 0, 0.0, None, 0)
+    assert e.value.code == L.ESHAPE
+    with pytest.raises(L.Nf4sError) as e:     # non-finite LoRA scale
+        L.streamed_linear_fwd(FAKE, d, FAKE, 16, FAKE, FAKE, FAKE, 16, float("nan"), None, 0)
+    assert e.value.code == L.EINVAL
+    with pytest.raises(L.Nf4sError) as e:
+        L.nf4_quantize_shard(FAKE, 7, 64, 64, FAKE, d, None, FAKE, 1 << 20)
+    assert e.value.code == L.EINVAL
+    with pytest.raises(L.Nf4sError) as e:     # missing workspace
+        L.nf4_quantize_shard(FAKE, L.DTYPE_F32, 64, 64, FAKE, d, None, None, 0)
+    assert e.value.code == L.EWORKSPACE
+    with pytest.raises(L.Nf4sError) as e:     # descriptor for another shape
+        L.nf4_quantize_shard(FAKE, L.DTYPE_F32, 128, 64, FAKE, d, None, FAKE, 1 << 20)
+    assert e.value.code in (L.ESHAPE,)
+    with pytest.raises(L.Nf4sError) as e:
+        L.lora_fwd(FAKE, 16, 100, FAKE, 16, FAKE)
+    assert e.value.code == L.ESHAPE
+    with pytest.raises(L.Nf4sError) as e:
+        L.lora_bwd(FAKE, FAKE, FAKE, 16, 64, 64, FAKE, 16, 2.0, FAKE, FAKE, FAKE, 2, FAKE, 1 << 30)
+    assert e.value.code == L.EINVAL
+
+
+def test_linear_workspace_is_required_when_split():
+    d = L.nf4s_tensor_layout(4096, 4096)
+    need = L.nf4s_workspace_bytes(L.OP_LINEAR_FWD, 512, 4096, 4096)
+    assert need > 0                            # 64 output tiles: the contraction is split
+    with pytest.raises(L.Nf4sError) as e:
+        L.streamed_linear_fwd(FAKE, d, FAKE, 512, FAKE, None, None, 0, 0.0, FAKE, need - 4)
+    assert e.value.code == L.EWORKSPACE
+
+
+def test_prefetch_and_pool_argument_errors():
+    with pytest.raises(L.Nf4sError) as e:
+        L.layer_prefetch(FAKE, 1024, FAKE, 2048, None)      # shard larger than the slot
+    assert e.value.code == L.ESLOT
+    with pytest.raises(L.Nf4sError) as e:
+        L.layer_prefetch(FAKE + 8, 1024, FAKE, 512, None)
+    assert e.value.code == L.EALIGN
+    with pytest.raises(L.Nf4sError) as e:
+        L.nf4s_pool_create([FAKE], 1024, 1, 2)               # pool of one slot
+    assert e.value.code == L.ESLOT
+    with pytest.raises(L.Nf4sError) as e:
+        L.nf4s_pool_create([FAKE] * 9, 1024, 1, 2)
+    assert e.value.code == L.ESLOT
+    with pytest.raises(L.Nf4sError) as e:
+        L.nf4s_pool_create([FAKE, FAKE], 1024, 1, 1)         # copy stream == compute stream
+    assert e.value.code == L.EINVAL

@@ -192,7 +192,9 @@ __device__ __forceinline__ bf16x8_t f32x8_to_bf16(const float* v) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-template <bool BWD>
+// SPLIT selects the output path (fp32 partials vs bf16 result) at compile time,
+// so the two variants also carry distinct kernel names in profiles.
+template <bool BWD, bool SPLIT>
 __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_STRIDE];
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (row >= g.M) continue;
-        if (g.part != nullptr) {
+        if (SPLIT) {
           g.part[((int64_t)split * g.M + row) * g.Nc + col] = acc[i][j][r];
         } else {
           bf16x2_t h;
@@ -394,10 +396,15 @@ hipError_t launch_linear(bool backward, const QPtrs& q, int64_t n_out, int64_t k
   g.r = r;
   g.scale = scale;
   const dim3 grid((unsigned)((g.Nc + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)p.splits);
-  if (backward)
-    hipLaunchKernelGGL(k_gemm<true>, grid, dim3(THREADS), 0, s, g, host_tables());
+  const bool split = p.splits > 1;
+  if (backward && split)
+    hipLaunchKernelGGL((k_gemm<true, true>), grid, dim3(THREADS), 0, s, g, host_tables());
+  else if (backward)
+    hipLaunchKernelGGL((k_gemm<true, false>), grid, dim3(THREADS), 0, s, g, host_tables());
+  else if (split)
+    hipLaunchKernelGGL((k_gemm<false, true>), grid, dim3(THREADS), 0, s, g, host_tables());
   else
-    hipLaunchKernelGGL(k_gemm<false>, grid, dim3(THREADS), 0, s, g, host_tables());
+    hipLaunchKernelGGL((k_gemm<false, false>), grid, dim3(THREADS), 0, s, g, host_tables());
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const int64_t n = M * g.Nc;

@@ -107,7 +107,10 @@ class LinearStack:
     """
 
     def __init__(self, shards: ShardSet, M, targets, lora, r=16, alpha=32, n_slots=2,
-                 mode="streamed", keep_outputs=True):
+                 mode="streamed", keep_outputs=True, time_calls=None):
+        """time_calls: optional predicate (direction, n_out, k_in) -> bool; the
+        linear calls it accepts are bracketed by timing events on the compute
+        stream and collected in self.timed as (direction, n_out, k_in, start, end)."""
         assert mode in ("streamed", "resident")
         self.sh = shards
         self.M = M
@@ -145,6 +148,8 @@ class LinearStack:
         self.y = {}
         self.dx = {}
         self.grads = {}
+        self.time_calls = time_calls
+        self.timed = []
 
     def close(self):
         if self.pool is not None:
@@ -174,12 +179,16 @@ class LinearStack:
                 A, B = self.lora[i][p]
                 u = self.u[p]
                 lora_fwd(x.data_ptr(), self.M, k, A.data_ptr(), self.r, u.data_ptr(), s)
+                ev = self._tick("fwd", n, k)
                 streamed_linear_fwd(base, self.sh.layout.descs[p], x.data_ptr(), self.M, y.data_ptr(),
                                     u.data_ptr(), B.data_ptr(), self.r, self.scale,
                                     self.ws.data_ptr(), self.ws.numel(), s)
+                self._tock(ev)
             else:
+                ev = self._tick("fwd", n, k)
                 streamed_linear_fwd(base, self.sh.layout.descs[p], x.data_ptr(), self.M, y.data_ptr(),
                                     None, None, 0, 0.0, self.ws.data_ptr(), self.ws.numel(), s)
+                self._tock(ev)
 
     def _layer_bwd(self, i, base, inputs, grads):
         s = self.compute.cuda_stream
@@ -198,12 +207,29 @@ class LinearStack:
                 lora_bwd(x.data_ptr(), dy.data_ptr(), self.u[p].data_ptr(), self.M, k, n, B.data_ptr(),
                          self.r, self.scale, dA.data_ptr(), dB.data_ptr(), self.du.data_ptr(), 0,
                          self.ws.data_ptr(), self.ws.numel(), s)
+                ev = self._tick("bwd", n, k)
                 streamed_linear_bwd(base, self.sh.layout.descs[p], dy.data_ptr(), self.M, dx.data_ptr(),
                                     self.du.data_ptr(), A.data_ptr(), self.r, self.ws.data_ptr(),
                                     self.ws.numel(), s)
+                self._tock(ev)
             else:
+                ev = self._tick("bwd", n, k)
                 streamed_linear_bwd(base, self.sh.layout.descs[p], dy.data_ptr(), self.M, dx.data_ptr(),
                                     None, None, 0, self.ws.data_ptr(), self.ws.numel(), s)
+                self._tock(ev)
+
+    def _tick(self, direction, n, k):
+        if self.time_calls is None or not self.time_calls(direction, n, k):
+            return None
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(self.compute)
+        return (direction, n, k, start, end)
+
+    def _tock(self, ev):
+        if ev is not None:
+            ev[4].record(self.compute)
+            self.timed.append(ev)
 
     # -- the step ------------------------------------------------------------------
     def step(self, inputs, grads):

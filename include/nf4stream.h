@@ -132,13 +132,15 @@ uint64_t nf4s_table_hash(void);
 /*
  * Scratch bytes an operation needs for the given shape (0 means none; ws may
  * then be NULL). op: NF4S_OP_QUANTIZE (n_out, k_in), NF4S_OP_LINEAR_FWD and
- * NF4S_OP_LINEAR_BWD and NF4S_OP_LORA_BWD (M, n_out, k_in). The value depends
- * on shapes only.
+ * NF4S_OP_LINEAR_BWD, NF4S_OP_LORA_FWD and NF4S_OP_LORA_BWD (M, n_out, k_in;
+ * the adapter sizes cover any rank up to NF4S_MAX_RANK). The value depends on
+ * shapes only.
  */
 #define NF4S_OP_QUANTIZE 1
 #define NF4S_OP_LINEAR_FWD 2
 #define NF4S_OP_LINEAR_BWD 3
 #define NF4S_OP_LORA_BWD 4
+#define NF4S_OP_LORA_FWD 5
 int nf4s_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, size_t* bytes);
 
 /*
@@ -193,7 +195,8 @@ int streamed_linear_fwd(const void* shard_dev, const nf4s_tensor_desc* d, const 
  *   dy: bf16 [M, n_out];  dx: bf16 [M, k_in];
  *   lora_du: nullable fp32 [M, r] (= scale * dy.B, from lora_bwd);
  *   lora_A:  fp32 [r, k_in] (required iff lora_du is given).
- * Errors as streamed_linear_fwd.
+ * Errors as streamed_linear_fwd; also ESHAPE for n_out < 64. For both
+ * directions M * max(n_out, k_in) must stay below 2^31.
  */
 int streamed_linear_bwd(const void* shard_dev, const nf4s_tensor_desc* d, const uint16_t* dy,
                         int64_t M, uint16_t* dx, const float* lora_du, const float* lora_A,
@@ -201,11 +204,15 @@ int streamed_linear_bwd(const void* shard_dev, const nf4s_tensor_desc* d, const 
 
 /*
  * LoRA down-projection, u = x.A^T in fp32 ([G] s2.1, adapter on q/v):
- *   x: bf16 [M, k_in]; A: fp32 [r, k_in]; u_out: fp32 [M, r].
- * Deterministic (fixed reduction order). Errors: EINVAL, ESHAPE, EALIGN.
+ *   x: bf16 [M, k_in]; A: fp32 [r, k_in] (16-byte aligned); u_out: fp32 [M, r];
+ *   ws: nf4s_workspace_bytes(NF4S_OP_LORA_FWD, M, n_out, k_in) bytes (partials
+ *       of the split contraction).
+ * Runs on the matrix cores with A split into bf16 hi + lo parts (about 17
+ * significant bits kept), fp32 accumulation. Deterministic (fixed reduction
+ * order). Errors: EINVAL, ESHAPE, EALIGN, EWORKSPACE.
  */
 int lora_fwd(const uint16_t* x, int64_t M, int64_t k_in, const float* A, int r, float* u_out,
-             void* stream);
+             void* ws, size_t ws_bytes, void* stream);
 
 /*
  * LoRA gradients for L with upstream dy ([G] s2.2 check 2: non-zero in every
@@ -215,6 +222,8 @@ int lora_fwd(const uint16_t* x, int64_t M, int64_t k_in, const float* A, int r, 
  *   dA    (+)= du^T.x             fp32 [r, k_in]
  * x: bf16 [M, k_in]; dy: bf16 [M, n_out]; u: fp32 [M, r] (x.A^T);
  * B: fp32 [n_out, r]. accumulate = 0 overwrites dA/dB, 1 adds to them.
+ * The fp32 operand of each product (B, u, du) is split into bf16 hi + lo
+ * parts for the matrix cores; accumulation is fp32.
  * ws: nf4s_workspace_bytes(NF4S_OP_LORA_BWD, M, n_out, k_in) bytes.
  * Reductions run in a fixed order, so results are bit-reproducible.
  * Errors: EINVAL, ESHAPE, EALIGN, EWORKSPACE.

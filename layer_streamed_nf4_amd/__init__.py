@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libnf4stream.so")
 OK, EINVAL, ESHAPE, EALIGN, ETABLE, EKEY, ESLOT, ENOTPINNED, EHIP, EWORKSPACE = (
     0, -1, -2, -3, -4, -5, -6, -7, -8, -9)
 DTYPE_F32, DTYPE_BF16 = 0, 1
-OP_QUANTIZE, OP_LINEAR_FWD, OP_LINEAR_BWD, OP_LORA_BWD = 1, 2, 3, 4
+OP_QUANTIZE, OP_LINEAR_FWD, OP_LINEAR_BWD, OP_LORA_BWD, OP_LORA_FWD = 1, 2, 3, 4, 5
 METHOD_NF4 = 1
 
 EXPORTS = (
@@ -74,7 +74,7 @@ _SIG = {
                                            ctypes.c_int, ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "streamed_linear_bwd": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P, _P,
                                            ctypes.c_int, _P, ctypes.c_size_t, _P]),
-    "lora_fwd": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, _P, _P]),
+    "lora_fwd": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, _P, _P, ctypes.c_size_t, _P]),
     "lora_bwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, ctypes.c_float,
                                 _P, _P, _P, ctypes.c_int, _P, ctypes.c_size_t, _P]),
     "layer_prefetch": (ctypes.c_int, [_P, ctypes.c_size_t, _P, ctypes.c_size_t, _P, _P, _P]),
@@ -165,8 +165,8 @@ def streamed_linear_bwd(shard, desc, dy, M, dx, lora_du, lora_A, r, ws, ws_bytes
                                      ws_bytes, stream))
 
 
-def lora_fwd(x, M, k_in, A, r, u_out, stream=0):
-    _check(lib().lora_fwd(x, M, k_in, A, r, u_out, stream))
+def lora_fwd(x, M, k_in, A, r, u_out, ws, ws_bytes, stream=0):
+    _check(lib().lora_fwd(x, M, k_in, A, r, u_out, ws, ws_bytes, stream))
 
 
 def lora_bwd(x, dy, u, M, k_in, n_out, B, r, scale, dA, dB, du_out, accumulate, ws, ws_bytes,

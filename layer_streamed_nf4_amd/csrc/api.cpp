@@ -176,9 +176,13 @@ int nf4s_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, size_t*
       *bytes = plan_gemm(M, bwd ? k_in : n_out, bwd ? n_out : k_in).ws_bytes;
       return NF4S_OK;
     }
+    case NF4S_OP_LORA_FWD:
+      if (M <= 0) return fail(NF4S_ESHAPE, "M=%lld must be positive", (long long)M);
+      *bytes = lora_fwd_ws_bytes(M, k_in, NF4S_MAX_RANK);
+      return NF4S_OK;
     case NF4S_OP_LORA_BWD:
       if (M <= 0) return fail(NF4S_ESHAPE, "M=%lld must be positive", (long long)M);
-      *bytes = lora_bwd_ws_bytes(M, k_in, n_out);
+      *bytes = lora_bwd_ws_bytes(M, n_out, NF4S_MAX_RANK);
       return NF4S_OK;
     default:
       return fail(NF4S_EINVAL, "unknown op %d", op);
@@ -223,6 +227,13 @@ static int linear_common(bool bwd, const void* shard_dev, const nf4s_tensor_desc
   int rc;
   if ((rc = check_desc(d))) return rc;
   if (M <= 0 || M > (1ll << 24)) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
+  // the kernels address activations and packed weights with 32-bit offsets,
+  // and the backward's last contraction window needs n_out >= 64
+  const int64_t widest = d->n_out > d->k_in ? d->n_out : d->k_in;
+  if (M * widest >= (1ll << 31) || d->n_out * d->k_in >= (1ll << 33))
+    return fail(NF4S_ESHAPE, "M=%lld with a %lldx%lld weight exceeds 32-bit offsets", (long long)M,
+                (long long)d->n_out, (long long)d->k_in);
+  if (bwd && d->n_out < 64) return fail(NF4S_ESHAPE, "backward needs n_out >= 64 (got %lld)", (long long)d->n_out);
   if ((rc = check_ptr(shard_dev, "shard_dev", 256))) return rc;
   if ((rc = check_ptr(a, bwd ? "dy" : "x"))) return rc;
   if ((rc = check_ptr(out, bwd ? "dx" : "y"))) return rc;
@@ -254,14 +265,16 @@ int streamed_linear_bwd(const void* shard_dev, const nf4s_tensor_desc* d, const 
 }
 
 int lora_fwd(const uint16_t* x, int64_t M, int64_t k_in, const float* A, int r, float* u_out,
-             void* stream) {
+             void* ws, size_t ws_bytes, void* stream) {
   int rc;
   if (M <= 0 || k_in <= 0 || k_in % 64) return fail(NF4S_ESHAPE, "M=%lld k_in=%lld", (long long)M, (long long)k_in);
   if ((rc = check_rank(r))) return rc;
   if ((rc = check_ptr(x, "x"))) return rc;
-  if ((rc = check_ptr(A, "A", 4))) return rc;
+  if ((rc = check_ptr(A, "A"))) return rc;
   if ((rc = check_ptr(u_out, "u_out", 4))) return rc;
-  hipError_t e = launch_lora_fwd(x, M, k_in, A, r, u_out, static_cast<hipStream_t>(stream));
+  if (M * k_in >= (1ll << 31)) return fail(NF4S_ESHAPE, "M x k_in too large");
+  if ((rc = check_ws(ws, ws_bytes, lora_fwd_ws_bytes(M, k_in, r)))) return rc;
+  hipError_t e = launch_lora_fwd(x, M, k_in, A, r, u_out, ws, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NF4S_OK : hip_fail(e, "lora_fwd launch");
 }
 
@@ -281,7 +294,9 @@ int lora_bwd(const uint16_t* x, const uint16_t* dy, const float* u, int64_t M, i
   if ((rc = check_ptr(dA, "dA", 4))) return rc;
   if ((rc = check_ptr(dB, "dB", 4))) return rc;
   if ((rc = check_ptr(du_out, "du_out", 4))) return rc;
-  if ((rc = check_ws(ws, ws_bytes, lora_bwd_ws_bytes(M, k_in, n_out)))) return rc;
+  if ((rc = check_ws(ws, ws_bytes, lora_bwd_ws_bytes(M, n_out, r)))) return rc;
+  if (M * (n_out > k_in ? n_out : k_in) >= (1ll << 31) || M * r >= (1ll << 31))
+    return fail(NF4S_ESHAPE, "M x width too large for the adapter kernels");
   hipError_t e = launch_lora_bwd(x, dy, u, M, k_in, n_out, B, r, scale, dA, dB, du_out, accumulate,
                                  ws, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NF4S_OK : hip_fail(e, "lora_bwd launch");

@@ -57,11 +57,12 @@ hipError_t launch_linear(bool backward, const QPtrs& q, int64_t n_out, int64_t k
                          const float* lora_r, int r, float scale, void* ws, hipStream_t s);
 
 hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t k_in, const float* A, int r,
-                           float* u, hipStream_t s);
+                           float* u, void* ws, hipStream_t s);
+size_t lora_fwd_ws_bytes(int64_t M, int64_t k_in, int r);
 hipError_t launch_lora_bwd(const uint16_t* x, const uint16_t* dy, const float* u, int64_t M,
                            int64_t k_in, int64_t n_out, const float* B, int r, float scale,
                            float* dA, float* dB, float* du, int accumulate, void* ws,
                            hipStream_t s);
-size_t lora_bwd_ws_bytes(int64_t M, int64_t k_in, int64_t n_out);
+size_t lora_bwd_ws_bytes(int64_t M, int64_t n_out, int r);
 
 }  // namespace nf4s

@@ -12,20 +12,23 @@
 // as is (backward: B[k][n] = W'[k][n]). The packed codes are read from HBM once
 // per workgroup, decoded in registers with the block scale
 // a' = fp32(fp32(C8[q8]*nested) + offset) and W' = bf16_rne(fp32(C4[code]*a')),
-// and written to LDS as bf16 in the column-major-by-contraction layout the
-// matrix cores read; W' never goes back to HBM. The backward orientation is
-// transposed on the way into LDS for free: a thread decodes a 4x8 patch and
-// pairs values along the contraction when it packs bf16.
+// and written to LDS as bf16 in the contraction-major layout the matrix cores
+// read; W' never goes back to HBM. A packed byte holds two codes, and one LDS
+// read of a 256-entry table gives both of their NF4 levels. The backward
+// orientation is transposed on the way into LDS for free: a thread decodes a
+// 4x8 patch and pairs values along the contraction when it packs bf16.
 //
 // Tiling for gfx950: 256 threads (4 wave64), output tile 256x128, contraction
 // step 64 (exactly one NF4 block per weight row in the forward direction),
 // v_mfma_f32_32x32x16_bf16 with each wave owning a 128x64 sub-tile (4x2 MFMA
-// tiles, 128 fp32 accumulators per lane), double-buffered LDS (stage n+1 is
-// fetched into registers while stage n feeds the matrix cores). LDS rows are
-// padded to 144 B so the 16-byte fragment reads of 8 consecutive lanes cover
-// all 32 banks. When the output has too few tiles to occupy the chip, the
-// contraction is split; each split writes fp32 partials and a second kernel
-// sums them in split order (deterministic, no atomics).
+// tiles, 128 fp32 accumulators per lane), double-buffered LDS, and register
+// rings that keep the weight stream and the activation tile two steps ahead.
+// All per-lane addresses are loop-invariant 32-bit offsets from per-step
+// uniform bases, so a step spends its vector instructions on decoding only.
+// LDS rows are padded to 144 B so the 16-byte fragment reads of 8 consecutive
+// lanes cover all 32 banks. When the output has too few tiles to occupy the
+// chip, the contraction is split; each split writes fp32 partials and a second
+// kernel sums them in split order (deterministic, no atomics).
 #include "common.h"
 #include "device.h"
 
@@ -37,6 +40,8 @@ constexpr int BN = 128;
 constexpr int BK = 64;
 constexpr int LDS_STRIDE = 72;  // bf16 elements per LDS row (64 + 8 pad = 144 B)
 constexpr int THREADS = 256;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
 
 struct GemmArgs {
   const uint8_t* packed;
@@ -55,128 +60,212 @@ struct GemmArgs {
   float scale;
 };
 
-template <bool BWD>
-struct BRegs;
-
-// Forward: thread t owns weight row n0 + t/2, contraction half t%2 (32 codes).
-template <>
-struct BRegs<false> {
-  uint4 w;
-  uint32_t q;
-  float nest;
-  bool valid;
+// A contraction step covers [k0, k0 + 64). When the contraction length Kc is
+// not a multiple of 64 (backward with n_out % 64 != 0) the last step reads the
+// window [Kc - 64, Kc) instead, and the weight rows it has already consumed
+// (below its nominal start) decode to zero.
+struct Step {
+  int64_t win;  // first contraction index actually read
+  int64_t nom;  // nominal first index; rows below it are masked
 };
 
-// Backward: thread t owns weight rows k0 + 4*(t/16) + i (i < 4) and output
-// columns n0 + 8*(t%16) + j (j < 8): four packed words, four scales.
-template <>
-struct BRegs<true> {
-  uint32_t w[4];
-  uint32_t q[4];
-  float nest[4];
-  bool valid[4];
+// ---- activation tile (A): 8 rows x 16 bytes per thread -------------------
+struct ALanes {
+  uint32_t off[8];  // byte offsets of the thread's 8 chunks at contraction 0
 };
 
-__device__ __forceinline__ void load_a(const GemmArgs& g, int64_t m0, int64_t k0, uint4 (&ra)[8]) {
+__device__ __forceinline__ ALanes a_lanes(const GemmArgs& g, int64_t m0) {
   const int t = threadIdx.x;
-  const int c = t & 7;
-  const int64_t kk = k0 + c * 8;
+  ALanes L;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int64_t row = m0 + (t >> 3) + 32 * i;
-    if (row < g.M && kk < g.Kc)
-      ra[i] = *reinterpret_cast<const uint4*>(g.a + row * g.Kc + kk);
-    else
-      ra[i] = make_uint4(0, 0, 0, 0);
+    int64_t row = m0 + (t >> 3) + 32 * i;
+    row = row < g.M ? row : g.M - 1;  // rows past M feed output rows never stored
+    L.off[i] = (uint32_t)((row * g.Kc + (t & 7) * 8) * 2);
   }
+  return L;
 }
 
-__device__ __forceinline__ void store_a(uint16_t* As, const uint4 (&ra)[8]) {
+__device__ __forceinline__ void load_a(const GemmArgs& g, const ALanes& L, int64_t win,
+                                       u32x4 (&ra)[8]) {
+  const char* base = reinterpret_cast<const char*>(g.a + win);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ra[i] = *reinterpret_cast<const u32x4*>(base + L.off[i]);
+}
+
+__device__ __forceinline__ void store_a(uint16_t* As, const u32x4 (&ra)[8]) {
   const int t = threadIdx.x;
   const int c = t & 7;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = (t >> 3) + 32 * i;
-    *reinterpret_cast<uint4*>(As + row * LDS_STRIDE + c * 8) = ra[i];
+    *reinterpret_cast<u32x4*>(As + row * LDS_STRIDE + c * 8) = ra[i];
   }
 }
 
-__device__ __forceinline__ void load_b(const GemmArgs& g, int64_t n0, int64_t k0, BRegs<false>& rb) {
+// ---- weight tile (B) ------------------------------------------------------
+template <bool BWD>
+struct WLanes;
+template <bool BWD>
+struct BRegs;
+
+// Forward: thread t owns weight row n0 + t/2 and contraction half t%2 (32 codes).
+template <>
+struct WLanes<false> {
+  uint32_t woff;  // byte offset of the thread's 16 packed bytes at contraction 0
+  uint32_t blk0;  // 64-block index at contraction 0
+  bool valid;     // row < n_out
+};
+template <>
+struct BRegs<false> {
+  u32x4 w;
+  uint32_t q;
+  float nest;
+};
+
+__device__ __forceinline__ WLanes<false> w_lanes_fwd(const GemmArgs& g, int64_t n0) {
   const int t = threadIdx.x;
-  const int64_t n = n0 + (t >> 1);
-  const int half = t & 1;
-  rb.valid = n < g.n_out;
-  if (rb.valid) {
-    const int64_t e = n * g.k_in + k0 + half * 32;
-    rb.w = *reinterpret_cast<const uint4*>(g.packed + e / 2);
-    const int64_t blk = (n * g.k_in + k0) / 64;
-    rb.q = g.q8[blk];
-    rb.nest = g.nested[blk >> 8];
-  }
+  WLanes<false> L;
+  int64_t n = n0 + (t >> 1);
+  L.valid = n < g.n_out;
+  n = L.valid ? n : g.n_out - 1;
+  L.woff = (uint32_t)(n * (g.k_in / 2) + (t & 1) * 16);
+  L.blk0 = (uint32_t)(n * (g.k_in / 64));
+  return L;
 }
 
-__device__ __forceinline__ void store_b(uint16_t* Bs, const BRegs<false>& rb, float off,
-                                        const float* c4, const float* c8) {
-  const int t = threadIdx.x;
-  const int row = t >> 1;
-  const int half = t & 1;
-  uint4* dst = reinterpret_cast<uint4*>(Bs + row * LDS_STRIDE + half * 32);
-  if (!rb.valid) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dst[j] = make_uint4(0, 0, 0, 0);
-    return;
-  }
-  const float a = decode_scale(c8[rb.q], rb.nest, off);
-  const uint32_t words[4] = {rb.w.x, rb.w.y, rb.w.z, rb.w.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t o[4];
-    dequant_word(words[j], a, c4, o);
-    dst[j] = make_uint4(o[0], o[1], o[2], o[3]);
-  }
+__device__ __forceinline__ void load_b(const GemmArgs& g, const WLanes<false>& L, Step s,
+                                       BRegs<false>& rb) {
+  rb.w = *reinterpret_cast<const u32x4*>(g.packed + s.win / 2 + L.woff);
+  const uint32_t blk = L.blk0 + (uint32_t)(s.win / 64);
+  rb.q = g.q8[blk];
+  rb.nest = g.nested[blk >> 8];
 }
 
-__device__ __forceinline__ void load_b(const GemmArgs& g, int64_t n0, int64_t k0, BRegs<true>& rb) {
+// Backward: thread t owns weight rows k0 + 4*(t/16) + i (i < 4) and output
+// columns n0 + 8*(t%16) + j (j < 8): four packed words, four 8-bit scale
+// codes packed in one register, four nested scales, a 4-bit validity mask.
+template <>
+struct WLanes<true> {
+  uint32_t woff[4];  // byte offsets of the 4 packed words at contraction 0
+  uint32_t blk0[4];  // 64-block indices at contraction 0
+  bool cvalid;       // columns < k_in
+};
+template <>
+struct BRegs<true> {
+  uint32_t w[4];
+  uint32_t q;
+  float nest[4];
+  uint32_t vmask;
+};
+
+__device__ __forceinline__ WLanes<true> w_lanes_bwd(const GemmArgs& g, int64_t n0) {
   const int t = threadIdx.x;
-  const int64_t col = n0 + 8 * (t & 15);
+  WLanes<true> L;
+  int64_t col = n0 + 8 * (t & 15);
+  L.cvalid = col < g.k_in;
+  col = L.cvalid ? col : g.k_in - 8;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t row = k0 + 4 * (t >> 4) + i;
-    rb.valid[i] = row < g.n_out && col < g.k_in;
-    if (rb.valid[i]) {
-      const int64_t e = row * g.k_in + col;
-      rb.w[i] = *reinterpret_cast<const uint32_t*>(g.packed + e / 2);
-      const int64_t blk = e / 64;
-      rb.q[i] = g.q8[blk];
-      rb.nest[i] = g.nested[blk >> 8];
-    }
+    const int64_t row = 4 * (t >> 4) + i;  // relative to the step's window
+    L.woff[i] = (uint32_t)((row * g.k_in + col) / 2);
+    L.blk0[i] = (uint32_t)((row * g.k_in + col) / 64);
+  }
+  return L;
+}
+
+__device__ __forceinline__ void load_b(const GemmArgs& g, const WLanes<true>& L, Step s,
+                                       BRegs<true>& rb) {
+  const int t = threadIdx.x;
+  const uint8_t* base = g.packed + s.win * (g.k_in / 2);
+  const uint32_t bstep = (uint32_t)(s.win * (g.k_in / 64));
+  rb.q = 0;
+  rb.vmask = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rb.w[i] = *reinterpret_cast<const uint32_t*>(base + L.woff[i]);
+    const uint32_t blk = bstep + L.blk0[i];
+    rb.q |= (uint32_t)g.q8[blk] << (8 * i);
+    rb.nest[i] = g.nested[blk >> 8];
+    const int64_t row = s.win + 4 * (t >> 4) + i;
+    rb.vmask |= (L.cvalid && row >= s.nom) ? (1u << i) : 0u;
   }
 }
 
-__device__ __forceinline__ void store_b(uint16_t* Bs, const BRegs<true>& rb, float off,
-                                        const float* c4, const float* c8) {
+// ---- decoding -------------------------------------------------------------
+// ptab[b] = (C4[b >> 4], C4[b & 15]): both levels of a packed byte, the even
+// element (high nibble) first.
+__device__ __forceinline__ float2 pair_of(const float2* ptab, uint32_t word, int byte) {
+  return ptab[(word >> (8 * byte)) & 0xFFu];
+}
+
+__device__ __forceinline__ float stage_scale(const BRegs<false>& rb, bool valid, float off,
+                                             const float* c8) {
+  return valid ? decode_scale(c8[rb.q], rb.nest, off) : 0.0f;
+}
+
+// Quarter Q of a forward stage: packed word Q (8 codes) -> 8 bf16 in LDS.
+template <int Q>
+__device__ __forceinline__ void store_b_quarter(uint16_t* Bs, const BRegs<false>& rb, float a,
+                                                const float2* ptab) {
   const int t = threadIdx.x;
-  float v[4][8];
+  const uint32_t word = rb.w[Q];
+  u32x4 o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (rb.valid[i]) {
-      const float a = decode_scale(c8[rb.q[i]], rb.nest[i], off);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = __fmul_rn(c4[nib(rb.w[i], j)], a);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
-    }
+  for (int p = 0; p < 4; ++p) {
+    const float2 c = pair_of(ptab, word, p);
+    o[p] = pack_bf16x2(__fmul_rn(c.x, a), __fmul_rn(c.y, a));
   }
-  const int cb = 8 * (t & 15);
+  *reinterpret_cast<u32x4*>(Bs + (t >> 1) * LDS_STRIDE + (t & 1) * 32 + Q * 8) = o;
+}
+
+struct Scales4 {
+  float a[4];
+};
+
+__device__ __forceinline__ Scales4 stage_scale(const BRegs<true>& rb, bool, float off,
+                                               const float* c8) {
+  Scales4 s;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    s.a[i] = ((rb.vmask >> i) & 1u) ? decode_scale(c8[(rb.q >> (8 * i)) & 0xFFu], rb.nest[i], off)
+                                    : 0.0f;
+  return s;
+}
+
+// Quarter Q of a backward stage: output columns 2Q and 2Q+1 of the thread's
+// 4x8 patch (byte Q of each row's word), each written as 4 consecutive
+// contraction values -- the transpose into the matrix-core layout happens here,
+// in the bf16 pairing.
+template <int Q>
+__device__ __forceinline__ void store_b_quarter(uint16_t* Bs, const BRegs<true>& rb,
+                                                const Scales4& sc, const float2* ptab) {
+  const int t = threadIdx.x;
+  const int cb = 8 * (t & 15) + 2 * Q;
   const int rbase = 4 * (t >> 4);
+  float v0[4], v1[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint2 pk;
-    pk.x = pack_bf16x2(v[0][j], v[1][j]);
-    pk.y = pack_bf16x2(v[2][j], v[3][j]);
-    *reinterpret_cast<uint2*>(Bs + (cb + j) * LDS_STRIDE + rbase) = pk;
+  for (int i = 0; i < 4; ++i) {
+    const float2 c = pair_of(ptab, rb.w[i], Q);
+    v0[i] = __fmul_rn(c.x, sc.a[i]);
+    v1[i] = __fmul_rn(c.y, sc.a[i]);
   }
+  uint2 p0, p1;
+  p0.x = pack_bf16x2(v0[0], v0[1]);
+  p0.y = pack_bf16x2(v0[2], v0[3]);
+  p1.x = pack_bf16x2(v1[0], v1[1]);
+  p1.y = pack_bf16x2(v1[2], v1[3]);
+  *reinterpret_cast<uint2*>(Bs + cb * LDS_STRIDE + rbase) = p0;
+  *reinterpret_cast<uint2*>(Bs + (cb + 1) * LDS_STRIDE + rbase) = p1;
+}
+
+template <typename R, typename S>
+__device__ __forceinline__ void store_b_all(uint16_t* Bs, const R& rb, const S& sc,
+                                            const float2* ptab) {
+  store_b_quarter<0>(Bs, rb, sc, ptab);
+  store_b_quarter<1>(Bs, rb, sc, ptab);
+  store_b_quarter<2>(Bs, rb, sc, ptab);
+  store_b_quarter<3>(Bs, rb, sc, ptab);
 }
 
 __device__ __forceinline__ bf16x8_t lds_frag(const uint16_t* base, int row, int kofs) {
@@ -184,12 +273,19 @@ __device__ __forceinline__ bf16x8_t lds_frag(const uint16_t* base, int row, int 
 }
 
 __device__ __forceinline__ bf16x8_t f32x8_to_bf16(const float* v) {
-  uint4 u;
-  u.x = pack_bf16x2(v[0], v[1]);
-  u.y = pack_bf16x2(v[2], v[3]);
-  u.z = pack_bf16x2(v[4], v[5]);
-  u.w = pack_bf16x2(v[6], v[7]);
+  u32x4 u;
+  u[0] = pack_bf16x2(v[0], v[1]);
+  u[1] = pack_bf16x2(v[2], v[3]);
+  u[2] = pack_bf16x2(v[4], v[5]);
+  u[3] = pack_bf16x2(v[6], v[7]);
   return __builtin_bit_cast(bf16x8_t, u);
+}
+
+__device__ __forceinline__ WLanes<false> w_lanes(const GemmArgs& g, int64_t n0, WLanes<false>*) {
+  return w_lanes_fwd(g, n0);
+}
+__device__ __forceinline__ WLanes<true> w_lanes(const GemmArgs& g, int64_t n0, WLanes<true>*) {
+  return w_lanes_bwd(g, n0);
 }
 
 // SPLIT selects the output path (fp32 partials vs bf16 result) at compile time,
@@ -198,11 +294,11 @@ template <bool BWD, bool SPLIT>
 __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_STRIDE];
-  __shared__ float s_c4[16];
+  __shared__ float2 s_pair[256];
   __shared__ float s_c8[256];
 
   const int t = threadIdx.x;
-  if (t < 16) s_c4[t] = tab.c4[t];
+  s_pair[t] = make_float2(tab.c4[t >> 4], tab.c4[t & 15]);
   s_c8[t] = tab.c8[t];
 
   const int64_t n0 = (int64_t)blockIdx.x * BN;
@@ -228,43 +324,98 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  uint4 ra[8];
-  BRegs<BWD> rb;
-  load_a(g, m0, kb, ra);
-  load_b(g, n0, kb, rb);
+  const ALanes al = a_lanes(g, m0);
+  const WLanes<BWD> wl = w_lanes(g, n0, static_cast<WLanes<BWD>*>(nullptr));
+  bool fwd_valid = true;
+  if constexpr (!BWD) fwd_valid = wl.valid;
+
+  // step kt (clamped to the last one for prefetches past the end)
+  auto step_of = [&](int kt) {
+    const int k = kt < nk ? kt : nk - 1;
+    Step s;
+    s.nom = kb + (int64_t)k * BK;
+    s.win = s.nom + BK <= g.Kc ? s.nom : g.Kc - BK;
+    return s;
+  };
+
+  // Software pipeline over contraction steps. Weight stage k lives in register
+  // slot k%4 and activation stage k in slot k%2; both are fetched two steps
+  // before use. Step kt feeds the matrix cores from LDS stage kt%2 while it
+  // decodes weight stage kt+1 into the other LDS stage (a quarter before each
+  // group of 8 MFMAs), fetches weight stage kt+3 and activation stage kt+2, and
+  // finally stores activation stage kt+1.
+  BRegs<BWD> rb0, rb1, rb2, rb3;
+  u32x4 ra0[8], ra1[8];
+  load_b(g, wl, step_of(0), rb0);
+  load_b(g, wl, step_of(1), rb1);
+  load_b(g, wl, step_of(2), rb2);
+  load_a(g, al, step_of(0).win, ra0);
+  load_a(g, al, step_of(1).win, ra1);
   __syncthreads();  // tables in LDS
-  store_a(As[0], ra);
-  store_b(Bs[0], rb, off, s_c4, s_c8);
+  store_a(As[0], ra0);
+  store_b_all(Bs[0], rb0, stage_scale(rb0, fwd_valid, off, s_c8), s_pair);
   __syncthreads();
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load_a(g, m0, kb + (int64_t)(kt + 1) * BK, ra);
-      load_b(g, n0, kb + (int64_t)(kt + 1) * BK, rb);
-    }
+  // MFMAs of one step from LDS stage st, fragments double-buffered across the
+  // four 16-wide sub-steps, with one quarter of the next weight stage decoded
+  // into the other LDS stage before each group of 8 MFMAs.
+  auto mma_and_decode = [&](int st, const BRegs<BWD>& w_deq) {
+    const auto sc = stage_scale(w_deq, fwd_valid, off, s_c8);
     const uint16_t* as = As[st];
     const uint16_t* bs = Bs[st];
+    uint16_t* bnext = Bs[st ^ 1];
+    bf16x8_t fa[2][4], fb[2][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[0][i] = lds_frag(as, wm * 128 + i * 32 + lrow, lk);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[0][j] = lds_frag(bs, wn * 64 + j * 32 + lrow, lk);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t fa[4], fb[2];
+      const int cur = kk & 1;
+      if (kk + 1 < BK / 16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = lds_frag(as, wm * 128 + i * 32 + lrow, kk * 16 + lk);
+        for (int i = 0; i < 4; ++i)
+          fa[cur ^ 1][i] = lds_frag(as, wm * 128 + i * 32 + lrow, (kk + 1) * 16 + lk);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = lds_frag(bs, wn * 64 + j * 32 + lrow, kk * 16 + lk);
+        for (int j = 0; j < 2; ++j)
+          fb[cur ^ 1][j] = lds_frag(bs, wn * 64 + j * 32 + lrow, (kk + 1) * 16 + lk);
+      }
+      if (kk == 0) store_b_quarter<0>(bnext, w_deq, sc, s_pair);
+      if (kk == 1) store_b_quarter<1>(bnext, w_deq, sc, s_pair);
+      if (kk == 2) store_b_quarter<2>(bnext, w_deq, sc, s_pair);
+      if (kk == 3) store_b_quarter<3>(bnext, w_deq, sc, s_pair);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      store_a(As[st ^ 1], ra);
-      store_b(Bs[st ^ 1], rb, off, s_c4, s_c8);
-    }
-    __syncthreads();
+  };
+
+  // One step over named ring registers (a macro, so nothing is address-taken
+  // and every ring slot stays in VGPRs).
+#define NF4S_GEMM_STEP(KT, WL, WD, AL, AS)            \
+  do {                                                \
+    const int kt_ = (KT);                             \
+    load_b(g, wl, step_of(kt_ + 3), WL);              \
+    load_a(g, al, step_of(kt_ + 2).win, AL);          \
+    __builtin_amdgcn_sched_barrier(0);                \
+    mma_and_decode(kt_ & 1, WD);                      \
+    store_a(As[(kt_ & 1) ^ 1], AS);                   \
+    __syncthreads();                                  \
+  } while (0)
+
+  const int nk4 = nk - nk % 4;
+  for (int kt = 0; kt < nk4; kt += 4) {
+    NF4S_GEMM_STEP(kt, rb3, rb1, ra0, ra1);
+    NF4S_GEMM_STEP(kt + 1, rb0, rb2, ra1, ra0);
+    NF4S_GEMM_STEP(kt + 2, rb1, rb3, ra0, ra1);
+    NF4S_GEMM_STEP(kt + 3, rb2, rb0, ra1, ra0);
   }
+  if (nk4 < nk) NF4S_GEMM_STEP(nk4, rb3, rb1, ra0, ra1);
+  if (nk4 + 1 < nk) NF4S_GEMM_STEP(nk4 + 1, rb0, rb2, ra1, ra0);
+  if (nk4 + 2 < nk) NF4S_GEMM_STEP(nk4 + 2, rb1, rb3, ra0, ra1);
+#undef NF4S_GEMM_STEP
 
   // LoRA term, contracted on the matrix cores in chunks of 16 over the rank:
   // forward  + u[m, :] . (s * B[n, :]),  backward + du[m, :] . A[:, n].
@@ -319,9 +470,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
         if (SPLIT) {
           g.part[((int64_t)split * g.M + row) * g.Nc + col] = acc[i][j][r];
         } else {
-          bf16x2_t h;
-          h[0] = (__bf16)acc[i][j][r];
-          g.out[row * g.Nc + col] = __builtin_bit_cast(uint32_t, h) & 0xFFFFu;
+          g.out[row * g.Nc + col] = (uint16_t)(pack_bf16x2(acc[i][j][r], 0.0f) & 0xFFFFu);
         }
       }
     }
@@ -347,9 +496,7 @@ __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ par
     for (int64_t e = i; e < n; ++e) {
       float s = part[e];
       for (int p = 1; p < splits; ++p) s += part[(int64_t)p * n + e];
-      bf16x2_t h;
-      h[0] = (__bf16)s;
-      out[e] = __builtin_bit_cast(uint32_t, h) & 0xFFFFu;
+      out[e] = (uint16_t)(pack_bf16x2(s, 0.0f) & 0xFFFFu);
     }
   }
 }

@@ -1,199 +1,275 @@
-// Rank-r LoRA adapter path in fp32, every reduction in a fixed order.
+// Rank-r LoRA adapter path on the matrix cores, every reduction in a fixed order.
 //
 // Gate walkthrough ("Soup layer-streamed NF4 training measured") section 2.1:
 // LoRA r16 on q_proj and v_proj over the frozen NF4 base; section 2.2 check 2:
 // the adapter gradients are non-zero in every layer; section 2.5: with B = 0
 // the gradient of A vanishes structurally.
 //
-//   lora_fwd: u  = x . A^T                     [M, r]   (row dots over k_in)
-//   lora_bwd: du = scale * dy . B              [M, r]   (row dots over n_out)
-//             dB = scale * dy^T . u            [n_out, r] (column dots over M)
-//             dA = du^T . x                    [r, k_in]  (column dots over M)
+//   lora_fwd: u  = x . A^T            [M, r]     contraction over k_in
+//   lora_bwd: du = scale * dy . B     [M, r]     contraction over n_out
+//             dB = scale * dy^T . u   [n_out, r] contraction over M
+//             dA = du^T . x           [r, k_in]  contraction over M
 //
-// Row dots: one wave per 4 rows, lanes stride the long dimension 8 elements at
-// a time, the 64 partial sums are folded by a fixed butterfly. Column dots: a
-// thread owns two adjacent columns and all r, the M rows are split over the
-// grid's y dimension, and the split partials are summed in split order by a
-// second kernel.
+// Every product pairs a bf16 activation (x or dy, exact) with an fp32 adapter
+// quantity F (A, B, u or du). F is split as F = hi + lo with hi = bf16(F) and
+// lo = bf16(F - hi), and the 16 rank columns of hi and the 16 of lo form the
+// 32 rows of one v_mfma_f32_32x32x16_bf16 operand; the two partial products
+// land in accumulator rows j and j + 16 of the same lane and are added there.
+// The split keeps about 17 bits of F, so the result carries fp32-level error
+// while running on the matrix cores.
+//
+// Row kernel (u, du): one workgroup per 32 rows of the output and 512-wide
+// chunk of the long contraction, its 4 waves take interleaved 16-wide slices,
+// their tiles are summed through LDS in wave order, and a second kernel adds
+// the chunks' partials in chunk order. Column kernel (dA, dB): one
+// workgroup per 32 output columns, its 8 waves take eighths of M, summed the
+// same way.
 #include "common.h"
 #include "device.h"
 
 namespace nf4s {
 namespace {
 
-constexpr int RCH = 16;        // rank handled per pass
-constexpr int ROWS = 4;        // rows per wave in the row-dot kernel
-constexpr int MSPLIT_ROWS = 32;  // rows per split in the column-dot kernel
+constexpr int RCH = 16;  // rank columns per pass
 
-__device__ __forceinline__ void bf16x8_to_f32(uint4 u, float* v) {
-  v[0] = __uint_as_float(u.x << 16);
-  v[1] = __uint_as_float(u.x & 0xFFFF0000u);
-  v[2] = __uint_as_float(u.y << 16);
-  v[3] = __uint_as_float(u.y & 0xFFFF0000u);
-  v[4] = __uint_as_float(u.z << 16);
-  v[5] = __uint_as_float(u.z & 0xFFFF0000u);
-  v[6] = __uint_as_float(u.w << 16);
-  v[7] = __uint_as_float(u.w & 0xFFFF0000u);
+__device__ __forceinline__ uint32_t bf16_bits(float v) {
+  return pack_bf16x2(v, 0.0f) & 0xFFFFu;
 }
 
-// out[m, r0 + j] = scale * sum_k X[m, k] * W(j, k), j < 16, where W(j, k) is
-// Wm[(r0 + j) * K + k] (TRANS_W = false, A[r, K]) or Wm[k * r + r0 + j]
-// (TRANS_W = true, B[K, r]).
-template <bool TRANS_W>
-__global__ __launch_bounds__(256) void k_rowdot(const uint16_t* __restrict__ X, int64_t M,
-                                                int64_t K, const float* __restrict__ Wm, int r,
-                                                float scale, float* __restrict__ out) {
+// hi part (first) or lo part (second) of v, as bf16 bits
+__device__ __forceinline__ uint32_t split_part(float v, bool lo) {
+  const uint32_t h = bf16_bits(v);
+  if (!lo) return h;
+  return bf16_bits(v - __uint_as_float(h << 16));
+}
+
+__device__ __forceinline__ bf16x8_t frag_from_f32(const float* v, bool lo) {
+  uint4 u;
+  u.x = split_part(v[0], lo) | (split_part(v[1], lo) << 16);
+  u.y = split_part(v[2], lo) | (split_part(v[3], lo) << 16);
+  u.z = split_part(v[4], lo) | (split_part(v[5], lo) << 16);
+  u.w = split_part(v[6], lo) | (split_part(v[7], lo) << 16);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+constexpr int ROW_WAVES = 4;
+constexpr int UNR = 8;                        // 16-wide slices per wave, loads issued together
+constexpr int ROW_CHUNK = ROW_WAVES * UNR * 16;  // contraction handled by one workgroup (512)
+
+// Partial row dots: part[ks, m, r0 + j] = sum over k in chunk ks of
+// X[m, k] * F(r0 + j, k), for one 32-row tile of m. F(j, k) = Fm[j * K + k]
+// (TRANS_F = false: A [r, K]) or Fm[k * r + j] (TRANS_F = true: B [K, r]).
+// MFMA view: C[rho, m] = sum_k F'[rho, k] X[m, k], rho < 16 the hi halves,
+// rho >= 16 the lo halves. Wave w takes slices w, w + 4, ... of the chunk; the
+// UNR loads of a wave are issued before its MFMAs; the 4 wave tiles are summed
+// through LDS in wave order.
+template <bool TRANS_F>
+__global__ __launch_bounds__(ROW_WAVES * 64) void k_lora_rows(const uint16_t* __restrict__ X,
+                                                               int64_t M, int64_t K,
+                                                               const float* __restrict__ Fm, int r,
+                                                               float* __restrict__ part) {
+  __shared__ float s_part[ROW_WAVES][64][8];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int64_t mbase = ((int64_t)blockIdx.x * 4 + wave) * ROWS;
-  const int r0 = blockIdx.y * RCH;
-  float acc[ROWS][RCH];
+  const int64_t m0 = (int64_t)blockIdx.x * 32;
+  const int ks = blockIdx.y;
+  const int r0 = blockIdx.z * RCH;
+  const int rho = lane & 31;
+  const bool lo = rho >= 16;
+  const int j = r0 + (rho & 15);
+  const int jc = j < r ? j : r - 1;
+  const int kq = (lane >> 5) * 8;
+  const int64_t m = m0 + rho;
+  const int64_t mc = m < M ? m : M - 1;  // rows past M feed unstored columns
+  float f[UNR][8];
+  uint4 xv[UNR];
 #pragma unroll
-  for (int i = 0; i < ROWS; ++i)
+  for (int u = 0; u < UNR; ++u) {
+    const int64_t k = (int64_t)ks * ROW_CHUNK + (int64_t)(u * ROW_WAVES + wave) * 16 + kq;
+    const bool ok = k < K;  // K % 8 == 0, so k < K covers all 8 elements
+    const int64_t kc = ok ? k : K - 8;
+    if (TRANS_F) {
 #pragma unroll
-    for (int j = 0; j < RCH; ++j) acc[i][j] = 0.0f;
-
-  for (int64_t k = (int64_t)lane * 8; k < K; k += 512) {
-    float w[RCH][8];
-#pragma unroll
-    for (int j = 0; j < RCH; ++j) {
-      const int rr = r0 + j;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        w[j][e] = (rr < r) ? (TRANS_W ? Wm[(k + e) * r + rr] : Wm[(int64_t)rr * K + k + e]) : 0.0f;
+      for (int e = 0; e < 8; ++e) f[u][e] = Fm[(kc + e) * r + jc];
+    } else {
+      const float4 a = *reinterpret_cast<const float4*>(Fm + (int64_t)jc * K + kc);
+      const float4 b = *reinterpret_cast<const float4*>(Fm + (int64_t)jc * K + kc + 4);
+      f[u][0] = a.x; f[u][1] = a.y; f[u][2] = a.z; f[u][3] = a.w;
+      f[u][4] = b.x; f[u][5] = b.y; f[u][6] = b.z; f[u][7] = b.w;
     }
+    if (!(ok && j < r)) {
 #pragma unroll
-    for (int i = 0; i < ROWS; ++i) {
-      const int64_t m = mbase + i;
-      if (m >= M) break;
-      float xv[8];
-      bf16x8_to_f32(*reinterpret_cast<const uint4*>(X + m * K + k), xv);
+      for (int e = 0; e < 8; ++e) f[u][e] = 0.0f;
+    }
+    xv[u] = *reinterpret_cast<const uint4*>(X + mc * K + kc);
+  }
+  f32x16_t acc;
 #pragma unroll
-      for (int j = 0; j < RCH; ++j)
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[i][j] = __builtin_fmaf(xv[e], w[j][e], acc[i][j]);
+  for (int u = 0; u < UNR; ++u) {
+    const bf16x8_t fa = frag_from_f32(f[u], lo);
+    const bf16x8_t fb = __builtin_bit_cast(bf16x8_t, xv[u]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc, 0, 0, 0);
+  }
+  // register r (< 8) holds rank row 8*(r/4) + 4*(lane/32) + r%4 (hi), r + 8 its lo
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s_part[wave][lane][i] = acc[i] + acc[i + 8];
+  __syncthreads();
+  if (wave == 0) {
+    const int64_t mo = m0 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float sum = s_part[0][lane][i];
+      for (int w = 1; w < ROW_WAVES; ++w) sum += s_part[w][lane][i];
+      const int jj = r0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (mo < M && jj < r) part[((int64_t)ks * M + mo) * r + jj] = sum;
     }
   }
-  // fixed butterfly over the 64 lanes; every lane ends with the full sum
+}
+
+// out[m, j] = scale * sum_ks part[ks, m, j], ks in order.
+__global__ __launch_bounds__(256) void k_rows_sum(const float* __restrict__ part, int nks,
+                                                  int64_t n, float scale,
+                                                  float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = part[i];
+  for (int p = 1; p < nks; ++p) s += part[(int64_t)p * n + i];
+  out[i] = scale * s;
+}
+
+int64_t row_chunks(int64_t K) { return (K + ROW_CHUNK - 1) / ROW_CHUNK; }
+
+hipError_t rowdot(bool trans_f, const uint16_t* X, int64_t M, int64_t K, const float* F, int r,
+                  float scale, float* out, float* part, hipStream_t s) {
+  const int64_t nks = row_chunks(K);
+  const dim3 grid((unsigned)((M + 31) / 32), (unsigned)nks, (unsigned)((r + RCH - 1) / RCH));
+  if (trans_f)
+    hipLaunchKernelGGL(k_lora_rows<true>, grid, dim3(ROW_WAVES * 64), 0, s, X, M, K, F, r, part);
+  else
+    hipLaunchKernelGGL(k_lora_rows<false>, grid, dim3(ROW_WAVES * 64), 0, s, X, M, K, F, r, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = M * r;
+  hipLaunchKernelGGL(k_rows_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part,
+                     (int)nks, n, scale, out);
+  return hipGetLastError();
+}
+
+constexpr int COL_WAVES = 8;
+constexpr int CUNR = 2;  // 16-row slices whose loads are issued together
+
+// out(r0 + j, c) (+)= scale * sum_m L[m, r0 + j] * G[m, c] for one 32-column
+// tile of c; out is [r, N] (dA) or, with TRANS_OUT, [N, r] (dB).
+// MFMA view: C[rho, c] = sum_m L'[rho, m] G[m, c]. The waves take consecutive
+// stretches of M; loads of CUNR 16-row slices are issued before their MFMAs.
+template <bool TRANS_OUT>
+__global__ __launch_bounds__(COL_WAVES * 64) void k_lora_cols(const uint16_t* __restrict__ G,
+                                                              int64_t M, int64_t N,
+                                                              const float* __restrict__ Lm, int r,
+                                                              float scale, int accumulate,
+                                                              float* __restrict__ out) {
+  __shared__ float s_part[COL_WAVES][64][8];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t c0 = (int64_t)blockIdx.x * 32;
+  const int r0 = blockIdx.y * RCH;
+  const int rho = lane & 31;
+  const bool lo = rho >= 16;
+  const int j = r0 + (rho & 15);
+  const int jc = j < r ? j : r - 1;
+  const int ms = (lane >> 5) * 8;
+  const int64_t c = c0 + rho;
+  const int64_t cc = c < N ? c : N - 1;  // columns past N are never stored
+  const int64_t per = ((M + COL_WAVES * 16 - 1) / (COL_WAVES * 16)) * 16;
+  const int64_t mb = wave * per;
+  const int64_t me = (mb + per < M) ? mb + per : M;
+  f32x16_t acc;
 #pragma unroll
-  for (int i = 0; i < ROWS; ++i)
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  // 32-bit element offsets from uniform bases (M * N < 2^31, checked on the host)
+  const uint32_t uN = (uint32_t)N;
+  const uint32_t ur = (uint32_t)r;
+  for (int64_t m1 = mb; m1 < me; m1 += 16 * CUNR) {
+    float f[CUNR][8];
+    uint32_t gq[CUNR][8];
 #pragma unroll
-    for (int j = 0; j < RCH; ++j)
+    for (int u = 0; u < CUNR; ++u) {
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) acc[i][j] += __shfl_xor(acc[i][j], o, 64);
-  if (lane < RCH) {
-    const int rr = r0 + lane;
-    if (rr < r) {
+      for (int e = 0; e < 8; ++e) {
+        const int64_t m = m1 + 16 * u + ms + e;
+        const bool ok = m < me;
+        const uint32_t mcl = (uint32_t)(ok ? m : me - 1);
+        const float fv = Lm[mcl * ur + (uint32_t)jc];
+        const uint32_t gv = G[mcl * uN + (uint32_t)cc];
+        f[u][e] = (ok && j < r) ? fv : 0.0f;
+        gq[u][e] = ok ? gv : 0u;
+      }
+    }
 #pragma unroll
-      for (int i = 0; i < ROWS; ++i) {
-        const int64_t m = mbase + i;
-        if (m >= M) break;
-        float v = 0.0f;
+    for (int u = 0; u < CUNR; ++u) {
+      const bf16x8_t fa = frag_from_f32(f[u], lo);
+      uint4 gv;
+      gv.x = gq[u][0] | (gq[u][1] << 16);
+      gv.y = gq[u][2] | (gq[u][3] << 16);
+      gv.z = gq[u][4] | (gq[u][5] << 16);
+      gv.w = gq[u][6] | (gq[u][7] << 16);
+      const bf16x8_t fb = __builtin_bit_cast(bf16x8_t, gv);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc, 0, 0, 0);
+    }
+  }
 #pragma unroll
-        for (int j = 0; j < RCH; ++j)
-          if (j == lane) v = acc[i][j];
-        out[m * r + rr] = scale * v;
+  for (int i = 0; i < 8; ++i) s_part[wave][lane][i] = acc[i] + acc[i + 8];
+  __syncthreads();
+  if (wave == 0) {
+    const int64_t co = c0 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float s = s_part[0][lane][i];
+      for (int w = 1; w < COL_WAVES; ++w) s += s_part[w][lane][i];
+      const int jj = r0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (co < N && jj < r) {
+        float* o = TRANS_OUT ? out + co * r + jj : out + (int64_t)jj * N + co;
+        const float v = scale * s;
+        *o = accumulate ? *o + v : v;
       }
     }
   }
 }
 
-// part[s, n, j] = sum over rows m of split s of G[m, n] * U[m, r0 + j].
-__global__ __launch_bounds__(256) void k_coldot(const uint16_t* __restrict__ G, int64_t M,
-                                                int64_t N, const float* __restrict__ U, int r,
-                                                int r0, float* __restrict__ part) {
-  const int64_t n = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
-  const int s = blockIdx.y;
-  const int64_t mb = (int64_t)s * MSPLIT_ROWS;
-  const int64_t me = (mb + MSPLIT_ROWS < M) ? mb + MSPLIT_ROWS : M;
-  if (n >= N) return;
-  float acc0[RCH], acc1[RCH];
-#pragma unroll
-  for (int j = 0; j < RCH; ++j) acc0[j] = acc1[j] = 0.0f;
-  for (int64_t m = mb; m < me; ++m) {
-    const uint32_t gv = *reinterpret_cast<const uint32_t*>(G + m * N + n);
-    const float g0 = __uint_as_float(gv << 16);
-    const float g1 = __uint_as_float(gv & 0xFFFF0000u);
-#pragma unroll
-    for (int j = 0; j < RCH; ++j) {
-      const float u = (r0 + j < r) ? U[m * r + r0 + j] : 0.0f;
-      acc0[j] = __builtin_fmaf(g0, u, acc0[j]);
-      acc1[j] = __builtin_fmaf(g1, u, acc1[j]);
-    }
-  }
-  float* p0 = part + ((int64_t)s * N + n) * RCH;
-#pragma unroll
-  for (int j = 0; j < RCH; ++j) {
-    p0[j] = acc0[j];
-    p0[RCH + j] = acc1[j];
-  }
-}
-
-// out (+)= scale * sum_s part[s, n, j], s in order; out is [N, r] (dB) or,
-// with TRANS_OUT, [r, N] (dA).
-template <bool TRANS_OUT>
-__global__ __launch_bounds__(256) void k_colsum(const float* __restrict__ part, int splits,
-                                                int64_t N, int r, int r0, float scale,
-                                                int accumulate, float* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over N * RCH
-  if (i >= N * RCH) return;
-  const int64_t n = i / RCH;
-  const int j = (int)(i % RCH);
-  if (r0 + j >= r) return;
-  float s = part[i];
-  for (int p = 1; p < splits; ++p) s += part[(int64_t)p * N * RCH + i];
-  s = scale * s;
-  float* o = TRANS_OUT ? out + (int64_t)(r0 + j) * N + n : out + n * r + r0 + j;
-  *o = accumulate ? *o + s : s;
-}
-
-template <bool TRANS_OUT>
-hipError_t coldot(const uint16_t* G, int64_t M, int64_t N, const float* U, int r, float scale,
-                  int accumulate, float* out, float* part, hipStream_t s) {
-  const int splits = (int)((M + MSPLIT_ROWS - 1) / MSPLIT_ROWS);
-  for (int r0 = 0; r0 < r; r0 += RCH) {
-    hipLaunchKernelGGL(k_coldot, dim3((unsigned)((N / 2 + 255) / 256), (unsigned)splits),
-                       dim3(256), 0, s, G, M, N, U, r, r0, part);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_colsum<TRANS_OUT>, dim3((unsigned)((N * RCH + 255) / 256)), dim3(256), 0, s, part,
-                       splits, N, r, r0, scale, accumulate, out);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
-
 }  // namespace
 
-size_t lora_bwd_ws_bytes(int64_t M, int64_t k_in, int64_t n_out) {
-  const int64_t splits = (M + MSPLIT_ROWS - 1) / MSPLIT_ROWS;
-  const int64_t n = k_in > n_out ? k_in : n_out;
-  return (size_t)splits * (size_t)n * RCH * sizeof(float);
+size_t lora_fwd_ws_bytes(int64_t M, int64_t k_in, int r) {
+  return (size_t)row_chunks(k_in) * (size_t)M * (size_t)r * sizeof(float);
+}
+
+size_t lora_bwd_ws_bytes(int64_t M, int64_t n_out, int r) {
+  return (size_t)row_chunks(n_out) * (size_t)M * (size_t)r * sizeof(float);
 }
 
 hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t k_in, const float* A, int r,
-                           float* u, hipStream_t s) {
-  const dim3 grid((unsigned)((M + 4 * ROWS - 1) / (4 * ROWS)), (unsigned)((r + RCH - 1) / RCH));
-  hipLaunchKernelGGL(k_rowdot<false>, grid, dim3(256), 0, s, x, M, k_in, A, r, 1.0f, u);
-  return hipGetLastError();
+                           float* u, void* ws, hipStream_t s) {
+  return rowdot(false, x, M, k_in, A, r, 1.0f, u, static_cast<float*>(ws), s);
 }
 
 hipError_t launch_lora_bwd(const uint16_t* x, const uint16_t* dy, const float* u, int64_t M,
                            int64_t k_in, int64_t n_out, const float* B, int r, float scale,
                            float* dA, float* dB, float* du, int accumulate, void* ws,
                            hipStream_t s) {
+  const unsigned rch = (unsigned)((r + RCH - 1) / RCH);
   // du = scale * dy . B
-  const dim3 grid((unsigned)((M + 4 * ROWS - 1) / (4 * ROWS)), (unsigned)((r + RCH - 1) / RCH));
-  hipLaunchKernelGGL(k_rowdot<true>, grid, dim3(256), 0, s, dy, M, n_out, B, r, scale, du);
-  hipError_t e = hipGetLastError();
+  hipError_t e = rowdot(true, dy, M, n_out, B, r, scale, du, static_cast<float*>(ws), s);
   if (e != hipSuccess) return e;
-  float* part = static_cast<float*>(ws);
-  // dB = scale * dy^T . u
-  e = coldot<false>(dy, M, n_out, u, r, scale, accumulate, dB, part, s);
+  // dB = scale * dy^T . u   ([n_out, r])
+  hipLaunchKernelGGL(k_lora_cols<true>, dim3((unsigned)((n_out + 31) / 32), rch),
+                     dim3(COL_WAVES * 64), 0, s, dy, M, n_out, u, r, scale, accumulate, dB);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // dA = du^T . x
-  return coldot<true>(x, M, k_in, du, r, 1.0f, accumulate, dA, part, s);
+  // dA = du^T . x           ([r, k_in])
+  hipLaunchKernelGGL(k_lora_cols<false>, dim3((unsigned)((k_in + 31) / 32), rch),
+                     dim3(COL_WAVES * 64), 0, s, x, M, k_in, du, r, 1.0f, accumulate, dA);
+  return hipGetLastError();
 }
 
 }  // namespace nf4s

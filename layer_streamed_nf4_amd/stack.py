@@ -20,7 +20,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import (DTYPE_F32, OP_LINEAR_BWD, OP_LINEAR_FWD, OP_LORA_BWD, OP_QUANTIZE, lora_bwd,
+from . import (DTYPE_F32, OP_LINEAR_BWD, OP_LINEAR_FWD, OP_LORA_BWD, OP_LORA_FWD, OP_QUANTIZE, lora_bwd,
                lora_fwd, nf4_quantize_shard, nf4s_pool_acquire, nf4s_pool_create,
                nf4s_pool_destroy, nf4s_pool_prefetch, nf4s_pool_release, nf4s_pool_set_layer,
                nf4s_pool_stats, nf4s_tensor_layout, nf4s_workspace_bytes, streamed_linear_bwd,
@@ -129,6 +129,7 @@ class LinearStack:
             n, k = shapes[p]
             ws = max(ws, nf4s_workspace_bytes(OP_LINEAR_FWD, M, n, k),
                      nf4s_workspace_bytes(OP_LINEAR_BWD, M, n, k),
+                     nf4s_workspace_bytes(OP_LORA_FWD, M, n, k),
                      nf4s_workspace_bytes(OP_LORA_BWD, M, n, k))
         self.ws = torch.empty(_round_up(max(ws, ALIGN)), dtype=torch.uint8, device=dev)
         # u = x . A^T per target, produced by the (re)computed forward of a layer
@@ -178,7 +179,8 @@ class LinearStack:
             if p in self.targets:
                 A, B = self.lora[i][p]
                 u = self.u[p]
-                lora_fwd(x.data_ptr(), self.M, k, A.data_ptr(), self.r, u.data_ptr(), s)
+                lora_fwd(x.data_ptr(), self.M, k, A.data_ptr(), self.r, u.data_ptr(),
+                         self.ws.data_ptr(), self.ws.numel(), s)
                 ev = self._tick("fwd", n, k)
                 streamed_linear_fwd(base, self.sh.layout.descs[p], x.data_ptr(), self.M, y.data_ptr(),
                                     u.data_ptr(), B.data_ptr(), self.r, self.scale,

@@ -146,7 +146,7 @@ def test_pointer_and_argument_errors():
         L.nf4_quantize_shard(FAKE, L.DTYPE_F32, 128, 64, FAKE, d, None, FAKE, 1 << 20)
     assert e.value.code in (L.ESHAPE,)
     with pytest.raises(L.Nf4sError) as e:
-        L.lora_fwd(FAKE, 16, 100, FAKE, 16, FAKE)
+        L.lora_fwd(FAKE, 16, 100, FAKE, 16, FAKE, FAKE, 1 << 20)
     assert e.value.code == L.ESHAPE
     with pytest.raises(L.Nf4sError) as e:
         L.lora_bwd(FAKE, FAKE, FAKE, 16, 64, 64, FAKE, 16, 2.0, FAKE, FAKE, FAKE, 2, FAKE, 1 << 30)

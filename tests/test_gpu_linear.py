@@ -51,10 +51,11 @@ def _run(c, lora=True):
     dB = torch.empty((n, R), dtype=torch.float32, device="cuda")
     wsf = ws_tensor(L.nf4s_workspace_bytes(L.OP_LINEAR_FWD, M, n, k))
     wsb = ws_tensor(L.nf4s_workspace_bytes(L.OP_LINEAR_BWD, M, n, k))
-    wsl = ws_tensor(L.nf4s_workspace_bytes(L.OP_LORA_BWD, M, n, k))
+    wsl = ws_tensor(max(L.nf4s_workspace_bytes(L.OP_LORA_BWD, M, n, k),
+                        L.nf4s_workspace_bytes(L.OP_LORA_FWD, M, n, k)))
     sp = c["shard"].data_ptr()
     if lora:
-        L.lora_fwd(x.data_ptr(), M, k, A.data_ptr(), R, u.data_ptr(), s)
+        L.lora_fwd(x.data_ptr(), M, k, A.data_ptr(), R, u.data_ptr(), wsl.data_ptr(), wsl.numel(), s)
         L.streamed_linear_fwd(sp, c["d"], x.data_ptr(), M, y.data_ptr(), u.data_ptr(), B.data_ptr(),
                               R, S, wsf.data_ptr(), wsf.numel(), s)
         L.lora_bwd(x.data_ptr(), dy.data_ptr(), u.data_ptr(), M, k, n, B.data_ptr(), R, S,

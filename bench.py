@@ -70,6 +70,73 @@ def lora_flops_per_token(model: str, targets) -> int:
     return synth.N_LAYERS[model] * sum(8 * r * (sh[p][0] + sh[p][1]) for p in targets)
 
 
+def gemm_source_hash() -> str:
+    """Hash of the fused-GEMM source: counters taken on another build do not apply."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    with open(os.path.join(here, "layer_streamed_nf4_amd", "csrc", "gemm.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_src_hash: str):
+    """HBM bytes per launch of the dominant kernel from the committed PMC summary,
+    if it was taken on this exact GEMM source; else None."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", "gemm_fwd_gate_8b_m512_pmc.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("<!--") and "=" in line:
+            k, v = line.strip("<!-> \n").split("=", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("gemm_src_sha256_16") != kernel_src_hash:
+        return None
+    try:
+        return int(float(fields["fetch_bytes"]) + float(fields["write_bytes"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def profile_gemm(spec: str, reps: int) -> None:
+    """Run one fused GEMM shape `fwd:N:K:M` or `bwd:N:K:M` (resident weight)
+    `reps` times, then a 64 MiB device copy whose FETCH/WRITE counters give the
+    scale of the memory counters. Used under rocprofv3."""
+    import torch
+    import layer_streamed_nf4_amd as L
+    direction, n, k, M = spec.split(":")
+    n, k, M = int(n), int(k), int(M)
+    dev = "cuda"
+    s = torch.cuda.current_stream().cuda_stream
+    g = torch.Generator(device=dev)
+    g.manual_seed(synth.BASE_SEED)
+    w = torch.randn((n, k), generator=g, device=dev) * 0.02
+    d = L.nf4s_tensor_layout(n, k)
+    shard = torch.zeros(d.end, dtype=torch.uint8, device=dev)
+    wq = torch.empty(max(256, L.nf4s_workspace_bytes(L.OP_QUANTIZE, 0, n, k)), dtype=torch.uint8, device=dev)
+    L.nf4_quantize_shard(w.data_ptr(), L.DTYPE_F32, n, k, shard.data_ptr(), d, None, wq.data_ptr(),
+                         wq.numel(), s)
+    bwd = direction == "bwd"
+    a = torch.randn((M, n if bwd else k), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty((M, k if bwd else n), dtype=torch.bfloat16, device=dev)
+    op = L.OP_LINEAR_BWD if bwd else L.OP_LINEAR_FWD
+    ws = torch.zeros(max(256, L.nf4s_workspace_bytes(op, M, n, k)), dtype=torch.uint8, device=dev)
+    for _ in range(reps):
+        if bwd:
+            L.streamed_linear_bwd(shard.data_ptr(), d, a.data_ptr(), M, out.data_ptr(), None, None, 0,
+                                  ws.data_ptr(), ws.numel(), s)
+        else:
+            L.streamed_linear_fwd(shard.data_ptr(), d, a.data_ptr(), M, out.data_ptr(), None, None, 0,
+                                  0.0, ws.data_ptr(), ws.numel(), s)
+    torch.cuda.synchronize()
+    src = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"profiled {spec} x{reps}; gemm source {gemm_source_hash()}", flush=True)
+
+
 def _cpu_baseline(model: str, M: int, targets) -> dict:
     """The oracle, as it stands, on one full layer of the step (dequantise the
     seven tensors, then forward and backward of the seven projections with the
@@ -108,7 +175,13 @@ def main():
     ap.add_argument("--slots", type=int, default=None)
     ap.add_argument("--no-resident", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile-gemm", default=None,
+                    help="only run one fused GEMM shape, e.g. fwd:14336:4096:512 (for rocprofv3)")
+    ap.add_argument("--reps", type=int, default=5)
     args = ap.parse_args()
+    if args.profile_gemm:
+        profile_gemm(args.profile_gemm, args.reps)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -229,7 +302,9 @@ def main():
         avg_flop = sum(dom_flops) / len(dom_flops)
         ach = avg_flop / (avg_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": traffic_from_profile(gemm_source_hash()),
+                    "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                     "kernel": "k_gemm<fwd,plain> (fused NF4 dequant + bf16 MFMA, x.W'^T)",
                     "launches": len(dom_ms), "avg_us": round(avg_ms * 1e3, 2),
                     "flop_per_launch": int(avg_flop)}

@@ -14,15 +14,20 @@
 // a' = fp32(fp32(C8[q8]*nested) + offset) and W' = bf16_rne(fp32(C4[code]*a')),
 // and written to LDS as bf16 in the contraction-major layout the matrix cores
 // read; W' never goes back to HBM. A packed byte holds two codes, and one LDS
-// read of a 256-entry table gives both of their NF4 levels. The backward
-// orientation is transposed on the way into LDS for free: a thread decodes a
-// 4x8 patch and pairs values along the contraction when it packs bf16.
+// read of a 256-entry table gives both of their NF4 levels; the table is
+// replicated 16 times so that lane l always reads the copy that lives in bank
+// pair (2(l%16), 2(l%16)+1), which makes the random lookups conflict-free.
+// The backward orientation is transposed on the way into LDS for free: a
+// thread decodes a 4x8 patch and pairs values along the contraction when it
+// packs bf16.
 //
-// Tiling for gfx950: 256 threads (4 wave64), output tile 256x128, contraction
-// step 64 (exactly one NF4 block per weight row in the forward direction),
-// v_mfma_f32_32x32x16_bf16 with each wave owning a 128x64 sub-tile (4x2 MFMA
-// tiles, 128 fp32 accumulators per lane), double-buffered LDS, and register
-// rings that keep the weight stream and the activation tile two steps ahead.
+// Tiling for gfx950: 512 threads (8 wave64, two per SIMD so that one wave's
+// LDS and memory waits are covered by the other's MFMAs), output tile
+// 256x128, contraction step 64 (exactly one NF4 block per weight row in the
+// forward direction), v_mfma_f32_32x32x16_bf16 with each wave owning a 64x64
+// sub-tile (2x2 MFMA tiles, 64 fp32 accumulators per lane), double-buffered
+// LDS, and register rings that keep the weight stream and the activation tile
+// two steps ahead.
 // All per-lane addresses are loop-invariant 32-bit offsets from per-step
 // uniform bases, so a step spends its vector instructions on decoding only.
 // LDS rows are padded to 144 B so the 16-byte fragment reads of 8 consecutive
@@ -39,7 +44,7 @@ constexpr int BM = 256;
 constexpr int BN = 128;
 constexpr int BK = 64;
 constexpr int LDS_STRIDE = 72;  // bf16 elements per LDS row (64 + 8 pad = 144 B)
-constexpr int THREADS = 256;
+constexpr int THREADS = 512;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
 
@@ -69,17 +74,20 @@ struct Step {
   int64_t nom;  // nominal first index; rows below it are masked
 };
 
-// ---- activation tile (A): 8 rows x 16 bytes per thread -------------------
+// ---- activation tile (A): 4 rows x 16 bytes per thread -------------------
+constexpr int A_CHUNKS = BM * BK / 8 / THREADS;  // 16-byte chunks per thread (4)
+constexpr int A_ROW_STEP = THREADS / 8;          // rows between a thread's chunks (64)
+
 struct ALanes {
-  uint32_t off[8];  // byte offsets of the thread's 8 chunks at contraction 0
+  uint32_t off[A_CHUNKS];  // byte offsets of the thread's chunks at contraction 0
 };
 
 __device__ __forceinline__ ALanes a_lanes(const GemmArgs& g, int64_t m0) {
   const int t = threadIdx.x;
   ALanes L;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int64_t row = m0 + (t >> 3) + 32 * i;
+  for (int i = 0; i < A_CHUNKS; ++i) {
+    int64_t row = m0 + (t >> 3) + A_ROW_STEP * i;
     row = row < g.M ? row : g.M - 1;  // rows past M feed output rows never stored
     L.off[i] = (uint32_t)((row * g.Kc + (t & 7) * 8) * 2);
   }
@@ -87,18 +95,18 @@ __device__ __forceinline__ ALanes a_lanes(const GemmArgs& g, int64_t m0) {
 }
 
 __device__ __forceinline__ void load_a(const GemmArgs& g, const ALanes& L, int64_t win,
-                                       u32x4 (&ra)[8]) {
+                                       u32x4 (&ra)[A_CHUNKS]) {
   const char* base = reinterpret_cast<const char*>(g.a + win);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ra[i] = *reinterpret_cast<const u32x4*>(base + L.off[i]);
+  for (int i = 0; i < A_CHUNKS; ++i) ra[i] = *reinterpret_cast<const u32x4*>(base + L.off[i]);
 }
 
-__device__ __forceinline__ void store_a(uint16_t* As, const u32x4 (&ra)[8]) {
+__device__ __forceinline__ void store_a(uint16_t* As, const u32x4 (&ra)[A_CHUNKS]) {
   const int t = threadIdx.x;
   const int c = t & 7;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = (t >> 3) + 32 * i;
+  for (int i = 0; i < A_CHUNKS; ++i) {
+    const int row = (t >> 3) + A_ROW_STEP * i;
     *reinterpret_cast<u32x4*>(As + row * LDS_STRIDE + c * 8) = ra[i];
   }
 }
@@ -109,16 +117,18 @@ struct WLanes;
 template <bool BWD>
 struct BRegs;
 
-// Forward: thread t owns weight row n0 + t/2 and contraction half t%2 (32 codes).
+// Forward: thread t owns weight row n0 + t/4 and contraction quarter t%4
+// (16 codes, two packed words).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <>
 struct WLanes<false> {
-  uint32_t woff;  // byte offset of the thread's 16 packed bytes at contraction 0
+  uint32_t woff;  // byte offset of the thread's 8 packed bytes at contraction 0
   uint32_t blk0;  // 64-block index at contraction 0
   bool valid;     // row < n_out
 };
 template <>
 struct BRegs<false> {
-  u32x4 w;
+  u32x2 w;
   uint32_t q;
   float nest;
 };
@@ -126,36 +136,37 @@ struct BRegs<false> {
 __device__ __forceinline__ WLanes<false> w_lanes_fwd(const GemmArgs& g, int64_t n0) {
   const int t = threadIdx.x;
   WLanes<false> L;
-  int64_t n = n0 + (t >> 1);
+  int64_t n = n0 + (t >> 2);
   L.valid = n < g.n_out;
   n = L.valid ? n : g.n_out - 1;
-  L.woff = (uint32_t)(n * (g.k_in / 2) + (t & 1) * 16);
+  L.woff = (uint32_t)(n * (g.k_in / 2) + (t & 3) * 8);
   L.blk0 = (uint32_t)(n * (g.k_in / 64));
   return L;
 }
 
 __device__ __forceinline__ void load_b(const GemmArgs& g, const WLanes<false>& L, Step s,
                                        BRegs<false>& rb) {
-  rb.w = *reinterpret_cast<const u32x4*>(g.packed + s.win / 2 + L.woff);
+  rb.w = *reinterpret_cast<const u32x2*>(g.packed + s.win / 2 + L.woff);
   const uint32_t blk = L.blk0 + (uint32_t)(s.win / 64);
   rb.q = g.q8[blk];
   rb.nest = g.nested[blk >> 8];
 }
 
-// Backward: thread t owns weight rows k0 + 4*(t/16) + i (i < 4) and output
-// columns n0 + 8*(t%16) + j (j < 8): four packed words, four 8-bit scale
-// codes packed in one register, four nested scales, a 4-bit validity mask.
+// Backward: thread t owns weight rows k0 + 2*(t/16) + i (i < 2) and output
+// columns n0 + 8*(t%16) + j (j < 8): two packed words, two 8-bit scale codes
+// packed in one register, two nested scales, a 2-bit validity mask.
+constexpr int BW_ROWS = 2;
 template <>
 struct WLanes<true> {
-  uint32_t woff[4];  // byte offsets of the 4 packed words at contraction 0
-  uint32_t blk0[4];  // 64-block indices at contraction 0
-  bool cvalid;       // columns < k_in
+  uint32_t woff[BW_ROWS];  // byte offsets of the packed words at contraction 0
+  uint32_t blk0[BW_ROWS];  // 64-block indices at contraction 0
+  bool cvalid;             // columns < k_in
 };
 template <>
 struct BRegs<true> {
-  uint32_t w[4];
+  uint32_t w[BW_ROWS];
   uint32_t q;
-  float nest[4];
+  float nest[BW_ROWS];
   uint32_t vmask;
 };
 
@@ -166,8 +177,8 @@ __device__ __forceinline__ WLanes<true> w_lanes_bwd(const GemmArgs& g, int64_t n
   L.cvalid = col < g.k_in;
   col = L.cvalid ? col : g.k_in - 8;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = 4 * (t >> 4) + i;  // relative to the step's window
+  for (int i = 0; i < BW_ROWS; ++i) {
+    const int64_t row = BW_ROWS * (t >> 4) + i;  // relative to the step's window
     L.woff[i] = (uint32_t)((row * g.k_in + col) / 2);
     L.blk0[i] = (uint32_t)((row * g.k_in + col) / 64);
   }
@@ -182,21 +193,25 @@ __device__ __forceinline__ void load_b(const GemmArgs& g, const WLanes<true>& L,
   rb.q = 0;
   rb.vmask = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < BW_ROWS; ++i) {
     rb.w[i] = *reinterpret_cast<const uint32_t*>(base + L.woff[i]);
     const uint32_t blk = bstep + L.blk0[i];
     rb.q |= (uint32_t)g.q8[blk] << (8 * i);
     rb.nest[i] = g.nested[blk >> 8];
-    const int64_t row = s.win + 4 * (t >> 4) + i;
+    const int64_t row = s.win + BW_ROWS * (t >> 4) + i;
     rb.vmask |= (L.cvalid && row >= s.nom) ? (1u << i) : 0u;
   }
 }
 
 // ---- decoding -------------------------------------------------------------
-// ptab[b] = (C4[b >> 4], C4[b & 15]): both levels of a packed byte, the even
-// element (high nibble) first.
+// Pair table: entry b = (C4[b >> 4], C4[b & 15]), both levels of a packed byte,
+// the even element (high nibble) first. Copy c of entry b sits at float2 index
+// 16*b + c, i.e. dwords 32*b + 2c and 32*b + 2c + 1: the copy fixes the LDS
+// bank pair whatever b is. `ptab` below is already offset by the lane's copy.
+constexpr int PAIR_COPIES = 16;
+
 __device__ __forceinline__ float2 pair_of(const float2* ptab, uint32_t word, int byte) {
-  return ptab[(word >> (8 * byte)) & 0xFFu];
+  return ptab[((word >> (8 * byte)) & 0xFFu) * PAIR_COPIES];
 }
 
 __device__ __forceinline__ float stage_scale(const BRegs<false>& rb, bool valid, float off,
@@ -204,37 +219,38 @@ __device__ __forceinline__ float stage_scale(const BRegs<false>& rb, bool valid,
   return valid ? decode_scale(c8[rb.q], rb.nest, off) : 0.0f;
 }
 
-// Quarter Q of a forward stage: packed word Q (8 codes) -> 8 bf16 in LDS.
+// Quarter Q of a forward stage: half Q%2 of packed word Q/2 (4 codes) -> 4
+// bf16 in LDS.
 template <int Q>
 __device__ __forceinline__ void store_b_quarter(uint16_t* Bs, const BRegs<false>& rb, float a,
                                                 const float2* ptab) {
   const int t = threadIdx.x;
-  const uint32_t word = rb.w[Q];
-  u32x4 o;
+  const uint32_t word = rb.w[Q >> 1];
+  u32x2 o;
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const float2 c = pair_of(ptab, word, p);
+  for (int p = 0; p < 2; ++p) {
+    const float2 c = pair_of(ptab, word, 2 * (Q & 1) + p);
     o[p] = pack_bf16x2(__fmul_rn(c.x, a), __fmul_rn(c.y, a));
   }
-  *reinterpret_cast<u32x4*>(Bs + (t >> 1) * LDS_STRIDE + (t & 1) * 32 + Q * 8) = o;
+  *reinterpret_cast<u32x2*>(Bs + (t >> 2) * LDS_STRIDE + (t & 3) * 16 + Q * 4) = o;
 }
 
 struct Scales4 {
-  float a[4];
+  float a[BW_ROWS];
 };
 
 __device__ __forceinline__ Scales4 stage_scale(const BRegs<true>& rb, bool, float off,
                                                const float* c8) {
   Scales4 s;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < BW_ROWS; ++i)
     s.a[i] = ((rb.vmask >> i) & 1u) ? decode_scale(c8[(rb.q >> (8 * i)) & 0xFFu], rb.nest[i], off)
                                     : 0.0f;
   return s;
 }
 
 // Quarter Q of a backward stage: output columns 2Q and 2Q+1 of the thread's
-// 4x8 patch (byte Q of each row's word), each written as 4 consecutive
+// 2x8 patch (byte Q of each row's word), each written as 2 consecutive
 // contraction values -- the transpose into the matrix-core layout happens here,
 // in the bf16 pairing.
 template <int Q>
@@ -242,21 +258,13 @@ __device__ __forceinline__ void store_b_quarter(uint16_t* Bs, const BRegs<true>&
                                                 const Scales4& sc, const float2* ptab) {
   const int t = threadIdx.x;
   const int cb = 8 * (t & 15) + 2 * Q;
-  const int rbase = 4 * (t >> 4);
-  float v0[4], v1[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float2 c = pair_of(ptab, rb.w[i], Q);
-    v0[i] = __fmul_rn(c.x, sc.a[i]);
-    v1[i] = __fmul_rn(c.y, sc.a[i]);
-  }
-  uint2 p0, p1;
-  p0.x = pack_bf16x2(v0[0], v0[1]);
-  p0.y = pack_bf16x2(v0[2], v0[3]);
-  p1.x = pack_bf16x2(v1[0], v1[1]);
-  p1.y = pack_bf16x2(v1[2], v1[3]);
-  *reinterpret_cast<uint2*>(Bs + cb * LDS_STRIDE + rbase) = p0;
-  *reinterpret_cast<uint2*>(Bs + (cb + 1) * LDS_STRIDE + rbase) = p1;
+  const int rbase = BW_ROWS * (t >> 4);
+  const float2 c0 = pair_of(ptab, rb.w[0], Q);
+  const float2 c1 = pair_of(ptab, rb.w[1], Q);
+  const uint32_t p0 = pack_bf16x2(__fmul_rn(c0.x, sc.a[0]), __fmul_rn(c1.x, sc.a[1]));
+  const uint32_t p1 = pack_bf16x2(__fmul_rn(c0.y, sc.a[0]), __fmul_rn(c1.y, sc.a[1]));
+  *reinterpret_cast<uint32_t*>(Bs + cb * LDS_STRIDE + rbase) = p0;
+  *reinterpret_cast<uint32_t*>(Bs + (cb + 1) * LDS_STRIDE + rbase) = p1;
 }
 
 template <typename R, typename S>
@@ -294,12 +302,17 @@ template <bool BWD, bool SPLIT>
 __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_STRIDE];
-  __shared__ float2 s_pair[256];
+  __shared__ float2 s_pair_all[256 * PAIR_COPIES];
   __shared__ float s_c8[256];
 
   const int t = threadIdx.x;
-  s_pair[t] = make_float2(tab.c4[t >> 4], tab.c4[t & 15]);
-  s_c8[t] = tab.c8[t];
+  if (t < 256) {
+    const float2 e = make_float2(tab.c4[t >> 4], tab.c4[t & 15]);
+#pragma unroll
+    for (int c = 0; c < PAIR_COPIES; ++c) s_pair_all[t * PAIR_COPIES + c] = e;
+    s_c8[t] = tab.c8[t];
+  }
+  const float2* s_pair = s_pair_all + (t & (PAIR_COPIES - 1));
 
   const int64_t n0 = (int64_t)blockIdx.x * BN;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
@@ -311,14 +324,14 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
 
   const int wave = t >> 6;
   const int lane = t & 63;
-  const int wm = wave >> 1;  // 128-row half of the tile
+  const int wm = wave >> 1;  // 64-row quarter of the tile
   const int wn = wave & 1;   // 64-column half of the tile
   const int lrow = lane & 31;
   const int lk = (lane >> 5) * 8;
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -345,7 +358,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
   // group of 8 MFMAs), fetches weight stage kt+3 and activation stage kt+2, and
   // finally stores activation stage kt+1.
   BRegs<BWD> rb0, rb1, rb2, rb3;
-  u32x4 ra0[8], ra1[8];
+  u32x4 ra0[A_CHUNKS], ra1[A_CHUNKS];
   load_b(g, wl, step_of(0), rb0);
   load_b(g, wl, step_of(1), rb1);
   load_b(g, wl, step_of(2), rb2);
@@ -364,9 +377,9 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
     const uint16_t* as = As[st];
     const uint16_t* bs = Bs[st];
     uint16_t* bnext = Bs[st ^ 1];
-    bf16x8_t fa[2][4], fb[2][2];
+    bf16x8_t fa[2][2], fb[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[0][i] = lds_frag(as, wm * 128 + i * 32 + lrow, lk);
+    for (int i = 0; i < 2; ++i) fa[0][i] = lds_frag(as, wm * 64 + i * 32 + lrow, lk);
 #pragma unroll
     for (int j = 0; j < 2; ++j) fb[0][j] = lds_frag(bs, wn * 64 + j * 32 + lrow, lk);
 #pragma unroll
@@ -374,8 +387,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
       const int cur = kk & 1;
       if (kk + 1 < BK / 16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          fa[cur ^ 1][i] = lds_frag(as, wm * 128 + i * 32 + lrow, (kk + 1) * 16 + lk);
+        for (int i = 0; i < 2; ++i)
+          fa[cur ^ 1][i] = lds_frag(as, wm * 64 + i * 32 + lrow, (kk + 1) * 16 + lk);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           fb[cur ^ 1][j] = lds_frag(bs, wn * 64 + j * 32 + lrow, (kk + 1) * 16 + lk);
@@ -385,7 +398,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
       if (kk == 2) store_b_quarter<2>(bnext, w_deq, sc, s_pair);
       if (kk == 3) store_b_quarter<3>(bnext, w_deq, sc, s_pair);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
@@ -421,10 +434,10 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
   // forward  + u[m, :] . (s * B[n, :]),  backward + du[m, :] . A[:, n].
   if (g.lora_l != nullptr && split == 0) {
     for (int r0 = 0; r0 < g.r; r0 += 16) {
-      bf16x8_t fa[4], fb[2];
+      bf16x8_t fa[2], fb[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t row = m0 + wm * 128 + i * 32 + lrow;
+      for (int i = 0; i < 2; ++i) {
+        const int64_t row = m0 + wm * 64 + i * 32 + lrow;
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -448,7 +461,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
         fb[j] = f32x8_to_bf16(v);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
@@ -458,14 +471,14 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
   // Accumulator layout of v_mfma_f32_32x32x16: register r of lane l holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the 32x32 tile.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int64_t col = n0 + wn * 64 + j * 32 + lrow;
       if (col >= g.Nc) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (row >= g.M) continue;
         if (SPLIT) {
           g.part[((int64_t)split * g.M + row) * g.Nc + col] = acc[i][j][r];

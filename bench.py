@@ -119,15 +119,18 @@ def profile_gemm(spec: str, reps: int) -> None:
     bwd = direction == "bwd"
     a = torch.randn((M, n if bwd else k), generator=g, device=dev).to(torch.bfloat16)
     out = torch.empty((M, k if bwd else n), dtype=torch.bfloat16, device=dev)
-    op = L.OP_LINEAR_BWD if bwd else L.OP_LINEAR_FWD
+    op = L.OP_LINEAR_BWD_PACKED if bwd else L.OP_LINEAR_FWD_PACKED
     ws = torch.zeros(max(256, L.nf4s_workspace_bytes(op, M, n, k)), dtype=torch.uint8, device=dev)
+    K = n if bwd else k
+    ap = torch.empty(L.nf4s_packed_activation_bytes(M, K), dtype=torch.uint8, device=dev)
+    L.nf4s_pack_activation(a.data_ptr(), M, K, ap.data_ptr(), ap.numel(), s)
     for _ in range(reps):
         if bwd:
-            L.streamed_linear_bwd(shard.data_ptr(), d, a.data_ptr(), M, out.data_ptr(), None, None, 0,
-                                  ws.data_ptr(), ws.numel(), s)
+            L.streamed_linear_bwd_packed(shard.data_ptr(), d, ap.data_ptr(), M, out.data_ptr(), None,
+                                         None, 0, ws.data_ptr(), ws.numel(), s)
         else:
-            L.streamed_linear_fwd(shard.data_ptr(), d, a.data_ptr(), M, out.data_ptr(), None, None, 0,
-                                  0.0, ws.data_ptr(), ws.numel(), s)
+            L.streamed_linear_fwd_packed(shard.data_ptr(), d, ap.data_ptr(), M, out.data_ptr(), None,
+                                         None, 0, 0.0, ws.data_ptr(), ws.numel(), s)
     torch.cuda.synchronize()
     src = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -225,15 +228,23 @@ def main():
 
     lora = [{p: lora_init(i, p) for p in targets} for i in range(n_layers)]
     gen.manual_seed(synth.BASE_SEED + 10**6)
-    xs = {p: torch.randn((M, sh[p][1]), generator=gen, device=dev).to(torch.bfloat16) for p in PROJ}
+    # the layer's dataflow: q, k, v read the normed hidden state, o the
+    # attention output, gate and up the normed hidden state of the MLP, down
+    # the gated product; each upstream gradient is its own tensor
+    role = {"q": "attn", "k": "attn", "v": "attn", "o": "o", "gate": "mlp", "up": "mlp", "down": "down"}
+    xs_role = {}
+    for p in PROJ:
+        if role[p] not in xs_role:
+            xs_role[role[p]] = torch.randn((M, sh[p][1]), generator=gen, device=dev).to(torch.bfloat16)
+    xs = {p: xs_role[role[p]] for p in PROJ}
     dys = {p: torch.randn((M, sh[p][0]), generator=gen, device=dev).to(torch.bfloat16) for p in PROJ}
     inputs = lambda i, p: xs[p]
     grads = lambda i, p: dys[p]
 
     # dominant kernel: the forward fused GEMM on shapes that need no split
-    # (gate/up at 8B): one streamed_linear_fwd call = one k_gemm<fwd,plain> launch
+    # (gate/up at 8B): one streamed_linear_fwd_packed call = one k_gemm<fwd,plain> launch
     def plain_fwd(direction, n, k):
-        return direction == "fwd" and L.nf4s_workspace_bytes(L.OP_LINEAR_FWD, M, n, k) == 0
+        return direction == "fwd" and L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, M, n, k) == 0
 
     def run(mode, n_slots, timed):
         st = LinearStack(shards, M, targets, lora, n_slots=n_slots, mode=mode, keep_outputs=False,

@@ -132,15 +132,18 @@ uint64_t nf4s_table_hash(void);
 /*
  * Scratch bytes an operation needs for the given shape (0 means none; ws may
  * then be NULL). op: NF4S_OP_QUANTIZE (n_out, k_in), NF4S_OP_LINEAR_FWD and
- * NF4S_OP_LINEAR_BWD, NF4S_OP_LORA_FWD and NF4S_OP_LORA_BWD (M, n_out, k_in;
- * the adapter sizes cover any rank up to NF4S_MAX_RANK). The value depends on
- * shapes only.
+ * NF4S_OP_LINEAR_BWD (the packed activation plus split partials),
+ * NF4S_OP_LINEAR_FWD_PACKED and NF4S_OP_LINEAR_BWD_PACKED (split partials
+ * only), NF4S_OP_LORA_FWD and NF4S_OP_LORA_BWD (M, n_out, k_in; the adapter
+ * sizes cover any rank up to NF4S_MAX_RANK). The value depends on shapes only.
  */
 #define NF4S_OP_QUANTIZE 1
 #define NF4S_OP_LINEAR_FWD 2
 #define NF4S_OP_LINEAR_BWD 3
 #define NF4S_OP_LORA_BWD 4
 #define NF4S_OP_LORA_FWD 5
+#define NF4S_OP_LINEAR_FWD_PACKED 6
+#define NF4S_OP_LINEAR_BWD_PACKED 7
 int nf4s_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, size_t* bytes);
 
 /*
@@ -195,12 +198,47 @@ int streamed_linear_fwd(const void* shard_dev, const nf4s_tensor_desc* d, const 
  *   dy: bf16 [M, n_out];  dx: bf16 [M, k_in];
  *   lora_du: nullable fp32 [M, r] (= scale * dy.B, from lora_bwd);
  *   lora_A:  fp32 [r, k_in] (required iff lora_du is given).
- * Errors as streamed_linear_fwd; also ESHAPE for n_out < 64. For both
- * directions M * max(n_out, k_in) must stay below 2^31.
+ * Errors as streamed_linear_fwd. For both directions M * max(n_out, k_in)
+ * must stay below 2^31 and the packed activation below 2^32 bytes.
  */
 int streamed_linear_bwd(const void* shard_dev, const nf4s_tensor_desc* d, const uint16_t* dy,
                         int64_t M, uint16_t* dx, const float* lora_du, const float* lora_A,
                         int r, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Activation packing. The matrix cores take their activation operand as
+ * 16-byte fragments (lane l: row l%32 of a 32-row block, 8 contraction values
+ * of a 16-wide block), so the GEMMs read it in that order: packed[(b*KB + s)
+ * *64 + l] = the 16 bytes of row 32b + l%32, columns 16s + 8(l/32) .. +8,
+ * with KB = 4*ceil(K/64), rows padded with zeros to a multiple of 256 and
+ * columns to a multiple of 64. The unpacked linear calls pack into their
+ * workspace on every call; a caller whose projections read the same input
+ * (q, k and v; gate and up) packs it once and calls the _packed variants.
+ *   nf4s_packed_activation_bytes: size of the packed form of a bf16 [M, K]
+ *     matrix (0 for M <= 0 or K not a positive multiple of 8).
+ *   nf4s_pack_activation: a bf16 [M, K] row-major (16-B aligned) -> packed
+ *     (256-B aligned, at least packed_bytes). Errors: EINVAL, ESHAPE, EALIGN,
+ *     EWORKSPACE.
+ */
+uint64_t nf4s_packed_activation_bytes(int64_t M, int64_t K);
+int nf4s_pack_activation(const uint16_t* a, int64_t M, int64_t K, void* packed, size_t packed_bytes,
+                         void* stream);
+
+/*
+ * streamed_linear_fwd / _bwd on an activation already packed with
+ * nf4s_pack_activation (x with K = k_in; dy with K = n_out) for the same M.
+ * ws: nf4s_workspace_bytes(NF4S_OP_LINEAR_FWD_PACKED / _BWD_PACKED) bytes
+ * (zero when the contraction is not split). Results are bit-identical to the
+ * unpacked calls. Errors as streamed_linear_fwd.
+ */
+int streamed_linear_fwd_packed(const void* shard_dev, const nf4s_tensor_desc* d,
+                               const void* x_packed, int64_t M, uint16_t* y, const float* lora_u,
+                               const float* lora_B, int r, float scale, void* ws, size_t ws_bytes,
+                               void* stream);
+int streamed_linear_bwd_packed(const void* shard_dev, const nf4s_tensor_desc* d,
+                               const void* dy_packed, int64_t M, uint16_t* dx,
+                               const float* lora_du, const float* lora_A, int r, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /*
  * LoRA down-projection, u = x.A^T in fp32 ([G] s2.1, adapter on q/v):

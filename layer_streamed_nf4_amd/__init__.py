@@ -21,6 +21,7 @@ OK, EINVAL, ESHAPE, EALIGN, ETABLE, EKEY, ESLOT, ENOTPINNED, EHIP, EWORKSPACE = 
     0, -1, -2, -3, -4, -5, -6, -7, -8, -9)
 DTYPE_F32, DTYPE_BF16 = 0, 1
 OP_QUANTIZE, OP_LINEAR_FWD, OP_LINEAR_BWD, OP_LORA_BWD, OP_LORA_FWD = 1, 2, 3, 4, 5
+OP_LINEAR_FWD_PACKED, OP_LINEAR_BWD_PACKED = 6, 7
 METHOD_NF4 = 1
 
 EXPORTS = (
@@ -30,6 +31,8 @@ EXPORTS = (
     "layer_prefetch", "nf4s_event_create", "nf4s_event_destroy", "nf4s_event_record",
     "nf4s_stream_wait_event", "nf4s_pool_create", "nf4s_pool_destroy", "nf4s_pool_set_layer",
     "nf4s_pool_prefetch", "nf4s_pool_acquire", "nf4s_pool_release", "nf4s_pool_stats",
+    "nf4s_packed_activation_bytes", "nf4s_pack_activation", "streamed_linear_fwd_packed",
+    "streamed_linear_bwd_packed",
 )
 
 
@@ -90,6 +93,13 @@ _SIG = {
     "nf4s_pool_acquire": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_P)]),
     "nf4s_pool_release": (ctypes.c_int, [_P, ctypes.c_int]),
     "nf4s_pool_stats": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)]),
+    "nf4s_packed_activation_bytes": (ctypes.c_uint64, [_I64, _I64]),
+    "nf4s_pack_activation": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_size_t, _P]),
+    "streamed_linear_fwd_packed": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P,
+                                                  _P, ctypes.c_int, ctypes.c_float, _P,
+                                                  ctypes.c_size_t, _P]),
+    "streamed_linear_bwd_packed": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P,
+                                                  _P, ctypes.c_int, _P, ctypes.c_size_t, _P]),
 }
 
 
@@ -163,6 +173,26 @@ def streamed_linear_fwd(shard, desc, x, M, y, lora_u, lora_B, r, scale, ws, ws_b
 def streamed_linear_bwd(shard, desc, dy, M, dx, lora_du, lora_A, r, ws, ws_bytes, stream=0):
     _check(lib().streamed_linear_bwd(shard, ctypes.byref(desc), dy, M, dx, lora_du, lora_A, r, ws,
                                      ws_bytes, stream))
+
+
+def nf4s_packed_activation_bytes(M, K):
+    return int(lib().nf4s_packed_activation_bytes(M, K))
+
+
+def nf4s_pack_activation(a, M, K, packed, packed_bytes, stream=0):
+    _check(lib().nf4s_pack_activation(a, M, K, packed, packed_bytes, stream))
+
+
+def streamed_linear_fwd_packed(shard, desc, x_packed, M, y, lora_u, lora_B, r, scale, ws, ws_bytes,
+                               stream=0):
+    _check(lib().streamed_linear_fwd_packed(shard, ctypes.byref(desc), x_packed, M, y, lora_u, lora_B,
+                                            r, scale, ws, ws_bytes, stream))
+
+
+def streamed_linear_bwd_packed(shard, desc, dy_packed, M, dx, lora_du, lora_A, r, ws, ws_bytes,
+                               stream=0):
+    _check(lib().streamed_linear_bwd_packed(shard, ctypes.byref(desc), dy_packed, M, dx, lora_du,
+                                            lora_A, r, ws, ws_bytes, stream))
 
 
 def lora_fwd(x, M, k_in, A, r, u_out, ws, ws_bytes, stream=0):

@@ -170,10 +170,14 @@ int nf4s_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, size_t*
       *bytes = quantize_ws_bytes(n_out, k_in);
       return NF4S_OK;
     case NF4S_OP_LINEAR_FWD:
-    case NF4S_OP_LINEAR_BWD: {
+    case NF4S_OP_LINEAR_BWD:
+    case NF4S_OP_LINEAR_FWD_PACKED:
+    case NF4S_OP_LINEAR_BWD_PACKED: {
       if (M <= 0) return fail(NF4S_ESHAPE, "M=%lld must be positive", (long long)M);
-      const bool bwd = op == NF4S_OP_LINEAR_BWD;
-      *bytes = plan_gemm(M, bwd ? k_in : n_out, bwd ? n_out : k_in).ws_bytes;
+      const bool bwd = op == NF4S_OP_LINEAR_BWD || op == NF4S_OP_LINEAR_BWD_PACKED;
+      const GemmPlan p = plan_gemm(M, bwd ? k_in : n_out, bwd ? n_out : k_in);
+      const bool packed = op == NF4S_OP_LINEAR_FWD_PACKED || op == NF4S_OP_LINEAR_BWD_PACKED;
+      *bytes = packed ? p.part_bytes : p.ws_bytes;
       return NF4S_OK;
     }
     case NF4S_OP_LORA_FWD:
@@ -220,22 +224,30 @@ int nf4_dequant(const void* shard_dev, const nf4s_tensor_desc* d, uint16_t* w_bf
   return e == hipSuccess ? NF4S_OK : hip_fail(e, "dequant launch");
 }
 
-static int linear_common(bool bwd, const void* shard_dev, const nf4s_tensor_desc* d,
-                         const uint16_t* a, int64_t M, uint16_t* out, const float* lora_l,
-                         const float* lora_r, int r, float scale, void* ws, size_t ws_bytes,
-                         void* stream) {
+// Packed activations are addressed with 32-bit offsets.
+static int check_packed_shape(int64_t M, int64_t K) {
+  if (M <= 0 || M > (1ll << 24)) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
+  if (K <= 0 || K % 8) return fail(NF4S_ESHAPE, "K=%lld must be a positive multiple of 8", (long long)K);
+  if (packed_activation_bytes(M, K) >= (1ull << 32))
+    return fail(NF4S_ESHAPE, "packed activation of %lldx%lld exceeds 32-bit offsets", (long long)M,
+                (long long)K);
+  return NF4S_OK;
+}
+
+// Shared validation of the linear calls; fills the plan.
+static int linear_checks(bool bwd, const void* shard_dev, const nf4s_tensor_desc* d, int64_t M,
+                         uint16_t* out, const float* lora_l, const float* lora_r, int r,
+                         float scale, GemmPlan* plan) {
   int rc;
   if ((rc = check_desc(d))) return rc;
   if (M <= 0 || M > (1ll << 24)) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
-  // the kernels address activations and packed weights with 32-bit offsets,
-  // and the backward's last contraction window needs n_out >= 64
+  // the kernels address outputs and packed weights with 32-bit offsets
   const int64_t widest = d->n_out > d->k_in ? d->n_out : d->k_in;
   if (M * widest >= (1ll << 31) || d->n_out * d->k_in >= (1ll << 33))
     return fail(NF4S_ESHAPE, "M=%lld with a %lldx%lld weight exceeds 32-bit offsets", (long long)M,
                 (long long)d->n_out, (long long)d->k_in);
-  if (bwd && d->n_out < 64) return fail(NF4S_ESHAPE, "backward needs n_out >= 64 (got %lld)", (long long)d->n_out);
+  if ((rc = check_packed_shape(M, bwd ? d->n_out : d->k_in))) return rc;
   if ((rc = check_ptr(shard_dev, "shard_dev", 256))) return rc;
-  if ((rc = check_ptr(a, bwd ? "dy" : "x"))) return rc;
   if ((rc = check_ptr(out, bwd ? "dx" : "y"))) return rc;
   if ((lora_l == nullptr) != (lora_r == nullptr))
     return fail(NF4S_EINVAL, "LoRA operands must be given together");
@@ -245,11 +257,59 @@ static int linear_common(bool bwd, const void* shard_dev, const nf4s_tensor_desc
     if ((rc = check_ptr(lora_r, bwd ? "lora_A" : "lora_B", 4))) return rc;
     if (!std::isfinite(scale)) return fail(NF4S_EINVAL, "scale is not finite");
   }
-  const GemmPlan p = plan_gemm(M, bwd ? d->k_in : d->n_out, bwd ? d->n_out : d->k_in);
+  *plan = plan_gemm(M, bwd ? d->k_in : d->n_out, bwd ? d->n_out : d->k_in);
+  return NF4S_OK;
+}
+
+static int linear_common(bool bwd, const void* shard_dev, const nf4s_tensor_desc* d,
+                         const uint16_t* a, int64_t M, uint16_t* out, const float* lora_l,
+                         const float* lora_r, int r, float scale, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int rc;
+  GemmPlan p;
+  if ((rc = linear_checks(bwd, shard_dev, d, M, out, lora_l, lora_r, r, scale, &p))) return rc;
+  if ((rc = check_ptr(a, bwd ? "dy" : "x"))) return rc;
   if ((rc = check_ws(ws, ws_bytes, p.ws_bytes))) return rc;
-  hipError_t e = launch_linear(bwd, resolve(shard_dev, d), d->n_out, d->k_in, a, M, out, lora_l,
-                               lora_r, lora_l ? r : 0, scale, ws, static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* packed = static_cast<uint8_t*>(ws);
+  hipError_t e = launch_pack(a, M, bwd ? d->n_out : d->k_in, packed, st);
+  if (e != hipSuccess) return hip_fail(e, "pack launch");
+  e = launch_linear_packed(bwd, resolve(shard_dev, d), d->n_out, d->k_in, packed, M, out, lora_l,
+                           lora_r, lora_l ? r : 0, scale, packed + p.frag_bytes, st);
   return e == hipSuccess ? NF4S_OK : hip_fail(e, "linear launch");
+}
+
+static int linear_packed(bool bwd, const void* shard_dev, const nf4s_tensor_desc* d,
+                         const void* a_packed, int64_t M, uint16_t* out, const float* lora_l,
+                         const float* lora_r, int r, float scale, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int rc;
+  GemmPlan p;
+  if ((rc = linear_checks(bwd, shard_dev, d, M, out, lora_l, lora_r, r, scale, &p))) return rc;
+  if ((rc = check_ptr(a_packed, bwd ? "dy_packed" : "x_packed", 256))) return rc;
+  if (p.part_bytes && (rc = check_ws(ws, ws_bytes, p.part_bytes))) return rc;
+  hipError_t e = launch_linear_packed(bwd, resolve(shard_dev, d), d->n_out, d->k_in,
+                                      static_cast<const uint8_t*>(a_packed), M, out, lora_l, lora_r,
+                                      lora_l ? r : 0, scale, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "linear launch");
+}
+
+uint64_t nf4s_packed_activation_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0 || K % 8) return 0;
+  return packed_activation_bytes(M, K);
+}
+
+int nf4s_pack_activation(const uint16_t* a, int64_t M, int64_t K, void* packed, size_t packed_bytes,
+                         void* stream) {
+  int rc;
+  if ((rc = check_packed_shape(M, K))) return rc;
+  if ((rc = check_ptr(a, "a"))) return rc;
+  if ((rc = check_ptr(packed, "packed", 256))) return rc;
+  const size_t need = packed_activation_bytes(M, K);
+  if (packed_bytes < need)
+    return fail(NF4S_EWORKSPACE, "packed buffer of %zu bytes needed, %zu given", need, packed_bytes);
+  hipError_t e = launch_pack(a, M, K, static_cast<uint8_t*>(packed), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "pack launch");
 }
 
 int streamed_linear_fwd(const void* shard_dev, const nf4s_tensor_desc* d, const uint16_t* x,
@@ -262,6 +322,22 @@ int streamed_linear_bwd(const void* shard_dev, const nf4s_tensor_desc* d, const 
                         int64_t M, uint16_t* dx, const float* lora_du, const float* lora_A, int r,
                         void* ws, size_t ws_bytes, void* stream) {
   return linear_common(true, shard_dev, d, dy, M, dx, lora_du, lora_A, r, 1.0f, ws, ws_bytes, stream);
+}
+
+int streamed_linear_fwd_packed(const void* shard_dev, const nf4s_tensor_desc* d,
+                               const void* x_packed, int64_t M, uint16_t* y, const float* lora_u,
+                               const float* lora_B, int r, float scale, void* ws, size_t ws_bytes,
+                               void* stream) {
+  return linear_packed(false, shard_dev, d, x_packed, M, y, lora_u, lora_B, r, scale, ws, ws_bytes,
+                       stream);
+}
+
+int streamed_linear_bwd_packed(const void* shard_dev, const nf4s_tensor_desc* d,
+                               const void* dy_packed, int64_t M, uint16_t* dx,
+                               const float* lora_du, const float* lora_A, int r, void* ws,
+                               size_t ws_bytes, void* stream) {
+  return linear_packed(true, shard_dev, d, dy_packed, M, dx, lora_du, lora_A, r, 1.0f, ws,
+                       ws_bytes, stream);
 }
 
 int lora_fwd(const uint16_t* x, int64_t M, int64_t k_in, const float* A, int r, float* u_out,

@@ -38,10 +38,13 @@ struct QPtrs {
 struct GemmPlan {
   int bm, bn;        // output tile
   int splits;        // split of the contraction (1 = none)
-  int64_t kc_chunk;  // contraction elements per split (multiple of 64)
-  size_t ws_bytes;   // fp32 partials when splits > 1
+  int64_t kc_chunk;   // contraction elements per split (multiple of 64)
+  size_t frag_bytes;  // packed activation (start of the workspace of the unpacked calls)
+  size_t part_bytes;  // fp32 partials when splits > 1
+  size_t ws_bytes;    // frag_bytes + part_bytes
 };
 GemmPlan plan_gemm(int64_t M, int64_t n_cols, int64_t k_contract);
+size_t packed_activation_bytes(int64_t M, int64_t K);
 
 // Kernel launchers (return hipError_t of the launch).
 hipError_t launch_quantize(const void* w, int dtype, int64_t n_out, int64_t k_in,
@@ -52,9 +55,11 @@ size_t quantize_ws_bytes(int64_t n_out, int64_t k_in);
 hipError_t launch_dequant(const QPtrs& q, int64_t n_out, int64_t k_in, uint16_t* out,
                           hipStream_t s);
 
-hipError_t launch_linear(bool backward, const QPtrs& q, int64_t n_out, int64_t k_in,
-                         const uint16_t* a, int64_t M, uint16_t* out, const float* lora_l,
-                         const float* lora_r, int r, float scale, void* ws, hipStream_t s);
+hipError_t launch_pack(const uint16_t* a, int64_t M, int64_t K, uint8_t* packed, hipStream_t s);
+hipError_t launch_linear_packed(bool backward, const QPtrs& q, int64_t n_out, int64_t k_in,
+                                const uint8_t* a_packed, int64_t M, uint16_t* out,
+                                const float* lora_l, const float* lora_r, int r, float scale,
+                                void* part_ws, hipStream_t s);
 
 hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t k_in, const float* A, int r,
                            float* u, void* ws, hipStream_t s);

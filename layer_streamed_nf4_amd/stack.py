@@ -20,11 +20,12 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import (DTYPE_F32, OP_LINEAR_BWD, OP_LINEAR_FWD, OP_LORA_BWD, OP_LORA_FWD, OP_QUANTIZE, lora_bwd,
-               lora_fwd, nf4_quantize_shard, nf4s_pool_acquire, nf4s_pool_create,
+from . import (DTYPE_F32, OP_LINEAR_BWD_PACKED, OP_LINEAR_FWD_PACKED, OP_LORA_BWD, OP_LORA_FWD,
+               OP_QUANTIZE, lora_bwd, lora_fwd, nf4_quantize_shard, nf4s_pack_activation,
+               nf4s_packed_activation_bytes, nf4s_pool_acquire, nf4s_pool_create,
                nf4s_pool_destroy, nf4s_pool_prefetch, nf4s_pool_release, nf4s_pool_set_layer,
-               nf4s_pool_stats, nf4s_tensor_layout, nf4s_workspace_bytes, streamed_linear_bwd,
-               streamed_linear_fwd)
+               nf4s_pool_stats, nf4s_tensor_layout, nf4s_workspace_bytes,
+               streamed_linear_bwd_packed, streamed_linear_fwd_packed)
 
 PROJ = ("q", "k", "v", "o", "gate", "up", "down")
 ALIGN = 256
@@ -125,13 +126,19 @@ class LinearStack:
         self.compute = torch.cuda.Stream()
         self.copy = torch.cuda.Stream()
         ws = 0
+        pk = 0
         for p in PROJ:
             n, k = shapes[p]
-            ws = max(ws, nf4s_workspace_bytes(OP_LINEAR_FWD, M, n, k),
-                     nf4s_workspace_bytes(OP_LINEAR_BWD, M, n, k),
+            ws = max(ws, nf4s_workspace_bytes(OP_LINEAR_FWD_PACKED, M, n, k),
+                     nf4s_workspace_bytes(OP_LINEAR_BWD_PACKED, M, n, k),
                      nf4s_workspace_bytes(OP_LORA_FWD, M, n, k),
                      nf4s_workspace_bytes(OP_LORA_BWD, M, n, k))
+            pk = max(pk, nf4s_packed_activation_bytes(M, k), nf4s_packed_activation_bytes(M, n))
         self.ws = torch.empty(_round_up(max(ws, ALIGN)), dtype=torch.uint8, device=dev)
+        # the activation of the current projection in the matrix cores' fragment
+        # order; projections that read the same input (q, k, v; gate, up) share it
+        self.packed = torch.empty(_round_up(pk), dtype=torch.uint8, device=dev)
+        self._packed_key = None
         # u = x . A^T per target, produced by the (re)computed forward of a layer
         # and consumed by that layer's backward
         self.u = {p: torch.empty((M, r), dtype=torch.float32, device=dev) for p in self.targets}
@@ -169,12 +176,24 @@ class LinearStack:
             store[key] = t
         return t
 
+    def _pack(self, a, K):
+        """Pack a (bf16 [M, K]) unless it is the input packed last; kernels run
+        in order on the compute stream, so one buffer serves all projections."""
+        key = (a.data_ptr(), K)
+        if key != self._packed_key:
+            nf4s_pack_activation(a.data_ptr(), self.M, K, self.packed.data_ptr(), self.packed.numel(),
+                                 self.compute.cuda_stream)
+            self._packed_key = key
+        return self.packed.data_ptr()
+
     def _layer_fwd(self, i, base, inputs, store_key):
         s = self.compute.cuda_stream
         shapes = self.sh.shapes
+        self._packed_key = None  # inputs may differ from layer to layer
         for p in PROJ:
             n, k = shapes[p]
             x = inputs(i, p)
+            xp = self._pack(x, k)
             y = self._out(self.y, (store_key(i), p), (self.M, n), torch.int16)
             if p in self.targets:
                 A, B = self.lora[i][p]
@@ -182,20 +201,21 @@ class LinearStack:
                 lora_fwd(x.data_ptr(), self.M, k, A.data_ptr(), self.r, u.data_ptr(),
                          self.ws.data_ptr(), self.ws.numel(), s)
                 ev = self._tick("fwd", n, k)
-                streamed_linear_fwd(base, self.sh.layout.descs[p], x.data_ptr(), self.M, y.data_ptr(),
-                                    u.data_ptr(), B.data_ptr(), self.r, self.scale,
-                                    self.ws.data_ptr(), self.ws.numel(), s)
+                streamed_linear_fwd_packed(base, self.sh.layout.descs[p], xp, self.M, y.data_ptr(),
+                                           u.data_ptr(), B.data_ptr(), self.r, self.scale,
+                                           self.ws.data_ptr(), self.ws.numel(), s)
                 self._tock(ev)
             else:
                 ev = self._tick("fwd", n, k)
-                streamed_linear_fwd(base, self.sh.layout.descs[p], x.data_ptr(), self.M, y.data_ptr(),
-                                    None, None, 0, 0.0, self.ws.data_ptr(), self.ws.numel(), s)
+                streamed_linear_fwd_packed(base, self.sh.layout.descs[p], xp, self.M, y.data_ptr(),
+                                           None, None, 0, 0.0, self.ws.data_ptr(), self.ws.numel(), s)
                 self._tock(ev)
 
     def _layer_bwd(self, i, base, inputs, grads):
         s = self.compute.cuda_stream
         shapes = self.sh.shapes
         key = i if self.keep else 0
+        self._packed_key = None
         for p in PROJ:
             n, k = shapes[p]
             x = inputs(i, p)
@@ -209,15 +229,17 @@ class LinearStack:
                 lora_bwd(x.data_ptr(), dy.data_ptr(), self.u[p].data_ptr(), self.M, k, n, B.data_ptr(),
                          self.r, self.scale, dA.data_ptr(), dB.data_ptr(), self.du.data_ptr(), 0,
                          self.ws.data_ptr(), self.ws.numel(), s)
+                dyp = self._pack(dy, n)
                 ev = self._tick("bwd", n, k)
-                streamed_linear_bwd(base, self.sh.layout.descs[p], dy.data_ptr(), self.M, dx.data_ptr(),
-                                    self.du.data_ptr(), A.data_ptr(), self.r, self.ws.data_ptr(),
-                                    self.ws.numel(), s)
+                streamed_linear_bwd_packed(base, self.sh.layout.descs[p], dyp, self.M, dx.data_ptr(),
+                                           self.du.data_ptr(), A.data_ptr(), self.r,
+                                           self.ws.data_ptr(), self.ws.numel(), s)
                 self._tock(ev)
             else:
+                dyp = self._pack(dy, n)
                 ev = self._tick("bwd", n, k)
-                streamed_linear_bwd(base, self.sh.layout.descs[p], dy.data_ptr(), self.M, dx.data_ptr(),
-                                    None, None, 0, self.ws.data_ptr(), self.ws.numel(), s)
+                streamed_linear_bwd_packed(base, self.sh.layout.descs[p], dyp, self.M, dx.data_ptr(),
+                                           None, None, 0, self.ws.data_ptr(), self.ws.numel(), s)
                 self._tock(ev)
 
     def _tick(self, direction, n, k):

@@ -178,3 +178,44 @@ def test_prefetch_and_pool_argument_errors():
     with pytest.raises(L.Nf4sError) as e:
         L.nf4s_pool_create([FAKE, FAKE], 1024, 1, 1)         # copy stream == compute stream
     assert e.value.code == L.EINVAL
+
+
+def test_packed_activation_bytes():
+    assert L.nf4s_packed_activation_bytes(512, 4096) == 512 * 4096 * 2
+    assert L.nf4s_packed_activation_bytes(300, 136) == 512 * 192 * 2
+    assert L.nf4s_packed_activation_bytes(1, 8) == 256 * 64 * 2
+    for M, K in ((0, 64), (16, 0), (16, 12), (-1, 64)):
+        assert L.nf4s_packed_activation_bytes(M, K) == 0
+
+
+def test_pack_and_packed_call_errors():
+    with pytest.raises(L.Nf4sError) as e:
+        L.nf4s_pack_activation(FAKE, 16, 12, FAKE, 1 << 20)          # K not a multiple of 8
+    assert e.value.code == L.ESHAPE
+    with pytest.raises(L.Nf4sError) as e:
+        L.nf4s_pack_activation(FAKE, 0, 64, FAKE, 1 << 20)
+    assert e.value.code == L.ESHAPE
+    with pytest.raises(L.Nf4sError) as e:
+        L.nf4s_pack_activation(FAKE, 16, 64, FAKE + 16, 1 << 20)     # packed buffer 256-B aligned
+    assert e.value.code == L.EALIGN
+    with pytest.raises(L.Nf4sError) as e:
+        L.nf4s_pack_activation(FAKE, 16, 64, FAKE, 1024)             # buffer too small
+    assert e.value.code == L.EWORKSPACE
+    d = _desc()
+    with pytest.raises(L.Nf4sError) as e:
+        L.streamed_linear_fwd_packed(FAKE, d, FAKE + 16, 16, FAKE, None, None, 0, 0.0, None, 0)
+    assert e.value.code == L.EALIGN
+    d.table_hash ^= 1
+    with pytest.raises(L.Nf4sError) as e:
+        L.streamed_linear_bwd_packed(FAKE, d, FAKE, 16, FAKE, None, None, 0, None, 0)
+    assert e.value.code == L.ETABLE
+
+
+def test_packed_workspace_is_split_partials_only():
+    # gate at M = 512: 112 x 2 output tiles fill the chip, no split, no scratch
+    assert L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, 512, 14336, 4096) == 0
+    # q at M = 512: 64 tiles, the contraction is split and partials are needed
+    need = L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, 512, 4096, 4096)
+    assert need > 0 and need % (512 * 4096 * 4) == 0
+    full = L.nf4s_workspace_bytes(L.OP_LINEAR_FWD, 512, 4096, 4096)
+    assert full == need + L.nf4s_packed_activation_bytes(512, 4096)

@@ -83,6 +83,9 @@ CASES = [
     ("q", 576, 576, 300),
     ("v", 192, 576, 1),
     ("o", 72, 128, 37),
+    # backward contractions shorter than one 64-step
+    ("k", 40, 64, 100),
+    ("o", 8, 128, 37),
 ]
 
 
@@ -149,3 +152,70 @@ def test_8b_shapes_sampled(proj, n, k):
         dx_ref += np.array([S * (dy[m] @ b) @ a[:, j] for m, j in zip(ms, ks)])
     assert linear.rel_err(got["y"][ms, ns], y_ref) <= TOL
     assert linear.rel_err(got["dx"][ms, ks], dx_ref) <= TOL
+
+
+def _pack_reference(a16, M, K):
+    """The documented packed layout, written out on the host: chunk
+    (b*KB + s)*64 + l holds row 32b + l%32, columns 16s + 8(l/32) .. +8."""
+    Mp, Kp = -(-M // 256) * 256, -(-K // 64) * 64
+    full = np.zeros((Mp, Kp), dtype=np.uint16)
+    full[:M, :K] = a16
+    out = np.empty(Mp * Kp, dtype=np.uint16)
+    KB = Kp // 16
+    pos = 0
+    for b in range(Mp // 32):
+        for s in range(KB):
+            for l in range(64):
+                out[pos:pos + 8] = full[32 * b + l % 32, 16 * s + 8 * (l // 32):16 * s + 8 * (l // 32) + 8]
+                pos += 8
+    return out
+
+
+@pytest.mark.parametrize("M,K", [(300, 136), (1, 8), (512, 576), (37, 72)])
+def test_pack_layout(M, K):
+    rng = np.random.Generator(np.random.PCG64(M * 1000 + K))
+    a16 = rng.integers(0, 1 << 16, size=(M, K), dtype=np.uint16)
+    nbytes = L.nf4s_packed_activation_bytes(M, K)
+    assert nbytes == (-(-M // 256) * 256) * (-(-K // 64) * 64) * 2
+    a = torch.from_numpy(a16.view(np.int16)).cuda()
+    packed = torch.full((nbytes,), 0x5A, dtype=torch.uint8, device="cuda")
+    L.nf4s_pack_activation(a.data_ptr(), M, K, packed.data_ptr(), nbytes, stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy().view(np.uint16), _pack_reference(a16, M, K))
+
+
+@pytest.mark.parametrize("proj,n,k,M,lora", [("q", 576, 576, 300, True), ("gate", 1536, 576, 512, False),
+                                              ("k", 40, 64, 100, True), ("q", 4096, 4096, 512, True)])
+def test_packed_calls_match_unpacked(proj, n, k, M, lora):
+    """The _packed entry points on nf4s_pack_activation output give the same
+    bits as the calls that pack internally (both contract the same operands
+    in the same order)."""
+    c = _setup(proj, n, k, M)
+    ref = _run(c, lora)
+    s = stream()
+    x, dy = dev_bf16bits(c["x"]), dev_bf16bits(c["dy"])
+    A, B = dev_f32(c["a"]), dev_f32(c["b"])
+    y = torch.empty((M, n), dtype=torch.int16, device="cuda")
+    dx = torch.empty((M, k), dtype=torch.int16, device="cuda")
+    xp = ws_tensor(L.nf4s_packed_activation_bytes(M, k))
+    dyp = ws_tensor(L.nf4s_packed_activation_bytes(M, n))
+    wsf = ws_tensor(L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, M, n, k))
+    wsb = ws_tensor(L.nf4s_workspace_bytes(L.OP_LINEAR_BWD_PACKED, M, n, k))
+    L.nf4s_pack_activation(x.data_ptr(), M, k, xp.data_ptr(), xp.numel(), s)
+    L.nf4s_pack_activation(dy.data_ptr(), M, n, dyp.data_ptr(), dyp.numel(), s)
+    sp = c["shard"].data_ptr()
+    if lora:
+        u = torch.from_numpy(np.ascontiguousarray(ref["u"])).cuda()
+        du = torch.from_numpy(np.ascontiguousarray(ref["du"])).cuda()
+        L.streamed_linear_fwd_packed(sp, c["d"], xp.data_ptr(), M, y.data_ptr(), u.data_ptr(),
+                                     B.data_ptr(), R, S, wsf.data_ptr(), wsf.numel(), s)
+        L.streamed_linear_bwd_packed(sp, c["d"], dyp.data_ptr(), M, dx.data_ptr(), du.data_ptr(),
+                                     A.data_ptr(), R, wsb.data_ptr(), wsb.numel(), s)
+    else:
+        L.streamed_linear_fwd_packed(sp, c["d"], xp.data_ptr(), M, y.data_ptr(), None, None, 0, 0.0,
+                                     wsf.data_ptr(), wsf.numel(), s)
+        L.streamed_linear_bwd_packed(sp, c["d"], dyp.data_ptr(), M, dx.data_ptr(), None, None, 0,
+                                     wsb.data_ptr(), wsb.numel(), s)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(y), np.asarray(ref["y"], dtype=np.float32).view(np.uint32) >> 16)
+    assert np.array_equal(host_u16(dx), np.asarray(ref["dx"], dtype=np.float32).view(np.uint32) >> 16)

@@ -15,10 +15,11 @@
 // and written to LDS as bf16 in the contraction-major layout the matrix cores
 // read; W' never goes back to HBM. A packed byte holds two codes, and one LDS
 // read of a 256-entry table gives both of their NF4 levels; the table is
-// replicated 16 times so that lane l always reads the copy that lives in bank
-// pair (2(l%16), 2(l%16)+1), which makes the random lookups conflict-free.
+// replicated 32 times so that lane l always reads the copy that lives in bank
+// pair (2(l%32), 2(l%32)+1) of the 64 LDS banks, which makes the random
+// lookups of a half-wave conflict-free.
 // The backward orientation is transposed on the way into LDS for free: a
-// thread decodes a 2x8 patch and pairs values along the contraction when it
+// thread decodes a 4x8 patch and pairs values along the contraction when it
 // packs bf16.
 //
 // Tiling for gfx950, sized by its LDS bandwidth (about 128 B per clock per
@@ -27,19 +28,22 @@
 // wave leaves between its MFMAs:
 //  * output tile 256x128 per workgroup, contraction step 64 (one NF4 block per
 //    weight row in the forward direction), v_mfma_f32_32x32x16_bf16;
-//  * 512 threads = 8 waves, two per SIMD. Waves w and w+4 own the same 64
-//    output rows x all 128 columns (2x4 MFMA tiles, 128 fp32 accumulators per
-//    lane) and split every step's contraction: w takes sub-steps 0-1, w+4
-//    sub-steps 2-3. Their accumulators are summed through LDS once, at the
-//    end. Each SIMD thus runs 32 MFMAs per step from two waves, so one wave's
-//    decode work and waits overlap the other's matrix work;
+//  * 512 threads = 8 waves, two per SIMD, with split roles. Waves 0-3 are the
+//    consumers: each owns 64 output rows x all 128 columns (2x4 MFMA tiles,
+//    128 fp32 accumulators per lane) and only loads its activation fragments
+//    and multiplies. Waves 4-7 are the producers: they only stream the packed
+//    weights and decode them into LDS. Every SIMD thus runs one wave of each
+//    kind, so the decode's vector work and LDS waits overlap the other wave's
+//    matrix work instead of competing with it step for step;
 //  * the activation operand never touches LDS: a first kernel rewrites it in
-//    MFMA fragment order (k_frag_pack), and each wave loads its fragments
-//    with contiguous 1 KB reads into a register ring two steps ahead;
-//  * the decoded weights go through a three-stage LDS ring: step s multiplies
-//    stage s, decodes stage s+2 and, before its barrier, already reads the
-//    first fragments of stage s+1, so the matrix cores restart without an
-//    LDS round trip after the barrier.
+//    MFMA fragment order (k_frag_pack), and each consumer loads its fragments
+//    with contiguous 1 KB reads; a sub-step's registers are refilled for the
+//    step two ahead as soon as its MFMAs are issued;
+//  * the decoded weights go through a four-stage LDS ring with one barrier
+//    per step: in step s the consumers multiply stage s and, before the
+//    barrier, read the first fragments of stage s+1; the producers finish
+//    stage s+2 from table lookups issued in step s-1, issue the lookups of
+//    stage s+3, and fetch the packed codes of stage s+5.
 // LDS traffic per step: 64 KB of weight fragments, 32 KB of table lookups and
 // 16 KB of decoded stores, against 1024 MFMA cycles per SIMD.
 // LDS rows are padded to 144 B so the 16-byte fragment reads of 8 consecutive
@@ -58,17 +62,16 @@ namespace {
 constexpr int BM = 256;
 constexpr int BN = 128;
 constexpr int BK = 64;
-constexpr int WAVES = 8;
-constexpr int THREADS = 64 * WAVES;
-constexpr int WAVE_ROWS = 64;         // output rows per wave (waves w and w+4 share them)
-constexpr int NSTAGE = 3;             // LDS ring of decoded weight stages
+constexpr int CONSUMERS = 4;          // waves 0-3 multiply, waves 4-7 decode
+constexpr int THREADS = 64 * 2 * CONSUMERS;
+constexpr int WAVE_ROWS = BM / CONSUMERS;  // 64 output rows per consumer wave
+constexpr int NSTAGE = 4;             // LDS ring of decoded weight stages
 constexpr int LDS_STRIDE = 72;        // bf16 elements per LDS row (64 + 8 pad = 144 B)
 constexpr int STAGE_ELEMS = BN * LDS_STRIDE;
-constexpr int PAIR_COPIES = 16;
+constexpr int PAIR_COPIES = 32;
 constexpr int SMEM_BYTES = NSTAGE * STAGE_ELEMS * 2 + 256 * PAIR_COPIES * 8 + 256 * 4;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct GemmArgs {
   const uint8_t* packed;
@@ -132,21 +135,19 @@ __global__ __launch_bounds__(256) void k_frag_pack(const uint16_t* __restrict__ 
 }
 
 struct AFrags {
-  u32x4 f[2][2];  // [row tile i][own sub-step]
+  u32x4 f[2][4];  // [row tile i][sub-step kk]
 };
 
 struct ALanes {
   uint32_t off[2];  // byte offsets of the lane's chunk in its two 32-row blocks at contraction 0
 };
 
-// Wave rows: group g = wave % 4; contraction half h = wave / 4.
-__device__ __forceinline__ ALanes a_lanes(const GemmArgs& g, int64_t m0, int grp, int half,
-                                          int lane) {
+__device__ __forceinline__ ALanes a_lanes(const GemmArgs& g, int64_t m0, int wave, int lane) {
   ALanes L;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int64_t blk = (m0 + grp * WAVE_ROWS + i * 32) / 32;
-    L.off[i] = (uint32_t)(blk * g.kblocks * FRAG_BYTES + (2 * half) * FRAG_BYTES + lane * 16);
+    const int64_t blk = (m0 + wave * WAVE_ROWS + i * 32) / 32;
+    L.off[i] = (uint32_t)(blk * g.kblocks * FRAG_BYTES + lane * 16);
   }
   return L;
 }
@@ -157,77 +158,78 @@ __device__ __forceinline__ void load_a(const GemmArgs& g, const ALanes& L, int64
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < 4; ++kk)
       r.f[i][kk] = *reinterpret_cast<const u32x4*>(base + L.off[i] + kk * FRAG_BYTES);
 }
 
-// ---- weight tile (B) ------------------------------------------------------
+// ---- weight tile (B), producer side ---------------------------------------
+// pt = producer thread index 0..255.
 template <bool BWD>
 struct WLanes;
 template <bool BWD>
 struct BRegs;
 
-// Forward: thread t owns weight row n0 + t/4 and contraction quarter t%4
-// (16 codes, two packed words).
+// Forward: producer thread pt owns weight row n0 + pt/2 and contraction half
+// pt%2 (32 codes, four packed words).
 template <>
 struct WLanes<false> {
-  uint32_t woff;  // byte offset of the thread's 8 packed bytes at contraction 0
+  uint32_t woff;  // byte offset of the thread's 16 packed bytes at contraction 0
   uint32_t blk0;  // 64-block index at contraction 0
   bool valid;     // row < n_out
 };
 template <>
 struct BRegs<false> {
-  u32x2 w;
+  u32x4 w;
   uint32_t q;
   float nest;
 };
 
-__device__ __forceinline__ WLanes<false> w_lanes_fwd(const GemmArgs& g, int64_t n0) {
-  const int t = threadIdx.x;
+__device__ __forceinline__ WLanes<false> w_lanes(const GemmArgs& g, int64_t n0, int pt,
+                                                 WLanes<false>*) {
   WLanes<false> L;
-  int64_t n = n0 + (t >> 2);
+  int64_t n = n0 + (pt >> 1);
   L.valid = n < g.n_out;
   n = L.valid ? n : g.n_out - 1;
-  L.woff = (uint32_t)(n * (g.k_in / 2) + (t & 3) * 8);
+  L.woff = (uint32_t)(n * (g.k_in / 2) + (pt & 1) * 16);
   L.blk0 = (uint32_t)(n * (g.k_in / 64));
   return L;
 }
 
-__device__ __forceinline__ void load_b(const GemmArgs& g, const WLanes<false>& L, Step s,
+__device__ __forceinline__ void load_b(const GemmArgs& g, const WLanes<false>& L, Step s, int,
                                        BRegs<false>& rb) {
-  rb.w = *reinterpret_cast<const u32x2*>(g.packed + s.k0 / 2 + L.woff);
+  rb.w = *reinterpret_cast<const u32x4*>(g.packed + s.k0 / 2 + L.woff);
   const uint32_t blk = L.blk0 + (uint32_t)(s.k0 / 64);
   rb.q = g.q8[blk];
   rb.nest = g.nested[blk >> 8];
 }
 
-// Backward: thread t owns weight rows k0 + 2*(t/16) + i (i < 2) and output
-// columns n0 + 8*(t%16) + j (j < 8): two packed words, two 8-bit scale codes
-// packed in one register, two nested scales, a 2-bit validity mask.
+// Backward: producer thread pt owns weight rows k0 + 4*(pt/16) + i (i < 4) and
+// output columns n0 + 8*(pt%16) + j (j < 8): four packed words, four 8-bit
+// scale codes packed in one register, four nested scales, a validity mask.
 template <>
 struct WLanes<true> {
-  uint32_t woff[2];  // byte offsets of the packed words at contraction 0
-  uint32_t blk0[2];  // 64-block indices at contraction 0
+  uint32_t woff[4];  // byte offsets of the packed words at contraction 0
+  uint32_t blk0[4];  // 64-block indices at contraction 0
   uint32_t col;      // first (clamped) column
   bool cvalid;       // columns < k_in
 };
 template <>
 struct BRegs<true> {
-  uint32_t w[2];
+  uint32_t w[4];
   uint32_t q;
-  float nest[2];
+  float nest[4];
   uint32_t vmask;
 };
 
-__device__ __forceinline__ WLanes<true> w_lanes_bwd(const GemmArgs& g, int64_t n0) {
-  const int t = threadIdx.x;
+__device__ __forceinline__ WLanes<true> w_lanes(const GemmArgs& g, int64_t n0, int pt,
+                                                WLanes<true>*) {
   WLanes<true> L;
-  int64_t col = n0 + 8 * (t & 15);
+  int64_t col = n0 + 8 * (pt & 15);
   L.cvalid = col < g.k_in;
   col = L.cvalid ? col : g.k_in - 8;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t row = 2 * (t >> 4) + i;  // relative to the step's start
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = 4 * (pt >> 4) + i;  // relative to the step's start
     L.woff[i] = (uint32_t)((row * g.k_in + col) / 2);
     L.blk0[i] = (uint32_t)((row * g.k_in + col) / 64);
   }
@@ -235,26 +237,25 @@ __device__ __forceinline__ WLanes<true> w_lanes_bwd(const GemmArgs& g, int64_t n
   return L;
 }
 
-__device__ __forceinline__ void load_b(const GemmArgs& g, const WLanes<true>& L, Step s,
+__device__ __forceinline__ void load_b(const GemmArgs& g, const WLanes<true>& L, Step s, int pt,
                                        BRegs<true>& rb) {
-  const int t = threadIdx.x;
   rb.q = 0;
   if (s.k0 + BK <= g.Kc) {  // uniform: every row of the step exists
     const uint8_t* base = g.packed + s.k0 * (g.k_in / 2);
     const uint32_t bstep = (uint32_t)(s.k0 * (g.k_in / 64));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
       rb.w[i] = *reinterpret_cast<const uint32_t*>(base + L.woff[i]);
       const uint32_t blk = bstep + L.blk0[i];
       rb.q |= (uint32_t)g.q8[blk] << (8 * i);
       rb.nest[i] = g.nested[blk >> 8];
     }
-    rb.vmask = L.cvalid ? 0x3u : 0u;
+    rb.vmask = L.cvalid ? 0xFu : 0u;
   } else {  // the last step of a contraction that is not a multiple of 64
     rb.vmask = 0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t row = s.k0 + 2 * (t >> 4) + i;
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = s.k0 + 4 * (pt >> 4) + i;
       const bool ok = row < g.Kc;
       const int64_t e = (ok ? row : g.Kc - 1) * g.k_in + L.col;  // code index
       rb.w[i] = *reinterpret_cast<const uint32_t*>(g.packed + e / 2);
@@ -269,66 +270,44 @@ __device__ __forceinline__ void load_b(const GemmArgs& g, const WLanes<true>& L,
 // ---- decoding -------------------------------------------------------------
 // Pair table: entry b = (C4[b >> 4], C4[b & 15]), both levels of a packed byte,
 // the even element (high nibble) first. Copy c of entry b sits at float2 index
-// 16*b + c, i.e. dwords 32*b + 2c and 32*b + 2c + 1: the copy fixes the LDS
+// 32*b + c, i.e. dwords 64*b + 2c and 64*b + 2c + 1: the copy fixes the LDS
 // bank pair whatever b is. `ptab` below is already offset by the lane's copy.
 __device__ __forceinline__ float2 pair_of(const float2* ptab, uint32_t word, int byte) {
   return ptab[((word >> (8 * byte)) & 0xFFu) * PAIR_COPIES];
 }
 
-// All table reads of a stage are issued together, ahead of the arithmetic
-// that consumes them, so their LDS latencies overlap.
-struct Pairs {
-  float2 v[8];  // forward: [word * 4 + byte]; backward: [byte * 2 + row]
+// The LDS reads of a stage's decode (scale-code lookups and pair table) are
+// issued one step before the arithmetic that consumes them, so the producer
+// never waits on LDS latency inside a step.
+template <int NR>
+struct Prep {
+  float2 v[16];  // forward: [word * 4 + byte]; backward: [byte * 4 + row]
+  float c8v[NR];
 };
 
-__device__ __forceinline__ float stage_scale(const BRegs<false>& rb, bool valid, float off,
-                                             const float* c8) {
-  const float a = decode_scale(c8[rb.q], rb.nest, off);
-  return valid ? a : 0.0f;
+__device__ __forceinline__ void prep_reads(const BRegs<false>& rb, const float2* ptab,
+                                           const float* c8, Prep<1>& pp) {
+  pp.c8v[0] = c8[rb.q];
+#pragma unroll
+  for (int jw = 0; jw < 4; ++jw)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) pp.v[jw * 4 + p] = pair_of(ptab, rb.w[jw], p);
 }
 
-__device__ __forceinline__ void load_pairs(const BRegs<false>& rb, const float2* ptab, Pairs& pr) {
+// Forward stage: the producer thread's 32 codes -> 32 bf16 of its weight row.
+__device__ __forceinline__ void finish_stage(uint16_t* Bs, const BRegs<false>& rb, const Prep<1>& pp,
+                                             bool valid, float off, int pt) {
+  const float a = valid ? decode_scale(pp.c8v[0], rb.nest, off) : 0.0f;
 #pragma unroll
-  for (int jw = 0; jw < 2; ++jw)
-#pragma unroll
-    for (int p = 0; p < 4; ++p) pr.v[jw * 4 + p] = pair_of(ptab, rb.w[jw], p);
-}
-
-// Forward stage: the thread's 16 codes -> 16 bf16 of its weight row in LDS.
-__device__ __forceinline__ void store_b(uint16_t* Bs, const Pairs& pr, float a) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int jw = 0; jw < 2; ++jw) {
+  for (int jw = 0; jw < 4; ++jw) {
     u32x4 o;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const float2 c = pr.v[jw * 4 + p];
+      const float2 c = pp.v[jw * 4 + p];
       o[p] = pack_bf16x2(__fmul_rn(c.x, a), __fmul_rn(c.y, a));
     }
-    *reinterpret_cast<u32x4*>(Bs + (t >> 2) * LDS_STRIDE + (t & 3) * 16 + jw * 8) = o;
+    *reinterpret_cast<u32x4*>(Bs + (pt >> 1) * LDS_STRIDE + (pt & 1) * 32 + jw * 8) = o;
   }
-}
-
-struct Scales2 {
-  float a[2];
-};
-
-__device__ __forceinline__ Scales2 stage_scale(const BRegs<true>& rb, bool, float off,
-                                               const float* c8) {
-  Scales2 s;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float a = decode_scale(c8[(rb.q >> (8 * i)) & 0xFFu], rb.nest[i], off);
-    s.a[i] = ((rb.vmask >> i) & 1u) ? a : 0.0f;
-  }
-  return s;
-}
-
-__device__ __forceinline__ void load_pairs(const BRegs<true>& rb, const float2* ptab, Pairs& pr) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) pr.v[q * 2 + i] = pair_of(ptab, rb.w[i], q);
 }
 
 // Backward LDS layout: stage[col][k] with the 16-byte chunk k/8 of column col
@@ -337,22 +316,43 @@ __device__ __forceinline__ int bwd_swizzle_off(int col, int k) {
   return ((((k >> 3) ^ (col >> 3)) & 7) << 3) | (k & 7);
 }
 
-// Backward stage: byte q of each of the thread's two row words gives output
-// columns 2q and 2q+1 of its 2x8 patch, each written as 2 consecutive
+__device__ __forceinline__ void prep_reads(const BRegs<true>& rb, const float2* ptab,
+                                           const float* c8, Prep<4>& pp) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pp.c8v[i] = c8[(rb.q >> (8 * i)) & 0xFFu];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pp.v[q * 4 + i] = pair_of(ptab, rb.w[i], q);
+}
+
+// Backward stage: byte q of each of the thread's four row words gives output
+// columns 2q and 2q+1 of its 4x8 patch, each written as 4 consecutive
 // contraction values -- the transpose into the matrix-core layout happens
 // here, in the bf16 pairing.
-__device__ __forceinline__ void store_b(uint16_t* Bs, const Pairs& pr, const Scales2& sc) {
-  const int t = threadIdx.x;
-  const int r0 = 2 * (t >> 4);
+__device__ __forceinline__ void finish_stage(uint16_t* Bs, const BRegs<true>& rb, const Prep<4>& pp,
+                                             bool, float off, int pt) {
+  float a[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    a[i] = ((rb.vmask >> i) & 1u) ? decode_scale(pp.c8v[i], rb.nest[i], off) : 0.0f;
+  const int r0 = 4 * (pt >> 4);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float2 c0 = pr.v[q * 2 + 0];
-    const float2 c1 = pr.v[q * 2 + 1];
-    const int cb = 8 * (t & 15) + 2 * q;
-    const uint32_t p0 = pack_bf16x2(__fmul_rn(c0.x, sc.a[0]), __fmul_rn(c1.x, sc.a[1]));
-    const uint32_t p1 = pack_bf16x2(__fmul_rn(c0.y, sc.a[0]), __fmul_rn(c1.y, sc.a[1]));
-    *reinterpret_cast<uint32_t*>(Bs + cb * LDS_STRIDE + bwd_swizzle_off(cb, r0)) = p0;
-    *reinterpret_cast<uint32_t*>(Bs + (cb + 1) * LDS_STRIDE + bwd_swizzle_off(cb + 1, r0)) = p1;
+    float v0[4], v1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v0[i] = __fmul_rn(pp.v[q * 4 + i].x, a[i]);
+      v1[i] = __fmul_rn(pp.v[q * 4 + i].y, a[i]);
+    }
+    const int cb = 8 * (pt & 15) + 2 * q;
+    uint2 p0, p1;
+    p0.x = pack_bf16x2(v0[0], v0[1]);
+    p0.y = pack_bf16x2(v0[2], v0[3]);
+    p1.x = pack_bf16x2(v1[0], v1[1]);
+    p1.y = pack_bf16x2(v1[2], v1[3]);
+    *reinterpret_cast<uint2*>(Bs + cb * LDS_STRIDE + bwd_swizzle_off(cb, r0)) = p0;
+    *reinterpret_cast<uint2*>(Bs + (cb + 1) * LDS_STRIDE + bwd_swizzle_off(cb + 1, r0)) = p1;
   }
 }
 
@@ -375,13 +375,6 @@ __device__ __forceinline__ bf16x8_t f32x8_to_bf16(const float* v) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
-__device__ __forceinline__ WLanes<false> w_lanes(const GemmArgs& g, int64_t n0, WLanes<false>*) {
-  return w_lanes_fwd(g, n0);
-}
-__device__ __forceinline__ WLanes<true> w_lanes(const GemmArgs& g, int64_t n0, WLanes<true>*) {
-  return w_lanes_bwd(g, n0);
-}
-
 // SPLIT selects the output path (fp32 partials vs bf16 result) at compile time,
 // so the two variants also carry distinct kernel names in profiles.
 template <bool BWD, bool SPLIT>
@@ -398,35 +391,26 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
     for (int c = 0; c < PAIR_COPIES; ++c) s_pair_all[t * PAIR_COPIES + c] = e;
     s_c8[t] = tab.c8[t];
   }
-  const float2* s_pair = s_pair_all + (t & (PAIR_COPIES - 1));
 
-  const int64_t n0 = (int64_t)blockIdx.x * BN;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int split = blockIdx.z;
+  // XCD-aware tile order. Workgroups are dealt to the 8 XCDs round-robin in
+  // launch order; give each XCD a contiguous run of tile indices instead, so
+  // that the workgroups sharing an L2 also share their activation rows (one
+  // 256-row tile of A per XCD at the gate shapes) and their weight columns.
+  const int ntx = (int)gridDim.x, nty = (int)gridDim.y;
+  const int total = ntx * nty * (int)gridDim.z;
+  const int lin = (int)blockIdx.x + ntx * ((int)blockIdx.y + nty * (int)blockIdx.z);
+  const int xcd = lin % 8, kth = lin / 8;
+  const int tile = xcd * (total / 8) + (xcd < total % 8 ? xcd : total % 8) + kth;
+  const int64_t n0 = (int64_t)(tile % ntx) * BN;
+  const int64_t m0 = (int64_t)((tile / ntx) % nty) * BM;
+  const int split = tile / (ntx * nty);
   const int64_t kb = split * g.kc_chunk;
   const int64_t ke = (kb + g.kc_chunk < g.Kc) ? kb + g.kc_chunk : g.Kc;
   const int nk = (int)((ke - kb + BK - 1) / BK);
-  const float off = g.offset[0];
-
-  const int wave = t >> 6;
-  const int grp = wave & 3;   // 64-row group of the tile
-  const int half = wave >> 2;  // contraction half of every step
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: role branches are scalar
   const int lane = t & 63;
   const int lrow = lane & 31;
   const int lk = (lane >> 5) * 8;
-
-  f32x16_t acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  const ALanes al = a_lanes(g, m0, grp, half, lane);
-  const WLanes<BWD> wl = w_lanes(g, n0, static_cast<WLanes<BWD>*>(nullptr));
-  bool fwd_valid = true;
-  if constexpr (!BWD) fwd_valid = wl.valid;
 
   // step kt (clamped to the last one for prefetches past the end)
   auto step_of = [&](int kt) {
@@ -436,176 +420,185 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
     return s;
   };
   auto stage = [&](int st) { return Bs0 + st * STAGE_ELEMS; };
-  auto decode = [&](uint16_t* bs, const BRegs<BWD>& W) {
-    const auto sc = stage_scale(W, fwd_valid, off, s_c8);
-    Pairs pr;
-    load_pairs(W, s_pair, pr);
-    store_b(bs, pr, sc);
-  };
 
-  // Pipeline: activation stage k lives in register slot k%3 and is fetched two
-  // steps before use; weight stage k lives in register slot k%3, is fetched
-  // two steps before it is decoded, and is decoded into LDS stage k%3 two
-  // steps before the matrix cores read it.
-  BRegs<BWD> wb0, wb1, wb2;
-  AFrags ar0, ar1, ar2;
-  load_b(g, wl, step_of(0), wb0);
-  load_b(g, wl, step_of(1), wb1);
-  load_b(g, wl, step_of(2), wb2);
-  load_a(g, al, step_of(0).k0, ar0);
-  load_a(g, al, step_of(1).k0, ar1);
-  __syncthreads();  // tables in LDS
-  decode(stage(0), wb0);
-  load_b(g, wl, step_of(3), wb0);
-  decode(stage(1), wb1);
-  __syncthreads();
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int kk0 = 2 * half;  // the wave's first sub-step
-  bf16x8_t fb0[4];           // its fragments of the stage about to be multiplied
+  // Both roles pass the same barriers: 2 in the prologue, 1 per step.
+  if (wave < CONSUMERS) {
+    // ---- consumer: activation stage k in register slot k%2; sub-step kk of
+    // stage k+2 is fetched into the slot as soon as the MFMAs of sub-step kk
+    // of stage k are issued
+    const ALanes al = a_lanes(g, m0, wave, lane);
+    AFrags ar0, ar1;
+    load_a(g, al, step_of(0).k0, ar0);
+    load_a(g, al, step_of(1).k0, ar1);
+    __syncthreads();  // tables in LDS
+    __syncthreads();  // weight stages 0 and 1 decoded
+    bf16x8_t fb0[4];  // fragments of sub-step 0 of the stage about to be multiplied
 #pragma unroll
-  for (int j = 0; j < 4; ++j) fb0[j] = b_frag<BWD>(stage(0), lane, j, kk0);
+    for (int j = 0; j < 4; ++j) fb0[j] = b_frag<BWD>(stage(0), lane, j, 0);
 
-  auto mfma_kk = [&](const AFrags& A, int kk, const bf16x8_t* fb) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, A.f[i][kk]), fb[j], acc[i][j], 0, 0, 0);
-  };
-
-  // One step: multiply the wave's two sub-steps of LDS stage `bs` (the first
-  // one's fragments already in fb0), decode weight registers `W` into LDS
-  // stage `bdec`, and read the first fragments of the next stage `bnext`.
-  auto compute = [&](const uint16_t* bs, uint16_t* bdec, const uint16_t* bnext, const AFrags& A,
-                     const BRegs<BWD>& W) {
-    const auto sc = stage_scale(W, fwd_valid, off, s_c8);
-    Pairs pr;
-    load_pairs(W, s_pair, pr);
-    bf16x8_t fb1[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb1[j] = b_frag<BWD>(bs, lane, j, kk0 + 1);
-    mfma_kk(A, 0, fb0);
-    store_b(bdec, pr, sc);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb0[j] = b_frag<BWD>(bnext, lane, j, kk0);
-    mfma_kk(A, 1, fb1);
-  };
-
-  // One step over named ring registers (a macro, so nothing is address-taken
-  // and every ring slot stays in VGPRs). SM = step % 3.
-#define NF4S_GEMM_STEP(KT, SM, ACUR, ALD, WDEC, WLD)                                  \
-  do {                                                                                \
-    const int kt_ = (KT);                                                             \
-    load_a(g, al, step_of(kt_ + 2).k0, ALD);                                          \
-    load_b(g, wl, step_of(kt_ + 4), WLD);                                             \
-    __builtin_amdgcn_sched_barrier(0);                                                \
-    compute(stage(SM), stage(((SM) + 2) % 3), stage(((SM) + 1) % 3), ACUR, WDEC);     \
-    __syncthreads();                                                                  \
-  } while (0)
-
-  const int nk3 = nk - nk % 3;
-  for (int kt = 0; kt < nk3; kt += 3) {
-    NF4S_GEMM_STEP(kt, 0, ar0, ar2, wb2, wb1);
-    NF4S_GEMM_STEP(kt + 1, 1, ar1, ar0, wb0, wb2);
-    NF4S_GEMM_STEP(kt + 2, 2, ar2, ar1, wb1, wb0);
-  }
-  if (nk3 < nk) NF4S_GEMM_STEP(nk3, 0, ar0, ar2, wb2, wb1);
-  if (nk3 + 1 < nk) NF4S_GEMM_STEP(nk3 + 1, 1, ar1, ar0, wb0, wb2);
-#undef NF4S_GEMM_STEP
-
-  // Sum the two contraction halves through LDS (the weight ring is free now):
-  // the wave of half h finishes column tiles j = 2h, 2h+1, so it hands the
-  // other two to its partner. Exchange slot of a tile: 16 registers x 64 lanes.
-  {
-    float* xch = reinterpret_cast<float*>(smem);
-    auto slot = [&](int g4, int i, int jj, int r) { return ((((g4 * 2 + i) * 2 + jj) * 16 + r) * 64 + lane); };
-    // round h: the half-(1-h) waves export tiles j = 2h + jj, the half-h waves add them
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (half != h) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) xch[slot(grp, i, jj, r)] = acc[i][2 * h + jj][r];
-      }
-      __syncthreads();
-      if (half == h) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][2 * h + jj][r] += xch[slot(grp, i, jj, r)];
-      }
-      __syncthreads();
-    }
-  }
-
-  // From here each wave owns row tiles i = 0, 1 of its group and column tiles
-  // j = 2*half + jj.
-  // LoRA term, contracted on the matrix cores in chunks of 16 over the rank:
-  // forward  + u[m, :] . (s * B[n, :]),  backward + du[m, :] . A[:, n].
-  if (g.lora_l != nullptr && split == 0) {
-    for (int r0 = 0; r0 < g.r; r0 += 16) {
-      bf16x8_t fa[2], fb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int64_t row = m0 + grp * WAVE_ROWS + i * 32 + lrow;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int rr = r0 + lk + e;
-          v[e] = (row < g.M && rr < g.r) ? g.lora_l[row * g.r + rr] : 0.0f;
-        }
-        fa[i] = f32x8_to_bf16(v);
-      }
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int64_t col = n0 + (2 * half + jj) * 32 + lrow;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int rr = r0 + lk + e;
-          float x = 0.0f;
-          if (col < g.Nc && rr < g.r)
-            x = BWD ? g.lora_r[(int64_t)rr * g.k_in + col] : g.scale * g.lora_r[col * g.r + rr];
-          v[e] = x;
-        }
-        fb[jj] = f32x8_to_bf16(v);
-      }
+    auto mfma_kk = [&](const AFrags& A, int kk, const bf16x8_t* fb) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          f32x16_t& c = half ? acc[i][2 + jj] : acc[i][jj];
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[jj], c, 0, 0, 0);
-        }
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, A.f[i][kk]), fb[j], acc[i][j], 0, 0, 0);
+    };
+    auto refill = [&](AFrags& A, int kk, int64_t k0) {
+      const uint8_t* base = g.afrag + (k0 / 16) * FRAG_BYTES + kk * FRAG_BYTES;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) A.f[i][kk] = *reinterpret_cast<const u32x4*>(base + al.off[i]);
+    };
+    // One step: multiply LDS stage `bs` (sub-step 0 fragments already in fb0)
+    // with activation slot A, reading each sub-step's fragments one sub-step
+    // ahead and refilling A for the step two ahead; end with the sub-step 0
+    // fragments of the next stage `bnext`.
+    auto multiply = [&](const uint16_t* bs, const uint16_t* bnext, AFrags& A, int64_t knext) {
+      bf16x8_t fb1[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb1[j] = b_frag<BWD>(bs, lane, j, 1);
+      mfma_kk(A, 0, fb0);
+      refill(A, 0, knext);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb0[j] = b_frag<BWD>(bs, lane, j, 2);
+      mfma_kk(A, 1, fb1);
+      refill(A, 1, knext);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb1[j] = b_frag<BWD>(bs, lane, j, 3);
+      mfma_kk(A, 2, fb0);
+      refill(A, 2, knext);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb0[j] = b_frag<BWD>(bnext, lane, j, 0);
+      mfma_kk(A, 3, fb1);
+      refill(A, 3, knext);
+    };
+#define NF4S_CONSUMER_STEP(KT, SM, ACUR)                                              \
+  do {                                                                                \
+    multiply(stage(SM), stage(((SM) + 1) % NSTAGE), ACUR, step_of((KT) + 2).k0);      \
+    __syncthreads();                                                                  \
+  } while (0)
+    const int nk4 = nk - nk % 4;
+    for (int kt = 0; kt < nk4; kt += 4) {
+      NF4S_CONSUMER_STEP(kt, 0, ar0);
+      NF4S_CONSUMER_STEP(kt + 1, 1, ar1);
+      NF4S_CONSUMER_STEP(kt + 2, 2, ar0);
+      NF4S_CONSUMER_STEP(kt + 3, 3, ar1);
     }
+    if (nk4 < nk) NF4S_CONSUMER_STEP(nk4, 0, ar0);
+    if (nk4 + 1 < nk) NF4S_CONSUMER_STEP(nk4 + 1, 1, ar1);
+    if (nk4 + 2 < nk) NF4S_CONSUMER_STEP(nk4 + 2, 2, ar0);
+#undef NF4S_CONSUMER_STEP
+
+    // LoRA term, contracted on the matrix cores in chunks of 16 over the rank:
+    // forward  + u[m, :] . (s * B[n, :]),  backward + du[m, :] . A[:, n].
+    if (g.lora_l != nullptr && split == 0) {
+      for (int r0 = 0; r0 < g.r; r0 += 16) {
+        bf16x8_t fa[2], fb[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int64_t row = m0 + wave * WAVE_ROWS + i * 32 + lrow;
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int rr = r0 + lk + e;
+            v[e] = (row < g.M && rr < g.r) ? g.lora_l[row * g.r + rr] : 0.0f;
+          }
+          fa[i] = f32x8_to_bf16(v);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t col = n0 + j * 32 + lrow;
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int rr = r0 + lk + e;
+            float x = 0.0f;
+            if (col < g.Nc && rr < g.r)
+              x = BWD ? g.lora_r[(int64_t)rr * g.k_in + col] : g.scale * g.lora_r[col * g.r + rr];
+            v[e] = x;
+          }
+          fb[j] = f32x8_to_bf16(v);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  } else {
+    // ---- producer: weight stage k lives in register slot k%4, is fetched in
+    // step k-5, has its table lookups issued in step k-3 and is decoded into
+    // LDS stage k%4 in step k-2
+    const int pt = t - 64 * CONSUMERS;
+    const WLanes<BWD> wl = w_lanes(g, n0, pt, static_cast<WLanes<BWD>*>(nullptr));
+    bool valid = true;
+    if constexpr (!BWD) valid = wl.valid;
+    const float off = g.offset[0];
+    const float2* s_pair = s_pair_all + (t & (PAIR_COPIES - 1));
+    BRegs<BWD> wb0, wb1, wb2, wb3;
+    Prep<BWD ? 4 : 1> pp;
+    load_b(g, wl, step_of(0), pt, wb0);
+    load_b(g, wl, step_of(1), pt, wb1);
+    load_b(g, wl, step_of(2), pt, wb2);
+    load_b(g, wl, step_of(3), pt, wb3);
+    __syncthreads();  // tables in LDS
+    prep_reads(wb0, s_pair, s_c8, pp);
+    finish_stage(stage(0), wb0, pp, valid, off, pt);
+    load_b(g, wl, step_of(4), pt, wb0);
+    prep_reads(wb1, s_pair, s_c8, pp);
+    finish_stage(stage(1), wb1, pp, valid, off, pt);
+    prep_reads(wb2, s_pair, s_c8, pp);
+    __syncthreads();
+#define NF4S_PRODUCER_STEP(KT, SM, WFIN, WPREP, WLD)                                 \
+  do {                                                                               \
+    load_b(g, wl, step_of((KT) + 5), pt, WLD);                                       \
+    finish_stage(stage(((SM) + 2) % NSTAGE), WFIN, pp, valid, off, pt);              \
+    prep_reads(WPREP, s_pair, s_c8, pp);                                             \
+    __syncthreads();                                                                 \
+  } while (0)
+    const int nk4 = nk - nk % 4;
+    for (int kt = 0; kt < nk4; kt += 4) {
+      NF4S_PRODUCER_STEP(kt, 0, wb2, wb3, wb1);
+      NF4S_PRODUCER_STEP(kt + 1, 1, wb3, wb0, wb2);
+      NF4S_PRODUCER_STEP(kt + 2, 2, wb0, wb1, wb3);
+      NF4S_PRODUCER_STEP(kt + 3, 3, wb1, wb2, wb0);
+    }
+    if (nk4 < nk) NF4S_PRODUCER_STEP(nk4, 0, wb2, wb3, wb1);
+    if (nk4 + 1 < nk) NF4S_PRODUCER_STEP(nk4 + 1, 1, wb3, wb0, wb2);
+    if (nk4 + 2 < nk) NF4S_PRODUCER_STEP(nk4 + 2, 2, wb0, wb1, wb3);
+#undef NF4S_PRODUCER_STEP
   }
 
   // Accumulator layout of v_mfma_f32_32x32x16: register r of lane l holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the 32x32 tile. The tile goes
   // out through LDS so that every global store writes 16 contiguous bytes
   // (bf16: the whole 256x128 tile at once; fp32 partials: 128 rows at a time).
-  __syncthreads();  // the exchange buffer is reused
+  // The weight ring is free: the last step ended with a barrier.
   if constexpr (!SPLIT) {
     constexpr int OS = BN + 8;  // bf16 per LDS row
     uint16_t* ot = reinterpret_cast<uint16_t*>(smem);
+    if (wave < CONSUMERS) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const f32x16_t& c = half ? acc[i][2 + jj] : acc[i][jj];
-        const int col = (2 * half + jj) * 32 + lrow;
+        for (int j = 0; j < 4; ++j) {
+          const int col = j * 32 + lrow;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = grp * WAVE_ROWS + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          ot[row * OS + col] = (uint16_t)(pack_bf16x2(c[r], 0.0f) & 0xFFFFu);
+          for (int r = 0; r < 16; ++r) {
+            const int row = wave * WAVE_ROWS + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            ot[row * OS + col] = (uint16_t)(pack_bf16x2(acc[i][j][r], 0.0f) & 0xFFFFu);
+          }
         }
-      }
+    }
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < BM * BN / 8 / THREADS; ++it) {
@@ -620,18 +613,17 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
     constexpr int OS = BN + 4;  // fp32 per LDS row
     float* ot = reinterpret_cast<float*>(smem);
 #pragma unroll
-    for (int ph = 0; ph < 2; ++ph) {  // rows [128 ph, 128 ph + 128): groups 2ph, 2ph+1
-      if ((grp >> 1) == ph) {
+    for (int ph = 0; ph < 2; ++ph) {  // rows [128 ph, 128 ph + 128): consumers 2ph, 2ph+1
+      if (wave < CONSUMERS && (wave >> 1) == ph) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const f32x16_t& c = half ? acc[i][2 + jj] : acc[i][jj];
-            const int col = (2 * half + jj) * 32 + lrow;
+          for (int j = 0; j < 4; ++j) {
+            const int col = j * 32 + lrow;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int row = (grp & 1) * WAVE_ROWS + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-              ot[row * OS + col] = c[r];
+              const int row = (wave & 1) * WAVE_ROWS + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+              ot[row * OS + col] = acc[i][j][r];
             }
           }
       }

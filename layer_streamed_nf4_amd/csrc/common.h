@@ -34,6 +34,13 @@ struct QPtrs {
   const float* offset;
 };
 
+// Packed activation layout shared by the packer (pack.hip) and the GEMMs
+// (gemm.hip): 1 KB fragments of (32 rows x 16 contraction values), rows padded
+// to a multiple of PACK_ROWS, contraction to a multiple of PACK_COLS.
+constexpr int PACK_ROWS = 256;
+constexpr int PACK_COLS = 64;
+constexpr int FRAG_BYTES = 1024;
+
 // Launch configuration of the dequant GEMMs, a function of the shape only.
 struct GemmPlan {
   int bm, bn;        // output tile

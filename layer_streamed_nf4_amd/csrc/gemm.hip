@@ -35,8 +35,8 @@
 //    weights and decode them into LDS. Every SIMD thus runs one wave of each
 //    kind, so the decode's vector work and LDS waits overlap the other wave's
 //    matrix work instead of competing with it step for step;
-//  * the activation operand never touches LDS: a first kernel rewrites it in
-//    MFMA fragment order (k_frag_pack), and each consumer loads its fragments
+//  * the activation operand never touches LDS: it arrives in MFMA fragment
+//    order (k_frag_pack, pack.hip), and each consumer loads its fragments
 //    with contiguous 1 KB reads; a sub-step's registers are refilled for the
 //    step two ahead as soon as its MFMAs are issued;
 //  * the decoded weights go through a four-stage LDS ring with one barrier
@@ -59,9 +59,9 @@
 namespace nf4s {
 namespace {
 
-constexpr int BM = 256;
+constexpr int BM = PACK_ROWS;  // the packed activation is padded to whole output tiles
 constexpr int BN = 128;
-constexpr int BK = 64;
+constexpr int BK = PACK_COLS;
 constexpr int CONSUMERS = 4;          // waves 0-3 multiply, waves 4-7 decode
 constexpr int THREADS = 64 * 2 * CONSUMERS;
 constexpr int WAVE_ROWS = BM / CONSUMERS;  // 64 output rows per consumer wave
@@ -102,37 +102,11 @@ struct Step {
 // For sub-step kk the 32x32x16 MFMA takes from lane l row l%32 of its 32-row
 // tile and contraction elements kk*16 + 8*(l/32) .. +8 (16 bytes). A row-major
 // activation puts consecutive lanes in different rows, which the vector memory
-// path serves at a quarter of its rate, so a first kernel rewrites A in
-// fragment order: 1 KB per (32-row block, 16-wide contraction block), lane
-// after lane, zero-padded to whole 256-row tiles and 64-wide steps. Every
-// fragment load of the GEMM is then one contiguous 1 KB read.
-constexpr int FRAG_BYTES = 1024;
+// path serves at a quarter of its rate, so the activation arrives rewritten
+// in fragment order (pack.hip): 1 KB per (32-row block, 16-wide contraction
+// block), lane after lane, zero-padded to whole 256-row tiles and 64-wide
+// steps. Every fragment load of the GEMM is then one contiguous 1 KB read.
 
-// One workgroup per (32-row block, 64-wide contraction step): read the 32x64
-// bf16 tile row by row (8 lanes per 128-byte row), transpose it through LDS,
-// write the four 1 KB fragments in lane order. Both global sides move whole
-// 64-byte runs per 4 lanes.
-__global__ __launch_bounds__(256) void k_frag_pack(const uint16_t* __restrict__ a, int64_t M,
-                                                   int64_t Kc, int64_t kblocks,
-                                                   uint8_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint8_t tile[32 * 144];
-  const int t = threadIdx.x;
-  const int64_t steps = kblocks / 4;
-  const int64_t b = blockIdx.x / steps;  // 32-row block
-  const int64_t st = blockIdx.x % steps; // 64-wide step
-  {
-    const int r = t >> 3, c = t & 7;
-    const int64_t row = 32 * b + r;
-    const int64_t k = 64 * st + 8 * c;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (row < M && k < Kc) v = *reinterpret_cast<const u32x4*>(a + row * Kc + k);
-    *reinterpret_cast<u32x4*>(tile + r * 144 + c * 16) = v;
-  }
-  __syncthreads();
-  const int f = t >> 6, lane = t & 63;  // fragment (16-wide block) and its lane
-  const u32x4 v = *reinterpret_cast<const u32x4*>(tile + (lane & 31) * 144 + (2 * f + (lane >> 5)) * 16);
-  *reinterpret_cast<u32x4*>(out + ((b * kblocks + 4 * st + f) * 64 + lane) * 16) = v;
-}
 
 struct AFrags {
   u32x4 f[2][4];  // [row tile i][sub-step kk]
@@ -392,18 +366,12 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
     s_c8[t] = tab.c8[t];
   }
 
-  // XCD-aware tile order. Workgroups are dealt to the 8 XCDs round-robin in
-  // launch order; give each XCD a contiguous run of tile indices instead, so
-  // that the workgroups sharing an L2 also share their activation rows (one
-  // 256-row tile of A per XCD at the gate shapes) and their weight columns.
-  const int ntx = (int)gridDim.x, nty = (int)gridDim.y;
-  const int total = ntx * nty * (int)gridDim.z;
-  const int lin = (int)blockIdx.x + ntx * ((int)blockIdx.y + nty * (int)blockIdx.z);
-  const int xcd = lin % 8, kth = lin / 8;
-  const int tile = xcd * (total / 8) + (xcd < total % 8 ? xcd : total % 8) + kth;
-  const int64_t n0 = (int64_t)(tile % ntx) * BN;
-  const int64_t m0 = (int64_t)((tile / ntx) % nty) * BM;
-  const int split = tile / (ntx * nty);
+  // Default launch order: the workgroups are dealt to the 8 XCDs round-robin,
+  // so both 256-row tiles of an output column block land on the same XCD and
+  // share its weight stream in L2.
+  const int64_t n0 = (int64_t)blockIdx.x * BN;
+  const int64_t m0 = (int64_t)blockIdx.y * BM;
+  const int split = blockIdx.z;
   const int64_t kb = split * g.kc_chunk;
   const int64_t ke = (kb + g.kc_chunk < g.Kc) ? kb + g.kc_chunk : g.Kc;
   const int nk = (int)((ke - kb + BK - 1) / BK);
@@ -668,9 +636,6 @@ __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ par
 
 }  // namespace
 
-size_t packed_activation_bytes(int64_t M, int64_t K) {
-  return (size_t)((M + BM - 1) / BM * BM) * (size_t)((K + BK - 1) / BK * BK) * 2;
-}
 
 GemmPlan plan_gemm(int64_t M, int64_t n_cols, int64_t k_contract) {
   GemmPlan p;
@@ -691,12 +656,6 @@ GemmPlan plan_gemm(int64_t M, int64_t n_cols, int64_t k_contract) {
   return p;
 }
 
-hipError_t launch_pack(const uint16_t* a, int64_t M, int64_t K, uint8_t* packed, hipStream_t s) {
-  const int64_t kblocks = (K + BK - 1) / BK * (BK / 16);
-  const int64_t packs = (int64_t)(packed_activation_bytes(M, K) / (4 * FRAG_BYTES));
-  hipLaunchKernelGGL(k_frag_pack, dim3((unsigned)packs), dim3(256), 0, s, a, M, K, kblocks, packed);
-  return hipGetLastError();
-}
 
 hipError_t launch_linear_packed(bool backward, const QPtrs& q, int64_t n_out, int64_t k_in,
                                 const uint8_t* a_packed, int64_t M, uint16_t* out,

@@ -169,6 +169,102 @@ def _cpu_baseline(model: str, M: int, targets) -> dict:
                       f"dequantise + fp64 forward/backward in {dt:.2f} s, scaled x{n_layers} layers"}
 
 
+def sweep(args) -> None:
+    """Where the copies hide: the 8B linear stack streamed and resident at
+    batch x 512 tokens for batch 1..16 (n = 2 slots, LoRA q/v), and at batch 4
+    for n = 2, 4, 8 slots. Per point: step times, copies and bytes per step,
+    and the overlap efficiency (t_copy + t_compute - t_step) / min(t_copy,
+    t_compute), where t_copy is the step's bytes at the same-session pinned
+    H2D rate and t_compute the resident step time (SURVEY-style crossover:
+    the copy hides once t_compute >= t_copy). One JSON line per point."""
+    import torch
+
+    import layer_streamed_nf4_amd as L
+    from layer_streamed_nf4_amd.stack import PROJ, LinearStack, ShardSet
+
+    L.lib()
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    model = "8b"
+    sh = synth.SHAPES[model]
+    n_layers = synth.N_LAYERS[model]
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+
+    def weight_fn(i, p):
+        gen.manual_seed(synth.weight_seed(i, p))
+        return torch.randn(sh[p], generator=gen, device=dev, dtype=torch.float32) * 0.02
+
+    shards = ShardSet(sh, n_layers, weight_fn)
+    host = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+    devb = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    cs = torch.cuda.Stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(cs):
+        devb.copy_(host, non_blocking=True)
+        e0.record(cs)
+        for _ in range(5):
+            devb.copy_(host, non_blocking=True)
+        e1.record(cs)
+    cs.synchronize()
+    h2d_peak = 5 * (256 << 20) / (e0.elapsed_time(e1) * 1e-3)
+    del host, devb
+    role = {"q": "attn", "k": "attn", "v": "attn", "o": "o", "gate": "mlp", "up": "mlp", "down": "down"}
+
+    def point(batch, slots, targets):
+        M = batch * 512
+        gen.manual_seed(synth.BASE_SEED + 10**6 + batch)
+        xs_role = {}
+        for p in PROJ:
+            if role[p] not in xs_role:
+                xs_role[role[p]] = torch.randn((M, sh[p][1]), generator=gen, device=dev).to(torch.bfloat16)
+        dys = {p: torch.randn((M, sh[p][0]), generator=gen, device=dev).to(torch.bfloat16) for p in PROJ}
+        lora = []
+        for i in range(n_layers):
+            d = {}
+            for p in targets:
+                gen.manual_seed(synth.BASE_SEED + 1000 * i + 10 * (PROJ.index(p) + 1) + 7)
+                d[p] = (torch.randn((synth.LORA_R, sh[p][1]), generator=gen, device=dev) * 0.01,
+                        torch.randn((sh[p][0], synth.LORA_R), generator=gen, device=dev) * 0.01)
+            lora.append(d)
+        inputs = lambda i, p: xs_role[role[p]]
+        grads = lambda i, p: dys[p]
+        out = {"kind": "sweep", "model": model, "batch": batch, "seq": 512, "tokens": M,
+               "slots": slots, "lora_targets": list(targets)}
+        for mode in ("streamed", "resident"):
+            st = LinearStack(shards, M, targets, lora, n_slots=slots, mode=mode, keep_outputs=False)
+            for _ in range(max(1, args.warmup)):
+                st.step(inputs, grads)
+            torch.cuda.synchronize()
+            c0, b0 = st.stats()
+            t = time.perf_counter()
+            for _ in range(args.steps):
+                st.step(inputs, grads)
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t) / args.steps
+            c1, b1 = st.stats()
+            st.close()
+            out[f"{mode}_ms"] = round(dt * 1e3, 2)
+            out[f"{mode}_tok_s"] = round(M / dt, 1)
+            if mode == "streamed":
+                out["copies_per_step"] = (c1 - c0) / args.steps
+                out["h2d_bytes_per_step"] = int((b1 - b0) / args.steps)
+        t_copy = out["h2d_bytes_per_step"] / h2d_peak * 1e3
+        t_comp, t_step = out["resident_ms"], out["streamed_ms"]
+        out["t_copy_ms_at_pinned_peak"] = round(t_copy, 2)
+        out["overlap_efficiency"] = round((t_copy + t_comp - t_step) / min(t_copy, t_comp), 3)
+        out["copy_hidden"] = t_comp >= t_copy
+        out["pinned_peak_gbs"] = round(h2d_peak / 1e9, 2)
+        print(json.dumps(out), flush=True)
+        del xs_role, dys, lora
+        torch.cuda.empty_cache()
+
+    for batch in (1, 2, 4, 8, 16):
+        point(batch, 2, ("q", "v"))
+    for slots in (4, 8):
+        point(4, slots, ("q", "v"))
+    point(4, 4, PROJ)  # the pages' config 4: B4, LoRA on all seven projections, n = 4
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,9 +277,14 @@ def main():
     ap.add_argument("--profile-gemm", default=None,
                     help="only run one fused GEMM shape, e.g. fwd:14336:4096:512 (for rocprofv3)")
     ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--sweep", action="store_true",
+                    help="batch x seq and slot sweep at the 8B shapes: one JSON line per point")
     args = ap.parse_args()
     if args.profile_gemm:
         profile_gemm(args.profile_gemm, args.reps)
+        return
+    if args.sweep:
+        sweep(args)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -92,6 +92,19 @@ class ShardSet:
         if int(status.item()) != 0:
             raise ValueError("non-finite weight in a quantised tensor")
 
+    @classmethod
+    def from_host(cls, shapes, n_layers, host):
+        """A shard set over existing host copies of the layer shards (for
+        example read back from a shard cache); nothing is quantised."""
+        self = cls.__new__(cls)
+        self.layout = LayerLayout(shapes)
+        self.n_layers = n_layers
+        self.shapes = shapes
+        assert len(host) == n_layers and all(h.numel() == self.layout.nbytes for h in host)
+        self.host = list(host)
+        self.device = []
+        return self
+
     def to_device(self):
         """Resident copies of every layer shard (the resident-NF4 reference)."""
         if not self.device:

@@ -140,3 +140,20 @@ def test_pageable_source_is_refused():
     with pytest.raises(L.Nf4sError) as e:
         L.layer_prefetch(slot.data_ptr(), 4096, src.data_ptr(), 4096, torch.cuda.Stream().cuda_stream)
     assert e.value.code == L.ENOTPINNED
+
+
+def test_shard_cache_roundtrip_streams_identically(world, resident, tmp_path):
+    """Shards quantised on the GPU, saved, loaded back into pinned memory and
+    streamed give the resident result bit for bit (gate walkthrough section 5:
+    a cached shard set is reused as is)."""
+    from layer_streamed_nf4_amd import shardcache
+    fp = shardcache.fingerprint_recipe({"model": MODEL, "weights": "synth.weight", "layers": N_LAYERS})
+    path = str(tmp_path / "shards")
+    shardcache.save(world["shards"], path, fp)
+    back = shardcache.load(path, SHAPES, N_LAYERS, fp)
+    for a, b in zip(world["shards"].host, back.host):
+        assert torch.equal(a, b)
+    w2 = dict(world)
+    w2["shards"] = back
+    got, _ = _run(w2, "streamed", 2)
+    _same(got, resident)

@@ -35,20 +35,24 @@ PEAK_HBM_GBS = 8000.0
 HOST_LINK_GBS = 63.0          # PCIe Gen5 x16, one direction, theoretical
 
 CONFIGS = {
-    # id: (model, batch, seq, lora targets, slots)
-    2: ("135m", 1, 512, ("q", "v"), 2),
-    3: ("8b", 1, 512, ("q", "v"), 2),
-    4: ("8b", 4, 512, ("q", "k", "v", "o", "gate", "up", "down"), 4),
+    # id: (model, batch, seq, lora targets, slots, reference pass)
+    2: ("135m", 1, 512, ("q", "v"), 2, None),
+    3: ("8b", 1, 512, ("q", "v"), 2, None),
+    4: ("8b", 4, 512, ("q", "k", "v", "o", "gate", "up", "down"), 4, None),
+    # preference step: 2 chosen/rejected pairs x seq 512 through 32B-class layers
+    # (251.5 MB each), a reference pass with the adapters off plus the policy step
+    5: ("32b", 4, 512, ("q", "v"), 2, "separate"),
 }
 
 
-def flops_per_token(model: str, lm_head: bool) -> int:
+def flops_per_token(model: str, lm_head: bool, reference: bool = False) -> int:
     """6 FLOP per frozen decoder-linear parameter per token (2 forward,
     2 recompute, 2 dL/dx; no dL/dW for a frozen base) plus, with the resident
     lm_head, 4 per lm_head parameter (2 forward, 2 dL/dx); the embedding
-    lookup counts 0. Convention of the gate walkthrough, section 4.4."""
+    lookup counts 0. Convention of the gate walkthrough, section 4.4. A
+    preference step adds the reference forward: 8 per parameter."""
     per_layer = sum(a * b for a, b in synth.SHAPES[model].values())
-    f = 6 * per_layer * synth.N_LAYERS[model]
+    f = (8 if reference else 6) * per_layer * synth.N_LAYERS[model]
     if lm_head:
         v, h = LM_HEAD[model]
         f += 4 * v * h
@@ -78,9 +82,10 @@ def gemm_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_src_hash: str):
+def traffic_from_profile(kernel_src_hash: str, spec: str):
     """HBM bytes per launch of the dominant kernel from the committed PMC summary,
-    if it was taken on this exact GEMM source; else None."""
+    if it was taken on this exact GEMM source and this shape (`fwd:N:K:M`);
+    else None."""
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(here, "profiles", "gemm_fwd_gate_8b_m512_pmc.md")
     if not os.path.exists(path):
@@ -90,7 +95,7 @@ def traffic_from_profile(kernel_src_hash: str):
         if line.startswith("<!--") and "=" in line:
             k, v = line.strip("<!-> \n").split("=", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("gemm_src_sha256_16") != kernel_src_hash:
+    if fields.get("gemm_src_sha256_16") != kernel_src_hash or fields.get("spec") != spec:
         return None
     try:
         return int(float(fields["fetch_bytes"]) + float(fields["write_bytes"]))
@@ -300,7 +305,7 @@ def main():
 
     L.lib()
     assert torch.cuda.is_available(), "bench.py needs the GPU"
-    model, batch, seq, targets, slots = CONFIGS[args.config]
+    model, batch, seq, targets, slots, reference = CONFIGS[args.config]
     if args.slots:
         slots = args.slots
     M = batch * seq
@@ -351,13 +356,13 @@ def main():
         st = LinearStack(shards, M, targets, lora, n_slots=n_slots, mode=mode, keep_outputs=False,
                          time_calls=plain_fwd if timed else None)
         for _ in range(args.warmup):
-            st.step(inputs, grads)
+            st.step(inputs, grads, reference=reference)
         torch.cuda.synchronize()
         st.timed.clear()
         c0, b0 = st.stats()
         t = time.perf_counter()
         for _ in range(args.steps):
-            st.step(inputs, grads)
+            st.step(inputs, grads, reference=reference)
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t) / args.steps
         c1, b1 = st.stats()
@@ -403,7 +408,7 @@ def main():
     del host, devb
 
     tokens = M
-    f_tok = flops_per_token(model, lm_head=False)
+    f_tok = flops_per_token(model, lm_head=False, reference=reference is not None)
     value = tokens / dt_s
     step_tflops = f_tok * tokens / dt_s / 1e12
     dom_ms = [d for (_, _, d) in durs]
@@ -415,7 +420,7 @@ def main():
         ach = avg_flop / (avg_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                    "traffic": traffic_from_profile(gemm_source_hash()),
+                    "traffic": traffic_from_profile(gemm_source_hash(), f"fwd:{n_d}:{k_d}:{M}"),
                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                     "kernel": "k_gemm<fwd,plain> (fused NF4 dequant + bf16 MFMA, x.W'^T)",
                     "launches": len(dom_ms), "avg_us": round(avg_ms * 1e3, 2),
@@ -436,7 +441,9 @@ def main():
                 "N(0,0.01) LoRA A/B; shapes stand in for the pages' checkpoints)",
         "config": {"workload": f"linear stack: {n_layers} layers of {model} projection shapes "
                                f"(q,k,v,o,gate,up,down), streamed from pinned host, "
-                               f"recompute in backward",
+                               f"recompute in backward"
+                               + (f", preference step (reference pass with adapters off, "
+                                  f"{reference})" if reference else ""),
                    "global_batch": batch, "seq_len": seq, "tokens_per_step": tokens,
                    "lora": {"r": synth.LORA_R, "alpha": synth.LORA_ALPHA, "targets": list(targets)},
                    "slots": slots, "parallelism": "single GPU"},

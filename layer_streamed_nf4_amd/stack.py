@@ -199,7 +199,7 @@ class LinearStack:
             self._packed_key = key
         return self.packed.data_ptr()
 
-    def _layer_fwd(self, i, base, inputs, store_key):
+    def _layer_fwd(self, i, base, inputs, store_key, adapters=True):
         s = self.compute.cuda_stream
         shapes = self.sh.shapes
         self._packed_key = None  # inputs may differ from layer to layer
@@ -208,7 +208,7 @@ class LinearStack:
             x = inputs(i, p)
             xp = self._pack(x, k)
             y = self._out(self.y, (store_key(i), p), (self.M, n), torch.int16)
-            if p in self.targets:
+            if adapters and p in self.targets:
                 A, B = self.lora[i][p]
                 u = self.u[p]
                 lora_fwd(x.data_ptr(), self.M, k, A.data_ptr(), self.r, u.data_ptr(),
@@ -269,15 +269,35 @@ class LinearStack:
             self.timed.append(ev)
 
     # -- the step ------------------------------------------------------------------
-    def step(self, inputs, grads):
+    def step(self, inputs, grads, reference=None):
         """Forward sweep then backward sweep with recompute. Kernels are queued
-        on the compute stream, copies on the copy stream; returns at once."""
+        on the compute stream, copies on the copy stream; returns at once.
+
+        reference: None for a plain adapter step; "separate" or "fused" for a
+        preference step, which also runs the reference model -- the same frozen
+        shards with the adapters switched off, no second model (kwkr.cn
+        "Soup v0.72.4 technical analysis", sections 3.1-3.3). "separate" gives
+        the reference its own forward sweep before the policy's (three reads
+        of every layer per step, the pages' ~1.5x); "fused" runs the reference
+        forward on each layer while the policy's forward holds it (two reads).
+        Reference outputs land in self.y with keys ("ref", i) (or
+        ("ref", 0) when outputs are not kept)."""
+        assert reference in (None, "separate", "fused")
         L = self.sh.n_layers
         fkey = (lambda i: ("f", i)) if self.keep else (lambda i: ("f", 0))
         rkey = (lambda i: ("r", i)) if self.keep else (lambda i: ("f", 0))
+        refkey = (lambda i: ("ref", i)) if self.keep else (lambda i: ("ref", 0))
         self.compute.wait_stream(torch.cuda.current_stream())
+        if reference == "separate":
+            for i in range(L):
+                # the last reference layer prefetches the policy's first
+                base = self._acquire(i, nxt=i + 1 if i + 1 < L else 0)
+                self._layer_fwd(i, base, inputs, refkey, adapters=False)
+                self._release(i)
         for i in range(L):
             base = self._acquire(i, nxt=i + 1 if i + 1 < L else None)
+            if reference == "fused":
+                self._layer_fwd(i, base, inputs, refkey, adapters=False)
             self._layer_fwd(i, base, inputs, fkey)
             self._release(i)
         for i in range(L - 1, -1, -1):

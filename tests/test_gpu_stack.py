@@ -157,3 +157,90 @@ def test_shard_cache_roundtrip_streams_identically(world, resident, tmp_path):
     w2["shards"] = back
     got, _ = _run(w2, "streamed", 2)
     _same(got, resident)
+
+
+@pytest.mark.parametrize("reference", ["separate", "fused"])
+def test_preference_step_streamed_equals_resident(world, resident, reference):
+    """Preference step: a reference pass with the adapters off over the same
+    streamed shards, then the policy step (kwkr.cn "Soup v0.72.4 technical
+    analysis", sections 3.1-3.3). Streamed == resident bit for bit; the policy
+    part equals the plain step; reference outputs equal the adapter-free
+    product; copies in one step from an empty pool: 3L - n (separate) or
+    2L - n (fused), against 2L - n for the plain step."""
+    print(f"preference {reference}", flush=True)
+
+    def run(mode):
+        st = LinearStack(world["shards"], M, TARGETS, world["lora"], n_slots=2, mode=mode)
+        st.step(lambda i, p: world["xd"][i, p], lambda i, p: world["dyd"][i, p], reference=reference)
+        torch.cuda.synchronize()
+        out = {("y",) + k: t.cpu().numpy().copy() for k, t in st.y.items()}
+        out.update({("dx",) + k: t.cpu().numpy().copy() for k, t in st.dx.items()})
+        out.update({("g",) + k: t.cpu().numpy().copy() for k, t in st.grads.items()})
+        stats = st.stats()
+        st.close()
+        return out, stats
+
+    streamed, (copies, _) = run("streamed")
+    res, _ = run("resident")
+    _same(streamed, res)
+    policy = {k: v for k, v in streamed.items() if not (k[0] == "y" and k[1][0] == "ref")}
+    _same(policy, resident)
+    assert copies == (3 if reference == "separate" else 2) * N_LAYERS - 2
+    # the reference outputs are the adapter-free products: equal to the policy
+    # output for non-adapted projections, different for the adapted ones
+    for i in (0, N_LAYERS - 1):
+        for p in PROJ:
+            ref = streamed[("y", ("ref", i), p)]
+            pol = streamed[("y", ("f", i), p)]
+            if p in TARGETS:
+                assert not np.array_equal(ref, pol), (i, p)
+            else:
+                assert np.array_equal(ref, pol), (i, p)
+
+
+def test_32b_layers_preference_streamed_equals_resident():
+    """Layers larger than 165 MiB (32B-class shapes: 251.5 MB per layer shard)
+    streamed through a 2-slot pool give the resident results bit for bit,
+    gradients included, in a preference step -- the size at which the pages'
+    streamed gradients went silently wrong (gate walkthrough section 2.5,
+    "Fine-Tune 8B Models on 4GB VRAM", "Boundary Conditions List")."""
+    require_gpu()
+    shapes = synth.SHAPES["32b"]
+    n_layers, m = 3, 64
+    g = torch.Generator(device="cuda")
+
+    def weight_fn(i, p):
+        g.manual_seed(synth.weight_seed(i, p))
+        return torch.randn(shapes[p], generator=g, device="cuda") * 0.02
+
+    shards = ShardSet(shapes, n_layers, weight_fn)
+    assert shards.layout.nbytes > 165 * 2**20
+    lora = []
+    for i in range(n_layers):
+        d = {}
+        for p in TARGETS:
+            n, k = shapes[p]
+            g.manual_seed(10_000 + 10 * i + PROJ.index(p))
+            d[p] = (torch.randn((16, k), generator=g, device="cuda") * 0.01,
+                    torch.randn((n, 16), generator=g, device="cuda") * 0.01)
+        lora.append(d)
+    g.manual_seed(77)
+    xs = {p: torch.randn((m, shapes[p][1]), generator=g, device="cuda").to(torch.bfloat16) for p in PROJ}
+    dys = {p: torch.randn((m, shapes[p][0]), generator=g, device="cuda").to(torch.bfloat16) for p in PROJ}
+
+    def run(mode):
+        st = LinearStack(shards, m, TARGETS, lora, n_slots=2, mode=mode)
+        st.step(lambda i, p: xs[p], lambda i, p: dys[p], reference="separate")
+        torch.cuda.synchronize()
+        out = {("y",) + k: t.cpu().numpy().copy() for k, t in st.y.items()}
+        out.update({("dx",) + k: t.cpu().numpy().copy() for k, t in st.dx.items()})
+        out.update({("g",) + k: t.cpu().numpy().copy() for k, t in st.grads.items()})
+        st.close()
+        return out
+
+    a, b = run("streamed"), run("resident")
+    _same(a, b)
+    for i in range(n_layers):
+        for p in TARGETS:
+            assert np.count_nonzero(a[("g", i, p, "dA")]) > 0
+            assert np.count_nonzero(a[("g", i, p, "dB")]) > 0

@@ -97,3 +97,41 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 def token_ids(n: int, vocab: int, step: int = 0) -> np.ndarray:
     return _rng(BASE_SEED + 2 * 10**6 + step).integers(0, vocab, size=n, dtype=np.int64)
+
+
+# Decoder hyper-parameters of the stand-in models (shapes and constants only).
+# 135m: SmolLM2-135M (llama architecture, tied embeddings); 8b: Llama-3.1-8B;
+# tiny: a 2-layer model small enough for the fp64 oracle and finite differences.
+DECODER = {
+    "tiny": dict(hidden=64, inter=128, heads=4, kv_heads=2, head_dim=16, vocab=256, layers=2,
+                 rope_theta=10000.0, eps=1e-5, tied=True),
+    "135m": dict(hidden=576, inter=1536, heads=9, kv_heads=3, head_dim=64, vocab=49152, layers=30,
+                 rope_theta=100000.0, eps=1e-5, tied=True),
+    "8b": dict(hidden=4096, inter=14336, heads=32, kv_heads=8, head_dim=128, vocab=128256, layers=32,
+               rope_theta=500000.0, eps=1e-5, tied=False),
+}
+SHAPES["tiny"] = _shapes(64, 128, 4, 16, 2)
+N_LAYERS["tiny"] = 2
+VOCAB["tiny"] = 256
+
+
+def embedding(model: str, which: str = "embed", sigma: float = 0.02) -> np.ndarray:
+    """Embedding (or untied lm_head) [vocab, hidden] ~ N(0, sigma) float32."""
+    c = DECODER[model]
+    seed = BASE_SEED + 500_000 + (0 if which == "embed" else 1)
+    return _rng(seed).standard_normal((c["vocab"], c["hidden"]), dtype=np.float32) * np.float32(sigma)
+
+
+def norm_weight(model: str, layer: int, which: str, sigma: float = 0.02) -> np.ndarray:
+    """RMSNorm weight [hidden] ~ N(1, sigma) float32 (which: attn, mlp, final)."""
+    c = DECODER[model]
+    seed = BASE_SEED + 600_000 + 10 * layer + ("attn", "mlp", "final").index(which)
+    return (1.0 + _rng(seed).standard_normal(c["hidden"], dtype=np.float32) * np.float32(sigma)).astype(np.float32)
+
+
+def token_batch(model: str, batch: int, seq: int, step: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """Token ids and next-token targets [batch, seq], uniform in [0, vocab)."""
+    g = _rng(BASE_SEED + 700_000 + step)
+    v = DECODER[model]["vocab"]
+    ids = g.integers(0, v, size=(batch, seq + 1), dtype=np.int64)
+    return ids[:, :-1].copy(), ids[:, 1:].copy()

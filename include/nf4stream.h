@@ -144,6 +144,10 @@ uint64_t nf4s_table_hash(void);
 #define NF4S_OP_LORA_FWD 5
 #define NF4S_OP_LINEAR_FWD_PACKED 6
 #define NF4S_OP_LINEAR_BWD_PACKED 7
+#define NF4S_OP_DENSE_FWD_PACKED 8   /* split partials of dense_linear_fwd_packed */
+#define NF4S_OP_DENSE_BWD_PACKED 9   /* split partials of dense_linear_bwd_packed */
+#define NF4S_OP_ATTENTION_BWD 10     /* M = tokens, n_out = heads (k_in ignored) */
+#define NF4S_OP_CROSS_ENTROPY 11     /* M = tokens (n_out, k_in ignored) */
 int nf4s_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, size_t* bytes);
 
 /*
@@ -269,6 +273,125 @@ int lora_fwd(const uint16_t* x, int64_t M, int64_t k_in, const float* A, int r, 
 int lora_bwd(const uint16_t* x, const uint16_t* dy, const float* u, int64_t M, int64_t k_in,
              int64_t n_out, const float* B, int r, float scale, float* dA, float* dB,
              float* du_out, int accumulate, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- the decoder around the streamed linears ----------------------------
+ *
+ * [G] s2.1-s2.2 and s4.3: a llama decoder (SmolLM2-135M, Llama-3.1-8B) whose
+ * seven layer projections are the streamed NF4 linears; the embedding table
+ * and the lm_head stay resident and unquantised in bf16, every layer body is
+ * checkpointed (recomputed in the backward), compute is bf16. The operations
+ * follow llama's published definitions (the pages name the architecture, not
+ * the formulas). Storage: bf16 for every tensor that feeds a product or the
+ * attention; fp32 for the residual stream h, norm statistics, softmax
+ * statistics and the adapters' optimiser state. All arithmetic is fp32, every
+ * reduction runs in a fixed order (results are bit-reproducible), and calls
+ * are asynchronous on `stream`. Tokens are rows t = b*S + s (batch-major).
+ */
+
+/*
+ * Resident bf16 linear (the lm_head, [G] s4.3: embed/lm_head stay bf16):
+ *   fwd: y[M, n_out] = bf16(x.W^T),  bwd: dx[M, k_in] = bf16(dy.W),
+ * fp32 accumulation on the matrix cores, W bf16 [n_out, k_in] row-major,
+ * activations packed with nf4s_pack_activation (x: K = k_in; dy: K = n_out).
+ * Shapes as the streamed linears (k_in % 64 == 0, n_out % 8 == 0).
+ * ws: nf4s_workspace_bytes(NF4S_OP_DENSE_FWD_PACKED / _BWD_PACKED) bytes.
+ * Errors: EINVAL, ESHAPE, EALIGN, EWORKSPACE, EHIP.
+ */
+int dense_linear_fwd_packed(const uint16_t* w, int64_t n_out, int64_t k_in, const void* x_packed,
+                            int64_t M, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+int dense_linear_bwd_packed(const uint16_t* w, int64_t n_out, int64_t k_in, const void* dy_packed,
+                            int64_t M, uint16_t* dx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Token embedding ([G] s4.3: resident bf16 embed_tokens, a lookup):
+ * h[t, :] = fp32(table[ids[t], :]). table bf16 [vocab, hidden]; ids int64 [T]
+ * (device); h fp32 [T, hidden]. An id outside [0, vocab) yields a NaN row
+ * (the table is never read out of bounds). Errors: EINVAL, ESHAPE, EALIGN.
+ */
+int nf4s_embed(const uint16_t* table, int64_t vocab, int64_t hidden, const int64_t* ids, int64_t T,
+               float* h, void* stream);
+
+/*
+ * RMSNorm: rstd[t] = 1/sqrt(mean_j x[t,j]^2 + eps), y = bf16(x * rstd * w).
+ * x fp32 [T, H]; w fp32 [H]; y bf16 [T, H]; rstd fp32 [T] (kept for the
+ * backward). Backward: with g = w * (dys[0] + ... + dys[n_dy-1]) (n_dy bf16
+ * [T, H] gradients of y, 1..3, summed in fp32 in that order),
+ *   d = rstd * g - x * rstd^3 * mean_j(g * x),
+ * written to dh (accumulate = 0) or added to it (accumulate = 1). dys is a
+ * host array of device pointers. Errors: EINVAL, ESHAPE, EALIGN.
+ */
+int nf4s_rmsnorm_fwd(const float* x, const float* w, int64_t T, int64_t H, float eps, uint16_t* y,
+                     float* rstd, void* stream);
+int nf4s_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float* x, const float* w,
+                     const float* rstd, int64_t T, int64_t H, int accumulate, float* dh,
+                     void* stream);
+
+/*
+ * Rotary embedding, rotate-half form, in place on bf16 x [T, heads*head_dim]:
+ * row t is position t % S; pair (j, j + d/2) of each head is rotated by the
+ * angle (t % S) * theta^(-2j/d) (inverse = 1: by minus that angle, which is
+ * the backward of the rotation). Results rounded to bf16. head_dim in
+ * {16, 32, 64, 128}; T a multiple of S. Errors: EINVAL, ESHAPE, EALIGN.
+ */
+int nf4s_rope(uint16_t* x, int64_t T, int64_t S, int heads, int head_dim, double theta, int inverse,
+              void* stream);
+
+/*
+ * Causal softmax attention with grouped KV heads (head h reads KV head
+ * h / (heads / kv_heads)), scale 1/sqrt(head_dim), fp32 online softmax:
+ *   q bf16 [B*S, heads*d]; k, v bf16 [B*S, kv_heads*d];
+ *   o bf16 [B*S, heads*d]; o_f32 nullable fp32 [B*S, heads*d] (the same
+ *   output before rounding, needed by the backward); lse fp32 [B, heads, S]
+ *   (log-sum-exp of each row's scaled scores).
+ * Backward from dout bf16 [B*S, heads*d]: dq bf16 (like q), dk, dv bf16 (like
+ * k, summed over the heads of a group in head order), with
+ * dS = P * (dP - rowsum(P * dP)) and rowsum(P * dP) = dout . o_f32.
+ * ws: nf4s_workspace_bytes(NF4S_OP_ATTENTION_BWD, B*S, heads, 0) bytes.
+ * head_dim in {16, 32, 64, 128}; heads % kv_heads == 0.
+ * Errors: EINVAL, ESHAPE, EALIGN, EWORKSPACE.
+ */
+int nf4s_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
+                       int64_t S, int heads, int kv_heads, int head_dim, uint16_t* o, float* o_f32,
+                       float* lse, void* stream);
+int nf4s_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* o_f32,
+                       const uint16_t* dout, const float* lse, int64_t B, int64_t S, int heads,
+                       int kv_heads, int head_dim, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * SwiGLU: out = bf16(silu(g) * u), silu(z) = z / (1 + e^-z); backward from ds:
+ * dg = bf16(ds * u * s * (1 + g * (1 - s))), du = bf16(ds * g * s), s the
+ * logistic of g. All bf16 [n]. Errors: EINVAL, ESHAPE, EALIGN.
+ */
+int nf4s_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* out, void* stream);
+int nf4s_swiglu_bwd(const uint16_t* ds, const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* dg,
+                    uint16_t* du, void* stream);
+
+/* Residual update out[i] = h[i] + y[i] (fp32 h and out, bf16 y; out may be
+ * h) and rounding y = bf16(x). */
+int nf4s_residual_add(const float* h, const uint16_t* y, int64_t n, float* out, void* stream);
+int nf4s_to_bf16(const float* x, int64_t n, uint16_t* y, void* stream);
+
+/*
+ * Mean token cross-entropy over bf16 logits [T, V] against int64 targets [T]:
+ * loss (device fp32 [1]) = mean_t (logsumexp(z_t) - z_t[target_t]), and
+ * dlogits bf16 [T, V] = (softmax(z_t) - onehot(target_t)) / T. A target
+ * outside [0, V) makes the loss NaN. ws: nf4s_workspace_bytes(
+ * NF4S_OP_CROSS_ENTROPY, T, 0, 0) bytes. Errors: EINVAL, ESHAPE, EALIGN,
+ * EWORKSPACE.
+ */
+int nf4s_cross_entropy(const uint16_t* logits, const int64_t* targets, int64_t T, int64_t V,
+                       float* loss, uint16_t* dlogits, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One AdamW step on fp32 parameters (the adapters' optimiser; [G] s4.1 uses a
+ * paged 8-bit AdamW, whose paging is an allocation strategy): with t = step
+ * (from 1), m = b1 m + (1-b1) g, v = b2 v + (1-b2) g^2,
+ * p = p (1 - lr wd) - lr (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps).
+ * p, m, v updated in place; g read. Errors: EINVAL, ESHAPE, EALIGN.
+ */
+int nf4s_adamw(float* p, const float* g, float* m, float* v, int64_t n, float lr, float beta1,
+               float beta2, float eps, float weight_decay, int64_t step, void* stream);
 
 /*
  * Enqueue one layer-shard copy host -> device slot on copy_stream, [E] (a

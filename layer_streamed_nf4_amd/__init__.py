@@ -22,6 +22,7 @@ OK, EINVAL, ESHAPE, EALIGN, ETABLE, EKEY, ESLOT, ENOTPINNED, EHIP, EWORKSPACE = 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 OP_QUANTIZE, OP_LINEAR_FWD, OP_LINEAR_BWD, OP_LORA_BWD, OP_LORA_FWD = 1, 2, 3, 4, 5
 OP_LINEAR_FWD_PACKED, OP_LINEAR_BWD_PACKED = 6, 7
+OP_DENSE_FWD_PACKED, OP_DENSE_BWD_PACKED, OP_ATTENTION_BWD, OP_CROSS_ENTROPY = 8, 9, 10, 11
 METHOD_NF4 = 1
 
 EXPORTS = (
@@ -32,7 +33,10 @@ EXPORTS = (
     "nf4s_stream_wait_event", "nf4s_pool_create", "nf4s_pool_destroy", "nf4s_pool_set_layer",
     "nf4s_pool_prefetch", "nf4s_pool_acquire", "nf4s_pool_release", "nf4s_pool_stats",
     "nf4s_packed_activation_bytes", "nf4s_pack_activation", "streamed_linear_fwd_packed",
-    "streamed_linear_bwd_packed",
+    "streamed_linear_bwd_packed", "dense_linear_fwd_packed", "dense_linear_bwd_packed",
+    "nf4s_embed", "nf4s_rmsnorm_fwd", "nf4s_rmsnorm_bwd", "nf4s_rope", "nf4s_attention_fwd",
+    "nf4s_attention_bwd", "nf4s_swiglu_fwd", "nf4s_swiglu_bwd", "nf4s_residual_add",
+    "nf4s_to_bf16", "nf4s_cross_entropy", "nf4s_adamw",
 )
 
 
@@ -100,6 +104,26 @@ _SIG = {
                                                   ctypes.c_size_t, _P]),
     "streamed_linear_bwd_packed": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P,
                                                   _P, ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "dense_linear_fwd_packed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "dense_linear_bwd_packed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "nf4s_embed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P]),
+    "nf4s_rmsnorm_fwd": (ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_float, _P, _P, _P]),
+    "nf4s_rmsnorm_bwd": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.c_int, _P, _P, _P, _I64, _I64,
+                                        ctypes.c_int, _P, _P]),
+    "nf4s_rope": (ctypes.c_int, [_P, _I64, _I64, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                 ctypes.c_int, _P]),
+    "nf4s_attention_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, _P, _P, _P, _P]),
+    "nf4s_attention_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, _P, _P, _P, _P,
+                                          ctypes.c_size_t, _P]),
+    "nf4s_swiglu_fwd": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
+    "nf4s_swiglu_bwd": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _P]),
+    "nf4s_residual_add": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
+    "nf4s_to_bf16": (ctypes.c_int, [_P, _I64, _P, _P]),
+    "nf4s_cross_entropy": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
+    "nf4s_adamw": (ctypes.c_int, [_P, _P, _P, _P, _I64, ctypes.c_float, ctypes.c_float,
+                                  ctypes.c_float, ctypes.c_float, ctypes.c_float, _I64, _P]),
 }
 
 
@@ -193,6 +217,66 @@ def streamed_linear_bwd_packed(shard, desc, dy_packed, M, dx, lora_du, lora_A, r
                                stream=0):
     _check(lib().streamed_linear_bwd_packed(shard, ctypes.byref(desc), dy_packed, M, dx, lora_du,
                                             lora_A, r, ws, ws_bytes, stream))
+
+
+def dense_linear_fwd_packed(w, n_out, k_in, x_packed, M, y, ws, ws_bytes, stream=0):
+    _check(lib().dense_linear_fwd_packed(w, n_out, k_in, x_packed, M, y, ws, ws_bytes, stream))
+
+
+def dense_linear_bwd_packed(w, n_out, k_in, dy_packed, M, dx, ws, ws_bytes, stream=0):
+    _check(lib().dense_linear_bwd_packed(w, n_out, k_in, dy_packed, M, dx, ws, ws_bytes, stream))
+
+
+def nf4s_embed(table, vocab, hidden, ids, T, h, stream=0):
+    _check(lib().nf4s_embed(table, vocab, hidden, ids, T, h, stream))
+
+
+def nf4s_rmsnorm_fwd(x, w, T, H, eps, y, rstd, stream=0):
+    _check(lib().nf4s_rmsnorm_fwd(x, w, T, H, eps, y, rstd, stream))
+
+
+def nf4s_rmsnorm_bwd(dys, x, w, rstd, T, H, accumulate, dh, stream=0):
+    """dys: a sequence of 1..3 device pointers (bf16 [T, H] gradients)."""
+    arr = (_P * len(dys))(*dys)
+    _check(lib().nf4s_rmsnorm_bwd(arr, len(dys), x, w, rstd, T, H, accumulate, dh, stream))
+
+
+def nf4s_rope(x, T, S, heads, head_dim, theta, inverse, stream=0):
+    _check(lib().nf4s_rope(x, T, S, heads, head_dim, theta, inverse, stream))
+
+
+def nf4s_attention_fwd(q, k, v, B, S, heads, kv_heads, head_dim, o, o_f32, lse, stream=0):
+    _check(lib().nf4s_attention_fwd(q, k, v, B, S, heads, kv_heads, head_dim, o, o_f32, lse, stream))
+
+
+def nf4s_attention_bwd(q, k, v, o_f32, dout, lse, B, S, heads, kv_heads, head_dim, dq, dk, dv, ws,
+                       ws_bytes, stream=0):
+    _check(lib().nf4s_attention_bwd(q, k, v, o_f32, dout, lse, B, S, heads, kv_heads, head_dim, dq,
+                                    dk, dv, ws, ws_bytes, stream))
+
+
+def nf4s_swiglu_fwd(g, u, n, out, stream=0):
+    _check(lib().nf4s_swiglu_fwd(g, u, n, out, stream))
+
+
+def nf4s_swiglu_bwd(ds, g, u, n, dg, du, stream=0):
+    _check(lib().nf4s_swiglu_bwd(ds, g, u, n, dg, du, stream))
+
+
+def nf4s_residual_add(h, y, n, out, stream=0):
+    _check(lib().nf4s_residual_add(h, y, n, out, stream))
+
+
+def nf4s_to_bf16(x, n, y, stream=0):
+    _check(lib().nf4s_to_bf16(x, n, y, stream))
+
+
+def nf4s_cross_entropy(logits, targets, T, V, loss, dlogits, ws, ws_bytes, stream=0):
+    _check(lib().nf4s_cross_entropy(logits, targets, T, V, loss, dlogits, ws, ws_bytes, stream))
+
+
+def nf4s_adamw(p, g, m, v, n, lr, beta1, beta2, eps, weight_decay, step, stream=0):
+    _check(lib().nf4s_adamw(p, g, m, v, n, lr, beta1, beta2, eps, weight_decay, step, stream))
 
 
 def lora_fwd(x, M, k_in, A, r, u_out, ws, ws_bytes, stream=0):

@@ -163,6 +163,16 @@ uint64_t nf4s_table_hash(void) { return host_table_hash(); }
 
 int nf4s_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, size_t* bytes) {
   if (!bytes) return fail(NF4S_EINVAL, "bytes is NULL");
+  if (op == NF4S_OP_ATTENTION_BWD || op == NF4S_OP_CROSS_ENTROPY) {
+    if (M <= 0 || M > (1ll << 24)) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
+    if (op == NF4S_OP_CROSS_ENTROPY) {
+      *bytes = cross_entropy_ws_bytes(M);
+      return NF4S_OK;
+    }
+    if (n_out <= 0 || n_out > 1024) return fail(NF4S_ESHAPE, "heads=%lld out of range", (long long)n_out);
+    *bytes = attention_bwd_ws_bytes(1, M, (int)n_out);
+    return NF4S_OK;
+  }
   int rc = check_shape(n_out, k_in);
   if (rc) return rc;
   switch (op) {
@@ -172,11 +182,14 @@ int nf4s_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, size_t*
     case NF4S_OP_LINEAR_FWD:
     case NF4S_OP_LINEAR_BWD:
     case NF4S_OP_LINEAR_FWD_PACKED:
-    case NF4S_OP_LINEAR_BWD_PACKED: {
+    case NF4S_OP_LINEAR_BWD_PACKED:
+    case NF4S_OP_DENSE_FWD_PACKED:
+    case NF4S_OP_DENSE_BWD_PACKED: {
       if (M <= 0) return fail(NF4S_ESHAPE, "M=%lld must be positive", (long long)M);
-      const bool bwd = op == NF4S_OP_LINEAR_BWD || op == NF4S_OP_LINEAR_BWD_PACKED;
+      const bool bwd = op == NF4S_OP_LINEAR_BWD || op == NF4S_OP_LINEAR_BWD_PACKED ||
+                       op == NF4S_OP_DENSE_BWD_PACKED;
       const GemmPlan p = plan_gemm(M, bwd ? k_in : n_out, bwd ? n_out : k_in);
-      const bool packed = op == NF4S_OP_LINEAR_FWD_PACKED || op == NF4S_OP_LINEAR_BWD_PACKED;
+      const bool packed = op != NF4S_OP_LINEAR_FWD && op != NF4S_OP_LINEAR_BWD;
       *bytes = packed ? p.part_bytes : p.ws_bytes;
       return NF4S_OK;
     }
@@ -395,6 +408,219 @@ int layer_prefetch(void* slot_dev, size_t slot_bytes, const void* host_pinned_sr
   if (record_ready && (e = hipEventRecord(static_cast<hipEvent_t>(record_ready), s)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
   return NF4S_OK;
+}
+
+// ---- resident dense linear (lm_head) -------------------------------------
+
+static int dense_common(bool bwd, const uint16_t* w, int64_t n_out, int64_t k_in,
+                        const void* a_packed, int64_t M, uint16_t* out, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int rc;
+  if ((rc = check_shape(n_out, k_in))) return rc;
+  if (M <= 0 || M > (1ll << 24)) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
+  const int64_t widest = n_out > k_in ? n_out : k_in;
+  if (M * widest >= (1ll << 31)) return fail(NF4S_ESHAPE, "M x width exceeds 32-bit offsets");
+  if ((rc = check_packed_shape(M, bwd ? n_out : k_in))) return rc;
+  if ((rc = check_ptr(w, "w"))) return rc;
+  if ((rc = check_ptr(a_packed, bwd ? "dy_packed" : "x_packed", 256))) return rc;
+  if ((rc = check_ptr(out, bwd ? "dx" : "y"))) return rc;
+  const GemmPlan p = plan_gemm(M, bwd ? k_in : n_out, bwd ? n_out : k_in);
+  if (p.part_bytes && (rc = check_ws(ws, ws_bytes, p.part_bytes))) return rc;
+  hipError_t e = launch_dense_packed(bwd, w, n_out, k_in, static_cast<const uint8_t*>(a_packed), M,
+                                     out, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "dense linear launch");
+}
+
+int dense_linear_fwd_packed(const uint16_t* w, int64_t n_out, int64_t k_in, const void* x_packed,
+                            int64_t M, uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  return dense_common(false, w, n_out, k_in, x_packed, M, y, ws, ws_bytes, stream);
+}
+
+int dense_linear_bwd_packed(const uint16_t* w, int64_t n_out, int64_t k_in, const void* dy_packed,
+                            int64_t M, uint16_t* dx, void* ws, size_t ws_bytes, void* stream) {
+  return dense_common(true, w, n_out, k_in, dy_packed, M, dx, ws, ws_bytes, stream);
+}
+
+// ---- decoder glue ----------------------------------------------------------
+
+static int check_rows(int64_t T, int64_t H) {
+  if (T <= 0 || H <= 0 || T > (1ll << 31) - 1 || H > (1ll << 24) || T * H >= (1ll << 40))
+    return fail(NF4S_ESHAPE, "rows=%lld width=%lld out of range", (long long)T, (long long)H);
+  return NF4S_OK;
+}
+
+static int check_count(int64_t n) {
+  if (n <= 0 || n >= (1ll << 40)) return fail(NF4S_ESHAPE, "element count %lld out of range", (long long)n);
+  return NF4S_OK;
+}
+
+static int launched(hipError_t e, const char* what) {
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, what);
+}
+
+int nf4s_embed(const uint16_t* table, int64_t vocab, int64_t hidden, const int64_t* ids, int64_t T,
+               float* h, void* stream) {
+  int rc;
+  if ((rc = check_rows(T, hidden))) return rc;
+  if (vocab <= 0 || vocab * hidden >= (1ll << 40)) return fail(NF4S_ESHAPE, "vocab=%lld", (long long)vocab);
+  if ((rc = check_ptr(table, "table", 2))) return rc;
+  if ((rc = check_ptr(ids, "ids", 8))) return rc;
+  if ((rc = check_ptr(h, "h", 4))) return rc;
+  return launched(launch_embed(table, vocab, ids, T, hidden, h, static_cast<hipStream_t>(stream)),
+                  "embed launch");
+}
+
+int nf4s_rmsnorm_fwd(const float* x, const float* w, int64_t T, int64_t H, float eps, uint16_t* y,
+                     float* rstd, void* stream) {
+  int rc;
+  if ((rc = check_rows(T, H))) return rc;
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(NF4S_EINVAL, "eps must be positive and finite");
+  if ((rc = check_ptr(x, "x", 4)) || (rc = check_ptr(w, "w", 4)) || (rc = check_ptr(y, "y", 2)) ||
+      (rc = check_ptr(rstd, "rstd", 4)))
+    return rc;
+  return launched(launch_rmsnorm_fwd(x, w, T, H, eps, y, rstd, static_cast<hipStream_t>(stream)),
+                  "rmsnorm_fwd launch");
+}
+
+int nf4s_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float* x, const float* w,
+                     const float* rstd, int64_t T, int64_t H, int accumulate, float* dh,
+                     void* stream) {
+  int rc;
+  if ((rc = check_rows(T, H))) return rc;
+  if (!dys) return fail(NF4S_EINVAL, "dys is NULL");
+  if (n_dy < 1 || n_dy > 3) return fail(NF4S_EINVAL, "n_dy=%d outside [1, 3]", n_dy);
+  for (int i = 0; i < n_dy; ++i)
+    if ((rc = check_ptr(dys[i], "dys[i]", 2))) return rc;
+  if (accumulate != 0 && accumulate != 1) return fail(NF4S_EINVAL, "accumulate must be 0 or 1");
+  if ((rc = check_ptr(x, "x", 4)) || (rc = check_ptr(w, "w", 4)) || (rc = check_ptr(rstd, "rstd", 4)) ||
+      (rc = check_ptr(dh, "dh", 4)))
+    return rc;
+  return launched(launch_rmsnorm_bwd(dys, n_dy, x, w, rstd, T, H, accumulate, dh,
+                                     static_cast<hipStream_t>(stream)),
+                  "rmsnorm_bwd launch");
+}
+
+static int check_heads(int heads, int head_dim) {
+  if (heads <= 0 || heads > 1024) return fail(NF4S_ESHAPE, "heads=%d out of range", heads);
+  if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return fail(NF4S_ESHAPE, "head_dim=%d not one of 16, 32, 64, 128", head_dim);
+  return NF4S_OK;
+}
+
+int nf4s_rope(uint16_t* x, int64_t T, int64_t S, int heads, int head_dim, double theta, int inverse,
+              void* stream) {
+  int rc;
+  if ((rc = check_heads(heads, head_dim))) return rc;
+  if (S <= 0 || T <= 0 || T % S) return fail(NF4S_ESHAPE, "rows=%lld must be a positive multiple of seq=%lld", (long long)T, (long long)S);
+  if ((rc = check_rows(T, (int64_t)heads * head_dim))) return rc;
+  if (!(theta > 1.0) || !std::isfinite(theta)) return fail(NF4S_EINVAL, "theta must be finite and > 1");
+  if (inverse != 0 && inverse != 1) return fail(NF4S_EINVAL, "inverse must be 0 or 1");
+  if ((rc = check_ptr(x, "x", 2))) return rc;
+  return launched(launch_rope(x, T, S, heads, head_dim, theta, inverse, static_cast<hipStream_t>(stream)),
+                  "rope launch");
+}
+
+static int check_attention(int64_t B, int64_t S, int heads, int kv_heads, int head_dim) {
+  int rc;
+  if ((rc = check_heads(heads, head_dim))) return rc;
+  if (kv_heads <= 0 || heads % kv_heads)
+    return fail(NF4S_ESHAPE, "heads=%d is not a multiple of kv_heads=%d", heads, kv_heads);
+  if (B <= 0 || S <= 0 || B * S > (1ll << 24) || B * heads * ((S + 63) / 64) >= (1ll << 31))
+    return fail(NF4S_ESHAPE, "batch=%lld seq=%lld out of range", (long long)B, (long long)S);
+  return NF4S_OK;
+}
+
+int nf4s_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
+                       int64_t S, int heads, int kv_heads, int head_dim, uint16_t* o, float* o_f32,
+                       float* lse, void* stream) {
+  int rc;
+  if ((rc = check_attention(B, S, heads, kv_heads, head_dim))) return rc;
+  if ((rc = check_ptr(q, "q", 2)) || (rc = check_ptr(k, "k", 2)) || (rc = check_ptr(v, "v", 2)) ||
+      (rc = check_ptr(o, "o", 2)) || (rc = check_ptr(lse, "lse", 4)))
+    return rc;
+  if (o_f32 && (rc = check_ptr(o_f32, "o_f32", 4))) return rc;
+  return launched(launch_attention_fwd(q, k, v, B, S, heads, kv_heads, head_dim, o, o_f32, lse,
+                                       static_cast<hipStream_t>(stream)),
+                  "attention_fwd launch");
+}
+
+int nf4s_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* o_f32,
+                       const uint16_t* dout, const float* lse, int64_t B, int64_t S, int heads,
+                       int kv_heads, int head_dim, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                       void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_attention(B, S, heads, kv_heads, head_dim))) return rc;
+  if ((rc = check_ptr(q, "q", 2)) || (rc = check_ptr(k, "k", 2)) || (rc = check_ptr(v, "v", 2)) ||
+      (rc = check_ptr(o_f32, "o_f32", 4)) || (rc = check_ptr(dout, "dout", 2)) ||
+      (rc = check_ptr(lse, "lse", 4)) || (rc = check_ptr(dq, "dq", 2)) || (rc = check_ptr(dk, "dk", 2)) ||
+      (rc = check_ptr(dv, "dv", 2)))
+    return rc;
+  if ((rc = check_ws(ws, ws_bytes, attention_bwd_ws_bytes(B, S, heads)))) return rc;
+  return launched(launch_attention_bwd(q, k, v, o_f32, dout, lse, B, S, heads, kv_heads, head_dim, dq,
+                                       dk, dv, ws, static_cast<hipStream_t>(stream)),
+                  "attention_bwd launch");
+}
+
+int nf4s_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* out, void* stream) {
+  int rc;
+  if ((rc = check_count(n))) return rc;
+  if ((rc = check_ptr(g, "g", 2)) || (rc = check_ptr(u, "u", 2)) || (rc = check_ptr(out, "out", 2))) return rc;
+  return launched(launch_swiglu_fwd(g, u, n, out, static_cast<hipStream_t>(stream)), "swiglu_fwd launch");
+}
+
+int nf4s_swiglu_bwd(const uint16_t* ds, const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* dg,
+                    uint16_t* du, void* stream) {
+  int rc;
+  if ((rc = check_count(n))) return rc;
+  if ((rc = check_ptr(ds, "ds", 2)) || (rc = check_ptr(g, "g", 2)) || (rc = check_ptr(u, "u", 2)) ||
+      (rc = check_ptr(dg, "dg", 2)) || (rc = check_ptr(du, "du", 2)))
+    return rc;
+  return launched(launch_swiglu_bwd(ds, g, u, n, dg, du, static_cast<hipStream_t>(stream)),
+                  "swiglu_bwd launch");
+}
+
+int nf4s_residual_add(const float* h, const uint16_t* y, int64_t n, float* out, void* stream) {
+  int rc;
+  if ((rc = check_count(n))) return rc;
+  if ((rc = check_ptr(h, "h", 4)) || (rc = check_ptr(y, "y", 2)) || (rc = check_ptr(out, "out", 4))) return rc;
+  return launched(launch_residual_add(h, y, n, out, static_cast<hipStream_t>(stream)),
+                  "residual_add launch");
+}
+
+int nf4s_to_bf16(const float* x, int64_t n, uint16_t* y, void* stream) {
+  int rc;
+  if ((rc = check_count(n))) return rc;
+  if ((rc = check_ptr(x, "x", 4)) || (rc = check_ptr(y, "y", 2))) return rc;
+  return launched(launch_f32_to_bf16(x, n, y, static_cast<hipStream_t>(stream)), "to_bf16 launch");
+}
+
+int nf4s_cross_entropy(const uint16_t* logits, const int64_t* targets, int64_t T, int64_t V,
+                       float* loss, uint16_t* dlogits, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_rows(T, V))) return rc;
+  if ((rc = check_ptr(logits, "logits", 2)) || (rc = check_ptr(targets, "targets", 8)) ||
+      (rc = check_ptr(loss, "loss", 4)) || (rc = check_ptr(dlogits, "dlogits", 2)))
+    return rc;
+  if ((rc = check_ws(ws, ws_bytes, cross_entropy_ws_bytes(T)))) return rc;
+  return launched(launch_cross_entropy(logits, targets, T, V, loss, dlogits, ws,
+                                       static_cast<hipStream_t>(stream)),
+                  "cross_entropy launch");
+}
+
+int nf4s_adamw(float* p, const float* g, float* m, float* v, int64_t n, float lr, float beta1,
+               float beta2, float eps, float weight_decay, int64_t step, void* stream) {
+  int rc;
+  if ((rc = check_count(n))) return rc;
+  if (step < 1) return fail(NF4S_EINVAL, "step=%lld must count from 1", (long long)step);
+  if (!std::isfinite(lr) || lr < 0.0f || !(beta1 >= 0.0f && beta1 < 1.0f) ||
+      !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps > 0.0f) || !std::isfinite(weight_decay))
+    return fail(NF4S_EINVAL, "AdamW hyper-parameters out of range");
+  if ((rc = check_ptr(p, "p", 4)) || (rc = check_ptr(g, "g", 4)) || (rc = check_ptr(m, "m", 4)) ||
+      (rc = check_ptr(v, "v", 4)))
+    return rc;
+  return launched(launch_adamw(p, g, m, v, n, lr, beta1, beta2, eps, weight_decay, step,
+                               static_cast<hipStream_t>(stream)),
+                  "adamw launch");
 }
 
 int nf4s_event_create(void** event_out) {

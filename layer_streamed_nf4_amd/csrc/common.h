@@ -67,6 +67,10 @@ hipError_t launch_linear_packed(bool backward, const QPtrs& q, int64_t n_out, in
                                 const uint8_t* a_packed, int64_t M, uint16_t* out,
                                 const float* lora_l, const float* lora_r, int r, float scale,
                                 void* part_ws, hipStream_t s);
+// The same GEMMs with a dense bf16 weight w[n_out, k_in] (the resident lm_head).
+hipError_t launch_dense_packed(bool backward, const uint16_t* w, int64_t n_out, int64_t k_in,
+                               const uint8_t* a_packed, int64_t M, uint16_t* out, void* part_ws,
+                               hipStream_t s);
 
 hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t k_in, const float* A, int r,
                            float* u, void* ws, hipStream_t s);
@@ -76,5 +80,36 @@ hipError_t launch_lora_bwd(const uint16_t* x, const uint16_t* dy, const float* u
                            float* dA, float* dB, float* du, int accumulate, void* ws,
                            hipStream_t s);
 size_t lora_bwd_ws_bytes(int64_t M, int64_t n_out, int r);
+
+// Decoder kernels (decoder.hip).
+hipError_t launch_embed(const uint16_t* E, int64_t V, const int64_t* ids, int64_t T, int64_t H,
+                        float* h, hipStream_t s);
+hipError_t launch_rmsnorm_fwd(const float* x, const float* w, int64_t T, int64_t H, float eps,
+                              uint16_t* y, float* rstd, hipStream_t s);
+hipError_t launch_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float* x, const float* w,
+                              const float* rstd, int64_t T, int64_t H, int accumulate, float* dh,
+                              hipStream_t s);
+hipError_t launch_rope(uint16_t* x, int64_t T, int64_t S, int heads, int d, double theta,
+                       int inverse, hipStream_t s);
+hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
+                                int64_t S, int H, int Hkv, int D, uint16_t* o, float* o_f32,
+                                float* lse, hipStream_t s);
+size_t attention_bwd_ws_bytes(int64_t B, int64_t S, int H);
+hipError_t launch_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const float* o_f32, const uint16_t* dout, const float* lse,
+                                int64_t B, int64_t S, int H, int Hkv, int D, uint16_t* dq,
+                                uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s);
+hipError_t launch_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* out,
+                             hipStream_t s);
+hipError_t launch_swiglu_bwd(const uint16_t* ds, const uint16_t* g, const uint16_t* u, int64_t n,
+                             uint16_t* dg, uint16_t* du, hipStream_t s);
+hipError_t launch_residual_add(const float* h, const uint16_t* y, int64_t n, float* out,
+                               hipStream_t s);
+hipError_t launch_f32_to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s);
+size_t cross_entropy_ws_bytes(int64_t T);
+hipError_t launch_cross_entropy(const uint16_t* logits, const int64_t* targets, int64_t T, int64_t V,
+                                float* loss, uint16_t* dlogits, void* ws, hipStream_t s);
+hipError_t launch_adamw(float* p, const float* g, float* m, float* v, int64_t n, float lr, float b1,
+                        float b2, float eps, float wd, int64_t step, hipStream_t s);
 
 }  // namespace nf4s

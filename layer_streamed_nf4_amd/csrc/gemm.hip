@@ -74,6 +74,7 @@ constexpr int SMEM_BYTES = NSTAGE * STAGE_ELEMS * 2 + 256 * PAIR_COPIES * 8 + 25
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
 
 struct GemmArgs {
+  const uint16_t* wd;  // dense bf16 weight [n_out, k_in] (DENSE kernels only)
   const uint8_t* packed;
   const uint8_t* q8;
   const float* nested;
@@ -330,6 +331,91 @@ __device__ __forceinline__ void finish_stage(uint16_t* Bs, const BRegs<true>& rb
   }
 }
 
+// ---- dense bf16 weight tile (the resident lm_head), producer side ---------
+// Same thread-to-tile map and LDS layouts as the NF4 producer, without the
+// decode: the forward copies 64 B of a weight row per thread, the backward
+// loads a 4x8 patch and pairs its values along the contraction on the way
+// into LDS. Rows and columns outside the weight load as zeros.
+template <bool BWD>
+struct DLanes;
+template <>
+struct DLanes<false> {
+  const uint16_t* row;  // the thread's weight row at contraction 0, plus its half
+  bool valid;
+};
+template <>
+struct DLanes<true> {
+  int64_t col;  // first (clamped) column
+  bool cvalid;
+};
+struct DRegs {
+  u32x4 w[4];
+};
+
+__device__ __forceinline__ DLanes<false> d_lanes(const GemmArgs& g, int64_t n0, int pt,
+                                                 DLanes<false>*) {
+  DLanes<false> L;
+  int64_t n = n0 + (pt >> 1);
+  L.valid = n < g.n_out;
+  n = L.valid ? n : g.n_out - 1;
+  L.row = g.wd + n * g.k_in + (pt & 1) * 32;
+  return L;
+}
+
+__device__ __forceinline__ void load_d(const GemmArgs&, const DLanes<false>& L, Step s, int,
+                                       DRegs& rb) {
+#pragma unroll
+  for (int jw = 0; jw < 4; ++jw) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(L.row + s.k0 + jw * 8);
+    rb.w[jw] = L.valid ? v : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+__device__ __forceinline__ void finish_dense(uint16_t* Bs, const DRegs& rb, int pt,
+                                             DLanes<false>*) {
+#pragma unroll
+  for (int jw = 0; jw < 4; ++jw)
+    *reinterpret_cast<u32x4*>(Bs + (pt >> 1) * LDS_STRIDE + (pt & 1) * 32 + jw * 8) = rb.w[jw];
+}
+
+__device__ __forceinline__ DLanes<true> d_lanes(const GemmArgs& g, int64_t n0, int pt,
+                                                DLanes<true>*) {
+  DLanes<true> L;
+  const int64_t col = n0 + 8 * (pt & 15);
+  L.cvalid = col < g.k_in;
+  L.col = L.cvalid ? col : g.k_in - 8;
+  return L;
+}
+
+__device__ __forceinline__ void load_d(const GemmArgs& g, const DLanes<true>& L, Step s, int pt,
+                                       DRegs& rb) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = s.k0 + 4 * (pt >> 4) + i;
+    const bool ok = L.cvalid && row < g.Kc;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(g.wd + (ok ? row : 0) * g.k_in + L.col);
+    rb.w[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Word q of row i holds columns 2q (low half) and 2q+1 (high half); column c
+// of the patch goes to LDS as its four contraction values r0..r0+3.
+__device__ __forceinline__ void finish_dense(uint16_t* Bs, const DRegs& rb, int pt, DLanes<true>*) {
+  const int r0 = 4 * (pt >> 4);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t w0 = rb.w[0][q], w1 = rb.w[1][q], w2 = rb.w[2][q], w3 = rb.w[3][q];
+    const int cb = 8 * (pt & 15) + 2 * q;
+    uint2 p0, p1;
+    p0.x = (w0 & 0xFFFFu) | (w1 << 16);
+    p0.y = (w2 & 0xFFFFu) | (w3 << 16);
+    p1.x = (w0 >> 16) | (w1 & 0xFFFF0000u);
+    p1.y = (w2 >> 16) | (w3 & 0xFFFF0000u);
+    *reinterpret_cast<uint2*>(Bs + cb * LDS_STRIDE + bwd_swizzle_off(cb, r0)) = p0;
+    *reinterpret_cast<uint2*>(Bs + (cb + 1) * LDS_STRIDE + bwd_swizzle_off(cb + 1, r0)) = p1;
+  }
+}
+
 // B fragment j (columns 32j .. 32j+31) of sub-step kk from an LDS stage:
 // lane l reads column 32j + l%32, contraction kk*16 + 8*(l/32) .. +8.
 template <bool BWD>
@@ -350,8 +436,9 @@ __device__ __forceinline__ bf16x8_t f32x8_to_bf16(const float* v) {
 }
 
 // SPLIT selects the output path (fp32 partials vs bf16 result) at compile time,
-// so the two variants also carry distinct kernel names in profiles.
-template <bool BWD, bool SPLIT>
+// so the two variants also carry distinct kernel names in profiles. DENSE
+// swaps the NF4 producer for the plain bf16 one.
+template <bool BWD, bool SPLIT, bool DENSE>
 __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_BYTES];
   uint16_t* const Bs0 = reinterpret_cast<uint16_t*>(smem);
@@ -359,7 +446,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
   float* const s_c8 = reinterpret_cast<float*>(smem + NSTAGE * STAGE_ELEMS * 2 + 256 * PAIR_COPIES * 8);
 
   const int t = threadIdx.x;
-  if (t < 256) {
+  if (!DENSE && t < 256) {
     const float2 e = make_float2(tab.c4[t >> 4], tab.c4[t & 15]);
 #pragma unroll
     for (int c = 0; c < PAIR_COPIES; ++c) s_pair_all[t * PAIR_COPIES + c] = e;
@@ -502,6 +589,38 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
     }
+  } else if constexpr (DENSE) {
+    // ---- dense producer: the same ring without the decode; stage k is
+    // fetched in step k-5 and stored into LDS stage k%4 in step k-2
+    const int pt = t - 64 * CONSUMERS;
+    const DLanes<BWD> dl = d_lanes(g, n0, pt, static_cast<DLanes<BWD>*>(nullptr));
+    DRegs wb0, wb1, wb2, wb3;
+    load_d(g, dl, step_of(0), pt, wb0);
+    load_d(g, dl, step_of(1), pt, wb1);
+    load_d(g, dl, step_of(2), pt, wb2);
+    load_d(g, dl, step_of(3), pt, wb3);
+    __syncthreads();  // tables in LDS (unused here; the barrier count is shared)
+    finish_dense(stage(0), wb0, pt, static_cast<DLanes<BWD>*>(nullptr));
+    load_d(g, dl, step_of(4), pt, wb0);
+    finish_dense(stage(1), wb1, pt, static_cast<DLanes<BWD>*>(nullptr));
+    __syncthreads();
+#define NF4S_DENSE_STEP(KT, SM, WFIN, WLD)                                          \
+  do {                                                                              \
+    load_d(g, dl, step_of((KT) + 5), pt, WLD);                                      \
+    finish_dense(stage(((SM) + 2) % NSTAGE), WFIN, pt, static_cast<DLanes<BWD>*>(nullptr)); \
+    __syncthreads();                                                                \
+  } while (0)
+    const int nk4 = nk - nk % 4;
+    for (int kt = 0; kt < nk4; kt += 4) {
+      NF4S_DENSE_STEP(kt, 0, wb2, wb1);
+      NF4S_DENSE_STEP(kt + 1, 1, wb3, wb2);
+      NF4S_DENSE_STEP(kt + 2, 2, wb0, wb3);
+      NF4S_DENSE_STEP(kt + 3, 3, wb1, wb0);
+    }
+    if (nk4 < nk) NF4S_DENSE_STEP(nk4, 0, wb2, wb1);
+    if (nk4 + 1 < nk) NF4S_DENSE_STEP(nk4 + 1, 1, wb3, wb2);
+    if (nk4 + 2 < nk) NF4S_DENSE_STEP(nk4 + 2, 2, wb0, wb3);
+#undef NF4S_DENSE_STEP
   } else {
     // ---- producer: weight stage k lives in register slot k%4, is fetched in
     // step k-5, has its table lookups issued in step k-3 and is decoded into
@@ -657,15 +776,19 @@ GemmPlan plan_gemm(int64_t M, int64_t n_cols, int64_t k_contract) {
 }
 
 
-hipError_t launch_linear_packed(bool backward, const QPtrs& q, int64_t n_out, int64_t k_in,
-                                const uint8_t* a_packed, int64_t M, uint16_t* out,
-                                const float* lora_l, const float* lora_r, int r, float scale,
-                                void* part_ws, hipStream_t s) {
+// Launches the GEMM (and the split sum when the contraction is split) for
+// C[M, Nc] = A . B with the weight given either as an NF4 tensor (q) or as a
+// dense bf16 matrix (wd).
+static hipError_t launch_gemm(bool backward, const QPtrs* q, const uint16_t* wd, int64_t n_out,
+                              int64_t k_in, const uint8_t* a_packed, int64_t M, uint16_t* out,
+                              const float* lora_l, const float* lora_r, int r, float scale,
+                              void* part_ws, hipStream_t s) {
   GemmArgs g;
-  g.packed = q.packed;
-  g.q8 = q.q8;
-  g.nested = q.nested;
-  g.offset = q.offset;
+  g.wd = wd;
+  g.packed = q ? q->packed : nullptr;
+  g.q8 = q ? q->q8 : nullptr;
+  g.nested = q ? q->nested : nullptr;
+  g.offset = q ? q->offset : nullptr;
   g.M = M;
   g.Kc = backward ? n_out : k_in;
   g.Nc = backward ? k_in : n_out;
@@ -683,20 +806,41 @@ hipError_t launch_linear_packed(bool backward, const QPtrs& q, int64_t n_out, in
   g.scale = scale;
   const dim3 grid((unsigned)((g.Nc + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)p.splits);
   const bool split = p.splits > 1;
-  if (backward && split)
-    hipLaunchKernelGGL((k_gemm<true, true>), grid, dim3(THREADS), 0, s, g, host_tables());
-  else if (backward)
-    hipLaunchKernelGGL((k_gemm<true, false>), grid, dim3(THREADS), 0, s, g, host_tables());
-  else if (split)
-    hipLaunchKernelGGL((k_gemm<false, true>), grid, dim3(THREADS), 0, s, g, host_tables());
-  else
-    hipLaunchKernelGGL((k_gemm<false, false>), grid, dim3(THREADS), 0, s, g, host_tables());
+  const Tables& tab = host_tables();
+#define NF4S_GEMM(B_, S_, D_) hipLaunchKernelGGL((k_gemm<B_, S_, D_>), grid, dim3(THREADS), 0, s, g, tab)
+  if (wd == nullptr) {
+    if (backward && split) NF4S_GEMM(true, true, false);
+    else if (backward) NF4S_GEMM(true, false, false);
+    else if (split) NF4S_GEMM(false, true, false);
+    else NF4S_GEMM(false, false, false);
+  } else {
+    if (backward && split) NF4S_GEMM(true, true, true);
+    else if (backward) NF4S_GEMM(true, false, true);
+    else if (split) NF4S_GEMM(false, true, true);
+    else NF4S_GEMM(false, false, true);
+  }
+#undef NF4S_GEMM
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const int64_t n = M * g.Nc;
   const dim3 g2((unsigned)((n / 4 + 1 + 255) / 256));
   hipLaunchKernelGGL(k_split_sum, g2, dim3(256), 0, s, g.part, p.splits, n, out);
   return hipGetLastError();
+}
+
+hipError_t launch_linear_packed(bool backward, const QPtrs& q, int64_t n_out, int64_t k_in,
+                                const uint8_t* a_packed, int64_t M, uint16_t* out,
+                                const float* lora_l, const float* lora_r, int r, float scale,
+                                void* part_ws, hipStream_t s) {
+  return launch_gemm(backward, &q, nullptr, n_out, k_in, a_packed, M, out, lora_l, lora_r, r, scale,
+                     part_ws, s);
+}
+
+hipError_t launch_dense_packed(bool backward, const uint16_t* w, int64_t n_out, int64_t k_in,
+                               const uint8_t* a_packed, int64_t M, uint16_t* out, void* part_ws,
+                               hipStream_t s) {
+  return launch_gemm(backward, nullptr, w, n_out, k_in, a_packed, M, out, nullptr, nullptr, 0, 0.0f,
+                     part_ws, s);
 }
 
 }  // namespace nf4s

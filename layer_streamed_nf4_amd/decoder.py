@@ -1,0 +1,343 @@
+"""The streamed NF4 QLoRA decoder training step over the C ABI.
+
+Orchestration only: every operation runs in libnf4stream's kernels (the
+streamed NF4 linears, the adapters, the resident bf16 lm_head, RMSNorm, rotary
+embedding, grouped causal attention, SwiGLU, cross-entropy, AdamW), and the
+slot bookkeeping lives in its native pool. torch provides device memory,
+pinned host memory and streams.
+
+The model is the llama decoder the pages train ("Soup layer-streamed NF4
+training measured", sections 2.1-2.2 and 4.3: SmolLM2-135M and
+Llama-3.1-8B-Instruct): pre-norm layers whose seven projections are NF4 shards
+streamed through a slot pool, LoRA on the target projections, embedding and
+lm_head resident in bf16, the body of every layer checkpointed. A step is
+
+  forward:  h_0 = E[ids]; for each layer i: h_{i+1} = layer_i(h_i), keeping
+            h_i only (streaming layer i+1 in while i computes);
+            logits = norm(h_L) . lm_head^T; loss = mean cross-entropy;
+  backward: dlogits -> dh_L; for i = L-1 .. 0: recompute layer_i from h_i
+            (its second read of the shard, streaming layer i-1 in), then
+            differentiate it; LoRA gradients are produced on the way;
+  update:   AdamW on every adapter parameter (one flat fp32 buffer).
+
+(English article "Fine-Tune 8B Models on 4GB VRAM", "The Principle of Layer
+Streaming": forward prefetches i+1, backward i-1, every layer read twice.)
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (OP_ATTENTION_BWD, OP_CROSS_ENTROPY, OP_DENSE_BWD_PACKED, OP_DENSE_FWD_PACKED,
+               OP_LINEAR_BWD_PACKED, OP_LINEAR_FWD_PACKED, OP_LORA_BWD, OP_LORA_FWD,
+               dense_linear_bwd_packed, dense_linear_fwd_packed, lora_bwd, lora_fwd, nf4s_adamw,
+               nf4s_attention_bwd, nf4s_attention_fwd, nf4s_cross_entropy, nf4s_embed,
+               nf4s_pack_activation, nf4s_packed_activation_bytes, nf4s_pool_acquire,
+               nf4s_pool_create, nf4s_pool_destroy, nf4s_pool_prefetch, nf4s_pool_release,
+               nf4s_pool_set_layer, nf4s_pool_stats, nf4s_residual_add, nf4s_rmsnorm_bwd,
+               nf4s_rmsnorm_fwd, nf4s_rope, nf4s_swiglu_bwd, nf4s_swiglu_fwd, nf4s_to_bf16,
+               nf4s_workspace_bytes, streamed_linear_bwd_packed, streamed_linear_fwd_packed)
+from .stack import ALIGN, PROJ, ShardSet, _round_up
+
+BF16 = torch.int16  # bf16 tensors travel as their bit patterns
+
+
+class Decoder:
+    """One training step of the decoder, streamed (slot pool) or resident.
+
+    cfg: hidden, inter, heads, kv_heads, head_dim, vocab, layers, rope_theta,
+         eps (the llama hyper-parameters of the model).
+    shards: the layers' NF4 shards (ShardSet with cfg's shapes).
+    embed, lm_head: bf16-bit device tensors [vocab, hidden] (the same tensor
+         when the embeddings are tied).
+    norms: {"attn": [L fp32 [hidden]], "mlp": [...], "final": fp32 [hidden]}.
+    lora: {(layer, proj): (A fp32 [r, k_in], B fp32 [n_out, r])} initial
+         adapter values (any device); copied into one flat parameter buffer.
+    """
+
+    def __init__(self, cfg, shards: ShardSet, embed, lm_head, norms, lora, batch, seq,
+                 targets=("q", "v"), r=16, alpha=32, n_slots=2, mode="streamed", lr=1e-4,
+                 betas=(0.9, 0.999), adam_eps=1e-8, weight_decay=0.0):
+        assert mode in ("streamed", "resident")
+        dev = "cuda"
+        self.cfg = cfg
+        self.sh = shards
+        self.L = shards.n_layers
+        self.B, self.S = batch, seq
+        self.M = M = batch * seq
+        self.targets = tuple(targets)
+        self.r = r
+        self.scale = alpha / r
+        self.mode = mode
+        self.lr, self.betas, self.adam_eps, self.wd = lr, betas, adam_eps, weight_decay
+        self.t = 0
+        H, I, V = cfg["hidden"], cfg["inter"], cfg["vocab"]
+        nh, nkv, hd = cfg["heads"], cfg["kv_heads"], cfg["head_dim"]
+        self.H, self.I, self.V = H, I, V
+        self.qd, self.kvd = nh * hd, nkv * hd
+        shapes = shards.shapes
+        assert shapes["q"] == (self.qd, H) and shapes["k"] == (self.kvd, H)
+        assert shapes["gate"] == (I, H) and shapes["down"] == (H, I)
+        self.embed, self.lm_head, self.norms = embed, lm_head, norms
+        self.compute = torch.cuda.Stream()
+        self.copy = torch.cuda.Stream()
+
+        # adapters: one flat fp32 buffer of every A and B (16-byte aligned
+        # views), with gradients and AdamW moments laid out the same way
+        n = 0
+        self._lora_off = {}
+        for i in range(self.L):
+            for p in self.targets:
+                no, ki = shapes[p]
+                self._lora_off[(i, p)] = (n, n + r * ki)
+                n += r * ki + no * r
+        self.n_params = n
+        self.params = torch.zeros(n, dtype=torch.float32, device=dev)
+        self.grads = torch.zeros(n, dtype=torch.float32, device=dev)
+        self.m = torch.zeros(n, dtype=torch.float32, device=dev)
+        self.v = torch.zeros(n, dtype=torch.float32, device=dev)
+        self.lora = {}
+        self.lora_grads = {}
+        for (i, p), (oa, ob) in self._lora_off.items():
+            no, ki = shapes[p]
+            A = self.params[oa:oa + r * ki].view(r, ki)
+            Bm = self.params[ob:ob + no * r].view(no, r)
+            a0, b0 = lora[(i, p)]
+            A.copy_(torch.as_tensor(a0, dtype=torch.float32))
+            Bm.copy_(torch.as_tensor(b0, dtype=torch.float32))
+            self.lora[(i, p)] = (A, Bm)
+            self.lora_grads[(i, p)] = (self.grads[oa:oa + r * ki].view(r, ki),
+                                       self.grads[ob:ob + no * r].view(no, r))
+
+        def f32(*shape):
+            return torch.empty(shape, dtype=torch.float32, device=dev)
+
+        def bf(*shape):
+            return torch.empty(shape, dtype=BF16, device=dev)
+
+        # residual stream checkpoints h_0 .. h_L (the layer inputs)
+        self.h = [f32(M, H) for _ in range(self.L + 1)]
+        # one layer's recomputable body
+        self.n1, self.rstd1 = bf(M, H), f32(M)
+        self.q, self.k, self.vv = bf(M, self.qd), bf(M, self.kvd), bf(M, self.kvd)
+        self.o, self.o32, self.lse = bf(M, self.qd), f32(M, self.qd), f32(batch, nh, seq)
+        self.ao, self.h_mid = bf(M, H), f32(M, H)
+        self.n2, self.rstd2 = bf(M, H), f32(M)
+        self.g, self.u_, self.sw, self.dn = bf(M, I), bf(M, I), bf(M, I), bf(M, H)
+        # head
+        self.hn, self.rstd_f = bf(M, H), f32(M)
+        self.logits, self.dlogits = bf(M, V), bf(M, V)
+        self.loss = f32(1)
+        # backward
+        self.dh, self.dd = f32(M, H), bf(M, H)
+        self.dsw, self.dg, self.du_ = bf(M, I), bf(M, I), bf(M, I)
+        self.dnx = [bf(M, H) for _ in range(3)]
+        self.do, self.dq, self.dk, self.dv = bf(M, self.qd), bf(M, self.qd), bf(M, self.kvd), bf(M, self.kvd)
+        self.dhn = bf(M, H)
+        # adapter intermediates: u = x . A^T per target (from the latest
+        # forward of the layer), du for the backward
+        self.u = {p: f32(M, r) for p in self.targets}
+        self.du = f32(M, r)
+
+        ws = max(nf4s_workspace_bytes(OP_ATTENTION_BWD, M, nh, 0),
+                 nf4s_workspace_bytes(OP_CROSS_ENTROPY, M, 0, 0),
+                 nf4s_workspace_bytes(OP_DENSE_FWD_PACKED, M, V, H),
+                 nf4s_workspace_bytes(OP_DENSE_BWD_PACKED, M, V, H))
+        pk = max(nf4s_packed_activation_bytes(M, H), nf4s_packed_activation_bytes(M, V))
+        for p in PROJ:
+            no, ki = shapes[p]
+            ws = max(ws, nf4s_workspace_bytes(OP_LINEAR_FWD_PACKED, M, no, ki),
+                     nf4s_workspace_bytes(OP_LINEAR_BWD_PACKED, M, no, ki),
+                     nf4s_workspace_bytes(OP_LORA_FWD, M, no, ki),
+                     nf4s_workspace_bytes(OP_LORA_BWD, M, no, ki))
+            pk = max(pk, nf4s_packed_activation_bytes(M, ki), nf4s_packed_activation_bytes(M, no))
+        self.ws = torch.empty(_round_up(max(ws, ALIGN)), dtype=torch.uint8, device=dev)
+        self.packed = torch.empty(_round_up(pk), dtype=torch.uint8, device=dev)
+        self._packed_key = None
+
+        self.pool = None
+        if mode == "streamed":
+            nb = shards.layout.nbytes
+            self.slots = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in range(n_slots)]
+            self.pool = nf4s_pool_create([s.data_ptr() for s in self.slots], nb,
+                                         self.copy.cuda_stream, self.compute.cuda_stream)
+            for i, hst in enumerate(shards.host):
+                nf4s_pool_set_layer(self.pool, i, hst.data_ptr(), nb)
+        else:
+            self.resident = shards.to_device()
+
+    def close(self):
+        if self.pool is not None:
+            torch.cuda.synchronize()
+            nf4s_pool_destroy(self.pool)
+            self.pool = None
+
+    def stats(self):
+        return nf4s_pool_stats(self.pool) if self.pool is not None else (0, 0)
+
+    # -- helpers ---------------------------------------------------------------------
+    @property
+    def _s(self):
+        return self.compute.cuda_stream
+
+    def _ws(self):
+        return self.ws.data_ptr(), self.ws.numel()
+
+    def _pack(self, a, K):
+        """Pack a (bf16 [M, K]) for the matrix cores unless it was the last
+        input packed; projections sharing an input share the packing."""
+        key = (a.data_ptr(), K)
+        if key != self._packed_key:
+            nf4s_pack_activation(a.data_ptr(), self.M, K, self.packed.data_ptr(), self.packed.numel(),
+                                 self._s)
+            self._packed_key = key
+        return self.packed.data_ptr()
+
+    def _fwd(self, base, i, p, x, y):
+        no, ki = self.sh.shapes[p]
+        xp = self._pack(x, ki)
+        d = self.sh.layout.descs[p]
+        if p in self.targets:
+            A, Bm = self.lora[(i, p)]
+            lora_fwd(x.data_ptr(), self.M, ki, A.data_ptr(), self.r, self.u[p].data_ptr(), *self._ws(),
+                     self._s)
+            streamed_linear_fwd_packed(base, d, xp, self.M, y.data_ptr(), self.u[p].data_ptr(),
+                                       Bm.data_ptr(), self.r, self.scale, *self._ws(), self._s)
+        else:
+            streamed_linear_fwd_packed(base, d, xp, self.M, y.data_ptr(), None, None, 0, 0.0,
+                                       *self._ws(), self._s)
+
+    def _bwd(self, base, i, p, x, dy, dx):
+        no, ki = self.sh.shapes[p]
+        d = self.sh.layout.descs[p]
+        dyp = self._pack(dy, no)
+        if p in self.targets:
+            A, Bm = self.lora[(i, p)]
+            dA, dB = self.lora_grads[(i, p)]
+            lora_bwd(x.data_ptr(), dy.data_ptr(), self.u[p].data_ptr(), self.M, ki, no, Bm.data_ptr(),
+                     self.r, self.scale, dA.data_ptr(), dB.data_ptr(), self.du.data_ptr(), 0,
+                     *self._ws(), self._s)
+            streamed_linear_bwd_packed(base, d, dyp, self.M, dx.data_ptr(), self.du.data_ptr(),
+                                       A.data_ptr(), self.r, *self._ws(), self._s)
+        else:
+            streamed_linear_bwd_packed(base, d, dyp, self.M, dx.data_ptr(), None, None, 0,
+                                       *self._ws(), self._s)
+
+    # -- one layer ---------------------------------------------------------------------
+    def _layer_fwd(self, i, base, recompute):
+        """Layer i's body from h_i. The recompute keeps the fp32 attention
+        output for the backward and skips h_{i+1}, which is already stored."""
+        c, s, M = self.cfg, self._s, self.M
+        H = self.H
+        self._packed_key = None
+        hin, hout = self.h[i], self.h[i + 1]
+        nf4s_rmsnorm_fwd(hin.data_ptr(), self.norms["attn"][i].data_ptr(), M, H, c["eps"],
+                         self.n1.data_ptr(), self.rstd1.data_ptr(), s)
+        self._fwd(base, i, "q", self.n1, self.q)
+        self._fwd(base, i, "k", self.n1, self.k)
+        self._fwd(base, i, "v", self.n1, self.vv)
+        nf4s_rope(self.q.data_ptr(), M, self.S, c["heads"], c["head_dim"], c["rope_theta"], 0, s)
+        nf4s_rope(self.k.data_ptr(), M, self.S, c["kv_heads"], c["head_dim"], c["rope_theta"], 0, s)
+        nf4s_attention_fwd(self.q.data_ptr(), self.k.data_ptr(), self.vv.data_ptr(), self.B, self.S,
+                           c["heads"], c["kv_heads"], c["head_dim"], self.o.data_ptr(),
+                           self.o32.data_ptr() if recompute else None, self.lse.data_ptr(), s)
+        self._fwd(base, i, "o", self.o, self.ao)
+        nf4s_residual_add(hin.data_ptr(), self.ao.data_ptr(), M * H, self.h_mid.data_ptr(), s)
+        nf4s_rmsnorm_fwd(self.h_mid.data_ptr(), self.norms["mlp"][i].data_ptr(), M, H, c["eps"],
+                         self.n2.data_ptr(), self.rstd2.data_ptr(), s)
+        self._fwd(base, i, "gate", self.n2, self.g)
+        self._fwd(base, i, "up", self.n2, self.u_)
+        nf4s_swiglu_fwd(self.g.data_ptr(), self.u_.data_ptr(), M * self.I, self.sw.data_ptr(), s)
+        self._fwd(base, i, "down", self.sw, self.dn)
+        if not recompute:
+            nf4s_residual_add(self.h_mid.data_ptr(), self.dn.data_ptr(), M * H, hout.data_ptr(), s)
+
+    def _layer_bwd(self, i, base):
+        """dh holds dL/dh_{i+1} on entry and dL/dh_i on exit; the layer's body
+        was just recomputed (with the fp32 attention output kept)."""
+        c, s, M, H = self.cfg, self._s, self.M, self.H
+        nf4s_to_bf16(self.dh.data_ptr(), M * H, self.dd.data_ptr(), s)
+        self._packed_key = None  # dd was rewritten
+        self._bwd(base, i, "down", self.sw, self.dd, self.dsw)
+        nf4s_swiglu_bwd(self.dsw.data_ptr(), self.g.data_ptr(), self.u_.data_ptr(), M * self.I,
+                        self.dg.data_ptr(), self.du_.data_ptr(), s)
+        self._bwd(base, i, "gate", self.n2, self.dg, self.dnx[0])
+        self._bwd(base, i, "up", self.n2, self.du_, self.dnx[1])
+        nf4s_rmsnorm_bwd([self.dnx[0].data_ptr(), self.dnx[1].data_ptr()], self.h_mid.data_ptr(),
+                         self.norms["mlp"][i].data_ptr(), self.rstd2.data_ptr(), M, H, 1,
+                         self.dh.data_ptr(), s)
+        nf4s_to_bf16(self.dh.data_ptr(), M * H, self.dd.data_ptr(), s)
+        self._packed_key = None
+        self._bwd(base, i, "o", self.o, self.dd, self.do)
+        nf4s_attention_bwd(self.q.data_ptr(), self.k.data_ptr(), self.vv.data_ptr(),
+                           self.o32.data_ptr(), self.do.data_ptr(), self.lse.data_ptr(), self.B,
+                           self.S, c["heads"], c["kv_heads"], c["head_dim"], self.dq.data_ptr(),
+                           self.dk.data_ptr(), self.dv.data_ptr(), *self._ws(), s)
+        nf4s_rope(self.dq.data_ptr(), M, self.S, c["heads"], c["head_dim"], c["rope_theta"], 1, s)
+        nf4s_rope(self.dk.data_ptr(), M, self.S, c["kv_heads"], c["head_dim"], c["rope_theta"], 1, s)
+        self._bwd(base, i, "q", self.n1, self.dq, self.dnx[0])
+        self._bwd(base, i, "k", self.n1, self.dk, self.dnx[1])
+        self._bwd(base, i, "v", self.n1, self.dv, self.dnx[2])
+        nf4s_rmsnorm_bwd([x.data_ptr() for x in self.dnx], self.h[i].data_ptr(),
+                         self.norms["attn"][i].data_ptr(), self.rstd1.data_ptr(), M, H, 1,
+                         self.dh.data_ptr(), s)
+
+    # -- the step ----------------------------------------------------------------------
+    def forward_backward(self, ids, targets):
+        """Queue the forward and backward sweeps for token ids / next-token
+        targets (device int64 [batch*seq]); returns at once. The loss lands in
+        self.loss, the logits in self.logits, adapter gradients in self.grads."""
+        c, M, H, V = self.cfg, self.M, self.H, self.V
+        assert ids.numel() == M and targets.numel() == M
+        assert ids.dtype == torch.int64 and targets.dtype == torch.int64
+        self.compute.wait_stream(torch.cuda.current_stream())
+        s = self._s
+        L = self.L
+        nf4s_embed(self.embed.data_ptr(), V, H, ids.data_ptr(), M, self.h[0].data_ptr(), s)
+        for i in range(L):
+            base = self._acquire(i, nxt=i + 1 if i + 1 < L else None)
+            self._layer_fwd(i, base, recompute=False)
+            self._release(i)
+        # head: final norm, resident lm_head, cross-entropy
+        self._packed_key = None
+        nf4s_rmsnorm_fwd(self.h[L].data_ptr(), self.norms["final"].data_ptr(), M, H, c["eps"],
+                         self.hn.data_ptr(), self.rstd_f.data_ptr(), s)
+        dense_linear_fwd_packed(self.lm_head.data_ptr(), V, H, self._pack(self.hn, H), M,
+                                self.logits.data_ptr(), *self._ws(), s)
+        nf4s_cross_entropy(self.logits.data_ptr(), targets.data_ptr(), M, V, self.loss.data_ptr(),
+                           self.dlogits.data_ptr(), *self._ws(), s)
+        dense_linear_bwd_packed(self.lm_head.data_ptr(), V, H, self._pack(self.dlogits, V), M,
+                                self.dhn.data_ptr(), *self._ws(), s)
+        nf4s_rmsnorm_bwd([self.dhn.data_ptr()], self.h[L].data_ptr(), self.norms["final"].data_ptr(),
+                         self.rstd_f.data_ptr(), M, H, 0, self.dh.data_ptr(), s)
+        # backward sweep: recompute layer i from its checkpoint, differentiate
+        for i in range(L - 1, -1, -1):
+            base = self._acquire(i, nxt=i - 1 if i > 0 else None)
+            self._layer_fwd(i, base, recompute=True)
+            self._layer_bwd(i, base)
+            self._release(i)
+        torch.cuda.current_stream().wait_stream(self.compute)
+
+    def optimizer_step(self):
+        """AdamW on every adapter parameter (one launch over the flat buffer)."""
+        self.t += 1
+        self.compute.wait_stream(torch.cuda.current_stream())
+        nf4s_adamw(self.params.data_ptr(), self.grads.data_ptr(), self.m.data_ptr(), self.v.data_ptr(),
+                   self.n_params, self.lr, self.betas[0], self.betas[1], self.adam_eps, self.wd,
+                   self.t, self._s)
+        torch.cuda.current_stream().wait_stream(self.compute)
+
+    def step(self, ids, targets):
+        self.forward_backward(ids, targets)
+        self.optimizer_step()
+
+    def _acquire(self, i, nxt):
+        if self.pool is None:
+            return self.resident[i].data_ptr()
+        base = nf4s_pool_acquire(self.pool, i)
+        if nxt is not None:
+            nf4s_pool_prefetch(self.pool, nxt)
+        return base
+
+    def _release(self, i):
+        if self.pool is not None:
+            nf4s_pool_release(self.pool, i)

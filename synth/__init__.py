@@ -122,6 +122,13 @@ def embedding(model: str, which: str = "embed", sigma: float = 0.02) -> np.ndarr
     return _rng(seed).standard_normal((c["vocab"], c["hidden"]), dtype=np.float32) * np.float32(sigma)
 
 
+def embedding_bits(model: str, which: str = "embed", sigma: float = 0.02) -> np.ndarray:
+    """The same table handed over as bf16 bit patterns (uint16, truncated):
+    embeddings and lm_head are stored in bf16."""
+    f = embedding(model, which, sigma)
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
 def norm_weight(model: str, layer: int, which: str, sigma: float = 0.02) -> np.ndarray:
     """RMSNorm weight [hidden] ~ N(1, sigma) float32 (which: attn, mlp, final)."""
     c = DECODER[model]

@@ -219,3 +219,48 @@ def test_packed_workspace_is_split_partials_only():
     assert need > 0 and need % (512 * 4096 * 4) == 0
     full = L.nf4s_workspace_bytes(L.OP_LINEAR_FWD, 512, 4096, 4096)
     assert full == need + L.nf4s_packed_activation_bytes(512, 4096)
+
+
+def _err(fn, *args):
+    with pytest.raises(L.Nf4sError) as e:
+        fn(*args)
+    return e.value.code
+
+
+def test_decoder_argument_errors():
+    """The decoder entry points validate on the host before any launch."""
+    assert _err(L.nf4s_rope, None, 4, 2, 2, 16, 1e4, 0) == L.EINVAL
+    assert _err(L.nf4s_rope, FAKE, 6, 4, 2, 16, 1e4, 0) == L.ESHAPE        # rows % seq
+    assert _err(L.nf4s_rope, FAKE, 6, 3, 1, 24, 1e4, 0) == L.ESHAPE        # no kernel for d=24
+    assert _err(L.nf4s_rope, FAKE, 6, 3, 1, 16, 1.0, 0) == L.EINVAL        # theta
+    assert _err(L.nf4s_rope, FAKE + 1, 6, 3, 1, 16, 1e4, 0) == L.EALIGN
+    assert _err(L.nf4s_attention_fwd, FAKE, FAKE, FAKE, 1, 4, 3, 2, 16, FAKE, None, FAKE) == L.ESHAPE
+    assert _err(L.nf4s_attention_fwd, FAKE, FAKE, FAKE, 0, 4, 4, 2, 16, FAKE, None, FAKE) == L.ESHAPE
+    assert _err(L.nf4s_attention_bwd, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 4, 2, 16, FAKE, FAKE,
+                FAKE, None, 0) == L.EWORKSPACE
+    assert _err(L.nf4s_rmsnorm_bwd, [], FAKE, FAKE, FAKE, 4, 4, 0, FAKE) == L.EINVAL
+    assert _err(L.nf4s_rmsnorm_bwd, [FAKE] * 4, FAKE, FAKE, FAKE, 4, 4, 0, FAKE) == L.EINVAL
+    assert _err(L.nf4s_rmsnorm_bwd, [FAKE], FAKE, FAKE, FAKE, 4, 4, 2, FAKE) == L.EINVAL
+    assert _err(L.nf4s_rmsnorm_fwd, FAKE, FAKE, 4, 4, 0.0, FAKE, FAKE) == L.EINVAL   # eps
+    assert _err(L.nf4s_rmsnorm_fwd, FAKE, FAKE, 0, 4, 1e-5, FAKE, FAKE) == L.ESHAPE
+    assert _err(L.nf4s_adamw, FAKE, FAKE, FAKE, FAKE, 16, 1e-3, 0.9, 0.999, 1e-8, 0.0, 0) == L.EINVAL
+    assert _err(L.nf4s_adamw, FAKE, FAKE, FAKE, FAKE, 16, 1e-3, 1.0, 0.999, 1e-8, 0.0, 1) == L.EINVAL
+    assert _err(L.nf4s_cross_entropy, FAKE, FAKE, 8, 100, FAKE, FAKE, FAKE, 4) == L.EWORKSPACE
+    assert _err(L.nf4s_cross_entropy, FAKE, FAKE + 4, 8, 100, FAKE, FAKE, FAKE, 1 << 20) == L.EALIGN
+    assert _err(L.nf4s_embed, FAKE, 0, 64, FAKE, 4, FAKE) == L.ESHAPE
+    assert _err(L.nf4s_swiglu_fwd, FAKE, FAKE, 0, FAKE) == L.ESHAPE
+    assert _err(L.nf4s_residual_add, FAKE, FAKE, 16, None) == L.EINVAL
+    assert _err(L.nf4s_to_bf16, FAKE + 2, 16, FAKE) == L.EALIGN
+    # the dense (lm_head) GEMM: whole 64-blocks along k_in, split partials required
+    assert _err(L.dense_linear_fwd_packed, FAKE, 256, 100, FAKE, 16, FAKE, None, 0) == L.ESHAPE
+    need = L.nf4s_workspace_bytes(L.OP_DENSE_BWD_PACKED, 512, 128256, 4096)
+    assert need > 0
+    assert _err(L.dense_linear_bwd_packed, FAKE, 128256, 4096, FAKE, 512, FAKE, None, 0) == L.EWORKSPACE
+
+
+def test_decoder_workspace_sizes():
+    assert L.nf4s_workspace_bytes(L.OP_ATTENTION_BWD, 512, 32, 0) == 512 * 32 * 4
+    assert L.nf4s_workspace_bytes(L.OP_CROSS_ENTROPY, 512, 0, 0) == 512 * 4
+    assert L.nf4s_workspace_bytes(L.OP_DENSE_FWD_PACKED, 512, 128256, 4096) == 0   # 2004 tiles
+    with pytest.raises(L.Nf4sError):
+        L.nf4s_workspace_bytes(L.OP_ATTENTION_BWD, 0, 32, 0)

@@ -1,23 +1,31 @@
-"""Benchmark: streamed NF4 + LoRA linear-stack training step on one MI355X.
+"""Benchmark: streamed NF4 + LoRA training step on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--gpus 1]
 
-Workload (default, 8B-shaped, batch 1 x seq 512): 32 layers of the
-Llama-3.1-8B projection shapes (q 4096x4096, k/v 1024x4096, o 4096x4096,
-gate/up 14336x4096, down 4096x14336) as NF4 double-quant shards in pinned host
-memory, LoRA r16 alpha32 on q and v, a 2-slot device pool fed by a side copy
-stream. One step = forward sweep over the 32 layers (prefetching i+1) and a
-backward sweep (prefetching i-1) that recomputes each layer and produces
-dx plus the LoRA gradients. Inputs are seeded synthetic tensors: W ~ N(0,0.02),
-x, dy ~ N(0,1) bf16, A, B ~ N(0,0.01); the pages' real checkpoints and data
-are not available and these shapes stand in for them.
+Workload (default, 8B-shaped, batch 1 x seq 512): the training step of a
+llama decoder of Llama-3.1-8B shape (32 layers, hidden 4096, 32 heads over 8
+KV heads, vocab 128256) whose seven projections per layer (q 4096x4096, k/v
+1024x4096, o 4096x4096, gate/up 14336x4096, down 4096x14336) are NF4
+double-quant shards in pinned host memory, streamed through a 2-slot device
+pool by a side copy stream; embedding and lm_head resident in bf16; LoRA r16
+alpha32 on q and v; AdamW on the adapters. One step = embedding, a forward
+sweep over the 32 layers (prefetching i+1) keeping only each layer's input,
+lm_head and cross-entropy, a backward sweep (prefetching i-1) that recomputes
+each layer and differentiates it, and the optimiser update. The linear stack
+alone (the seven projections per layer with seeded inputs and upstream
+gradients, no attention/norms/head) is timed beside it. Inputs are seeded
+synthetic tensors: W ~ N(0,0.02), embeddings N(0,0.02) bf16, norm weights
+N(1,0.02), token ids uniform, A, B ~ N(0,0.01); the pages' real checkpoints
+and data are not available and these shapes stand in for them.
 
-Prints one JSON line. value = streamed tokens/s (B*S per step time); extra
-fields carry the resident run, the step's achieved TFLOP/s against the bf16
-MFMA peak (6 FLOP per frozen linear weight and token: 2 forward, 2 recompute,
-2 dL/dx), the H2D rate against the host link, the roofline of the dominant
-kernel (the forward fused dequant GEMM) timed live with HIP events, and the
-CPU oracle timed on a bounded sample of the same step.
+Prints one JSON line. value = streamed tokens/s of the decoder step (B*S per
+step time); extra fields carry the resident run, the step's achieved TFLOP/s
+against the bf16 MFMA peak (the pages' convention: 6 FLOP per frozen linear
+weight and token -- 2 forward, 2 recompute, 2 dL/dx -- plus 4 per lm_head
+weight; attention and LoRA FLOPs not counted), the H2D rate against the host
+link, the roofline of the dominant kernel (the forward fused dequant GEMM)
+timed live with HIP events inside the decoder step, the linear stack, and
+the CPU oracle timed on a bounded sample of the same step.
 """
 from __future__ import annotations
 
@@ -174,6 +182,60 @@ def _cpu_baseline(model: str, M: int, targets) -> dict:
                       f"dequantise + fp64 forward/backward in {dt:.2f} s, scaled x{n_layers} layers"}
 
 
+def _cpu_baseline_decoder(model: str, batch: int, seq: int, targets) -> dict:
+    """The decoder oracle, as it stands, on a bounded sample of the same step:
+    the fp64 forward and backward of the head alone (embedding, final norm,
+    lm_head, cross-entropy; no layer) and of one full layer plus the head,
+    both timed, and the dequantisation of the layer's q tensor, timed and
+    scaled to the layer's parameters. The step is the head plus L layers.
+    The oracle caches activations
+    instead of recomputing; weight values do not change its time, so the
+    sample uses the seeded fp32 weights and one table for embedding and
+    lm_head."""
+    import numpy as np
+
+    from oracle import decoder as odec, nf4 as onf4
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    c = dict(synth.DECODER[model])
+    c.pop("tied")
+    n_layers = c["layers"]
+    sh = synth.SHAPES[model]
+    qq = onf4.quantize(synth.weight(0, "q", *sh["q"]))
+    t0 = time.perf_counter()
+    onf4.dequantize_bf16(qq)
+    p_layer = sum(a * b for a, b in sh.values())
+    t_deq = (time.perf_counter() - t0) * p_layer / (sh["q"][0] * sh["q"][1])
+    W = [{p: synth.weight(0, p, *sh[p]).astype(np.float64) for p in odec.PROJ}]
+    E = synth.bf16_bits_to_f32(synth.embedding_bits(model)).astype(np.float64)
+    lora = [{p: tuple(a.astype(np.float64) for a in synth.lora_pair(0, p, *sh[p])) for p in targets}]
+    ids, tg = synth.token_batch(model, batch, seq)
+    norm = lambda w: synth.norm_weight(model, 0, w).astype(np.float64)  # noqa: E731
+    def timed(layers):
+        cfg = odec.Config(**{**c, "layers": layers}, targets=tuple(targets))
+        P = odec.Params(embed=E, lm_head=E, w_attn=[norm("attn")] * layers,
+                        w_mlp=[norm("mlp")] * layers, w_final=norm("final"), W=W[:layers],
+                        lora=lora[:layers])
+        t0 = time.perf_counter()
+        _, _, cache = odec.forward(P, ids, tg, cfg)
+        odec.backward(P, cache, cfg)
+        return time.perf_counter() - t0
+
+    t_head = timed(0)
+    t_one = timed(1)
+    t_layer = t_one - t_head + t_deq
+    t_step = t_head + n_layers * t_layer
+    M = batch * seq
+    return {"value": M / t_step, "unit": "tok/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{model} decoder at B{batch} S{seq} (LoRA {'/'.join(targets)}), fp64 "
+                      f"forward + backward: head alone {t_head:.2f} s, one layer + head "
+                      f"{t_one:.2f} s; layer dequantisation {t_deq:.2f} s (scaled from q); "
+                      f"step = head + {n_layers} x layer = {t_step:.1f} s"}
+
+
 def sweep(args) -> None:
     """Where the copies hide: the 8B linear stack streamed and resident at
     batch x 512 tokens for batch 1..16 (n = 2 slots, LoRA q/v), and at batch 4
@@ -279,6 +341,10 @@ def main():
     ap.add_argument("--slots", type=int, default=None)
     ap.add_argument("--no-resident", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decoder", action="store_true",
+                    help="time the linear stack only (no attention, norms, lm_head, optimizer)")
+    ap.add_argument("--no-linear", action="store_true",
+                    help="skip the linear-stack legs (decoder configurations only)")
     ap.add_argument("--profile-gemm", default=None,
                     help="only run one fused GEMM shape, e.g. fwd:14336:4096:512 (for rocprofv3)")
     ap.add_argument("--reps", type=int, default=5)
@@ -370,13 +436,70 @@ def main():
         st.close()
         return dt, (b1 - b0) / args.steps, (c1 - c0) / args.steps, durs
 
-    dt_s, h2d_bytes, copies, durs = run("streamed", slots, True)
-    print(f"[bench] streamed: {dt_s * 1e3:.1f} ms/step, {copies:.0f} copies/step", file=sys.stderr,
-          flush=True)
-    dt_r = None
-    if not args.no_resident:
-        dt_r, _, _, _ = run("resident", slots, False)
-        print(f"[bench] resident: {dt_r * 1e3:.1f} ms/step", file=sys.stderr, flush=True)
+    use_decoder = model in synth.DECODER and reference is None and not args.no_decoder
+    # the linear stack: the streamed projections alone
+    lin_s = lin_r = None
+    lin_copies, lin_durs = 0, []
+    if not (use_decoder and args.no_linear):
+        lin_s, lin_h2d, lin_copies, lin_durs = run("streamed", slots, not use_decoder)
+        print(f"[bench] linear stack streamed: {lin_s * 1e3:.1f} ms/step, {lin_copies:.0f} "
+              f"copies/step", file=sys.stderr, flush=True)
+        if not args.no_resident:
+            lin_r, _, _, _ = run("resident", slots, False)
+            print(f"[bench] linear stack resident: {lin_r * 1e3:.1f} ms/step", file=sys.stderr,
+                  flush=True)
+
+    dec = None
+    if use_decoder:
+        from layer_streamed_nf4_amd.decoder import Decoder
+
+        c = synth.DECODER[model]
+        V, H = c["vocab"], c["hidden"]
+        gen.manual_seed(synth.BASE_SEED + 500_000)
+        embed = (torch.randn((V, H), generator=gen, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16)
+        if c["tied"]:
+            head = embed
+        else:
+            gen.manual_seed(synth.BASE_SEED + 500_001)
+            head = (torch.randn((V, H), generator=gen, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16)
+        norms = {w: [torch.from_numpy(synth.norm_weight(model, i, w)).to(dev) for i in range(n_layers)]
+                 for w in ("attn", "mlp")}
+        norms["final"] = torch.from_numpy(synth.norm_weight(model, 0, "final")).to(dev)
+        lora_map = {(i, p): lora[i][p] for i in range(n_layers) for p in targets}
+        ids_np, tg_np = synth.token_batch(model, batch, seq)
+        ids = torch.from_numpy(ids_np.reshape(-1)).to(dev)
+        tgs = torch.from_numpy(tg_np.reshape(-1)).to(dev)
+
+        def run_dec(mode, n_slots, timed):
+            d = Decoder(c, shards, embed, head, norms, lora_map, batch, seq, targets=targets,
+                        n_slots=n_slots, mode=mode, time_calls=plain_fwd if timed else None)
+            for _ in range(args.warmup):
+                d.step(ids, tgs)
+            torch.cuda.synchronize()
+            d.timed.clear()
+            c0, b0 = d.stats()
+            t = time.perf_counter()
+            for _ in range(args.steps):
+                d.step(ids, tgs)
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t) / args.steps
+            c1, b1 = d.stats()
+            durs = [(n, k, s_.elapsed_time(e_)) for (_, n, k, s_, e_) in d.timed]
+            loss = float(d.loss.item())
+            d.close()
+            return dt, (b1 - b0) / args.steps, (c1 - c0) / args.steps, durs, loss
+
+        dt_s, h2d_bytes, copies, durs, loss_s = run_dec("streamed", slots, True)
+        print(f"[bench] decoder streamed: {dt_s * 1e3:.1f} ms/step, {copies:.0f} copies/step, "
+              f"loss {loss_s:.4f}", file=sys.stderr, flush=True)
+        dt_r, loss_r = None, None
+        if not args.no_resident:
+            dt_r, _, _, _, loss_r = run_dec("resident", slots, False)
+            print(f"[bench] decoder resident: {dt_r * 1e3:.1f} ms/step, loss {loss_r:.4f}",
+                  file=sys.stderr, flush=True)
+        dec = dict(loss_streamed=loss_s, loss_resident=loss_r)
+    else:
+        dt_s, h2d_bytes, copies, durs, dt_r = lin_s, lin_h2d, lin_copies, lin_durs, lin_r
 
     # same-session ceilings: hipBLASLt bf16 GEMM at the dominant shape, pinned H2D
     n_d, k_d = sh["gate"]
@@ -408,7 +531,8 @@ def main():
     del host, devb
 
     tokens = M
-    f_tok = flops_per_token(model, lm_head=False, reference=reference is not None)
+    f_tok = flops_per_token(model, lm_head=use_decoder, reference=reference is not None)
+    f_lin = flops_per_token(model, lm_head=False, reference=reference is not None)
     value = tokens / dt_s
     step_tflops = f_tok * tokens / dt_s / 1e12
     dom_ms = [d for (_, _, d) in durs]
@@ -425,6 +549,17 @@ def main():
                     "kernel": "k_gemm<fwd,plain> (fused NF4 dequant + bf16 MFMA, x.W'^T)",
                     "launches": len(dom_ms), "avg_us": round(avg_ms * 1e3, 2),
                     "flop_per_launch": int(avg_flop)}
+    if use_decoder:
+        workload = (f"decoder training step: llama {model} ({n_layers} layers, hidden {H}, "
+                    f"{c['heads']} heads / {c['kv_heads']} KV heads, vocab {V}); the seven "
+                    f"projections per layer streamed from pinned host as NF4 shards, embedding "
+                    f"and lm_head resident bf16, checkpointed layers recomputed in the backward, "
+                    f"AdamW on the adapters")
+    else:
+        workload = (f"linear stack: {n_layers} layers of {model} projection shapes "
+                    f"(q,k,v,o,gate,up,down), streamed from pinned host, recompute in backward"
+                    + (f", preference step (reference pass with adapters off, {reference})"
+                       if reference else ""))
     out = {
         "metric": "streamed NF4+LoRA train tok/s, 8B layer shape seq512; % of bf16 MFMA peak",
         "value": round(value, 1),
@@ -437,13 +572,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,0.02) weights in NF4 double-quant, N(0,1) bf16 x/dy, "
-                "N(0,0.01) LoRA A/B; shapes stand in for the pages' checkpoints)",
-        "config": {"workload": f"linear stack: {n_layers} layers of {model} projection shapes "
-                               f"(q,k,v,o,gate,up,down), streamed from pinned host, "
-                               f"recompute in backward"
-                               + (f", preference step (reference pass with adapters off, "
-                                  f"{reference})" if reference else ""),
+        "data": "synthetic (seeded N(0,0.02) weights in NF4 double-quant, N(0,0.02) bf16 "
+                "embeddings, N(1,0.02) norm weights, uniform token ids, N(0,0.01) LoRA A/B; "
+                "shapes stand in for the pages' checkpoints and data)",
+        "config": {"workload": workload,
                    "global_batch": batch, "seq_len": seq, "tokens_per_step": tokens,
                    "lora": {"r": synth.LORA_R, "alpha": synth.LORA_ALPHA, "targets": list(targets)},
                    "slots": slots, "parallelism": "single GPU"},
@@ -465,9 +597,17 @@ def main():
         "context": "pages (NVIDIA, full model incl. attention/lm_head/optimizer): 119.6 tok/s at "
                    "3.32 GB on an RTX 3050 Laptop 4 GB, 113 tok/s on an H100 -- context only",
     }
+    if use_decoder:
+        out["decoder"] = dec
+        out["linear_stack"] = None if lin_s is None else {
+            "streamed_tok_s": round(tokens / lin_s, 1), "streamed_ms_per_step": round(lin_s * 1e3, 3),
+            "resident_tok_s": None if lin_r is None else round(tokens / lin_r, 1),
+            "resident_ms_per_step": None if lin_r is None else round(lin_r * 1e3, 3),
+            "flop_per_token": f_lin, "copies_per_step": lin_copies}
     if not args.no_cpu:
-        print("[bench] timing the CPU oracle on one layer", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = _cpu_baseline(model, M, targets)
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = (_cpu_baseline_decoder(model, batch, seq, targets) if use_decoder
+                               else _cpu_baseline(model, M, targets))
     print(json.dumps(out), flush=True)
 
 

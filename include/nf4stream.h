@@ -146,7 +146,7 @@ uint64_t nf4s_table_hash(void);
 #define NF4S_OP_LINEAR_BWD_PACKED 7
 #define NF4S_OP_DENSE_FWD_PACKED 8   /* split partials of dense_linear_fwd_packed */
 #define NF4S_OP_DENSE_BWD_PACKED 9   /* split partials of dense_linear_bwd_packed */
-#define NF4S_OP_ATTENTION_BWD 10     /* M = tokens, n_out = heads (k_in ignored) */
+#define NF4S_OP_ATTENTION_BWD 10     /* M = tokens, n_out = heads, k_in = head_dim */
 #define NF4S_OP_CROSS_ENTROPY 11     /* M = tokens (n_out, k_in ignored) */
 int nf4s_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, size_t* bytes);
 
@@ -330,8 +330,8 @@ int nf4s_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float* x, const
  * Rotary embedding, rotate-half form, in place on bf16 x [T, heads*head_dim]:
  * row t is position t % S; pair (j, j + d/2) of each head is rotated by the
  * angle (t % S) * theta^(-2j/d) (inverse = 1: by minus that angle, which is
- * the backward of the rotation). Results rounded to bf16. head_dim in
- * {16, 32, 64, 128}; T a multiple of S. Errors: EINVAL, ESHAPE, EALIGN.
+ * the backward of the rotation). Results rounded to bf16. head_dim even,
+ * at most 256; T a multiple of S. Errors: EINVAL, ESHAPE, EALIGN.
  */
 int nf4s_rope(uint16_t* x, int64_t T, int64_t S, int heads, int head_dim, double theta, int inverse,
               void* stream);
@@ -346,9 +346,12 @@ int nf4s_rope(uint16_t* x, int64_t T, int64_t S, int heads, int head_dim, double
  * Backward from dout bf16 [B*S, heads*d]: dq bf16 (like q), dk, dv bf16 (like
  * k, summed over the heads of a group in head order), with
  * dS = P * (dP - rowsum(P * dP)) and rowsum(P * dP) = dout . o_f32.
- * ws: nf4s_workspace_bytes(NF4S_OP_ATTENTION_BWD, B*S, heads, 0) bytes.
- * head_dim in {16, 32, 64, 128}; heads % kv_heads == 0.
- * Errors: EINVAL, ESHAPE, EALIGN, EWORKSPACE.
+ * ws: nf4s_workspace_bytes(NF4S_OP_ATTENTION_BWD, B*S, heads, head_dim)
+ * bytes (rowsum and per-head fp32 partials of dk, dv, summed per group in
+ * head order). The products run on the matrix cores with P and dS split into
+ * bf16 high + low parts (about 16 significant bits), fp32 accumulation.
+ * head_dim in {32, 64, 128}; heads % kv_heads == 0; every tensor argument
+ * except lse 16-byte aligned. Errors: EINVAL, ESHAPE, EALIGN, EWORKSPACE.
  */
 int nf4s_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
                        int64_t S, int heads, int kv_heads, int head_dim, uint16_t* o, float* o_f32,

@@ -170,7 +170,9 @@ int nf4s_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, size_t*
       return NF4S_OK;
     }
     if (n_out <= 0 || n_out > 1024) return fail(NF4S_ESHAPE, "heads=%lld out of range", (long long)n_out);
-    *bytes = attention_bwd_ws_bytes(1, M, (int)n_out);
+    if (k_in != 32 && k_in != 64 && k_in != 128)
+      return fail(NF4S_ESHAPE, "head_dim=%lld not one of 32, 64, 128", (long long)k_in);
+    *bytes = attention_bwd_ws_bytes(1, M, (int)n_out, (int)k_in);
     return NF4S_OK;
   }
   int rc = check_shape(n_out, k_in);
@@ -502,8 +504,8 @@ int nf4s_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float* x, const
 
 static int check_heads(int heads, int head_dim) {
   if (heads <= 0 || heads > 1024) return fail(NF4S_ESHAPE, "heads=%d out of range", heads);
-  if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
-    return fail(NF4S_ESHAPE, "head_dim=%d not one of 16, 32, 64, 128", head_dim);
+  if (head_dim <= 0 || head_dim > 256 || head_dim % 2)
+    return fail(NF4S_ESHAPE, "head_dim=%d must be even and at most 256", head_dim);
   return NF4S_OK;
 }
 
@@ -523,10 +525,14 @@ int nf4s_rope(uint16_t* x, int64_t T, int64_t S, int heads, int head_dim, double
 static int check_attention(int64_t B, int64_t S, int heads, int kv_heads, int head_dim) {
   int rc;
   if ((rc = check_heads(heads, head_dim))) return rc;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return fail(NF4S_ESHAPE, "head_dim=%d not one of 32, 64, 128", head_dim);
   if (kv_heads <= 0 || heads % kv_heads)
     return fail(NF4S_ESHAPE, "heads=%d is not a multiple of kv_heads=%d", heads, kv_heads);
   if (B <= 0 || S <= 0 || B * S > (1ll << 24) || B * heads * ((S + 63) / 64) >= (1ll << 31))
     return fail(NF4S_ESHAPE, "batch=%lld seq=%lld out of range", (long long)B, (long long)S);
+  if (B * S * heads * head_dim >= (1ll << 31) / 4)
+    return fail(NF4S_ESHAPE, "attention of %lld tokens x %d heads too large", (long long)(B * S), heads);
   return NF4S_OK;
 }
 
@@ -535,10 +541,11 @@ int nf4s_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        float* lse, void* stream) {
   int rc;
   if ((rc = check_attention(B, S, heads, kv_heads, head_dim))) return rc;
-  if ((rc = check_ptr(q, "q", 2)) || (rc = check_ptr(k, "k", 2)) || (rc = check_ptr(v, "v", 2)) ||
-      (rc = check_ptr(o, "o", 2)) || (rc = check_ptr(lse, "lse", 4)))
+  // the kernels move 16-byte fragments of q, k, v and store o / o_f32 in 8- and 16-byte pieces
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
+      (rc = check_ptr(o, "o")) || (rc = check_ptr(lse, "lse", 4)))
     return rc;
-  if (o_f32 && (rc = check_ptr(o_f32, "o_f32", 4))) return rc;
+  if (o_f32 && (rc = check_ptr(o_f32, "o_f32"))) return rc;
   return launched(launch_attention_fwd(q, k, v, B, S, heads, kv_heads, head_dim, o, o_f32, lse,
                                        static_cast<hipStream_t>(stream)),
                   "attention_fwd launch");
@@ -550,12 +557,12 @@ int nf4s_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                        void* ws, size_t ws_bytes, void* stream) {
   int rc;
   if ((rc = check_attention(B, S, heads, kv_heads, head_dim))) return rc;
-  if ((rc = check_ptr(q, "q", 2)) || (rc = check_ptr(k, "k", 2)) || (rc = check_ptr(v, "v", 2)) ||
-      (rc = check_ptr(o_f32, "o_f32", 4)) || (rc = check_ptr(dout, "dout", 2)) ||
-      (rc = check_ptr(lse, "lse", 4)) || (rc = check_ptr(dq, "dq", 2)) || (rc = check_ptr(dk, "dk", 2)) ||
-      (rc = check_ptr(dv, "dv", 2)))
+  if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
+      (rc = check_ptr(o_f32, "o_f32")) || (rc = check_ptr(dout, "dout")) ||
+      (rc = check_ptr(lse, "lse", 4)) || (rc = check_ptr(dq, "dq")) || (rc = check_ptr(dk, "dk")) ||
+      (rc = check_ptr(dv, "dv")))
     return rc;
-  if ((rc = check_ws(ws, ws_bytes, attention_bwd_ws_bytes(B, S, heads)))) return rc;
+  if ((rc = check_ws(ws, ws_bytes, attention_bwd_ws_bytes(B, S, heads, head_dim)))) return rc;
   return launched(launch_attention_bwd(q, k, v, o_f32, dout, lse, B, S, heads, kv_heads, head_dim, dq,
                                        dk, dv, ws, static_cast<hipStream_t>(stream)),
                   "attention_bwd launch");

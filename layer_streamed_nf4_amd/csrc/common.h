@@ -94,7 +94,7 @@ hipError_t launch_rope(uint16_t* x, int64_t T, int64_t S, int heads, int d, doub
 hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
                                 int64_t S, int H, int Hkv, int D, uint16_t* o, float* o_f32,
                                 float* lse, hipStream_t s);
-size_t attention_bwd_ws_bytes(int64_t B, int64_t S, int H);
+size_t attention_bwd_ws_bytes(int64_t B, int64_t S, int H, int D);
 hipError_t launch_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const float* o_f32, const uint16_t* dout, const float* lse,
                                 int64_t B, int64_t S, int H, int Hkv, int D, uint16_t* dq,

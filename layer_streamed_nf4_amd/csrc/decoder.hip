@@ -131,246 +131,426 @@ __global__ __launch_bounds__(256) void k_rope(uint16_t* __restrict__ x, int64_t 
   v[j + half] = f2bf(x2 * c + x1 * s);
 }
 
-// ---- attention --------------------------------------------------------------
-// A workgroup owns 64 query rows of one (sequence, head); 4 lanes per query,
-// each holding d/4 of the query and of the output accumulator. Key/value
-// blocks of 64 rows are staged in LDS as bf16. Online softmax in fp32.
-constexpr int QB = 64;  // queries (and keys) per block
-constexpr int MAXD = 128;
+// ---- attention on the matrix cores -------------------------------------------
+// One wave per 32-row block of one (sequence, head), v_mfma_f32_32x32x16_bf16.
+// Operand layouts of that instruction: lane l supplies row (A) or column (B)
+// l%32 and the 8 contraction values 8*(l/32) .. +8 of a 16-wide step; result
+// register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+//
+// The query-side kernels compute the transposed products S^T = K . Q^T and
+// O^T = V^T . P^T (dQ^T = K^T . dS^T), so that lane l owns query l%32: the
+// softmax statistics and the rescaling of the output stay in the lane, and
+// the row reductions are in-register plus one exchange between the two
+// half-waves. The key-side kernel computes S = Q . K^T and dV^T = dO^T . P,
+// dK^T = Q^T . dS with lane l owning key l%32.
+//
+// The probabilities (and dS) feed the next product without moving: its
+// contraction index is taken in the order the score registers hold it --
+// step kk, lane half hf, slot e <-> position 16kk + 8(e/4) + 4hf + e%4 of the
+// 32-block -- and the other operand is read from a transposed LDS tile in
+// that same order (two 8-byte reads of four consecutive positions). P and dS
+// enter the matrix cores as a bf16 high part plus a bf16 low part (about 16
+// significant bits), K, Q, V and dO are bf16 already, and accumulation is
+// fp32, so the attention arithmetic keeps fp32-level accuracy.
+constexpr int AB = 32;  // rows per block (queries or keys)
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.0f;
+  return z;
+}
+
+// Eight fp32 values as bf16 high and low parts (hi + lo carries ~16 bits).
+__device__ __forceinline__ void split8(const float* x, bf16x8_t& hi, bf16x8_t& lo) {
+  u32x4_t h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t hp = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    const float h0 = __uint_as_float(hp << 16), h1 = __uint_as_float(hp & 0xFFFF0000u);
+    h[i] = hp;
+    l[i] = pack_bf16x2(x[2 * i] - h0, x[2 * i + 1] - h1);
+  }
+  hi = __builtin_bit_cast(bf16x8_t, h);
+  lo = __builtin_bit_cast(bf16x8_t, l);
+}
+
+// Row offset of result register r in its 32x32 tile for lane half hf.
+__device__ __forceinline__ int crow(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
+
+// Stage rows [r0, r0 + 32) (clamped to the sequence) of a [rows, ld] bf16
+// matrix, columns [c0, c0 + D), into LDS: row-major `rm` (row stride D + 8)
+// and/or transposed `tr` (tr[d * TS + row], row stride TS = 36). Each lane
+// moves four rows x 8 columns per item: four 16-byte loads, four 16-byte
+// row-major stores and eight 8-byte transposed stores.
+template <int D>
+__device__ __forceinline__ void stage_block(const uint16_t* __restrict__ src, int64_t ld, int64_t c0,
+                                            int64_t base_row, int64_t r0, int64_t S, uint16_t* rm,
+                                            uint16_t* tr, int lane) {
+  constexpr int RS = D + 8, TS = 36, CH = D / 8;
+  for (int it = lane; it < 8 * CH; it += 64) {
+    const int rg = it / CH, ch = it % CH;  // rows 4rg..4rg+3, columns 8ch..8ch+7
+    u32x4_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t rr = r0 + 4 * rg + i;
+      const int64_t row = base_row + (rr < S ? rr : S - 1);
+      v[i] = *reinterpret_cast<const u32x4_t*>(src + row * ld + c0 + 8 * ch);
+      if (rm != nullptr) *reinterpret_cast<u32x4_t*>(rm + (4 * rg + i) * RS + 8 * ch) = v[i];
+    }
+    if (tr != nullptr) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = (e & 1) * 16;
+        uint2 w;
+        w.x = ((v[0][e >> 1] >> sh) & 0xFFFFu) | (((v[1][e >> 1] >> sh) & 0xFFFFu) << 16);
+        w.y = ((v[2][e >> 1] >> sh) & 0xFFFFu) | (((v[3][e >> 1] >> sh) & 0xFFFFu) << 16);
+        *reinterpret_cast<uint2*>(tr + (8 * ch + e) * TS + 4 * rg) = w;
+      }
+    }
+  }
+}
+
+// A operand from a row-major LDS tile: row l%32, contraction values
+// 16kk + 8*(l/32) .. +8.
+template <int D>
+__device__ __forceinline__ bf16x8_t frag_rm(const uint16_t* rm, int c, int hf, int kk) {
+  return *reinterpret_cast<const bf16x8_t*>(rm + c * (D + 8) + 16 * kk + 8 * hf);
+}
+
+// A operand from a transposed LDS tile: row d, contraction positions in the
+// score-register order of step kk.
+__device__ __forceinline__ bf16x8_t frag_tr(const uint16_t* tr, int d, int hf, int kk) {
+  const uint16_t* p = tr + d * 36 + 16 * kk + 4 * hf;
+  const uint2 lo = *reinterpret_cast<const uint2*>(p);
+  const uint2 hi = *reinterpret_cast<const uint2*>(p + 8);
+  u32x4_t u;
+  u[0] = lo.x;
+  u[1] = lo.y;
+  u[2] = hi.x;
+  u[3] = hi.y;
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+// Operand with lane l = row l%32 of a global bf16 matrix (a query or key row),
+// the 16-wide contraction steps of the head dimension.
+template <int D>
+__device__ __forceinline__ void row_frags(const uint16_t* __restrict__ rowp, int hf, bf16x8_t* f) {
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) f[kk] = *reinterpret_cast<const bf16x8_t*>(rowp + 16 * kk + 8 * hf);
+}
 
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ q,
-                                                  const uint16_t* __restrict__ k,
-                                                  const uint16_t* __restrict__ v, int64_t S,
-                                                  int H, int Hkv, uint16_t* __restrict__ o,
-                                                  float* __restrict__ o_f32,
-                                                  float* __restrict__ lse) {
-  constexpr int DL = D / 4;  // dims per lane
-  __shared__ uint16_t Ks[QB * D];
-  __shared__ uint16_t Vs[QB * D];
-  const int t = threadIdx.x, qi = t >> 2, part = t & 3;
-  const int64_t nqb = (S + QB - 1) / QB;
+__global__ __launch_bounds__(64) void k_attn_fwd(const uint16_t* __restrict__ q,
+                                                 const uint16_t* __restrict__ k,
+                                                 const uint16_t* __restrict__ v, int64_t S, int H,
+                                                 int Hkv, uint16_t* __restrict__ o,
+                                                 float* __restrict__ o_f32,
+                                                 float* __restrict__ lse) {
+  constexpr int KS = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[AB * (D + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * 36];
+  const int lane = threadIdx.x, hf = lane >> 5, c = lane & 31;
+  const int64_t nqb = (S + AB - 1) / AB;
   const int64_t b = blockIdx.x / (H * nqb);
   const int h = (int)((blockIdx.x / nqb) % H);
   const int64_t qb = blockIdx.x % nqb;
   const int g = h / (H / Hkv);
-  const int64_t qpos = qb * QB + qi;  // position within the sequence
-  const bool qvalid = qpos < S;
+  const int64_t ldq = (int64_t)H * D, ldk = (int64_t)Hkv * D;
+  const int64_t qpos = qb * AB + c;
+  const int64_t qrow = b * S + (qpos < S ? qpos : S - 1);
   const float scale = 1.0f / sqrtf((float)D);
-  float qv[DL], acc[DL];
-  const int64_t qrow = b * S + (qvalid ? qpos : S - 1);
+  bf16x8_t qf[KS];
+  row_frags<D>(q + qrow * ldq + (int64_t)h * D, hf, qf);
+  f32x16_t acc[DT];
 #pragma unroll
-  for (int e = 0; e < DL; ++e) {
-    qv[e] = bf2f(q[qrow * (int64_t)H * D + (int64_t)h * D + part * DL + e]) * scale;
-    acc[e] = 0.0f;
-  }
-  float m = -INFINITY, l = 0.0f;
+  for (int j = 0; j < DT; ++j) acc[j] = zero16();
+  float m = -INFINITY, lsum = 0.0f;
   for (int64_t kb = 0; kb <= qb; ++kb) {
     __syncthreads();
-    for (int idx = t; idx < QB * D; idx += 256) {
-      const int r = idx / D, c = idx % D;
-      const int64_t kpos = kb * QB + r;
-      const int64_t krow = b * S + (kpos < S ? kpos : S - 1);
-      Ks[idx] = k[krow * (int64_t)Hkv * D + (int64_t)g * D + c];
-      Vs[idx] = v[krow * (int64_t)Hkv * D + (int64_t)g * D + c];
-    }
+    stage_block<D>(k, ldk, (int64_t)g * D, b * S, kb * AB, S, Ks, nullptr, lane);
+    stage_block<D>(v, ldk, (int64_t)g * D, b * S, kb * AB, S, nullptr, Vt, lane);
     __syncthreads();
-    const int jmax = (int)min((int64_t)QB, S - kb * QB);
-    for (int j = 0; j < jmax; ++j) {
-      const int64_t kpos = kb * QB + j;
-      float s = 0.0f;
+    f32x16_t st = zero16();
 #pragma unroll
-      for (int e = 0; e < DL; ++e) s += qv[e] * bf2f(Ks[j * D + part * DL + e]);
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      if (kpos > qpos) continue;  // causal (uniform within a query's 4 lanes)
-      if (s > m) {
-        const float corr = __expf(m - s);
-        l *= corr;
+    for (int kk = 0; kk < KS; ++kk) st = mfma32(frag_rm<D>(Ks, c, hf, kk), qf[kk], st);
+    float mt = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < DL; ++e) acc[e] *= corr;
-        m = s;
+    for (int r = 0; r < 16; ++r) {
+      const int64_t key = kb * AB + crow(r, hf);
+      st[r] = (key <= qpos && key < S) ? st[r] * scale : -INFINITY;
+      mt = fmaxf(mt, st[r]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);  // finite: key kb*32 <= qpos and < S
+    const float corr = __expf(m - mn);
+    float p[16], ps = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = __expf(st[r] - mn);
+      ps += p[r];
+    }
+    ps += __shfl_xor(ps, 32);
+    lsum = lsum * corr + ps;
+    m = mn;
+#pragma unroll
+    for (int j = 0; j < DT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][r] *= corr;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_t ph, pl;
+      split8(p + 8 * kk, ph, pl);
+#pragma unroll
+      for (int j = 0; j < DT; ++j) {
+        const bf16x8_t va = frag_tr(Vt, 32 * j + c, hf, kk);
+        acc[j] = mfma32(va, ph, acc[j]);
+        acc[j] = mfma32(va, pl, acc[j]);
       }
-      const float p = __expf(s - m);
-      l += p;
-#pragma unroll
-      for (int e = 0; e < DL; ++e) acc[e] += p * bf2f(Vs[j * D + part * DL + e]);
     }
   }
-  if (!qvalid) return;
-  const float inv = 1.0f / l;
+  if (qpos >= S) return;
+  const float inv = 1.0f / lsum;
 #pragma unroll
-  for (int e = 0; e < DL; ++e) {
-    const int64_t idx = qrow * (int64_t)H * D + (int64_t)h * D + part * DL + e;
-    o[idx] = f2bf(acc[e] * inv);
-    if (o_f32 != nullptr) o_f32[idx] = acc[e] * inv;
-  }
-  if (part == 0) lse[(b * H + h) * S + qpos] = m + logf(l);
+  for (int j = 0; j < DT; ++j)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d0 = 32 * j + 8 * rq + 4 * hf;
+      const int64_t idx = qrow * ldq + (int64_t)h * D + d0;
+      float4 f;
+      f.x = acc[j][4 * rq] * inv;
+      f.y = acc[j][4 * rq + 1] * inv;
+      f.z = acc[j][4 * rq + 2] * inv;
+      f.w = acc[j][4 * rq + 3] * inv;
+      uint2 w;
+      w.x = pack_bf16x2(f.x, f.y);
+      w.y = pack_bf16x2(f.z, f.w);
+      *reinterpret_cast<uint2*>(o + idx) = w;
+      if (o_f32 != nullptr) *reinterpret_cast<float4*>(o_f32 + idx) = f;
+    }
+  if (hf == 0) lse[(b * H + h) * S + qpos] = m + logf(lsum);
 }
 
-// Dsum[row, h] = sum_j P_ij dP_ij = dO_i . O_i with the unrounded (fp32)
-// attention output; one thread per (row, head).
-__global__ __launch_bounds__(256) void k_attn_dsum(const float* __restrict__ o,
-                                                   const uint16_t* __restrict__ dout, int64_t T,
-                                                   int H, int D, float* __restrict__ dsum) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= T * H) return;
-  float s = 0.0f;
-  for (int e = 0; e < D; ++e) s += o[i * D + e] * bf2f(dout[i * D + e]);
-  dsum[i] = s;
-}
-
-// dQ for 64 query rows of one (sequence, head).
+// dQ of a 32-query block of one head; also writes Dsum = dO . O (fp32) of
+// its queries for the key-side kernel.
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_dq(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64) void k_attn_dq(const uint16_t* __restrict__ q,
+                                                const uint16_t* __restrict__ k,
+                                                const uint16_t* __restrict__ v,
+                                                const float* __restrict__ o_f32,
+                                                const uint16_t* __restrict__ dout,
+                                                const float* __restrict__ lse, int64_t S, int H,
+                                                int Hkv, float* __restrict__ dsum,
+                                                uint16_t* __restrict__ dq) {
+  constexpr int KS = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[AB * (D + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[AB * (D + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * 36];
+  const int lane = threadIdx.x, hf = lane >> 5, c = lane & 31;
+  const int64_t nqb = (S + AB - 1) / AB;
+  const int64_t b = blockIdx.x / (H * nqb);
+  const int h = (int)((blockIdx.x / nqb) % H);
+  const int64_t qb = blockIdx.x % nqb;
+  const int g = h / (H / Hkv);
+  const int64_t ldq = (int64_t)H * D, ldk = (int64_t)Hkv * D;
+  const int64_t qpos = qb * AB + c;
+  const int64_t qrow = b * S + (qpos < S ? qpos : S - 1);
+  const float scale = 1.0f / sqrtf((float)D);
+  bf16x8_t qf[KS], df[KS];
+  row_frags<D>(q + qrow * ldq + (int64_t)h * D, hf, qf);
+  row_frags<D>(dout + qrow * ldq + (int64_t)h * D, hf, df);
+  // Dsum over the lane's half of the head dimension, then both halves
+  float di = 0.0f;
+  {
+    const float* orow = o_f32 + qrow * ldq + (int64_t)h * D;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const u32x4_t u = __builtin_bit_cast(u32x4_t, df[kk]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float dv = __uint_as_float((e & 1) ? (u[e >> 1] & 0xFFFF0000u) : (u[e >> 1] << 16));
+        di += dv * orow[16 * kk + 8 * hf + e];
+      }
+    }
+    di += __shfl_xor(di, 32);
+  }
+  if (hf == 0 && qpos < S) dsum[qrow * H + h] = di;
+  const float L = lse[(b * H + h) * S + (qpos < S ? qpos : S - 1)];
+  f32x16_t acc[DT];
+#pragma unroll
+  for (int j = 0; j < DT; ++j) acc[j] = zero16();
+  for (int64_t kb = 0; kb <= qb; ++kb) {
+    __syncthreads();
+    stage_block<D>(k, ldk, (int64_t)g * D, b * S, kb * AB, S, Ks, Kt, lane);
+    stage_block<D>(v, ldk, (int64_t)g * D, b * S, kb * AB, S, Vs, nullptr, lane);
+    __syncthreads();
+    f32x16_t st = zero16(), dp = zero16();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      st = mfma32(frag_rm<D>(Ks, c, hf, kk), qf[kk], st);
+      dp = mfma32(frag_rm<D>(Vs, c, hf, kk), df[kk], dp);
+    }
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t key = kb * AB + crow(r, hf);
+      const float pr = (key <= qpos && key < S) ? __expf(st[r] * scale - L) : 0.0f;
+      ds[r] = pr * (dp[r] - di) * scale;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_t sh, sl;
+      split8(ds + 8 * kk, sh, sl);
+#pragma unroll
+      for (int j = 0; j < DT; ++j) {
+        const bf16x8_t ka = frag_tr(Kt, 32 * j + c, hf, kk);
+        acc[j] = mfma32(ka, sh, acc[j]);
+        acc[j] = mfma32(ka, sl, acc[j]);
+      }
+    }
+  }
+  if (qpos >= S) return;
+#pragma unroll
+  for (int j = 0; j < DT; ++j)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d0 = 32 * j + 8 * rq + 4 * hf;
+      uint2 w;
+      w.x = pack_bf16x2(acc[j][4 * rq], acc[j][4 * rq + 1]);
+      w.y = pack_bf16x2(acc[j][4 * rq + 2], acc[j][4 * rq + 3]);
+      *reinterpret_cast<uint2*>(dq + qrow * ldq + (int64_t)h * D + d0) = w;
+    }
+}
+
+// dK, dV of a 32-key block for one query head (fp32 partials per head; the
+// heads of a KV group are summed afterwards in head order).
+template <int D>
+__global__ __launch_bounds__(64) void k_attn_dkv(const uint16_t* __restrict__ q,
                                                  const uint16_t* __restrict__ k,
                                                  const uint16_t* __restrict__ v,
                                                  const uint16_t* __restrict__ dout,
                                                  const float* __restrict__ lse,
                                                  const float* __restrict__ dsum, int64_t S, int H,
-                                                 int Hkv, uint16_t* __restrict__ dq) {
-  constexpr int DL = D / 4;
-  __shared__ uint16_t Ks[QB * D];
-  __shared__ uint16_t Vs[QB * D];
-  const int t = threadIdx.x, qi = t >> 2, part = t & 3;
-  const int64_t nqb = (S + QB - 1) / QB;
-  const int64_t b = blockIdx.x / (H * nqb);
-  const int h = (int)((blockIdx.x / nqb) % H);
-  const int64_t qb = blockIdx.x % nqb;
+                                                 int Hkv, float* __restrict__ pk,
+                                                 float* __restrict__ pv) {
+  constexpr int KS = D / 16, DT = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[AB * (D + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t Os[AB * (D + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * 36];
+  __shared__ __attribute__((aligned(16))) uint16_t Ot[D * 36];
+  __shared__ float Ls[AB], Dl[AB];
+  const int lane = threadIdx.x, hf = lane >> 5, c = lane & 31;
+  const int64_t nkb = (S + AB - 1) / AB;
+  const int64_t b = blockIdx.x / (H * nkb);
+  const int h = (int)((blockIdx.x / nkb) % H);
+  const int64_t kb = blockIdx.x % nkb;
   const int g = h / (H / Hkv);
-  const int64_t qpos = qb * QB + qi;
-  const bool qvalid = qpos < S;
+  const int64_t ldq = (int64_t)H * D, ldk = (int64_t)Hkv * D;
+  const int64_t kpos = kb * AB + c;
+  const int64_t krow = b * S + (kpos < S ? kpos : S - 1);
   const float scale = 1.0f / sqrtf((float)D);
-  const int64_t qrow = b * S + (qvalid ? qpos : S - 1);
-  float qv[DL], dov[DL], acc[DL];
+  bf16x8_t kf[KS], vf[KS];
+  row_frags<D>(k + krow * ldk + (int64_t)g * D, hf, kf);
+  row_frags<D>(v + krow * ldk + (int64_t)g * D, hf, vf);
+  f32x16_t adk[DT], adv[DT];
 #pragma unroll
-  for (int e = 0; e < DL; ++e) {
-    const int64_t idx = qrow * (int64_t)H * D + (int64_t)h * D + part * DL + e;
-    qv[e] = bf2f(q[idx]) * scale;
-    dov[e] = bf2f(dout[idx]);
-    acc[e] = 0.0f;
+  for (int j = 0; j < DT; ++j) {
+    adk[j] = zero16();
+    adv[j] = zero16();
   }
-  const float L = lse[(b * H + h) * S + (qvalid ? qpos : S - 1)];
-  const float Di = dsum[qrow * H + h];
-  for (int64_t kb = 0; kb <= qb; ++kb) {
+  for (int64_t qb = kb; qb < nkb; ++qb) {
     __syncthreads();
-    for (int idx = t; idx < QB * D; idx += 256) {
-      const int r = idx / D, c = idx % D;
-      const int64_t kpos = kb * QB + r;
-      const int64_t krow = b * S + (kpos < S ? kpos : S - 1);
-      Ks[idx] = k[krow * (int64_t)Hkv * D + (int64_t)g * D + c];
-      Vs[idx] = v[krow * (int64_t)Hkv * D + (int64_t)g * D + c];
+    stage_block<D>(q, ldq, (int64_t)h * D, b * S, qb * AB, S, Qs, Qt, lane);
+    stage_block<D>(dout, ldq, (int64_t)h * D, b * S, qb * AB, S, Os, Ot, lane);
+    if (lane < AB) {
+      const int64_t qp = qb * AB + lane;
+      const int64_t qc = qp < S ? qp : S - 1;
+      Ls[lane] = lse[(b * H + h) * S + qc];
+      Dl[lane] = dsum[(b * S + qc) * H + h];
     }
     __syncthreads();
-    const int jmax = (int)min((int64_t)QB, S - kb * QB);
-    for (int j = 0; j < jmax; ++j) {
-      const int64_t kpos = kb * QB + j;
-      float s = 0.0f, dp = 0.0f;
+    f32x16_t st = zero16(), dp = zero16();
 #pragma unroll
-      for (int e = 0; e < DL; ++e) {
-        s += qv[e] * bf2f(Ks[j * D + part * DL + e]);
-        dp += dov[e] * bf2f(Vs[j * D + part * DL + e]);
+    for (int kk = 0; kk < KS; ++kk) {
+      st = mfma32(frag_rm<D>(Qs, c, hf, kk), kf[kk], st);
+      dp = mfma32(frag_rm<D>(Os, c, hf, kk), vf[kk], dp);
+    }
+    float p[16], ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qr = crow(r, hf);
+      const int64_t qp = qb * AB + qr;
+      const bool ok = kpos <= qp && qp < S;
+      p[r] = ok ? __expf(st[r] * scale - Ls[qr]) : 0.0f;
+      ds[r] = p[r] * (dp[r] - Dl[qr]) * scale;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_t ph, pl, sh, sl;
+      split8(p + 8 * kk, ph, pl);
+      split8(ds + 8 * kk, sh, sl);
+#pragma unroll
+      for (int j = 0; j < DT; ++j) {
+        const bf16x8_t oa = frag_tr(Ot, 32 * j + c, hf, kk);
+        adv[j] = mfma32(oa, ph, adv[j]);
+        adv[j] = mfma32(oa, pl, adv[j]);
+        const bf16x8_t qa = frag_tr(Qt, 32 * j + c, hf, kk);
+        adk[j] = mfma32(qa, sh, adk[j]);
+        adk[j] = mfma32(qa, sl, adk[j]);
       }
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      dp += __shfl_xor(dp, 1);
-      dp += __shfl_xor(dp, 2);
-      if (kpos > qpos) continue;
-      const float p = __expf(s - L);
-      const float ds = p * (dp - Di) * scale;
-#pragma unroll
-      for (int e = 0; e < DL; ++e) acc[e] += ds * bf2f(Ks[j * D + part * DL + e]);
     }
   }
-  if (!qvalid) return;
+  if (kpos >= S) return;
+  const int64_t prow = (krow * H + h) * D;
 #pragma unroll
-  for (int e = 0; e < DL; ++e) dq[qrow * (int64_t)H * D + (int64_t)h * D + part * DL + e] = f2bf(acc[e]);
+  for (int j = 0; j < DT; ++j)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d0 = 32 * j + 8 * rq + 4 * hf;
+      *reinterpret_cast<float4*>(pk + prow + d0) =
+          make_float4(adk[j][4 * rq], adk[j][4 * rq + 1], adk[j][4 * rq + 2], adk[j][4 * rq + 3]);
+      *reinterpret_cast<float4*>(pv + prow + d0) =
+          make_float4(adv[j][4 * rq], adv[j][4 * rq + 1], adv[j][4 * rq + 2], adv[j][4 * rq + 3]);
+    }
 }
 
-// dK, dV for 64 key rows of one (sequence, KV head), summed over the heads of
-// the group in head order.
-template <int D>
-__global__ __launch_bounds__(256) void k_attn_dkv(const uint16_t* __restrict__ q,
-                                                  const uint16_t* __restrict__ k,
-                                                  const uint16_t* __restrict__ v,
-                                                  const uint16_t* __restrict__ dout,
-                                                  const float* __restrict__ lse,
-                                                  const float* __restrict__ dsum, int64_t S, int H,
-                                                  int Hkv, uint16_t* __restrict__ dk,
-                                                  uint16_t* __restrict__ dv) {
-  constexpr int DL = D / 4;
-  __shared__ uint16_t Qs[QB * D];
-  __shared__ uint16_t Os[QB * D];
-  __shared__ float Ls[QB];
-  __shared__ float Ds[QB];
-  const int t = threadIdx.x, ki = t >> 2, part = t & 3;
-  const int64_t nkb = (S + QB - 1) / QB;
-  const int64_t b = blockIdx.x / (Hkv * nkb);
-  const int g = (int)((blockIdx.x / nkb) % Hkv);
-  const int64_t kb = blockIdx.x % nkb;
+// dk[row, g, :] = bf16(sum over the heads of group g, in head order, of the
+// per-head partials); one thread per (row, kv head, 4 dims).
+__global__ __launch_bounds__(256) void k_attn_group_sum(const float* __restrict__ pk,
+                                                        const float* __restrict__ pv, int64_t T,
+                                                        int H, int Hkv, int D,
+                                                        uint16_t* __restrict__ dk,
+                                                        uint16_t* __restrict__ dv) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n4 = T * Hkv * (D / 4);
+  if (i >= n4) return;
+  const int d4 = (int)(i % (D / 4));
+  const int64_t rg = i / (D / 4);
+  const int g = (int)(rg % Hkv);
+  const int64_t row = rg / Hkv;
   const int grp = H / Hkv;
-  const int64_t kpos = kb * QB + ki;
-  const bool kvalid = kpos < S;
-  const float scale = 1.0f / sqrtf((float)D);
-  const int64_t krow = b * S + (kvalid ? kpos : S - 1);
-  float kv_[DL], vv[DL], dka[DL], dva[DL];
-#pragma unroll
-  for (int e = 0; e < DL; ++e) {
-    const int64_t idx = krow * (int64_t)Hkv * D + (int64_t)g * D + part * DL + e;
-    kv_[e] = bf2f(k[idx]);
-    vv[e] = bf2f(v[idx]);
-    dka[e] = 0.0f;
-    dva[e] = 0.0f;
-  }
+  float4 sk = make_float4(0.f, 0.f, 0.f, 0.f), sv = sk;
   for (int hh = 0; hh < grp; ++hh) {
-    const int h = g * grp + hh;
-    for (int64_t qb = kb; qb < nkb; ++qb) {
-      __syncthreads();
-      for (int idx = t; idx < QB * D; idx += 256) {
-        const int r = idx / D, c = idx % D;
-        const int64_t qp = qb * QB + r;
-        const int64_t qrow = b * S + (qp < S ? qp : S - 1);
-        Qs[idx] = q[qrow * (int64_t)H * D + (int64_t)h * D + c];
-        Os[idx] = dout[qrow * (int64_t)H * D + (int64_t)h * D + c];
-      }
-      if (t < QB) {
-        const int64_t qp = qb * QB + t;
-        const int64_t qc = qp < S ? qp : S - 1;
-        Ls[t] = lse[(b * H + h) * S + qc];
-        Ds[t] = dsum[(b * S + qc) * H + h];
-      }
-      __syncthreads();
-      const int imax = (int)min((int64_t)QB, S - qb * QB);
-      for (int i = 0; i < imax; ++i) {
-        const int64_t qp = qb * QB + i;
-        float s = 0.0f, dp = 0.0f;
-#pragma unroll
-        for (int e = 0; e < DL; ++e) {
-          s += bf2f(Qs[i * D + part * DL + e]) * kv_[e];
-          dp += bf2f(Os[i * D + part * DL + e]) * vv[e];
-        }
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        dp += __shfl_xor(dp, 1);
-        dp += __shfl_xor(dp, 2);
-        if (qp < kpos) continue;
-        const float p = __expf(s * scale - Ls[i]);
-        const float ds = p * (dp - Ds[i]) * scale;
-#pragma unroll
-        for (int e = 0; e < DL; ++e) {
-          dva[e] += p * bf2f(Os[i * D + part * DL + e]);
-          dka[e] += ds * bf2f(Qs[i * D + part * DL + e]);
-        }
-      }
-    }
+    const int64_t off = (row * H + g * grp + hh) * D + 4 * d4;
+    const float4 a = *reinterpret_cast<const float4*>(pk + off);
+    const float4 bq = *reinterpret_cast<const float4*>(pv + off);
+    sk.x += a.x; sk.y += a.y; sk.z += a.z; sk.w += a.w;
+    sv.x += bq.x; sv.y += bq.y; sv.z += bq.z; sv.w += bq.w;
   }
-  if (!kvalid) return;
-#pragma unroll
-  for (int e = 0; e < DL; ++e) {
-    const int64_t idx = krow * (int64_t)Hkv * D + (int64_t)g * D + part * DL + e;
-    dk[idx] = f2bf(dka[e]);
-    dv[idx] = f2bf(dva[e]);
-  }
+  const int64_t out = (row * Hkv + g) * D + 4 * d4;
+  uint2 wk, wv;
+  wk.x = pack_bf16x2(sk.x, sk.y);
+  wk.y = pack_bf16x2(sk.z, sk.w);
+  wv.x = pack_bf16x2(sv.x, sv.y);
+  wv.y = pack_bf16x2(sv.z, sv.w);
+  *reinterpret_cast<uint2*>(dk + out) = wk;
+  *reinterpret_cast<uint2*>(dv + out) = wv;
 }
 
 // ---- elementwise ------------------------------------------------------------
@@ -495,7 +675,6 @@ hipError_t launch_rope(uint16_t* x, int64_t T, int64_t S, int heads, int d, doub
 
 #define NF4S_DISPATCH_D(D_, CALL) \
   switch (D_) {                   \
-    case 16: CALL(16); break;     \
     case 32: CALL(32); break;     \
     case 64: CALL(64); break;     \
     case 128: CALL(128); break;   \
@@ -505,29 +684,42 @@ hipError_t launch_rope(uint16_t* x, int64_t T, int64_t S, int heads, int d, doub
 hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
                                 int64_t S, int H, int Hkv, int D, uint16_t* o, float* o_f32,
                                 float* lse, hipStream_t s) {
-  const unsigned grid = (unsigned)(B * H * ((S + QB - 1) / QB));
-#define CALL(DD) hipLaunchKernelGGL(k_attn_fwd<DD>, dim3(grid), dim3(256), 0, s, q, k, v, S, H, Hkv, o, o_f32, lse)
+  const unsigned grid = (unsigned)(B * H * ((S + AB - 1) / AB));
+#define CALL(DD) hipLaunchKernelGGL(k_attn_fwd<DD>, dim3(grid), dim3(64), 0, s, q, k, v, S, H, Hkv, o, o_f32, lse)
   NF4S_DISPATCH_D(D, CALL)
 #undef CALL
   return hipGetLastError();
 }
 
-size_t attention_bwd_ws_bytes(int64_t B, int64_t S, int H) { return (size_t)(B * S * H) * sizeof(float); }
+// Workspace: Dsum [B*S, H] fp32, then the per-head dK and dV partials
+// [B*S, H, D] fp32 each (256-byte aligned sections).
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t attention_bwd_ws_bytes(int64_t B, int64_t S, int H, int D) {
+  const size_t rows = (size_t)(B * S);
+  return align256(rows * H * sizeof(float)) + 2 * align256(rows * H * D * sizeof(float));
+}
 
 hipError_t launch_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const float* o_f32, const uint16_t* dout, const float* lse,
                                 int64_t B, int64_t S, int H, int Hkv, int D, uint16_t* dq,
                                 uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
-  float* dsum = static_cast<float*>(ws);
-  hipLaunchKernelGGL(k_attn_dsum, dim3(grid_of(B * S * H)), dim3(256), 0, s, o_f32, dout, B * S, H,
-                     D, dsum);
-  const unsigned gq = (unsigned)(B * H * ((S + QB - 1) / QB));
-  const unsigned gk = (unsigned)(B * Hkv * ((S + QB - 1) / QB));
+  const size_t rows = (size_t)(B * S);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  float* dsum = reinterpret_cast<float*>(w);
+  float* pk = reinterpret_cast<float*>(w + align256(rows * H * sizeof(float)));
+  float* pv = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(pk) + align256(rows * H * D * sizeof(float)));
+  const unsigned grid = (unsigned)(B * H * ((S + AB - 1) / AB));
 #define CALL(DD)                                                                                   \
-  hipLaunchKernelGGL(k_attn_dq<DD>, dim3(gq), dim3(256), 0, s, q, k, v, dout, lse, dsum, S, H, Hkv, dq); \
-  hipLaunchKernelGGL(k_attn_dkv<DD>, dim3(gk), dim3(256), 0, s, q, k, v, dout, lse, dsum, S, H, Hkv, dk, dv)
+  hipLaunchKernelGGL(k_attn_dq<DD>, dim3(grid), dim3(64), 0, s, q, k, v, o_f32, dout, lse, S, H, Hkv, \
+                     dsum, dq);                                                                    \
+  hipLaunchKernelGGL(k_attn_dkv<DD>, dim3(grid), dim3(64), 0, s, q, k, v, dout, lse, dsum, S, H, Hkv, \
+                     pk, pv)
   NF4S_DISPATCH_D(D, CALL)
 #undef CALL
+  const int64_t n4 = (int64_t)rows * Hkv * (D / 4);
+  hipLaunchKernelGGL(k_attn_group_sum, dim3(grid_of(n4)), dim3(256), 0, s, pk, pv, (int64_t)rows, H,
+                     Hkv, D, dk, dv);
   return hipGetLastError();
 }
 #undef NF4S_DISPATCH_D

@@ -56,8 +56,14 @@ class Decoder:
 
     def __init__(self, cfg, shards: ShardSet, embed, lm_head, norms, lora, batch, seq,
                  targets=("q", "v"), r=16, alpha=32, n_slots=2, mode="streamed", lr=1e-4,
-                 betas=(0.9, 0.999), adam_eps=1e-8, weight_decay=0.0):
+                 betas=(0.9, 0.999), adam_eps=1e-8, weight_decay=0.0, time_calls=None):
+        """time_calls: optional predicate (direction, n_out, k_in) -> bool; the
+        streamed linear forward calls it accepts are bracketed by timing
+        events on the compute stream, collected in self.timed as
+        (direction, n_out, k_in, start, end)."""
         assert mode in ("streamed", "resident")
+        self.time_calls = time_calls
+        self.timed = []
         dev = "cuda"
         self.cfg = cfg
         self.sh = shards
@@ -138,7 +144,7 @@ class Decoder:
         self.u = {p: f32(M, r) for p in self.targets}
         self.du = f32(M, r)
 
-        ws = max(nf4s_workspace_bytes(OP_ATTENTION_BWD, M, nh, 0),
+        ws = max(nf4s_workspace_bytes(OP_ATTENTION_BWD, M, nh, hd),
                  nf4s_workspace_bytes(OP_CROSS_ENTROPY, M, 0, 0),
                  nf4s_workspace_bytes(OP_DENSE_FWD_PACKED, M, V, H),
                  nf4s_workspace_bytes(OP_DENSE_BWD_PACKED, M, V, H))
@@ -200,11 +206,27 @@ class Decoder:
             A, Bm = self.lora[(i, p)]
             lora_fwd(x.data_ptr(), self.M, ki, A.data_ptr(), self.r, self.u[p].data_ptr(), *self._ws(),
                      self._s)
+            ev = self._tick("fwd", no, ki)
             streamed_linear_fwd_packed(base, d, xp, self.M, y.data_ptr(), self.u[p].data_ptr(),
                                        Bm.data_ptr(), self.r, self.scale, *self._ws(), self._s)
         else:
+            ev = self._tick("fwd", no, ki)
             streamed_linear_fwd_packed(base, d, xp, self.M, y.data_ptr(), None, None, 0, 0.0,
                                        *self._ws(), self._s)
+        self._tock(ev)
+
+    def _tick(self, direction, n, k):
+        if self.time_calls is None or not self.time_calls(direction, n, k):
+            return None
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(self.compute)
+        return (direction, n, k, start, end)
+
+    def _tock(self, ev):
+        if ev is not None:
+            ev[4].record(self.compute)
+            self.timed.append(ev)
 
     def _bwd(self, base, i, p, x, dy, dx):
         no, ki = self.sh.shapes[p]

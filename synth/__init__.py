@@ -103,14 +103,14 @@ def token_ids(n: int, vocab: int, step: int = 0) -> np.ndarray:
 # 135m: SmolLM2-135M (llama architecture, tied embeddings); 8b: Llama-3.1-8B;
 # tiny: a 2-layer model small enough for the fp64 oracle and finite differences.
 DECODER = {
-    "tiny": dict(hidden=64, inter=128, heads=4, kv_heads=2, head_dim=16, vocab=256, layers=2,
+    "tiny": dict(hidden=128, inter=256, heads=4, kv_heads=2, head_dim=32, vocab=256, layers=2,
                  rope_theta=10000.0, eps=1e-5, tied=True),
     "135m": dict(hidden=576, inter=1536, heads=9, kv_heads=3, head_dim=64, vocab=49152, layers=30,
                  rope_theta=100000.0, eps=1e-5, tied=True),
     "8b": dict(hidden=4096, inter=14336, heads=32, kv_heads=8, head_dim=128, vocab=128256, layers=32,
                rope_theta=500000.0, eps=1e-5, tied=False),
 }
-SHAPES["tiny"] = _shapes(64, 128, 4, 16, 2)
+SHAPES["tiny"] = _shapes(128, 256, 4, 32, 2)
 N_LAYERS["tiny"] = 2
 VOCAB["tiny"] = 256
 

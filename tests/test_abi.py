@@ -231,12 +231,13 @@ def test_decoder_argument_errors():
     """The decoder entry points validate on the host before any launch."""
     assert _err(L.nf4s_rope, None, 4, 2, 2, 16, 1e4, 0) == L.EINVAL
     assert _err(L.nf4s_rope, FAKE, 6, 4, 2, 16, 1e4, 0) == L.ESHAPE        # rows % seq
-    assert _err(L.nf4s_rope, FAKE, 6, 3, 1, 24, 1e4, 0) == L.ESHAPE        # no kernel for d=24
+    assert _err(L.nf4s_rope, FAKE, 6, 3, 1, 25, 1e4, 0) == L.ESHAPE        # odd head size
     assert _err(L.nf4s_rope, FAKE, 6, 3, 1, 16, 1.0, 0) == L.EINVAL        # theta
     assert _err(L.nf4s_rope, FAKE + 1, 6, 3, 1, 16, 1e4, 0) == L.EALIGN
     assert _err(L.nf4s_attention_fwd, FAKE, FAKE, FAKE, 1, 4, 3, 2, 16, FAKE, None, FAKE) == L.ESHAPE
     assert _err(L.nf4s_attention_fwd, FAKE, FAKE, FAKE, 0, 4, 4, 2, 16, FAKE, None, FAKE) == L.ESHAPE
-    assert _err(L.nf4s_attention_bwd, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 4, 2, 16, FAKE, FAKE,
+    assert _err(L.nf4s_attention_fwd, FAKE, FAKE, FAKE, 1, 4, 4, 2, 16, FAKE, None, FAKE) == L.ESHAPE
+    assert _err(L.nf4s_attention_bwd, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 4, 2, 32, FAKE, FAKE,
                 FAKE, None, 0) == L.EWORKSPACE
     assert _err(L.nf4s_rmsnorm_bwd, [], FAKE, FAKE, FAKE, 4, 4, 0, FAKE) == L.EINVAL
     assert _err(L.nf4s_rmsnorm_bwd, [FAKE] * 4, FAKE, FAKE, FAKE, 4, 4, 0, FAKE) == L.EINVAL
@@ -259,8 +260,10 @@ def test_decoder_argument_errors():
 
 
 def test_decoder_workspace_sizes():
-    assert L.nf4s_workspace_bytes(L.OP_ATTENTION_BWD, 512, 32, 0) == 512 * 32 * 4
+    assert L.nf4s_workspace_bytes(L.OP_ATTENTION_BWD, 512, 32, 128) == 512 * 32 * 4 * (1 + 2 * 128)
     assert L.nf4s_workspace_bytes(L.OP_CROSS_ENTROPY, 512, 0, 0) == 512 * 4
     assert L.nf4s_workspace_bytes(L.OP_DENSE_FWD_PACKED, 512, 128256, 4096) == 0   # 2004 tiles
     with pytest.raises(L.Nf4sError):
-        L.nf4s_workspace_bytes(L.OP_ATTENTION_BWD, 0, 32, 0)
+        L.nf4s_workspace_bytes(L.OP_ATTENTION_BWD, 0, 32, 128)
+    with pytest.raises(L.Nf4sError):
+        L.nf4s_workspace_bytes(L.OP_ATTENTION_BWD, 512, 32, 16)

@@ -314,7 +314,7 @@ int nf4s_embed(const uint16_t* table, int64_t vocab, int64_t hidden, const int64
 /*
  * RMSNorm: rstd[t] = 1/sqrt(mean_j x[t,j]^2 + eps), y = bf16(x * rstd * w).
  * x fp32 [T, H]; w fp32 [H]; y bf16 [T, H]; rstd fp32 [T] (kept for the
- * backward). Backward: with g = w * (dys[0] + ... + dys[n_dy-1]) (n_dy bf16
+ * backward); H a multiple of 8, x, w, y, dys and dh 16-byte aligned. Backward: with g = w * (dys[0] + ... + dys[n_dy-1]) (n_dy bf16
  * [T, H] gradients of y, 1..3, summed in fp32 in that order),
  *   d = rstd * g - x * rstd^3 * mean_j(g * x),
  * written to dh (accumulate = 0) or added to it (accumulate = 1). dys is a
@@ -330,8 +330,10 @@ int nf4s_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float* x, const
  * Rotary embedding, rotate-half form, in place on bf16 x [T, heads*head_dim]:
  * row t is position t % S; pair (j, j + d/2) of each head is rotated by the
  * angle (t % S) * theta^(-2j/d) (inverse = 1: by minus that angle, which is
- * the backward of the rotation). Results rounded to bf16. head_dim even,
- * at most 256; T a multiple of S. Errors: EINVAL, ESHAPE, EALIGN.
+ * the backward of the rotation); the angle, its sine and cosine are fp64,
+ * the rotation fp32, results rounded to bf16. head_dim a multiple of 8, at
+ * most 256; T a multiple of S; x 8-byte aligned. Errors: EINVAL, ESHAPE,
+ * EALIGN.
  */
 int nf4s_rope(uint16_t* x, int64_t T, int64_t S, int heads, int head_dim, double theta, int inverse,
               void* stream);

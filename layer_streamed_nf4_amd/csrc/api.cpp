@@ -472,12 +472,18 @@ int nf4s_embed(const uint16_t* table, int64_t vocab, int64_t hidden, const int64
                   "embed launch");
 }
 
+// The norms move 8 elements (16/32 bytes) per access.
+static int check_norm_width(int64_t H) {
+  if (H % 8) return fail(NF4S_ESHAPE, "hidden=%lld is not a multiple of 8", (long long)H);
+  return NF4S_OK;
+}
+
 int nf4s_rmsnorm_fwd(const float* x, const float* w, int64_t T, int64_t H, float eps, uint16_t* y,
                      float* rstd, void* stream) {
   int rc;
-  if ((rc = check_rows(T, H))) return rc;
+  if ((rc = check_rows(T, H)) || (rc = check_norm_width(H))) return rc;
   if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(NF4S_EINVAL, "eps must be positive and finite");
-  if ((rc = check_ptr(x, "x", 4)) || (rc = check_ptr(w, "w", 4)) || (rc = check_ptr(y, "y", 2)) ||
+  if ((rc = check_ptr(x, "x")) || (rc = check_ptr(w, "w")) || (rc = check_ptr(y, "y")) ||
       (rc = check_ptr(rstd, "rstd", 4)))
     return rc;
   return launched(launch_rmsnorm_fwd(x, w, T, H, eps, y, rstd, static_cast<hipStream_t>(stream)),
@@ -488,14 +494,14 @@ int nf4s_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float* x, const
                      const float* rstd, int64_t T, int64_t H, int accumulate, float* dh,
                      void* stream) {
   int rc;
-  if ((rc = check_rows(T, H))) return rc;
+  if ((rc = check_rows(T, H)) || (rc = check_norm_width(H))) return rc;
   if (!dys) return fail(NF4S_EINVAL, "dys is NULL");
   if (n_dy < 1 || n_dy > 3) return fail(NF4S_EINVAL, "n_dy=%d outside [1, 3]", n_dy);
   for (int i = 0; i < n_dy; ++i)
-    if ((rc = check_ptr(dys[i], "dys[i]", 2))) return rc;
+    if ((rc = check_ptr(dys[i], "dys[i]"))) return rc;
   if (accumulate != 0 && accumulate != 1) return fail(NF4S_EINVAL, "accumulate must be 0 or 1");
-  if ((rc = check_ptr(x, "x", 4)) || (rc = check_ptr(w, "w", 4)) || (rc = check_ptr(rstd, "rstd", 4)) ||
-      (rc = check_ptr(dh, "dh", 4)))
+  if ((rc = check_ptr(x, "x")) || (rc = check_ptr(w, "w")) || (rc = check_ptr(rstd, "rstd", 4)) ||
+      (rc = check_ptr(dh, "dh")))
     return rc;
   return launched(launch_rmsnorm_bwd(dys, n_dy, x, w, rstd, T, H, accumulate, dh,
                                      static_cast<hipStream_t>(stream)),
@@ -513,11 +519,12 @@ int nf4s_rope(uint16_t* x, int64_t T, int64_t S, int heads, int head_dim, double
               void* stream) {
   int rc;
   if ((rc = check_heads(heads, head_dim))) return rc;
+  if (head_dim % 8) return fail(NF4S_ESHAPE, "head_dim=%d is not a multiple of 8", head_dim);
   if (S <= 0 || T <= 0 || T % S) return fail(NF4S_ESHAPE, "rows=%lld must be a positive multiple of seq=%lld", (long long)T, (long long)S);
   if ((rc = check_rows(T, (int64_t)heads * head_dim))) return rc;
   if (!(theta > 1.0) || !std::isfinite(theta)) return fail(NF4S_EINVAL, "theta must be finite and > 1");
   if (inverse != 0 && inverse != 1) return fail(NF4S_EINVAL, "inverse must be 0 or 1");
-  if ((rc = check_ptr(x, "x", 2))) return rc;
+  if ((rc = check_ptr(x, "x", 8))) return rc;
   return launched(launch_rope(x, T, S, heads, head_dim, theta, inverse, static_cast<hipStream_t>(stream)),
                   "rope launch");
 }

@@ -25,33 +25,55 @@ namespace {
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ uint16_t f2bf(float f) { return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xFFFFu); }
 
-// Sum over a 256-thread workgroup in a fixed tree; every thread gets the total.
+// Sum over a 256-thread workgroup in a fixed order (butterfly within each
+// wave, then the four wave sums in wave order); every thread gets the total.
 __device__ __forceinline__ float block_sum(float v, float* red) {
-  const int t = threadIdx.x;
-  red[t] = v;
-  __syncthreads();
 #pragma unroll
-  for (int s = 128; s > 0; s >>= 1) {
-    if (t < s) red[t] += red[t + s];
-    __syncthreads();
-  }
-  const float r = red[0];
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();  // red may still be read by a previous call
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  return r;
+  return ((red[0] + red[1]) + red[2]) + red[3];
 }
 
 __device__ __forceinline__ float block_max(float v, float* red) {
-  const int t = threadIdx.x;
-  red[t] = v;
-  __syncthreads();
 #pragma unroll
-  for (int s = 128; s > 0; s >>= 1) {
-    if (t < s) red[t] = fmaxf(red[t], red[t + s]);
-    __syncthreads();
-  }
-  const float r = red[0];
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   __syncthreads();
-  return r;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// Eight consecutive bf16 values (16 bytes) as fp32.
+__device__ __forceinline__ void load8_bf16(const uint16_t* p, float* f) {
+  const u32x4v u = *reinterpret_cast<const u32x4v*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(u[i] << 16);
+    f[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ void store8_bf16(uint16_t* p, const float* f) {
+  u32x4v u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  *reinterpret_cast<u32x4v*>(p) = u;
+}
+
+__device__ __forceinline__ void load8_f32(const float* p, float* f) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+__device__ __forceinline__ void store8_f32(float* p, const float* f) {
+  *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
 }
 
 // h[t, :] = E[ids[t], :] (bf16 -> fp32 residual stream); an id outside
@@ -66,20 +88,34 @@ __global__ __launch_bounds__(256) void k_embed(const uint16_t* __restrict__ E, i
   for (int64_t j = threadIdx.x; j < H; j += 256) h[t * H + j] = ok ? bf2f(row[j]) : __builtin_nanf("");
 }
 
-// y = bf16(x * rstd * w), rstd = 1/sqrt(mean(x^2) + eps); one workgroup per row
+// y = bf16(x * rstd * w), rstd = 1/sqrt(mean(x^2) + eps); one workgroup per
+// row, 8 elements (16- and 32-byte accesses) per thread and step.
 __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const float* __restrict__ x,
                                                      const float* __restrict__ w, int64_t H,
                                                      float eps, uint16_t* __restrict__ y,
                                                      float* __restrict__ rstd) {
-  __shared__ float red[256];
+  __shared__ float red[4];
   const int64_t t = blockIdx.x;
   const float* xr = x + t * H;
+  const int nc = (int)(H / 8);
   float ss = 0.0f;
-  for (int64_t j = threadIdx.x; j < H; j += 256) ss += xr[j] * xr[j];
+  for (int c = threadIdx.x; c < nc; c += 256) {
+    float f[8];
+    load8_f32(xr + 8 * c, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
+  }
   ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)H + eps);
   if (threadIdx.x == 0) rstd[t] = r;
-  for (int64_t j = threadIdx.x; j < H; j += 256) y[t * H + j] = f2bf(xr[j] * r * w[j]);
+  for (int c = threadIdx.x; c < nc; c += 256) {
+    float f[8], g[8];
+    load8_f32(xr + 8 * c, f);
+    load8_f32(w + 8 * c, g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = f[e] * r * g[e];
+    store8_bf16(y + t * H + 8 * c, f);
+  }
 }
 
 // dh (+)= rstd * g - x * rstd^3 * mean(g * x), g = w * (sum of the n bf16 inputs)
@@ -87,48 +123,90 @@ struct DyPtrs {
   const uint16_t* p[3];
 };
 
+__device__ __forceinline__ void dy_sum8(const DyPtrs& dys, int n_dy, int64_t off, float* f) {
+  load8_bf16(dys.p[0] + off, f);
+  for (int i = 1; i < n_dy; ++i) {
+    float u[8];
+    load8_bf16(dys.p[i] + off, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] += u[e];
+  }
+}
+
 __global__ __launch_bounds__(256) void k_rmsnorm_bwd(DyPtrs dys, int n_dy, const float* __restrict__ x,
                                                      const float* __restrict__ w,
                                                      const float* __restrict__ rstd, int64_t H,
                                                      int accumulate, float* __restrict__ dh) {
-  __shared__ float red[256];
+  __shared__ float red[4];
   const int64_t t = blockIdx.x;
   const float* xr = x + t * H;
   const float r = rstd[t];
-  auto dy_at = [&](int64_t j) {
-    float s = bf2f(dys.p[0][t * H + j]);
-    if (n_dy > 1) s += bf2f(dys.p[1][t * H + j]);
-    if (n_dy > 2) s += bf2f(dys.p[2][t * H + j]);
-    return s;
-  };
+  const int nc = (int)(H / 8);
   float acc = 0.0f;
-  for (int64_t j = threadIdx.x; j < H; j += 256) acc += dy_at(j) * w[j] * xr[j];
+  for (int c = threadIdx.x; c < nc; c += 256) {
+    float dy[8], f[8], g[8];
+    dy_sum8(dys, n_dy, t * H + 8 * c, dy);
+    load8_f32(xr + 8 * c, f);
+    load8_f32(w + 8 * c, g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += dy[e] * g[e] * f[e];
+  }
   acc = block_sum(acc, red);
-  const float c = r * r * r * acc / (float)H;
-  for (int64_t j = threadIdx.x; j < H; j += 256) {
-    const float d = r * dy_at(j) * w[j] - xr[j] * c;
-    dh[t * H + j] = accumulate ? dh[t * H + j] + d : d;
+  const float cc = r * r * r * acc / (float)H;
+  for (int c = threadIdx.x; c < nc; c += 256) {
+    float dy[8], f[8], g[8], o[8];
+    dy_sum8(dys, n_dy, t * H + 8 * c, dy);
+    load8_f32(xr + 8 * c, f);
+    load8_f32(w + 8 * c, g);
+    if (accumulate) load8_f32(dh + t * H + 8 * c, o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = r * dy[e] * g[e] - f[e] * cc;
+      o[e] = accumulate ? o[e] + d : d;
+    }
+    store8_f32(dh + t * H + 8 * c, o);
   }
 }
 
 // In-place rotary embedding of bf16 x[T, heads * d]; row t is position t % S.
+// inv[j] = theta^(-2j/d) (computed on the host in fp64); the angle and its
+// sine and cosine are fp64, the rotation fp32. One thread per 4 pairs.
+struct InvFreq {
+  double f[128];
+};
+
 __global__ __launch_bounds__(256) void k_rope(uint16_t* __restrict__ x, int64_t T, int64_t S,
-                                              int heads, int d, double theta, int inverse) {
-  const int64_t n = T * heads * (d / 2);
+                                              int heads, int d, InvFreq inv, int inverse) {
+  const int half = d / 2, q4 = half / 4;
+  const int64_t n = T * heads * q4;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  const int half = d / 2;
-  const int j = (int)(i % half);
-  const int64_t th = i / half;  // (row, head)
-  const int64_t row = th / heads;
-  const int64_t pos = row % S;
-  const double ang = (double)pos * pow(theta, -2.0 * j / d);
-  const float c = (float)cos(ang);
-  const float s = inverse ? -(float)sin(ang) : (float)sin(ang);
+  const int j0 = 4 * (int)(i % q4);
+  const int64_t th = i / q4;  // (row, head)
+  const int64_t pos = (th / heads) % S;
   uint16_t* v = x + th * d;
-  const float x1 = bf2f(v[j]), x2 = bf2f(v[j + half]);
-  v[j] = f2bf(x1 * c - x2 * s);
-  v[j + half] = f2bf(x2 * c + x1 * s);
+  const uint2 a = *reinterpret_cast<const uint2*>(v + j0);
+  const uint2 b = *reinterpret_cast<const uint2*>(v + j0 + half);
+  const uint32_t aw[2] = {a.x, a.y}, bw[2] = {b.x, b.y};
+  float o1[4], o2[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    double sd, cd;
+    sincos((double)pos * inv.f[j0 + e], &sd, &cd);
+    const float c = (float)cd, sn = inverse ? -(float)sd : (float)sd;
+    const uint32_t wa = aw[e >> 1], wb = bw[e >> 1];
+    const float x1 = __uint_as_float((e & 1) ? (wa & 0xFFFF0000u) : (wa << 16));
+    const float x2 = __uint_as_float((e & 1) ? (wb & 0xFFFF0000u) : (wb << 16));
+    o1[e] = x1 * c - x2 * sn;
+    o2[e] = x2 * c + x1 * sn;
+  }
+  uint2 ra, rb;
+  ra.x = pack_bf16x2(o1[0], o1[1]);
+  ra.y = pack_bf16x2(o1[2], o1[3]);
+  rb.x = pack_bf16x2(o2[0], o2[1]);
+  rb.y = pack_bf16x2(o2[2], o2[3]);
+  *reinterpret_cast<uint2*>(v + j0) = ra;
+  *reinterpret_cast<uint2*>(v + j0 + half) = rb;
 }
 
 // ---- attention on the matrix cores -------------------------------------------
@@ -668,8 +746,10 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float*
 
 hipError_t launch_rope(uint16_t* x, int64_t T, int64_t S, int heads, int d, double theta,
                        int inverse, hipStream_t s) {
-  hipLaunchKernelGGL(k_rope, dim3(grid_of(T * heads * (d / 2))), dim3(256), 0, s, x, T, S, heads, d,
-                     theta, inverse);
+  InvFreq inv;
+  for (int j = 0; j < 128; ++j) inv.f[j] = j < d / 2 ? pow(theta, -2.0 * j / d) : 0.0;
+  hipLaunchKernelGGL(k_rope, dim3(grid_of(T * heads * (d / 8))), dim3(256), 0, s, x, T, S, heads, d,
+                     inv, inverse);
   return hipGetLastError();
 }
 

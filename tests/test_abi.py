@@ -232,18 +232,21 @@ def test_decoder_argument_errors():
     assert _err(L.nf4s_rope, None, 4, 2, 2, 16, 1e4, 0) == L.EINVAL
     assert _err(L.nf4s_rope, FAKE, 6, 4, 2, 16, 1e4, 0) == L.ESHAPE        # rows % seq
     assert _err(L.nf4s_rope, FAKE, 6, 3, 1, 25, 1e4, 0) == L.ESHAPE        # odd head size
+    assert _err(L.nf4s_rope, FAKE, 6, 3, 1, 12, 1e4, 0) == L.ESHAPE        # not a multiple of 8
+    assert _err(L.nf4s_rmsnorm_fwd, FAKE, FAKE, 4, 12, 1e-5, FAKE, FAKE) == L.ESHAPE  # width % 8
+    assert _err(L.nf4s_rmsnorm_fwd, FAKE + 8, FAKE, 4, 16, 1e-5, FAKE, FAKE) == L.EALIGN
     assert _err(L.nf4s_rope, FAKE, 6, 3, 1, 16, 1.0, 0) == L.EINVAL        # theta
-    assert _err(L.nf4s_rope, FAKE + 1, 6, 3, 1, 16, 1e4, 0) == L.EALIGN
+    assert _err(L.nf4s_rope, FAKE + 4, 6, 3, 1, 16, 1e4, 0) == L.EALIGN
     assert _err(L.nf4s_attention_fwd, FAKE, FAKE, FAKE, 1, 4, 3, 2, 16, FAKE, None, FAKE) == L.ESHAPE
     assert _err(L.nf4s_attention_fwd, FAKE, FAKE, FAKE, 0, 4, 4, 2, 16, FAKE, None, FAKE) == L.ESHAPE
     assert _err(L.nf4s_attention_fwd, FAKE, FAKE, FAKE, 1, 4, 4, 2, 16, FAKE, None, FAKE) == L.ESHAPE
     assert _err(L.nf4s_attention_bwd, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 4, 2, 32, FAKE, FAKE,
                 FAKE, None, 0) == L.EWORKSPACE
-    assert _err(L.nf4s_rmsnorm_bwd, [], FAKE, FAKE, FAKE, 4, 4, 0, FAKE) == L.EINVAL
-    assert _err(L.nf4s_rmsnorm_bwd, [FAKE] * 4, FAKE, FAKE, FAKE, 4, 4, 0, FAKE) == L.EINVAL
-    assert _err(L.nf4s_rmsnorm_bwd, [FAKE], FAKE, FAKE, FAKE, 4, 4, 2, FAKE) == L.EINVAL
-    assert _err(L.nf4s_rmsnorm_fwd, FAKE, FAKE, 4, 4, 0.0, FAKE, FAKE) == L.EINVAL   # eps
-    assert _err(L.nf4s_rmsnorm_fwd, FAKE, FAKE, 0, 4, 1e-5, FAKE, FAKE) == L.ESHAPE
+    assert _err(L.nf4s_rmsnorm_bwd, [], FAKE, FAKE, FAKE, 4, 8, 0, FAKE) == L.EINVAL
+    assert _err(L.nf4s_rmsnorm_bwd, [FAKE] * 4, FAKE, FAKE, FAKE, 4, 8, 0, FAKE) == L.EINVAL
+    assert _err(L.nf4s_rmsnorm_bwd, [FAKE], FAKE, FAKE, FAKE, 4, 8, 2, FAKE) == L.EINVAL
+    assert _err(L.nf4s_rmsnorm_fwd, FAKE, FAKE, 4, 8, 0.0, FAKE, FAKE) == L.EINVAL   # eps
+    assert _err(L.nf4s_rmsnorm_fwd, FAKE, FAKE, 0, 8, 1e-5, FAKE, FAKE) == L.ESHAPE
     assert _err(L.nf4s_adamw, FAKE, FAKE, FAKE, FAKE, 16, 1e-3, 0.9, 0.999, 1e-8, 0.0, 0) == L.EINVAL
     assert _err(L.nf4s_adamw, FAKE, FAKE, FAKE, FAKE, 16, 1e-3, 1.0, 0.999, 1e-8, 0.0, 1) == L.EINVAL
     assert _err(L.nf4s_cross_entropy, FAKE, FAKE, 8, 100, FAKE, FAKE, FAKE, 4) == L.EWORKSPACE

@@ -305,7 +305,7 @@ def test_decoder_entry_point_errors():
                              lse.data_ptr())
     assert e.value.code == L.ESHAPE
     with pytest.raises(L.Nf4sError) as e:
-        L.nf4s_rmsnorm_bwd([], 0, 0, 0, 4, 4, 0, 0)
+        L.nf4s_rmsnorm_bwd([], 0, 0, 0, 4, 8, 0, 0)
     assert e.value.code in (L.EINVAL,)
     with pytest.raises(L.Nf4sError) as e:
         L.nf4s_adamw(lse.data_ptr(), lse.data_ptr(), lse.data_ptr(), lse.data_ptr(), 16, 1e-3, 0.9,

@@ -31,6 +31,15 @@ Readings where the pages are silent (llama's published definitions):
   * the optimiser of the adapters is plain AdamW (decoupled weight decay,
     bias-corrected moments) in fp32; the pages' paged 8-bit AdamW is an
     allocation strategy of a library, not part of the step's arithmetic.
+
+Preference step ("Soup v0.72.4 technical analysis", sections 3.1-3.3): the
+reference model is the same frozen base with the adapters switched off, the
+policy the base with them on; no second model. The pages name DPO without
+writing its loss; reading: the DPO objective of Rafailov et al. (2023),
+    L = -mean_p log sigmoid(beta * ((lp_c - lr_c) - (lp_r - lr_r))),
+with lp / lr the policy / reference log-probability of a sequence, the sum of
+its masked per-token log-probabilities log softmax(z_t)[target_t], and
+sequences ordered chosen, rejected per pair.
 """
 from __future__ import annotations
 
@@ -179,9 +188,9 @@ def adamw(p, g, m, v, t, lr, beta1=0.9, beta2=0.999, eps=1e-8, wd=0.0):
 
 # ---- the model -----------------------------------------------------------------
 
-def _lin(x, P: Params, l, p, cfg):
+def _lin(x, P: Params, l, p, cfg, adapters=True):
     y = x @ P.W[l][p].T
-    if p in cfg.targets:
+    if adapters and p in cfg.targets:
         a, b = P.lora[l][p]
         y = y + cfg.scale * ((x @ a.T) @ b.T)
     return y
@@ -197,8 +206,9 @@ def _lin_bwd(x, dy, P: Params, l, p, cfg, grads):
     return dx
 
 
-def forward(P: Params, ids, targets, cfg: Config, exact=False):
-    """Returns (loss, logits [B*S, V], cache)."""
+def forward(P: Params, ids, targets, cfg: Config, exact=False, adapters=True):
+    """Returns (loss, logits [B*S, V], cache). adapters=False evaluates the
+    frozen base alone (the reference model of a preference step)."""
     B, S = ids.shape
     T = B * S
     cos, sin = rope_tables(S, cfg.head_dim, cfg.rope_theta)
@@ -209,20 +219,20 @@ def forward(P: Params, ids, targets, cfg: Config, exact=False):
         c = {"h_in": h}
         n1, c["rstd1"] = rmsnorm(h, P.w_attn[l], cfg.eps)
         n1 = _r(n1, exact)
-        q = _r(_lin(n1, P, l, "q", cfg), exact).reshape(B, S, cfg.heads, cfg.head_dim)
-        k = _r(_lin(n1, P, l, "k", cfg), exact).reshape(B, S, cfg.kv_heads, cfg.head_dim)
-        v = _r(_lin(n1, P, l, "v", cfg), exact).reshape(B, S, cfg.kv_heads, cfg.head_dim)
+        q = _r(_lin(n1, P, l, "q", cfg, adapters), exact).reshape(B, S, cfg.heads, cfg.head_dim)
+        k = _r(_lin(n1, P, l, "k", cfg, adapters), exact).reshape(B, S, cfg.kv_heads, cfg.head_dim)
+        v = _r(_lin(n1, P, l, "v", cfg, adapters), exact).reshape(B, S, cfg.kv_heads, cfg.head_dim)
         qr, kr = _r(rope(q, cos, sin), exact), _r(rope(k, cos, sin), exact)
         o, Pm = attention(qr, kr, v, grp)
         o = _r(o, exact).reshape(T, -1)
-        h = h + _r(_lin(o, P, l, "o", cfg), exact)
+        h = h + _r(_lin(o, P, l, "o", cfg, adapters), exact)
         c.update(n1=n1, qr=qr, kr=kr, v=v, P=Pm, o=o, h_mid=h)
         n2, c["rstd2"] = rmsnorm(h, P.w_mlp[l], cfg.eps)
         n2 = _r(n2, exact)
-        g = _r(_lin(n2, P, l, "gate", cfg), exact)
-        u = _r(_lin(n2, P, l, "up", cfg), exact)
+        g = _r(_lin(n2, P, l, "gate", cfg, adapters), exact)
+        u = _r(_lin(n2, P, l, "up", cfg, adapters), exact)
         sw = _r(silu(g) * u, exact)
-        h = h + _r(_lin(sw, P, l, "down", cfg), exact)
+        h = h + _r(_lin(sw, P, l, "down", cfg, adapters), exact)
         c.update(n2=n2, g=g, u=u, sw=sw)
         cache["layers"].append(c)
     hn, rstd_f = rmsnorm(h, P.w_final, cfg.eps)
@@ -265,3 +275,53 @@ def backward(P: Params, cache, cfg: Config, exact=False):
                + _r(_lin_bwd(c["n1"], dv, P, l, "v", cfg, grads), exact))
         dh = dh + rmsnorm_bwd(dn1, c["h_in"], P.w_attn[l], c["rstd1"])
     return {"lora": grads, "dh0": dh}
+
+
+# ---- preference step -------------------------------------------------------------
+
+def token_nll(logits, targets):
+    """Per-token negative log-probability of the target: logsumexp(z_t) - z_t[target_t]."""
+    m = logits.max(axis=-1, keepdims=True)
+    lse = (m + np.log(np.sum(np.exp(logits - m), axis=-1, keepdims=True)))[:, 0]
+    return lse - logits[np.arange(logits.shape[0]), targets]
+
+
+def log_sigmoid(x):
+    return -(np.maximum(-x, 0.0) + np.log1p(np.exp(-np.abs(x))))
+
+
+def dpo_loss(nll_policy, nll_ref, mask, seq, beta):
+    """DPO over sequences of length seq ordered chosen, rejected per pair.
+    Returns (loss, coef) with coef[s] = dL/d(nll summed over sequence s's
+    masked tokens) -- the weight of (softmax - onehot) in that sequence's
+    logit gradient."""
+    lp = -(mask * nll_policy).reshape(-1, seq).sum(axis=1)
+    lr = -(mask * nll_ref).reshape(-1, seq).sum(axis=1)
+    n = lp.size // 2
+    delta = beta * ((lp[0::2] - lr[0::2]) - (lp[1::2] - lr[1::2]))
+    loss = float(-np.mean(log_sigmoid(delta)))
+    g = -(1.0 / n) * np.exp(log_sigmoid(-delta))   # dL/d delta = -sigmoid(-delta)/n
+    coef = np.empty(2 * n)
+    coef[0::2] = -beta * g     # d lp_c = -d nll_c
+    coef[1::2] = beta * g
+    return loss, coef
+
+
+def dpo_step(P: Params, ids, targets, mask, cfg: Config, beta, exact=False):
+    """Reference forward (adapters off), policy forward and backward for the
+    DPO loss. ids/targets [2 * pairs, S] ordered chosen, rejected per pair;
+    mask [2 * pairs, S] weights of the response tokens. Returns (loss,
+    {"lora": ..., "dh0": ...}, policy logits)."""
+    S = ids.shape[1]
+    _, ref_logits, _ = forward(P, ids, targets, cfg, exact, adapters=False)
+    _, logits, cache = forward(P, ids, targets, cfg, exact)
+    t = targets.reshape(-1)
+    m = mask.reshape(-1).astype(np.float64)
+    loss, coef = dpo_loss(token_nll(logits, t), token_nll(ref_logits, t), m, S, beta)
+    z = logits - logits.max(axis=-1, keepdims=True)
+    p = np.exp(z)
+    p /= p.sum(axis=-1, keepdims=True)
+    p[np.arange(t.size), t] -= 1.0
+    w = np.repeat(coef, S) * m
+    cache["dlogits"] = p * w[:, None]
+    return loss, backward(P, cache, cfg, exact), logits

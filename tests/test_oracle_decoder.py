@@ -209,3 +209,86 @@ def test_bf16_rounding_points():
     assert abs(le - lr_) < 0.05 * abs(le)
     for x in (logits, cache["hn"], cache["layers"][0]["n1"], cache["layers"][1]["sw"]):
         assert np.array_equal(D.bf16(x), x)
+
+
+# ---- preference step (DPO) ----------------------------------------------------------
+
+def _pref_batch(cfg, pairs=2, S=10, prompt=4, seed=8, share_prompt=True):
+    """Chosen/rejected sequences (sharing a prompt unless told otherwise);
+    mask = response targets."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ids = rng.integers(0, cfg.vocab, size=(2 * pairs, S + 1))
+    for p in range(pairs if share_prompt else 0):
+        ids[2 * p + 1, :prompt] = ids[2 * p, :prompt]
+    mask = np.zeros((2 * pairs, S))
+    mask[:, prompt - 1:] = 1.0
+    return ids[:, :-1].copy(), ids[:, 1:].copy(), mask
+
+
+def test_token_nll_against_logsumexp():
+    rng = np.random.Generator(np.random.PCG64(12))
+    z = rng.standard_normal((6, 50)) * 2
+    t = rng.integers(0, 50, size=6)
+    assert np.allclose(D.token_nll(z, t), logsumexp(z, axis=1) - z[np.arange(6), t], atol=1e-13)
+
+
+def test_dpo_loss_closed_form_and_coefficients():
+    """One pair of length 2: delta = beta*((lp_c - lr_c) - (lp_r - lr_r)) and
+    L = log(1 + e^-delta); the coefficients are dL/d(masked nll sums)."""
+    beta = 0.1
+    nll_p = np.array([1.0, 2.0, 0.5, 3.0])
+    nll_r = np.array([1.5, 1.5, 1.0, 1.0])
+    mask = np.array([0.0, 1.0, 1.0, 1.0])
+    lp_c, lp_r = -2.0, -3.5
+    lr_c, lr_r = -1.5, -2.0
+    delta = beta * ((lp_c - lr_c) - (lp_r - lr_r))
+    loss, coef = D.dpo_loss(nll_p, nll_r, mask, 2, beta)
+    assert abs(loss - math.log1p(math.exp(-delta))) < 1e-15
+    e = 1e-7
+    for s in range(2):
+        bump = np.zeros(4)
+        bump[2 * s + 1] = e              # a masked-in token of sequence s
+        fd = (D.dpo_loss(nll_p + bump, nll_r, mask, 2, beta)[0]
+              - D.dpo_loss(nll_p - bump, nll_r, mask, 2, beta)[0]) / (2 * e)
+        assert abs(fd - coef[s]) < 1e-9, (s, fd, coef[s])
+    # a policy that favours the chosen answer more than the reference does: loss < ln 2
+    assert delta > 0 and loss < math.log(2)
+
+
+def test_dpo_zero_adapters_gives_ln2_and_no_dA():
+    """B = 0 makes the policy equal the reference: delta = 0, L = ln 2 exactly,
+    and dA vanishes while dB does not ("Soup layer-streamed NF4 training
+    measured", section 2.5: with B = 0 the A gradient is structurally zero)."""
+    cfg = _cfg()
+    P = _params(cfg, b_scale=0.0)
+    ids, tg, mask = _pref_batch(cfg)
+    loss, g, _ = D.dpo_step(P, ids, tg, mask, cfg, beta=0.1, exact=True)
+    assert abs(loss - math.log(2)) < 1e-15
+    for (l, p), (dA, dB) in g["lora"].items():
+        assert np.all(dA == 0) and np.any(dB != 0), (l, p)
+
+
+@pytest.mark.parametrize("share_prompt", [True, False])
+def test_dpo_finite_differences(share_prompt):
+    """With distinct prompts the masked-out prompt tokens would contribute if
+    the mask were ignored (a shared prompt cancels between chosen and
+    rejected), so both layouts are checked."""
+    cfg = _cfg()
+    P = _params(cfg)
+    ids, tg, mask = _pref_batch(cfg, share_prompt=share_prompt)
+    beta = 0.5
+    loss, g, _ = D.dpo_step(P, ids, tg, mask, cfg, beta, exact=True)
+    rng = np.random.Generator(np.random.PCG64(13))
+    eps = 1e-5
+    for (l, p), (dA, dB) in g["lora"].items():
+        a, b = P.lora[l][p]
+        for arr, grad in ((a, dA), (b, dB)):
+            idx = tuple(rng.integers(0, s) for s in arr.shape)
+            old = arr[idx]
+            arr[idx] = old + eps
+            lp_ = D.dpo_step(P, ids, tg, mask, cfg, beta, exact=True)[0]
+            arr[idx] = old - eps
+            lm_ = D.dpo_step(P, ids, tg, mask, cfg, beta, exact=True)[0]
+            arr[idx] = old
+            fd = (lp_ - lm_) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-8 + 1e-4 * abs(fd), (l, p, idx, fd, grad[idx])

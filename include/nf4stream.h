@@ -389,6 +389,33 @@ int nf4s_cross_entropy(const uint16_t* logits, const int64_t* targets, int64_t T
                        float* loss, uint16_t* dlogits, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Preference step (DPO), "Soup v0.72.4 technical analysis" s3.1-3.3: the
+ * reference model is the same streamed base with the adapters off, the policy
+ * the base with them on; no second model. Sequences are rows of S tokens,
+ * ordered chosen, rejected per pair; mask fp32 [T] weights the tokens that
+ * count (the response).
+ *   nf4s_token_nll:  nll[t] = logsumexp(z_t) - z_t[target_t] (fp32 [T]; NaN
+ *                    for a target outside [0, V)); logits bf16 [T, V].
+ *   nf4s_dpo_loss:   lp / lr = -sum_t mask * nll over each sequence (policy /
+ *                    reference), delta = beta ((lp_c - lr_c) - (lp_r - lr_r)),
+ *                    loss (device fp32 [1]) = -mean over pairs of
+ *                    log sigmoid(delta) (the DPO objective of Rafailov et al.
+ *                    2023, the pages name the method, not its formula);
+ *                    seq_coef fp32 [2 pairs] = dL/d(masked nll sum) of each
+ *                    sequence. Fixed-order sums.
+ *   nf4s_logit_grad: dlogits[t] = bf16(seq_coef[t/S] * mask[t] *
+ *                    (softmax(z_t) - onehot(target_t))), the logits' gradient.
+ * Errors: EINVAL, ESHAPE, EALIGN.
+ */
+int nf4s_token_nll(const uint16_t* logits, const int64_t* targets, int64_t T, int64_t V, float* nll,
+                   void* stream);
+int nf4s_dpo_loss(const float* nll_policy, const float* nll_ref, const float* mask, int64_t pairs,
+                  int64_t S, float beta, float* loss, float* seq_coef, void* stream);
+int nf4s_logit_grad(const uint16_t* logits, const int64_t* targets, const float* seq_coef,
+                    const float* mask, int64_t T, int64_t S, int64_t V, uint16_t* dlogits,
+                    void* stream);
+
+/*
  * One AdamW step on fp32 parameters (the adapters' optimiser; [G] s4.1 uses a
  * paged 8-bit AdamW, whose paging is an allocation strategy): with t = step
  * (from 1), m = b1 m + (1-b1) g, v = b2 v + (1-b2) g^2,

@@ -36,7 +36,8 @@ EXPORTS = (
     "streamed_linear_bwd_packed", "dense_linear_fwd_packed", "dense_linear_bwd_packed",
     "nf4s_embed", "nf4s_rmsnorm_fwd", "nf4s_rmsnorm_bwd", "nf4s_rope", "nf4s_attention_fwd",
     "nf4s_attention_bwd", "nf4s_swiglu_fwd", "nf4s_swiglu_bwd", "nf4s_residual_add",
-    "nf4s_to_bf16", "nf4s_cross_entropy", "nf4s_adamw",
+    "nf4s_to_bf16", "nf4s_cross_entropy", "nf4s_adamw", "nf4s_token_nll", "nf4s_dpo_loss",
+    "nf4s_logit_grad",
 )
 
 
@@ -124,6 +125,9 @@ _SIG = {
     "nf4s_cross_entropy": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
     "nf4s_adamw": (ctypes.c_int, [_P, _P, _P, _P, _I64, ctypes.c_float, ctypes.c_float,
                                   ctypes.c_float, ctypes.c_float, ctypes.c_float, _I64, _P]),
+    "nf4s_token_nll": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
+    "nf4s_dpo_loss": (ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P, _P]),
+    "nf4s_logit_grad": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
 }
 
 
@@ -277,6 +281,18 @@ def nf4s_cross_entropy(logits, targets, T, V, loss, dlogits, ws, ws_bytes, strea
 
 def nf4s_adamw(p, g, m, v, n, lr, beta1, beta2, eps, weight_decay, step, stream=0):
     _check(lib().nf4s_adamw(p, g, m, v, n, lr, beta1, beta2, eps, weight_decay, step, stream))
+
+
+def nf4s_token_nll(logits, targets, T, V, nll, stream=0):
+    _check(lib().nf4s_token_nll(logits, targets, T, V, nll, stream))
+
+
+def nf4s_dpo_loss(nll_policy, nll_ref, mask, pairs, S, beta, loss, seq_coef, stream=0):
+    _check(lib().nf4s_dpo_loss(nll_policy, nll_ref, mask, pairs, S, beta, loss, seq_coef, stream))
+
+
+def nf4s_logit_grad(logits, targets, seq_coef, mask, T, S, V, dlogits, stream=0):
+    _check(lib().nf4s_logit_grad(logits, targets, seq_coef, mask, T, S, V, dlogits, stream))
 
 
 def lora_fwd(x, M, k_in, A, r, u_out, ws, ws_bytes, stream=0):

@@ -621,6 +621,47 @@ int nf4s_cross_entropy(const uint16_t* logits, const int64_t* targets, int64_t T
                   "cross_entropy launch");
 }
 
+int nf4s_token_nll(const uint16_t* logits, const int64_t* targets, int64_t T, int64_t V, float* nll,
+                   void* stream) {
+  int rc;
+  if ((rc = check_rows(T, V))) return rc;
+  if ((rc = check_ptr(logits, "logits", 2)) || (rc = check_ptr(targets, "targets", 8)) ||
+      (rc = check_ptr(nll, "nll", 4)))
+    return rc;
+  return launched(launch_token_nll(logits, targets, T, V, nll, static_cast<hipStream_t>(stream)),
+                  "token_nll launch");
+}
+
+int nf4s_dpo_loss(const float* nll_policy, const float* nll_ref, const float* mask, int64_t pairs,
+                  int64_t S, float beta, float* loss, float* seq_coef, void* stream) {
+  int rc;
+  if (pairs <= 0 || pairs > 4096 || S <= 0 || 2 * pairs * S >= (1ll << 31))
+    return fail(NF4S_ESHAPE, "pairs=%lld seq=%lld out of range", (long long)pairs, (long long)S);
+  if (!std::isfinite(beta) || !(beta > 0.0f)) return fail(NF4S_EINVAL, "beta must be positive and finite");
+  if ((rc = check_ptr(nll_policy, "nll_policy", 4)) || (rc = check_ptr(nll_ref, "nll_ref", 4)) ||
+      (rc = check_ptr(mask, "mask", 4)) || (rc = check_ptr(loss, "loss", 4)) ||
+      (rc = check_ptr(seq_coef, "seq_coef", 4)))
+    return rc;
+  return launched(launch_dpo(nll_policy, nll_ref, mask, pairs, S, beta, loss, seq_coef,
+                             static_cast<hipStream_t>(stream)),
+                  "dpo launch");
+}
+
+int nf4s_logit_grad(const uint16_t* logits, const int64_t* targets, const float* seq_coef,
+                    const float* mask, int64_t T, int64_t S, int64_t V, uint16_t* dlogits,
+                    void* stream) {
+  int rc;
+  if ((rc = check_rows(T, V))) return rc;
+  if (S <= 0 || T % S) return fail(NF4S_ESHAPE, "rows=%lld must be a multiple of seq=%lld", (long long)T, (long long)S);
+  if ((rc = check_ptr(logits, "logits", 2)) || (rc = check_ptr(targets, "targets", 8)) ||
+      (rc = check_ptr(seq_coef, "seq_coef", 4)) || (rc = check_ptr(mask, "mask", 4)) ||
+      (rc = check_ptr(dlogits, "dlogits", 2)))
+    return rc;
+  return launched(launch_logit_grad(logits, targets, seq_coef, mask, T, S, V, dlogits,
+                                    static_cast<hipStream_t>(stream)),
+                  "logit_grad launch");
+}
+
 int nf4s_adamw(float* p, const float* g, float* m, float* v, int64_t n, float lr, float beta1,
                float beta2, float eps, float weight_decay, int64_t step, void* stream) {
   int rc;

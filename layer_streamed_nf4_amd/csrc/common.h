@@ -109,6 +109,13 @@ hipError_t launch_f32_to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_
 size_t cross_entropy_ws_bytes(int64_t T);
 hipError_t launch_cross_entropy(const uint16_t* logits, const int64_t* targets, int64_t T, int64_t V,
                                 float* loss, uint16_t* dlogits, void* ws, hipStream_t s);
+hipError_t launch_token_nll(const uint16_t* logits, const int64_t* targets, int64_t T, int64_t V,
+                            float* nll, hipStream_t s);
+hipError_t launch_dpo(const float* nll_p, const float* nll_r, const float* mask, int64_t pairs,
+                      int64_t S, float beta, float* loss, float* coef, hipStream_t s);
+hipError_t launch_logit_grad(const uint16_t* logits, const int64_t* targets, const float* coef,
+                             const float* mask, int64_t T, int64_t S, int64_t V, uint16_t* dlogits,
+                             hipStream_t s);
 hipError_t launch_adamw(float* p, const float* g, float* m, float* v, int64_t n, float lr, float b1,
                         float b2, float eps, float wd, int64_t step, hipStream_t s);
 

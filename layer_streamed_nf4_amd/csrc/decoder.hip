@@ -704,6 +704,89 @@ __global__ __launch_bounds__(256) void k_mean(const float* __restrict__ x, int64
   if (threadIdx.x == 0) out[0] = s / (float)n;
 }
 
+// ---- preference step (DPO) ---------------------------------------------------
+// Per-token negative log-probability of the target, logsumexp(z_t) - z_t[y_t]
+// (fp32; NaN for a target outside [0, V)); one workgroup per row.
+__global__ __launch_bounds__(256) void k_token_nll(const uint16_t* __restrict__ logits,
+                                                   const int64_t* __restrict__ targets, int64_t V,
+                                                   float* __restrict__ nll) {
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  const uint16_t* z = logits + t * V;
+  float m = -INFINITY;
+  for (int64_t j = threadIdx.x; j < V; j += 256) m = fmaxf(m, bf2f(z[j]));
+  m = block_max(m, red);
+  float s = 0.0f;
+  for (int64_t j = threadIdx.x; j < V; j += 256) s += expf(bf2f(z[j]) - m);
+  s = block_sum(s, red);
+  const int64_t tg = targets[t];
+  const bool ok = tg >= 0 && tg < V;
+  if (threadIdx.x == 0) nll[t] = ok ? m + logf(s) - bf2f(z[tg]) : __builtin_nanf("");
+}
+
+__device__ __forceinline__ float log_sigmoid(float x) {
+  return -(fmaxf(-x, 0.0f) + log1pf(expf(-fabsf(x))));
+}
+
+// DPO over n_seq = 2 * pairs sequences of S tokens (chosen, rejected per
+// pair): lp / lr = -sum of mask * nll (policy / reference) per sequence, in
+// a fixed order; delta = beta * ((lp_c - lr_c) - (lp_r - lr_r));
+// loss = -mean log sigmoid(delta); coef[s] = dL/d(sum of masked nll of s).
+// One workgroup.
+__global__ __launch_bounds__(256) void k_dpo(const float* __restrict__ nll_p,
+                                             const float* __restrict__ nll_r,
+                                             const float* __restrict__ mask, int64_t pairs,
+                                             int64_t S, float beta, float* __restrict__ loss,
+                                             float* __restrict__ coef) {
+  __shared__ float red[4];
+  float total = 0.0f;
+  for (int64_t p = 0; p < pairs; ++p) {
+    float v[4];  // lp_c, lr_c, lp_r, lr_r
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t base = (2 * p + (q >> 1)) * S;
+      const float* src = (q & 1) ? nll_r : nll_p;
+      float a = 0.0f;
+      for (int64_t j = threadIdx.x; j < S; j += 256) a += mask[base + j] * src[base + j];
+      v[q] = -block_sum(a, red);
+    }
+    const float delta = beta * ((v[0] - v[1]) - (v[2] - v[3]));
+    const float sig_neg = expf(log_sigmoid(-delta));  // sigmoid(-delta)
+    const float g = sig_neg / (float)pairs;           // -dL/d delta
+    if (threadIdx.x == 0) {
+      coef[2 * p] = beta * g;
+      coef[2 * p + 1] = -beta * g;
+    }
+    total += log_sigmoid(delta);
+  }
+  if (threadIdx.x == 0) loss[0] = -total / (float)pairs;
+}
+
+// dlogits[t] = bf16(coef[t / S] * mask[t] * (softmax(z_t) - onehot(y_t))).
+__global__ __launch_bounds__(256) void k_logit_grad(const uint16_t* __restrict__ logits,
+                                                    const int64_t* __restrict__ targets,
+                                                    const float* __restrict__ coef,
+                                                    const float* __restrict__ mask, int64_t S,
+                                                    int64_t V, uint16_t* __restrict__ dlogits) {
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  const uint16_t* z = logits + t * V;
+  float m = -INFINITY;
+  for (int64_t j = threadIdx.x; j < V; j += 256) m = fmaxf(m, bf2f(z[j]));
+  m = block_max(m, red);
+  float s = 0.0f;
+  for (int64_t j = threadIdx.x; j < V; j += 256) s += expf(bf2f(z[j]) - m);
+  s = block_sum(s, red);
+  const float lse = m + logf(s);
+  const float w = coef[t / S] * mask[t];
+  const int64_t tg = targets[t];
+  for (int64_t j = threadIdx.x; j < V; j += 256) {
+    float p = expf(bf2f(z[j]) - lse);
+    if (j == tg) p -= 1.0f;
+    dlogits[t * V + j] = f2bf(w * p);
+  }
+}
+
 __global__ __launch_bounds__(256) void k_adamw(float* __restrict__ p, const float* __restrict__ g,
                                                float* __restrict__ m, float* __restrict__ v,
                                                int64_t n, float lr, float b1, float b2, float eps,
@@ -834,6 +917,26 @@ hipError_t launch_cross_entropy(const uint16_t* logits, const int64_t* targets, 
   float* rows = static_cast<float*>(ws);
   hipLaunchKernelGGL(k_ce_rows, dim3((unsigned)T), dim3(256), 0, s, logits, targets, T, V, rows, dlogits);
   hipLaunchKernelGGL(k_mean, dim3(1), dim3(256), 0, s, rows, T, loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_nll(const uint16_t* logits, const int64_t* targets, int64_t T, int64_t V,
+                            float* nll, hipStream_t s) {
+  hipLaunchKernelGGL(k_token_nll, dim3((unsigned)T), dim3(256), 0, s, logits, targets, V, nll);
+  return hipGetLastError();
+}
+
+hipError_t launch_dpo(const float* nll_p, const float* nll_r, const float* mask, int64_t pairs,
+                      int64_t S, float beta, float* loss, float* coef, hipStream_t s) {
+  hipLaunchKernelGGL(k_dpo, dim3(1), dim3(256), 0, s, nll_p, nll_r, mask, pairs, S, beta, loss, coef);
+  return hipGetLastError();
+}
+
+hipError_t launch_logit_grad(const uint16_t* logits, const int64_t* targets, const float* coef,
+                             const float* mask, int64_t T, int64_t S, int64_t V, uint16_t* dlogits,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(k_logit_grad, dim3((unsigned)T), dim3(256), 0, s, logits, targets, coef, mask, S,
+                     V, dlogits);
   return hipGetLastError();
 }
 

@@ -30,7 +30,8 @@ import torch
 from . import (OP_ATTENTION_BWD, OP_CROSS_ENTROPY, OP_DENSE_BWD_PACKED, OP_DENSE_FWD_PACKED,
                OP_LINEAR_BWD_PACKED, OP_LINEAR_FWD_PACKED, OP_LORA_BWD, OP_LORA_FWD,
                dense_linear_bwd_packed, dense_linear_fwd_packed, lora_bwd, lora_fwd, nf4s_adamw,
-               nf4s_attention_bwd, nf4s_attention_fwd, nf4s_cross_entropy, nf4s_embed,
+               nf4s_attention_bwd, nf4s_attention_fwd, nf4s_cross_entropy, nf4s_dpo_loss,
+               nf4s_embed, nf4s_logit_grad, nf4s_token_nll,
                nf4s_pack_activation, nf4s_packed_activation_bytes, nf4s_pool_acquire,
                nf4s_pool_create, nf4s_pool_destroy, nf4s_pool_prefetch, nf4s_pool_release,
                nf4s_pool_set_layer, nf4s_pool_stats, nf4s_residual_add, nf4s_rmsnorm_bwd,
@@ -198,11 +199,11 @@ class Decoder:
             self._packed_key = key
         return self.packed.data_ptr()
 
-    def _fwd(self, base, i, p, x, y):
+    def _fwd(self, base, i, p, x, y, adapters=True):
         no, ki = self.sh.shapes[p]
         xp = self._pack(x, ki)
         d = self.sh.layout.descs[p]
-        if p in self.targets:
+        if adapters and p in self.targets:
             A, Bm = self.lora[(i, p)]
             lora_fwd(x.data_ptr(), self.M, ki, A.data_ptr(), self.r, self.u[p].data_ptr(), *self._ws(),
                      self._s)
@@ -245,31 +246,35 @@ class Decoder:
                                        *self._ws(), self._s)
 
     # -- one layer ---------------------------------------------------------------------
-    def _layer_fwd(self, i, base, recompute):
+    def _layer_fwd(self, i, base, recompute, adapters=True, hin=None, hout=None):
         """Layer i's body from h_i. The recompute keeps the fp32 attention
-        output for the backward and skips h_{i+1}, which is already stored."""
+        output for the backward and skips h_{i+1}, which is already stored.
+        adapters=False runs the frozen base alone (the reference model);
+        hin/hout default to the checkpoints h_i, h_{i+1}."""
         c, s, M = self.cfg, self._s, self.M
         H = self.H
         self._packed_key = None
-        hin, hout = self.h[i], self.h[i + 1]
+        hin = self.h[i] if hin is None else hin
+        hout = self.h[i + 1] if hout is None else hout
+        a = adapters
         nf4s_rmsnorm_fwd(hin.data_ptr(), self.norms["attn"][i].data_ptr(), M, H, c["eps"],
                          self.n1.data_ptr(), self.rstd1.data_ptr(), s)
-        self._fwd(base, i, "q", self.n1, self.q)
-        self._fwd(base, i, "k", self.n1, self.k)
-        self._fwd(base, i, "v", self.n1, self.vv)
+        self._fwd(base, i, "q", self.n1, self.q, a)
+        self._fwd(base, i, "k", self.n1, self.k, a)
+        self._fwd(base, i, "v", self.n1, self.vv, a)
         nf4s_rope(self.q.data_ptr(), M, self.S, c["heads"], c["head_dim"], c["rope_theta"], 0, s)
         nf4s_rope(self.k.data_ptr(), M, self.S, c["kv_heads"], c["head_dim"], c["rope_theta"], 0, s)
         nf4s_attention_fwd(self.q.data_ptr(), self.k.data_ptr(), self.vv.data_ptr(), self.B, self.S,
                            c["heads"], c["kv_heads"], c["head_dim"], self.o.data_ptr(),
                            self.o32.data_ptr() if recompute else None, self.lse.data_ptr(), s)
-        self._fwd(base, i, "o", self.o, self.ao)
+        self._fwd(base, i, "o", self.o, self.ao, a)
         nf4s_residual_add(hin.data_ptr(), self.ao.data_ptr(), M * H, self.h_mid.data_ptr(), s)
         nf4s_rmsnorm_fwd(self.h_mid.data_ptr(), self.norms["mlp"][i].data_ptr(), M, H, c["eps"],
                          self.n2.data_ptr(), self.rstd2.data_ptr(), s)
-        self._fwd(base, i, "gate", self.n2, self.g)
-        self._fwd(base, i, "up", self.n2, self.u_)
+        self._fwd(base, i, "gate", self.n2, self.g, a)
+        self._fwd(base, i, "up", self.n2, self.u_, a)
         nf4s_swiglu_fwd(self.g.data_ptr(), self.u_.data_ptr(), M * self.I, self.sw.data_ptr(), s)
-        self._fwd(base, i, "down", self.sw, self.dn)
+        self._fwd(base, i, "down", self.sw, self.dn, a)
         if not recompute:
             nf4s_residual_add(self.h_mid.data_ptr(), self.dn.data_ptr(), M * H, hout.data_ptr(), s)
 
@@ -304,40 +309,119 @@ class Decoder:
                          self.dh.data_ptr(), s)
 
     # -- the step ----------------------------------------------------------------------
-    def forward_backward(self, ids, targets):
-        """Queue the forward and backward sweeps for token ids / next-token
-        targets (device int64 [batch*seq]); returns at once. The loss lands in
-        self.loss, the logits in self.logits, adapter gradients in self.grads."""
-        c, M, H, V = self.cfg, self.M, self.H, self.V
-        assert ids.numel() == M and targets.numel() == M
+    def _check_ids(self, ids, targets):
+        assert ids.numel() == self.M and targets.numel() == self.M
         assert ids.dtype == torch.int64 and targets.dtype == torch.int64
-        self.compute.wait_stream(torch.cuda.current_stream())
-        s = self._s
-        L = self.L
-        nf4s_embed(self.embed.data_ptr(), V, H, ids.data_ptr(), M, self.h[0].data_ptr(), s)
-        for i in range(L):
-            base = self._acquire(i, nxt=i + 1 if i + 1 < L else None)
-            self._layer_fwd(i, base, recompute=False)
-            self._release(i)
-        # head: final norm, resident lm_head, cross-entropy
+
+    def _head_fwd(self, h_last):
+        """Final norm and the resident lm_head: self.logits from h_L."""
+        c, M, H, V, s = self.cfg, self.M, self.H, self.V, self._s
         self._packed_key = None
-        nf4s_rmsnorm_fwd(self.h[L].data_ptr(), self.norms["final"].data_ptr(), M, H, c["eps"],
+        nf4s_rmsnorm_fwd(h_last.data_ptr(), self.norms["final"].data_ptr(), M, H, c["eps"],
                          self.hn.data_ptr(), self.rstd_f.data_ptr(), s)
         dense_linear_fwd_packed(self.lm_head.data_ptr(), V, H, self._pack(self.hn, H), M,
                                 self.logits.data_ptr(), *self._ws(), s)
-        nf4s_cross_entropy(self.logits.data_ptr(), targets.data_ptr(), M, V, self.loss.data_ptr(),
-                           self.dlogits.data_ptr(), *self._ws(), s)
+
+    def _forward_sweep(self, adapters, nxt_last=None):
+        """Layers 0..L-1 from h_0 (the last one prefetching nxt_last)."""
+        L = self.L
+        for i in range(L):
+            base = self._acquire(i, nxt=i + 1 if i + 1 < L else nxt_last)
+            self._layer_fwd(i, base, recompute=False, adapters=adapters)
+            self._release(i)
+
+    def _backward(self):
+        """From self.dlogits: lm_head and final norm backward, then the
+        backward sweep that recomputes each layer and differentiates it."""
+        M, H, V, s, L = self.M, self.H, self.V, self._s, self.L
+        self._packed_key = None
         dense_linear_bwd_packed(self.lm_head.data_ptr(), V, H, self._pack(self.dlogits, V), M,
                                 self.dhn.data_ptr(), *self._ws(), s)
         nf4s_rmsnorm_bwd([self.dhn.data_ptr()], self.h[L].data_ptr(), self.norms["final"].data_ptr(),
                          self.rstd_f.data_ptr(), M, H, 0, self.dh.data_ptr(), s)
-        # backward sweep: recompute layer i from its checkpoint, differentiate
         for i in range(L - 1, -1, -1):
             base = self._acquire(i, nxt=i - 1 if i > 0 else None)
             self._layer_fwd(i, base, recompute=True)
             self._layer_bwd(i, base)
             self._release(i)
+
+    def forward_backward(self, ids, targets):
+        """Queue the forward and backward sweeps for token ids / next-token
+        targets (device int64 [batch*seq]); returns at once. The loss lands in
+        self.loss, the logits in self.logits, adapter gradients in self.grads."""
+        M, H, V = self.M, self.H, self.V
+        self._check_ids(ids, targets)
+        self.compute.wait_stream(torch.cuda.current_stream())
+        s = self._s
+        nf4s_embed(self.embed.data_ptr(), V, H, ids.data_ptr(), M, self.h[0].data_ptr(), s)
+        self._forward_sweep(adapters=True)
+        self._head_fwd(self.h[self.L])
+        nf4s_cross_entropy(self.logits.data_ptr(), targets.data_ptr(), M, V, self.loss.data_ptr(),
+                           self.dlogits.data_ptr(), *self._ws(), s)
+        self._backward()
         torch.cuda.current_stream().wait_stream(self.compute)
+
+    def preference_forward_backward(self, ids, targets, mask, beta=0.1, schedule="separate"):
+        """DPO step ("Soup v0.72.4 technical analysis", sections 3.1-3.3): the
+        reference model is the same streamed base with the adapters off, the
+        policy the base with them on; no second model. Rows are 2 * pairs
+        sequences of S tokens ordered chosen, rejected per pair; mask (fp32
+        [batch*seq]) weights the response tokens.
+
+        schedule "separate": a reference forward sweep, then the policy's
+        forward and backward sweeps (three reads of a layer per step, the
+        pages' ~1.5x of the plain step); "fused": the reference forward of a
+        layer runs while the policy's forward holds it (two reads). Both give
+        identical results. Loss in self.loss, policy logits in self.logits,
+        reference log-probabilities in self.nll_ref, gradients in self.grads."""
+        assert schedule in ("separate", "fused")
+        assert self.B % 2 == 0, "sequences come in chosen/rejected pairs"
+        M, H, V, S, L = self.M, self.H, self.V, self.S, self.L
+        self._check_ids(ids, targets)
+        assert mask.numel() == M and mask.dtype == torch.float32
+        self._ensure_preference_buffers(schedule)
+        self.compute.wait_stream(torch.cuda.current_stream())
+        s = self._s
+        nf4s_embed(self.embed.data_ptr(), V, H, ids.data_ptr(), M, self.h[0].data_ptr(), s)
+        if schedule == "separate":
+            # the last reference layer prefetches the policy's first
+            self._forward_sweep(adapters=False, nxt_last=0)
+            self._head_fwd(self.h[L])
+            nf4s_token_nll(self.logits.data_ptr(), targets.data_ptr(), M, V, self.nll_ref.data_ptr(), s)
+            self._forward_sweep(adapters=True)
+        else:
+            href = self.href
+            for i in range(L):
+                base = self._acquire(i, nxt=i + 1 if i + 1 < L else None)
+                self._layer_fwd(i, base, recompute=False, adapters=False,
+                                hin=self.h[0] if i == 0 else href[i % 2], hout=href[(i + 1) % 2])
+                self._layer_fwd(i, base, recompute=False)
+                self._release(i)
+            self._head_fwd(href[L % 2])
+            nf4s_token_nll(self.logits.data_ptr(), targets.data_ptr(), M, V, self.nll_ref.data_ptr(), s)
+        self._head_fwd(self.h[L])
+        nf4s_token_nll(self.logits.data_ptr(), targets.data_ptr(), M, V, self.nll_pol.data_ptr(), s)
+        nf4s_dpo_loss(self.nll_pol.data_ptr(), self.nll_ref.data_ptr(), mask.data_ptr(), self.B // 2, S,
+                      beta, self.loss.data_ptr(), self.seq_coef.data_ptr(), s)
+        nf4s_logit_grad(self.logits.data_ptr(), targets.data_ptr(), self.seq_coef.data_ptr(),
+                        mask.data_ptr(), M, S, V, self.dlogits.data_ptr(), s)
+        self._backward()
+        torch.cuda.current_stream().wait_stream(self.compute)
+
+    def _ensure_preference_buffers(self, schedule):
+        dev = "cuda"
+        if not hasattr(self, "nll_ref"):
+            self.nll_ref = torch.empty(self.M, dtype=torch.float32, device=dev)
+            self.nll_pol = torch.empty(self.M, dtype=torch.float32, device=dev)
+            self.seq_coef = torch.empty(self.B, dtype=torch.float32, device=dev)
+        if schedule == "fused" and not hasattr(self, "href"):
+            # the reference model's residual stream (current and next layer)
+            self.href = [torch.empty((self.M, self.H), dtype=torch.float32, device=dev)
+                         for _ in range(2)]
+
+    def preference_step(self, ids, targets, mask, beta=0.1, schedule="separate"):
+        self.preference_forward_backward(ids, targets, mask, beta, schedule)
+        self.optimizer_step()
 
     def optimizer_step(self):
         """AdamW on every adapter parameter (one launch over the flat buffer)."""

@@ -142,3 +142,18 @@ def token_batch(model: str, batch: int, seq: int, step: int = 0) -> tuple[np.nda
     v = DECODER[model]["vocab"]
     ids = g.integers(0, v, size=(batch, seq + 1), dtype=np.int64)
     return ids[:, :-1].copy(), ids[:, 1:].copy()
+
+
+def preference_batch(model: str, pairs: int, seq: int, prompt: int, step: int = 0):
+    """Chosen/rejected sequences for a preference step: 2 * pairs rows of seq
+    tokens ordered chosen, rejected per pair; the two rows of a pair share
+    their first `prompt` tokens and draw their responses independently.
+    Returns ids, next-token targets [2 * pairs, seq] and the response mask
+    (fp32: 1 where the target is a response token)."""
+    g = _rng(BASE_SEED + 800_000 + step)
+    v = DECODER[model]["vocab"]
+    full = g.integers(0, v, size=(2 * pairs, seq + 1), dtype=np.int64)
+    full[1::2, :prompt] = full[0::2, :prompt]
+    mask = np.zeros((2 * pairs, seq), dtype=np.float32)
+    mask[:, max(prompt - 1, 0):] = 1.0
+    return full[:, :-1].copy(), full[:, 1:].copy(), mask

@@ -486,3 +486,124 @@ def test_135m_loss_curve_streamed_equals_resident(w135):
     c = curves["resident"]
     print("loss curve", c[0], c[-1], flush=True)
     assert c[-1] < c[0], c
+
+
+# ---- preference step (DPO) ----------------------------------------------------------
+
+def test_token_nll_dpo_and_logit_grad_kernels():
+    """The three preference-step kernels against the oracle on shared inputs."""
+    require_gpu()
+    g = _rng(90)
+    pairs, S, V = 3, 37, 1000
+    T = 2 * pairs * S
+    z = _bits(g.standard_normal((T, V)) * 2)
+    tg = g.integers(0, V, size=T)
+    mask = (g.random(T) < 0.7).astype(np.float32)
+    nll_ref = (np.abs(g.standard_normal(T)) * 3).astype(np.float32)
+    zd, md, rd = dev_bf16bits(z), dev_f32(mask), dev_f32(nll_ref)
+    td = torch.from_numpy(tg.astype(np.int64)).to("cuda")
+    nll = torch.empty(T, dtype=torch.float32, device="cuda")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    coef = torch.empty(2 * pairs, dtype=torch.float32, device="cuda")
+    dz = torch.empty_like(zd)
+    L.nf4s_token_nll(zd.data_ptr(), td.data_ptr(), T, V, nll.data_ptr(), stream())
+    L.nf4s_dpo_loss(nll.data_ptr(), rd.data_ptr(), md.data_ptr(), pairs, S, 0.1, loss.data_ptr(),
+                    coef.data_ptr(), stream())
+    L.nf4s_logit_grad(zd.data_ptr(), td.data_ptr(), coef.data_ptr(), md.data_ptr(), T, S, V,
+                      dz.data_ptr(), stream())
+    torch.cuda.synchronize()
+    zv = _vals(z)
+    ref_nll = D.token_nll(zv, tg)
+    _check_f32(nll.cpu().numpy(), ref_nll, what="nll")
+    # the loss and coefficients from the GPU's own nll (the kernel under test is the reduction)
+    gn = nll.cpu().numpy().astype(np.float64)
+    ref_loss, ref_coef = D.dpo_loss(gn, nll_ref.astype(np.float64), mask.astype(np.float64), S, 0.1)
+    assert abs(float(loss.item()) - ref_loss) <= 1e-5 * abs(ref_loss), (float(loss.item()), ref_loss)
+    _check_f32(coef.cpu().numpy(), ref_coef, what="coef")
+    p = np.exp(zv - zv.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    p[np.arange(T), tg] -= 1.0
+    w = np.repeat(coef.cpu().numpy().astype(np.float64), S) * mask
+    _check_bf16(host_u16(dz), D.bf16(p * w[:, None]), abs_slack=1e-4, what="dlogits")
+
+
+def _pref(w, pairs, prompt):
+    ids, tg, mask = synth.preference_batch(w["model"], pairs, w["seq"], prompt)
+    return ids, tg, mask
+
+
+def _run_pref(w, shards, mode, schedule, pairs, prompt, n_slots=2, lora=None):
+    if lora is not None:
+        w = dict(w, lora=lora)
+    dec = _decoder(w, shards, mode, n_slots)
+    ids, tg, mask = _pref(w, pairs, prompt)
+    dec.preference_forward_backward(torch.from_numpy(ids.reshape(-1)).to("cuda"),
+                                    torch.from_numpy(tg.reshape(-1)).to("cuda"),
+                                    dev_f32(mask.reshape(-1)), beta=0.1, schedule=schedule)
+    torch.cuda.synchronize()
+    out = dict(loss=dec.loss.cpu().numpy().copy(), logits=host_u16(dec.logits).copy(),
+               grads=dec.grads.cpu().numpy().copy(), nll_ref=dec.nll_ref.cpu().numpy().copy(),
+               split={k: (a.cpu().numpy().copy(), b.cpu().numpy().copy())
+                      for k, (a, b) in dec.lora_grads.items()},
+               stats=dec.stats())
+    dec.close()
+    return out
+
+
+def test_tiny_dpo_step_matches_oracle():
+    """Reference sweep (adapters off) + policy step on 2 pairs x S70 with a
+    20-token shared prompt, LoRA on all seven, against oracle.dpo_step. Bound
+    as the plain step for logits and gradients; the loss compares differences
+    of 50-token log-probability sums, 5e-3 relative."""
+    require_gpu()
+    w = _world("tiny", 4, 70, targets=PROJ)
+    got = _run_pref(w, _shards(w), "resident", "separate", pairs=2, prompt=20)
+    P = _oracle_params(w)
+    cfg = _oracle_cfg(w)
+    ids, tg, mask = _pref(w, 2, 20)
+    loss, g, logits = D.dpo_step(P, ids, tg, mask, cfg, 0.1)
+    print(f"dpo oracle loss {loss:.6f} gpu {float(got['loss'][0]):.6f}", flush=True)
+    assert abs(float(got["loss"][0]) - loss) <= 5e-3 * abs(loss)
+    gl = _vals(got["logits"]).reshape(logits.shape)
+    assert np.max(np.abs(gl - logits)) / np.max(np.abs(logits)) <= 2e-2
+    for key, (dA, dB) in g["lora"].items():
+        gA, gB = got["split"][key]
+        for a, b in ((gA, dA), (gB, dB)):
+            assert np.max(np.abs(a - b)) / np.max(np.abs(b)) <= 2e-2, key
+
+
+@pytest.fixture(scope="module")
+def pref135(w135):
+    w, shards = w135
+    w = dict(w, batch=4)
+    return w, shards, _run_pref(w, shards, "resident", "separate", pairs=2, prompt=128)
+
+
+@pytest.mark.parametrize("mode,schedule,n_slots", [("streamed", "separate", 2), ("streamed", "fused", 2),
+                                                   ("resident", "fused", 2), ("streamed", "separate", 3)])
+def test_135m_dpo_streamed_equals_resident(pref135, mode, schedule, n_slots):
+    """2 pairs x 512 tokens at 135M shapes: every schedule and pool size gives
+    the resident separate result bit for bit; copies for one step from an
+    empty pool: 3L - n with its own reference sweep, 2L - n fused (the pages'
+    ~1.5x layer reads of a preference step against 1x)."""
+    w, shards, ref = pref135
+    print(f"135m dpo {mode} {schedule} n={n_slots}", flush=True)
+    got = _run_pref(w, shards, mode, schedule, pairs=2, prompt=128, n_slots=n_slots)
+    for k in ("loss", "logits", "grads", "nll_ref"):
+        assert np.array_equal(got[k].view(np.uint8), ref[k].view(np.uint8)), k
+    if mode == "streamed":
+        Ln = w["nl"]
+        expect = (3 * Ln - n_slots) if schedule == "separate" else (2 * Ln - n_slots)
+        assert got["stats"][0] == expect, (got["stats"], expect)
+
+
+def test_135m_dpo_zero_adapters_is_ln2(w135):
+    """B = 0: the policy equals the reference bit for bit, so delta = 0 and the
+    loss is ln 2; dA vanishes and dB does not."""
+    w, shards = w135
+    w = dict(w, batch=4)
+    lora0 = {k: (a, np.zeros_like(b)) for k, (a, b) in w["lora"].items()}
+    got = _run_pref(w, shards, "resident", "separate", pairs=2, prompt=128, lora=lora0)
+    assert abs(float(got["loss"][0]) - math.log(2)) <= 2e-7, got["loss"]     # one fp32 unit
+    for key, (dA, dB) in got["split"].items():
+        assert np.all(dA == 0) and np.any(dB != 0), key

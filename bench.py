@@ -58,12 +58,13 @@ def flops_per_token(model: str, lm_head: bool, reference: bool = False) -> int:
     2 recompute, 2 dL/dx; no dL/dW for a frozen base) plus, with the resident
     lm_head, 4 per lm_head parameter (2 forward, 2 dL/dx); the embedding
     lookup counts 0. Convention of the gate walkthrough, section 4.4. A
-    preference step adds the reference forward: 8 per parameter."""
+    preference step adds the reference forward: 8 per decoder-linear and 6 per
+    lm_head parameter."""
     per_layer = sum(a * b for a, b in synth.SHAPES[model].values())
     f = (8 if reference else 6) * per_layer * synth.N_LAYERS[model]
     if lm_head:
         v, h = LM_HEAD[model]
-        f += 4 * v * h
+        f += (6 if reference else 4) * v * h
     return f
 
 
@@ -182,12 +183,16 @@ def _cpu_baseline(model: str, M: int, targets) -> dict:
                       f"dequantise + fp64 forward/backward in {dt:.2f} s, scaled x{n_layers} layers"}
 
 
-def _cpu_baseline_decoder(model: str, batch: int, seq: int, targets) -> dict:
+def _cpu_baseline_decoder(model: str, batch: int, seq: int, targets, preference=None) -> dict:
     """The decoder oracle, as it stands, on a bounded sample of the same step:
     the fp64 forward and backward of the head alone (embedding, final norm,
     lm_head, cross-entropy; no layer) and of one full layer plus the head,
     both timed, and the dequantisation of the layer's q tensor, timed and
     scaled to the layer's parameters. The step is the head plus L layers.
+    A preference step (oracle.decoder.dpo_step: reference forward, policy
+    forward and backward) is sampled on one pair of 128-token sequences and
+    scaled to the step's tokens (the sample's work is linear in tokens but
+    for the attention, which is small at these lengths).
     The oracle caches activations
     instead of recomputing; weight values do not change its time, so the
     sample uses the seeded fp32 weights and one table for embedding and
@@ -212,25 +217,37 @@ def _cpu_baseline_decoder(model: str, batch: int, seq: int, targets) -> dict:
     W = [{p: synth.weight(0, p, *sh[p]).astype(np.float64) for p in odec.PROJ}]
     E = synth.bf16_bits_to_f32(synth.embedding_bits(model)).astype(np.float64)
     lora = [{p: tuple(a.astype(np.float64) for a in synth.lora_pair(0, p, *sh[p])) for p in targets}]
-    ids, tg = synth.token_batch(model, batch, seq)
     norm = lambda w: synth.norm_weight(model, 0, w).astype(np.float64)  # noqa: E731
+    if preference:
+        s_seq = min(seq, 128)
+        ids, tg, mask = synth.preference_batch(model, 1, s_seq, s_seq // 4)
+        scale_tokens = (batch * seq) / ids.size
+    else:
+        ids, tg = synth.token_batch(model, batch, seq)
+        scale_tokens = 1.0
+
     def timed(layers):
         cfg = odec.Config(**{**c, "layers": layers}, targets=tuple(targets))
         P = odec.Params(embed=E, lm_head=E, w_attn=[norm("attn")] * layers,
                         w_mlp=[norm("mlp")] * layers, w_final=norm("final"), W=W[:layers],
                         lora=lora[:layers])
         t0 = time.perf_counter()
-        _, _, cache = odec.forward(P, ids, tg, cfg)
-        odec.backward(P, cache, cfg)
-        return time.perf_counter() - t0
+        if preference:
+            odec.dpo_step(P, ids, tg, mask, cfg, 0.1)
+        else:
+            _, _, cache = odec.forward(P, ids, tg, cfg)
+            odec.backward(P, cache, cfg)
+        return (time.perf_counter() - t0) * scale_tokens
 
     t_head = timed(0)
     t_one = timed(1)
     t_layer = t_one - t_head + t_deq
     t_step = t_head + n_layers * t_layer
     M = batch * seq
+    what = (f"DPO step sampled on 1 pair x {ids.shape[1]} tokens, scaled x{scale_tokens:g} to "
+            f"B{batch} S{seq}" if preference else f"B{batch} S{seq}")
     return {"value": M / t_step, "unit": "tok/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{model} decoder at B{batch} S{seq} (LoRA {'/'.join(targets)}), fp64 "
+            "sample": f"{model} decoder, {what} (LoRA {'/'.join(targets)}), fp64 "
                       f"forward + backward: head alone {t_head:.2f} s, one layer + head "
                       f"{t_one:.2f} s; layer dequantisation {t_deq:.2f} s (scaled from q); "
                       f"step = head + {n_layers} x layer = {t_step:.1f} s"}
@@ -436,7 +453,7 @@ def main():
         st.close()
         return dt, (b1 - b0) / args.steps, (c1 - c0) / args.steps, durs
 
-    use_decoder = model in synth.DECODER and reference is None and not args.no_decoder
+    use_decoder = model in synth.DECODER and not args.no_decoder
     # the linear stack: the streamed projections alone
     lin_s = lin_r = None
     lin_copies, lin_durs = 0, []
@@ -466,38 +483,57 @@ def main():
                  for w in ("attn", "mlp")}
         norms["final"] = torch.from_numpy(synth.norm_weight(model, 0, "final")).to(dev)
         lora_map = {(i, p): lora[i][p] for i in range(n_layers) for p in targets}
-        ids_np, tg_np = synth.token_batch(model, batch, seq)
+        if reference:
+            # preference pairs: 2 pairs x (chosen, rejected), a shared 128-token prompt
+            ids_np, tg_np, mask_np = synth.preference_batch(model, batch // 2, seq, 128)
+            mask = torch.from_numpy(mask_np.reshape(-1)).to(dev)
+        else:
+            ids_np, tg_np = synth.token_batch(model, batch, seq)
         ids = torch.from_numpy(ids_np.reshape(-1)).to(dev)
         tgs = torch.from_numpy(tg_np.reshape(-1)).to(dev)
+
+        def one_step(d):
+            if reference:
+                d.preference_step(ids, tgs, mask, beta=0.1, schedule=reference)
+            else:
+                d.step(ids, tgs)
 
         def run_dec(mode, n_slots, timed):
             d = Decoder(c, shards, embed, head, norms, lora_map, batch, seq, targets=targets,
                         n_slots=n_slots, mode=mode, time_calls=plain_fwd if timed else None)
-            for _ in range(args.warmup):
-                d.step(ids, tgs)
+            first = None
+            for w_ in range(args.warmup):
+                one_step(d)
+                if w_ == 0:
+                    first = d.loss.clone()   # before any optimiser update
             torch.cuda.synchronize()
             d.timed.clear()
             c0, b0 = d.stats()
             t = time.perf_counter()
-            for _ in range(args.steps):
-                d.step(ids, tgs)
+            for k_ in range(args.steps):
+                one_step(d)
+                if first is None:            # no warm-up: the first timed step's loss
+                    first = d.loss.clone()
             torch.cuda.synchronize()
             dt = (time.perf_counter() - t) / args.steps
             c1, b1 = d.stats()
             durs = [(n, k, s_.elapsed_time(e_)) for (_, n, k, s_, e_) in d.timed]
-            loss = float(d.loss.item())
+            loss = (float(first.item()), float(d.loss.item()))
             d.close()
             return dt, (b1 - b0) / args.steps, (c1 - c0) / args.steps, durs, loss
 
         dt_s, h2d_bytes, copies, durs, loss_s = run_dec("streamed", slots, True)
         print(f"[bench] decoder streamed: {dt_s * 1e3:.1f} ms/step, {copies:.0f} copies/step, "
-              f"loss {loss_s:.4f}", file=sys.stderr, flush=True)
+              f"loss first/last step {loss_s[0]:.6f} / {loss_s[1]:.6f}", file=sys.stderr, flush=True)
         dt_r, loss_r = None, None
         if not args.no_resident:
             dt_r, _, _, _, loss_r = run_dec("resident", slots, False)
-            print(f"[bench] decoder resident: {dt_r * 1e3:.1f} ms/step, loss {loss_r:.4f}",
-                  file=sys.stderr, flush=True)
-        dec = dict(loss_streamed=loss_s, loss_resident=loss_r)
+            print(f"[bench] decoder resident: {dt_r * 1e3:.1f} ms/step, loss first/last step "
+                  f"{loss_r[0]:.6f} / {loss_r[1]:.6f}", file=sys.stderr, flush=True)
+        dec = dict(loss_first_step=loss_s[0], loss_last_step_streamed=loss_s[1],
+                   loss_last_step_resident=None if loss_r is None else loss_r[1],
+                   losses_identical=None if loss_r is None else loss_s == loss_r,
+                   steps_taken=args.warmup + args.steps)
     else:
         dt_s, h2d_bytes, copies, durs, dt_r = lin_s, lin_h2d, lin_copies, lin_durs, lin_r
 
@@ -554,7 +590,10 @@ def main():
                     f"{c['heads']} heads / {c['kv_heads']} KV heads, vocab {V}); the seven "
                     f"projections per layer streamed from pinned host as NF4 shards, embedding "
                     f"and lm_head resident bf16, checkpointed layers recomputed in the backward, "
-                    f"AdamW on the adapters")
+                    f"AdamW on the adapters"
+                    + (f"; DPO preference step on {batch // 2} chosen/rejected pairs, reference "
+                       f"model = the same shards with adapters off ({reference} sweep)"
+                       if reference else ""))
     else:
         workload = (f"linear stack: {n_layers} layers of {model} projection shapes "
                     f"(q,k,v,o,gate,up,down), streamed from pinned host, recompute in backward"
@@ -606,8 +645,8 @@ def main():
             "flop_per_token": f_lin, "copies_per_step": lin_copies}
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = (_cpu_baseline_decoder(model, batch, seq, targets) if use_decoder
-                               else _cpu_baseline(model, M, targets))
+        out["cpu_baseline"] = (_cpu_baseline_decoder(model, batch, seq, targets, reference)
+                               if use_decoder else _cpu_baseline(model, M, targets))
     print(json.dumps(out), flush=True)
 
 

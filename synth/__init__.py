@@ -109,6 +109,10 @@ DECODER = {
                  rope_theta=100000.0, eps=1e-5, tied=True),
     "8b": dict(hidden=4096, inter=14336, heads=32, kv_heads=8, head_dim=128, vocab=128256, layers=32,
                rope_theta=500000.0, eps=1e-5, tied=False),
+    # 32B class (the shapes of the 32B layers above; llama definitions, no
+    # projection biases)
+    "32b": dict(hidden=5120, inter=27648, heads=40, kv_heads=8, head_dim=128, vocab=152064, layers=64,
+                rope_theta=1000000.0, eps=1e-6, tied=False),
 }
 SHAPES["tiny"] = _shapes(128, 256, 4, 32, 2)
 N_LAYERS["tiny"] = 2

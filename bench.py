@@ -517,7 +517,8 @@ def main():
             torch.cuda.synchronize()
             dt = (time.perf_counter() - t) / args.steps
             c1, b1 = d.stats()
-            durs = [(n, k, s_.elapsed_time(e_)) for (_, n, k, s_, e_) in d.timed]
+            durs = [(n, k, s_.elapsed_time(e_) / cnt) for (_, n, k, s_, e_, cnt) in d.timed
+                    for _ in range(cnt)]
             loss = (float(first.item()), float(d.loss.item()))
             d.close()
             return dt, (b1 - b0) / args.steps, (c1 - c0) / args.steps, durs, loss

@@ -262,34 +262,64 @@ __device__ __forceinline__ void split8(const float* x, bf16x8_t& hi, bf16x8_t& l
 // Row offset of result register r in its 32x32 tile for lane half hf.
 __device__ __forceinline__ int crow(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 
-// Stage rows [r0, r0 + 32) (clamped to the sequence) of a [rows, ld] bf16
-// matrix, columns [c0, c0 + D), into LDS: row-major `rm` (row stride D + 8)
-// and/or transposed `tr` (tr[d * TS + row], row stride TS = 36). Each lane
-// moves four rows x 8 columns per item: four 16-byte loads, four 16-byte
-// row-major stores and eight 8-byte transposed stores.
+// A 32-row block of a [rows, ld] bf16 matrix (rows r0 .. r0 + 31 of one
+// sequence, clamped to it; columns c0 .. c0 + D) in the registers of one wave:
+// item it = lane + 64 x covers rows 4(it / (D/8)) .. +4 and columns 8(it % (D/8))
+// .. +8, as four 16-byte loads. Loading a block one step ahead of its use
+// hides the memory latency behind the current block's products.
 template <int D>
-__device__ __forceinline__ void stage_block(const uint16_t* __restrict__ src, int64_t ld, int64_t c0,
-                                            int64_t base_row, int64_t r0, int64_t S, uint16_t* rm,
-                                            uint16_t* tr, int lane) {
-  constexpr int RS = D + 8, TS = 36, CH = D / 8;
-  for (int it = lane; it < 8 * CH; it += 64) {
-    const int rg = it / CH, ch = it % CH;  // rows 4rg..4rg+3, columns 8ch..8ch+7
-    u32x4_t v[4];
+struct BlockRegs {
+  static constexpr int ITEMS = 8 * (D / 8);           // 4-row x 8-column items per block
+  static constexpr int PER_LANE = (ITEMS + 63) / 64;
+  u32x4_t v[PER_LANE][4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_block(const uint16_t* __restrict__ src, int64_t ld, int64_t c0,
+                                           int64_t base_row, int64_t r0, int64_t S, int lane,
+                                           BlockRegs<D>& br) {
+  constexpr int CH = D / 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t rr = r0 + 4 * rg + i;
-      const int64_t row = base_row + (rr < S ? rr : S - 1);
-      v[i] = *reinterpret_cast<const u32x4_t*>(src + row * ld + c0 + 8 * ch);
-      if (rm != nullptr) *reinterpret_cast<u32x4_t*>(rm + (4 * rg + i) * RS + 8 * ch) = v[i];
+  for (int x = 0; x < BlockRegs<D>::PER_LANE; ++x) {
+    const int it = lane + 64 * x;
+    if (it < BlockRegs<D>::ITEMS) {
+      const int rg = it / CH, ch = it % CH;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t rr = r0 + 4 * rg + i;
+        const int64_t row = base_row + (rr < S ? rr : S - 1);
+        br.v[x][i] = *reinterpret_cast<const u32x4_t*>(src + row * ld + c0 + 8 * ch);
+      }
     }
-    if (tr != nullptr) {
+  }
+}
+
+// The block into LDS: row-major `rm` (row stride D + 8) and/or transposed
+// `tr` (tr[d * 36 + row]); 16-byte row-major stores, 8-byte transposed stores
+// of four consecutive rows.
+template <int D>
+__device__ __forceinline__ void store_block(const BlockRegs<D>& br, uint16_t* rm, uint16_t* tr,
+                                            int lane) {
+  constexpr int RS = D + 8, TS = 36, CH = D / 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        uint2 w;
-        w.x = ((v[0][e >> 1] >> sh) & 0xFFFFu) | (((v[1][e >> 1] >> sh) & 0xFFFFu) << 16);
-        w.y = ((v[2][e >> 1] >> sh) & 0xFFFFu) | (((v[3][e >> 1] >> sh) & 0xFFFFu) << 16);
-        *reinterpret_cast<uint2*>(tr + (8 * ch + e) * TS + 4 * rg) = w;
+  for (int x = 0; x < BlockRegs<D>::PER_LANE; ++x) {
+    const int it = lane + 64 * x;
+    if (it < BlockRegs<D>::ITEMS) {
+      const int rg = it / CH, ch = it % CH;
+      if (rm != nullptr) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<u32x4_t*>(rm + (4 * rg + i) * RS + 8 * ch) = br.v[x][i];
+      }
+      if (tr != nullptr) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int sh = (e & 1) * 16;
+          uint2 w;
+          w.x = ((br.v[x][0][e >> 1] >> sh) & 0xFFFFu) | (((br.v[x][1][e >> 1] >> sh) & 0xFFFFu) << 16);
+          w.y = ((br.v[x][2][e >> 1] >> sh) & 0xFFFFu) | (((br.v[x][3][e >> 1] >> sh) & 0xFFFFu) << 16);
+          *reinterpret_cast<uint2*>(tr + (8 * ch + e) * TS + 4 * rg) = w;
+        }
       }
     }
   }
@@ -324,17 +354,35 @@ __device__ __forceinline__ void row_frags(const uint16_t* __restrict__ rowp, int
   for (int kk = 0; kk < D / 16; ++kk) f[kk] = *reinterpret_cast<const bf16x8_t*>(rowp + 16 * kk + 8 * hf);
 }
 
+// Work split: a workgroup of AW waves owns one 32-row block; wave w walks the
+// other side's blocks w, w + AW, ... of the causal range with its own LDS
+// tiles (no workgroup barrier inside the walk), and the waves' partial results
+// are combined through LDS in wave order at the end.
+constexpr int AW = 4;
+constexpr int RM_ELEMS(int D) { return AB * (D + 8); }
+constexpr int TR_ELEMS(int D) { return D * 36; }
+
+// Per-lane partial results of the AW waves go through LDS lane-major:
+// part[((w * 64 + lane) * NV) + i].
+template <int NV>
+__device__ __forceinline__ void park(float* part, int wave, int lane, const float* v) {
+#pragma unroll
+  for (int i = 0; i < NV; i += 4)
+    *reinterpret_cast<float4*>(part + (wave * 64 + lane) * NV + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+}
+
 template <int D>
-__global__ __launch_bounds__(64) void k_attn_fwd(const uint16_t* __restrict__ q,
-                                                 const uint16_t* __restrict__ k,
-                                                 const uint16_t* __restrict__ v, int64_t S, int H,
-                                                 int Hkv, uint16_t* __restrict__ o,
-                                                 float* __restrict__ o_f32,
-                                                 float* __restrict__ lse) {
-  constexpr int KS = D / 16, DT = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[AB * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * 36];
-  const int lane = threadIdx.x, hf = lane >> 5, c = lane & 31;
+__global__ __launch_bounds__(64 * AW, 1) void k_attn_fwd(const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ v, int64_t S,
+                                                         int H, int Hkv, uint16_t* __restrict__ o,
+                                                         float* __restrict__ o_f32,
+                                                         float* __restrict__ lse) {
+  constexpr int KS = D / 16, DT = D / 32, WS = RM_ELEMS(D) + TR_ELEMS(D);
+  __shared__ __attribute__((aligned(16))) uint16_t smem[AW * WS];
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, hf = lane >> 5, c = lane & 31;
+  uint16_t* const Ks = smem + wave * WS;
+  uint16_t* const Vt = Ks + RM_ELEMS(D);
   const int64_t nqb = (S + AB - 1) / AB;
   const int64_t b = blockIdx.x / (H * nqb);
   const int h = (int)((blockIdx.x / nqb) % H);
@@ -346,15 +394,24 @@ __global__ __launch_bounds__(64) void k_attn_fwd(const uint16_t* __restrict__ q,
   const float scale = 1.0f / sqrtf((float)D);
   bf16x8_t qf[KS];
   row_frags<D>(q + qrow * ldq + (int64_t)h * D, hf, qf);
-  f32x16_t acc[DT];
+  float acc[DT][16];
 #pragma unroll
-  for (int j = 0; j < DT; ++j) acc[j] = zero16();
+  for (int j = 0; j < DT; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
   float m = -INFINITY, lsum = 0.0f;
-  for (int64_t kb = 0; kb <= qb; ++kb) {
-    __syncthreads();
-    stage_block<D>(k, ldk, (int64_t)g * D, b * S, kb * AB, S, Ks, nullptr, lane);
-    stage_block<D>(v, ldk, (int64_t)g * D, b * S, kb * AB, S, nullptr, Vt, lane);
-    __syncthreads();
+  BlockRegs<D> rk, rv;
+  if (wave <= qb) {
+    load_block<D>(k, ldk, (int64_t)g * D, b * S, wave * AB, S, lane, rk);
+    load_block<D>(v, ldk, (int64_t)g * D, b * S, wave * AB, S, lane, rv);
+  }
+  for (int64_t kb = wave; kb <= qb; kb += AW) {
+    store_block<D>(rk, Ks, nullptr, lane);
+    store_block<D>(rv, nullptr, Vt, lane);
+    if (kb + AW <= qb) {
+      load_block<D>(k, ldk, (int64_t)g * D, b * S, (kb + AW) * AB, S, lane, rk);
+      load_block<D>(v, ldk, (int64_t)g * D, b * S, (kb + AW) * AB, S, lane, rv);
+    }
     f32x16_t st = zero16();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) st = mfma32(frag_rm<D>(Ks, c, hf, kk), qf[kk], st);
@@ -378,59 +435,86 @@ __global__ __launch_bounds__(64) void k_attn_fwd(const uint16_t* __restrict__ q,
     lsum = lsum * corr + ps;
     m = mn;
 #pragma unroll
-    for (int j = 0; j < DT; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][r] *= corr;
-#pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       bf16x8_t ph, pl;
       split8(p + 8 * kk, ph, pl);
 #pragma unroll
       for (int j = 0; j < DT; ++j) {
+        f32x16_t a;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[r] = kk == 0 ? acc[j][r] * corr : acc[j][r];
         const bf16x8_t va = frag_tr(Vt, 32 * j + c, hf, kk);
-        acc[j] = mfma32(va, ph, acc[j]);
-        acc[j] = mfma32(va, pl, acc[j]);
+        a = mfma32(va, ph, a);
+        a = mfma32(va, pl, a);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] = a[r];
       }
     }
   }
+  // combine the waves: O = sum_w O_w e^(m_w - m) / sum_w l_w e^(m_w - m)
+  __syncthreads();
+  float* part = reinterpret_cast<float*>(smem);          // [AW][64][DT * 16]
+  float* ml = part + AW * 64 * DT * 16;                  // [AW][64][2]
+  park<DT * 16>(part, wave, lane, &acc[0][0]);
+  ml[(wave * 64 + lane) * 2] = m;
+  ml[(wave * 64 + lane) * 2 + 1] = lsum;
+  __syncthreads();
+  if (wave >= DT) return;  // wave w combines output tile j = w
+  float mw[AW], mx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < AW; ++w) {
+    mw[w] = ml[(w * 64 + lane) * 2];
+    mx = fmaxf(mx, mw[w]);
+  }
+  float ltot = 0.0f, f[AW];
+#pragma unroll
+  for (int w = 0; w < AW; ++w) {
+    f[w] = __expf(mw[w] - mx);
+    ltot += ml[(w * 64 + lane) * 2 + 1] * f[w];
+  }
   if (qpos >= S) return;
-  const float inv = 1.0f / lsum;
+  const int j = wave;
+  const float inv = 1.0f / ltot;
 #pragma unroll
-  for (int j = 0; j < DT; ++j)
+  for (int rq = 0; rq < 4; ++rq) {
+    float4 fo;
+    float* fv = &fo.x;
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int d0 = 32 * j + 8 * rq + 4 * hf;
-      const int64_t idx = qrow * ldq + (int64_t)h * D + d0;
-      float4 f;
-      f.x = acc[j][4 * rq] * inv;
-      f.y = acc[j][4 * rq + 1] * inv;
-      f.z = acc[j][4 * rq + 2] * inv;
-      f.w = acc[j][4 * rq + 3] * inv;
-      uint2 w;
-      w.x = pack_bf16x2(f.x, f.y);
-      w.y = pack_bf16x2(f.z, f.w);
-      *reinterpret_cast<uint2*>(o + idx) = w;
-      if (o_f32 != nullptr) *reinterpret_cast<float4*>(o_f32 + idx) = f;
+    for (int e = 0; e < 4; ++e) {
+      float sacc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < AW; ++w) sacc += part[(w * 64 + lane) * DT * 16 + j * 16 + 4 * rq + e] * f[w];
+      fv[e] = sacc * inv;
     }
-  if (hf == 0) lse[(b * H + h) * S + qpos] = m + logf(lsum);
+    const int d0 = 32 * j + 8 * rq + 4 * hf;
+    const int64_t idx = qrow * ldq + (int64_t)h * D + d0;
+    uint2 wv;
+    wv.x = pack_bf16x2(fo.x, fo.y);
+    wv.y = pack_bf16x2(fo.z, fo.w);
+    *reinterpret_cast<uint2*>(o + idx) = wv;
+    if (o_f32 != nullptr) *reinterpret_cast<float4*>(o_f32 + idx) = fo;
+  }
+  if (j == 0 && hf == 0) lse[(b * H + h) * S + qpos] = mx + logf(ltot);
 }
 
-// dQ of a 32-query block of one head; also writes Dsum = dO . O (fp32) of
+// dQ of a 32-query block of one head (the key blocks split over AW waves,
+// the partial dQ summed in wave order); also writes Dsum = dO . O (fp32) of
 // its queries for the key-side kernel.
 template <int D>
-__global__ __launch_bounds__(64) void k_attn_dq(const uint16_t* __restrict__ q,
-                                                const uint16_t* __restrict__ k,
-                                                const uint16_t* __restrict__ v,
-                                                const float* __restrict__ o_f32,
-                                                const uint16_t* __restrict__ dout,
-                                                const float* __restrict__ lse, int64_t S, int H,
-                                                int Hkv, float* __restrict__ dsum,
-                                                uint16_t* __restrict__ dq) {
-  constexpr int KS = D / 16, DT = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[AB * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[AB * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * 36];
-  const int lane = threadIdx.x, hf = lane >> 5, c = lane & 31;
+__global__ __launch_bounds__(64 * AW, 1) void k_attn_dq(const uint16_t* __restrict__ q,
+                                                        const uint16_t* __restrict__ k,
+                                                        const uint16_t* __restrict__ v,
+                                                        const float* __restrict__ o_f32,
+                                                        const uint16_t* __restrict__ dout,
+                                                        const float* __restrict__ lse, int64_t S,
+                                                        int H, int Hkv, float* __restrict__ dsum,
+                                                        uint16_t* __restrict__ dq) {
+  constexpr int KS = D / 16, DT = D / 32, WS = 2 * RM_ELEMS(D) + TR_ELEMS(D);
+  __shared__ __attribute__((aligned(16))) uint16_t smem[AW * WS];
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, hf = lane >> 5, c = lane & 31;
+  uint16_t* const Ks = smem + wave * WS;
+  uint16_t* const Vs = Ks + RM_ELEMS(D);
+  uint16_t* const Kt = Vs + RM_ELEMS(D);
   const int64_t nqb = (S + AB - 1) / AB;
   const int64_t b = blockIdx.x / (H * nqb);
   const int h = (int)((blockIdx.x / nqb) % H);
@@ -458,16 +542,25 @@ __global__ __launch_bounds__(64) void k_attn_dq(const uint16_t* __restrict__ q,
     }
     di += __shfl_xor(di, 32);
   }
-  if (hf == 0 && qpos < S) dsum[qrow * H + h] = di;
+  if (wave == 0 && hf == 0 && qpos < S) dsum[qrow * H + h] = di;
   const float L = lse[(b * H + h) * S + (qpos < S ? qpos : S - 1)];
-  f32x16_t acc[DT];
+  float acc[DT][16];
 #pragma unroll
-  for (int j = 0; j < DT; ++j) acc[j] = zero16();
-  for (int64_t kb = 0; kb <= qb; ++kb) {
-    __syncthreads();
-    stage_block<D>(k, ldk, (int64_t)g * D, b * S, kb * AB, S, Ks, Kt, lane);
-    stage_block<D>(v, ldk, (int64_t)g * D, b * S, kb * AB, S, Vs, nullptr, lane);
-    __syncthreads();
+  for (int j = 0; j < DT; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+  BlockRegs<D> rk, rv;
+  if (wave <= qb) {
+    load_block<D>(k, ldk, (int64_t)g * D, b * S, wave * AB, S, lane, rk);
+    load_block<D>(v, ldk, (int64_t)g * D, b * S, wave * AB, S, lane, rv);
+  }
+  for (int64_t kb = wave; kb <= qb; kb += AW) {
+    store_block<D>(rk, Ks, Kt, lane);
+    store_block<D>(rv, Vs, nullptr, lane);
+    if (kb + AW <= qb) {
+      load_block<D>(k, ldk, (int64_t)g * D, b * S, (kb + AW) * AB, S, lane, rk);
+      load_block<D>(v, ldk, (int64_t)g * D, b * S, (kb + AW) * AB, S, lane, rv);
+    }
     f32x16_t st = zero16(), dp = zero16();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -487,43 +580,63 @@ __global__ __launch_bounds__(64) void k_attn_dq(const uint16_t* __restrict__ q,
       split8(ds + 8 * kk, sh, sl);
 #pragma unroll
       for (int j = 0; j < DT; ++j) {
+        f32x16_t a;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[r] = acc[j][r];
         const bf16x8_t ka = frag_tr(Kt, 32 * j + c, hf, kk);
-        acc[j] = mfma32(ka, sh, acc[j]);
-        acc[j] = mfma32(ka, sl, acc[j]);
+        a = mfma32(ka, sh, a);
+        a = mfma32(ka, sl, a);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] = a[r];
       }
     }
   }
-  if (qpos >= S) return;
+  __syncthreads();
+  float* part = reinterpret_cast<float*>(smem);  // [AW][64][DT * 16]
+  park<DT * 16>(part, wave, lane, &acc[0][0]);
+  __syncthreads();
+  if (wave >= DT || qpos >= S) return;
+  const int j = wave;
 #pragma unroll
-  for (int j = 0; j < DT; ++j)
+  for (int rq = 0; rq < 4; ++rq) {
+    float sv[4];
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int d0 = 32 * j + 8 * rq + 4 * hf;
-      uint2 w;
-      w.x = pack_bf16x2(acc[j][4 * rq], acc[j][4 * rq + 1]);
-      w.y = pack_bf16x2(acc[j][4 * rq + 2], acc[j][4 * rq + 3]);
-      *reinterpret_cast<uint2*>(dq + qrow * ldq + (int64_t)h * D + d0) = w;
+    for (int e = 0; e < 4; ++e) {
+      float sacc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < AW; ++w) sacc += part[(w * 64 + lane) * DT * 16 + j * 16 + 4 * rq + e];
+      sv[e] = sacc;
     }
+    const int d0 = 32 * j + 8 * rq + 4 * hf;
+    uint2 wv;
+    wv.x = pack_bf16x2(sv[0], sv[1]);
+    wv.y = pack_bf16x2(sv[2], sv[3]);
+    *reinterpret_cast<uint2*>(dq + qrow * ldq + (int64_t)h * D + d0) = wv;
+  }
 }
 
-// dK, dV of a 32-key block for one query head (fp32 partials per head; the
-// heads of a KV group are summed afterwards in head order).
+// dK, dV of a 32-key block for one query head (the query blocks split over AW
+// waves and summed in wave order; fp32 partials per head, the heads of a KV
+// group summed afterwards in head order).
 template <int D>
-__global__ __launch_bounds__(64) void k_attn_dkv(const uint16_t* __restrict__ q,
-                                                 const uint16_t* __restrict__ k,
-                                                 const uint16_t* __restrict__ v,
-                                                 const uint16_t* __restrict__ dout,
-                                                 const float* __restrict__ lse,
-                                                 const float* __restrict__ dsum, int64_t S, int H,
-                                                 int Hkv, float* __restrict__ pk,
-                                                 float* __restrict__ pv) {
+__global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ v,
+                                                         const uint16_t* __restrict__ dout,
+                                                         const float* __restrict__ lse,
+                                                         const float* __restrict__ dsum, int64_t S,
+                                                         int H, int Hkv, float* __restrict__ pk,
+                                                         float* __restrict__ pv) {
   constexpr int KS = D / 16, DT = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[AB * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t Os[AB * (D + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * 36];
-  __shared__ __attribute__((aligned(16))) uint16_t Ot[D * 36];
-  __shared__ float Ls[AB], Dl[AB];
-  const int lane = threadIdx.x, hf = lane >> 5, c = lane & 31;
+  constexpr int WS = 2 * RM_ELEMS(D) + 2 * TR_ELEMS(D) + 4 * AB;  // + lse and Dsum (fp32) of the block
+  __shared__ __attribute__((aligned(16))) uint16_t smem[AW * WS];
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, hf = lane >> 5, c = lane & 31;
+  uint16_t* const Qs = smem + wave * WS;
+  uint16_t* const Os = Qs + RM_ELEMS(D);
+  uint16_t* const Qt = Os + RM_ELEMS(D);
+  uint16_t* const Ot = Qt + TR_ELEMS(D);
+  float* const Ls = reinterpret_cast<float*>(Ot + TR_ELEMS(D));
+  float* const Dl = Ls + AB;
   const int64_t nkb = (S + AB - 1) / AB;
   const int64_t b = blockIdx.x / (H * nkb);
   const int h = (int)((blockIdx.x / nkb) % H);
@@ -536,23 +649,33 @@ __global__ __launch_bounds__(64) void k_attn_dkv(const uint16_t* __restrict__ q,
   bf16x8_t kf[KS], vf[KS];
   row_frags<D>(k + krow * ldk + (int64_t)g * D, hf, kf);
   row_frags<D>(v + krow * ldk + (int64_t)g * D, hf, vf);
-  f32x16_t adk[DT], adv[DT];
+  float adk[DT][16], adv[DT][16];
 #pragma unroll
-  for (int j = 0; j < DT; ++j) {
-    adk[j] = zero16();
-    adv[j] = zero16();
+  for (int j = 0; j < DT; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      adk[j][r] = 0.0f;
+      adv[j][r] = 0.0f;
+    }
+  BlockRegs<D> rq, ro;
+  const int64_t q0 = kb + wave;
+  if (q0 < nkb) {
+    load_block<D>(q, ldq, (int64_t)h * D, b * S, q0 * AB, S, lane, rq);
+    load_block<D>(dout, ldq, (int64_t)h * D, b * S, q0 * AB, S, lane, ro);
   }
-  for (int64_t qb = kb; qb < nkb; ++qb) {
-    __syncthreads();
-    stage_block<D>(q, ldq, (int64_t)h * D, b * S, qb * AB, S, Qs, Qt, lane);
-    stage_block<D>(dout, ldq, (int64_t)h * D, b * S, qb * AB, S, Os, Ot, lane);
+  for (int64_t qb = q0; qb < nkb; qb += AW) {
+    store_block<D>(rq, Qs, Qt, lane);
+    store_block<D>(ro, Os, Ot, lane);
     if (lane < AB) {
       const int64_t qp = qb * AB + lane;
       const int64_t qc = qp < S ? qp : S - 1;
       Ls[lane] = lse[(b * H + h) * S + qc];
       Dl[lane] = dsum[(b * S + qc) * H + h];
     }
-    __syncthreads();
+    if (qb + AW < nkb) {
+      load_block<D>(q, ldq, (int64_t)h * D, b * S, (qb + AW) * AB, S, lane, rq);
+      load_block<D>(dout, ldq, (int64_t)h * D, b * S, (qb + AW) * AB, S, lane, ro);
+    }
     f32x16_t st = zero16(), dp = zero16();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -575,27 +698,62 @@ __global__ __launch_bounds__(64) void k_attn_dkv(const uint16_t* __restrict__ q,
       split8(ds + 8 * kk, sh, sl);
 #pragma unroll
       for (int j = 0; j < DT; ++j) {
+        f32x16_t a, bq;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          a[r] = adv[j][r];
+          bq[r] = adk[j][r];
+        }
         const bf16x8_t oa = frag_tr(Ot, 32 * j + c, hf, kk);
-        adv[j] = mfma32(oa, ph, adv[j]);
-        adv[j] = mfma32(oa, pl, adv[j]);
+        a = mfma32(oa, ph, a);
+        a = mfma32(oa, pl, a);
         const bf16x8_t qa = frag_tr(Qt, 32 * j + c, hf, kk);
-        adk[j] = mfma32(qa, sh, adk[j]);
-        adk[j] = mfma32(qa, sl, adk[j]);
+        bq = mfma32(qa, sh, bq);
+        bq = mfma32(qa, sl, bq);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          adv[j][r] = a[r];
+          adk[j][r] = bq[r];
+        }
       }
     }
   }
-  if (kpos >= S) return;
+  __syncthreads();
+  float* part = reinterpret_cast<float*>(smem);  // [AW][64][2 * DT * 16]
+  {
+    float both[2 * DT * 16];
+#pragma unroll
+    for (int j = 0; j < DT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        both[j * 16 + r] = adk[j][r];
+        both[DT * 16 + j * 16 + r] = adv[j][r];
+      }
+    park<2 * DT * 16>(part, wave, lane, both);
+  }
+  __syncthreads();
+  if (wave >= DT || kpos >= S) return;
+  const int j = wave;
   const int64_t prow = (krow * H + h) * D;
 #pragma unroll
-  for (int j = 0; j < DT; ++j)
+  for (int rq2 = 0; rq2 < 4; ++rq2) {
+    float sk[4], sv[4];
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int d0 = 32 * j + 8 * rq + 4 * hf;
-      *reinterpret_cast<float4*>(pk + prow + d0) =
-          make_float4(adk[j][4 * rq], adk[j][4 * rq + 1], adk[j][4 * rq + 2], adk[j][4 * rq + 3]);
-      *reinterpret_cast<float4*>(pv + prow + d0) =
-          make_float4(adv[j][4 * rq], adv[j][4 * rq + 1], adv[j][4 * rq + 2], adv[j][4 * rq + 3]);
+    for (int e = 0; e < 4; ++e) {
+      float a = 0.0f, bsum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < AW; ++w) {
+        const float* pw = part + (w * 64 + lane) * 2 * DT * 16;
+        a += pw[j * 16 + 4 * rq2 + e];
+        bsum += pw[DT * 16 + j * 16 + 4 * rq2 + e];
+      }
+      sk[e] = a;
+      sv[e] = bsum;
     }
+    const int d0 = 32 * j + 8 * rq2 + 4 * hf;
+    *reinterpret_cast<float4*>(pk + prow + d0) = make_float4(sk[0], sk[1], sk[2], sk[3]);
+    *reinterpret_cast<float4*>(pv + prow + d0) = make_float4(sv[0], sv[1], sv[2], sv[3]);
+  }
 }
 
 // dk[row, g, :] = bf16(sum over the heads of group g, in head order, of the
@@ -848,7 +1006,7 @@ hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, const uint
                                 int64_t S, int H, int Hkv, int D, uint16_t* o, float* o_f32,
                                 float* lse, hipStream_t s) {
   const unsigned grid = (unsigned)(B * H * ((S + AB - 1) / AB));
-#define CALL(DD) hipLaunchKernelGGL(k_attn_fwd<DD>, dim3(grid), dim3(64), 0, s, q, k, v, S, H, Hkv, o, o_f32, lse)
+#define CALL(DD) hipLaunchKernelGGL(k_attn_fwd<DD>, dim3(grid), dim3(64 * AW), 0, s, q, k, v, S, H, Hkv, o, o_f32, lse)
   NF4S_DISPATCH_D(D, CALL)
 #undef CALL
   return hipGetLastError();
@@ -874,9 +1032,9 @@ hipError_t launch_attention_bwd(const uint16_t* q, const uint16_t* k, const uint
   float* pv = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(pk) + align256(rows * H * D * sizeof(float)));
   const unsigned grid = (unsigned)(B * H * ((S + AB - 1) / AB));
 #define CALL(DD)                                                                                   \
-  hipLaunchKernelGGL(k_attn_dq<DD>, dim3(grid), dim3(64), 0, s, q, k, v, o_f32, dout, lse, S, H, Hkv, \
+  hipLaunchKernelGGL(k_attn_dq<DD>, dim3(grid), dim3(64 * AW), 0, s, q, k, v, o_f32, dout, lse, S, H, Hkv, \
                      dsum, dq);                                                                    \
-  hipLaunchKernelGGL(k_attn_dkv<DD>, dim3(grid), dim3(64), 0, s, q, k, v, dout, lse, dsum, S, H, Hkv, \
+  hipLaunchKernelGGL(k_attn_dkv<DD>, dim3(grid), dim3(64 * AW), 0, s, q, k, v, dout, lse, dsum, S, H, Hkv, \
                      pk, pv)
   NF4S_DISPATCH_D(D, CALL)
 #undef CALL

@@ -515,30 +515,42 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
     // One step: multiply LDS stage `bs` (sub-step 0 fragments already in fb0)
     // with activation slot A, reading each sub-step's fragments one sub-step
     // ahead and refilling A for the step two ahead; end with the sub-step 0
-    // fragments of the next stage `bnext`.
+    // fragments of the next stage `bnext`. The scheduling barriers keep this
+    // order: left alone, the compiler hoists the MFMAs of a sub-step above
+    // the workgroup barrier and then issues the next fragment reads right
+    // before their first use, exposing the LDS latency.
     auto multiply = [&](const uint16_t* bs, const uint16_t* bnext, AFrags& A, int64_t knext) {
       bf16x8_t fb1[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) fb1[j] = b_frag<BWD>(bs, lane, j, 1);
+      __builtin_amdgcn_sched_barrier(0);
       mfma_kk(A, 0, fb0);
       refill(A, 0, knext);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) fb0[j] = b_frag<BWD>(bs, lane, j, 2);
+      __builtin_amdgcn_sched_barrier(0);
       mfma_kk(A, 1, fb1);
       refill(A, 1, knext);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) fb1[j] = b_frag<BWD>(bs, lane, j, 3);
+      __builtin_amdgcn_sched_barrier(0);
       mfma_kk(A, 2, fb0);
       refill(A, 2, knext);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) fb0[j] = b_frag<BWD>(bnext, lane, j, 0);
+      __builtin_amdgcn_sched_barrier(0);
       mfma_kk(A, 3, fb1);
       refill(A, 3, knext);
     };
 #define NF4S_CONSUMER_STEP(KT, SM, ACUR)                                              \
   do {                                                                                \
     multiply(stage(SM), stage(((SM) + 1) % NSTAGE), ACUR, step_of((KT) + 2).k0);      \
+    __builtin_amdgcn_sched_barrier(0);                                                \
     __syncthreads();                                                                  \
+    __builtin_amdgcn_sched_barrier(0);                                                \
   } while (0)
     const int nk4 = nk - nk % 4;
     for (int kt = 0; kt < nk4; kt += 4) {
@@ -645,12 +657,16 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
     finish_stage(stage(1), wb1, pp, valid, off, pt);
     prep_reads(wb2, s_pair, s_c8, pp);
     __syncthreads();
+// (the scheduling barriers keep the next stage's decode arithmetic below the
+// workgroup barrier, so the table lookups issued here overlap the wait)
 #define NF4S_PRODUCER_STEP(KT, SM, WFIN, WPREP, WLD)                                 \
   do {                                                                               \
     load_b(g, wl, step_of((KT) + 5), pt, WLD);                                       \
     finish_stage(stage(((SM) + 2) % NSTAGE), WFIN, pp, valid, off, pt);              \
     prep_reads(WPREP, s_pair, s_c8, pp);                                             \
+    __builtin_amdgcn_sched_barrier(0);                                               \
     __syncthreads();                                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                               \
   } while (0)
     const int nk4 = nk - nk % 4;
     for (int kt = 0; kt < nk4; kt += 4) {

@@ -61,10 +61,12 @@ class Decoder:
         """time_calls: optional predicate (direction, n_out, k_in) -> bool; the
         streamed linear forward calls it accepts are bracketed by timing
         events on the compute stream, collected in self.timed as
-        (direction, n_out, k_in, start, end)."""
+        (direction, n_out, k_in, start, end, launches) -- launches = 2 when
+        one bracket spans the gate and up GEMMs."""
         assert mode in ("streamed", "resident")
         self.time_calls = time_calls
         self.timed = []
+        self._open = None
         dev = "cuda"
         self.cfg = cfg
         self.sh = shards
@@ -199,7 +201,10 @@ class Decoder:
             self._packed_key = key
         return self.packed.data_ptr()
 
-    def _fwd(self, base, i, p, x, y, adapters=True):
+    def _fwd(self, base, i, p, x, y, adapters=True, span=None):
+        """span: None times this GEMM alone (if time_calls accepts it); "open"
+        starts a bracket that the next call with span="close" ends, timing two
+        back-to-back GEMM launches with one pair of events."""
         no, ki = self.sh.shapes[p]
         xp = self._pack(x, ki)
         d = self.sh.layout.descs[p]
@@ -207,14 +212,16 @@ class Decoder:
             A, Bm = self.lora[(i, p)]
             lora_fwd(x.data_ptr(), self.M, ki, A.data_ptr(), self.r, self.u[p].data_ptr(), *self._ws(),
                      self._s)
-            ev = self._tick("fwd", no, ki)
-            streamed_linear_fwd_packed(base, d, xp, self.M, y.data_ptr(), self.u[p].data_ptr(),
-                                       Bm.data_ptr(), self.r, self.scale, *self._ws(), self._s)
+            lora = (self.u[p].data_ptr(), Bm.data_ptr(), self.r, self.scale)
         else:
-            ev = self._tick("fwd", no, ki)
-            streamed_linear_fwd_packed(base, d, xp, self.M, y.data_ptr(), None, None, 0, 0.0,
-                                       *self._ws(), self._s)
-        self._tock(ev)
+            lora = (None, None, 0, 0.0)
+        ev = self._open if span == "close" else self._tick("fwd", no, ki)
+        streamed_linear_fwd_packed(base, d, xp, self.M, y.data_ptr(), *lora, *self._ws(), self._s)
+        if span == "open":
+            self._open = ev
+        else:
+            self._tock(ev, launches=2 if span == "close" else 1)
+            self._open = None
 
     def _tick(self, direction, n, k):
         if self.time_calls is None or not self.time_calls(direction, n, k):
@@ -224,10 +231,10 @@ class Decoder:
         start.record(self.compute)
         return (direction, n, k, start, end)
 
-    def _tock(self, ev):
+    def _tock(self, ev, launches=1):
         if ev is not None:
             ev[4].record(self.compute)
-            self.timed.append(ev)
+            self.timed.append(ev + (launches,))
 
     def _bwd(self, base, i, p, x, dy, dx):
         no, ki = self.sh.shapes[p]
@@ -271,8 +278,11 @@ class Decoder:
         nf4s_residual_add(hin.data_ptr(), self.ao.data_ptr(), M * H, self.h_mid.data_ptr(), s)
         nf4s_rmsnorm_fwd(self.h_mid.data_ptr(), self.norms["mlp"][i].data_ptr(), M, H, c["eps"],
                          self.n2.data_ptr(), self.rstd2.data_ptr(), s)
-        self._fwd(base, i, "gate", self.n2, self.g, a)
-        self._fwd(base, i, "up", self.n2, self.u_, a)
+        # gate and up read the same input back to back: one timing bracket
+        # spans both GEMMs when neither carries an adapter
+        pair = not (a and ("gate" in self.targets or "up" in self.targets))
+        self._fwd(base, i, "gate", self.n2, self.g, a, span="open" if pair else None)
+        self._fwd(base, i, "up", self.n2, self.u_, a, span="close" if pair else None)
         nf4s_swiglu_fwd(self.g.data_ptr(), self.u_.data_ptr(), M * self.I, self.sw.data_ptr(), s)
         self._fwd(base, i, "down", self.sw, self.dn, a)
         if not recompute:

@@ -543,6 +543,7 @@ def _run_pref(w, shards, mode, schedule, pairs, prompt, n_slots=2, lora=None):
     torch.cuda.synchronize()
     out = dict(loss=dec.loss.cpu().numpy().copy(), logits=host_u16(dec.logits).copy(),
                grads=dec.grads.cpu().numpy().copy(), nll_ref=dec.nll_ref.cpu().numpy().copy(),
+               nll_pol=dec.nll_pol.cpu().numpy().copy(),
                split={k: (a.cpu().numpy().copy(), b.cpu().numpy().copy())
                       for k, (a, b) in dec.lora_grads.items()},
                stats=dec.stats())
@@ -550,26 +551,46 @@ def _run_pref(w, shards, mode, schedule, pairs, prompt, n_slots=2, lora=None):
     return out
 
 
-def test_tiny_dpo_step_matches_oracle():
-    """Reference sweep (adapters off) + policy step on 2 pairs x S70 with a
-    20-token shared prompt, LoRA on all seven, against oracle.dpo_step. Bound
-    as the plain step for logits and gradients; the loss compares differences
-    of 50-token log-probability sums, 5e-3 relative."""
-    require_gpu()
-    w = _world("tiny", 4, 70, targets=PROJ)
-    got = _run_pref(w, _shards(w), "resident", "separate", pairs=2, prompt=20)
+def _check_dpo_against_oracle(w, got, pairs, prompt, beta=0.1):
+    """The DPO loss compares two nearly equal models (policy = reference plus
+    the adapters), so it amplifies the one-unit bf16 flips that both sides
+    are entitled to; it is checked through the well-conditioned quantities:
+    each sequence's policy and reference log-probability against the oracle
+    (1e-4 relative, the plain step's loss bar), the loss within the bound
+    those errors imply (|dL/d delta| <= 1, delta = beta times a signed sum of
+    a pair's four log-probabilities, so |dL| <= beta / pairs * sum |d log p|,
+    plus fp32 slack), the policy logits and the adapter gradients (2e-2 of
+    the largest, as the plain step)."""
     P = _oracle_params(w)
     cfg = _oracle_cfg(w)
-    ids, tg, mask = _pref(w, 2, 20)
-    loss, g, logits = D.dpo_step(P, ids, tg, mask, cfg, 0.1)
-    print(f"dpo oracle loss {loss:.6f} gpu {float(got['loss'][0]):.6f}", flush=True)
-    assert abs(float(got["loss"][0]) - loss) <= 5e-3 * abs(loss)
+    ids, tg, mask = _pref(w, pairs, prompt)
+    loss, g, logits = D.dpo_step(P, ids, tg, mask, cfg, beta)
+    ref_logits = D.forward(P, ids, tg, cfg, adapters=False)[1]
+    t, m, S = tg.reshape(-1), mask.reshape(-1).astype(np.float64), ids.shape[1]
+    seq = lambda nll: -(m * nll).reshape(-1, S).sum(axis=1)  # noqa: E731
+    o_lp, o_lr = seq(D.token_nll(logits, t)), seq(D.token_nll(ref_logits, t))
+    g_lp, g_lr = seq(got["nll_pol"].astype(np.float64)), seq(got["nll_ref"].astype(np.float64))
+    assert np.all(np.abs(g_lp - o_lp) <= 1e-4 * np.abs(o_lp)), (g_lp, o_lp)
+    assert np.all(np.abs(g_lr - o_lr) <= 1e-4 * np.abs(o_lr)), (g_lr, o_lr)
+    bound = beta / pairs * float(np.sum(np.abs(g_lp - o_lp) + np.abs(g_lr - o_lr))) + 1e-5 * abs(loss)
+    gloss = float(got["loss"][0])
+    print(f"dpo oracle loss {loss:.6f} gpu {gloss:.6f} bound {bound:.2e}", flush=True)
+    assert abs(gloss - loss) <= bound, (gloss, loss, bound)
     gl = _vals(got["logits"]).reshape(logits.shape)
     assert np.max(np.abs(gl - logits)) / np.max(np.abs(logits)) <= 2e-2
     for key, (dA, dB) in g["lora"].items():
         gA, gB = got["split"][key]
         for a, b in ((gA, dA), (gB, dB)):
             assert np.max(np.abs(a - b)) / np.max(np.abs(b)) <= 2e-2, key
+
+
+def test_tiny_dpo_step_matches_oracle():
+    """Reference sweep (adapters off) + policy step on 2 pairs x S70 with a
+    20-token shared prompt, LoRA on all seven, against oracle.dpo_step."""
+    require_gpu()
+    w = _world("tiny", 4, 70, targets=PROJ)
+    got = _run_pref(w, _shards(w), "resident", "separate", pairs=2, prompt=20)
+    _check_dpo_against_oracle(w, got, pairs=2, prompt=20)
 
 
 @pytest.fixture(scope="module")
@@ -607,3 +628,43 @@ def test_135m_dpo_zero_adapters_is_ln2(w135):
     assert abs(float(got["loss"][0]) - math.log(2)) <= 2e-7, got["loss"]     # one fp32 unit
     for key, (dA, dB) in got["split"].items():
         assert np.all(dA == 0) and np.any(dB != 0), key
+
+
+# ---- full widths: one layer of the 8B and 32B-class models -----------------------------
+
+def _one_layer_world(model, batch, seq, targets=("q", "v")):
+    """The model at its real widths (hidden, heads, head size, vocabulary) with
+    one decoder layer, so the fp64 oracle finishes in seconds."""
+    w = _world(model, batch, seq, targets)
+    w["nl"] = 1
+    w["c"] = dict(w["c"], layers=1)
+    w["norms"] = {"attn": w["norms"]["attn"][:1], "mlp": w["norms"]["mlp"][:1], "final": w["norms"]["final"]}
+    w["lora"] = {k: v for k, v in w["lora"].items() if k[0] == 0}
+    return w
+
+
+def test_8b_widths_one_layer_matches_oracle_and_streams_identically():
+    """Llama-8B widths (hidden 4096, 32 heads over 8 KV heads of 128, vocab
+    128,256, untied head), one layer, B1 S512 -- the shapes the benchmark
+    times -- against the oracle end to end; and streamed (n = 2) == resident
+    bit for bit. Bound as the tiny model (one layer): 2e-2."""
+    require_gpu()
+    print("8b widths, one layer", flush=True)
+    w = _one_layer_world("8b", 1, 512)
+    shards = _shards(w)
+    res = _run_once(w, shards, "resident")
+    st = _run_once(w, shards, "streamed")
+    assert np.array_equal(res["logits"], st["logits"])
+    assert np.array_equal(res["grads"].view(np.uint32), st["grads"].view(np.uint32))
+    _compare_with_oracle(w, res, tol_logits=2e-2, tol_grads=2e-2, tol_loss=1e-4)
+
+
+def test_32b_widths_one_layer_dpo_matches_oracle():
+    """32B-class widths (hidden 5120, 40 heads over 8 KV heads, vocab 152,064),
+    one layer, the DPO step on one pair of 128-token sequences with a 32-token
+    shared prompt, against oracle.dpo_step (checked as the tiny DPO step)."""
+    require_gpu()
+    print("32b widths, one layer, dpo", flush=True)
+    w = _one_layer_world("32b", 2, 128)
+    got = _run_pref(w, _shards(w), "resident", "separate", pairs=1, prompt=32)
+    _check_dpo_against_oracle(w, got, pairs=1, prompt=32)

@@ -93,10 +93,10 @@ def gemm_source_hash() -> str:
 
 def traffic_from_profile(kernel_src_hash: str, spec: str):
     """HBM bytes per launch of the dominant kernel from the committed PMC summary,
-    if it was taken on this exact GEMM source and this shape (`fwd:N:K:M`);
+    if it was taken on this exact GEMM source and this shape (`fwd:N:K:M`, or `fwd:N1+N2:K:M` for a grouped launch);
     else None."""
     here = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(here, "profiles", "gemm_fwd_gate_8b_m512_pmc.md")
+    path = os.path.join(here, "profiles", "gemm_fwd_gate_up_8b_m512_pmc.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -115,36 +115,55 @@ def traffic_from_profile(kernel_src_hash: str, spec: str):
 def profile_gemm(spec: str, reps: int) -> None:
     """Run one fused GEMM shape `fwd:N:K:M` or `bwd:N:K:M` (resident weight)
     `reps` times, then a 64 MiB device copy whose FETCH/WRITE counters give the
-    scale of the memory counters. Used under rocprofv3."""
+    scale of the memory counters. `fwd:N1+N2:K:M` runs the grouped forward of
+    weights of N1 and N2 outputs reading one input. Used under rocprofv3."""
     import torch
     import layer_streamed_nf4_amd as L
-    direction, n, k, M = spec.split(":")
-    n, k, M = int(n), int(k), int(M)
+    direction, ns, k, M = spec.split(":")
+    ns = [int(x) for x in ns.split("+")]
+    k, M = int(k), int(M)
     dev = "cuda"
     s = torch.cuda.current_stream().cuda_stream
     g = torch.Generator(device=dev)
     g.manual_seed(synth.BASE_SEED)
-    w = torch.randn((n, k), generator=g, device=dev) * 0.02
-    d = L.nf4s_tensor_layout(n, k)
-    shard = torch.zeros(d.end, dtype=torch.uint8, device=dev)
-    wq = torch.empty(max(256, L.nf4s_workspace_bytes(L.OP_QUANTIZE, 0, n, k)), dtype=torch.uint8, device=dev)
-    L.nf4_quantize_shard(w.data_ptr(), L.DTYPE_F32, n, k, shard.data_ptr(), d, None, wq.data_ptr(),
-                         wq.numel(), s)
+    descs, end = [], 0
+    for n in ns:
+        descs.append(L.nf4s_tensor_layout(n, k, end))
+        end = descs[-1].end
+    shard = torch.zeros(end, dtype=torch.uint8, device=dev)
+    for n, d in zip(ns, descs):
+        w = torch.randn((n, k), generator=g, device=dev) * 0.02
+        wq = torch.empty(max(256, L.nf4s_workspace_bytes(L.OP_QUANTIZE, 0, n, k)), dtype=torch.uint8,
+                         device=dev)
+        L.nf4_quantize_shard(w.data_ptr(), L.DTYPE_F32, n, k, shard.data_ptr(), d, None,
+                             wq.data_ptr(), wq.numel(), s)
     bwd = direction == "bwd"
+    n = ns[0]
     a = torch.randn((M, n if bwd else k), generator=g, device=dev).to(torch.bfloat16)
-    out = torch.empty((M, k if bwd else n), dtype=torch.bfloat16, device=dev)
-    op = L.OP_LINEAR_BWD_PACKED if bwd else L.OP_LINEAR_FWD_PACKED
-    ws = torch.zeros(max(256, L.nf4s_workspace_bytes(op, M, n, k)), dtype=torch.uint8, device=dev)
+    outs = [torch.empty((M, k if bwd else n_), dtype=torch.bfloat16, device=dev) for n_ in ns]
+    if len(ns) > 1:
+        assert not bwd, "grouped launches are forward only"
+        ws_bytes = L.grouped_workspace_bytes(ns, k, M)
+    else:
+        op = L.OP_LINEAR_BWD_PACKED if bwd else L.OP_LINEAR_FWD_PACKED
+        ws_bytes = L.nf4s_workspace_bytes(op, M, n, k)
+    ws = torch.zeros(max(256, ws_bytes), dtype=torch.uint8, device=dev)
     K = n if bwd else k
     ap = torch.empty(L.nf4s_packed_activation_bytes(M, K), dtype=torch.uint8, device=dev)
     L.nf4s_pack_activation(a.data_ptr(), M, K, ap.data_ptr(), ap.numel(), s)
     for _ in range(reps):
         if bwd:
-            L.streamed_linear_bwd_packed(shard.data_ptr(), d, ap.data_ptr(), M, out.data_ptr(), None,
-                                         None, 0, ws.data_ptr(), ws.numel(), s)
+            L.streamed_linear_bwd_packed(shard.data_ptr(), descs[0], ap.data_ptr(), M,
+                                         outs[0].data_ptr(), None, None, 0, ws.data_ptr(),
+                                         ws.numel(), s)
+        elif len(ns) > 1:
+            L.streamed_linear_fwd_grouped(shard.data_ptr(), descs, ap.data_ptr(), M,
+                                          [o.data_ptr() for o in outs], None, None, 0, 0.0,
+                                          ws.data_ptr(), ws.numel(), s)
         else:
-            L.streamed_linear_fwd_packed(shard.data_ptr(), d, ap.data_ptr(), M, out.data_ptr(), None,
-                                         None, 0, 0.0, ws.data_ptr(), ws.numel(), s)
+            L.streamed_linear_fwd_packed(shard.data_ptr(), descs[0], ap.data_ptr(), M,
+                                         outs[0].data_ptr(), None, None, 0, 0.0, ws.data_ptr(),
+                                         ws.numel(), s)
     torch.cuda.synchronize()
     src = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -247,10 +266,41 @@ def _cpu_baseline_decoder(model: str, batch: int, seq: int, targets, preference=
     what = (f"DPO step sampled on 1 pair x {ids.shape[1]} tokens, scaled x{scale_tokens:g} to "
             f"B{batch} S{seq}" if preference else f"B{batch} S{seq}")
     return {"value": M / t_step, "unit": "tok/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": f"{model} decoder, {what} (LoRA {'/'.join(targets)}), fp64 "
                       f"forward + backward: head alone {t_head:.2f} s, one layer + head "
                       f"{t_one:.2f} s; layer dequantisation {t_deq:.2f} s (scaled from q); "
                       f"step = head + {n_layers} x layer = {t_step:.1f} s"}
+
+
+def _cpu_model() -> str | None:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _gpu_clock_and_temp() -> dict:
+    """SCLK and edge/junction temperature read through rocm-smi right after
+    the timed region (None where the tool or a field is unavailable)."""
+    import subprocess
+    out = {"sclk_mhz": None, "temperature_c": None}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showtemp", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        data = json.loads(r.stdout[r.stdout.index("{"):])
+        card = next(iter(v for k, v in data.items() if k.startswith("card")))
+        for k, v in card.items():
+            if k.startswith("sclk") and "speed" in k and out["sclk_mhz"] is None:
+                out["sclk_mhz"] = float(str(v).strip("()Mhz").split("Mhz")[0])
+            if "junction" in k.lower() and "temperature" in k.lower():
+                out["temperature_c"] = float(v)
+    except Exception:  # noqa: BLE001 -- reporting only
+        pass
+    return out
 
 
 def sweep(args) -> None:
@@ -538,8 +588,15 @@ def main():
     else:
         dt_s, h2d_bytes, copies, durs, dt_r = lin_s, lin_h2d, lin_copies, lin_durs, lin_r
 
+    peak_mem = torch.cuda.max_memory_allocated()
+    gpu_state = _gpu_clock_and_temp()
+
     # same-session ceilings: hipBLASLt bf16 GEMM at the dominant shape, pinned H2D
     n_d, k_d = sh["gate"]
+    # the decoder runs gate and up as one grouped launch over both weights:
+    # the dominant launch (and its dense same-shape ceiling) has 2 x n_out
+    if use_decoder:
+        n_d = 2 * n_d
     a = torch.randn((M, k_d), device=dev, dtype=torch.bfloat16)
     w = torch.randn((n_d, k_d), device=dev, dtype=torch.bfloat16)
     for _ in range(3):
@@ -575,15 +632,19 @@ def main():
     dom_ms = [d for (_, _, d) in durs]
     dom_flops = [2 * M * n * k for (n, k, _) in durs]
     roofline = None
+    n_g, k_g = sh["gate"]
+    dom_spec = f"fwd:{n_g}+{n_g}:{k_g}:{M}" if use_decoder else f"fwd:{n_g}:{k_g}:{M}"
     if dom_ms:
         avg_ms = sum(dom_ms) / len(dom_ms)
         avg_flop = sum(dom_flops) / len(dom_flops)
         ach = avg_flop / (avg_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                    "traffic": traffic_from_profile(gemm_source_hash(), f"fwd:{n_d}:{k_d}:{M}"),
+                    "traffic": traffic_from_profile(gemm_source_hash(), dom_spec),
                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
-                    "kernel": "k_gemm<fwd,plain> (fused NF4 dequant + bf16 MFMA, x.W'^T)",
+                    "kernel": "k_gemm<fwd,plain> (fused NF4 dequant + bf16 MFMA, x.W'^T)"
+                              + ("; one grouped launch = gate and up" if use_decoder else ""),
+                    "spec": dom_spec,
                     "launches": len(dom_ms), "avg_us": round(avg_ms * 1e3, 2),
                     "flop_per_launch": int(avg_flop)}
     if use_decoder:
@@ -631,7 +692,15 @@ def main():
         "h2d": {"bytes_per_step": int(h2d_bytes), "copies_per_step": copies,
                 "effective_gbs": round(h2d_bytes / dt_s / 1e9, 2),
                 "pinned_peak_gbs_same_session": round(h2d_peak, 2),
-                "host_link_theoretical_gbs": HOST_LINK_GBS},
+                "host_link_theoretical_gbs": HOST_LINK_GBS,
+                # (t_copy + t_compute - t_step) / min(t_copy, t_compute), with t_copy the
+                # step's bytes at the same-session pinned rate, t_compute the resident step
+                "overlap_efficiency": None if dt_r is None else round(
+                    (h2d_bytes / (h2d_peak * 1e9) + dt_r - dt_s)
+                    / min(h2d_bytes / (h2d_peak * 1e9), dt_r), 3)},
+        "device": {"peak_memory_allocated_gb": round(peak_mem / 1e9, 3),
+                   "sclk_mhz_after_timed_region": gpu_state["sclk_mhz"],
+                   "junction_temperature_c_after_timed_region": gpu_state["temperature_c"]},
         "roofline": roofline,
         "hipblaslt_bf16_same_shape_tflops": round(blas_tflops, 1),
         "context": "pages (NVIDIA, full model incl. attention/lm_head/optimizer): 119.6 tok/s at "

@@ -245,6 +245,32 @@ int streamed_linear_bwd_packed(const void* shard_dev, const nf4s_tensor_desc* d,
                                size_t ws_bytes, void* stream);
 
 /*
+ * Forward of n (1..3) NF4 linears of one shard that read the same input, in
+ * one launch ([G] s2.1: q, k and v read the normed hidden state, as do gate
+ * and up): for each i, ys[i] is streamed_linear_fwd_packed of descs[i] on
+ * x_packed. One grid covers the column tiles of all n weights, so projections
+ * too narrow to fill the chip alone (k and v under grouped-query attention)
+ * share a launch, and the contraction is split for the group as a whole.
+ *   descs:   host array of n descriptors of the shard, all with the same k_in;
+ *   x_packed: nf4s_pack_activation of bf16 x [M, k_in] (256-B aligned);
+ *   ys:      host array of n device pointers, bf16 [M, descs[i].n_out];
+ *   lora_us, lora_Bs: nullable host arrays of n device pointers; entry i is
+ *            fp32 [M, r] / [descs[i].n_out, r] or NULL in both (no adapter);
+ *   ws:      nf4s_grouped_workspace_bytes(n, n_outs, k_in, M) bytes (zero
+ *            when the contraction is not split).
+ * Outputs equal the single calls' up to the grouping of the fp32 accumulation
+ * (the group's split count may differ from a single weight's); deterministic.
+ * Errors: EINVAL (n out of range, unpaired LoRA operands), ESHAPE (k_in
+ * differs, sizes), EALIGN, ETABLE, EKEY, EWORKSPACE.
+ */
+int nf4s_grouped_workspace_bytes(int n, const int64_t* n_outs, int64_t k_in, int64_t M,
+                                 size_t* bytes);
+int streamed_linear_fwd_grouped(const void* shard_dev, const nf4s_tensor_desc* descs, int n,
+                                const void* x_packed, int64_t M, uint16_t* const* ys,
+                                const float* const* lora_us, const float* const* lora_Bs, int r,
+                                float scale, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * LoRA down-projection, u = x.A^T in fp32 ([G] s2.1, adapter on q/v):
  *   x: bf16 [M, k_in]; A: fp32 [r, k_in] (16-byte aligned); u_out: fp32 [M, r];
  *   ws: nf4s_workspace_bytes(NF4S_OP_LORA_FWD, M, n_out, k_in) bytes (partials

@@ -34,6 +34,7 @@ EXPORTS = (
     "nf4s_pool_prefetch", "nf4s_pool_acquire", "nf4s_pool_release", "nf4s_pool_stats",
     "nf4s_packed_activation_bytes", "nf4s_pack_activation", "streamed_linear_fwd_packed",
     "streamed_linear_bwd_packed", "dense_linear_fwd_packed", "dense_linear_bwd_packed",
+    "nf4s_grouped_workspace_bytes", "streamed_linear_fwd_grouped",
     "nf4s_embed", "nf4s_rmsnorm_fwd", "nf4s_rmsnorm_bwd", "nf4s_rope", "nf4s_attention_fwd",
     "nf4s_attention_bwd", "nf4s_swiglu_fwd", "nf4s_swiglu_bwd", "nf4s_residual_add",
     "nf4s_to_bf16", "nf4s_cross_entropy", "nf4s_adamw", "nf4s_token_nll", "nf4s_dpo_loss",
@@ -105,6 +106,10 @@ _SIG = {
                                                   ctypes.c_size_t, _P]),
     "streamed_linear_bwd_packed": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P,
                                                   _P, ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "nf4s_grouped_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P]),
+    "streamed_linear_fwd_grouped": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), ctypes.c_int, _P,
+                                                   _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float,
+                                                   _P, ctypes.c_size_t, _P]),
     "dense_linear_fwd_packed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
     "dense_linear_bwd_packed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
     "nf4s_embed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P]),
@@ -221,6 +226,35 @@ def streamed_linear_bwd_packed(shard, desc, dy_packed, M, dx, lora_du, lora_A, r
                                stream=0):
     _check(lib().streamed_linear_bwd_packed(shard, ctypes.byref(desc), dy_packed, M, dx, lora_du,
                                             lora_A, r, ws, ws_bytes, stream))
+
+
+def grouped_workspace_bytes(n_outs, k_in, M):
+    """Workspace of streamed_linear_fwd_grouped for weights of n_outs outputs."""
+    arr = (ctypes.c_int64 * len(n_outs))(*n_outs)
+    out = ctypes.c_size_t()
+    _check(lib().nf4s_grouped_workspace_bytes(len(n_outs), ctypes.cast(arr, ctypes.c_void_p), k_in, M,
+                                              ctypes.byref(out)))
+    return out.value
+
+
+def _ptr_array(ptrs):
+    if ptrs is None:
+        return None
+    return ctypes.cast((ctypes.c_void_p * len(ptrs))(*[p or None for p in ptrs]), ctypes.c_void_p)
+
+
+def streamed_linear_fwd_grouped(shard, descs, x_packed, M, ys, lora_us, lora_Bs, r, scale, ws,
+                                ws_bytes, stream=0):
+    """One launch of the forward of len(descs) weights reading x_packed.
+
+    descs: TensorDesc list; ys: device pointers; lora_us / lora_Bs: None or
+    lists of device pointers (None entries: no adapter on that weight).
+    """
+    n = len(descs)
+    darr = (TensorDesc * n)(*descs)
+    _check(lib().streamed_linear_fwd_grouped(shard, darr, n, x_packed, M, _ptr_array(ys),
+                                             _ptr_array(lora_us), _ptr_array(lora_Bs), r, scale, ws,
+                                             ws_bytes, stream))
 
 
 def dense_linear_fwd_packed(w, n_out, k_in, x_packed, M, y, ws, ws_bytes, stream=0):

@@ -355,6 +355,83 @@ int streamed_linear_bwd_packed(const void* shard_dev, const nf4s_tensor_desc* d,
                        ws_bytes, stream);
 }
 
+static int check_group(int n, const int64_t* n_outs, int64_t k_in, int64_t M) {
+  if (n < 1 || n > GEMM_MAX_SEG)
+    return fail(NF4S_EINVAL, "group of %d weights (1..%d allowed)", n, GEMM_MAX_SEG);
+  if (!n_outs) return fail(NF4S_EINVAL, "n_outs is NULL");
+  int rc;
+  if ((rc = check_packed_shape(M, k_in))) return rc;
+  int64_t tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    if ((rc = check_shape(n_outs[i], k_in))) return rc;
+    const int64_t widest = n_outs[i] > k_in ? n_outs[i] : k_in;
+    if (M * widest >= (1ll << 31))
+      return fail(NF4S_ESHAPE, "M=%lld with a %lldx%lld weight exceeds 32-bit offsets", (long long)M,
+                  (long long)n_outs[i], (long long)k_in);
+    tiles += (n_outs[i] + 127) / 128;
+  }
+  if (tiles >= (1ll << 31)) return fail(NF4S_ESHAPE, "too many column tiles");
+  return NF4S_OK;
+}
+
+int nf4s_grouped_workspace_bytes(int n, const int64_t* n_outs, int64_t k_in, int64_t M,
+                                 size_t* bytes) {
+  if (!bytes) return fail(NF4S_EINVAL, "bytes is NULL");
+  int rc;
+  if ((rc = check_group(n, n_outs, k_in, M))) return rc;
+  *bytes = plan_gemm_grouped(M, n_outs, n, k_in).part_bytes;
+  return NF4S_OK;
+}
+
+int streamed_linear_fwd_grouped(const void* shard_dev, const nf4s_tensor_desc* descs, int n,
+                                const void* x_packed, int64_t M, uint16_t* const* ys,
+                                const float* const* lora_us, const float* const* lora_Bs, int r,
+                                float scale, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if (!descs || !ys) return fail(NF4S_EINVAL, "descs and ys must be given");
+  if (n < 1 || n > GEMM_MAX_SEG)
+    return fail(NF4S_EINVAL, "group of %d weights (1..%d allowed)", n, GEMM_MAX_SEG);
+  int64_t n_outs[GEMM_MAX_SEG];
+  QPtrs q[GEMM_MAX_SEG];
+  bool any_lora = false;
+  for (int i = 0; i < n; ++i) {
+    if ((rc = check_desc(&descs[i]))) return rc;
+    if (descs[i].k_in != descs[0].k_in)
+      return fail(NF4S_ESHAPE, "weight %d has k_in=%lld, weight 0 has %lld", i,
+                  (long long)descs[i].k_in, (long long)descs[0].k_in);
+    n_outs[i] = descs[i].n_out;
+    if ((rc = check_ptr(ys[i], "ys[i]"))) return rc;
+    const float* u = lora_us ? lora_us[i] : nullptr;
+    const float* B = lora_Bs ? lora_Bs[i] : nullptr;
+    if ((u == nullptr) != (B == nullptr))
+      return fail(NF4S_EINVAL, "LoRA operands of weight %d must be given together", i);
+    if (u) {
+      any_lora = true;
+      if ((rc = check_ptr(u, "lora_us[i]", 4))) return rc;
+      if ((rc = check_ptr(B, "lora_Bs[i]", 4))) return rc;
+    }
+  }
+  const int64_t k_in = descs[0].k_in;
+  if ((rc = check_group(n, n_outs, k_in, M))) return rc;
+  for (int i = 0; i < n; ++i)
+    if (descs[i].n_out * k_in >= (1ll << 33))
+      return fail(NF4S_ESHAPE, "a %lldx%lld weight exceeds 32-bit offsets", (long long)descs[i].n_out,
+                  (long long)k_in);
+  if (any_lora) {
+    if ((rc = check_rank(r))) return rc;
+    if (!std::isfinite(scale)) return fail(NF4S_EINVAL, "scale is not finite");
+  }
+  if ((rc = check_ptr(shard_dev, "shard_dev", 256))) return rc;
+  if ((rc = check_ptr(x_packed, "x_packed", 256))) return rc;
+  const GemmPlan p = plan_gemm_grouped(M, n_outs, n, k_in);
+  if (p.part_bytes && (rc = check_ws(ws, ws_bytes, p.part_bytes))) return rc;
+  for (int i = 0; i < n; ++i) q[i] = resolve(shard_dev, &descs[i]);
+  hipError_t e = launch_linear_grouped_fwd(q, n, n_outs, k_in, static_cast<const uint8_t*>(x_packed),
+                                           M, ys, lora_us, lora_Bs, any_lora ? r : 0, scale, ws,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "grouped linear launch");
+}
+
 int lora_fwd(const uint16_t* x, int64_t M, int64_t k_in, const float* A, int r, float* u_out,
              void* ws, size_t ws_bytes, void* stream) {
   int rc;

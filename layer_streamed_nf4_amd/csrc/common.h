@@ -41,6 +41,9 @@ constexpr int PACK_ROWS = 256;
 constexpr int PACK_COLS = 64;
 constexpr int FRAG_BYTES = 1024;
 
+// Weights one grouped forward launch covers (q, k and v read the same input).
+constexpr int GEMM_MAX_SEG = 3;
+
 // Launch configuration of the dequant GEMMs, a function of the shape only.
 struct GemmPlan {
   int bm, bn;        // output tile
@@ -51,6 +54,8 @@ struct GemmPlan {
   size_t ws_bytes;    // frag_bytes + part_bytes
 };
 GemmPlan plan_gemm(int64_t M, int64_t n_cols, int64_t k_contract);
+// The same for a grouped forward of nseg weights of n_cols[i] outputs.
+GemmPlan plan_gemm_grouped(int64_t M, const int64_t* n_cols, int nseg, int64_t k_contract);
 size_t packed_activation_bytes(int64_t M, int64_t K);
 
 // Kernel launchers (return hipError_t of the launch).
@@ -67,6 +72,13 @@ hipError_t launch_linear_packed(bool backward, const QPtrs& q, int64_t n_out, in
                                 const uint8_t* a_packed, int64_t M, uint16_t* out,
                                 const float* lora_l, const float* lora_r, int r, float scale,
                                 void* part_ws, hipStream_t s);
+// Forward of nseg (<= GEMM_MAX_SEG) NF4 linears reading the same packed
+// activation, in one launch (lora_us / lora_Bs entries may be null).
+hipError_t launch_linear_grouped_fwd(const QPtrs* q, int nseg, const int64_t* n_outs, int64_t k_in,
+                                     const uint8_t* x_packed, int64_t M, uint16_t* const* ys,
+                                     const float* const* lora_us, const float* const* lora_Bs,
+                                     int r, float scale, void* part_ws, hipStream_t s);
+
 // The same GEMMs with a dense bf16 weight w[n_out, k_in] (the resident lm_head).
 hipError_t launch_dense_packed(bool backward, const uint16_t* w, int64_t n_out, int64_t k_in,
                                const uint8_t* a_packed, int64_t M, uint16_t* out, void* part_ws,

@@ -73,6 +73,22 @@ constexpr int SMEM_BYTES = NSTAGE * STAGE_ELEMS * 2 + 256 * PAIR_COPIES * 8 + 25
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
 
+// One weight of a grouped launch: the forward of up to GEMM_MAX_SEG NF4
+// linears that read the same activation (q, k and v; gate and up) runs as one
+// grid whose column tiles are dealt to the weights in order.
+struct GemmSeg {
+  const uint8_t* packed;
+  const uint8_t* q8;
+  const float* nested;
+  const float* offset;
+  uint16_t* out;         // bf16 [M, Nc]
+  float* part;           // fp32 [splits, M, Nc] (splits > 1)
+  const float* lora_l;   // fp32 [M, r]
+  const float* lora_r;   // fwd: B fp32 [n_out, r]; bwd: A fp32 [r, k_in]
+  int64_t n_out;
+  int tile0;             // first column tile of this weight
+};
+
 struct GemmArgs {
   const uint16_t* wd;  // dense bf16 weight [n_out, k_in] (DENSE kernels only)
   const uint8_t* packed;
@@ -90,6 +106,8 @@ struct GemmArgs {
   const float* lora_r;  // fwd: B fp32 [n_out, r]; bwd: A fp32 [r, k_in]
   int r;
   float scale;
+  int nseg;             // weights in the launch (1 unless a grouped forward)
+  GemmSeg seg[GEMM_MAX_SEG];
 };
 
 // A contraction step covers [k0, k0 + 64). The packed activation is zero past
@@ -439,7 +457,23 @@ __device__ __forceinline__ bf16x8_t f32x8_to_bf16(const float* v) {
 // so the two variants also carry distinct kernel names in profiles. DENSE
 // swaps the NF4 producer for the plain bf16 one.
 template <bool BWD, bool SPLIT, bool DENSE>
-__global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
+__global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
+  // the weight this workgroup's column tile belongs to (uniform per workgroup)
+  int sgi = 0;
+#pragma unroll
+  for (int q = 1; q < GEMM_MAX_SEG; ++q)
+    if (q < ga.nseg && (int)blockIdx.x >= ga.seg[q].tile0) sgi = q;
+  GemmArgs g = ga;
+  g.packed = ga.seg[sgi].packed;
+  g.q8 = ga.seg[sgi].q8;
+  g.nested = ga.seg[sgi].nested;
+  g.offset = ga.seg[sgi].offset;
+  g.out = ga.seg[sgi].out;
+  g.part = ga.seg[sgi].part;
+  g.lora_l = ga.seg[sgi].lora_l;
+  g.lora_r = ga.seg[sgi].lora_r;
+  g.n_out = ga.seg[sgi].n_out;
+  if (!BWD) g.Nc = g.n_out;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_BYTES];
   uint16_t* const Bs0 = reinterpret_cast<uint16_t*>(smem);
   float2* const s_pair_all = reinterpret_cast<float2*>(smem + NSTAGE * STAGE_ELEMS * 2);
@@ -456,7 +490,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
   // Default launch order: the workgroups are dealt to the 8 XCDs round-robin,
   // so both 256-row tiles of an output column block land on the same XCD and
   // share its weight stream in L2.
-  const int64_t n0 = (int64_t)blockIdx.x * BN;
+  const int64_t n0 = (int64_t)((int)blockIdx.x - ga.seg[sgi].tile0) * BN;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int split = blockIdx.z;
   const int64_t kb = split * g.kc_chunk;
@@ -745,9 +779,19 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs g, Tables tab) {
   }
 }
 
-// Sum of the split partials in split order, rounded once to bf16.
-__global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ part, int splits,
-                                                   int64_t n, uint16_t* __restrict__ out) {
+// Sum of the split partials in split order, rounded once to bf16; blockIdx.y
+// selects the weight of a grouped launch.
+struct SumSegs {
+  const float* part[GEMM_MAX_SEG];
+  uint16_t* out[GEMM_MAX_SEG];
+  int64_t n[GEMM_MAX_SEG];
+};
+
+__global__ __launch_bounds__(256) void k_split_sum(SumSegs sg, int splits) {
+  const int sgi = blockIdx.y;
+  const float* __restrict__ part = sg.part[sgi];
+  uint16_t* __restrict__ out = sg.out[sgi];
+  const int64_t n = sg.n[sgi];
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (i >= n) return;
   if (i + 4 <= n) {
@@ -772,11 +816,15 @@ __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ par
 }  // namespace
 
 
-GemmPlan plan_gemm(int64_t M, int64_t n_cols, int64_t k_contract) {
+static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+GemmPlan plan_gemm_grouped(int64_t M, const int64_t* n_cols, int nseg, int64_t k_contract) {
   GemmPlan p;
   p.bm = BM;
   p.bn = BN;
-  const int64_t tiles = ((M + BM - 1) / BM) * ((n_cols + BN - 1) / BN);
+  int64_t col_tiles = 0;
+  for (int q = 0; q < nseg; ++q) col_tiles += (n_cols[q] + BN - 1) / BN;
+  const int64_t tiles = ((M + BM - 1) / BM) * col_tiles;
   const int64_t nk = (k_contract + BK - 1) / BK;
   int splits = 1;
   // Split the contraction while the grid is short of the chip's 256 CUs and
@@ -786,41 +834,71 @@ GemmPlan plan_gemm(int64_t M, int64_t n_cols, int64_t k_contract) {
   p.kc_chunk = steps_per * BK;
   p.splits = (int)((nk + steps_per - 1) / steps_per);
   p.frag_bytes = packed_activation_bytes(M, k_contract);
-  p.part_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)n_cols * sizeof(float) : 0;
+  p.part_bytes = 0;
+  if (p.splits > 1)
+    for (int q = 0; q < nseg; ++q)
+      p.part_bytes += round256((size_t)p.splits * (size_t)M * (size_t)n_cols[q] * sizeof(float));
   p.ws_bytes = p.frag_bytes + p.part_bytes;
   return p;
 }
 
+GemmPlan plan_gemm(int64_t M, int64_t n_cols, int64_t k_contract) {
+  return plan_gemm_grouped(M, &n_cols, 1, k_contract);
+}
 
 // Launches the GEMM (and the split sum when the contraction is split) for
-// C[M, Nc] = A . B with the weight given either as an NF4 tensor (q) or as a
-// dense bf16 matrix (wd).
-static hipError_t launch_gemm(bool backward, const QPtrs* q, const uint16_t* wd, int64_t n_out,
-                              int64_t k_in, const uint8_t* a_packed, int64_t M, uint16_t* out,
-                              const float* lora_l, const float* lora_r, int r, float scale,
-                              void* part_ws, hipStream_t s) {
-  GemmArgs g;
+// C[M, Nc] = A . B with the weight given either as NF4 tensors (q: nseg of
+// them, forward only when nseg > 1) or as a dense bf16 matrix (wd).
+static hipError_t launch_gemm(bool backward, const QPtrs* q, int nseg, const uint16_t* wd,
+                              const int64_t* n_outs, int64_t k_in, const uint8_t* a_packed,
+                              int64_t M, uint16_t* const* outs, const float* const* lora_ls,
+                              const float* const* lora_rs, int r, float scale, void* part_ws,
+                              hipStream_t s) {
+  GemmArgs g = {};
   g.wd = wd;
-  g.packed = q ? q->packed : nullptr;
-  g.q8 = q ? q->q8 : nullptr;
-  g.nested = q ? q->nested : nullptr;
-  g.offset = q ? q->offset : nullptr;
   g.M = M;
-  g.Kc = backward ? n_out : k_in;
-  g.Nc = backward ? k_in : n_out;
-  g.n_out = n_out;
   g.k_in = k_in;
-  g.out = out;
-  const GemmPlan p = plan_gemm(M, g.Nc, g.Kc);
+  g.Kc = backward ? n_outs[0] : k_in;
+  g.Nc = backward ? k_in : n_outs[0];
+  g.n_out = n_outs[0];
+  int64_t ncols[GEMM_MAX_SEG];
+  for (int i = 0; i < nseg; ++i) ncols[i] = backward ? k_in : n_outs[i];
+  const GemmPlan p = plan_gemm_grouped(M, ncols, nseg, g.Kc);
   g.afrag = a_packed;
   g.kblocks = (g.Kc + BK - 1) / BK * (BK / 16);
-  g.part = p.splits > 1 ? static_cast<float*>(part_ws) : nullptr;
   g.kc_chunk = p.kc_chunk;
-  g.lora_l = lora_l;
-  g.lora_r = lora_r;
   g.r = r;
   g.scale = scale;
-  const dim3 grid((unsigned)((g.Nc + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)p.splits);
+  g.nseg = nseg;
+  SumSegs sum = {};
+  int tile0 = 0;
+  int64_t max_n = 0;
+  uint8_t* part = static_cast<uint8_t*>(part_ws);
+  for (int i = 0; i < nseg; ++i) {
+    GemmSeg& sg = g.seg[i];
+    if (q) {
+      sg.packed = q[i].packed;
+      sg.q8 = q[i].q8;
+      sg.nested = q[i].nested;
+      sg.offset = q[i].offset;
+    }
+    sg.out = outs[i];
+    sg.lora_l = lora_ls ? lora_ls[i] : nullptr;
+    sg.lora_r = lora_rs ? lora_rs[i] : nullptr;
+    sg.n_out = n_outs[i];
+    sg.tile0 = tile0;
+    tile0 += (int)((ncols[i] + BN - 1) / BN);
+    const int64_t n = M * ncols[i];
+    if (p.splits > 1) {
+      sg.part = reinterpret_cast<float*>(part);
+      part += round256((size_t)p.splits * (size_t)n * sizeof(float));
+    }
+    sum.part[i] = sg.part;
+    sum.out[i] = sg.out;
+    sum.n[i] = n;
+    max_n = n > max_n ? n : max_n;
+  }
+  const dim3 grid((unsigned)tile0, (unsigned)((M + BM - 1) / BM), (unsigned)p.splits);
   const bool split = p.splits > 1;
   const Tables& tab = host_tables();
 #define NF4S_GEMM(B_, S_, D_) hipLaunchKernelGGL((k_gemm<B_, S_, D_>), grid, dim3(THREADS), 0, s, g, tab)
@@ -838,9 +916,8 @@ static hipError_t launch_gemm(bool backward, const QPtrs* q, const uint16_t* wd,
 #undef NF4S_GEMM
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  const int64_t n = M * g.Nc;
-  const dim3 g2((unsigned)((n / 4 + 1 + 255) / 256));
-  hipLaunchKernelGGL(k_split_sum, g2, dim3(256), 0, s, g.part, p.splits, n, out);
+  const dim3 g2((unsigned)((max_n / 4 + 1 + 255) / 256), (unsigned)nseg);
+  hipLaunchKernelGGL(k_split_sum, g2, dim3(256), 0, s, sum, p.splits);
   return hipGetLastError();
 }
 
@@ -848,15 +925,23 @@ hipError_t launch_linear_packed(bool backward, const QPtrs& q, int64_t n_out, in
                                 const uint8_t* a_packed, int64_t M, uint16_t* out,
                                 const float* lora_l, const float* lora_r, int r, float scale,
                                 void* part_ws, hipStream_t s) {
-  return launch_gemm(backward, &q, nullptr, n_out, k_in, a_packed, M, out, lora_l, lora_r, r, scale,
-                     part_ws, s);
+  return launch_gemm(backward, &q, 1, nullptr, &n_out, k_in, a_packed, M, &out, &lora_l, &lora_r, r,
+                     scale, part_ws, s);
+}
+
+hipError_t launch_linear_grouped_fwd(const QPtrs* q, int nseg, const int64_t* n_outs, int64_t k_in,
+                                     const uint8_t* x_packed, int64_t M, uint16_t* const* ys,
+                                     const float* const* lora_us, const float* const* lora_Bs,
+                                     int r, float scale, void* part_ws, hipStream_t s) {
+  return launch_gemm(false, q, nseg, nullptr, n_outs, k_in, x_packed, M, ys, lora_us, lora_Bs, r,
+                     scale, part_ws, s);
 }
 
 hipError_t launch_dense_packed(bool backward, const uint16_t* w, int64_t n_out, int64_t k_in,
                                const uint8_t* a_packed, int64_t M, uint16_t* out, void* part_ws,
                                hipStream_t s) {
-  return launch_gemm(backward, nullptr, w, n_out, k_in, a_packed, M, out, nullptr, nullptr, 0, 0.0f,
-                     part_ws, s);
+  return launch_gemm(backward, nullptr, 1, w, &n_out, k_in, a_packed, M, &out, nullptr, nullptr, 0,
+                     0.0f, part_ws, s);
 }
 
 }  // namespace nf4s

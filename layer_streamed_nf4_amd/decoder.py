@@ -36,7 +36,8 @@ from . import (OP_ATTENTION_BWD, OP_CROSS_ENTROPY, OP_DENSE_BWD_PACKED, OP_DENSE
                nf4s_pool_create, nf4s_pool_destroy, nf4s_pool_prefetch, nf4s_pool_release,
                nf4s_pool_set_layer, nf4s_pool_stats, nf4s_residual_add, nf4s_rmsnorm_bwd,
                nf4s_rmsnorm_fwd, nf4s_rope, nf4s_swiglu_bwd, nf4s_swiglu_fwd, nf4s_to_bf16,
-               nf4s_workspace_bytes, streamed_linear_bwd_packed, streamed_linear_fwd_packed)
+               nf4s_workspace_bytes, streamed_linear_bwd_packed, streamed_linear_fwd_packed,
+               streamed_linear_fwd_grouped, grouped_workspace_bytes)
 from .stack import ALIGN, PROJ, ShardSet, _round_up
 
 BF16 = torch.int16  # bf16 tensors travel as their bit patterns
@@ -61,12 +62,11 @@ class Decoder:
         """time_calls: optional predicate (direction, n_out, k_in) -> bool; the
         streamed linear forward calls it accepts are bracketed by timing
         events on the compute stream, collected in self.timed as
-        (direction, n_out, k_in, start, end, launches) -- launches = 2 when
-        one bracket spans the gate and up GEMMs."""
+        (direction, n_out, k_in, start, end, launches); a grouped launch
+        (q, k, v; gate, up) is one entry whose n_out is the group's total."""
         assert mode in ("streamed", "resident")
         self.time_calls = time_calls
         self.timed = []
-        self._open = None
         dev = "cuda"
         self.cfg = cfg
         self.sh = shards
@@ -159,6 +159,8 @@ class Decoder:
                      nf4s_workspace_bytes(OP_LORA_FWD, M, no, ki),
                      nf4s_workspace_bytes(OP_LORA_BWD, M, no, ki))
             pk = max(pk, nf4s_packed_activation_bytes(M, ki), nf4s_packed_activation_bytes(M, no))
+        for grp in (("q", "k", "v"), ("gate", "up")):
+            ws = max(ws, grouped_workspace_bytes([shapes[p][0] for p in grp], shapes[grp[0]][1], M))
         self.ws = torch.empty(_round_up(max(ws, ALIGN)), dtype=torch.uint8, device=dev)
         self.packed = torch.empty(_round_up(pk), dtype=torch.uint8, device=dev)
         self._packed_key = None
@@ -201,27 +203,34 @@ class Decoder:
             self._packed_key = key
         return self.packed.data_ptr()
 
-    def _fwd(self, base, i, p, x, y, adapters=True, span=None):
-        """span: None times this GEMM alone (if time_calls accepts it); "open"
-        starts a bracket that the next call with span="close" ends, timing two
-        back-to-back GEMM launches with one pair of events."""
-        no, ki = self.sh.shapes[p]
+    def _fwd(self, base, i, ps, x, ys, adapters=True):
+        """Forward of the projections ps, all reading x (q, k, v or gate, up,
+        or a single one), as one GEMM launch writing ys; each launch the
+        time_calls predicate accepts is one timed entry with n_out the sum."""
+        ki = self.sh.shapes[ps[0]][1]
         xp = self._pack(x, ki)
-        d = self.sh.layout.descs[p]
-        if adapters and p in self.targets:
-            A, Bm = self.lora[(i, p)]
-            lora_fwd(x.data_ptr(), self.M, ki, A.data_ptr(), self.r, self.u[p].data_ptr(), *self._ws(),
-                     self._s)
-            lora = (self.u[p].data_ptr(), Bm.data_ptr(), self.r, self.scale)
+        us, Bs = [], []
+        for p in ps:
+            if adapters and p in self.targets:
+                A, Bm = self.lora[(i, p)]
+                lora_fwd(x.data_ptr(), self.M, ki, A.data_ptr(), self.r, self.u[p].data_ptr(),
+                         *self._ws(), self._s)
+                us.append(self.u[p].data_ptr())
+                Bs.append(Bm.data_ptr())
+            else:
+                us.append(None)
+                Bs.append(None)
+        r = self.r if any(us) else 0
+        scale = self.scale if any(us) else 0.0
+        ev = self._tick("fwd", sum(self.sh.shapes[p][0] for p in ps), ki)
+        if len(ps) == 1:
+            streamed_linear_fwd_packed(base, self.sh.layout.descs[ps[0]], xp, self.M, ys[0].data_ptr(),
+                                       us[0], Bs[0], r, scale, *self._ws(), self._s)
         else:
-            lora = (None, None, 0, 0.0)
-        ev = self._open if span == "close" else self._tick("fwd", no, ki)
-        streamed_linear_fwd_packed(base, d, xp, self.M, y.data_ptr(), *lora, *self._ws(), self._s)
-        if span == "open":
-            self._open = ev
-        else:
-            self._tock(ev, launches=2 if span == "close" else 1)
-            self._open = None
+            streamed_linear_fwd_grouped(base, [self.sh.layout.descs[p] for p in ps], xp, self.M,
+                                        [y.data_ptr() for y in ys], us, Bs, r, scale, *self._ws(),
+                                        self._s)
+        self._tock(ev)
 
     def _tick(self, direction, n, k):
         if self.time_calls is None or not self.time_calls(direction, n, k):
@@ -266,25 +275,19 @@ class Decoder:
         a = adapters
         nf4s_rmsnorm_fwd(hin.data_ptr(), self.norms["attn"][i].data_ptr(), M, H, c["eps"],
                          self.n1.data_ptr(), self.rstd1.data_ptr(), s)
-        self._fwd(base, i, "q", self.n1, self.q, a)
-        self._fwd(base, i, "k", self.n1, self.k, a)
-        self._fwd(base, i, "v", self.n1, self.vv, a)
+        self._fwd(base, i, ("q", "k", "v"), self.n1, (self.q, self.k, self.vv), a)
         nf4s_rope(self.q.data_ptr(), M, self.S, c["heads"], c["head_dim"], c["rope_theta"], 0, s)
         nf4s_rope(self.k.data_ptr(), M, self.S, c["kv_heads"], c["head_dim"], c["rope_theta"], 0, s)
         nf4s_attention_fwd(self.q.data_ptr(), self.k.data_ptr(), self.vv.data_ptr(), self.B, self.S,
                            c["heads"], c["kv_heads"], c["head_dim"], self.o.data_ptr(),
                            self.o32.data_ptr() if recompute else None, self.lse.data_ptr(), s)
-        self._fwd(base, i, "o", self.o, self.ao, a)
+        self._fwd(base, i, ("o",), self.o, (self.ao,), a)
         nf4s_residual_add(hin.data_ptr(), self.ao.data_ptr(), M * H, self.h_mid.data_ptr(), s)
         nf4s_rmsnorm_fwd(self.h_mid.data_ptr(), self.norms["mlp"][i].data_ptr(), M, H, c["eps"],
                          self.n2.data_ptr(), self.rstd2.data_ptr(), s)
-        # gate and up read the same input back to back: one timing bracket
-        # spans both GEMMs when neither carries an adapter
-        pair = not (a and ("gate" in self.targets or "up" in self.targets))
-        self._fwd(base, i, "gate", self.n2, self.g, a, span="open" if pair else None)
-        self._fwd(base, i, "up", self.n2, self.u_, a, span="close" if pair else None)
+        self._fwd(base, i, ("gate", "up"), self.n2, (self.g, self.u_), a)
         nf4s_swiglu_fwd(self.g.data_ptr(), self.u_.data_ptr(), M * self.I, self.sw.data_ptr(), s)
-        self._fwd(base, i, "down", self.sw, self.dn, a)
+        self._fwd(base, i, ("down",), self.sw, (self.dn,), a)
         if not recompute:
             nf4s_residual_add(self.h_mid.data_ptr(), self.dn.data_ptr(), M * H, hout.data_ptr(), s)
 

@@ -270,3 +270,42 @@ def test_decoder_workspace_sizes():
         L.nf4s_workspace_bytes(L.OP_ATTENTION_BWD, 0, 32, 128)
     with pytest.raises(L.Nf4sError):
         L.nf4s_workspace_bytes(L.OP_ATTENTION_BWD, 512, 32, 16)
+
+
+def test_grouped_forward_workspace():
+    # q, k, v of the 8B layer at M = 512: 2 x 48 tiles, the contraction split
+    # in two, partials for all three outputs
+    assert L.grouped_workspace_bytes([4096, 1024, 1024], 4096, 512) == 2 * 512 * 6144 * 4
+    # gate and up: 2 x 224 tiles fill the chip, no split, no scratch
+    assert L.grouped_workspace_bytes([14336, 14336], 4096, 512) == 0
+    # a group of one plans like the single call
+    assert L.grouped_workspace_bytes([4096], 4096, 512) == \
+        L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, 512, 4096, 4096)
+    assert _err(L.grouped_workspace_bytes, [64] * 4, 64, 16) == L.EINVAL
+    assert _err(L.grouped_workspace_bytes, [], 64, 16) == L.EINVAL
+    assert _err(L.grouped_workspace_bytes, [64, 60], 64, 16) == L.ESHAPE
+    assert _err(L.grouped_workspace_bytes, [64, 64], 64, 0) == L.ESHAPE
+
+
+def test_grouped_forward_argument_errors():
+    d = [L.nf4s_tensor_layout(64, 128, 0)]
+    d.append(L.nf4s_tensor_layout(32, 128, d[0].end))
+    fwd = L.streamed_linear_fwd_grouped
+    ys = [FAKE, FAKE]
+    # only error paths: every call below is refused before any launch
+    assert _err(fwd, FAKE, [d[0]] * 4, FAKE, 16, [FAKE] * 4, None, None, 0, 0.0, None, 0) == L.EINVAL
+    other = L.nf4s_tensor_layout(64, 64, d[1].end)
+    assert _err(fwd, FAKE, [d[0], other], FAKE, 16, ys, None, None, 0, 0.0, None, 0) == L.ESHAPE
+    assert _err(fwd, FAKE, d, FAKE, 16, ys, [FAKE, None], [None, None], 16, 2.0, None, 0) == L.EINVAL
+    assert _err(fwd, FAKE, d, FAKE, 16, ys, [FAKE, None], [FAKE, None], 0, 2.0, None, 0) == L.EINVAL
+    assert _err(fwd, FAKE, d, FAKE + 16, 16, ys, None, None, 0, 0.0, None, 0) == L.EALIGN
+    assert _err(fwd, FAKE, d, FAKE, 16, [FAKE, FAKE + 2], None, None, 0, 0.0, None, 0) == L.EALIGN
+    assert _err(fwd, FAKE, d, FAKE, 0, ys, None, None, 0, 0.0, None, 0) == L.ESHAPE
+    bad = L.nf4s_tensor_layout(32, 128, d[0].end)
+    bad.table_hash ^= 1
+    assert _err(fwd, FAKE, [d[0], bad], FAKE, 16, ys, None, None, 0, 0.0, None, 0) == L.ETABLE
+    # q, k, v at 8B widths and M = 512 split the contraction: workspace required
+    q = [L.nf4s_tensor_layout(4096, 4096, 0)]
+    q.append(L.nf4s_tensor_layout(1024, 4096, q[0].end))
+    q.append(L.nf4s_tensor_layout(1024, 4096, q[1].end))
+    assert _err(fwd, FAKE, q, FAKE, 512, [FAKE] * 3, None, None, 0, 0.0, FAKE, 1024) == L.EWORKSPACE

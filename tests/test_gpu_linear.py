@@ -219,3 +219,122 @@ def test_packed_calls_match_unpacked(proj, n, k, M, lora):
     torch.cuda.synchronize()
     assert np.array_equal(host_u16(y), np.asarray(ref["y"], dtype=np.float32).view(np.uint32) >> 16)
     assert np.array_equal(host_u16(dx), np.asarray(ref["dx"], dtype=np.float32).view(np.uint32) >> 16)
+
+
+def _group_setup(projs, ns, k, M, lora_on, layer=0, step=0):
+    """One device shard holding the NF4 form of each weight of the group."""
+    descs, end = [], 0
+    for n in ns:
+        descs.append(L.nf4s_tensor_layout(n, k, end))
+        end = descs[-1].end
+    shard = torch.zeros(end, dtype=torch.uint8, device="cuda")
+    s = stream()
+    ws_ = []
+    parts = []
+    for p, n, d in zip(projs, ns, descs):
+        w = synth.weight(layer, p, n, k)
+        wsq = ws_tensor(L.nf4s_workspace_bytes(L.OP_QUANTIZE, 0, n, k))
+        wd = dev_f32(w)
+        L.nf4_quantize_shard(wd.data_ptr(), L.DTYPE_F32, n, k, shard.data_ptr(), d, None,
+                             wsq.data_ptr(), wsq.numel(), s)
+        ws_.append((wsq, wd))
+        a, b = synth.lora_pair(layer, p, n, k)
+        parts.append(dict(w=w, a=a, b=b, n=n, lora=p in lora_on))
+    torch.cuda.synchronize()
+    x = synth.activation((M, k), step, 0)
+    return dict(shard=shard, descs=descs, parts=parts, x=x, k=k, M=M)
+
+
+def _group_run(c, grouped):
+    """The group's outputs from one grouped launch, or from one
+    streamed_linear_fwd_packed call per weight (same packed input, same u)."""
+    k, M = c["k"], c["M"]
+    s = stream()
+    x = dev_bf16bits(c["x"])
+    xp = ws_tensor(L.nf4s_packed_activation_bytes(M, k))
+    L.nf4s_pack_activation(x.data_ptr(), M, k, xp.data_ptr(), xp.numel(), s)
+    wsl = ws_tensor(L.nf4s_workspace_bytes(L.OP_LORA_FWD, M, 64, k))
+    ys, us, Bs, keep = [], [], [], []
+    for part in c["parts"]:
+        ys.append(torch.empty((M, part["n"]), dtype=torch.int16, device="cuda"))
+        if part["lora"]:
+            A, B = dev_f32(part["a"]), dev_f32(part["b"])
+            u = torch.empty((M, R), dtype=torch.float32, device="cuda")
+            L.lora_fwd(x.data_ptr(), M, k, A.data_ptr(), R, u.data_ptr(), wsl.data_ptr(), wsl.numel(), s)
+            keep += [A, B, u]
+            us.append(u.data_ptr())
+            Bs.append(B.data_ptr())
+        else:
+            us.append(None)
+            Bs.append(None)
+    any_lora = any(us)
+    r, sc = (R, S) if any_lora else (0, 0.0)
+    sp = c["shard"].data_ptr()
+    if grouped:
+        ws = ws_tensor(L.grouped_workspace_bytes([p["n"] for p in c["parts"]], k, M))
+        L.streamed_linear_fwd_grouped(sp, c["descs"], xp.data_ptr(), M, [y.data_ptr() for y in ys],
+                                      us, Bs, r, sc, ws.data_ptr(), ws.numel(), s)
+    else:
+        for d, y, u, B in zip(c["descs"], ys, us, Bs):
+            ws = ws_tensor(L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, M, d.n_out, k))
+            L.streamed_linear_fwd_packed(sp, d, xp.data_ptr(), M, y.data_ptr(), u, B,
+                                         R if u else 0, S if u else 0.0, ws.data_ptr(), ws.numel(), s)
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return [host_u16(y) for y in ys]
+
+
+GROUPS = [
+    # (projections, n_outs, k_in, M, adapters on): 135M q/k/v with q, v
+    # adapters and a ragged M; 135M gate/up; three ragged narrow weights
+    (("q", "k", "v"), (576, 192, 192), 576, 300, ("q", "v")),
+    (("gate", "up"), (1536, 1536), 576, 512, ()),
+    (("q", "k", "v"), (72, 40, 136), 128, 37, ("k",)),
+    (("o",), (576,), 576, 1, ("o",)),
+]
+
+
+@pytest.mark.parametrize("projs,ns,k,M,lora_on", GROUPS)
+def test_grouped_forward_matches_oracle(projs, ns, k, M, lora_on):
+    print(f"grouped {projs} {ns}x{k} M={M} lora={lora_on}", flush=True)
+    c = _group_setup(projs, ns, k, M, lora_on)
+    got = _group_run(c, grouped=True)
+    x = bits_to_f32(c["x"])
+    for part, y in zip(c["parts"], got):
+        wq = bits_to_f32(nf4.dequantize_bf16(nf4.quantize(part["w"]))).astype(np.float64)
+        a, b, s = (part["a"], part["b"], S) if part["lora"] else (None, None, 0.0)
+        y_ref, _ = linear.forward(x, wq, a, b, s)
+        assert linear.rel_err(bits_to_f32(y), y_ref) <= TOL
+
+
+@pytest.mark.parametrize("projs,ns,k,M,lora_on", [
+    (("gate", "up"), (1536, 1536), 576, 512, ("up",)),
+    (("gate", "up"), (14336, 14336), 4096, 512, ()),
+])
+def test_grouped_forward_bit_identical_when_split_matches(projs, ns, k, M, lora_on):
+    """When the group's plan keeps each weight's split count (here: no split
+    alone or grouped), every output tile is contracted in the same order as by
+    the single call, so the bits agree."""
+    splits_single = [L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, M, n, k) for n in ns]
+    assert splits_single == [0] * len(ns) and L.grouped_workspace_bytes(list(ns), k, M) == 0
+    c = _group_setup(projs, ns, k, M, lora_on)
+    g, single = _group_run(c, True), _group_run(c, False)
+    for a, b in zip(g, single):
+        assert np.array_equal(a, b)
+
+
+def test_grouped_forward_8b_qkv_close_to_single_calls():
+    """q, k, v at 8B widths, M = 512 (the decoder step's launch): the group
+    splits the contraction in two where the single calls split it in four and
+    eight, so outputs agree to bf16 rounding of differently ordered fp32 sums;
+    the single calls are checked against the oracle at these shapes."""
+    c = _group_setup(("q", "k", "v"), (4096, 1024, 1024), 4096, 512, ("q", "v"))
+    g, single = _group_run(c, True), _group_run(c, False)
+    for a, b in zip(g, single):
+        fa, fb = bits_to_f32(a).astype(np.float64), bits_to_f32(b).astype(np.float64)
+        assert np.max(np.abs(fa - fb)) <= 2.0 ** -7 * np.max(np.abs(fb))
+        # one bf16 step apart at most, except where cancellation leaves a
+        # result far below the size of its terms
+        ia, ib = a.astype(np.int32), b.astype(np.int32)
+        far = (np.abs(ia - ib) > 1) & (np.abs(fb) > 2.0 ** -6 * np.max(np.abs(fb)))
+        assert np.count_nonzero(far) == 0

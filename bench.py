@@ -481,7 +481,7 @@ def main():
     grads = lambda i, p: dys[p]
 
     # dominant kernel: the forward fused GEMM on shapes that need no split
-    # (gate/up at 8B): one streamed_linear_fwd_packed call = one k_gemm<fwd,plain> launch
+    # (gate/up at 8B): one call = one k_gemm_fwd launch
     def plain_fwd(direction, n, k):
         return direction == "fwd" and L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, M, n, k) == 0
 
@@ -642,8 +642,8 @@ def main():
                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                     "traffic": traffic_from_profile(gemm_source_hash(), dom_spec),
                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-scaled)",
-                    "kernel": "k_gemm<fwd,plain> (fused NF4 dequant + bf16 MFMA, x.W'^T)"
-                              + ("; one grouped launch = gate and up" if use_decoder else ""),
+                    "kernel": "k_gemm_fwd (fused NF4 dequant + bf16 MFMA, x.W'^T, 512x128 tiles, "
+                              "no split)" + ("; one grouped launch = gate and up" if use_decoder else ""),
                     "spec": dom_spec,
                     "launches": len(dom_ms), "avg_us": round(avg_ms * 1e3, 2),
                     "flop_per_launch": int(avg_flop)}

@@ -190,7 +190,8 @@ int nf4s_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, size_t*
       if (M <= 0) return fail(NF4S_ESHAPE, "M=%lld must be positive", (long long)M);
       const bool bwd = op == NF4S_OP_LINEAR_BWD || op == NF4S_OP_LINEAR_BWD_PACKED ||
                        op == NF4S_OP_DENSE_BWD_PACKED;
-      const GemmPlan p = plan_gemm(M, bwd ? k_in : n_out, bwd ? n_out : k_in);
+      const bool dense = op == NF4S_OP_DENSE_FWD_PACKED || op == NF4S_OP_DENSE_BWD_PACKED;
+      const GemmPlan p = plan_gemm(M, bwd ? k_in : n_out, bwd ? n_out : k_in, !bwd && !dense);
       const bool packed = op != NF4S_OP_LINEAR_FWD && op != NF4S_OP_LINEAR_BWD;
       *bytes = packed ? p.part_bytes : p.ws_bytes;
       return NF4S_OK;
@@ -272,7 +273,7 @@ static int linear_checks(bool bwd, const void* shard_dev, const nf4s_tensor_desc
     if ((rc = check_ptr(lora_r, bwd ? "lora_A" : "lora_B", 4))) return rc;
     if (!std::isfinite(scale)) return fail(NF4S_EINVAL, "scale is not finite");
   }
-  *plan = plan_gemm(M, bwd ? d->k_in : d->n_out, bwd ? d->n_out : d->k_in);
+  *plan = plan_gemm(M, bwd ? d->k_in : d->n_out, bwd ? d->n_out : d->k_in, !bwd);
   return NF4S_OK;
 }
 
@@ -379,7 +380,7 @@ int nf4s_grouped_workspace_bytes(int n, const int64_t* n_outs, int64_t k_in, int
   if (!bytes) return fail(NF4S_EINVAL, "bytes is NULL");
   int rc;
   if ((rc = check_group(n, n_outs, k_in, M))) return rc;
-  *bytes = plan_gemm_grouped(M, n_outs, n, k_in).part_bytes;
+  *bytes = plan_gemm_grouped(M, n_outs, n, k_in, true).part_bytes;
   return NF4S_OK;
 }
 
@@ -423,7 +424,7 @@ int streamed_linear_fwd_grouped(const void* shard_dev, const nf4s_tensor_desc* d
   }
   if ((rc = check_ptr(shard_dev, "shard_dev", 256))) return rc;
   if ((rc = check_ptr(x_packed, "x_packed", 256))) return rc;
-  const GemmPlan p = plan_gemm_grouped(M, n_outs, n, k_in);
+  const GemmPlan p = plan_gemm_grouped(M, n_outs, n, k_in, true);
   if (p.part_bytes && (rc = check_ws(ws, ws_bytes, p.part_bytes))) return rc;
   for (int i = 0; i < n; ++i) q[i] = resolve(shard_dev, &descs[i]);
   hipError_t e = launch_linear_grouped_fwd(q, n, n_outs, k_in, static_cast<const uint8_t*>(x_packed),
@@ -503,7 +504,7 @@ static int dense_common(bool bwd, const uint16_t* w, int64_t n_out, int64_t k_in
   if ((rc = check_ptr(w, "w"))) return rc;
   if ((rc = check_ptr(a_packed, bwd ? "dy_packed" : "x_packed", 256))) return rc;
   if ((rc = check_ptr(out, bwd ? "dx" : "y"))) return rc;
-  const GemmPlan p = plan_gemm(M, bwd ? k_in : n_out, bwd ? n_out : k_in);
+  const GemmPlan p = plan_gemm(M, bwd ? k_in : n_out, bwd ? n_out : k_in, false);
   if (p.part_bytes && (rc = check_ws(ws, ws_bytes, p.part_bytes))) return rc;
   hipError_t e = launch_dense_packed(bwd, w, n_out, k_in, static_cast<const uint8_t*>(a_packed), M,
                                      out, ws, static_cast<hipStream_t>(stream));

@@ -53,9 +53,11 @@ struct GemmPlan {
   size_t part_bytes;  // fp32 partials when splits > 1
   size_t ws_bytes;    // frag_bytes + part_bytes
 };
-GemmPlan plan_gemm(int64_t M, int64_t n_cols, int64_t k_contract);
+// fwd_nf4: the forward NF4 kernel (512-row tiles); else k_gemm (256-row tiles).
+GemmPlan plan_gemm(int64_t M, int64_t n_cols, int64_t k_contract, bool fwd_nf4);
 // The same for a grouped forward of nseg weights of n_cols[i] outputs.
-GemmPlan plan_gemm_grouped(int64_t M, const int64_t* n_cols, int nseg, int64_t k_contract);
+GemmPlan plan_gemm_grouped(int64_t M, const int64_t* n_cols, int nseg, int64_t k_contract,
+                           bool fwd_nf4);
 size_t packed_activation_bytes(int64_t M, int64_t K);
 
 // Kernel launchers (return hipError_t of the launch).

@@ -458,11 +458,35 @@ __device__ __forceinline__ bf16x8_t f32x8_to_bf16(const float* v) {
 // swaps the NF4 producer for the plain bf16 one.
 template <bool BWD, bool SPLIT, bool DENSE>
 __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
+  // Tile order. Workgroups are dispatched in flattened-id order and dealt to
+  // the 8 XCDs round-robin; each XCD has its own L2. NF4 weights stream at
+  // 0.52 B per weight, an eighth of the activation bytes a tile reads, so the
+  // launch order is kept: the workgroups running together share one row
+  // tile of the activation in L2. A dense bf16 weight is 4x heavier and the
+  // lm_head grid spans many waves, so there ids are mapped to put all row
+  // tiles of a column tile on one XCD at the same time (ids ct%8 + 8*rt in a
+  // block of 8*R ids) and each weight tile leaves HBM once.
+  const int C = (int)gridDim.x, R = (int)gridDim.y;
+  const int id = (int)blockIdx.x + C * (int)blockIdx.y;
+  const int full = C / 8 * 8;
+  int ct, rt;
+  if (!DENSE) {
+    ct = (int)blockIdx.x;
+    rt = (int)blockIdx.y;
+  } else if (id < full * R) {
+    const int w = id % (8 * R);
+    ct = id / (8 * R) * 8 + w % 8;
+    rt = w / 8;
+  } else {
+    const int j = id - full * R;
+    ct = full + j / R;
+    rt = j % R;
+  }
   // the weight this workgroup's column tile belongs to (uniform per workgroup)
   int sgi = 0;
 #pragma unroll
   for (int q = 1; q < GEMM_MAX_SEG; ++q)
-    if (q < ga.nseg && (int)blockIdx.x >= ga.seg[q].tile0) sgi = q;
+    if (q < ga.nseg && ct >= ga.seg[q].tile0) sgi = q;
   GemmArgs g = ga;
   g.packed = ga.seg[sgi].packed;
   g.q8 = ga.seg[sgi].q8;
@@ -487,11 +511,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
     s_c8[t] = tab.c8[t];
   }
 
-  // Default launch order: the workgroups are dealt to the 8 XCDs round-robin,
-  // so both 256-row tiles of an output column block land on the same XCD and
-  // share its weight stream in L2.
-  const int64_t n0 = (int64_t)((int)blockIdx.x - ga.seg[sgi].tile0) * BN;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
+  const int64_t n0 = (int64_t)(ct - ga.seg[sgi].tile0) * BN;
+  const int64_t m0 = (int64_t)rt * BM;
   const int split = blockIdx.z;
   const int64_t kb = split * g.kc_chunk;
   const int64_t ke = (kb + g.kc_chunk < g.Kc) ? kb + g.kc_chunk : g.Kc;
@@ -779,6 +800,298 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
   }
 }
 
+// ---- forward kernel: one wave per SIMD ------------------------------------
+// The forward orientation (x . W'^T, NF4 weight) runs on a second design that
+// gives each wave the whole matrix-core register budget: 256 threads = 4
+// waves, one per SIMD, each owning 128 output rows x 128 columns (4x4 MFMA
+// tiles, 256 fp32 accumulators per lane in the accumulation registers); the
+// workgroup tile is 512 rows x 128 columns, so every decoded weight tile
+// feeds twice the rows of k_gemm and each wave reads half the LDS bytes per
+// MFMA. Every wave also decodes its quarter of the weight tile; that work is
+// placed between the MFMAs in a fixed order (one scheduling barrier per
+// MFMA) so it runs while the matrix pipe is busy:
+//  * sub-step g of step s: 16 MFMAs; after the first four, the B fragments
+//    of the next sub-step (or of the next stage's sub-step 0) are read; after
+//    every fourth, one activation fragment is refilled for step s+2;
+//  * sub-step 0 issues the pair-table lookups of stage s+2, sub-step 1 does
+//    its arithmetic, sub-step 2 stores it, sub-step 3 fetches the packed
+//    codes of step s+4;
+//  * three LDS stages: stage s+1 is complete at the barrier that ends step
+//    s-1, so its first fragments are read before the barrier of step s;
+//  * the packed codes of even and odd steps live in two register sets that
+//    are never copied (a copy of a value still in flight would wait for every
+//    older load).
+// The decode and the contraction order per output element are those of
+// k_gemm: results are bit-identical for the same split of the contraction.
+constexpr int FBM = 512;
+constexpr int FTHREADS = 256;
+constexpr int FNST = 3;
+constexpr int F_SMEM_BYTES = FNST * STAGE_ELEMS * 2 + 256 * PAIR_COPIES * 8 + 256 * 4;
+
+struct FSlot {
+  u32x4 w;     // 32 packed codes of the thread's weight row half
+  uint32_t q;  // 8-bit scale code of the row's 64-block
+  float nest;  // nested scale of that block
+};
+
+__global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables tab) {
+  const int ct = (int)blockIdx.x;
+  int sgi = 0;
+#pragma unroll
+  for (int q = 1; q < GEMM_MAX_SEG; ++q)
+    if (q < ga.nseg && ct >= ga.seg[q].tile0) sgi = q;
+  const uint8_t* const packed = ga.seg[sgi].packed;
+  const uint8_t* const q8 = ga.seg[sgi].q8;
+  const float* const nested = ga.seg[sgi].nested;
+  const float off = ga.seg[sgi].offset[0];
+  const int64_t n_out = ga.seg[sgi].n_out;
+  const int64_t n0 = (int64_t)(ct - ga.seg[sgi].tile0) * BN;
+  const int64_t m0 = (int64_t)blockIdx.y * FBM;
+  const int split = blockIdx.z;
+  const int64_t M = ga.M, k_in = ga.k_in;
+  const int64_t kb = split * ga.kc_chunk;
+  const int64_t ke = (kb + ga.kc_chunk < ga.Kc) ? kb + ga.kc_chunk : ga.Kc;
+  const int nk = (int)((ke - kb + BK - 1) / BK);
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[F_SMEM_BYTES];
+  uint16_t* const Bs0 = reinterpret_cast<uint16_t*>(smem);
+  float2* const s_pair_all = reinterpret_cast<float2*>(smem + FNST * STAGE_ELEMS * 2);
+  float* const s_c8 = reinterpret_cast<float*>(smem + FNST * STAGE_ELEMS * 2 + 256 * PAIR_COPIES * 8);
+  const int t = threadIdx.x;
+  {
+    const float2 e = make_float2(tab.c4[t >> 4], tab.c4[t & 15]);
+#pragma unroll
+    for (int c = 0; c < PAIR_COPIES; ++c) s_pair_all[t * PAIR_COPIES + c] = e;
+    s_c8[t] = tab.c8[t];
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
+  const int lrow = lane & 31;
+  const int lk = (lane >> 5) * 8;
+  auto stage = [&](int st) { return Bs0 + st * STAGE_ELEMS; };
+
+  // activation fragments: the rows of a wave past the packed activation (a
+  // last tile of fewer than 512 rows) re-read its last 32-row block; those
+  // rows are never stored
+  const __amdgpu_buffer_rsrc_t ar =
+      __builtin_amdgcn_make_buffer_rsrc((void*)ga.afrag, (short)0, (int)0xFFFFFFFFu, 0x00020000);
+  const int64_t nblk = (M + PACK_ROWS - 1) / PACK_ROWS * (PACK_ROWS / 32);
+  uint32_t aoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int64_t b = (m0 + wave * 128 + i * 32) / 32;
+    b = b < nblk ? b : nblk - 1;
+    aoff[i] = (uint32_t)(b * ga.kblocks * FRAG_BYTES + lane * 16);
+  }
+  // contraction step k (clamped to the last one) -> activation byte offset of its sub-step 0
+  auto a_soff = [&](int k) {
+    const int kc = k < nk ? k : nk - 1;
+    return (int)(((kb + (int64_t)kc * BK) / 16) * FRAG_BYTES);
+  };
+
+  // weights: thread t owns row n0 + t/2 (clamped; scale forced to 0 past
+  // n_out) and the contraction half t%2 of every step
+  int64_t wrow = n0 + (t >> 1);
+  const bool valid = wrow < n_out;
+  wrow = valid ? wrow : n_out - 1;
+  const __amdgpu_buffer_rsrc_t wr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)packed, (short)0, (int)0xFFFFFFFFu, 0x00020000);
+  const __amdgpu_buffer_rsrc_t qr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)q8, (short)0, (int)0xFFFFFFFFu, 0x00020000);
+  const __amdgpu_buffer_rsrc_t nr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)nested, (short)0, (int)0xFFFFFFFFu, 0x00020000);
+  const uint32_t woff = (uint32_t)(wrow * (k_in / 2) + (t & 1) * 16);
+  const uint32_t blk0 = (uint32_t)(wrow * (k_in / 64));
+  // (all loads of the loop are buffer loads: one return-order class, so the
+  // compiler's wait counts stay exact)
+  auto load_w = [&](int k, FSlot& sl) {
+    const int kc = k < nk ? k : nk - 1;
+    const int64_t k0 = kb + (int64_t)kc * BK;
+    sl.w = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, (int)(k0 / 2), 0);
+    const uint32_t blk = blk0 + (uint32_t)(k0 / 64);
+    sl.q = __builtin_amdgcn_raw_buffer_load_b8(qr, blk, 0, 0);
+    sl.nest = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(nr, (blk >> 8) * 4, 0, 0));
+  };
+  const float2* const ptab = s_pair_all + (t & (PAIR_COPIES - 1));
+  float2 pv[16];
+  float pc, ascale;
+  uint32_t ow[16];
+  auto lookup = [&](const FSlot& sl, int u) { pv[u] = pair_of(ptab, sl.w[u >> 2], u & 3); };
+  auto unit = [&](int u) { ow[u] = pack_bf16x2(__fmul_rn(pv[u].x, ascale), __fmul_rn(pv[u].y, ascale)); };
+  auto store_w = [&](int jw, int st) {
+    u32x4 o;
+    o[0] = ow[jw * 4];
+    o[1] = ow[jw * 4 + 1];
+    o[2] = ow[jw * 4 + 2];
+    o[3] = ow[jw * 4 + 3];
+    *reinterpret_cast<u32x4*>(stage(st) + (t >> 1) * LDS_STRIDE + (t & 1) * 32 + jw * 8) = o;
+  };
+  auto decode_all = [&](const FSlot& sl, int st) {  // prologue: a whole stage at once
+    pc = s_c8[sl.q];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) lookup(sl, u);
+    ascale = valid ? decode_scale(pc, sl.nest, off) : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) unit(u);
+#pragma unroll
+    for (int jw = 0; jw < 4; ++jw) store_w(jw, st);
+  };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // prologue: stages 0 and 1 decoded; then the codes of steps 2 and 3 and
+  // the activation of steps 0 and 1 are issued in the order the loop keeps
+  // (codes before the younger activation loads), so the wait counts the
+  // compiler derives at the loop head hold on both paths into it
+  {
+    FSlot p0, p1;
+    load_w(0, p0);
+    load_w(1, p1);
+    __syncthreads();  // tables in LDS
+    decode_all(p0, 0);
+    decode_all(p1, 1);
+  }
+  FSlot sa, sb;
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(2, sa);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(3, sb);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 A0[4][4], A1[4][4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      A0[i][g] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[i], a_soff(0) + g * FRAG_BYTES, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      A1[i][g] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[i], a_soff(1) + g * FRAG_BYTES, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  __syncthreads();
+  bf16x8_t fb0[4], fb1[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fb0[j] = b_frag<false>(stage(0), lane, j, 0);
+
+  auto step = [&](int s, u32x4 (&A)[4][4], FSlot& sl) {
+    const int st = s % FNST, s1 = (s + 1) % FNST, s2 = (s + 2) % FNST;
+    const int a2 = a_soff(s + 2);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x8_t(&fc)[4] = (g & 1) ? fb1 : fb0;
+      bf16x8_t(&fn)[4] = (g & 1) ? fb0 : fb1;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const int i = m >> 2, j = m & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, A[i][g]), fc[j],
+                                                            acc[i][j], 0, 0, 0);
+        if (m < 4) fn[m] = (g < 3) ? b_frag<false>(stage(st), lane, m, g + 1) : b_frag<false>(stage(s1), lane, m, 0);
+        if (j == 3) A[i][g] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[i], a2 + g * FRAG_BYTES, 0);
+        if (g == 0) {
+          if (m == 4) pc = s_c8[sl.q];
+          if (m >= 4) lookup(sl, m - 4);
+          if (m >= 12) lookup(sl, m);
+        }
+        if (g == 1) {
+          if (m == 0) ascale = valid ? decode_scale(pc, sl.nest, off) : 0.0f;
+          unit(m);
+        }
+        if (g == 2 && (m & 3) == 1) store_w(m >> 2, s2);
+        if (g == 3 && m == 8) load_w(s + 4, sl);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int s = 0;
+  for (; s + 1 < nk; s += 2) {
+    step(s, A0, sa);
+    step(s + 1, A1, sb);
+  }
+  if (s < nk) step(s, A0, sa);
+
+  // LoRA term on the matrix cores, in chunks of 16 over the rank (split 0):
+  // + u[m, :] . (s * B[n, :])
+  if (ga.seg[sgi].lora_l != nullptr && split == 0) {
+    const float* const lu = ga.seg[sgi].lora_l;
+    const float* const lb = ga.seg[sgi].lora_r;
+    for (int r0 = 0; r0 < ga.r; r0 += 16) {
+      bf16x8_t fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = m0 + wave * 128 + i * 32 + lrow;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int rr = r0 + lk + e;
+          v[e] = (row < M && rr < ga.r) ? lu[row * ga.r + rr] : 0.0f;
+        }
+        fa[i] = f32x8_to_bf16(v);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = n0 + j * 32 + lrow;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int rr = r0 + lk + e;
+          v[e] = (col < n_out && rr < ga.r) ? ga.scale * lb[col * ga.r + rr] : 0.0f;
+        }
+        fb[j] = f32x8_to_bf16(v);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // Output through LDS (the ring is free after the last barrier) so that
+  // every global store writes 16 contiguous bytes. Accumulator register r of
+  // lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32 of its 32x32 tile.
+  constexpr int OS = BN + 8;  // bf16 per LDS row; 256 rows (two waves) per pass
+  uint16_t* const ot = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* const out = ga.seg[sgi].out;
+#pragma unroll
+  for (int ph = 0; ph < 2; ++ph) {
+    if ((wave >> 1) == ph) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = j * 32 + lrow;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = (wave & 1) * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            ot[row * OS + col] = (uint16_t)(pack_bf16x2(acc[i][j][r], 0.0f) & 0xFFFFu);
+          }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 256 * BN / 8 / FTHREADS; ++it) {
+      const int q = it * FTHREADS + t;
+      const int row = q / (BN / 8), c8 = q % (BN / 8);
+      const int64_t grow = m0 + 256 * ph + row, gcol = n0 + 8 * c8;
+      if (grow < M && gcol < n_out)
+        *reinterpret_cast<u32x4*>(out + grow * n_out + gcol) = *reinterpret_cast<const u32x4*>(ot + row * OS + 8 * c8);
+    }
+    __syncthreads();
+  }
+}
+
 // Sum of the split partials in split order, rounded once to bf16; blockIdx.y
 // selects the weight of a grouped launch.
 struct SumSegs {
@@ -818,13 +1131,13 @@ __global__ __launch_bounds__(256) void k_split_sum(SumSegs sg, int splits) {
 
 static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-GemmPlan plan_gemm_grouped(int64_t M, const int64_t* n_cols, int nseg, int64_t k_contract) {
+static GemmPlan plan_tiles(int64_t M, const int64_t* n_cols, int nseg, int64_t k_contract, int bm) {
   GemmPlan p;
-  p.bm = BM;
+  p.bm = bm;
   p.bn = BN;
   int64_t col_tiles = 0;
   for (int q = 0; q < nseg; ++q) col_tiles += (n_cols[q] + BN - 1) / BN;
-  const int64_t tiles = ((M + BM - 1) / BM) * col_tiles;
+  const int64_t tiles = ((M + p.bm - 1) / p.bm) * col_tiles;
   const int64_t nk = (k_contract + BK - 1) / BK;
   int splits = 1;
   // Split the contraction while the grid is short of the chip's 256 CUs and
@@ -842,8 +1155,22 @@ GemmPlan plan_gemm_grouped(int64_t M, const int64_t* n_cols, int nseg, int64_t k
   return p;
 }
 
-GemmPlan plan_gemm(int64_t M, int64_t n_cols, int64_t k_contract) {
-  return plan_gemm_grouped(M, &n_cols, 1, k_contract);
+// The forward NF4 GEMM runs on k_gemm_fwd (512-row tiles) when that grid
+// needs no split of the contraction; otherwise on k_gemm, whose 256-row tiles
+// give twice the tiles and so at most half the splits: at M = 512 the fp32
+// partials of a split launch cost more than the faster kernel saves. Both
+// kernels give the same bits for the same split.
+GemmPlan plan_gemm_grouped(int64_t M, const int64_t* n_cols, int nseg, int64_t k_contract,
+                           bool fwd_nf4) {
+  if (fwd_nf4) {
+    const GemmPlan wide = plan_tiles(M, n_cols, nseg, k_contract, FBM);
+    if (wide.splits == 1) return wide;
+  }
+  return plan_tiles(M, n_cols, nseg, k_contract, BM);
+}
+
+GemmPlan plan_gemm(int64_t M, int64_t n_cols, int64_t k_contract, bool fwd_nf4) {
+  return plan_gemm_grouped(M, &n_cols, 1, k_contract, fwd_nf4);
 }
 
 // Launches the GEMM (and the split sum when the contraction is split) for
@@ -863,7 +1190,8 @@ static hipError_t launch_gemm(bool backward, const QPtrs* q, int nseg, const uin
   g.n_out = n_outs[0];
   int64_t ncols[GEMM_MAX_SEG];
   for (int i = 0; i < nseg; ++i) ncols[i] = backward ? k_in : n_outs[i];
-  const GemmPlan p = plan_gemm_grouped(M, ncols, nseg, g.Kc);
+  const bool fwd_nf4 = !backward && wd == nullptr;
+  const GemmPlan p = plan_gemm_grouped(M, ncols, nseg, g.Kc, fwd_nf4);
   g.afrag = a_packed;
   g.kblocks = (g.Kc + BK - 1) / BK * (BK / 16);
   g.kc_chunk = p.kc_chunk;
@@ -898,11 +1226,14 @@ static hipError_t launch_gemm(bool backward, const QPtrs* q, int nseg, const uin
     sum.n[i] = n;
     max_n = n > max_n ? n : max_n;
   }
-  const dim3 grid((unsigned)tile0, (unsigned)((M + BM - 1) / BM), (unsigned)p.splits);
+  const dim3 grid((unsigned)tile0, (unsigned)((M + p.bm - 1) / p.bm), (unsigned)p.splits);
   const bool split = p.splits > 1;
   const Tables& tab = host_tables();
+  // forward NF4 without a split: k_gemm_fwd; everything else: k_gemm
 #define NF4S_GEMM(B_, S_, D_) hipLaunchKernelGGL((k_gemm<B_, S_, D_>), grid, dim3(THREADS), 0, s, g, tab)
-  if (wd == nullptr) {
+  if (fwd_nf4 && p.bm == FBM) {
+    hipLaunchKernelGGL(k_gemm_fwd, grid, dim3(FTHREADS), 0, s, g, tab);
+  } else if (wd == nullptr) {
     if (backward && split) NF4S_GEMM(true, true, false);
     else if (backward) NF4S_GEMM(true, false, false);
     else if (split) NF4S_GEMM(false, true, false);

@@ -212,13 +212,18 @@ def test_pack_and_packed_call_errors():
 
 
 def test_packed_workspace_is_split_partials_only():
-    # gate at M = 512: 112 x 2 output tiles fill the chip, no split, no scratch
-    assert L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, 512, 14336, 4096) == 0
-    # q at M = 512: 64 tiles, the contraction is split and partials are needed
+    # forward tiles are 512 x 128: gate at M = 1024 has 112 x 2 tiles and
+    # fills the chip unsplit, no scratch
+    assert L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, 1024, 14336, 4096) == 0
+    # gate at M = 512: 112 tiles, the contraction splits in two
+    assert L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, 512, 14336, 4096) == 2 * 512 * 14336 * 4
+    # q at M = 512: 32 tiles, split with partials of every split
     need = L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, 512, 4096, 4096)
     assert need > 0 and need % (512 * 4096 * 4) == 0
     full = L.nf4s_workspace_bytes(L.OP_LINEAR_FWD, 512, 4096, 4096)
     assert full == need + L.nf4s_packed_activation_bytes(512, 4096)
+    # backward tiles are 256 x 128: dx of gate at M = 512 (32 x 2 tiles) splits
+    assert L.nf4s_workspace_bytes(L.OP_LINEAR_BWD_PACKED, 512, 14336, 4096) > 0
 
 
 def _err(fn, *args):
@@ -273,10 +278,10 @@ def test_decoder_workspace_sizes():
 
 
 def test_grouped_forward_workspace():
-    # q, k, v of the 8B layer at M = 512: 2 x 48 tiles, the contraction split
-    # in two, partials for all three outputs
-    assert L.grouped_workspace_bytes([4096, 1024, 1024], 4096, 512) == 2 * 512 * 6144 * 4
-    # gate and up: 2 x 224 tiles fill the chip, no split, no scratch
+    # q, k, v of the 8B layer at M = 512: 48 tiles of 512 x 128, the
+    # contraction split in four, partials for all three outputs
+    assert L.grouped_workspace_bytes([4096, 1024, 1024], 4096, 512) == 4 * 512 * 6144 * 4
+    # gate and up: 224 tiles fill the chip, no split, no scratch
     assert L.grouped_workspace_bytes([14336, 14336], 4096, 512) == 0
     # a group of one plans like the single call
     assert L.grouped_workspace_bytes([4096], 4096, 512) == \

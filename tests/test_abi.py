@@ -212,13 +212,14 @@ def test_pack_and_packed_call_errors():
 
 
 def test_packed_workspace_is_split_partials_only():
-    # forward tiles are 512 x 128: gate at M = 1024 has 112 x 2 tiles and
-    # fills the chip unsplit, no scratch
+    # the forward runs on 512 x 128 tiles where they fill the chip unsplit
+    # (gate at M = 1024: 112 x 2 tiles), else on 256 x 128 tiles: gate at
+    # M = 512 then has 112 x 2 tiles, again unsplit; no scratch either way
     assert L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, 1024, 14336, 4096) == 0
-    # gate at M = 512: 112 tiles, the contraction splits in two
-    assert L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, 512, 14336, 4096) == 2 * 512 * 14336 * 4
-    # q at M = 512: 32 tiles, split with partials of every split
+    assert L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, 512, 14336, 4096) == 0
+    # q at M = 512: 32 x 2 tiles of 256 x 128, split in four
     need = L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, 512, 4096, 4096)
+    assert need == 4 * 512 * 4096 * 4
     assert need > 0 and need % (512 * 4096 * 4) == 0
     full = L.nf4s_workspace_bytes(L.OP_LINEAR_FWD, 512, 4096, 4096)
     assert full == need + L.nf4s_packed_activation_bytes(512, 4096)
@@ -278,10 +279,11 @@ def test_decoder_workspace_sizes():
 
 
 def test_grouped_forward_workspace():
-    # q, k, v of the 8B layer at M = 512: 48 tiles of 512 x 128, the
-    # contraction split in four, partials for all three outputs
-    assert L.grouped_workspace_bytes([4096, 1024, 1024], 4096, 512) == 4 * 512 * 6144 * 4
-    # gate and up: 224 tiles fill the chip, no split, no scratch
+    # q, k, v of the 8B layer at M = 512: 48 x 2 tiles of 256 x 128 (512-row
+    # tiles would need a split), the contraction split in two, partials for
+    # all three outputs
+    assert L.grouped_workspace_bytes([4096, 1024, 1024], 4096, 512) == 2 * 512 * 6144 * 4
+    # gate and up: 224 tiles of 512 x 128 fill the chip, no split, no scratch
     assert L.grouped_workspace_bytes([14336, 14336], 4096, 512) == 0
     # a group of one plans like the single call
     assert L.grouped_workspace_bytes([4096], 4096, 512) == \

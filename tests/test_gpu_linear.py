@@ -325,9 +325,10 @@ def test_grouped_forward_bit_identical_when_split_matches(projs, ns, k, M, lora_
 
 def test_grouped_forward_8b_qkv_close_to_single_calls():
     """q, k, v at 8B widths, M = 512 (the decoder step's launch): the group
-    splits the contraction in four where the single calls split it in eight,
-    so outputs agree to bf16 rounding of differently ordered fp32 sums; the
-    single calls are checked against the oracle at these shapes."""
+    splits the contraction in two where the single calls split it in four
+    (q) and eight (k, v), so outputs agree to bf16 rounding of differently
+    ordered fp32 sums; the single calls are checked against the oracle at
+    these shapes."""
     c = _group_setup(("q", "k", "v"), (4096, 1024, 1024), 4096, 512, ("q", "v"))
     g, single = _group_run(c, True), _group_run(c, False)
     for a, b in zip(g, single):

@@ -825,31 +825,102 @@ __global__ __launch_bounds__(256) void k_f32_to_bf16(const float* __restrict__ x
   if (i < n) y[i] = f2bf(x[i]);
 }
 
+// ---- rows of logits: one 1024-thread workgroup per row ----------------------
+// A row of a large vocabulary (128,256 bf16 = 256 KB) is read twice: once
+// for its log-sum-exp, with a running maximum and a sum rescaled whenever the
+// maximum grows (one exponential per element), and once for the gradient.
+// Rows whose length is a multiple of 8 and whose start is 16-byte aligned are
+// read 16 bytes per lane. The partial (max, sum) pairs are combined in a
+// fixed order: a butterfly inside each wave, then the 16 waves in order.
+constexpr int ROW_THREADS = 1024;
+
+__device__ __forceinline__ void ms_add(float& m, float& s, float x) {
+  if (x > m) {
+    s = s * expf(m - x) + 1.0f;
+    m = x;
+  } else if (x != -INFINITY) {
+    s += expf(x - m);
+  }
+}
+
+__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;  // both parts empty
+  s = (m == -INFINITY ? 0.0f : s * expf(m - M)) + (m2 == -INFINITY ? 0.0f : s2 * expf(m2 - M));
+  m = M;
+}
+
+__device__ __forceinline__ bool row_vec(const uint16_t* z, int64_t V) {
+  return V % 8 == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0;
+}
+
+// log-sum-exp of z[0, V) (fp32); red holds 2 * 16 floats
+__device__ __forceinline__ float row_lse(const uint16_t* __restrict__ z, int64_t V, float* red) {
+  float m = -INFINITY, s = 0.0f;
+  if (row_vec(z, V)) {
+    for (int64_t j = threadIdx.x; j < V / 8; j += ROW_THREADS) {
+      float x[8];
+      load8_bf16(z + 8 * j, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ms_add(m, s, x[e]);
+    }
+  } else {
+    for (int64_t j = threadIdx.x; j < V; j += ROW_THREADS) ms_add(m, s, bf2f(z[j]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+    ms_merge(m, s, m2, s2);
+  }
+  __syncthreads();  // red may still be read by a previous call
+  if ((threadIdx.x & 63) == 0) {
+    red[2 * (threadIdx.x >> 6)] = m;
+    red[2 * (threadIdx.x >> 6) + 1] = s;
+  }
+  __syncthreads();
+  float M = red[0], S = red[1];
+  for (int w = 1; w < ROW_THREADS / 64; ++w) ms_merge(M, S, red[2 * w], red[2 * w + 1]);
+  return M + logf(S);
+}
+
+// out[j] = bf16(w * (exp(z[j] - lse) - [j == tg])) over the row
+__device__ __forceinline__ void row_grad(const uint16_t* __restrict__ z, int64_t V, float lse, int64_t tg, float w,
+                         uint16_t* __restrict__ out) {
+  if (row_vec(z, V) && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+    for (int64_t j = threadIdx.x; j < V / 8; j += ROW_THREADS) {
+      float x[8];
+      load8_bf16(z + 8 * j, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float p = expf(x[e] - lse);
+        if (8 * j + e == tg) p -= 1.0f;
+        x[e] = w * p;
+      }
+      store8_bf16(out + 8 * j, x);
+    }
+  } else {
+    for (int64_t j = threadIdx.x; j < V; j += ROW_THREADS) {
+      float p = expf(bf2f(z[j]) - lse);
+      if (j == tg) p -= 1.0f;
+      out[j] = f2bf(w * p);
+    }
+  }
+}
+
 // Cross-entropy of one row of bf16 logits: row loss and bf16 gradient
 // (softmax - onehot) / T. A target outside [0, V) makes the row loss NaN.
-__global__ __launch_bounds__(256) void k_ce_rows(const uint16_t* __restrict__ logits,
-                                                 const int64_t* __restrict__ targets, int64_t T,
-                                                 int64_t V, float* __restrict__ row_loss,
-                                                 uint16_t* __restrict__ dlogits) {
-  __shared__ float red[256];
+__global__ __launch_bounds__(ROW_THREADS) void k_ce_rows(const uint16_t* __restrict__ logits,
+                                                         const int64_t* __restrict__ targets, int64_t T,
+                                                         int64_t V, float* __restrict__ row_loss,
+                                                         uint16_t* __restrict__ dlogits) {
+  __shared__ float red[2 * ROW_THREADS / 64];
   const int64_t t = blockIdx.x;
   const uint16_t* z = logits + t * V;
-  float m = -INFINITY;
-  for (int64_t j = threadIdx.x; j < V; j += 256) m = fmaxf(m, bf2f(z[j]));
-  m = block_max(m, red);
-  float s = 0.0f;
-  for (int64_t j = threadIdx.x; j < V; j += 256) s += expf(bf2f(z[j]) - m);
-  s = block_sum(s, red);
-  const float lse = m + logf(s);
+  const float lse = row_lse(z, V, red);
   const int64_t tg = targets[t];
   const bool ok = tg >= 0 && tg < V;
   if (threadIdx.x == 0) row_loss[t] = ok ? lse - bf2f(z[tg]) : __builtin_nanf("");
-  const float invT = 1.0f / (float)T;
-  for (int64_t j = threadIdx.x; j < V; j += 256) {
-    float p = expf(bf2f(z[j]) - lse);
-    if (j == tg) p -= 1.0f;
-    dlogits[t * V + j] = f2bf(p * invT);
-  }
+  row_grad(z, V, lse, tg, 1.0f / (float)T, dlogits + t * V);
 }
 
 // loss = mean of the row losses, summed in a fixed order by one workgroup
@@ -865,21 +936,16 @@ __global__ __launch_bounds__(256) void k_mean(const float* __restrict__ x, int64
 // ---- preference step (DPO) ---------------------------------------------------
 // Per-token negative log-probability of the target, logsumexp(z_t) - z_t[y_t]
 // (fp32; NaN for a target outside [0, V)); one workgroup per row.
-__global__ __launch_bounds__(256) void k_token_nll(const uint16_t* __restrict__ logits,
-                                                   const int64_t* __restrict__ targets, int64_t V,
-                                                   float* __restrict__ nll) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(ROW_THREADS) void k_token_nll(const uint16_t* __restrict__ logits,
+                                                           const int64_t* __restrict__ targets,
+                                                           int64_t V, float* __restrict__ nll) {
+  __shared__ float red[2 * ROW_THREADS / 64];
   const int64_t t = blockIdx.x;
   const uint16_t* z = logits + t * V;
-  float m = -INFINITY;
-  for (int64_t j = threadIdx.x; j < V; j += 256) m = fmaxf(m, bf2f(z[j]));
-  m = block_max(m, red);
-  float s = 0.0f;
-  for (int64_t j = threadIdx.x; j < V; j += 256) s += expf(bf2f(z[j]) - m);
-  s = block_sum(s, red);
+  const float lse = row_lse(z, V, red);
   const int64_t tg = targets[t];
   const bool ok = tg >= 0 && tg < V;
-  if (threadIdx.x == 0) nll[t] = ok ? m + logf(s) - bf2f(z[tg]) : __builtin_nanf("");
+  if (threadIdx.x == 0) nll[t] = ok ? lse - bf2f(z[tg]) : __builtin_nanf("");
 }
 
 __device__ __forceinline__ float log_sigmoid(float x) {
@@ -921,28 +987,16 @@ __global__ __launch_bounds__(256) void k_dpo(const float* __restrict__ nll_p,
 }
 
 // dlogits[t] = bf16(coef[t / S] * mask[t] * (softmax(z_t) - onehot(y_t))).
-__global__ __launch_bounds__(256) void k_logit_grad(const uint16_t* __restrict__ logits,
-                                                    const int64_t* __restrict__ targets,
-                                                    const float* __restrict__ coef,
-                                                    const float* __restrict__ mask, int64_t S,
-                                                    int64_t V, uint16_t* __restrict__ dlogits) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(ROW_THREADS) void k_logit_grad(const uint16_t* __restrict__ logits,
+                                                            const int64_t* __restrict__ targets,
+                                                            const float* __restrict__ coef,
+                                                            const float* __restrict__ mask, int64_t S,
+                                                            int64_t V, uint16_t* __restrict__ dlogits) {
+  __shared__ float red[2 * ROW_THREADS / 64];
   const int64_t t = blockIdx.x;
   const uint16_t* z = logits + t * V;
-  float m = -INFINITY;
-  for (int64_t j = threadIdx.x; j < V; j += 256) m = fmaxf(m, bf2f(z[j]));
-  m = block_max(m, red);
-  float s = 0.0f;
-  for (int64_t j = threadIdx.x; j < V; j += 256) s += expf(bf2f(z[j]) - m);
-  s = block_sum(s, red);
-  const float lse = m + logf(s);
-  const float w = coef[t / S] * mask[t];
-  const int64_t tg = targets[t];
-  for (int64_t j = threadIdx.x; j < V; j += 256) {
-    float p = expf(bf2f(z[j]) - lse);
-    if (j == tg) p -= 1.0f;
-    dlogits[t * V + j] = f2bf(w * p);
-  }
+  const float lse = row_lse(z, V, red);
+  row_grad(z, V, lse, targets[t], coef[t / S] * mask[t], dlogits + t * V);
 }
 
 __global__ __launch_bounds__(256) void k_adamw(float* __restrict__ p, const float* __restrict__ g,
@@ -1073,14 +1127,15 @@ size_t cross_entropy_ws_bytes(int64_t T) { return (size_t)T * sizeof(float); }
 hipError_t launch_cross_entropy(const uint16_t* logits, const int64_t* targets, int64_t T, int64_t V,
                                 float* loss, uint16_t* dlogits, void* ws, hipStream_t s) {
   float* rows = static_cast<float*>(ws);
-  hipLaunchKernelGGL(k_ce_rows, dim3((unsigned)T), dim3(256), 0, s, logits, targets, T, V, rows, dlogits);
+  hipLaunchKernelGGL(k_ce_rows, dim3((unsigned)T), dim3(ROW_THREADS), 0, s, logits, targets, T, V, rows,
+                     dlogits);
   hipLaunchKernelGGL(k_mean, dim3(1), dim3(256), 0, s, rows, T, loss);
   return hipGetLastError();
 }
 
 hipError_t launch_token_nll(const uint16_t* logits, const int64_t* targets, int64_t T, int64_t V,
                             float* nll, hipStream_t s) {
-  hipLaunchKernelGGL(k_token_nll, dim3((unsigned)T), dim3(256), 0, s, logits, targets, V, nll);
+  hipLaunchKernelGGL(k_token_nll, dim3((unsigned)T), dim3(ROW_THREADS), 0, s, logits, targets, V, nll);
   return hipGetLastError();
 }
 
@@ -1093,8 +1148,8 @@ hipError_t launch_dpo(const float* nll_p, const float* nll_r, const float* mask,
 hipError_t launch_logit_grad(const uint16_t* logits, const int64_t* targets, const float* coef,
                              const float* mask, int64_t T, int64_t S, int64_t V, uint16_t* dlogits,
                              hipStream_t s) {
-  hipLaunchKernelGGL(k_logit_grad, dim3((unsigned)T), dim3(256), 0, s, logits, targets, coef, mask, S,
-                     V, dlogits);
+  hipLaunchKernelGGL(k_logit_grad, dim3((unsigned)T), dim3(ROW_THREADS), 0, s, logits, targets, coef,
+                     mask, S, V, dlogits);
   return hipGetLastError();
 }
 

@@ -67,6 +67,7 @@ class Decoder:
         assert mode in ("streamed", "resident")
         self.time_calls = time_calls
         self.timed = []
+        self._kept_last = False  # the last layer's body is still in the buffers
         dev = "cuda"
         self.cfg = cfg
         self.sh = shards
@@ -262,9 +263,11 @@ class Decoder:
                                        *self._ws(), self._s)
 
     # -- one layer ---------------------------------------------------------------------
-    def _layer_fwd(self, i, base, recompute, adapters=True, hin=None, hout=None):
+    def _layer_fwd(self, i, base, recompute, adapters=True, hin=None, hout=None, keep=False):
         """Layer i's body from h_i. The recompute keeps the fp32 attention
-        output for the backward and skips h_{i+1}, which is already stored.
+        output for the backward and skips h_{i+1}, which is already stored;
+        keep=True keeps it in a first forward too (the last layer, whose
+        backward follows the head with the body buffers intact).
         adapters=False runs the frozen base alone (the reference model);
         hin/hout default to the checkpoints h_i, h_{i+1}."""
         c, s, M = self.cfg, self._s, self.M
@@ -280,7 +283,7 @@ class Decoder:
         nf4s_rope(self.k.data_ptr(), M, self.S, c["kv_heads"], c["head_dim"], c["rope_theta"], 0, s)
         nf4s_attention_fwd(self.q.data_ptr(), self.k.data_ptr(), self.vv.data_ptr(), self.B, self.S,
                            c["heads"], c["kv_heads"], c["head_dim"], self.o.data_ptr(),
-                           self.o32.data_ptr() if recompute else None, self.lse.data_ptr(), s)
+                           self.o32.data_ptr() if recompute or keep else None, self.lse.data_ptr(), s)
         self._fwd(base, i, ("o",), self.o, (self.ao,), a)
         nf4s_residual_add(hin.data_ptr(), self.ao.data_ptr(), M * H, self.h_mid.data_ptr(), s)
         nf4s_rmsnorm_fwd(self.h_mid.data_ptr(), self.norms["mlp"][i].data_ptr(), M, H, c["eps"],
@@ -336,12 +339,17 @@ class Decoder:
                                 self.logits.data_ptr(), *self._ws(), s)
 
     def _forward_sweep(self, adapters, nxt_last=None):
-        """Layers 0..L-1 from h_0 (the last one prefetching nxt_last)."""
+        """Layers 0..L-1 from h_0 (the last one prefetching nxt_last). With
+        the adapters on, the last layer's body stays in the buffers for the
+        backward, which then skips its recompute (same kernels, same inputs:
+        the same bits)."""
         L = self.L
         for i in range(L):
             base = self._acquire(i, nxt=i + 1 if i + 1 < L else nxt_last)
-            self._layer_fwd(i, base, recompute=False, adapters=adapters)
+            keep = adapters and i == L - 1
+            self._layer_fwd(i, base, recompute=False, adapters=adapters, keep=keep)
             self._release(i)
+        self._kept_last = adapters
 
     def _backward(self):
         """From self.dlogits: lm_head and final norm backward, then the
@@ -354,9 +362,11 @@ class Decoder:
                          self.rstd_f.data_ptr(), M, H, 0, self.dh.data_ptr(), s)
         for i in range(L - 1, -1, -1):
             base = self._acquire(i, nxt=i - 1 if i > 0 else None)
-            self._layer_fwd(i, base, recompute=True)
+            if not (i == L - 1 and self._kept_last):
+                self._layer_fwd(i, base, recompute=True)
             self._layer_bwd(i, base)
             self._release(i)
+        self._kept_last = False
 
     def forward_backward(self, ids, targets):
         """Queue the forward and backward sweeps for token ids / next-token
@@ -408,8 +418,9 @@ class Decoder:
                 base = self._acquire(i, nxt=i + 1 if i + 1 < L else None)
                 self._layer_fwd(i, base, recompute=False, adapters=False,
                                 hin=self.h[0] if i == 0 else href[i % 2], hout=href[(i + 1) % 2])
-                self._layer_fwd(i, base, recompute=False)
+                self._layer_fwd(i, base, recompute=False, keep=i == L - 1)
                 self._release(i)
+            self._kept_last = True
             self._head_fwd(href[L % 2])
             nf4s_token_nll(self.logits.data_ptr(), targets.data_ptr(), M, V, self.nll_ref.data_ptr(), s)
         self._head_fwd(self.h[L])

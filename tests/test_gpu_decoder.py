@@ -174,8 +174,10 @@ def test_swiglu_fwd_bwd(n):
     _check_bf16(host_u16(du), D.bf16(ru), abs_slack=1e-6, what="du")
 
 
-@pytest.mark.parametrize("T,V", [(37, 1000), (4, 49152), (2, 128256)])
+@pytest.mark.parametrize("T,V", [(37, 1000), (4, 49152), (2, 128256), (3, 1001)])
 def test_cross_entropy(T, V):
+    # V = 1001: rows neither a multiple of 8 long nor 16-byte aligned (the
+    # element-wise path of the row kernels)
     require_gpu()
     print(f"cross-entropy T={T} V={V}", flush=True)
     g = _rng(50 + V)
@@ -490,11 +492,13 @@ def test_135m_loss_curve_streamed_equals_resident(w135):
 
 # ---- preference step (DPO) ----------------------------------------------------------
 
-def test_token_nll_dpo_and_logit_grad_kernels():
-    """The three preference-step kernels against the oracle on shared inputs."""
+@pytest.mark.parametrize("V", [1000, 1001])
+def test_token_nll_dpo_and_logit_grad_kernels(V):
+    """The three preference-step kernels against the oracle on shared inputs
+    (V = 1001: the element-wise path of the row kernels)."""
     require_gpu()
     g = _rng(90)
-    pairs, S, V = 3, 37, 1000
+    pairs, S = 3, 37
     T = 2 * pairs * S
     z = _bits(g.standard_normal((T, V)) * 2)
     tg = g.integers(0, V, size=T)

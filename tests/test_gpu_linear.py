@@ -291,6 +291,11 @@ GROUPS = [
     (("gate", "up"), (1536, 1536), 576, 512, ()),
     (("q", "k", "v"), (72, 40, 136), 128, 37, ("k",)),
     (("o",), (576,), 576, 1, ("o",)),
+    # 512-row tiles (a contraction of 9 steps is never split): two row tiles,
+    # the second ragged, and a ragged column tile, adapters on two weights
+    (("q", "k", "v"), (576, 200, 136), 576, 700, ("q", "v")),
+    # a single 64-wide contraction step
+    (("gate", "up"), (256, 64), 64, 300, ("up",)),
 ]
 
 
@@ -310,11 +315,15 @@ def test_grouped_forward_matches_oracle(projs, ns, k, M, lora_on):
 @pytest.mark.parametrize("projs,ns,k,M,lora_on", [
     (("gate", "up"), (1536, 1536), 576, 512, ("up",)),
     (("gate", "up"), (14336, 14336), 4096, 1024, ()),
+    # grouped: 224 tiles of 512 rows (k_gemm_fwd); alone: 2 x 112 tiles of
+    # 256 rows (k_gemm) -- two kernels, one decode and one contraction order
+    (("gate", "up"), (14336, 14336), 4096, 512, ("up",)),
 ])
 def test_grouped_forward_bit_identical_when_split_matches(projs, ns, k, M, lora_on):
     """When the group's plan keeps each weight's split count (here: no split
     alone or grouped), every output tile is contracted in the same order as by
-    the single call, so the bits agree."""
+    the single call, so the bits agree -- also where the grouped launch and
+    the single calls run on different kernels."""
     splits_single = [L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, M, n, k) for n in ns]
     assert splits_single == [0] * len(ns) and L.grouped_workspace_bytes(list(ns), k, M) == 0
     c = _group_setup(projs, ns, k, M, lora_on)

@@ -338,16 +338,26 @@ int nf4s_embed(const uint16_t* table, int64_t vocab, int64_t hidden, const int64
                float* h, void* stream);
 
 /*
+ * Packed outputs. The producers of GEMM inputs below take an optional
+ * `packed` pointer (NULL: none): the bf16 result [T, width] is then also
+ * written in the MFMA fragment order of nf4s_pack_activation (256-B aligned,
+ * nf4s_packed_activation_bytes(T, width) bytes), ready for the _packed GEMM
+ * calls without a separate packing pass. It equals nf4s_pack_activation's
+ * output except in the rows past T, which are left as they were (the GEMMs
+ * compute them but never store them); the columns past width up to the next
+ * multiple of 64 are written as zeros.
+ *
  * RMSNorm: rstd[t] = 1/sqrt(mean_j x[t,j]^2 + eps), y = bf16(x * rstd * w).
- * x fp32 [T, H]; w fp32 [H]; y bf16 [T, H]; rstd fp32 [T] (kept for the
- * backward); H a multiple of 8, x, w, y, dys and dh 16-byte aligned. Backward: with g = w * (dys[0] + ... + dys[n_dy-1]) (n_dy bf16
+ * x fp32 [T, H]; w fp32 [H]; y bf16 [T, H] (and packed, see above); rstd fp32
+ * [T] (kept for the backward); H a multiple of 8, x, w, y, dys and dh 16-byte
+ * aligned. Backward: with g = w * (dys[0] + ... + dys[n_dy-1]) (n_dy bf16
  * [T, H] gradients of y, 1..3, summed in fp32 in that order),
  *   d = rstd * g - x * rstd^3 * mean_j(g * x),
  * written to dh (accumulate = 0) or added to it (accumulate = 1). dys is a
  * host array of device pointers. Errors: EINVAL, ESHAPE, EALIGN.
  */
 int nf4s_rmsnorm_fwd(const float* x, const float* w, int64_t T, int64_t H, float eps, uint16_t* y,
-                     float* rstd, void* stream);
+                     float* rstd, void* packed, void* stream);
 int nf4s_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float* x, const float* w,
                      const float* rstd, int64_t T, int64_t H, int accumulate, float* dh,
                      void* stream);
@@ -392,16 +402,20 @@ int nf4s_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
 /*
  * SwiGLU: out = bf16(silu(g) * u), silu(z) = z / (1 + e^-z); backward from ds:
  * dg = bf16(ds * u * s * (1 + g * (1 - s))), du = bf16(ds * g * s), s the
- * logistic of g. All bf16 [n]. Errors: EINVAL, ESHAPE, EALIGN.
+ * logistic of g. All bf16 [T, width], width a multiple of 8, 16-byte aligned;
+ * packed outputs as above (out; dg and du). Errors: EINVAL, ESHAPE, EALIGN.
  */
-int nf4s_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* out, void* stream);
-int nf4s_swiglu_bwd(const uint16_t* ds, const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* dg,
-                    uint16_t* du, void* stream);
+int nf4s_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t T, int64_t width, uint16_t* out,
+                    void* packed, void* stream);
+int nf4s_swiglu_bwd(const uint16_t* ds, const uint16_t* g, const uint16_t* u, int64_t T,
+                    int64_t width, uint16_t* dg, uint16_t* du, void* dg_packed, void* du_packed,
+                    void* stream);
 
 /* Residual update out[i] = h[i] + y[i] (fp32 h and out, bf16 y; out may be
- * h) and rounding y = bf16(x). */
+ * h), and rounding y = bf16(x) of an fp32 [T, width] matrix (width a multiple
+ * of 8, 16-byte aligned; packed output as above). */
 int nf4s_residual_add(const float* h, const uint16_t* y, int64_t n, float* out, void* stream);
-int nf4s_to_bf16(const float* x, int64_t n, uint16_t* y, void* stream);
+int nf4s_to_bf16(const float* x, int64_t T, int64_t width, uint16_t* y, void* packed, void* stream);
 
 /*
  * Mean token cross-entropy over bf16 logits [T, V] against int64 targets [T]:

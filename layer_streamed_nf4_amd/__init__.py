@@ -113,7 +113,7 @@ _SIG = {
     "dense_linear_fwd_packed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
     "dense_linear_bwd_packed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
     "nf4s_embed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P]),
-    "nf4s_rmsnorm_fwd": (ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_float, _P, _P, _P]),
+    "nf4s_rmsnorm_fwd": (ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_float, _P, _P, _P, _P]),
     "nf4s_rmsnorm_bwd": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.c_int, _P, _P, _P, _I64, _I64,
                                         ctypes.c_int, _P, _P]),
     "nf4s_rope": (ctypes.c_int, [_P, _I64, _I64, ctypes.c_int, ctypes.c_int, ctypes.c_double,
@@ -123,10 +123,10 @@ _SIG = {
     "nf4s_attention_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int, _P, _P, _P, _P,
                                           ctypes.c_size_t, _P]),
-    "nf4s_swiglu_fwd": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
-    "nf4s_swiglu_bwd": (ctypes.c_int, [_P, _P, _P, _I64, _P, _P, _P]),
+    "nf4s_swiglu_fwd": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
+    "nf4s_swiglu_bwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P]),
     "nf4s_residual_add": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
-    "nf4s_to_bf16": (ctypes.c_int, [_P, _I64, _P, _P]),
+    "nf4s_to_bf16": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "nf4s_cross_entropy": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]),
     "nf4s_adamw": (ctypes.c_int, [_P, _P, _P, _P, _I64, ctypes.c_float, ctypes.c_float,
                                   ctypes.c_float, ctypes.c_float, ctypes.c_float, _I64, _P]),
@@ -269,8 +269,8 @@ def nf4s_embed(table, vocab, hidden, ids, T, h, stream=0):
     _check(lib().nf4s_embed(table, vocab, hidden, ids, T, h, stream))
 
 
-def nf4s_rmsnorm_fwd(x, w, T, H, eps, y, rstd, stream=0):
-    _check(lib().nf4s_rmsnorm_fwd(x, w, T, H, eps, y, rstd, stream))
+def nf4s_rmsnorm_fwd(x, w, T, H, eps, y, rstd, stream=0, packed=None):
+    _check(lib().nf4s_rmsnorm_fwd(x, w, T, H, eps, y, rstd, packed, stream))
 
 
 def nf4s_rmsnorm_bwd(dys, x, w, rstd, T, H, accumulate, dh, stream=0):
@@ -293,20 +293,20 @@ def nf4s_attention_bwd(q, k, v, o_f32, dout, lse, B, S, heads, kv_heads, head_di
                                     dk, dv, ws, ws_bytes, stream))
 
 
-def nf4s_swiglu_fwd(g, u, n, out, stream=0):
-    _check(lib().nf4s_swiglu_fwd(g, u, n, out, stream))
+def nf4s_swiglu_fwd(g, u, T, width, out, stream=0, packed=None):
+    _check(lib().nf4s_swiglu_fwd(g, u, T, width, out, packed, stream))
 
 
-def nf4s_swiglu_bwd(ds, g, u, n, dg, du, stream=0):
-    _check(lib().nf4s_swiglu_bwd(ds, g, u, n, dg, du, stream))
+def nf4s_swiglu_bwd(ds, g, u, T, width, dg, du, stream=0, dg_packed=None, du_packed=None):
+    _check(lib().nf4s_swiglu_bwd(ds, g, u, T, width, dg, du, dg_packed, du_packed, stream))
 
 
 def nf4s_residual_add(h, y, n, out, stream=0):
     _check(lib().nf4s_residual_add(h, y, n, out, stream))
 
 
-def nf4s_to_bf16(x, n, y, stream=0):
-    _check(lib().nf4s_to_bf16(x, n, y, stream))
+def nf4s_to_bf16(x, T, width, y, stream=0, packed=None):
+    _check(lib().nf4s_to_bf16(x, T, width, y, packed, stream))
 
 
 def nf4s_cross_entropy(logits, targets, T, V, loss, dlogits, ws, ws_bytes, stream=0):

@@ -552,19 +552,27 @@ int nf4s_embed(const uint16_t* table, int64_t vocab, int64_t hidden, const int64
 
 // The norms move 8 elements (16/32 bytes) per access.
 static int check_norm_width(int64_t H) {
-  if (H % 8) return fail(NF4S_ESHAPE, "hidden=%lld is not a multiple of 8", (long long)H);
+  if (H % 8) return fail(NF4S_ESHAPE, "width=%lld is not a multiple of 8", (long long)H);
   return NF4S_OK;
 }
 
+// an optional packed output: 256-B aligned, offsets within 32 bits
+static int check_packed_out(const void* packed, int64_t T, int64_t W) {
+  if (!packed) return NF4S_OK;
+  int rc;
+  if ((rc = check_packed_shape(T, W))) return rc;
+  return check_ptr(packed, "packed", 256);
+}
+
 int nf4s_rmsnorm_fwd(const float* x, const float* w, int64_t T, int64_t H, float eps, uint16_t* y,
-                     float* rstd, void* stream) {
+                     float* rstd, void* packed, void* stream) {
   int rc;
   if ((rc = check_rows(T, H)) || (rc = check_norm_width(H))) return rc;
   if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(NF4S_EINVAL, "eps must be positive and finite");
   if ((rc = check_ptr(x, "x")) || (rc = check_ptr(w, "w")) || (rc = check_ptr(y, "y")) ||
-      (rc = check_ptr(rstd, "rstd", 4)))
+      (rc = check_ptr(rstd, "rstd", 4)) || (rc = check_packed_out(packed, T, H)))
     return rc;
-  return launched(launch_rmsnorm_fwd(x, w, T, H, eps, y, rstd, static_cast<hipStream_t>(stream)),
+  return launched(launch_rmsnorm_fwd(x, w, T, H, eps, y, rstd, packed, static_cast<hipStream_t>(stream)),
                   "rmsnorm_fwd launch");
 }
 
@@ -653,21 +661,28 @@ int nf4s_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
                   "attention_bwd launch");
 }
 
-int nf4s_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* out, void* stream) {
+int nf4s_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t T, int64_t width, uint16_t* out,
+                    void* packed, void* stream) {
   int rc;
-  if ((rc = check_count(n))) return rc;
-  if ((rc = check_ptr(g, "g", 2)) || (rc = check_ptr(u, "u", 2)) || (rc = check_ptr(out, "out", 2))) return rc;
-  return launched(launch_swiglu_fwd(g, u, n, out, static_cast<hipStream_t>(stream)), "swiglu_fwd launch");
+  if ((rc = check_rows(T, width)) || (rc = check_norm_width(width))) return rc;
+  if ((rc = check_ptr(g, "g")) || (rc = check_ptr(u, "u")) || (rc = check_ptr(out, "out")) ||
+      (rc = check_packed_out(packed, T, width)))
+    return rc;
+  return launched(launch_swiglu_fwd(g, u, T, width, out, packed, static_cast<hipStream_t>(stream)),
+                  "swiglu_fwd launch");
 }
 
-int nf4s_swiglu_bwd(const uint16_t* ds, const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* dg,
-                    uint16_t* du, void* stream) {
+int nf4s_swiglu_bwd(const uint16_t* ds, const uint16_t* g, const uint16_t* u, int64_t T,
+                    int64_t width, uint16_t* dg, uint16_t* du, void* dg_packed, void* du_packed,
+                    void* stream) {
   int rc;
-  if ((rc = check_count(n))) return rc;
-  if ((rc = check_ptr(ds, "ds", 2)) || (rc = check_ptr(g, "g", 2)) || (rc = check_ptr(u, "u", 2)) ||
-      (rc = check_ptr(dg, "dg", 2)) || (rc = check_ptr(du, "du", 2)))
+  if ((rc = check_rows(T, width)) || (rc = check_norm_width(width))) return rc;
+  if ((rc = check_ptr(ds, "ds")) || (rc = check_ptr(g, "g")) || (rc = check_ptr(u, "u")) ||
+      (rc = check_ptr(dg, "dg")) || (rc = check_ptr(du, "du")) ||
+      (rc = check_packed_out(dg_packed, T, width)) || (rc = check_packed_out(du_packed, T, width)))
     return rc;
-  return launched(launch_swiglu_bwd(ds, g, u, n, dg, du, static_cast<hipStream_t>(stream)),
+  return launched(launch_swiglu_bwd(ds, g, u, T, width, dg, du, dg_packed, du_packed,
+                                    static_cast<hipStream_t>(stream)),
                   "swiglu_bwd launch");
 }
 
@@ -679,11 +694,13 @@ int nf4s_residual_add(const float* h, const uint16_t* y, int64_t n, float* out, 
                   "residual_add launch");
 }
 
-int nf4s_to_bf16(const float* x, int64_t n, uint16_t* y, void* stream) {
+int nf4s_to_bf16(const float* x, int64_t T, int64_t width, uint16_t* y, void* packed, void* stream) {
   int rc;
-  if ((rc = check_count(n))) return rc;
-  if ((rc = check_ptr(x, "x", 4)) || (rc = check_ptr(y, "y", 2))) return rc;
-  return launched(launch_f32_to_bf16(x, n, y, static_cast<hipStream_t>(stream)), "to_bf16 launch");
+  if ((rc = check_rows(T, width)) || (rc = check_norm_width(width))) return rc;
+  if ((rc = check_ptr(x, "x")) || (rc = check_ptr(y, "y")) || (rc = check_packed_out(packed, T, width)))
+    return rc;
+  return launched(launch_f32_to_bf16(x, T, width, y, packed, static_cast<hipStream_t>(stream)),
+                  "to_bf16 launch");
 }
 
 int nf4s_cross_entropy(const uint16_t* logits, const int64_t* targets, int64_t T, int64_t V,

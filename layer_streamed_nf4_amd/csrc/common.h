@@ -98,8 +98,10 @@ size_t lora_bwd_ws_bytes(int64_t M, int64_t n_out, int r);
 // Decoder kernels (decoder.hip).
 hipError_t launch_embed(const uint16_t* E, int64_t V, const int64_t* ids, int64_t T, int64_t H,
                         float* h, hipStream_t s);
+// packed (nullable): y also in MFMA fragment order, as k_frag_pack writes it
+// except for rows past T (left as they are; the GEMMs never store them)
 hipError_t launch_rmsnorm_fwd(const float* x, const float* w, int64_t T, int64_t H, float eps,
-                              uint16_t* y, float* rstd, hipStream_t s);
+                              uint16_t* y, float* rstd, void* packed, hipStream_t s);
 hipError_t launch_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float* x, const float* w,
                               const float* rstd, int64_t T, int64_t H, int accumulate, float* dh,
                               hipStream_t s);
@@ -113,13 +115,15 @@ hipError_t launch_attention_bwd(const uint16_t* q, const uint16_t* k, const uint
                                 const float* o_f32, const uint16_t* dout, const float* lse,
                                 int64_t B, int64_t S, int H, int Hkv, int D, uint16_t* dq,
                                 uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s);
-hipError_t launch_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* out,
-                             hipStream_t s);
-hipError_t launch_swiglu_bwd(const uint16_t* ds, const uint16_t* g, const uint16_t* u, int64_t n,
-                             uint16_t* dg, uint16_t* du, hipStream_t s);
+hipError_t launch_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t T, int64_t W,
+                             uint16_t* out, void* packed, hipStream_t s);
+hipError_t launch_swiglu_bwd(const uint16_t* ds, const uint16_t* g, const uint16_t* u, int64_t T,
+                             int64_t W, uint16_t* dg, uint16_t* du, void* dg_packed,
+                             void* du_packed, hipStream_t s);
 hipError_t launch_residual_add(const float* h, const uint16_t* y, int64_t n, float* out,
                                hipStream_t s);
-hipError_t launch_f32_to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s);
+hipError_t launch_f32_to_bf16(const float* x, int64_t T, int64_t W, uint16_t* y, void* packed,
+                              hipStream_t s);
 size_t cross_entropy_ws_bytes(int64_t T);
 hipError_t launch_cross_entropy(const uint16_t* logits, const int64_t* targets, int64_t T, int64_t V,
                                 float* loss, uint16_t* dlogits, void* ws, hipStream_t s);

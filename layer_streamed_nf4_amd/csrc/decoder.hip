@@ -90,10 +90,12 @@ __global__ __launch_bounds__(256) void k_embed(const uint16_t* __restrict__ E, i
 
 // y = bf16(x * rstd * w), rstd = 1/sqrt(mean(x^2) + eps); one workgroup per
 // row, 8 elements (16- and 32-byte accesses) per thread and step.
+// packed (nullable): y also in MFMA fragment order (K = H), for the GEMMs
 __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const float* __restrict__ x,
                                                      const float* __restrict__ w, int64_t H,
                                                      float eps, uint16_t* __restrict__ y,
-                                                     float* __restrict__ rstd) {
+                                                     float* __restrict__ rstd,
+                                                     uint8_t* __restrict__ packed) {
   __shared__ float red[4];
   const int64_t t = blockIdx.x;
   const float* xr = x + t * H;
@@ -114,7 +116,15 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const float* __restrict__ x
     load8_f32(w + 8 * c, g);
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] = f[e] * r * g[e];
-    store8_bf16(y + t * H + 8 * c, f);
+    u32x4v o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    *reinterpret_cast<u32x4v*>(y + t * H + 8 * c) = o;
+    if (packed) {
+      const int64_t kb = (H + 63) / 64 * 4;
+      *reinterpret_cast<u32x4v*>(packed + frag_offset(t, 8 * c, kb)) = o;
+      if (c == nc - 1) frag_zero_tail(packed, t, H, kb);
+    }
   }
 }
 
@@ -790,26 +800,97 @@ __global__ __launch_bounds__(256) void k_attn_group_sum(const float* __restrict_
 }
 
 // ---- elementwise ------------------------------------------------------------
+// Element-wise kernels over a [T, W] matrix (W a multiple of 8), one
+// workgroup per 32 x 64 tile (one 64-wide step of one 32-row block): thread t
+// takes row t/8, columns 8*(t%8) .. +8 of the tile, so row-major reads and
+// writes are 128 contiguous bytes per 8 lanes. With a packed pointer the bf16
+// result also goes through LDS and leaves in MFMA fragment order (K = W):
+// the tile's four fragments, 4 KB contiguous, for the GEMM that reads it
+// next; rows past T are not written, columns past W are written as zeros.
+constexpr int EW_STRIDE = 144;  // bytes per staged row (128 + 16: conflict-free reads)
+
+struct EwTile {
+  int64_t rb, st;  // the workgroup's 32-row block and 64-wide step
+  int64_t m, c;    // the thread's row and first column
+  bool ok;         // m < T and c < W
+};
+
+__device__ __forceinline__ EwTile ew_tile(int64_t T, int64_t W) {
+  EwTile e;
+  const int64_t steps = (W + 63) / 64;
+  e.rb = (int64_t)blockIdx.x / steps;
+  e.st = (int64_t)blockIdx.x % steps;
+  e.m = 32 * e.rb + (threadIdx.x >> 3);
+  e.c = 64 * e.st + 8 * (threadIdx.x & 7);
+  e.ok = e.m < T && e.c < W;
+  return e;
+}
+
+// Writes the thread's 8 results (row-major when out is set, packed when
+// packed is set); stage is 32 * EW_STRIDE bytes of LDS. Every thread of the
+// workgroup must call it (it holds a barrier).
+__device__ __forceinline__ void ew_store(const EwTile& e, int64_t T, int64_t W, uint16_t* out,
+                                         uint8_t* packed, uint8_t* stage, const float* f) {
+  u32x4v o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  if (!e.ok) o = u32x4v{0u, 0u, 0u, 0u};
+  if (out && e.ok) *reinterpret_cast<u32x4v*>(out + e.m * W + e.c) = o;
+  if (!packed) return;
+  *reinterpret_cast<u32x4v*>(stage + (threadIdx.x >> 3) * EW_STRIDE + (threadIdx.x & 7) * 16) = o;
+  __syncthreads();
+  const int f16 = threadIdx.x >> 6, lane = threadIdx.x & 63;  // 16-wide block of the step, lane
+  const int64_t row = 32 * e.rb + (lane & 31);
+  if (row < T) {
+    const u32x4v w = *reinterpret_cast<const u32x4v*>(stage + (lane & 31) * EW_STRIDE +
+                                                      (2 * f16 + (lane >> 5)) * 16);
+    const int64_t kb = (W + 63) / 64 * 4;
+    const int64_t frag = e.rb * kb + 4 * e.st + f16;
+    *reinterpret_cast<u32x4v*>(packed + (frag * 64 + lane) * 16) = w;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_swiglu_fwd(const uint16_t* __restrict__ g,
-                                                    const uint16_t* __restrict__ u, int64_t n,
-                                                    uint16_t* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const float gv = bf2f(g[i]);
-  out[i] = f2bf(gv / (1.0f + __expf(-gv)) * bf2f(u[i]));
+                                                    const uint16_t* __restrict__ u, int64_t T,
+                                                    int64_t W, uint16_t* __restrict__ out,
+                                                    uint8_t* __restrict__ packed) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[32 * EW_STRIDE];
+  const EwTile e = ew_tile(T, W);
+  float o[8] = {};
+  if (e.ok) {
+    float gv[8], uv[8];
+    load8_bf16(g + e.m * W + e.c, gv);
+    load8_bf16(u + e.m * W + e.c, uv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = gv[i] / (1.0f + __expf(-gv[i])) * uv[i];
+  }
+  ew_store(e, T, W, out, packed, stage, o);
 }
 
 __global__ __launch_bounds__(256) void k_swiglu_bwd(const uint16_t* __restrict__ ds,
                                                     const uint16_t* __restrict__ g,
-                                                    const uint16_t* __restrict__ u, int64_t n,
-                                                    uint16_t* __restrict__ dg,
-                                                    uint16_t* __restrict__ du) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const float gv = bf2f(g[i]), uv = bf2f(u[i]), d = bf2f(ds[i]);
-  const float sg = 1.0f / (1.0f + __expf(-gv));
-  dg[i] = f2bf(d * uv * (sg * (1.0f + gv * (1.0f - sg))));
-  du[i] = f2bf(d * gv * sg);
+                                                    const uint16_t* __restrict__ u, int64_t T,
+                                                    int64_t W, uint16_t* __restrict__ dg,
+                                                    uint16_t* __restrict__ du,
+                                                    uint8_t* __restrict__ dg_packed,
+                                                    uint8_t* __restrict__ du_packed) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[2][32 * EW_STRIDE];
+  const EwTile e = ew_tile(T, W);
+  float og[8] = {}, ou[8] = {};
+  if (e.ok) {
+    float gv[8], uv[8], d[8];
+    load8_bf16(g + e.m * W + e.c, gv);
+    load8_bf16(u + e.m * W + e.c, uv);
+    load8_bf16(ds + e.m * W + e.c, d);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sg = 1.0f / (1.0f + __expf(-gv[i]));
+      og[i] = d[i] * uv[i] * (sg * (1.0f + gv[i] * (1.0f - sg)));
+      ou[i] = d[i] * gv[i] * sg;
+    }
+  }
+  ew_store(e, T, W, dg, dg_packed, stage[0], og);
+  ew_store(e, T, W, du, du_packed, stage[1], ou);
 }
 
 // out = h + y (fp32 residual stream plus a bf16 branch output); out may be h
@@ -819,10 +900,14 @@ __global__ __launch_bounds__(256) void k_residual_add(const float* h, const uint
   if (i < n) out[i] = h[i] + bf2f(y[i]);
 }
 
-__global__ __launch_bounds__(256) void k_f32_to_bf16(const float* __restrict__ x, int64_t n,
-                                                     uint16_t* __restrict__ y) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) y[i] = f2bf(x[i]);
+__global__ __launch_bounds__(256) void k_f32_to_bf16(const float* __restrict__ x, int64_t T,
+                                                     int64_t W, uint16_t* __restrict__ y,
+                                                     uint8_t* __restrict__ packed) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[32 * EW_STRIDE];
+  const EwTile e = ew_tile(T, W);
+  float f[8] = {};
+  if (e.ok) load8_f32(x + e.m * W + e.c, f);
+  ew_store(e, T, W, y, packed, stage, f);
 }
 
 // ---- rows of logits: one 1024-thread workgroup per row ----------------------
@@ -1016,6 +1101,11 @@ __global__ __launch_bounds__(256) void k_adamw(float* __restrict__ p, const floa
 
 inline unsigned grid_of(int64_t n) { return (unsigned)((n + 255) / 256); }
 
+// one workgroup per 32 x 64 tile of a [T, W] matrix (T * W < 2^40: < 2^29 tiles)
+inline dim3 ew_grid(int64_t T, int64_t W) {
+  return dim3((unsigned)(((T + 31) / 32) * ((W + 63) / 64)));
+}
+
 }  // namespace
 
 hipError_t launch_embed(const uint16_t* E, int64_t V, const int64_t* ids, int64_t T, int64_t H,
@@ -1025,8 +1115,9 @@ hipError_t launch_embed(const uint16_t* E, int64_t V, const int64_t* ids, int64_
 }
 
 hipError_t launch_rmsnorm_fwd(const float* x, const float* w, int64_t T, int64_t H, float eps,
-                              uint16_t* y, float* rstd, hipStream_t s) {
-  hipLaunchKernelGGL(k_rmsnorm_fwd, dim3((unsigned)T), dim3(256), 0, s, x, w, H, eps, y, rstd);
+                              uint16_t* y, float* rstd, void* packed, hipStream_t s) {
+  hipLaunchKernelGGL(k_rmsnorm_fwd, dim3((unsigned)T), dim3(256), 0, s, x, w, H, eps, y, rstd,
+                     static_cast<uint8_t*>(packed));
   return hipGetLastError();
 }
 
@@ -1099,15 +1190,18 @@ hipError_t launch_attention_bwd(const uint16_t* q, const uint16_t* k, const uint
 }
 #undef NF4S_DISPATCH_D
 
-hipError_t launch_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* out,
-                             hipStream_t s) {
-  hipLaunchKernelGGL(k_swiglu_fwd, dim3(grid_of(n)), dim3(256), 0, s, g, u, n, out);
+hipError_t launch_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t T, int64_t W,
+                             uint16_t* out, void* packed, hipStream_t s) {
+  hipLaunchKernelGGL(k_swiglu_fwd, ew_grid(T, W), dim3(256), 0, s, g, u, T, W, out,
+                     static_cast<uint8_t*>(packed));
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu_bwd(const uint16_t* ds, const uint16_t* g, const uint16_t* u, int64_t n,
-                             uint16_t* dg, uint16_t* du, hipStream_t s) {
-  hipLaunchKernelGGL(k_swiglu_bwd, dim3(grid_of(n)), dim3(256), 0, s, ds, g, u, n, dg, du);
+hipError_t launch_swiglu_bwd(const uint16_t* ds, const uint16_t* g, const uint16_t* u, int64_t T,
+                             int64_t W, uint16_t* dg, uint16_t* du, void* dg_packed,
+                             void* du_packed, hipStream_t s) {
+  hipLaunchKernelGGL(k_swiglu_bwd, ew_grid(T, W), dim3(256), 0, s, ds, g, u, T, W, dg, du,
+                     static_cast<uint8_t*>(dg_packed), static_cast<uint8_t*>(du_packed));
   return hipGetLastError();
 }
 
@@ -1117,8 +1211,10 @@ hipError_t launch_residual_add(const float* h, const uint16_t* y, int64_t n, flo
   return hipGetLastError();
 }
 
-hipError_t launch_f32_to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s) {
-  hipLaunchKernelGGL(k_f32_to_bf16, dim3(grid_of(n)), dim3(256), 0, s, x, n, y);
+hipError_t launch_f32_to_bf16(const float* x, int64_t T, int64_t W, uint16_t* y, void* packed,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(k_f32_to_bf16, ew_grid(T, W), dim3(256), 0, s, x, T, W, y,
+                     static_cast<uint8_t*>(packed));
   return hipGetLastError();
 }
 

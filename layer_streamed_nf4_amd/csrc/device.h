@@ -41,4 +41,19 @@ __device__ __forceinline__ void dequant_word(uint32_t word, float a, const float
   }
 }
 
+// Byte offset of the 16 bytes holding row m, columns c .. c+7 (c a multiple of
+// 8) of a bf16 [M, K] matrix in MFMA fragment order (the layout k_frag_pack
+// writes): fragment (m/32, c/16), lane m%32 + 32*((c/8)%2); kb = 16-wide
+// blocks per 32-row block, 4 * ceil(K/64).
+__device__ __forceinline__ int64_t frag_offset(int64_t m, int64_t c, int64_t kb) {
+  return (((m >> 5) * kb + (c >> 4)) * 64 + (m & 31) + 32 * ((c >> 3) & 1)) * 16;
+}
+
+// Zero the padding of row m past K (up to the next multiple of 64), which
+// the GEMMs contract with zero weights and so must not be NaN.
+__device__ __forceinline__ void frag_zero_tail(uint8_t* packed, int64_t m, int64_t K, int64_t kb) {
+  for (int64_t c = K; c < kb * 16; c += 8)
+    *reinterpret_cast<uint4*>(packed + frag_offset(m, c, kb)) = make_uint4(0u, 0u, 0u, 0u);
+}
+
 }  // namespace nf4s

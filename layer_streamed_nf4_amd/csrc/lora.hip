@@ -22,7 +22,7 @@
 // chunk of the long contraction, its 4 waves take interleaved 16-wide slices,
 // their tiles are summed through LDS in wave order, and a second kernel adds
 // the chunks' partials in chunk order. Column kernel (dA, dB): one
-// workgroup per 32 output columns, its 8 waves take eighths of M, summed the
+// workgroup per 32 output columns, its 16 waves take sixteenths of M, summed the
 // same way.
 #include "common.h"
 #include "device.h"
@@ -157,7 +157,7 @@ hipError_t rowdot(bool trans_f, const uint16_t* X, int64_t M, int64_t K, const f
   return hipGetLastError();
 }
 
-constexpr int COL_WAVES = 8;
+constexpr int COL_WAVES = 16;
 constexpr int CUNR = 2;  // 16-row slices whose loads are issued together
 
 // out(r0 + j, c) (+)= scale * sum_m L[m, r0 + j] * G[m, c] for one 32-column

@@ -152,19 +152,25 @@ class Decoder:
                  nf4s_workspace_bytes(OP_CROSS_ENTROPY, M, 0, 0),
                  nf4s_workspace_bytes(OP_DENSE_FWD_PACKED, M, V, H),
                  nf4s_workspace_bytes(OP_DENSE_BWD_PACKED, M, V, H))
-        pk = max(nf4s_packed_activation_bytes(M, H), nf4s_packed_activation_bytes(M, V))
+        pk_layer = nf4s_packed_activation_bytes(M, H)
         for p in PROJ:
             no, ki = shapes[p]
             ws = max(ws, nf4s_workspace_bytes(OP_LINEAR_FWD_PACKED, M, no, ki),
                      nf4s_workspace_bytes(OP_LINEAR_BWD_PACKED, M, no, ki),
                      nf4s_workspace_bytes(OP_LORA_FWD, M, no, ki),
                      nf4s_workspace_bytes(OP_LORA_BWD, M, no, ki))
-            pk = max(pk, nf4s_packed_activation_bytes(M, ki), nf4s_packed_activation_bytes(M, no))
+            pk_layer = max(pk_layer, nf4s_packed_activation_bytes(M, ki),
+                           nf4s_packed_activation_bytes(M, no))
+        pk = max(pk_layer, nf4s_packed_activation_bytes(M, V))
         for grp in (("q", "k", "v"), ("gate", "up")):
             ws = max(ws, grouped_workspace_bytes([shapes[p][0] for p in grp], shapes[grp[0]][1], M))
         self.ws = torch.empty(_round_up(max(ws, ALIGN)), dtype=torch.uint8, device=dev)
+        # packed (MFMA fragment order) GEMM inputs: two buffers, so that the
+        # two outputs of the SwiGLU backward can both be produced packed
         self.packed = torch.empty(_round_up(pk), dtype=torch.uint8, device=dev)
+        self.packed_b = torch.empty(_round_up(pk_layer), dtype=torch.uint8, device=dev)
         self._packed_key = None
+        self._packed_key_b = None
 
         self.pool = None
         if mode == "streamed":
@@ -195,13 +201,25 @@ class Decoder:
         return self.ws.data_ptr(), self.ws.numel()
 
     def _pack(self, a, K):
-        """Pack a (bf16 [M, K]) for the matrix cores unless it was the last
-        input packed; projections sharing an input share the packing."""
+        """The packed form of a (bf16 [M, K]) for the matrix cores: the one
+        its producer wrote (see _produced), else packed now into the main
+        buffer unless it was the last input packed there."""
         key = (a.data_ptr(), K)
+        if key == self._packed_key_b:
+            return self.packed_b.data_ptr()
         if key != self._packed_key:
             nf4s_pack_activation(a.data_ptr(), self.M, K, self.packed.data_ptr(), self.packed.numel(),
                                  self._s)
             self._packed_key = key
+        return self.packed.data_ptr()
+
+    def _produced(self, a, K, second=False):
+        """Mark a (bf16 [M, K]) as written packed by its producer into the main
+        (or second) buffer; returns that buffer's pointer for the producer."""
+        if second:
+            self._packed_key_b = (a.data_ptr(), K)
+            return self.packed_b.data_ptr()
+        self._packed_key = (a.data_ptr(), K)
         return self.packed.data_ptr()
 
     def _fwd(self, base, i, ps, x, ys, adapters=True):
@@ -272,12 +290,12 @@ class Decoder:
         hin/hout default to the checkpoints h_i, h_{i+1}."""
         c, s, M = self.cfg, self._s, self.M
         H = self.H
-        self._packed_key = None
+        self._packed_key = self._packed_key_b = None
         hin = self.h[i] if hin is None else hin
         hout = self.h[i + 1] if hout is None else hout
         a = adapters
         nf4s_rmsnorm_fwd(hin.data_ptr(), self.norms["attn"][i].data_ptr(), M, H, c["eps"],
-                         self.n1.data_ptr(), self.rstd1.data_ptr(), s)
+                         self.n1.data_ptr(), self.rstd1.data_ptr(), s, packed=self._produced(self.n1, H))
         self._fwd(base, i, ("q", "k", "v"), self.n1, (self.q, self.k, self.vv), a)
         nf4s_rope(self.q.data_ptr(), M, self.S, c["heads"], c["head_dim"], c["rope_theta"], 0, s)
         nf4s_rope(self.k.data_ptr(), M, self.S, c["kv_heads"], c["head_dim"], c["rope_theta"], 0, s)
@@ -287,9 +305,10 @@ class Decoder:
         self._fwd(base, i, ("o",), self.o, (self.ao,), a)
         nf4s_residual_add(hin.data_ptr(), self.ao.data_ptr(), M * H, self.h_mid.data_ptr(), s)
         nf4s_rmsnorm_fwd(self.h_mid.data_ptr(), self.norms["mlp"][i].data_ptr(), M, H, c["eps"],
-                         self.n2.data_ptr(), self.rstd2.data_ptr(), s)
+                         self.n2.data_ptr(), self.rstd2.data_ptr(), s, packed=self._produced(self.n2, H))
         self._fwd(base, i, ("gate", "up"), self.n2, (self.g, self.u_), a)
-        nf4s_swiglu_fwd(self.g.data_ptr(), self.u_.data_ptr(), M * self.I, self.sw.data_ptr(), s)
+        nf4s_swiglu_fwd(self.g.data_ptr(), self.u_.data_ptr(), M, self.I, self.sw.data_ptr(), s,
+                        packed=self._produced(self.sw, self.I))
         self._fwd(base, i, ("down",), self.sw, (self.dn,), a)
         if not recompute:
             nf4s_residual_add(self.h_mid.data_ptr(), self.dn.data_ptr(), M * H, hout.data_ptr(), s)
@@ -298,18 +317,20 @@ class Decoder:
         """dh holds dL/dh_{i+1} on entry and dL/dh_i on exit; the layer's body
         was just recomputed (with the fp32 attention output kept)."""
         c, s, M, H = self.cfg, self._s, self.M, self.H
-        nf4s_to_bf16(self.dh.data_ptr(), M * H, self.dd.data_ptr(), s)
-        self._packed_key = None  # dd was rewritten
+        self._packed_key = self._packed_key_b = None
+        nf4s_to_bf16(self.dh.data_ptr(), M, H, self.dd.data_ptr(), s, packed=self._produced(self.dd, H))
         self._bwd(base, i, "down", self.sw, self.dd, self.dsw)
-        nf4s_swiglu_bwd(self.dsw.data_ptr(), self.g.data_ptr(), self.u_.data_ptr(), M * self.I,
-                        self.dg.data_ptr(), self.du_.data_ptr(), s)
+        nf4s_swiglu_bwd(self.dsw.data_ptr(), self.g.data_ptr(), self.u_.data_ptr(), M, self.I,
+                        self.dg.data_ptr(), self.du_.data_ptr(), s,
+                        dg_packed=self._produced(self.dg, self.I),
+                        du_packed=self._produced(self.du_, self.I, second=True))
         self._bwd(base, i, "gate", self.n2, self.dg, self.dnx[0])
         self._bwd(base, i, "up", self.n2, self.du_, self.dnx[1])
         nf4s_rmsnorm_bwd([self.dnx[0].data_ptr(), self.dnx[1].data_ptr()], self.h_mid.data_ptr(),
                          self.norms["mlp"][i].data_ptr(), self.rstd2.data_ptr(), M, H, 1,
                          self.dh.data_ptr(), s)
-        nf4s_to_bf16(self.dh.data_ptr(), M * H, self.dd.data_ptr(), s)
-        self._packed_key = None
+        self._packed_key_b = None
+        nf4s_to_bf16(self.dh.data_ptr(), M, H, self.dd.data_ptr(), s, packed=self._produced(self.dd, H))
         self._bwd(base, i, "o", self.o, self.dd, self.do)
         nf4s_attention_bwd(self.q.data_ptr(), self.k.data_ptr(), self.vv.data_ptr(),
                            self.o32.data_ptr(), self.do.data_ptr(), self.lse.data_ptr(), self.B,
@@ -332,9 +353,9 @@ class Decoder:
     def _head_fwd(self, h_last):
         """Final norm and the resident lm_head: self.logits from h_L."""
         c, M, H, V, s = self.cfg, self.M, self.H, self.V, self._s
-        self._packed_key = None
+        self._packed_key = self._packed_key_b = None
         nf4s_rmsnorm_fwd(h_last.data_ptr(), self.norms["final"].data_ptr(), M, H, c["eps"],
-                         self.hn.data_ptr(), self.rstd_f.data_ptr(), s)
+                         self.hn.data_ptr(), self.rstd_f.data_ptr(), s, packed=self._produced(self.hn, H))
         dense_linear_fwd_packed(self.lm_head.data_ptr(), V, H, self._pack(self.hn, H), M,
                                 self.logits.data_ptr(), *self._ws(), s)
 
@@ -355,7 +376,7 @@ class Decoder:
         """From self.dlogits: lm_head and final norm backward, then the
         backward sweep that recomputes each layer and differentiates it."""
         M, H, V, s, L = self.M, self.H, self.V, self._s, self.L
-        self._packed_key = None
+        self._packed_key = self._packed_key_b = None
         dense_linear_bwd_packed(self.lm_head.data_ptr(), V, H, self._pack(self.dlogits, V), M,
                                 self.dhn.data_ptr(), *self._ws(), s)
         nf4s_rmsnorm_bwd([self.dhn.data_ptr()], self.h[L].data_ptr(), self.norms["final"].data_ptr(),

@@ -258,9 +258,16 @@ def test_decoder_argument_errors():
     assert _err(L.nf4s_cross_entropy, FAKE, FAKE, 8, 100, FAKE, FAKE, FAKE, 4) == L.EWORKSPACE
     assert _err(L.nf4s_cross_entropy, FAKE, FAKE + 4, 8, 100, FAKE, FAKE, FAKE, 1 << 20) == L.EALIGN
     assert _err(L.nf4s_embed, FAKE, 0, 64, FAKE, 4, FAKE) == L.ESHAPE
-    assert _err(L.nf4s_swiglu_fwd, FAKE, FAKE, 0, FAKE) == L.ESHAPE
+    assert _err(L.nf4s_swiglu_fwd, FAKE, FAKE, 0, 8, FAKE) == L.ESHAPE
+    assert _err(L.nf4s_swiglu_fwd, FAKE, FAKE, 4, 12, FAKE) == L.ESHAPE            # width % 8
+    assert _err(L.nf4s_swiglu_fwd, FAKE, FAKE, 4, 16, FAKE, 0, FAKE + 16) == L.EALIGN  # packed 256-B
+    assert _err(L.nf4s_swiglu_bwd, FAKE, FAKE, FAKE, 4, 16, FAKE, FAKE + 8) == L.EALIGN
+    assert _err(L.nf4s_swiglu_bwd, FAKE, FAKE, FAKE, 4, 16, FAKE, FAKE, 0, None, FAKE + 64) == L.EALIGN
+    assert _err(L.nf4s_rmsnorm_fwd, FAKE, FAKE, 4, 16, 1e-5, FAKE, FAKE, 0, FAKE + 32) == L.EALIGN
     assert _err(L.nf4s_residual_add, FAKE, FAKE, 16, None) == L.EINVAL
-    assert _err(L.nf4s_to_bf16, FAKE + 2, 16, FAKE) == L.EALIGN
+    assert _err(L.nf4s_to_bf16, FAKE + 2, 2, 8, FAKE) == L.EALIGN
+    assert _err(L.nf4s_to_bf16, FAKE, 2, 10, FAKE) == L.ESHAPE                     # width % 8
+    assert _err(L.nf4s_to_bf16, FAKE, 2, 8, FAKE, 0, FAKE + 128) == L.EALIGN
     # the dense (lm_head) GEMM: whole 64-blocks along k_in, split partials required
     assert _err(L.dense_linear_fwd_packed, FAKE, 256, 100, FAKE, 16, FAKE, None, 0) == L.ESHAPE
     need = L.nf4s_workspace_bytes(L.OP_DENSE_BWD_PACKED, 512, 128256, 4096)

@@ -155,23 +155,81 @@ def test_attention_fwd_bwd(B, S, H, Hkv, d):
     _check_bf16(host_u16(dv), D.bf16(rv).reshape(B * S, -1), abs_slack=1e-4, what="dv")
 
 
-@pytest.mark.parametrize("n", [1, 1000, 512 * 1536 + 7])
-def test_swiglu_fwd_bwd(n):
+@pytest.mark.parametrize("T,W", [(1, 8), (5, 1000), (512, 1536)])
+def test_swiglu_fwd_bwd(T, W):
     require_gpu()
     g = _rng(40)
+    n = T * W
     gb, ub, db = (_bits(g.standard_normal(n) * 3) for _ in range(3))
     gd, ud, dd = (dev_bf16bits(a) for a in (gb, ub, db))
     out = torch.empty(n, dtype=torch.int16, device="cuda")
     dg = torch.empty_like(out)
     du = torch.empty_like(out)
-    L.nf4s_swiglu_fwd(gd.data_ptr(), ud.data_ptr(), n, out.data_ptr(), stream())
-    L.nf4s_swiglu_bwd(dd.data_ptr(), gd.data_ptr(), ud.data_ptr(), n, dg.data_ptr(), du.data_ptr(), stream())
+    L.nf4s_swiglu_fwd(gd.data_ptr(), ud.data_ptr(), T, W, out.data_ptr(), stream())
+    L.nf4s_swiglu_bwd(dd.data_ptr(), gd.data_ptr(), ud.data_ptr(), T, W, dg.data_ptr(), du.data_ptr(),
+                      stream())
     torch.cuda.synchronize()
     gv, uv, dv = _vals(gb), _vals(ub), _vals(db)
     _check_bf16(host_u16(out), D.bf16(D.silu(gv) * uv), abs_slack=1e-6, what="swiglu")
     rg, ru = D.swiglu_bwd(dv, gv, uv)
     _check_bf16(host_u16(dg), D.bf16(rg), abs_slack=1e-6, what="dg")
     _check_bf16(host_u16(du), D.bf16(ru), abs_slack=1e-6, what="du")
+
+
+@pytest.mark.parametrize("T,W", [(37, 72), (300, 576), (512, 1536), (33, 4104)])
+def test_producers_write_the_packed_layout(T, W):
+    """RMSNorm, SwiGLU (both directions) and the fp32 -> bf16 rounding write
+    their bf16 result a second time in MFMA fragment order: equal, byte for
+    byte, to nf4s_pack_activation of the row-major result in every row < T
+    (columns past W zero); rows past T are left untouched."""
+    require_gpu()
+    print(f"packed producers T={T} W={W}", flush=True)
+    g = _rng(60 + W)
+    nbytes = L.nf4s_packed_activation_bytes(T, W)
+    kb = nbytes // ((T + 255) // 256 * 256) // 2 // 16   # 16-wide blocks per 32-row block
+    s = stream()
+
+    def packed_rows_equal(y, packed):
+        ref = ws_tensor(nbytes)
+        L.nf4s_pack_activation(y.data_ptr(), T, W, ref.data_ptr(), nbytes, s)
+        torch.cuda.synchronize()
+        a = packed.cpu().numpy()[:nbytes].reshape(-1, kb, 64, 16)
+        b = ref.cpu().numpy()[:nbytes].reshape(-1, kb, 64, 16)
+        rows = np.arange(a.shape[0] * 32)
+        for blk in range(a.shape[0]):
+            valid = (rows[blk * 32:(blk + 1) * 32] < T)
+            lanes = np.concatenate([valid, valid])   # lane l holds row l % 32
+            assert np.array_equal(a[blk][:, lanes], b[blk][:, lanes]), blk
+            assert not np.any(b[blk][:, ~lanes])     # the reference pads with zeros
+
+    sentinel = lambda: torch.full((nbytes,), 0x7F, dtype=torch.uint8, device="cuda")  # noqa: E731
+    x = dev_f32(g.standard_normal((T, W)).astype(np.float32))
+    w = dev_f32((1 + 0.1 * g.standard_normal(W)).astype(np.float32))
+    y = torch.empty((T, W), dtype=torch.int16, device="cuda")
+    rstd = torch.empty(T, dtype=torch.float32, device="cuda")
+    pk = sentinel()
+    L.nf4s_rmsnorm_fwd(x.data_ptr(), w.data_ptr(), T, W, 1e-5, y.data_ptr(), rstd.data_ptr(), s,
+                       packed=pk.data_ptr())
+    packed_rows_equal(y, pk)
+    gb, ub, db = (dev_bf16bits(_bits(g.standard_normal((T, W)) * 2)) for _ in range(3))
+    pk = sentinel()
+    L.nf4s_swiglu_fwd(gb.data_ptr(), ub.data_ptr(), T, W, y.data_ptr(), s, packed=pk.data_ptr())
+    packed_rows_equal(y, pk)
+    dgo, duo = torch.empty_like(y), torch.empty_like(y)
+    pg, pu = sentinel(), sentinel()
+    L.nf4s_swiglu_bwd(db.data_ptr(), gb.data_ptr(), ub.data_ptr(), T, W, dgo.data_ptr(), duo.data_ptr(),
+                      s, dg_packed=pg.data_ptr(), du_packed=pu.data_ptr())
+    packed_rows_equal(dgo, pg)
+    packed_rows_equal(duo, pu)
+    pk = sentinel()
+    L.nf4s_to_bf16(x.data_ptr(), T, W, y.data_ptr(), s, packed=pk.data_ptr())
+    packed_rows_equal(y, pk)
+    # rows past T keep the sentinel
+    if (T + 255) // 256 * 256 > T:
+        a = pk.cpu().numpy()[:nbytes].reshape(-1, kb, 64, 16)
+        last = a[T // 32]
+        lanes = np.concatenate([np.arange(32) + (T // 32) * 32 >= T] * 2)
+        assert np.all(last[:, lanes] == 0x7F)
 
 
 @pytest.mark.parametrize("T,V", [(37, 1000), (4, 49152), (2, 128256), (3, 1001)])

@@ -69,7 +69,10 @@ constexpr int NSTAGE = 4;             // LDS ring of decoded weight stages
 constexpr int LDS_STRIDE = 72;        // bf16 elements per LDS row (64 + 8 pad = 144 B)
 constexpr int STAGE_ELEMS = BN * LDS_STRIDE;
 constexpr int PAIR_COPIES = 32;
-constexpr int SMEM_BYTES = NSTAGE * STAGE_ELEMS * 2 + 256 * PAIR_COPIES * 8 + 256 * 4;
+// backward: the block scales of a stage (2 column blocks x 64 rows), a ring of NSTAGE
+constexpr int SCALE_FLOATS = 2 * 64;
+constexpr int SMEM_BYTES = NSTAGE * STAGE_ELEMS * 2 + 256 * PAIR_COPIES * 8 + 256 * 4 +
+                           NSTAGE * SCALE_FLOATS * 4;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
 
@@ -197,21 +200,26 @@ __device__ __forceinline__ void load_b(const GemmArgs& g, const WLanes<false>& L
 }
 
 // Backward: producer thread pt owns weight rows k0 + 4*(pt/16) + i (i < 4) and
-// output columns n0 + 8*(pt%16) + j (j < 8): four packed words, four 8-bit
-// scale codes packed in one register, four nested scales, a validity mask.
+// output columns n0 + 8*(pt%16) + j (j < 8): four packed words. The 128
+// block scales of a step (64 rows x 2 column blocks of 64) are loaded and
+// decoded once, by producer threads 0..127 (row pt/2, column block pt%2),
+// and shared through LDS; a scale is 0 for a row past the contraction or a
+// column block past k_in, which zeroes the decoded weights there.
 template <>
 struct WLanes<true> {
   uint32_t woff[4];  // byte offsets of the packed words at contraction 0
-  uint32_t blk0[4];  // 64-block indices at contraction 0
   uint32_t col;      // first (clamped) column
   bool cvalid;       // columns < k_in
+  bool sload;        // this thread loads a block scale
+  bool scol;         // its column block lies inside k_in
+  uint32_t sblk;     // its column block index (clamped)
 };
 template <>
 struct BRegs<true> {
   uint32_t w[4];
-  uint32_t q;
-  float nest[4];
-  uint32_t vmask;
+  uint32_t q;    // (scale loaders) raw 8-bit scale code
+  float nest;    // (scale loaders) nested scale
+  bool sok;      // (scale loaders) row and column block inside the weight
 };
 
 __device__ __forceinline__ WLanes<true> w_lanes(const GemmArgs& g, int64_t n0, int pt,
@@ -224,39 +232,35 @@ __device__ __forceinline__ WLanes<true> w_lanes(const GemmArgs& g, int64_t n0, i
   for (int i = 0; i < 4; ++i) {
     const int64_t row = 4 * (pt >> 4) + i;  // relative to the step's start
     L.woff[i] = (uint32_t)((row * g.k_in + col) / 2);
-    L.blk0[i] = (uint32_t)((row * g.k_in + col) / 64);
   }
   L.col = (uint32_t)col;
+  L.sload = pt < 2 * 64;
+  const int64_t bcol = n0 + 64 * (pt & 1);
+  L.scol = bcol < g.k_in;
+  L.sblk = (uint32_t)((L.scol ? bcol : 0) / 64);
   return L;
 }
 
 __device__ __forceinline__ void load_b(const GemmArgs& g, const WLanes<true>& L, Step s, int pt,
                                        BRegs<true>& rb) {
-  rb.q = 0;
   if (s.k0 + BK <= g.Kc) {  // uniform: every row of the step exists
     const uint8_t* base = g.packed + s.k0 * (g.k_in / 2);
-    const uint32_t bstep = (uint32_t)(s.k0 * (g.k_in / 64));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      rb.w[i] = *reinterpret_cast<const uint32_t*>(base + L.woff[i]);
-      const uint32_t blk = bstep + L.blk0[i];
-      rb.q |= (uint32_t)g.q8[blk] << (8 * i);
-      rb.nest[i] = g.nested[blk >> 8];
-    }
-    rb.vmask = L.cvalid ? 0xFu : 0u;
+    for (int i = 0; i < 4; ++i) rb.w[i] = *reinterpret_cast<const uint32_t*>(base + L.woff[i]);
   } else {  // the last step of a contraction that is not a multiple of 64
-    rb.vmask = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t row = s.k0 + 4 * (pt >> 4) + i;
-      const bool ok = row < g.Kc;
-      const int64_t e = (ok ? row : g.Kc - 1) * g.k_in + L.col;  // code index
+      const int64_t e = (row < g.Kc ? row : g.Kc - 1) * g.k_in + L.col;  // code index
       rb.w[i] = *reinterpret_cast<const uint32_t*>(g.packed + e / 2);
-      const uint32_t blk = (uint32_t)(e / 64);
-      rb.q |= (uint32_t)g.q8[blk] << (8 * i);
-      rb.nest[i] = g.nested[blk >> 8];
-      rb.vmask |= (L.cvalid && ok) ? (1u << i) : 0u;
     }
+  }
+  if (L.sload) {  // uniform per wave
+    const int64_t row = s.k0 + (pt >> 1);
+    rb.sok = L.scol && row < g.Kc;
+    const uint32_t blk = (uint32_t)((row < g.Kc ? row : g.Kc - 1) * (g.k_in / 64)) + L.sblk;
+    rb.q = g.q8[blk];
+    rb.nest = g.nested[blk >> 8];
   }
 }
 
@@ -309,27 +313,30 @@ __device__ __forceinline__ int bwd_swizzle_off(int col, int k) {
   return ((((k >> 3) ^ (col >> 3)) & 7) << 3) | (k & 7);
 }
 
+// Also decodes and publishes the thread's block scale (scale loaders), for
+// the stage's decode after the next workgroup barrier; sc is the stage's
+// slot of the scale ring.
 __device__ __forceinline__ void prep_reads(const BRegs<true>& rb, const float2* ptab,
-                                           const float* c8, Prep<4>& pp) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pp.c8v[i] = c8[(rb.q >> (8 * i)) & 0xFFu];
+                                           const float* c8, Prep<1>& pp, float* sc, float off,
+                                           int pt) {
+  float cq = 0.0f;
+  if (pt < 2 * 64) cq = c8[rb.q];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int i = 0; i < 4; ++i) pp.v[q * 4 + i] = pair_of(ptab, rb.w[i], q);
+  if (pt < 2 * 64) sc[(pt & 1) * 64 + (pt >> 1)] = rb.sok ? decode_scale(cq, rb.nest, off) : 0.0f;
 }
 
 // Backward stage: byte q of each of the thread's four row words gives output
 // columns 2q and 2q+1 of its 4x8 patch, each written as 4 consecutive
 // contraction values -- the transpose into the matrix-core layout happens
 // here, in the bf16 pairing.
-__device__ __forceinline__ void finish_stage(uint16_t* Bs, const BRegs<true>& rb, const Prep<4>& pp,
-                                             bool, float off, int pt) {
-  float a[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    a[i] = ((rb.vmask >> i) & 1u) ? decode_scale(pp.c8v[i], rb.nest[i], off) : 0.0f;
+__device__ __forceinline__ void finish_stage(uint16_t* Bs, const BRegs<true>&, const Prep<1>& pp,
+                                             const float* sc, int pt) {
   const int r0 = 4 * (pt >> 4);
+  const float4 a4 = *reinterpret_cast<const float4*>(sc + ((pt & 15) >> 3) * 64 + r0);
+  const float a[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     float v0[4], v1[4];
@@ -502,6 +509,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
   uint16_t* const Bs0 = reinterpret_cast<uint16_t*>(smem);
   float2* const s_pair_all = reinterpret_cast<float2*>(smem + NSTAGE * STAGE_ELEMS * 2);
   float* const s_c8 = reinterpret_cast<float*>(smem + NSTAGE * STAGE_ELEMS * 2 + 256 * PAIR_COPIES * 8);
+  float* const s_scale =
+      reinterpret_cast<float*>(smem + NSTAGE * STAGE_ELEMS * 2 + 256 * PAIR_COPIES * 8 + 256 * 4);
 
   const int t = threadIdx.x;
   if (!DENSE && t < 256) {
@@ -549,6 +558,10 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
     load_a(g, al, step_of(0).k0, ar0);
     load_a(g, al, step_of(1).k0, ar1);
     __syncthreads();  // tables in LDS
+    if constexpr (BWD && !DENSE) {
+      __syncthreads();  // block scales of stage 0 published
+      __syncthreads();  // block scales of stage 1 published
+    }
     __syncthreads();  // weight stages 0 and 1 decoded
     bf16x8_t fb0[4];  // fragments of sub-step 0 of the stage about to be multiplied
 #pragma unroll
@@ -699,26 +712,37 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
     const float off = g.offset[0];
     const float2* s_pair = s_pair_all + (t & (PAIR_COPIES - 1));
     BRegs<BWD> wb0, wb1, wb2, wb3;
-    Prep<BWD ? 4 : 1> pp;
+    Prep<1> pp;
+    // table lookups of stage st (backward: also publish its block scales)
+    auto prep = [&](const BRegs<BWD>& rb, int st) {
+      if constexpr (BWD) prep_reads(rb, s_pair, s_c8, pp, s_scale + st * SCALE_FLOATS, off, pt);
+      else prep_reads(rb, s_pair, s_c8, pp);
+    };
+    auto fin = [&](const BRegs<BWD>& rb, int st) {
+      if constexpr (BWD) finish_stage(stage(st), rb, pp, s_scale + st * SCALE_FLOATS, pt);
+      else finish_stage(stage(st), rb, pp, valid, off, pt);
+    };
     load_b(g, wl, step_of(0), pt, wb0);
     load_b(g, wl, step_of(1), pt, wb1);
     load_b(g, wl, step_of(2), pt, wb2);
     load_b(g, wl, step_of(3), pt, wb3);
     __syncthreads();  // tables in LDS
-    prep_reads(wb0, s_pair, s_c8, pp);
-    finish_stage(stage(0), wb0, pp, valid, off, pt);
+    prep(wb0, 0);
+    if constexpr (BWD) __syncthreads();  // block scales of stage 0 published
+    fin(wb0, 0);
     load_b(g, wl, step_of(4), pt, wb0);
-    prep_reads(wb1, s_pair, s_c8, pp);
-    finish_stage(stage(1), wb1, pp, valid, off, pt);
-    prep_reads(wb2, s_pair, s_c8, pp);
+    prep(wb1, 1);
+    if constexpr (BWD) __syncthreads();  // block scales of stage 1 published
+    fin(wb1, 1);
+    prep(wb2, 2);
     __syncthreads();
 // (the scheduling barriers keep the next stage's decode arithmetic below the
 // workgroup barrier, so the table lookups issued here overlap the wait)
 #define NF4S_PRODUCER_STEP(KT, SM, WFIN, WPREP, WLD)                                 \
   do {                                                                               \
     load_b(g, wl, step_of((KT) + 5), pt, WLD);                                       \
-    finish_stage(stage(((SM) + 2) % NSTAGE), WFIN, pp, valid, off, pt);              \
-    prep_reads(WPREP, s_pair, s_c8, pp);                                             \
+    fin(WFIN, ((SM) + 2) % NSTAGE);                                                  \
+    prep(WPREP, ((SM) + 3) % NSTAGE);                                                \
     __builtin_amdgcn_sched_barrier(0);                                               \
     __syncthreads();                                                                 \
     __builtin_amdgcn_sched_barrier(0);                                               \

@@ -382,7 +382,7 @@ __device__ __forceinline__ void park(float* part, int wave, int lane, const floa
 }
 
 template <int D>
-__global__ __launch_bounds__(64 * AW, 1) void k_attn_fwd(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * AW, 2) void k_attn_fwd(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v, int64_t S,
                                                          int H, int Hkv, uint16_t* __restrict__ o,

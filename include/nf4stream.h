@@ -300,6 +300,32 @@ int lora_bwd(const uint16_t* x, const uint16_t* dy, const float* u, int64_t M, i
              int64_t n_out, const float* B, int r, float scale, float* dA, float* dB,
              float* du_out, int accumulate, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Grouped adapters ([G] s2.1: the q and v adapters of a layer read the same
+ * normed input x): n in [1, NF4S_MAX_LORA_GROUP] adapters in one launch of
+ * each kernel. The array arguments are host arrays of n device pointers (or,
+ * for n_outs, of n output widths); entry i is what the single call of adapter
+ * i takes, with the same alignment and shape rules:
+ *   lora_fwd_grouped: u_out[i] = x.A[i]^T;
+ *   lora_bwd_grouped: du_out[i], dB[i], dA[i] as lora_bwd(x, dy[i], u[i],
+ *     n_outs[i], B[i]), one scale and accumulate flag for the group.
+ * Results are bit-identical to the n single calls (same kernels and
+ * reduction order per adapter).
+ * ws: nf4s_lora_grouped_workspace_bytes(n, n_outs, k_in, M, backward) bytes
+ * (the sum of the single calls' workspaces; the forward ignores n_outs'
+ * values but takes the array). Errors: EINVAL (n out of range, NULL arrays),
+ * ESHAPE, EALIGN, EWORKSPACE.
+ */
+#define NF4S_MAX_LORA_GROUP 3
+int nf4s_lora_grouped_workspace_bytes(int n, const int64_t* n_outs, int64_t k_in, int64_t M,
+                                      int backward, size_t* bytes);
+int lora_fwd_grouped(const uint16_t* x, int64_t M, int64_t k_in, const float* const* A, int n, int r,
+                     float* const* u_out, void* ws, size_t ws_bytes, void* stream);
+int lora_bwd_grouped(const uint16_t* x, const uint16_t* const* dy, const float* const* u, int64_t M,
+                     int64_t k_in, const int64_t* n_outs, const float* const* B, int n, int r,
+                     float scale, float* const* dA, float* const* dB, float* const* du_out,
+                     int accumulate, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- the decoder around the streamed linears ----------------------------
  *
  * [G] s2.1-s2.2 and s4.3: a llama decoder (SmolLM2-135M, Llama-3.1-8B) whose

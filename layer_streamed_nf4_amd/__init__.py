@@ -35,6 +35,7 @@ EXPORTS = (
     "nf4s_packed_activation_bytes", "nf4s_pack_activation", "streamed_linear_fwd_packed",
     "streamed_linear_bwd_packed", "dense_linear_fwd_packed", "dense_linear_bwd_packed",
     "nf4s_grouped_workspace_bytes", "streamed_linear_fwd_grouped",
+    "nf4s_lora_grouped_workspace_bytes", "lora_fwd_grouped", "lora_bwd_grouped",
     "nf4s_embed", "nf4s_rmsnorm_fwd", "nf4s_rmsnorm_bwd", "nf4s_rope", "nf4s_attention_fwd",
     "nf4s_attention_bwd", "nf4s_swiglu_fwd", "nf4s_swiglu_bwd", "nf4s_residual_add",
     "nf4s_to_bf16", "nf4s_cross_entropy", "nf4s_adamw", "nf4s_token_nll", "nf4s_dpo_loss",
@@ -110,6 +111,13 @@ _SIG = {
     "streamed_linear_fwd_grouped": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), ctypes.c_int, _P,
                                                    _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float,
                                                    _P, ctypes.c_size_t, _P]),
+    "nf4s_lora_grouped_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, ctypes.c_int,
+                                                         _P]),
+    "lora_fwd_grouped": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, ctypes.c_int, _P, _P,
+                                        ctypes.c_size_t, _P]),
+    "lora_bwd_grouped": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_float, _P, _P, _P, ctypes.c_int, _P, ctypes.c_size_t,
+                                        _P]),
     "dense_linear_fwd_packed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
     "dense_linear_bwd_packed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
     "nf4s_embed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P]),
@@ -337,6 +345,32 @@ def lora_bwd(x, dy, u, M, k_in, n_out, B, r, scale, dA, dB, du_out, accumulate, 
              stream=0):
     _check(lib().lora_bwd(x, dy, u, M, k_in, n_out, B, r, scale, dA, dB, du_out, accumulate, ws,
                           ws_bytes, stream))
+
+
+def _i64_array(vals):
+    return ctypes.cast((ctypes.c_int64 * len(vals))(*vals), ctypes.c_void_p)
+
+
+def lora_grouped_workspace_bytes(n_outs, k_in, M, backward):
+    """Workspace of lora_fwd_grouped / lora_bwd_grouped (any rank up to the maximum)."""
+    out = ctypes.c_size_t()
+    _check(lib().nf4s_lora_grouped_workspace_bytes(len(n_outs), _i64_array(n_outs), k_in, M,
+                                                   int(bool(backward)), ctypes.byref(out)))
+    return out.value
+
+
+def lora_fwd_grouped(x, M, k_in, As, r, u_outs, ws, ws_bytes, stream=0):
+    """u_outs[i] = x.As[i]^T for the adapters reading x, in one launch per kernel."""
+    _check(lib().lora_fwd_grouped(x, M, k_in, _ptr_array(As), len(As), r, _ptr_array(u_outs), ws,
+                                  ws_bytes, stream))
+
+
+def lora_bwd_grouped(x, dys, us, M, k_in, n_outs, Bs, r, scale, dAs, dBs, du_outs, accumulate, ws,
+                     ws_bytes, stream=0):
+    """lora_bwd of each adapter reading x (lists of device pointers), one launch per kernel."""
+    _check(lib().lora_bwd_grouped(x, _ptr_array(dys), _ptr_array(us), M, k_in, _i64_array(n_outs),
+                                  _ptr_array(Bs), len(Bs), r, scale, _ptr_array(dAs), _ptr_array(dBs),
+                                  _ptr_array(du_outs), accumulate, ws, ws_bytes, stream))
 
 
 def layer_prefetch(slot, slot_bytes, host_src, nbytes, copy_stream, wait_free=None, record_ready=None):

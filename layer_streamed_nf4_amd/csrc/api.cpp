@@ -471,6 +471,86 @@ int lora_bwd(const uint16_t* x, const uint16_t* dy, const float* u, int64_t M, i
   return e == hipSuccess ? NF4S_OK : hip_fail(e, "lora_bwd launch");
 }
 
+namespace {
+int check_lora_group(int n, const int64_t* n_outs, int64_t k_in, int64_t M) {
+  if (n < 1 || n > NF4S_MAX_LORA_GROUP)
+    return fail(NF4S_EINVAL, "group of %d adapters (1..%d allowed)", n, NF4S_MAX_LORA_GROUP);
+  if (!n_outs) return fail(NF4S_EINVAL, "n_outs is NULL");
+  if (M <= 0) return fail(NF4S_ESHAPE, "M=%lld must be positive", (long long)M);
+  int rc;
+  for (int i = 0; i < n; ++i) {
+    if ((rc = check_shape(n_outs[i], k_in))) return rc;
+    if (M * (n_outs[i] > k_in ? n_outs[i] : k_in) >= (1ll << 31))
+      return fail(NF4S_ESHAPE, "M x width too large for the adapter kernels");
+  }
+  return NF4S_OK;
+}
+
+size_t lora_group_ws(int n, const int64_t* n_outs, int64_t k_in, int64_t M, int r, bool bwd) {
+  size_t b = 0;
+  for (int i = 0; i < n; ++i)
+    b += bwd ? lora_bwd_ws_bytes(M, n_outs[i], r) : lora_fwd_ws_bytes(M, k_in, r);
+  return b;
+}
+
+int check_ptrs(const void* const* p, int n, const char* what, int align) {
+  if (!p) return fail(NF4S_EINVAL, "%s is NULL", what);
+  int rc;
+  for (int i = 0; i < n; ++i)
+    if ((rc = check_ptr(p[i], what, align))) return rc;
+  return NF4S_OK;
+}
+}  // namespace
+
+int nf4s_lora_grouped_workspace_bytes(int n, const int64_t* n_outs, int64_t k_in, int64_t M,
+                                      int backward, size_t* bytes) {
+  if (!bytes) return fail(NF4S_EINVAL, "bytes is NULL");
+  int rc;
+  if ((rc = check_lora_group(n, n_outs, k_in, M))) return rc;
+  *bytes = lora_group_ws(n, n_outs, k_in, M, NF4S_MAX_RANK, backward != 0);
+  return NF4S_OK;
+}
+
+int lora_fwd_grouped(const uint16_t* x, int64_t M, int64_t k_in, const float* const* A, int n, int r,
+                     float* const* u_out, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  int64_t n_outs[NF4S_MAX_LORA_GROUP];
+  if (n >= 1 && n <= NF4S_MAX_LORA_GROUP)
+    for (int i = 0; i < n; ++i) n_outs[i] = 64;  // the forward reads no output width
+  if ((rc = check_lora_group(n, n_outs, k_in, M))) return rc;
+  if ((rc = check_rank(r))) return rc;
+  if ((rc = check_ptr(x, "x"))) return rc;
+  if ((rc = check_ptrs(reinterpret_cast<const void* const*>(A), n, "A", 4))) return rc;
+  if ((rc = check_ptrs(reinterpret_cast<const void* const*>(u_out), n, "u_out", 4))) return rc;
+  if ((rc = check_ws(ws, ws_bytes, lora_group_ws(n, n_outs, k_in, M, r, false)))) return rc;
+  hipError_t e =
+      launch_lora_fwd_grouped(x, M, k_in, A, n, r, u_out, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "lora_fwd_grouped launch");
+}
+
+int lora_bwd_grouped(const uint16_t* x, const uint16_t* const* dy, const float* const* u, int64_t M,
+                     int64_t k_in, const int64_t* n_outs, const float* const* B, int n, int r,
+                     float scale, float* const* dA, float* const* dB, float* const* du_out,
+                     int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_lora_group(n, n_outs, k_in, M))) return rc;
+  if ((rc = check_rank(r))) return rc;
+  if (!std::isfinite(scale)) return fail(NF4S_EINVAL, "scale is not finite");
+  if (accumulate != 0 && accumulate != 1) return fail(NF4S_EINVAL, "accumulate must be 0 or 1");
+  if ((rc = check_ptr(x, "x"))) return rc;
+  if ((rc = check_ptrs(reinterpret_cast<const void* const*>(dy), n, "dy", 16))) return rc;
+  if ((rc = check_ptrs(reinterpret_cast<const void* const*>(u), n, "u", 4))) return rc;
+  if ((rc = check_ptrs(reinterpret_cast<const void* const*>(B), n, "B", 4))) return rc;
+  if ((rc = check_ptrs(reinterpret_cast<const void* const*>(dA), n, "dA", 4))) return rc;
+  if ((rc = check_ptrs(reinterpret_cast<const void* const*>(dB), n, "dB", 4))) return rc;
+  if ((rc = check_ptrs(reinterpret_cast<const void* const*>(du_out), n, "du_out", 4))) return rc;
+  if (M * r >= (1ll << 31)) return fail(NF4S_ESHAPE, "M x r too large for the adapter kernels");
+  if ((rc = check_ws(ws, ws_bytes, lora_group_ws(n, n_outs, k_in, M, r, true)))) return rc;
+  hipError_t e = launch_lora_bwd_grouped(x, dy, u, M, k_in, n_outs, B, n, r, scale, dA, dB, du_out,
+                                         accumulate, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "lora_bwd_grouped launch");
+}
+
 int layer_prefetch(void* slot_dev, size_t slot_bytes, const void* host_pinned_src, size_t bytes,
                    void* copy_stream, void* wait_slot_free, void* record_ready) {
   int rc;

@@ -94,6 +94,15 @@ hipError_t launch_lora_bwd(const uint16_t* x, const uint16_t* dy, const float* u
                            float* dA, float* dB, float* du, int accumulate, void* ws,
                            hipStream_t s);
 size_t lora_bwd_ws_bytes(int64_t M, int64_t n_out, int r);
+// n (<= 3) adapters reading one input x in one launch of each kernel; their
+// workspaces (as above) follow each other in ws
+hipError_t launch_lora_fwd_grouped(const uint16_t* x, int64_t M, int64_t k_in, const float* const* A,
+                                   int n, int r, float* const* u, void* ws, hipStream_t s);
+hipError_t launch_lora_bwd_grouped(const uint16_t* x, const uint16_t* const* dy,
+                                   const float* const* u, int64_t M, int64_t k_in,
+                                   const int64_t* n_out, const float* const* B, int n, int r,
+                                   float scale, float* const* dA, float* const* dB,
+                                   float* const* du, int accumulate, void* ws, hipStream_t s);
 
 // Decoder kernels (decoder.hip).
 hipError_t launch_embed(const uint16_t* E, int64_t V, const int64_t* ids, int64_t T, int64_t H,

@@ -56,24 +56,43 @@ constexpr int ROW_WAVES = 4;
 constexpr int UNR = 8;                        // 16-wide slices per wave, loads issued together
 constexpr int ROW_CHUNK = ROW_WAVES * UNR * 16;  // contraction handled by one workgroup (512)
 
+// Adapters of one launch (the projections that read one input, e.g. q and
+// v): the grid's last dimension runs over them.
+constexpr int LORA_MAX = NF4S_MAX_LORA_GROUP;
+struct RowsSeg {
+  const uint16_t* X;  // [M, K]
+  const float* F;     // A [r, K] or B [K, r]
+  float* part;        // [nks, M, r] chunk partials
+  float* out;         // [M, r]
+  int64_t K;
+  int nks;            // 512-wide chunks of K
+};
+struct RowsArgs {
+  RowsSeg seg[LORA_MAX];
+};
+
 // Partial row dots: part[ks, m, r0 + j] = sum over k in chunk ks of
 // X[m, k] * F(r0 + j, k), for one 32-row tile of m. F(j, k) = Fm[j * K + k]
 // (TRANS_F = false: A [r, K]) or Fm[k * r + j] (TRANS_F = true: B [K, r]).
 // MFMA view: C[rho, m] = sum_k F'[rho, k] X[m, k], rho < 16 the hi halves,
 // rho >= 16 the lo halves. Wave w takes slices w, w + 4, ... of the chunk; the
 // UNR loads of a wave are issued before its MFMAs; the 4 wave tiles are summed
-// through LDS in wave order.
+// through LDS in wave order. blockIdx.z = rank chunk + rch * adapter.
 template <bool TRANS_F>
-__global__ __launch_bounds__(ROW_WAVES * 64) void k_lora_rows(const uint16_t* __restrict__ X,
-                                                               int64_t M, int64_t K,
-                                                               const float* __restrict__ Fm, int r,
-                                                               float* __restrict__ part) {
+__global__ __launch_bounds__(ROW_WAVES * 64) void k_lora_rows(RowsArgs ra, int64_t M, int r, int rch) {
   __shared__ float s_part[ROW_WAVES][64][8];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int64_t m0 = (int64_t)blockIdx.x * 32;
   const int ks = blockIdx.y;
-  const int r0 = blockIdx.z * RCH;
+  const int ad = blockIdx.z / rch;
+  const int r0 = (blockIdx.z % rch) * RCH;
+  const RowsSeg& sg = ra.seg[ad];
+  if (ks >= sg.nks) return;  // uniform: this adapter's contraction has fewer chunks
+  const uint16_t* __restrict__ X = sg.X;
+  const float* __restrict__ Fm = sg.F;
+  float* __restrict__ part = sg.part;
+  const int64_t K = sg.K;
   const int rho = lane & 31;
   const bool lo = rho >= 16;
   const int j = r0 + (rho & 15);
@@ -128,53 +147,82 @@ __global__ __launch_bounds__(ROW_WAVES * 64) void k_lora_rows(const uint16_t* __
   }
 }
 
-// out[m, j] = scale * sum_ks part[ks, m, j], ks in order.
-__global__ __launch_bounds__(256) void k_rows_sum(const float* __restrict__ part, int nks,
-                                                  int64_t n, float scale,
-                                                  float* __restrict__ out) {
+// out[m, j] = scale * sum_ks part[ks, m, j], ks in order; blockIdx.y = adapter.
+__global__ __launch_bounds__(256) void k_rows_sum(RowsArgs ra, int64_t n, float scale) {
+  const RowsSeg& sg = ra.seg[blockIdx.y];
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  float s = part[i];
-  for (int p = 1; p < nks; ++p) s += part[(int64_t)p * n + i];
-  out[i] = scale * s;
+  float s = sg.part[i];
+  for (int p = 1; p < sg.nks; ++p) s += sg.part[(int64_t)p * n + i];
+  sg.out[i] = scale * s;
 }
 
 int64_t row_chunks(int64_t K) { return (K + ROW_CHUNK - 1) / ROW_CHUNK; }
 
-hipError_t rowdot(bool trans_f, const uint16_t* X, int64_t M, int64_t K, const float* F, int r,
-                  float scale, float* out, float* part, hipStream_t s) {
-  const int64_t nks = row_chunks(K);
-  const dim3 grid((unsigned)((M + 31) / 32), (unsigned)nks, (unsigned)((r + RCH - 1) / RCH));
+// n adapters: X[i] [M, K[i]] against F[i]; partials packed one after the other in ws
+hipError_t rowdot(bool trans_f, int n, const uint16_t* const* X, int64_t M, const int64_t* K,
+                  const float* const* F, int r, float scale, float* const* out, float* ws,
+                  hipStream_t s) {
+  RowsArgs ra = {};
+  int64_t nks_max = 0;
+  float* part = ws;
+  for (int i = 0; i < n; ++i) {
+    RowsSeg& sg = ra.seg[i];
+    sg.X = X[i];
+    sg.F = F[i];
+    sg.out = out[i];
+    sg.K = K[i];
+    sg.nks = (int)row_chunks(K[i]);
+    sg.part = part;
+    part += (size_t)sg.nks * (size_t)M * (size_t)r;
+    nks_max = sg.nks > nks_max ? sg.nks : nks_max;
+  }
+  const int rch = (r + RCH - 1) / RCH;
+  const dim3 grid((unsigned)((M + 31) / 32), (unsigned)nks_max, (unsigned)(rch * n));
   if (trans_f)
-    hipLaunchKernelGGL(k_lora_rows<true>, grid, dim3(ROW_WAVES * 64), 0, s, X, M, K, F, r, part);
+    hipLaunchKernelGGL(k_lora_rows<true>, grid, dim3(ROW_WAVES * 64), 0, s, ra, M, r, rch);
   else
-    hipLaunchKernelGGL(k_lora_rows<false>, grid, dim3(ROW_WAVES * 64), 0, s, X, M, K, F, r, part);
+    hipLaunchKernelGGL(k_lora_rows<false>, grid, dim3(ROW_WAVES * 64), 0, s, ra, M, r, rch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n = M * r;
-  hipLaunchKernelGGL(k_rows_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part,
-                     (int)nks, n, scale, out);
+  const int64_t nel = M * r;
+  hipLaunchKernelGGL(k_rows_sum, dim3((unsigned)((nel + 255) / 256), (unsigned)n), dim3(256), 0, s, ra,
+                     nel, scale);
   return hipGetLastError();
 }
 
 constexpr int COL_WAVES = 16;
 constexpr int CUNR = 2;  // 16-row slices whose loads are issued together
 
+struct ColsSeg {
+  const uint16_t* G;  // [M, N]
+  const float* L;     // [M, r]
+  float* out;         // [r, N] or [N, r]
+  int64_t N;
+};
+struct ColsArgs {
+  ColsSeg seg[LORA_MAX];
+};
+
 // out(r0 + j, c) (+)= scale * sum_m L[m, r0 + j] * G[m, c] for one 32-column
 // tile of c; out is [r, N] (dA) or, with TRANS_OUT, [N, r] (dB).
 // MFMA view: C[rho, c] = sum_m L'[rho, m] G[m, c]. The waves take consecutive
 // stretches of M; loads of CUNR 16-row slices are issued before their MFMAs.
+// blockIdx.z = adapter.
 template <bool TRANS_OUT>
-__global__ __launch_bounds__(COL_WAVES * 64) void k_lora_cols(const uint16_t* __restrict__ G,
-                                                              int64_t M, int64_t N,
-                                                              const float* __restrict__ Lm, int r,
-                                                              float scale, int accumulate,
-                                                              float* __restrict__ out) {
+__global__ __launch_bounds__(COL_WAVES * 64) void k_lora_cols(ColsArgs ca, int64_t M, int r,
+                                                              float scale, int accumulate) {
   __shared__ float s_part[COL_WAVES][64][8];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int64_t c0 = (int64_t)blockIdx.x * 32;
   const int r0 = blockIdx.y * RCH;
+  const ColsSeg& sg = ca.seg[blockIdx.z];
+  const int64_t N = sg.N;
+  if (c0 >= N) return;  // uniform: this adapter is narrower than the grid
+  const uint16_t* __restrict__ G = sg.G;
+  const float* __restrict__ Lm = sg.L;
+  float* __restrict__ out = sg.out;
   const int rho = lane & 31;
   const bool lo = rho >= 16;
   const int j = r0 + (rho & 15);
@@ -250,25 +298,52 @@ size_t lora_bwd_ws_bytes(int64_t M, int64_t n_out, int r) {
 
 hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t k_in, const float* A, int r,
                            float* u, void* ws, hipStream_t s) {
-  return rowdot(false, x, M, k_in, A, r, 1.0f, u, static_cast<float*>(ws), s);
+  return launch_lora_fwd_grouped(x, M, k_in, &A, 1, r, &u, ws, s);
+}
+
+hipError_t launch_lora_fwd_grouped(const uint16_t* x, int64_t M, int64_t k_in, const float* const* A,
+                                   int n, int r, float* const* u, void* ws, hipStream_t s) {
+  const uint16_t* X[LORA_MAX];
+  int64_t K[LORA_MAX];
+  for (int i = 0; i < n; ++i) {
+    X[i] = x;
+    K[i] = k_in;
+  }
+  return rowdot(false, n, X, M, K, A, r, 1.0f, u, static_cast<float*>(ws), s);
 }
 
 hipError_t launch_lora_bwd(const uint16_t* x, const uint16_t* dy, const float* u, int64_t M,
                            int64_t k_in, int64_t n_out, const float* B, int r, float scale,
                            float* dA, float* dB, float* du, int accumulate, void* ws,
                            hipStream_t s) {
+  return launch_lora_bwd_grouped(x, &dy, &u, M, k_in, &n_out, &B, 1, r, scale, &dA, &dB, &du,
+                                 accumulate, ws, s);
+}
+
+hipError_t launch_lora_bwd_grouped(const uint16_t* x, const uint16_t* const* dy,
+                                   const float* const* u, int64_t M, int64_t k_in,
+                                   const int64_t* n_out, const float* const* B, int n, int r,
+                                   float scale, float* const* dA, float* const* dB,
+                                   float* const* du, int accumulate, void* ws, hipStream_t s) {
   const unsigned rch = (unsigned)((r + RCH - 1) / RCH);
   // du = scale * dy . B
-  hipError_t e = rowdot(true, dy, M, n_out, B, r, scale, du, static_cast<float*>(ws), s);
+  hipError_t e = rowdot(true, n, dy, M, n_out, B, r, scale, du, static_cast<float*>(ws), s);
   if (e != hipSuccess) return e;
+  ColsArgs cb = {}, ca = {};
+  int64_t nmax = 0;
+  for (int i = 0; i < n; ++i) {
+    cb.seg[i] = ColsSeg{dy[i], u[i], dB[i], n_out[i]};
+    ca.seg[i] = ColsSeg{x, du[i], dA[i], k_in};
+    nmax = n_out[i] > nmax ? n_out[i] : nmax;
+  }
   // dB = scale * dy^T . u   ([n_out, r])
-  hipLaunchKernelGGL(k_lora_cols<true>, dim3((unsigned)((n_out + 31) / 32), rch),
-                     dim3(COL_WAVES * 64), 0, s, dy, M, n_out, u, r, scale, accumulate, dB);
+  hipLaunchKernelGGL(k_lora_cols<true>, dim3((unsigned)((nmax + 31) / 32), rch, (unsigned)n),
+                     dim3(COL_WAVES * 64), 0, s, cb, M, r, scale, accumulate);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dA = du^T . x           ([r, k_in])
-  hipLaunchKernelGGL(k_lora_cols<false>, dim3((unsigned)((k_in + 31) / 32), rch),
-                     dim3(COL_WAVES * 64), 0, s, x, M, k_in, du, r, 1.0f, accumulate, dA);
+  hipLaunchKernelGGL(k_lora_cols<false>, dim3((unsigned)((k_in + 31) / 32), rch, (unsigned)n),
+                     dim3(COL_WAVES * 64), 0, s, ca, M, r, 1.0f, accumulate);
   return hipGetLastError();
 }
 

@@ -28,8 +28,9 @@ from __future__ import annotations
 import torch
 
 from . import (OP_ATTENTION_BWD, OP_CROSS_ENTROPY, OP_DENSE_BWD_PACKED, OP_DENSE_FWD_PACKED,
-               OP_LINEAR_BWD_PACKED, OP_LINEAR_FWD_PACKED, OP_LORA_BWD, OP_LORA_FWD,
-               dense_linear_bwd_packed, dense_linear_fwd_packed, lora_bwd, lora_fwd, nf4s_adamw,
+               OP_LINEAR_BWD_PACKED, OP_LINEAR_FWD_PACKED,
+               dense_linear_bwd_packed, dense_linear_fwd_packed, lora_bwd_grouped, lora_fwd_grouped,
+               lora_grouped_workspace_bytes, nf4s_adamw,
                nf4s_attention_bwd, nf4s_attention_fwd, nf4s_cross_entropy, nf4s_dpo_loss,
                nf4s_embed, nf4s_logit_grad, nf4s_token_nll,
                nf4s_pack_activation, nf4s_packed_activation_bytes, nf4s_pool_acquire,
@@ -39,6 +40,10 @@ from . import (OP_ATTENTION_BWD, OP_CROSS_ENTROPY, OP_DENSE_BWD_PACKED, OP_DENSE
                nf4s_workspace_bytes, streamed_linear_bwd_packed, streamed_linear_fwd_packed,
                streamed_linear_fwd_grouped, grouped_workspace_bytes)
 from .stack import ALIGN, PROJ, ShardSet, _round_up
+
+# projections that read the same input: q, k, v the normed h; gate, up the
+# normed h_mid; o and down each their own
+GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 
 BF16 = torch.int16  # bf16 tensors travel as their bit patterns
 
@@ -146,7 +151,7 @@ class Decoder:
         # adapter intermediates: u = x . A^T per target (from the latest
         # forward of the layer), du for the backward
         self.u = {p: f32(M, r) for p in self.targets}
-        self.du = f32(M, r)
+        self.du = {p: f32(M, r) for p in self.targets}
 
         ws = max(nf4s_workspace_bytes(OP_ATTENTION_BWD, M, nh, hd),
                  nf4s_workspace_bytes(OP_CROSS_ENTROPY, M, 0, 0),
@@ -156,14 +161,18 @@ class Decoder:
         for p in PROJ:
             no, ki = shapes[p]
             ws = max(ws, nf4s_workspace_bytes(OP_LINEAR_FWD_PACKED, M, no, ki),
-                     nf4s_workspace_bytes(OP_LINEAR_BWD_PACKED, M, no, ki),
-                     nf4s_workspace_bytes(OP_LORA_FWD, M, no, ki),
-                     nf4s_workspace_bytes(OP_LORA_BWD, M, no, ki))
+                     nf4s_workspace_bytes(OP_LINEAR_BWD_PACKED, M, no, ki))
             pk_layer = max(pk_layer, nf4s_packed_activation_bytes(M, ki),
                            nf4s_packed_activation_bytes(M, no))
         pk = max(pk_layer, nf4s_packed_activation_bytes(M, V))
         for grp in (("q", "k", "v"), ("gate", "up")):
             ws = max(ws, grouped_workspace_bytes([shapes[p][0] for p in grp], shapes[grp[0]][1], M))
+        for grp in GROUPS:
+            tg = [p for p in grp if p in self.targets]
+            if tg:
+                n_outs, ki = [shapes[p][0] for p in tg], shapes[tg[0]][1]
+                ws = max(ws, lora_grouped_workspace_bytes(n_outs, ki, M, False),
+                         lora_grouped_workspace_bytes(n_outs, ki, M, True))
         self.ws = torch.empty(_round_up(max(ws, ALIGN)), dtype=torch.uint8, device=dev)
         # packed (MFMA fragment order) GEMM inputs: two buffers, so that the
         # two outputs of the SwiGLU backward can both be produced packed
@@ -228,17 +237,13 @@ class Decoder:
         time_calls predicate accepts is one timed entry with n_out the sum."""
         ki = self.sh.shapes[ps[0]][1]
         xp = self._pack(x, ki)
-        us, Bs = [], []
-        for p in ps:
-            if adapters and p in self.targets:
-                A, Bm = self.lora[(i, p)]
-                lora_fwd(x.data_ptr(), self.M, ki, A.data_ptr(), self.r, self.u[p].data_ptr(),
-                         *self._ws(), self._s)
-                us.append(self.u[p].data_ptr())
-                Bs.append(Bm.data_ptr())
-            else:
-                us.append(None)
-                Bs.append(None)
+        tg = [p for p in ps if adapters and p in self.targets]
+        if tg:
+            # u = x . A^T of every adapter reading x, one launch per kernel
+            lora_fwd_grouped(x.data_ptr(), self.M, ki, [self.lora[(i, p)][0].data_ptr() for p in tg],
+                             self.r, [self.u[p].data_ptr() for p in tg], *self._ws(), self._s)
+        us = [self.u[p].data_ptr() if p in tg else None for p in ps]
+        Bs = [self.lora[(i, p)][1].data_ptr() if p in tg else None for p in ps]
         r = self.r if any(us) else 0
         scale = self.scale if any(us) else 0.0
         ev = self._tick("fwd", sum(self.sh.shapes[p][0] for p in ps), ki)
@@ -264,21 +269,31 @@ class Decoder:
             ev[4].record(self.compute)
             self.timed.append(ev + (launches,))
 
-    def _bwd(self, base, i, p, x, dy, dx):
-        no, ki = self.sh.shapes[p]
-        d = self.sh.layout.descs[p]
-        dyp = self._pack(dy, no)
-        if p in self.targets:
-            A, Bm = self.lora[(i, p)]
-            dA, dB = self.lora_grads[(i, p)]
-            lora_bwd(x.data_ptr(), dy.data_ptr(), self.u[p].data_ptr(), self.M, ki, no, Bm.data_ptr(),
-                     self.r, self.scale, dA.data_ptr(), dB.data_ptr(), self.du.data_ptr(), 0,
-                     *self._ws(), self._s)
-            streamed_linear_bwd_packed(base, d, dyp, self.M, dx.data_ptr(), self.du.data_ptr(),
-                                       A.data_ptr(), self.r, *self._ws(), self._s)
-        else:
-            streamed_linear_bwd_packed(base, d, dyp, self.M, dx.data_ptr(), None, None, 0,
-                                       *self._ws(), self._s)
+    def _bwd(self, base, i, ps, x, dys, dxs):
+        """Backward of the projections ps, all reading x: the adapter
+        gradients of the targets among them (one launch per kernel), then
+        dx of each projection with its adapter's du . A added."""
+        ki = self.sh.shapes[ps[0]][1]
+        tg = [p for p in ps if p in self.targets]
+        if tg:
+            dy_of = dict(zip(ps, dys))
+            lora_bwd_grouped(x.data_ptr(), [dy_of[p].data_ptr() for p in tg],
+                             [self.u[p].data_ptr() for p in tg], self.M, ki,
+                             [self.sh.shapes[p][0] for p in tg],
+                             [self.lora[(i, p)][1].data_ptr() for p in tg], self.r, self.scale,
+                             [self.lora_grads[(i, p)][0].data_ptr() for p in tg],
+                             [self.lora_grads[(i, p)][1].data_ptr() for p in tg],
+                             [self.du[p].data_ptr() for p in tg], 0, *self._ws(), self._s)
+        for p, dy, dx in zip(ps, dys, dxs):
+            no = self.sh.shapes[p][0]
+            dyp = self._pack(dy, no)
+            if p in tg:
+                streamed_linear_bwd_packed(base, self.sh.layout.descs[p], dyp, self.M, dx.data_ptr(),
+                                           self.du[p].data_ptr(), self.lora[(i, p)][0].data_ptr(),
+                                           self.r, *self._ws(), self._s)
+            else:
+                streamed_linear_bwd_packed(base, self.sh.layout.descs[p], dyp, self.M, dx.data_ptr(),
+                                           None, None, 0, *self._ws(), self._s)
 
     # -- one layer ---------------------------------------------------------------------
     def _layer_fwd(self, i, base, recompute, adapters=True, hin=None, hout=None, keep=False):
@@ -319,28 +334,25 @@ class Decoder:
         c, s, M, H = self.cfg, self._s, self.M, self.H
         self._packed_key = self._packed_key_b = None
         nf4s_to_bf16(self.dh.data_ptr(), M, H, self.dd.data_ptr(), s, packed=self._produced(self.dd, H))
-        self._bwd(base, i, "down", self.sw, self.dd, self.dsw)
+        self._bwd(base, i, ("down",), self.sw, (self.dd,), (self.dsw,))
         nf4s_swiglu_bwd(self.dsw.data_ptr(), self.g.data_ptr(), self.u_.data_ptr(), M, self.I,
                         self.dg.data_ptr(), self.du_.data_ptr(), s,
                         dg_packed=self._produced(self.dg, self.I),
                         du_packed=self._produced(self.du_, self.I, second=True))
-        self._bwd(base, i, "gate", self.n2, self.dg, self.dnx[0])
-        self._bwd(base, i, "up", self.n2, self.du_, self.dnx[1])
+        self._bwd(base, i, ("gate", "up"), self.n2, (self.dg, self.du_), self.dnx[:2])
         nf4s_rmsnorm_bwd([self.dnx[0].data_ptr(), self.dnx[1].data_ptr()], self.h_mid.data_ptr(),
                          self.norms["mlp"][i].data_ptr(), self.rstd2.data_ptr(), M, H, 1,
                          self.dh.data_ptr(), s)
         self._packed_key_b = None
         nf4s_to_bf16(self.dh.data_ptr(), M, H, self.dd.data_ptr(), s, packed=self._produced(self.dd, H))
-        self._bwd(base, i, "o", self.o, self.dd, self.do)
+        self._bwd(base, i, ("o",), self.o, (self.dd,), (self.do,))
         nf4s_attention_bwd(self.q.data_ptr(), self.k.data_ptr(), self.vv.data_ptr(),
                            self.o32.data_ptr(), self.do.data_ptr(), self.lse.data_ptr(), self.B,
                            self.S, c["heads"], c["kv_heads"], c["head_dim"], self.dq.data_ptr(),
                            self.dk.data_ptr(), self.dv.data_ptr(), *self._ws(), s)
         nf4s_rope(self.dq.data_ptr(), M, self.S, c["heads"], c["head_dim"], c["rope_theta"], 1, s)
         nf4s_rope(self.dk.data_ptr(), M, self.S, c["kv_heads"], c["head_dim"], c["rope_theta"], 1, s)
-        self._bwd(base, i, "q", self.n1, self.dq, self.dnx[0])
-        self._bwd(base, i, "k", self.n1, self.dk, self.dnx[1])
-        self._bwd(base, i, "v", self.n1, self.dv, self.dnx[2])
+        self._bwd(base, i, ("q", "k", "v"), self.n1, (self.dq, self.dk, self.dv), self.dnx)
         nf4s_rmsnorm_bwd([x.data_ptr() for x in self.dnx], self.h[i].data_ptr(),
                          self.norms["attn"][i].data_ptr(), self.rstd1.data_ptr(), M, H, 1,
                          self.dh.data_ptr(), s)

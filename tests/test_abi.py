@@ -323,3 +323,46 @@ def test_grouped_forward_argument_errors():
     q.append(L.nf4s_tensor_layout(1024, 4096, q[0].end))
     q.append(L.nf4s_tensor_layout(1024, 4096, q[1].end))
     assert _err(fwd, FAKE, q, FAKE, 512, [FAKE] * 3, None, None, 0, 0.0, FAKE, 1024) == L.EWORKSPACE
+
+
+def test_grouped_lora_workspace():
+    ns, k, M = [4096, 1024], 4096, 512
+    single_f = sum(L.nf4s_workspace_bytes(L.OP_LORA_FWD, M, n, k) for n in ns)
+    single_b = sum(L.nf4s_workspace_bytes(L.OP_LORA_BWD, M, n, k) for n in ns)
+    assert L.lora_grouped_workspace_bytes(ns, k, M, False) == single_f
+    assert L.lora_grouped_workspace_bytes(ns, k, M, True) == single_b
+    # backward partials: ceil(n_out / 512) chunks of M x 64 fp32 per adapter
+    assert single_b == (8 + 2) * M * 64 * 4
+    assert _err(L.lora_grouped_workspace_bytes, [64] * 4, 64, 16, True) == L.EINVAL
+    assert _err(L.lora_grouped_workspace_bytes, [], 64, 16, True) == L.EINVAL
+    assert _err(L.lora_grouped_workspace_bytes, [64, 60], 64, 16, True) == L.ESHAPE
+    assert _err(L.lora_grouped_workspace_bytes, [64], 100, 16, False) == L.ESHAPE
+    assert _err(L.lora_grouped_workspace_bytes, [64], 64, 0, False) == L.ESHAPE
+
+
+def test_grouped_lora_argument_errors():
+    # only error paths: every call below is refused before any launch
+    fwd, bwd = L.lora_fwd_grouped, L.lora_bwd_grouped
+    two = [FAKE, FAKE]
+    assert _err(fwd, FAKE, 16, 64, [FAKE] * 4, 16, [FAKE] * 4, FAKE, 1 << 30) == L.EINVAL
+    assert _err(fwd, FAKE, 16, 100, two, 16, two, FAKE, 1 << 30) == L.ESHAPE
+    assert _err(fwd, FAKE, 0, 64, two, 16, two, FAKE, 1 << 30) == L.ESHAPE
+    assert _err(fwd, FAKE, 16, 64, two, 65, two, FAKE, 1 << 30) == L.EINVAL
+    assert _err(fwd, FAKE, 16, 64, [FAKE, FAKE + 2], 16, two, FAKE, 1 << 30) == L.EALIGN
+    assert _err(fwd, FAKE, 16, 64, two, 16, [FAKE, None], FAKE, 1 << 30) == L.EINVAL
+    assert _err(fwd, FAKE, 16, 64, two, 16, two, FAKE, 16) == L.EWORKSPACE
+    ok = dict(x=FAKE, dys=two, us=two, M=16, k_in=64, n_outs=[64, 128], Bs=two, r=16, scale=2.0,
+              dAs=two, dBs=two, du_outs=two, accumulate=0, ws=FAKE, ws_bytes=1 << 30)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return _err(bwd, a["x"], a["dys"], a["us"], a["M"], a["k_in"], a["n_outs"], a["Bs"], a["r"],
+                    a["scale"], a["dAs"], a["dBs"], a["du_outs"], a["accumulate"], a["ws"],
+                    a["ws_bytes"])
+    assert call(n_outs=[64, 60]) == L.ESHAPE
+    assert call(accumulate=2) == L.EINVAL
+    assert call(scale=float("nan")) == L.EINVAL
+    assert call(dys=[FAKE, FAKE + 8]) == L.EALIGN
+    assert call(dBs=[FAKE, FAKE + 2]) == L.EALIGN
+    assert call(du_outs=[None, FAKE]) == L.EINVAL
+    assert call(ws_bytes=64) == L.EWORKSPACE

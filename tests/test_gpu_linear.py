@@ -348,3 +348,94 @@ def test_grouped_forward_8b_qkv_close_to_single_calls():
         ia, ib = a.astype(np.int32), b.astype(np.int32)
         far = (np.abs(ia - ib) > 1) & (np.abs(fb) > 2.0 ** -6 * np.max(np.abs(fb)))
         assert np.count_nonzero(far) == 0
+
+
+def _lora_group_run(projs, ns, k, M, r, grouped, layer=0, step=0):
+    """u, du, dA, dB of each adapter reading one x: from the grouped calls, or
+    one lora_fwd / lora_bwd per adapter. The backward runs twice, the second
+    time accumulating into dA, dB."""
+    s = stream()
+    x = dev_bf16bits(synth.activation((M, k), step, 0))
+    ad = []
+    for i, (p, n) in enumerate(zip(projs, ns)):
+        a, b = synth.lora_pair(layer, p, n, k, r=r)
+        ad.append(dict(n=n, A=dev_f32(a), B=dev_f32(b),
+                       dy=dev_bf16bits(synth.activation((M, n), step, 1 + i)),
+                       u=torch.empty((M, r), dtype=torch.float32, device="cuda"),
+                       du=torch.empty((M, r), dtype=torch.float32, device="cuda"),
+                       dA=torch.empty((r, k), dtype=torch.float32, device="cuda"),
+                       dB=torch.empty((n, r), dtype=torch.float32, device="cuda")))
+    ptrs = lambda key: [d[key].data_ptr() for d in ad]  # noqa: E731
+    out = []
+    if grouped:
+        wsf = ws_tensor(L.lora_grouped_workspace_bytes(list(ns), k, M, False))
+        wsb = ws_tensor(L.lora_grouped_workspace_bytes(list(ns), k, M, True))
+        L.lora_fwd_grouped(x.data_ptr(), M, k, ptrs("A"), r, ptrs("u"), wsf.data_ptr(), wsf.numel(), s)
+        for acc in (0, 1):
+            L.lora_bwd_grouped(x.data_ptr(), ptrs("dy"), ptrs("u"), M, k, list(ns), ptrs("B"), r, S,
+                               ptrs("dA"), ptrs("dB"), ptrs("du"), acc, wsb.data_ptr(), wsb.numel(), s)
+            torch.cuda.synchronize()
+            out.append([{key: d[key].cpu().numpy() for key in ("u", "du", "dA", "dB")} for d in ad])
+    else:
+        for d in ad:
+            ws = ws_tensor(max(L.nf4s_workspace_bytes(L.OP_LORA_FWD, M, d["n"], k),
+                               L.nf4s_workspace_bytes(L.OP_LORA_BWD, M, d["n"], k)))
+            L.lora_fwd(x.data_ptr(), M, k, d["A"].data_ptr(), r, d["u"].data_ptr(), ws.data_ptr(),
+                       ws.numel(), s)
+        for acc in (0, 1):
+            for d in ad:
+                ws = ws_tensor(L.nf4s_workspace_bytes(L.OP_LORA_BWD, M, d["n"], k))
+                L.lora_bwd(x.data_ptr(), d["dy"].data_ptr(), d["u"].data_ptr(), M, k, d["n"],
+                           d["B"].data_ptr(), r, S, d["dA"].data_ptr(), d["dB"].data_ptr(),
+                           d["du"].data_ptr(), acc, ws.data_ptr(), ws.numel(), s)
+                torch.cuda.synchronize()
+            out.append([{key: d[key].cpu().numpy() for key in ("u", "du", "dA", "dB")} for d in ad])
+    return out
+
+
+LORA_GROUPS = [
+    # (projections, n_outs, k_in, M, r)
+    # q and v adapters at 8B widths, M = 512: the decoder step's launches
+    (("q", "v"), (4096, 1024), 4096, 512, 16),
+    (("q", "k", "v"), (576, 192, 192), 576, 300, 16),
+    # a rank past one 16-column pass, ragged M
+    (("gate", "up"), (1536, 1536), 576, 37, 40),
+    (("o",), (72,), 128, 1, 8),
+    # backward contraction chunks 1, 2 and 1: the grid's chunk count is the
+    # largest, the other adapters' extra workgroups return at once
+    (("q", "k", "v"), (40, 520, 64), 64, 100, 16),
+]
+
+
+@pytest.mark.parametrize("projs,ns,k,M,r", LORA_GROUPS)
+def test_grouped_lora_bit_identical_to_single_calls(projs, ns, k, M, r):
+    """Each adapter of a grouped call runs the single call's kernels with the
+    same chunking and reduction order, so every output bit agrees, also on
+    the accumulating backward."""
+    print(f"lora group {projs} {ns}x{k} M={M} r={r}", flush=True)
+    g = _lora_group_run(projs, ns, k, M, r, True)
+    one = _lora_group_run(projs, ns, k, M, r, False)
+    for pass_g, pass_1 in zip(g, one):
+        for dg, d1 in zip(pass_g, pass_1):
+            for key in dg:
+                assert np.array_equal(dg[key].view(np.uint32), d1[key].view(np.uint32)), key
+
+
+@pytest.mark.parametrize("projs,ns,k,M,r", LORA_GROUPS[1:])
+def test_grouped_lora_matches_oracle(projs, ns, k, M, r):
+    print(f"lora group oracle {projs} {ns}x{k} M={M} r={r}", flush=True)
+    first, second = _lora_group_run(projs, ns, k, M, r, True)
+    x = bits_to_f32(synth.activation((M, k), 0, 0))
+    for i, (p, n) in enumerate(zip(projs, ns)):
+        a, b = synth.lora_pair(0, p, n, k, r=r)
+        dy = bits_to_f32(synth.activation((M, n), 0, 1 + i))
+        w0 = np.zeros((n, k))
+        _, u_ref = linear.forward(x, w0, a, b, S)
+        ref = linear.backward(x, dy, w0, a, b, S)
+        assert linear.rel_err(first[i]["u"], u_ref) <= 1e-5
+        assert linear.rel_err(first[i]["du"], ref["du"]) <= 1e-5
+        assert linear.rel_err(first[i]["dA"], ref["dA"]) <= 1e-5
+        assert linear.rel_err(first[i]["dB"], ref["dB"]) <= 1e-5
+        # the second backward adds the same gradients once more
+        assert linear.rel_err(second[i]["dA"], 2 * ref["dA"]) <= 1e-5
+        assert linear.rel_err(second[i]["dB"], 2 * ref["dB"]) <= 1e-5

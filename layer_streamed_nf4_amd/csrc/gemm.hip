@@ -268,9 +268,16 @@ __device__ __forceinline__ void load_b(const GemmArgs& g, const WLanes<true>& L,
 // Pair table: entry b = (C4[b >> 4], C4[b & 15]), both levels of a packed byte,
 // the even element (high nibble) first. Copy c of entry b sits at float2 index
 // 32*b + c, i.e. dwords 64*b + 2c and 64*b + 2c + 1: the copy fixes the LDS
-// bank pair whatever b is. `ptab` below is already offset by the lane's copy.
-__device__ __forceinline__ float2 pair_of(const float2* ptab, uint32_t word, int byte) {
-  return ptab[((word >> (8 * byte)) & 0xFFu) * PAIR_COPIES];
+// bank pair whatever b is. The byte offset of copy c of entry b, 256 b + 8 c,
+// is one byte permute of the code word (byte 1 the code byte, byte 0 the
+// copy's offset 8 c < 256, bytes 2 and 3 zero).
+struct PairTab {
+  const uint8_t* base;  // the table in LDS
+  uint32_t copy8;       // 8 * the lane's copy
+};
+__device__ __forceinline__ float2 pair_of(const PairTab& pt, uint32_t word, int byte) {
+  const uint32_t sel = 0x0C0C0000u | ((4u + (uint32_t)byte) << 8);
+  return *reinterpret_cast<const float2*>(pt.base + __builtin_amdgcn_perm(word, pt.copy8, sel));
 }
 
 // The LDS reads of a stage's decode (scale-code lookups and pair table) are
@@ -282,7 +289,7 @@ struct Prep {
   float c8v[NR];
 };
 
-__device__ __forceinline__ void prep_reads(const BRegs<false>& rb, const float2* ptab,
+__device__ __forceinline__ void prep_reads(const BRegs<false>& rb, const PairTab& ptab,
                                            const float* c8, Prep<1>& pp) {
   pp.c8v[0] = c8[rb.q];
 #pragma unroll
@@ -316,7 +323,7 @@ __device__ __forceinline__ int bwd_swizzle_off(int col, int k) {
 // Also decodes and publishes the thread's block scale (scale loaders), for
 // the stage's decode after the next workgroup barrier; sc is the stage's
 // slot of the scale ring.
-__device__ __forceinline__ void prep_reads(const BRegs<true>& rb, const float2* ptab,
+__device__ __forceinline__ void prep_reads(const BRegs<true>& rb, const PairTab& ptab,
                                            const float* c8, Prep<1>& pp, float* sc, float off,
                                            int pt) {
   float cq = 0.0f;
@@ -573,7 +580,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, A.f[i][kk]), fb[j], acc[i][j], 0, 0, 0);
+              fb[j], __builtin_bit_cast(bf16x8_t, A.f[i][kk]), acc[i][j], 0, 0, 0);
     };
     auto refill = [&](AFrags& A, int kk, int64_t k0) {
       const uint8_t* base = g.afrag + (k0 / 16) * FRAG_BYTES + kk * FRAG_BYTES;
@@ -666,7 +673,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
       }
     }
   } else if constexpr (DENSE) {
@@ -710,7 +717,8 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
     bool valid = true;
     if constexpr (!BWD) valid = wl.valid;
     const float off = g.offset[0];
-    const float2* s_pair = s_pair_all + (t & (PAIR_COPIES - 1));
+    const PairTab s_pair{reinterpret_cast<const uint8_t*>(s_pair_all),
+                         (uint32_t)(t & (PAIR_COPIES - 1)) * 8u};
     BRegs<BWD> wb0, wb1, wb2, wb3;
     Prep<1> pp;
     // table lookups of stage st (backward: also publish its block scales)
@@ -760,11 +768,13 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
 #undef NF4S_PRODUCER_STEP
   }
 
-  // Accumulator layout of v_mfma_f32_32x32x16: register r of lane l holds
-  // row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the 32x32 tile. The tile goes
-  // out through LDS so that every global store writes 16 contiguous bytes
-  // (bf16: the whole 256x128 tile at once; fp32 partials: 128 rows at a time).
-  // The weight ring is free: the last step ended with a barrier.
+  // The products are formed transposed (weight fragment first), so register
+  // r of lane l holds output row l%32 and column 8*(r/4) + 4*(l/32) + r%4 of
+  // its 32x32 tile: registers 4q..4q+3 are four adjacent columns, one LDS
+  // store. The tile goes out through LDS so that every global store writes
+  // 16 contiguous bytes (bf16: the whole 256x128 tile at once; fp32
+  // partials: 128 rows at a time). The weight ring is free: the last step
+  // ended with a barrier.
   if constexpr (!SPLIT) {
     constexpr int OS = BN + 8;  // bf16 per LDS row
     uint16_t* ot = reinterpret_cast<uint16_t*>(smem);
@@ -773,11 +783,13 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int col = j * 32 + lrow;
+          const int row = wave * WAVE_ROWS + i * 32 + lrow;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = wave * WAVE_ROWS + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            ot[row * OS + col] = (uint16_t)(pack_bf16x2(acc[i][j][r], 0.0f) & 0xFFFFu);
+          for (int q = 0; q < 4; ++q) {
+            uint2 v;
+            v.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+            v.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            *reinterpret_cast<uint2*>(ot + row * OS + j * 32 + 8 * q + 4 * (lane >> 5)) = v;
           }
         }
     }
@@ -801,11 +813,12 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int col = j * 32 + lrow;
+            const int row = (wave & 1) * WAVE_ROWS + i * 32 + lrow;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int row = (wave & 1) * WAVE_ROWS + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-              ot[row * OS + col] = acc[i][j][r];
+            for (int q = 0; q < 4; ++q) {
+              float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]);
+              *reinterpret_cast<float4*>(ot + row * OS + j * 32 + 8 * q + 4 * (lane >> 5)) = v;
             }
           }
       }
@@ -844,7 +857,9 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
 //    s-1, so its first fragments are read before the barrier of step s;
 //  * the packed codes of even and odd steps live in two register sets that
 //    are never copied (a copy of a value still in flight would wait for every
-//    older load).
+//    older load);
+//  * the loop is unrolled by six steps (two register sets x three stages), so
+//    the stage addresses are constants.
 // The decode and the contraction order per output element are those of
 // k_gemm: results are bit-identical for the same split of the contraction.
 constexpr int FBM = 512;
@@ -936,7 +951,7 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables ta
     sl.q = __builtin_amdgcn_raw_buffer_load_b8(qr, blk, 0, 0);
     sl.nest = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(nr, (blk >> 8) * 4, 0, 0));
   };
-  const float2* const ptab = s_pair_all + (t & (PAIR_COPIES - 1));
+  const PairTab ptab{reinterpret_cast<const uint8_t*>(s_pair_all), (uint32_t)(t & (PAIR_COPIES - 1)) * 8u};
   float2 pv[16];
   float pc, ascale;
   uint32_t ow[16];
@@ -1007,8 +1022,10 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables ta
 #pragma unroll
   for (int j = 0; j < 4; ++j) fb0[j] = b_frag<false>(stage(0), lane, j, 0);
 
-  auto step = [&](int s, u32x4 (&A)[4][4], FSlot& sl) {
-    const int st = s % FNST, s1 = (s + 1) % FNST, s2 = (s + 2) % FNST;
+  // st = s % FNST, a constant where the loop below is unrolled by six
+  auto step = [&](int s, int st, u32x4 (&A)[4][4], FSlot& sl) __attribute__((always_inline)) {
+    const int s1 = st + 1 < FNST ? st + 1 : st + 1 - FNST;
+    const int s2 = st + 2 < FNST ? st + 2 : st + 2 - FNST;
     const int a2 = a_soff(s + 2);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -1017,7 +1034,7 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables ta
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         const int i = m >> 2, j = m & 3;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, A[i][g]), fc[j],
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc[j], __builtin_bit_cast(bf16x8_t, A[i][g]),
                                                             acc[i][j], 0, 0, 0);
         if (m < 4) fn[m] = (g < 3) ? b_frag<false>(stage(st), lane, m, g + 1) : b_frag<false>(stage(s1), lane, m, 0);
         if (j == 3) A[i][g] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[i], a2 + g * FRAG_BYTES, 0);
@@ -1039,11 +1056,19 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables ta
     __builtin_amdgcn_sched_barrier(0);
   };
   int s = 0;
-  for (; s + 1 < nk; s += 2) {
-    step(s, A0, sa);
-    step(s + 1, A1, sb);
+  for (; s + 5 < nk; s += 6) {
+    step(s, 0, A0, sa);
+    step(s + 1, 1, A1, sb);
+    step(s + 2, 2, A0, sa);
+    step(s + 3, 0, A1, sb);
+    step(s + 4, 1, A0, sa);
+    step(s + 5, 2, A1, sb);
   }
-  if (s < nk) step(s, A0, sa);
+  for (; s + 1 < nk; s += 2) {
+    step(s, s % FNST, A0, sa);
+    step(s + 1, (s + 1) % FNST, A1, sb);
+  }
+  if (s < nk) step(s, s % FNST, A0, sa);
 
   // LoRA term on the matrix cores, in chunks of 16 over the rank (split 0):
   // + u[m, :] . (s * B[n, :])
@@ -1078,13 +1103,16 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables ta
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
   }
 
   // Output through LDS (the ring is free after the last barrier) so that
-  // every global store writes 16 contiguous bytes. Accumulator register r of
-  // lane l holds row 8*(r/4) + 4*(l/32) + r%4, column l%32 of its 32x32 tile.
+  // every global store writes 16 contiguous bytes. The products are formed
+  // transposed (weight fragment as the first operand), so accumulator
+  // register r of lane l holds output row l%32 and column 8*(r/4) + 4*(l/32)
+  // + r%4 of its 32x32 tile: registers 4q..4q+3 are four adjacent columns,
+  // one 8-byte LDS store.
   constexpr int OS = BN + 8;  // bf16 per LDS row; 256 rows (two waves) per pass
   uint16_t* const ot = reinterpret_cast<uint16_t*>(smem);
   uint16_t* const out = ga.seg[sgi].out;
@@ -1095,11 +1123,14 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables ta
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int col = j * 32 + lrow;
+          const int row = (wave & 1) * 128 + i * 32 + lrow;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = (wave & 1) * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            ot[row * OS + col] = (uint16_t)(pack_bf16x2(acc[i][j][r], 0.0f) & 0xFFFFu);
+          for (int q = 0; q < 4; ++q) {
+            const int col = j * 32 + 8 * q + 4 * (lane >> 5);
+            uint2 v;
+            v.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+            v.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            *reinterpret_cast<uint2*>(ot + row * OS + col) = v;
           }
         }
     }

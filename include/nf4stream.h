@@ -271,6 +271,36 @@ int streamed_linear_fwd_grouped(const void* shard_dev, const nf4s_tensor_desc* d
                                 float scale, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Grouped backward ([G] s2.1 and s4.4: the input gradient of the layer's
+ * normed input is the sum over the projections that read it, q, k and v, or
+ * gate and up): for n in [1, 3] weights sharing k_in,
+ *   dx = bf16( sum_i (dy_i.W'_i + du_i.A_i) )
+ * as one contraction over the dy_i placed one after the other, rounded to
+ * bf16 once (the sum of the single calls' outputs rounds each term).
+ *   descs:     host array of n descriptors of the shard, all with the same
+ *              k_in; with n > 1 every n_out a multiple of 64;
+ *   dy_packed: host array of n device pointers, nf4s_pack_activation of bf16
+ *              dy_i [M, descs[i].n_out] (256-B aligned);
+ *   dx:        bf16 [M, k_in];
+ *   lora_dus, lora_As: nullable host arrays of n device pointers; entry i is
+ *              fp32 [M, r] / [r, k_in] or NULL in both (no adapter);
+ *   ws:        nf4s_grouped_bwd_workspace_bytes(n, n_outs, k_in, M) bytes
+ *              (fp32 partials of the split contraction; zero when unsplit).
+ * Each weight's contraction is split on its own, so a workgroup reads one
+ * weight; the partials of all weights are summed in a fixed order
+ * (deterministic). A group of one equals streamed_linear_bwd_packed bit for
+ * bit. Errors: EINVAL (n out of range, unpaired LoRA operands), ESHAPE
+ * (k_in differs, n_out not a multiple of 64 in a group, sizes), EALIGN,
+ * ETABLE, EKEY, EWORKSPACE.
+ */
+int nf4s_grouped_bwd_workspace_bytes(int n, const int64_t* n_outs, int64_t k_in, int64_t M,
+                                     size_t* bytes);
+int streamed_linear_bwd_grouped(const void* shard_dev, const nf4s_tensor_desc* descs, int n,
+                                const void* const* dy_packed, int64_t M, uint16_t* dx,
+                                const float* const* lora_dus, const float* const* lora_As, int r,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/*
  * LoRA down-projection, u = x.A^T in fp32 ([G] s2.1, adapter on q/v):
  *   x: bf16 [M, k_in]; A: fp32 [r, k_in] (16-byte aligned); u_out: fp32 [M, r];
  *   ws: nf4s_workspace_bytes(NF4S_OP_LORA_FWD, M, n_out, k_in) bytes (partials

@@ -36,6 +36,7 @@ EXPORTS = (
     "streamed_linear_bwd_packed", "dense_linear_fwd_packed", "dense_linear_bwd_packed",
     "nf4s_grouped_workspace_bytes", "streamed_linear_fwd_grouped",
     "nf4s_lora_grouped_workspace_bytes", "lora_fwd_grouped", "lora_bwd_grouped",
+    "nf4s_grouped_bwd_workspace_bytes", "streamed_linear_bwd_grouped",
     "nf4s_embed", "nf4s_rmsnorm_fwd", "nf4s_rmsnorm_bwd", "nf4s_rope", "nf4s_attention_fwd",
     "nf4s_attention_bwd", "nf4s_swiglu_fwd", "nf4s_swiglu_bwd", "nf4s_residual_add",
     "nf4s_to_bf16", "nf4s_cross_entropy", "nf4s_adamw", "nf4s_token_nll", "nf4s_dpo_loss",
@@ -111,6 +112,10 @@ _SIG = {
     "streamed_linear_fwd_grouped": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), ctypes.c_int, _P,
                                                    _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float,
                                                    _P, ctypes.c_size_t, _P]),
+    "nf4s_grouped_bwd_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P]),
+    "streamed_linear_bwd_grouped": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), ctypes.c_int, _P,
+                                                   _I64, _P, _P, _P, ctypes.c_int, _P,
+                                                   ctypes.c_size_t, _P]),
     "nf4s_lora_grouped_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, ctypes.c_int,
                                                          _P]),
     "lora_fwd_grouped": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, ctypes.c_int, _P, _P,
@@ -262,6 +267,29 @@ def streamed_linear_fwd_grouped(shard, descs, x_packed, M, ys, lora_us, lora_Bs,
     darr = (TensorDesc * n)(*descs)
     _check(lib().streamed_linear_fwd_grouped(shard, darr, n, x_packed, M, _ptr_array(ys),
                                              _ptr_array(lora_us), _ptr_array(lora_Bs), r, scale, ws,
+                                             ws_bytes, stream))
+
+
+def grouped_bwd_workspace_bytes(n_outs, k_in, M):
+    """Workspace of streamed_linear_bwd_grouped for weights of n_outs outputs."""
+    arr = (ctypes.c_int64 * len(n_outs))(*n_outs)
+    out = ctypes.c_size_t()
+    _check(lib().nf4s_grouped_bwd_workspace_bytes(len(n_outs), ctypes.cast(arr, ctypes.c_void_p), k_in,
+                                                  M, ctypes.byref(out)))
+    return out.value
+
+
+def streamed_linear_bwd_grouped(shard, descs, dy_packed, M, dx, lora_dus, lora_As, r, ws, ws_bytes,
+                                stream=0):
+    """dx = sum of the backward of len(descs) weights (one launch).
+
+    dy_packed: device pointers of the packed dy_i; lora_dus / lora_As: None or
+    lists of device pointers (None entries: no adapter on that weight).
+    """
+    n = len(descs)
+    darr = (TensorDesc * n)(*descs)
+    _check(lib().streamed_linear_bwd_grouped(shard, darr, n, _ptr_array(dy_packed), M, dx,
+                                             _ptr_array(lora_dus), _ptr_array(lora_As), r, ws,
                                              ws_bytes, stream))
 
 

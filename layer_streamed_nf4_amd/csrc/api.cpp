@@ -433,6 +433,78 @@ int streamed_linear_fwd_grouped(const void* shard_dev, const nf4s_tensor_desc* d
   return e == hipSuccess ? NF4S_OK : hip_fail(e, "grouped linear launch");
 }
 
+static int check_bwd_group(int n, const int64_t* n_outs, int64_t k_in, int64_t M) {
+  if (n < 1 || n > GEMM_MAX_SEG)
+    return fail(NF4S_EINVAL, "group of %d weights (1..%d allowed)", n, GEMM_MAX_SEG);
+  if (!n_outs) return fail(NF4S_EINVAL, "n_outs is NULL");
+  if (M <= 0 || M > (1ll << 24)) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
+  int rc;
+  for (int i = 0; i < n; ++i) {
+    if ((rc = check_shape(n_outs[i], k_in))) return rc;
+    if ((rc = check_packed_shape(M, n_outs[i]))) return rc;
+    if (n > 1 && n_outs[i] % 64)
+      return fail(NF4S_ESHAPE, "n_out=%lld of a grouped backward must be a multiple of 64",
+                  (long long)n_outs[i]);
+    const int64_t widest = n_outs[i] > k_in ? n_outs[i] : k_in;
+    if (M * widest >= (1ll << 31) || n_outs[i] * k_in >= (1ll << 33))
+      return fail(NF4S_ESHAPE, "M=%lld with a %lldx%lld weight exceeds 32-bit offsets", (long long)M,
+                  (long long)n_outs[i], (long long)k_in);
+  }
+  return NF4S_OK;
+}
+
+int nf4s_grouped_bwd_workspace_bytes(int n, const int64_t* n_outs, int64_t k_in, int64_t M,
+                                     size_t* bytes) {
+  if (!bytes) return fail(NF4S_EINVAL, "bytes is NULL");
+  int rc;
+  if ((rc = check_bwd_group(n, n_outs, k_in, M))) return rc;
+  *bytes = plan_bwd_grouped(M, n_outs, n, k_in).part_bytes;
+  return NF4S_OK;
+}
+
+int streamed_linear_bwd_grouped(const void* shard_dev, const nf4s_tensor_desc* descs, int n,
+                                const void* const* dy_packed, int64_t M, uint16_t* dx,
+                                const float* const* lora_dus, const float* const* lora_As, int r,
+                                void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if (!descs || !dy_packed) return fail(NF4S_EINVAL, "descs and dy_packed must be given");
+  if (n < 1 || n > GEMM_MAX_SEG)
+    return fail(NF4S_EINVAL, "group of %d weights (1..%d allowed)", n, GEMM_MAX_SEG);
+  int64_t n_outs[GEMM_MAX_SEG];
+  QPtrs q[GEMM_MAX_SEG];
+  const uint8_t* dyp[GEMM_MAX_SEG];
+  bool any_lora = false;
+  for (int i = 0; i < n; ++i) {
+    if ((rc = check_desc(&descs[i]))) return rc;
+    if (descs[i].k_in != descs[0].k_in)
+      return fail(NF4S_ESHAPE, "weight %d has k_in=%lld, weight 0 has %lld", i,
+                  (long long)descs[i].k_in, (long long)descs[0].k_in);
+    n_outs[i] = descs[i].n_out;
+    if ((rc = check_ptr(dy_packed[i], "dy_packed[i]", 256))) return rc;
+    dyp[i] = static_cast<const uint8_t*>(dy_packed[i]);
+    const float* du = lora_dus ? lora_dus[i] : nullptr;
+    const float* A = lora_As ? lora_As[i] : nullptr;
+    if ((du == nullptr) != (A == nullptr))
+      return fail(NF4S_EINVAL, "LoRA operands of weight %d must be given together", i);
+    if (du) {
+      any_lora = true;
+      if ((rc = check_ptr(du, "lora_dus[i]", 4))) return rc;
+      if ((rc = check_ptr(A, "lora_As[i]", 4))) return rc;
+    }
+  }
+  const int64_t k_in = descs[0].k_in;
+  if ((rc = check_bwd_group(n, n_outs, k_in, M))) return rc;
+  if (any_lora && (rc = check_rank(r))) return rc;
+  if ((rc = check_ptr(shard_dev, "shard_dev", 256))) return rc;
+  if ((rc = check_ptr(dx, "dx"))) return rc;
+  const BwdGroupPlan bp = plan_bwd_grouped(M, n_outs, n, k_in);
+  if (bp.part_bytes && (rc = check_ws(ws, ws_bytes, bp.part_bytes))) return rc;
+  for (int i = 0; i < n; ++i) q[i] = resolve(shard_dev, &descs[i]);
+  hipError_t e = launch_linear_grouped_bwd(q, n, n_outs, k_in, dyp, M, dx, lora_dus, lora_As,
+                                           any_lora ? r : 0, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "grouped backward launch");
+}
+
 int lora_fwd(const uint16_t* x, int64_t M, int64_t k_in, const float* A, int r, float* u_out,
              void* ws, size_t ws_bytes, void* stream) {
   int rc;

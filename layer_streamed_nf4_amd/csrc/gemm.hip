@@ -76,9 +76,13 @@ constexpr int SMEM_BYTES = NSTAGE * STAGE_ELEMS * 2 + 256 * PAIR_COPIES * 8 + 25
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
 
-// One weight of a grouped launch: the forward of up to GEMM_MAX_SEG NF4
-// linears that read the same activation (q, k and v; gate and up) runs as one
-// grid whose column tiles are dealt to the weights in order.
+// One weight of a grouped launch. Forward: up to GEMM_MAX_SEG NF4 linears
+// that read the same activation (q, k and v; gate and up) run as one grid
+// whose column tiles are dealt to the weights in order. Backward: the dx of
+// such a group is one sum, dx = sum_j dy_j . W'_j, so the weights lie along
+// the contraction instead; the grid's split index z is dealt to them in
+// order (splits z0_j .. z0_{j+1}-1 cover weight j, each with its own dy_j),
+// every split writes its own fp32 partial and one sum adds them all.
 struct GemmSeg {
   const uint8_t* packed;
   const uint8_t* q8;
@@ -89,7 +93,11 @@ struct GemmSeg {
   const float* lora_l;   // fp32 [M, r]
   const float* lora_r;   // fwd: B fp32 [n_out, r]; bwd: A fp32 [r, k_in]
   int64_t n_out;
-  int tile0;             // first column tile of this weight
+  int tile0;             // forward: first column tile of this weight
+  int z0;                // backward: first split of this weight
+  const uint8_t* afrag;  // backward: dy_j in fragment order
+  int64_t kblocks;       // backward: its 16-wide blocks per 32-row block
+  int64_t kc_chunk;      // backward: contraction rows per split of this weight
 };
 
 struct GemmArgs {
@@ -278,6 +286,22 @@ struct PairTab {
 __device__ __forceinline__ float2 pair_of(const PairTab& pt, uint32_t word, int byte) {
   const uint32_t sel = 0x0C0C0000u | ((4u + (uint32_t)byte) << 8);
   return *reinterpret_cast<const float2*>(pt.base + __builtin_amdgcn_perm(word, pt.copy8, sel));
+}
+
+// Fill the pair table and the nested-code table in LDS (threads t < 256).
+// 16-byte slot f = 256 i + t holds copies 2(t%16) and 2(t%16)+1 of entry
+// e = f/16 = 16 i + t/16, i.e. (C4[i], C4[t/16]): consecutive lanes store
+// consecutive 16 bytes, so the stores meet no bank conflicts.
+__device__ __forceinline__ void fill_tables(float2* s_pair, float* s_c8, const Tables& tab, int t) {
+  static_assert(PAIR_COPIES == 32, "16-byte slots of 16 per entry");
+  const float lo = tab.c4[t >> 4];
+  float4* const p4 = reinterpret_cast<float4*>(s_pair);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float hi = tab.c4[i];
+    p4[i * 256 + t] = make_float4(hi, lo, hi, lo);
+  }
+  s_c8[t] = tab.c8[t];
 }
 
 // The LDS reads of a stage's decode (scale-code lookups and pair table) are
@@ -496,11 +520,12 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
     ct = full + j / R;
     rt = j % R;
   }
-  // the weight this workgroup's column tile belongs to (uniform per workgroup)
+  // the weight this workgroup belongs to (uniform per workgroup): by column
+  // tile in the forward, by split in the backward
   int sgi = 0;
 #pragma unroll
   for (int q = 1; q < GEMM_MAX_SEG; ++q)
-    if (q < ga.nseg && ct >= ga.seg[q].tile0) sgi = q;
+    if (q < ga.nseg && (BWD ? (int)blockIdx.z >= ga.seg[q].z0 : ct >= ga.seg[q].tile0)) sgi = q;
   GemmArgs g = ga;
   g.packed = ga.seg[sgi].packed;
   g.q8 = ga.seg[sgi].q8;
@@ -512,6 +537,12 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
   g.lora_r = ga.seg[sgi].lora_r;
   g.n_out = ga.seg[sgi].n_out;
   if (!BWD) g.Nc = g.n_out;
+  if (BWD) {  // the weight's own dy, contraction length and split chunk
+    g.afrag = ga.seg[sgi].afrag;
+    g.kblocks = ga.seg[sgi].kblocks;
+    g.kc_chunk = ga.seg[sgi].kc_chunk;
+    g.Kc = g.n_out;
+  }
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_BYTES];
   uint16_t* const Bs0 = reinterpret_cast<uint16_t*>(smem);
   float2* const s_pair_all = reinterpret_cast<float2*>(smem + NSTAGE * STAGE_ELEMS * 2);
@@ -520,16 +551,12 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
       reinterpret_cast<float*>(smem + NSTAGE * STAGE_ELEMS * 2 + 256 * PAIR_COPIES * 8 + 256 * 4);
 
   const int t = threadIdx.x;
-  if (!DENSE && t < 256) {
-    const float2 e = make_float2(tab.c4[t >> 4], tab.c4[t & 15]);
-#pragma unroll
-    for (int c = 0; c < PAIR_COPIES; ++c) s_pair_all[t * PAIR_COPIES + c] = e;
-    s_c8[t] = tab.c8[t];
-  }
+  if (!DENSE && t < 256) fill_tables(s_pair_all, s_c8, tab, t);
 
   const int64_t n0 = (int64_t)(ct - ga.seg[sgi].tile0) * BN;
   const int64_t m0 = (int64_t)rt * BM;
-  const int split = blockIdx.z;
+  const int zpart = blockIdx.z;                         // the partial this workgroup writes
+  const int split = zpart - (BWD ? ga.seg[sgi].z0 : 0);  // its split of the weight's contraction
   const int64_t kb = split * g.kc_chunk;
   const int64_t ke = (kb + g.kc_chunk < g.Kc) ? kb + g.kc_chunk : g.Kc;
   const int nk = (int)((ke - kb + BK - 1) / BK);
@@ -829,7 +856,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
         const int row = q / (BN / 4), c4 = q % (BN / 4);
         const int64_t grow = m0 + 128 * ph + row, gcol = n0 + 4 * c4;
         if (grow < g.M && gcol < g.Nc)
-          *reinterpret_cast<u32x4*>(g.part + ((int64_t)split * g.M + grow) * g.Nc + gcol) =
+          *reinterpret_cast<u32x4*>(g.part + ((int64_t)zpart * g.M + grow) * g.Nc + gcol) =
               *reinterpret_cast<const u32x4*>(ot + row * OS + 4 * c4);
       }
       __syncthreads();
@@ -897,12 +924,7 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables ta
   float2* const s_pair_all = reinterpret_cast<float2*>(smem + FNST * STAGE_ELEMS * 2);
   float* const s_c8 = reinterpret_cast<float*>(smem + FNST * STAGE_ELEMS * 2 + 256 * PAIR_COPIES * 8);
   const int t = threadIdx.x;
-  {
-    const float2 e = make_float2(tab.c4[t >> 4], tab.c4[t & 15]);
-#pragma unroll
-    for (int c = 0; c < PAIR_COPIES; ++c) s_pair_all[t * PAIR_COPIES + c] = e;
-    s_c8[t] = tab.c8[t];
-  }
+  fill_tables(s_pair_all, s_c8, tab, t);
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
   const int lrow = lane & 31;
@@ -984,39 +1006,36 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables ta
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // prologue: stages 0 and 1 decoded; then the codes of steps 2 and 3 and
-  // the activation of steps 0 and 1 are issued in the order the loop keeps
-  // (codes before the younger activation loads), so the wait counts the
-  // compiler derives at the loop head hold on both paths into it
-  {
-    FSlot p0, p1;
-    load_w(0, p0);
-    load_w(1, p1);
-    __syncthreads();  // tables in LDS
-    decode_all(p0, 0);
-    decode_all(p1, 1);
-  }
-  FSlot sa, sb;
-  __builtin_amdgcn_sched_barrier(0);
-  load_w(2, sa);
-  __builtin_amdgcn_sched_barrier(0);
-  load_w(3, sb);
-  __builtin_amdgcn_sched_barrier(0);
+  // prologue: every load is issued before the first decode, so the
+  // activation's latency overlaps the decode of stages 0 and 1. After the
+  // codes of steps 0 and 1 come the activation of step 0 and the codes of
+  // step 2, then the activation of step 1 and the codes of step 3, in the
+  // order a step of the loop issues them (the codes after the second
+  // activation refill of sub-step 3), so the wait counts the compiler derives
+  // at the loop head are the steady-state ones on both paths into it
+  FSlot p0, p1, sa, sb;
   u32x4 A0[4][4], A1[4][4];
+  load_w(0, p0);
+  load_w(1, p1);
+  __builtin_amdgcn_sched_barrier(0);
+  auto issue_a = [&](u32x4 (&A)[4][4], int k, FSlot& sl, int kw) {
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      A0[i][g] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[i], a_soff(0) + g * FRAG_BYTES, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-  for (int g = 0; g < 4; ++g)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      A1[i][g] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[i], a_soff(1) + g * FRAG_BYTES, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      for (int i = 0; i < 4; ++i) {
+        A[i][g] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[i], a_soff(k) + g * FRAG_BYTES, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (g == 3 && i == 1) {
+          load_w(kw, sl);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+  };
+  issue_a(A0, 0, sa, 2);
+  issue_a(A1, 1, sb, 3);
+  __syncthreads();  // tables in LDS
+  decode_all(p0, 0);
+  decode_all(p1, 1);
   __syncthreads();
   bf16x8_t fb0[4], fb1[4];
 #pragma unroll
@@ -1266,6 +1285,11 @@ static hipError_t launch_gemm(bool backward, const QPtrs* q, int nseg, const uin
       sg.offset = q[i].offset;
     }
     sg.out = outs[i];
+    if (backward) {  // the single weight along the contraction
+      sg.afrag = a_packed;
+      sg.kblocks = g.kblocks;
+      sg.kc_chunk = p.kc_chunk;
+    }
     sg.lora_l = lora_ls ? lora_ls[i] : nullptr;
     sg.lora_r = lora_rs ? lora_rs[i] : nullptr;
     sg.n_out = n_outs[i];
@@ -1321,6 +1345,87 @@ hipError_t launch_linear_grouped_fwd(const QPtrs* q, int nseg, const int64_t* n_
                                      int r, float scale, void* part_ws, hipStream_t s) {
   return launch_gemm(false, q, nseg, nullptr, n_outs, k_in, x_packed, M, ys, lora_us, lora_Bs, r,
                      scale, part_ws, s);
+}
+
+// Splits of a grouped backward: split j's contraction into S_j chunks of c
+// steps, the smallest c for which the grid still fits one wave of 256
+// workgroups (so the slowest workgroup runs as few steps as possible), never
+// below 8 steps; a group of one plans as the single call.
+BwdGroupPlan plan_bwd_grouped(int64_t M, const int64_t* n_outs, int n, int64_t k_in) {
+  BwdGroupPlan bp = {};
+  if (n == 1) {
+    const GemmPlan p = plan_gemm(M, k_in, n_outs[0], false);
+    bp.splits[0] = p.splits;
+    bp.kc_chunk[0] = p.kc_chunk;
+    bp.total = p.splits;
+  } else {
+    const int64_t tiles = ((M + BM - 1) / BM) * ((k_in + BN - 1) / BN);
+    int64_t steps[GEMM_MAX_SEG], cmax = 0;
+    for (int j = 0; j < n; ++j) {
+      steps[j] = (n_outs[j] + BK - 1) / BK;
+      cmax = steps[j] > cmax ? steps[j] : cmax;
+    }
+    int64_t best = cmax;
+    for (int64_t c = cmax; c >= 8; --c) {
+      int64_t sz = 0;
+      for (int j = 0; j < n; ++j) sz += (steps[j] + c - 1) / c;
+      if (tiles * sz > 256) break;
+      best = c;
+    }
+    bp.total = 0;
+    for (int j = 0; j < n; ++j) {
+      const int64_t c = best < steps[j] ? best : steps[j];
+      bp.splits[j] = (int)((steps[j] + c - 1) / c);
+      bp.kc_chunk[j] = c * BK;
+      bp.total += bp.splits[j];
+    }
+  }
+  bp.part_bytes = bp.total > 1 ? round256((size_t)bp.total * (size_t)M * (size_t)k_in * sizeof(float)) : 0;
+  return bp;
+}
+
+hipError_t launch_linear_grouped_bwd(const QPtrs* q, int n, const int64_t* n_outs, int64_t k_in,
+                                     const uint8_t* const* dy_packed, int64_t M, uint16_t* dx,
+                                     const float* const* lora_dus, const float* const* lora_As,
+                                     int r, void* part_ws, hipStream_t s) {
+  const BwdGroupPlan bp = plan_bwd_grouped(M, n_outs, n, k_in);
+  GemmArgs g = {};
+  g.M = M;
+  g.k_in = k_in;
+  g.Nc = k_in;
+  g.r = r;
+  g.nseg = n;
+  int z0 = 0;
+  for (int j = 0; j < n; ++j) {
+    GemmSeg& sg = g.seg[j];
+    sg.packed = q[j].packed;
+    sg.q8 = q[j].q8;
+    sg.nested = q[j].nested;
+    sg.offset = q[j].offset;
+    sg.out = dx;
+    sg.part = bp.total > 1 ? static_cast<float*>(part_ws) : nullptr;
+    sg.lora_l = lora_dus ? lora_dus[j] : nullptr;
+    sg.lora_r = lora_As ? lora_As[j] : nullptr;
+    sg.n_out = n_outs[j];
+    sg.z0 = z0;
+    sg.afrag = dy_packed[j];
+    sg.kblocks = (n_outs[j] + BK - 1) / BK * (BK / 16);
+    sg.kc_chunk = bp.kc_chunk[j];
+    z0 += bp.splits[j];
+  }
+  const dim3 grid((unsigned)((k_in + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)bp.total);
+  const Tables& tab = host_tables();
+  if (bp.total > 1) hipLaunchKernelGGL((k_gemm<true, true, false>), grid, dim3(THREADS), 0, s, g, tab);
+  else hipLaunchKernelGGL((k_gemm<true, false, false>), grid, dim3(THREADS), 0, s, g, tab);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || bp.total == 1) return e;
+  SumSegs sum = {};
+  sum.part[0] = static_cast<const float*>(part_ws);
+  sum.out[0] = dx;
+  sum.n[0] = M * k_in;
+  hipLaunchKernelGGL(k_split_sum, dim3((unsigned)((M * k_in / 4 + 1 + 255) / 256), 1u), dim3(256), 0, s,
+                     sum, bp.total);
+  return hipGetLastError();
 }
 
 hipError_t launch_dense_packed(bool backward, const uint16_t* w, int64_t n_out, int64_t k_in,

@@ -38,7 +38,8 @@ from . import (OP_ATTENTION_BWD, OP_CROSS_ENTROPY, OP_DENSE_BWD_PACKED, OP_DENSE
                nf4s_pool_set_layer, nf4s_pool_stats, nf4s_residual_add, nf4s_rmsnorm_bwd,
                nf4s_rmsnorm_fwd, nf4s_rope, nf4s_swiglu_bwd, nf4s_swiglu_fwd, nf4s_to_bf16,
                nf4s_workspace_bytes, streamed_linear_bwd_packed, streamed_linear_fwd_packed,
-               streamed_linear_fwd_grouped, grouped_workspace_bytes)
+               streamed_linear_fwd_grouped, grouped_workspace_bytes, grouped_bwd_workspace_bytes,
+               streamed_linear_bwd_grouped)
 from .stack import ALIGN, PROJ, ShardSet, _round_up
 
 # projections that read the same input: q, k, v the normed h; gate, up the
@@ -167,6 +168,16 @@ class Decoder:
         pk = max(pk_layer, nf4s_packed_activation_bytes(M, V))
         for grp in (("q", "k", "v"), ("gate", "up")):
             ws = max(ws, grouped_workspace_bytes([shapes[p][0] for p in grp], shapes[grp[0]][1], M))
+        # the backward of q, k, v (and of gate, up) as one contraction when
+        # every member would split its contraction alone (small M): one
+        # launch and one sum instead of one of each per projection
+        self._group_bwd = {}
+        for grp in (("q", "k", "v"), ("gate", "up")):
+            n_outs, ki = [shapes[p][0] for p in grp], shapes[grp[0]][1]
+            self._group_bwd[grp] = all(n % 64 == 0 for n in n_outs) and all(
+                nf4s_workspace_bytes(OP_LINEAR_BWD_PACKED, M, n, ki) > 0 for n in n_outs)
+            if self._group_bwd[grp]:
+                ws = max(ws, grouped_bwd_workspace_bytes(n_outs, ki, M))
         for grp in GROUPS:
             tg = [p for p in grp if p in self.targets]
             if tg:
@@ -175,9 +186,11 @@ class Decoder:
                          lora_grouped_workspace_bytes(n_outs, ki, M, True))
         self.ws = torch.empty(_round_up(max(ws, ALIGN)), dtype=torch.uint8, device=dev)
         # packed (MFMA fragment order) GEMM inputs: two buffers, so that the
-        # two outputs of the SwiGLU backward can both be produced packed
+        # two outputs of the SwiGLU backward can both be produced packed, and a
+        # third for the third dy of a grouped q, k, v backward
         self.packed = torch.empty(_round_up(pk), dtype=torch.uint8, device=dev)
         self.packed_b = torch.empty(_round_up(pk_layer), dtype=torch.uint8, device=dev)
+        self.packed_c = torch.empty(_round_up(pk_layer), dtype=torch.uint8, device=dev)
         self._packed_key = None
         self._packed_key_b = None
 
@@ -269,10 +282,36 @@ class Decoder:
             ev[4].record(self.compute)
             self.timed.append(ev + (launches,))
 
+    def _pack_group(self, dys, nos):
+        """Packed pointers of the dys, one buffer each: those their producer
+        wrote packed, the others packed now into the buffers left free."""
+        bufs = [(self.packed, "_packed_key"), (self.packed_b, "_packed_key_b"), (self.packed_c, None)]
+        keys = [(dy.data_ptr(), no) for dy, no in zip(dys, nos)]
+        out, used = [None] * len(dys), set()
+        for j, key in enumerate(keys):
+            for bi, (buf, attr) in enumerate(bufs):
+                if bi not in used and attr is not None and getattr(self, attr) == key:
+                    out[j] = buf.data_ptr()
+                    used.add(bi)
+                    break
+        for j, key in enumerate(keys):
+            if out[j] is None:
+                bi = next(b for b in range(len(bufs)) if b not in used)
+                buf, attr = bufs[bi]
+                nf4s_pack_activation(dys[j].data_ptr(), self.M, nos[j], buf.data_ptr(), buf.numel(),
+                                     self._s)
+                if attr is not None:
+                    setattr(self, attr, key)
+                used.add(bi)
+                out[j] = buf.data_ptr()
+        return out
+
     def _bwd(self, base, i, ps, x, dys, dxs):
         """Backward of the projections ps, all reading x: the adapter
         gradients of the targets among them (one launch per kernel), then
-        dx of each projection with its adapter's du . A added."""
+        dx with each adapter's du . A added: one sum in dxs[0] when the group
+        runs as one contraction, else one dx per projection. Returns the dx
+        tensors that hold the result."""
         ki = self.sh.shapes[ps[0]][1]
         tg = [p for p in ps if p in self.targets]
         if tg:
@@ -284,6 +323,14 @@ class Decoder:
                              [self.lora_grads[(i, p)][0].data_ptr() for p in tg],
                              [self.lora_grads[(i, p)][1].data_ptr() for p in tg],
                              [self.du[p].data_ptr() for p in tg], 0, *self._ws(), self._s)
+        if len(ps) > 1 and self._group_bwd.get(tuple(ps)):
+            nos = [self.sh.shapes[p][0] for p in ps]
+            streamed_linear_bwd_grouped(
+                base, [self.sh.layout.descs[p] for p in ps], self._pack_group(dys, nos), self.M,
+                dxs[0].data_ptr(), [self.du[p].data_ptr() if p in tg else None for p in ps],
+                [self.lora[(i, p)][0].data_ptr() if p in tg else None for p in ps],
+                self.r if tg else 0, *self._ws(), self._s)
+            return dxs[:1]
         for p, dy, dx in zip(ps, dys, dxs):
             no = self.sh.shapes[p][0]
             dyp = self._pack(dy, no)
@@ -294,6 +341,7 @@ class Decoder:
             else:
                 streamed_linear_bwd_packed(base, self.sh.layout.descs[p], dyp, self.M, dx.data_ptr(),
                                            None, None, 0, *self._ws(), self._s)
+        return list(dxs)
 
     # -- one layer ---------------------------------------------------------------------
     def _layer_fwd(self, i, base, recompute, adapters=True, hin=None, hout=None, keep=False):
@@ -339,8 +387,8 @@ class Decoder:
                         self.dg.data_ptr(), self.du_.data_ptr(), s,
                         dg_packed=self._produced(self.dg, self.I),
                         du_packed=self._produced(self.du_, self.I, second=True))
-        self._bwd(base, i, ("gate", "up"), self.n2, (self.dg, self.du_), self.dnx[:2])
-        nf4s_rmsnorm_bwd([self.dnx[0].data_ptr(), self.dnx[1].data_ptr()], self.h_mid.data_ptr(),
+        dn = self._bwd(base, i, ("gate", "up"), self.n2, (self.dg, self.du_), self.dnx[:2])
+        nf4s_rmsnorm_bwd([x.data_ptr() for x in dn], self.h_mid.data_ptr(),
                          self.norms["mlp"][i].data_ptr(), self.rstd2.data_ptr(), M, H, 1,
                          self.dh.data_ptr(), s)
         self._packed_key_b = None
@@ -352,8 +400,8 @@ class Decoder:
                            self.dk.data_ptr(), self.dv.data_ptr(), *self._ws(), s)
         nf4s_rope(self.dq.data_ptr(), M, self.S, c["heads"], c["head_dim"], c["rope_theta"], 1, s)
         nf4s_rope(self.dk.data_ptr(), M, self.S, c["kv_heads"], c["head_dim"], c["rope_theta"], 1, s)
-        self._bwd(base, i, ("q", "k", "v"), self.n1, (self.dq, self.dk, self.dv), self.dnx)
-        nf4s_rmsnorm_bwd([x.data_ptr() for x in self.dnx], self.h[i].data_ptr(),
+        dn = self._bwd(base, i, ("q", "k", "v"), self.n1, (self.dq, self.dk, self.dv), self.dnx)
+        nf4s_rmsnorm_bwd([x.data_ptr() for x in dn], self.h[i].data_ptr(),
                          self.norms["attn"][i].data_ptr(), self.rstd1.data_ptr(), M, H, 1,
                          self.dh.data_ptr(), s)
 

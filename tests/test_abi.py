@@ -366,3 +366,45 @@ def test_grouped_lora_argument_errors():
     assert call(dBs=[FAKE, FAKE + 2]) == L.EALIGN
     assert call(du_outs=[None, FAKE]) == L.EINVAL
     assert call(ws_bytes=64) == L.EWORKSPACE
+
+
+def test_grouped_backward_workspace():
+    # q, k, v of the 8B layer at M = 512: 64 tiles of 256 x 128; q's 64 steps
+    # in two splits, k and v one each: 256 workgroups of at most 32 steps,
+    # four fp32 partials of 512 x 4096
+    assert L.grouped_bwd_workspace_bytes([4096, 1024, 1024], 4096, 512) == 4 * 512 * 4096 * 4
+    # gate and up: 224 steps each, two splits each
+    assert L.grouped_bwd_workspace_bytes([14336, 14336], 4096, 512) == 4 * 512 * 4096 * 4
+    # a group of one plans like the single call
+    for n, k, M in ((4096, 4096, 512), (40, 64, 100), (14336, 4096, 2048)):
+        assert L.grouped_bwd_workspace_bytes([n], k, M) == \
+            L.nf4s_workspace_bytes(L.OP_LINEAR_BWD_PACKED, M, n, k)
+    assert _err(L.grouped_bwd_workspace_bytes, [64] * 4, 64, 16) == L.EINVAL
+    assert _err(L.grouped_bwd_workspace_bytes, [], 64, 16) == L.EINVAL
+    assert _err(L.grouped_bwd_workspace_bytes, [64, 72], 64, 16) == L.ESHAPE
+    assert _err(L.grouped_bwd_workspace_bytes, [64, 64], 100, 16) == L.ESHAPE
+    assert _err(L.grouped_bwd_workspace_bytes, [64, 64], 64, 0) == L.ESHAPE
+
+
+def test_grouped_backward_argument_errors():
+    d = [L.nf4s_tensor_layout(64, 128, 0)]
+    d.append(L.nf4s_tensor_layout(128, 128, d[0].end))
+    bwd = L.streamed_linear_bwd_grouped
+    two = [FAKE, FAKE]
+    # only error paths: every call below is refused before any launch
+    assert _err(bwd, FAKE, [d[0]] * 4, [FAKE] * 4, 16, FAKE, None, None, 0, None, 0) == L.EINVAL
+    other = L.nf4s_tensor_layout(64, 64, d[1].end)
+    assert _err(bwd, FAKE, [d[0], other], two, 16, FAKE, None, None, 0, None, 0) == L.ESHAPE
+    odd = L.nf4s_tensor_layout(72, 128, d[1].end)
+    assert _err(bwd, FAKE, [d[0], odd], two, 16, FAKE, None, None, 0, None, 0) == L.ESHAPE
+    assert _err(bwd, FAKE, d, [FAKE, FAKE + 16], 16, FAKE, None, None, 0, None, 0) == L.EALIGN
+    assert _err(bwd, FAKE, d, two, 16, FAKE + 2, None, None, 0, None, 0) == L.EALIGN
+    assert _err(bwd, FAKE, d, two, 16, FAKE, [FAKE, None], [None, None], 16, None, 0) == L.EINVAL
+    assert _err(bwd, FAKE, d, two, 16, FAKE, [FAKE, None], [FAKE, None], 0, None, 0) == L.EINVAL
+    assert _err(bwd, FAKE, d, two, 0, FAKE, None, None, 0, None, 0) == L.ESHAPE
+    bad = L.nf4s_tensor_layout(128, 128, d[0].end)
+    bad.table_hash ^= 1
+    assert _err(bwd, FAKE, [d[0], bad], two, 16, FAKE, None, None, 0, None, 0) == L.ETABLE
+    q = [L.nf4s_tensor_layout(4096, 4096, 0)]
+    q.append(L.nf4s_tensor_layout(1024, 4096, q[0].end))
+    assert _err(bwd, FAKE, q, two, 512, FAKE, None, None, 0, FAKE, 1024) == L.EWORKSPACE

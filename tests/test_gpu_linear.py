@@ -439,3 +439,124 @@ def test_grouped_lora_matches_oracle(projs, ns, k, M, r):
         # the second backward adds the same gradients once more
         assert linear.rel_err(second[i]["dA"], 2 * ref["dA"]) <= 1e-5
         assert linear.rel_err(second[i]["dB"], 2 * ref["dB"]) <= 1e-5
+
+
+def _bwd_group_run(c, grouped, lora_on):
+    """dx of a group from one streamed_linear_bwd_grouped call, or the list of
+    single streamed_linear_bwd_packed outputs (same packed dy_j, du_j, A_j).
+    du_j is a seeded fp32 stand-in [M, r]; dy_j are seeded bf16."""
+    k, M = c["k"], c["M"]
+    s = stream()
+    keep, dyps, dus, As = [], [], [], []
+    for i, part in enumerate(c["parts"]):
+        dy = dev_bf16bits(part["dy"])
+        dyp = ws_tensor(L.nf4s_packed_activation_bytes(M, part["n"]))
+        L.nf4s_pack_activation(dy.data_ptr(), M, part["n"], dyp.data_ptr(), dyp.numel(), s)
+        keep += [dy, dyp]
+        dyps.append(dyp.data_ptr())
+        if part["p"] in lora_on:
+            du, A = dev_f32(part["du"]), dev_f32(part["a"])
+            keep += [du, A]
+            dus.append(du.data_ptr())
+            As.append(A.data_ptr())
+        else:
+            dus.append(None)
+            As.append(None)
+    sp = c["shard"].data_ptr()
+    r = R if any(dus) else 0
+    if grouped:
+        dx = torch.empty((M, k), dtype=torch.int16, device="cuda")
+        ws = ws_tensor(L.grouped_bwd_workspace_bytes([p["n"] for p in c["parts"]], k, M))
+        L.streamed_linear_bwd_grouped(sp, c["descs"], dyps, M, dx.data_ptr(), dus, As, r, ws.data_ptr(),
+                                      ws.numel(), s)
+        torch.cuda.synchronize()
+        return host_u16(dx)
+    outs = []
+    for d, dyp, du, A in zip(c["descs"], dyps, dus, As):
+        dx = torch.empty((M, k), dtype=torch.int16, device="cuda")
+        ws = ws_tensor(L.nf4s_workspace_bytes(L.OP_LINEAR_BWD_PACKED, M, d.n_out, k))
+        L.streamed_linear_bwd_packed(sp, d, dyp, M, dx.data_ptr(), du, A, R if du else 0, ws.data_ptr(),
+                                     ws.numel(), s)
+        torch.cuda.synchronize()
+        outs.append(host_u16(dx))
+    return outs
+
+
+def _bwd_group_setup(projs, ns, k, M, layer=0, step=0):
+    c = _group_setup(projs, ns, k, M, (), layer, step)
+    for i, (p, part) in enumerate(zip(projs, c["parts"])):
+        part["p"] = p
+        part["dy"] = synth.activation((M, part["n"]), step, 1 + i)
+        part["du"] = synth.lora_pair(layer + 1, p, M, k)[1]  # seeded fp32 [M, r]
+    return c
+
+
+BWD_GROUPS = [
+    # (projections, n_outs, k_in, M, adapters on)
+    (("q", "k", "v"), (576, 192, 192), 576, 300, ("q", "v")),
+    (("gate", "up"), (1536, 1536), 576, 512, ()),
+    (("q", "k", "v"), (128, 64, 192), 128, 37, ("k",)),
+    (("gate", "up"), (256, 64), 64, 513, ("up",)),
+    # a group of one may have any n_out % 8 == 0 (a ragged last step)
+    (("o",), (40,), 64, 100, ("o",)),
+]
+
+
+@pytest.mark.parametrize("projs,ns,k,M,lora_on", BWD_GROUPS)
+def test_grouped_backward_matches_oracle(projs, ns, k, M, lora_on):
+    """dx = sum_j (dy_j . W'_j + du_j . A_j) against the oracle's dequantised
+    weights in fp64."""
+    print(f"grouped bwd {projs} {ns}x{k} M={M} lora={lora_on}", flush=True)
+    c = _bwd_group_setup(projs, ns, k, M)
+    got = bits_to_f32(_bwd_group_run(c, True, lora_on)).astype(np.float64)
+    ref = np.zeros((M, k))
+    for p, part in zip(projs, c["parts"]):
+        wq = bits_to_f32(nf4.dequantize_bf16(nf4.quantize(part["w"]))).astype(np.float64)
+        ref += bits_to_f32(part["dy"]).astype(np.float64) @ wq
+        if p in lora_on:
+            ref += part["du"].astype(np.float64) @ part["a"].astype(np.float64)
+    assert linear.rel_err(got, ref) <= TOL
+
+
+@pytest.mark.parametrize("projs,ns,k,M,lora_on", [
+    (("q",), (576,), 576, 300, ("q",)),
+    (("o",), (40,), 64, 100, ("o",)),
+    (("gate",), (14336,), 4096, 512, ()),
+    (("v",), (1024,), 4096, 512, ("v",)),
+])
+def test_grouped_backward_of_one_is_the_single_call(projs, ns, k, M, lora_on):
+    """A group of one plans and contracts exactly as streamed_linear_bwd_packed."""
+    c = _bwd_group_setup(projs, ns, k, M)
+    g = _bwd_group_run(c, True, lora_on)
+    (one,) = _bwd_group_run(c, False, lora_on)
+    assert np.array_equal(g, one)
+
+
+@pytest.mark.parametrize("projs,ns,lora_on", [
+    (("q", "k", "v"), (4096, 1024, 1024), ("q", "v")),
+    (("gate", "up"), (14336, 14336), ()),
+])
+def test_grouped_backward_8b_sampled(projs, ns, lora_on):
+    """8B widths at M = 512, as the decoder step launches them: 512 sampled
+    outputs recomputed by the oracle one by one, and the whole result within
+    bf16 rounding of the sum of the single calls."""
+    print(f"grouped bwd 8b {projs}", flush=True)
+    k, M = 4096, 512
+    c = _bwd_group_setup(projs, ns, k, M, layer=3)
+    got = _bwd_group_run(c, True, lora_on)
+    singles = _bwd_group_run(c, False, lora_on)
+    rng = np.random.Generator(np.random.PCG64(91))
+    ms, ks = rng.integers(0, M, 512), rng.integers(0, k, 512)
+    ref = np.zeros(512)
+    for p, part in zip(projs, c["parts"]):
+        wq = bits_to_f32(nf4.dequantize_bf16(nf4.quantize(part["w"]))).astype(np.float64)
+        dy = bits_to_f32(part["dy"]).astype(np.float64)
+        ref += np.array([dy[m] @ wq[:, j] for m, j in zip(ms, ks)])
+        if p in lora_on:
+            du, a = part["du"].astype(np.float64), part["a"].astype(np.float64)
+            ref += np.array([du[m] @ a[:, j] for m, j in zip(ms, ks)])
+    g = bits_to_f32(got).astype(np.float64)
+    assert linear.rel_err(g[ms, ks], ref) <= TOL
+    total = sum(bits_to_f32(o).astype(np.float64) for o in singles)
+    # the single calls round each term to bf16 before the sum
+    assert np.max(np.abs(g - total)) <= 2.0 ** -6 * np.max(np.abs(total))

@@ -250,11 +250,7 @@ class Decoder:
         time_calls predicate accepts is one timed entry with n_out the sum."""
         ki = self.sh.shapes[ps[0]][1]
         xp = self._pack(x, ki)
-        tg = [p for p in ps if adapters and p in self.targets]
-        if tg:
-            # u = x . A^T of every adapter reading x, one launch per kernel
-            lora_fwd_grouped(x.data_ptr(), self.M, ki, [self.lora[(i, p)][0].data_ptr() for p in tg],
-                             self.r, [self.u[p].data_ptr() for p in tg], *self._ws(), self._s)
+        tg = self._lora_u(i, ps, x, adapters)
         us = [self.u[p].data_ptr() if p in tg else None for p in ps]
         Bs = [self.lora[(i, p)][1].data_ptr() if p in tg else None for p in ps]
         r = self.r if any(us) else 0
@@ -268,6 +264,16 @@ class Decoder:
                                         [y.data_ptr() for y in ys], us, Bs, r, scale, *self._ws(),
                                         self._s)
         self._tock(ev)
+
+    def _lora_u(self, i, ps, x, adapters=True):
+        """u = x . A^T of every adapter among ps (all reading x), one launch
+        per kernel; returns those projections."""
+        tg = [p for p in ps if adapters and p in self.targets]
+        if tg:
+            ki = self.sh.shapes[ps[0]][1]
+            lora_fwd_grouped(x.data_ptr(), self.M, ki, [self.lora[(i, p)][0].data_ptr() for p in tg],
+                             self.r, [self.u[p].data_ptr() for p in tg], *self._ws(), self._s)
+        return tg
 
     def _tick(self, direction, n, k):
         if self.time_calls is None or not self.time_calls(direction, n, k):
@@ -346,7 +352,8 @@ class Decoder:
     # -- one layer ---------------------------------------------------------------------
     def _layer_fwd(self, i, base, recompute, adapters=True, hin=None, hout=None, keep=False):
         """Layer i's body from h_i. The recompute keeps the fp32 attention
-        output for the backward and skips h_{i+1}, which is already stored;
+        output for the backward and skips h_{i+1}, which is already stored
+        (and with it the down projection's product, which nothing else reads);
         keep=True keeps it in a first forward too (the last layer, whose
         backward follows the head with the body buffers intact).
         adapters=False runs the frozen base alone (the reference model);
@@ -372,8 +379,12 @@ class Decoder:
         self._fwd(base, i, ("gate", "up"), self.n2, (self.g, self.u_), a)
         nf4s_swiglu_fwd(self.g.data_ptr(), self.u_.data_ptr(), M, self.I, self.sw.data_ptr(), s,
                         packed=self._produced(self.sw, self.I))
-        self._fwd(base, i, ("down",), self.sw, (self.dn,), a)
-        if not recompute:
+        if recompute:
+            # h_{i+1} is stored and the backward reads no output of the down
+            # projection: only its adapter's u is recomputed
+            self._lora_u(i, ("down",), self.sw, a)
+        else:
+            self._fwd(base, i, ("down",), self.sw, (self.dn,), a)
             nf4s_residual_add(self.h_mid.data_ptr(), self.dn.data_ptr(), M * H, hout.data_ptr(), s)
 
     def _layer_bwd(self, i, base):

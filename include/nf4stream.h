@@ -410,13 +410,16 @@ int nf4s_embed(const uint16_t* table, int64_t vocab, int64_t hidden, const int64
  * [T, H] gradients of y, 1..3, summed in fp32 in that order),
  *   d = rstd * g - x * rstd^3 * mean_j(g * x),
  * written to dh (accumulate = 0) or added to it (accumulate = 1). dys is a
- * host array of device pointers. Errors: EINVAL, ESHAPE, EALIGN.
+ * host array of device pointers. y (nullable) receives the resulting dh as
+ * bf16 [T, H] (what nf4s_to_bf16 would write), packed (nullable, needs y)
+ * also in fragment order, so the next GEMM's input leaves with the norm's
+ * backward. Errors: EINVAL, ESHAPE, EALIGN.
  */
 int nf4s_rmsnorm_fwd(const float* x, const float* w, int64_t T, int64_t H, float eps, uint16_t* y,
                      float* rstd, void* packed, void* stream);
 int nf4s_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float* x, const float* w,
                      const float* rstd, int64_t T, int64_t H, int accumulate, float* dh,
-                     void* stream);
+                     uint16_t* y, void* packed, void* stream);
 
 /*
  * Rotary embedding, rotate-half form, in place on bf16 x [T, heads*head_dim]:

@@ -128,7 +128,7 @@ _SIG = {
     "nf4s_embed": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P]),
     "nf4s_rmsnorm_fwd": (ctypes.c_int, [_P, _P, _I64, _I64, ctypes.c_float, _P, _P, _P, _P]),
     "nf4s_rmsnorm_bwd": (ctypes.c_int, [ctypes.POINTER(_P), ctypes.c_int, _P, _P, _P, _I64, _I64,
-                                        ctypes.c_int, _P, _P]),
+                                        ctypes.c_int, _P, _P, _P, _P]),
     "nf4s_rope": (ctypes.c_int, [_P, _I64, _I64, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                  ctypes.c_int, _P]),
     "nf4s_attention_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_int, ctypes.c_int,
@@ -309,10 +309,11 @@ def nf4s_rmsnorm_fwd(x, w, T, H, eps, y, rstd, stream=0, packed=None):
     _check(lib().nf4s_rmsnorm_fwd(x, w, T, H, eps, y, rstd, packed, stream))
 
 
-def nf4s_rmsnorm_bwd(dys, x, w, rstd, T, H, accumulate, dh, stream=0):
-    """dys: a sequence of 1..3 device pointers (bf16 [T, H] gradients)."""
+def nf4s_rmsnorm_bwd(dys, x, w, rstd, T, H, accumulate, dh, stream=0, y=None, packed=None):
+    """dys: a sequence of 1..3 device pointers (bf16 [T, H] gradients);
+    y / packed: optional bf16 copies of the resulting dh (row-major / packed)."""
     arr = (_P * len(dys))(*dys)
-    _check(lib().nf4s_rmsnorm_bwd(arr, len(dys), x, w, rstd, T, H, accumulate, dh, stream))
+    _check(lib().nf4s_rmsnorm_bwd(arr, len(dys), x, w, rstd, T, H, accumulate, dh, y, packed, stream))
 
 
 def nf4s_rope(x, T, S, heads, head_dim, theta, inverse, stream=0):

@@ -730,7 +730,7 @@ int nf4s_rmsnorm_fwd(const float* x, const float* w, int64_t T, int64_t H, float
 
 int nf4s_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float* x, const float* w,
                      const float* rstd, int64_t T, int64_t H, int accumulate, float* dh,
-                     void* stream) {
+                     uint16_t* y, void* packed, void* stream) {
   int rc;
   if ((rc = check_rows(T, H)) || (rc = check_norm_width(H))) return rc;
   if (!dys) return fail(NF4S_EINVAL, "dys is NULL");
@@ -741,7 +741,10 @@ int nf4s_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float* x, const
   if ((rc = check_ptr(x, "x")) || (rc = check_ptr(w, "w")) || (rc = check_ptr(rstd, "rstd", 4)) ||
       (rc = check_ptr(dh, "dh")))
     return rc;
-  return launched(launch_rmsnorm_bwd(dys, n_dy, x, w, rstd, T, H, accumulate, dh,
+  if (packed && !y) return fail(NF4S_EINVAL, "packed output needs y");
+  if (y && (rc = check_ptr(y, "y"))) return rc;
+  if (packed && (rc = check_packed_out(packed, T, H))) return rc;
+  return launched(launch_rmsnorm_bwd(dys, n_dy, x, w, rstd, T, H, accumulate, dh, y, packed,
                                      static_cast<hipStream_t>(stream)),
                   "rmsnorm_bwd launch");
 }

@@ -135,9 +135,10 @@ hipError_t launch_embed(const uint16_t* E, int64_t V, const int64_t* ids, int64_
 // except for rows past T (left as they are; the GEMMs never store them)
 hipError_t launch_rmsnorm_fwd(const float* x, const float* w, int64_t T, int64_t H, float eps,
                               uint16_t* y, float* rstd, void* packed, hipStream_t s);
+// y, packed (nullable): the resulting dh also as bf16 (and in fragment order)
 hipError_t launch_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float* x, const float* w,
                               const float* rstd, int64_t T, int64_t H, int accumulate, float* dh,
-                              hipStream_t s);
+                              uint16_t* y, void* packed, hipStream_t s);
 hipError_t launch_rope(uint16_t* x, int64_t T, int64_t S, int heads, int d, double theta,
                        int inverse, hipStream_t s);
 hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,

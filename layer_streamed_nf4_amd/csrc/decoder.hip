@@ -143,10 +143,14 @@ __device__ __forceinline__ void dy_sum8(const DyPtrs& dys, int n_dy, int64_t off
   }
 }
 
+// y, packed (nullable): the resulting dh row also as bf16, row-major and in
+// MFMA fragment order (the next GEMM's input), as k_f32_to_bf16 writes them
 __global__ __launch_bounds__(256) void k_rmsnorm_bwd(DyPtrs dys, int n_dy, const float* __restrict__ x,
                                                      const float* __restrict__ w,
                                                      const float* __restrict__ rstd, int64_t H,
-                                                     int accumulate, float* __restrict__ dh) {
+                                                     int accumulate, float* __restrict__ dh,
+                                                     uint16_t* __restrict__ y,
+                                                     uint8_t* __restrict__ packed) {
   __shared__ float red[4];
   const int64_t t = blockIdx.x;
   const float* xr = x + t * H;
@@ -175,6 +179,17 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(DyPtrs dys, int n_dy, const
       o[e] = accumulate ? o[e] + d : d;
     }
     store8_f32(dh + t * H + 8 * c, o);
+    if (y) {
+      u32x4v b;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b[i] = pack_bf16x2(o[2 * i], o[2 * i + 1]);
+      *reinterpret_cast<u32x4v*>(y + t * H + 8 * c) = b;
+      if (packed) {
+        const int64_t kb = (H + 63) / 64 * 4;
+        *reinterpret_cast<u32x4v*>(packed + frag_offset(t, 8 * c, kb)) = b;
+        if (c == nc - 1) frag_zero_tail(packed, t, H, kb);
+      }
+    }
   }
 }
 
@@ -1123,10 +1138,10 @@ hipError_t launch_rmsnorm_fwd(const float* x, const float* w, int64_t T, int64_t
 
 hipError_t launch_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float* x, const float* w,
                               const float* rstd, int64_t T, int64_t H, int accumulate, float* dh,
-                              hipStream_t s) {
+                              uint16_t* y, void* packed, hipStream_t s) {
   DyPtrs d{{dys[0], n_dy > 1 ? dys[1] : nullptr, n_dy > 2 ? dys[2] : nullptr}};
   hipLaunchKernelGGL(k_rmsnorm_bwd, dim3((unsigned)T), dim3(256), 0, s, d, n_dy, x, w, rstd, H,
-                     accumulate, dh);
+                     accumulate, dh, y, static_cast<uint8_t*>(packed));
   return hipGetLastError();
 }
 

@@ -312,12 +312,14 @@ class Decoder:
                 out[j] = buf.data_ptr()
         return out
 
-    def _bwd(self, base, i, ps, x, dys, dxs):
+    def _bwd(self, base, i, ps, x, dys, dxs, dy_packed=None):
         """Backward of the projections ps, all reading x: the adapter
         gradients of the targets among them (one launch per kernel), then
         dx with each adapter's du . A added: one sum in dxs[0] when the group
         runs as one contraction, else one dx per projection. Returns the dx
-        tensors that hold the result."""
+        tensors that hold the result. dy_packed: the packed dy of a single
+        projection, when its producer wrote it."""
+        assert dy_packed is None or len(ps) == 1
         ki = self.sh.shapes[ps[0]][1]
         tg = [p for p in ps if p in self.targets]
         if tg:
@@ -339,7 +341,7 @@ class Decoder:
             return dxs[:1]
         for p, dy, dx in zip(ps, dys, dxs):
             no = self.sh.shapes[p][0]
-            dyp = self._pack(dy, no)
+            dyp = self._pack(dy, no) if dy_packed is None else dy_packed
             if p in tg:
                 streamed_linear_bwd_packed(base, self.sh.layout.descs[p], dyp, self.M, dx.data_ptr(),
                                            self.du[p].data_ptr(), self.lora[(i, p)][0].data_ptr(),
@@ -377,33 +379,37 @@ class Decoder:
         nf4s_rmsnorm_fwd(self.h_mid.data_ptr(), self.norms["mlp"][i].data_ptr(), M, H, c["eps"],
                          self.n2.data_ptr(), self.rstd2.data_ptr(), s, packed=self._produced(self.n2, H))
         self._fwd(base, i, ("gate", "up"), self.n2, (self.g, self.u_), a)
-        nf4s_swiglu_fwd(self.g.data_ptr(), self.u_.data_ptr(), M, self.I, self.sw.data_ptr(), s,
-                        packed=self._produced(self.sw, self.I))
         if recompute:
             # h_{i+1} is stored and the backward reads no output of the down
-            # projection: only its adapter's u is recomputed
-            self._lora_u(i, ("down",), self.sw, a)
+            # projection: only its adapter's u is recomputed, from the SwiGLU
+            # output, which nothing else in the backward reads
+            if a and "down" in self.targets:
+                nf4s_swiglu_fwd(self.g.data_ptr(), self.u_.data_ptr(), M, self.I, self.sw.data_ptr(), s)
+                self._lora_u(i, ("down",), self.sw, a)
         else:
+            nf4s_swiglu_fwd(self.g.data_ptr(), self.u_.data_ptr(), M, self.I, self.sw.data_ptr(), s,
+                            packed=self._produced(self.sw, self.I))
             self._fwd(base, i, ("down",), self.sw, (self.dn,), a)
             nf4s_residual_add(self.h_mid.data_ptr(), self.dn.data_ptr(), M * H, hout.data_ptr(), s)
 
     def _layer_bwd(self, i, base):
-        """dh holds dL/dh_{i+1} on entry and dL/dh_i on exit; the layer's body
+        """dh holds dL/dh_{i+1} on entry (and dd its bf16 form, packed in
+        packed_c) and dL/dh_i on exit (likewise, for i > 0); the layer's body
         was just recomputed (with the fp32 attention output kept)."""
         c, s, M, H = self.cfg, self._s, self.M, self.H
         self._packed_key = self._packed_key_b = None
-        nf4s_to_bf16(self.dh.data_ptr(), M, H, self.dd.data_ptr(), s, packed=self._produced(self.dd, H))
-        self._bwd(base, i, ("down",), self.sw, (self.dd,), (self.dsw,))
+        self._bwd(base, i, ("down",), self.sw, (self.dd,), (self.dsw,),
+                  dy_packed=self.packed_c.data_ptr())
         nf4s_swiglu_bwd(self.dsw.data_ptr(), self.g.data_ptr(), self.u_.data_ptr(), M, self.I,
                         self.dg.data_ptr(), self.du_.data_ptr(), s,
                         dg_packed=self._produced(self.dg, self.I),
                         du_packed=self._produced(self.du_, self.I, second=True))
         dn = self._bwd(base, i, ("gate", "up"), self.n2, (self.dg, self.du_), self.dnx[:2])
+        self._packed_key_b = None
+        # the norm's backward also leaves dh as the o projection's bf16 input
         nf4s_rmsnorm_bwd([x.data_ptr() for x in dn], self.h_mid.data_ptr(),
                          self.norms["mlp"][i].data_ptr(), self.rstd2.data_ptr(), M, H, 1,
-                         self.dh.data_ptr(), s)
-        self._packed_key_b = None
-        nf4s_to_bf16(self.dh.data_ptr(), M, H, self.dd.data_ptr(), s, packed=self._produced(self.dd, H))
+                         self.dh.data_ptr(), s, y=self.dd.data_ptr(), packed=self._produced(self.dd, H))
         self._bwd(base, i, ("o",), self.o, (self.dd,), (self.do,))
         nf4s_attention_bwd(self.q.data_ptr(), self.k.data_ptr(), self.vv.data_ptr(),
                            self.o32.data_ptr(), self.do.data_ptr(), self.lse.data_ptr(), self.B,
@@ -414,7 +420,8 @@ class Decoder:
         dn = self._bwd(base, i, ("q", "k", "v"), self.n1, (self.dq, self.dk, self.dv), self.dnx)
         nf4s_rmsnorm_bwd([x.data_ptr() for x in dn], self.h[i].data_ptr(),
                          self.norms["attn"][i].data_ptr(), self.rstd1.data_ptr(), M, H, 1,
-                         self.dh.data_ptr(), s)
+                         self.dh.data_ptr(), s, y=self.dd.data_ptr() if i > 0 else None,
+                         packed=self.packed_c.data_ptr() if i > 0 else None)
 
     # -- the step ----------------------------------------------------------------------
     def _check_ids(self, ids, targets):
@@ -450,8 +457,11 @@ class Decoder:
         self._packed_key = self._packed_key_b = None
         dense_linear_bwd_packed(self.lm_head.data_ptr(), V, H, self._pack(self.dlogits, V), M,
                                 self.dhn.data_ptr(), *self._ws(), s)
+        # (every norm backward of the sweep also leaves dh as bf16 dd, packed
+        # in packed_c: the input of the next layer's down-projection backward)
         nf4s_rmsnorm_bwd([self.dhn.data_ptr()], self.h[L].data_ptr(), self.norms["final"].data_ptr(),
-                         self.rstd_f.data_ptr(), M, H, 0, self.dh.data_ptr(), s)
+                         self.rstd_f.data_ptr(), M, H, 0, self.dh.data_ptr(), s, y=self.dd.data_ptr(),
+                         packed=self.packed_c.data_ptr())
         for i in range(L - 1, -1, -1):
             base = self._acquire(i, nxt=i - 1 if i > 0 else None)
             if not (i == L - 1 and self._kept_last):

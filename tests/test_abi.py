@@ -251,6 +251,9 @@ def test_decoder_argument_errors():
     assert _err(L.nf4s_rmsnorm_bwd, [], FAKE, FAKE, FAKE, 4, 8, 0, FAKE) == L.EINVAL
     assert _err(L.nf4s_rmsnorm_bwd, [FAKE] * 4, FAKE, FAKE, FAKE, 4, 8, 0, FAKE) == L.EINVAL
     assert _err(L.nf4s_rmsnorm_bwd, [FAKE], FAKE, FAKE, FAKE, 4, 8, 2, FAKE) == L.EINVAL
+    # a packed copy needs the bf16 one; both 16-byte aligned
+    assert _err(L.nf4s_rmsnorm_bwd, [FAKE], FAKE, FAKE, FAKE, 4, 8, 0, FAKE, 0, None, FAKE) == L.EINVAL
+    assert _err(L.nf4s_rmsnorm_bwd, [FAKE], FAKE, FAKE, FAKE, 4, 8, 0, FAKE, 0, FAKE + 2) == L.EALIGN
     assert _err(L.nf4s_rmsnorm_fwd, FAKE, FAKE, 4, 8, 0.0, FAKE, FAKE) == L.EINVAL   # eps
     assert _err(L.nf4s_rmsnorm_fwd, FAKE, FAKE, 0, 8, 1e-5, FAKE, FAKE) == L.ESHAPE
     assert _err(L.nf4s_adamw, FAKE, FAKE, FAKE, FAKE, 16, 1e-3, 0.9, 0.999, 1e-8, 0.0, 0) == L.EINVAL

@@ -224,6 +224,17 @@ def test_producers_write_the_packed_layout(T, W):
     pk = sentinel()
     L.nf4s_to_bf16(x.data_ptr(), T, W, y.data_ptr(), s, packed=pk.data_ptr())
     packed_rows_equal(y, pk)
+    # the norm backward's bf16 copy of its result: the bits nf4s_to_bf16 gives
+    # for that fp32 result, row-major and packed (accumulating into dh)
+    dh = dev_f32(g.standard_normal((T, W)).astype(np.float32))
+    yb, ybt = torch.empty_like(y), torch.empty_like(y)
+    pb = sentinel()
+    L.nf4s_rmsnorm_bwd([db.data_ptr(), gb.data_ptr()], x.data_ptr(), w.data_ptr(), rstd.data_ptr(), T, W,
+                       1, dh.data_ptr(), s, y=yb.data_ptr(), packed=pb.data_ptr())
+    L.nf4s_to_bf16(dh.data_ptr(), T, W, ybt.data_ptr(), s)
+    torch.cuda.synchronize()
+    assert torch.equal(yb, ybt)
+    packed_rows_equal(yb, pb)
     # rows past T keep the sentinel
     if (T + 255) // 256 * 256 > T:
         a = pk.cpu().numpy()[:nbytes].reshape(-1, kb, 64, 16)

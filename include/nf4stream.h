@@ -265,6 +265,21 @@ int streamed_linear_bwd_packed(const void* shard_dev, const nf4s_tensor_desc* d,
  */
 int nf4s_grouped_workspace_bytes(int n, const int64_t* n_outs, int64_t k_in, int64_t M,
                                  size_t* bytes);
+
+/*
+ * Forward into the residual stream (the o and down projections of a llama
+ * layer, [G] s2.1): y as streamed_linear_fwd_packed writes it, and
+ *   h_out = h_in + y        fp32 [M, n_out], y's bf16 values added in fp32
+ * (h_in may be h_out). When the contraction is split the sum of the partials
+ * writes both at once; otherwise a residual kernel follows the GEMM. The
+ * results equal streamed_linear_fwd_packed followed by nf4s_residual_add bit
+ * for bit. ws as for streamed_linear_fwd_packed. Errors: as there, and EINVAL
+ * / EALIGN for h_in, h_out (16-byte aligned).
+ */
+int streamed_linear_fwd_residual(const void* shard_dev, const nf4s_tensor_desc* d,
+                                 const void* x_packed, int64_t M, uint16_t* y, const float* lora_u,
+                                 const float* lora_B, int r, float scale, const float* h_in,
+                                 float* h_out, void* ws, size_t ws_bytes, void* stream);
 int streamed_linear_fwd_grouped(const void* shard_dev, const nf4s_tensor_desc* descs, int n,
                                 const void* x_packed, int64_t M, uint16_t* const* ys,
                                 const float* const* lora_us, const float* const* lora_Bs, int r,

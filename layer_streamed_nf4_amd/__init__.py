@@ -36,7 +36,7 @@ EXPORTS = (
     "streamed_linear_bwd_packed", "dense_linear_fwd_packed", "dense_linear_bwd_packed",
     "nf4s_grouped_workspace_bytes", "streamed_linear_fwd_grouped",
     "nf4s_lora_grouped_workspace_bytes", "lora_fwd_grouped", "lora_bwd_grouped",
-    "nf4s_grouped_bwd_workspace_bytes", "streamed_linear_bwd_grouped",
+    "nf4s_grouped_bwd_workspace_bytes", "streamed_linear_bwd_grouped", "streamed_linear_fwd_residual",
     "nf4s_embed", "nf4s_rmsnorm_fwd", "nf4s_rmsnorm_bwd", "nf4s_rope", "nf4s_attention_fwd",
     "nf4s_attention_bwd", "nf4s_swiglu_fwd", "nf4s_swiglu_bwd", "nf4s_residual_add",
     "nf4s_to_bf16", "nf4s_cross_entropy", "nf4s_adamw", "nf4s_token_nll", "nf4s_dpo_loss",
@@ -112,6 +112,9 @@ _SIG = {
     "streamed_linear_fwd_grouped": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), ctypes.c_int, _P,
                                                    _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float,
                                                    _P, ctypes.c_size_t, _P]),
+    "streamed_linear_fwd_residual": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P, _P,
+                                                    ctypes.c_int, ctypes.c_float, _P, _P, _P,
+                                                    ctypes.c_size_t, _P]),
     "nf4s_grouped_bwd_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P]),
     "streamed_linear_bwd_grouped": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), ctypes.c_int, _P,
                                                    _I64, _P, _P, _P, ctypes.c_int, _P,
@@ -268,6 +271,13 @@ def streamed_linear_fwd_grouped(shard, descs, x_packed, M, ys, lora_us, lora_Bs,
     _check(lib().streamed_linear_fwd_grouped(shard, darr, n, x_packed, M, _ptr_array(ys),
                                              _ptr_array(lora_us), _ptr_array(lora_Bs), r, scale, ws,
                                              ws_bytes, stream))
+
+
+def streamed_linear_fwd_residual(shard, desc, x_packed, M, y, lora_u, lora_B, r, scale, h_in, h_out, ws,
+                                 ws_bytes, stream=0):
+    """y = the forward of desc on x_packed (bf16) and h_out = h_in + y (fp32)."""
+    _check(lib().streamed_linear_fwd_residual(shard, ctypes.byref(desc), x_packed, M, y, lora_u, lora_B,
+                                              r, scale, h_in, h_out, ws, ws_bytes, stream))
 
 
 def grouped_bwd_workspace_bytes(n_outs, k_in, M):

@@ -348,6 +348,23 @@ int streamed_linear_fwd_packed(const void* shard_dev, const nf4s_tensor_desc* d,
                        stream);
 }
 
+int streamed_linear_fwd_residual(const void* shard_dev, const nf4s_tensor_desc* d,
+                                 const void* x_packed, int64_t M, uint16_t* y, const float* lora_u,
+                                 const float* lora_B, int r, float scale, const float* h_in,
+                                 float* h_out, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  GemmPlan p;
+  if ((rc = linear_checks(false, shard_dev, d, M, y, lora_u, lora_B, r, scale, &p))) return rc;
+  if ((rc = check_ptr(x_packed, "x_packed", 256))) return rc;
+  if ((rc = check_ptr(h_in, "h_in")) || (rc = check_ptr(h_out, "h_out"))) return rc;
+  if (p.part_bytes && (rc = check_ws(ws, ws_bytes, p.part_bytes))) return rc;
+  hipError_t e = launch_linear_fwd_residual(resolve(shard_dev, d), d->n_out, d->k_in,
+                                            static_cast<const uint8_t*>(x_packed), M, y, lora_u, lora_B,
+                                            lora_u ? r : 0, scale, h_in, h_out, ws,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "linear launch");
+}
+
 int streamed_linear_bwd_packed(const void* shard_dev, const nf4s_tensor_desc* d,
                                const void* dy_packed, int64_t M, uint16_t* dx,
                                const float* lora_du, const float* lora_A, int r, void* ws,

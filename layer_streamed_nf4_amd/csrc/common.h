@@ -74,6 +74,13 @@ hipError_t launch_linear_packed(bool backward, const QPtrs& q, int64_t n_out, in
                                 const uint8_t* a_packed, int64_t M, uint16_t* out,
                                 const float* lora_l, const float* lora_r, int r, float scale,
                                 void* part_ws, hipStream_t s);
+// The forward with the residual stream: y as launch_linear_packed writes it,
+// and h_out = h_in + y (fp32 [M, n_out]), summed with the split partials or,
+// unsplit, by k_residual_add.
+hipError_t launch_linear_fwd_residual(const QPtrs& q, int64_t n_out, int64_t k_in,
+                                      const uint8_t* x_packed, int64_t M, uint16_t* y,
+                                      const float* lora_u, const float* lora_B, int r, float scale,
+                                      const float* h_in, float* h_out, void* part_ws, hipStream_t s);
 // Forward of nseg (<= GEMM_MAX_SEG) NF4 linears reading the same packed
 // activation, in one launch (lora_us / lora_Bs entries may be null).
 hipError_t launch_linear_grouped_fwd(const QPtrs* q, int nseg, const int64_t* n_outs, int64_t k_in,

@@ -1167,11 +1167,15 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables ta
 }
 
 // Sum of the split partials in split order, rounded once to bf16; blockIdx.y
-// selects the weight of a grouped launch.
+// selects the weight of a grouped launch. With res_out, also the residual
+// stream res_out = res_in + bf16 result in fp32 (what k_residual_add computes
+// from the bf16 output).
 struct SumSegs {
   const float* part[GEMM_MAX_SEG];
   uint16_t* out[GEMM_MAX_SEG];
   int64_t n[GEMM_MAX_SEG];
+  const float* res_in[GEMM_MAX_SEG];
+  float* res_out[GEMM_MAX_SEG];
 };
 
 __global__ __launch_bounds__(256) void k_split_sum(SumSegs sg, int splits) {
@@ -1191,11 +1195,22 @@ __global__ __launch_bounds__(256) void k_split_sum(SumSegs sg, int splits) {
     o.x = pack_bf16x2(s.x, s.y);
     o.y = pack_bf16x2(s.z, s.w);
     *reinterpret_cast<uint2*>(out + i) = o;
+    if (sg.res_out[sgi]) {
+      const float4 h = *reinterpret_cast<const float4*>(sg.res_in[sgi] + i);
+      float4 r;
+      r.x = h.x + __uint_as_float(o.x << 16);
+      r.y = h.y + __uint_as_float(o.x & 0xFFFF0000u);
+      r.z = h.z + __uint_as_float(o.y << 16);
+      r.w = h.w + __uint_as_float(o.y & 0xFFFF0000u);
+      *reinterpret_cast<float4*>(sg.res_out[sgi] + i) = r;
+    }
   } else {
     for (int64_t e = i; e < n; ++e) {
       float s = part[e];
       for (int p = 1; p < splits; ++p) s += part[(int64_t)p * n + e];
-      out[e] = (uint16_t)(pack_bf16x2(s, 0.0f) & 0xFFFFu);
+      const uint32_t b = pack_bf16x2(s, 0.0f) & 0xFFFFu;
+      out[e] = (uint16_t)b;
+      if (sg.res_out[sgi]) sg.res_out[sgi][e] = sg.res_in[sgi][e] + __uint_as_float(b << 16);
     }
   }
 }
@@ -1254,7 +1269,8 @@ static hipError_t launch_gemm(bool backward, const QPtrs* q, int nseg, const uin
                               const int64_t* n_outs, int64_t k_in, const uint8_t* a_packed,
                               int64_t M, uint16_t* const* outs, const float* const* lora_ls,
                               const float* const* lora_rs, int r, float scale, void* part_ws,
-                              hipStream_t s) {
+                              hipStream_t s, const float* res_in = nullptr,
+                              float* res_out = nullptr) {
   GemmArgs g = {};
   g.wd = wd;
   g.M = M;
@@ -1303,6 +1319,8 @@ static hipError_t launch_gemm(bool backward, const QPtrs* q, int nseg, const uin
     sum.part[i] = sg.part;
     sum.out[i] = sg.out;
     sum.n[i] = n;
+    sum.res_in[i] = res_in;
+    sum.res_out[i] = res_out;
     max_n = n > max_n ? n : max_n;
   }
   const dim3 grid((unsigned)tile0, (unsigned)((M + p.bm - 1) / p.bm), (unsigned)p.splits);
@@ -1325,7 +1343,9 @@ static hipError_t launch_gemm(bool backward, const QPtrs* q, int nseg, const uin
   }
 #undef NF4S_GEMM
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
+  if (e != hipSuccess) return e;
+  if (p.splits == 1)  // the residual from the bf16 output, as a kernel of its own
+    return res_out ? launch_residual_add(res_in, outs[0], M * n_outs[0], res_out, s) : hipSuccess;
   const dim3 g2((unsigned)((max_n / 4 + 1 + 255) / 256), (unsigned)nseg);
   hipLaunchKernelGGL(k_split_sum, g2, dim3(256), 0, s, sum, p.splits);
   return hipGetLastError();
@@ -1337,6 +1357,14 @@ hipError_t launch_linear_packed(bool backward, const QPtrs& q, int64_t n_out, in
                                 void* part_ws, hipStream_t s) {
   return launch_gemm(backward, &q, 1, nullptr, &n_out, k_in, a_packed, M, &out, &lora_l, &lora_r, r,
                      scale, part_ws, s);
+}
+
+hipError_t launch_linear_fwd_residual(const QPtrs& q, int64_t n_out, int64_t k_in,
+                                      const uint8_t* x_packed, int64_t M, uint16_t* y,
+                                      const float* lora_u, const float* lora_B, int r, float scale,
+                                      const float* h_in, float* h_out, void* part_ws, hipStream_t s) {
+  return launch_gemm(false, &q, 1, nullptr, &n_out, k_in, x_packed, M, &y, &lora_u, &lora_B, r, scale,
+                     part_ws, s, h_in, h_out);
 }
 
 hipError_t launch_linear_grouped_fwd(const QPtrs* q, int nseg, const int64_t* n_outs, int64_t k_in,

@@ -35,11 +35,11 @@ from . import (OP_ATTENTION_BWD, OP_CROSS_ENTROPY, OP_DENSE_BWD_PACKED, OP_DENSE
                nf4s_embed, nf4s_logit_grad, nf4s_token_nll,
                nf4s_pack_activation, nf4s_packed_activation_bytes, nf4s_pool_acquire,
                nf4s_pool_create, nf4s_pool_destroy, nf4s_pool_prefetch, nf4s_pool_release,
-               nf4s_pool_set_layer, nf4s_pool_stats, nf4s_residual_add, nf4s_rmsnorm_bwd,
-               nf4s_rmsnorm_fwd, nf4s_rope, nf4s_swiglu_bwd, nf4s_swiglu_fwd, nf4s_to_bf16,
+               nf4s_pool_set_layer, nf4s_pool_stats, nf4s_rmsnorm_bwd,
+               nf4s_rmsnorm_fwd, nf4s_rope, nf4s_swiglu_bwd, nf4s_swiglu_fwd,
                nf4s_workspace_bytes, streamed_linear_bwd_packed, streamed_linear_fwd_packed,
                streamed_linear_fwd_grouped, grouped_workspace_bytes, grouped_bwd_workspace_bytes,
-               streamed_linear_bwd_grouped)
+               streamed_linear_bwd_grouped, streamed_linear_fwd_residual)
 from .stack import ALIGN, PROJ, ShardSet, _round_up
 
 # projections that read the same input: q, k, v the normed h; gate, up the
@@ -244,7 +244,7 @@ class Decoder:
         self._packed_key = (a.data_ptr(), K)
         return self.packed.data_ptr()
 
-    def _fwd(self, base, i, ps, x, ys, adapters=True):
+    def _fwd(self, base, i, ps, x, ys, adapters=True, res=None):
         """Forward of the projections ps, all reading x (q, k, v or gate, up,
         or a single one), as one GEMM launch writing ys; each launch the
         time_calls predicate accepts is one timed entry with n_out the sum."""
@@ -256,7 +256,12 @@ class Decoder:
         r = self.r if any(us) else 0
         scale = self.scale if any(us) else 0.0
         ev = self._tick("fwd", sum(self.sh.shapes[p][0] for p in ps), ki)
-        if len(ps) == 1:
+        if res is not None:  # a single projection into the residual stream: res = (h_in, h_out)
+            assert len(ps) == 1
+            streamed_linear_fwd_residual(base, self.sh.layout.descs[ps[0]], xp, self.M, ys[0].data_ptr(),
+                                         us[0], Bs[0], r, scale, res[0].data_ptr(), res[1].data_ptr(),
+                                         *self._ws(), self._s)
+        elif len(ps) == 1:
             streamed_linear_fwd_packed(base, self.sh.layout.descs[ps[0]], xp, self.M, ys[0].data_ptr(),
                                        us[0], Bs[0], r, scale, *self._ws(), self._s)
         else:
@@ -374,8 +379,7 @@ class Decoder:
         nf4s_attention_fwd(self.q.data_ptr(), self.k.data_ptr(), self.vv.data_ptr(), self.B, self.S,
                            c["heads"], c["kv_heads"], c["head_dim"], self.o.data_ptr(),
                            self.o32.data_ptr() if recompute or keep else None, self.lse.data_ptr(), s)
-        self._fwd(base, i, ("o",), self.o, (self.ao,), a)
-        nf4s_residual_add(hin.data_ptr(), self.ao.data_ptr(), M * H, self.h_mid.data_ptr(), s)
+        self._fwd(base, i, ("o",), self.o, (self.ao,), a, res=(hin, self.h_mid))
         nf4s_rmsnorm_fwd(self.h_mid.data_ptr(), self.norms["mlp"][i].data_ptr(), M, H, c["eps"],
                          self.n2.data_ptr(), self.rstd2.data_ptr(), s, packed=self._produced(self.n2, H))
         self._fwd(base, i, ("gate", "up"), self.n2, (self.g, self.u_), a)
@@ -389,8 +393,7 @@ class Decoder:
         else:
             nf4s_swiglu_fwd(self.g.data_ptr(), self.u_.data_ptr(), M, self.I, self.sw.data_ptr(), s,
                             packed=self._produced(self.sw, self.I))
-            self._fwd(base, i, ("down",), self.sw, (self.dn,), a)
-            nf4s_residual_add(self.h_mid.data_ptr(), self.dn.data_ptr(), M * H, hout.data_ptr(), s)
+            self._fwd(base, i, ("down",), self.sw, (self.dn,), a, res=(self.h_mid, hout))
 
     def _layer_bwd(self, i, base):
         """dh holds dL/dh_{i+1} on entry (and dd its bf16 form, packed in

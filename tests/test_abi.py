@@ -411,3 +411,16 @@ def test_grouped_backward_argument_errors():
     q = [L.nf4s_tensor_layout(4096, 4096, 0)]
     q.append(L.nf4s_tensor_layout(1024, 4096, q[0].end))
     assert _err(bwd, FAKE, q, two, 512, FAKE, None, None, 0, FAKE, 1024) == L.EWORKSPACE
+
+
+def test_residual_forward_argument_errors():
+    d = L.nf4s_tensor_layout(64, 128, 0)
+    f = L.streamed_linear_fwd_residual
+    # only error paths: every call below is refused before any launch
+    assert _err(f, FAKE, d, FAKE, 16, FAKE, None, None, 0, 0.0, None, FAKE, None, 0) == L.EINVAL
+    assert _err(f, FAKE, d, FAKE, 16, FAKE, None, None, 0, 0.0, FAKE, FAKE + 4, None, 0) == L.EALIGN
+    assert _err(f, FAKE, d, FAKE + 16, 16, FAKE, None, None, 0, 0.0, FAKE, FAKE, None, 0) == L.EALIGN
+    assert _err(f, FAKE, d, FAKE, 16, FAKE, FAKE, None, 16, 2.0, FAKE, FAKE, None, 0) == L.EINVAL
+    assert _err(f, FAKE, d, FAKE, 0, FAKE, None, None, 0, 0.0, FAKE, FAKE, None, 0) == L.ESHAPE
+    o = L.nf4s_tensor_layout(4096, 4096, 0)
+    assert _err(f, FAKE, o, FAKE, 512, FAKE, None, None, 0, 0.0, FAKE, FAKE, FAKE, 64) == L.EWORKSPACE

@@ -560,3 +560,38 @@ def test_grouped_backward_8b_sampled(projs, ns, lora_on):
     total = sum(bits_to_f32(o).astype(np.float64) for o in singles)
     # the single calls round each term to bf16 before the sum
     assert np.max(np.abs(g - total)) <= 2.0 ** -6 * np.max(np.abs(total))
+
+
+@pytest.mark.parametrize("proj,n,k,M,lora,inplace", [
+    ("o", 4096, 4096, 512, True, False),    # split contraction: the sum writes both
+    ("down", 4096, 14336, 512, False, True),
+    ("o", 576, 576, 300, True, True),       # unsplit: a residual kernel follows
+    ("o", 72, 128, 37, False, False),       # ragged tiles, n not a multiple of 4 rows
+])
+def test_forward_into_residual_equals_forward_plus_residual_add(proj, n, k, M, lora, inplace):
+    print(f"residual fwd {proj} {n}x{k} M={M} lora={lora} inplace={inplace}", flush=True)
+    c = _setup(proj, n, k, M)
+    s = stream()
+    x = dev_bf16bits(c["x"])
+    xp = ws_tensor(L.nf4s_packed_activation_bytes(M, k))
+    L.nf4s_pack_activation(x.data_ptr(), M, k, xp.data_ptr(), xp.numel(), s)
+    A, B = dev_f32(c["a"]), dev_f32(c["b"])
+    u = torch.empty((M, R), dtype=torch.float32, device="cuda")
+    wsl = ws_tensor(L.nf4s_workspace_bytes(L.OP_LORA_FWD, M, n, k))
+    L.lora_fwd(x.data_ptr(), M, k, A.data_ptr(), R, u.data_ptr(), wsl.data_ptr(), wsl.numel(), s)
+    lu, lb, r, sc = (u.data_ptr(), B.data_ptr(), R, S) if lora else (None, None, 0, 0.0)
+    h = dev_f32(bits_to_f32(synth.activation((M, n), 3, 7)))
+    ws = ws_tensor(L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, M, n, k))
+    sp = c["shard"].data_ptr()
+    y1, y2 = (torch.empty((M, n), dtype=torch.int16, device="cuda") for _ in range(2))
+    ref = torch.empty_like(h)
+    L.streamed_linear_fwd_packed(sp, c["d"], xp.data_ptr(), M, y1.data_ptr(), lu, lb, r, sc, ws.data_ptr(),
+                                 ws.numel(), s)
+    L.nf4s_residual_add(h.data_ptr(), y1.data_ptr(), M * n, ref.data_ptr(), s)
+    out = h.clone() if inplace else torch.empty_like(h)
+    hin = out if inplace else h
+    L.streamed_linear_fwd_residual(sp, c["d"], xp.data_ptr(), M, y2.data_ptr(), lu, lb, r, sc,
+                                   hin.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(), s)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert torch.equal(ref.view(torch.int32), out.view(torch.int32))

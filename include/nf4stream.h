@@ -418,6 +418,8 @@ int nf4s_embed(const uint16_t* table, int64_t vocab, int64_t hidden, const int64
  * compute them but never store them); the columns past width up to the next
  * multiple of 64 are written as zeros.
  *
+ * (nf4s_attention_fwd writes o this way too, width = heads*head_dim.)
+ *
  * RMSNorm: rstd[t] = 1/sqrt(mean_j x[t,j]^2 + eps), y = bf16(x * rstd * w).
  * x fp32 [T, H]; w fp32 [H]; y bf16 [T, H] (and packed, see above); rstd fp32
  * [T] (kept for the backward); H a multiple of 8, x, w, y, dys and dh 16-byte
@@ -447,6 +449,10 @@ int nf4s_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float* x, const
  */
 int nf4s_rope(uint16_t* x, int64_t T, int64_t S, int heads, int head_dim, double theta, int inverse,
               void* stream);
+/* The same on queries q [T, q_heads*head_dim] and keys k [T, k_heads*head_dim]
+ * in one launch (each element as nf4s_rope rotates it). */
+int nf4s_rope_pair(uint16_t* q, int q_heads, uint16_t* k, int k_heads, int64_t T, int64_t S,
+                   int head_dim, double theta, int inverse, void* stream);
 
 /*
  * Causal softmax attention with grouped KV heads (head h reads KV head
@@ -467,7 +473,7 @@ int nf4s_rope(uint16_t* x, int64_t T, int64_t S, int heads, int head_dim, double
  */
 int nf4s_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
                        int64_t S, int heads, int kv_heads, int head_dim, uint16_t* o, float* o_f32,
-                       float* lse, void* stream);
+                       float* lse, void* packed, void* stream);
 int nf4s_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* o_f32,
                        const uint16_t* dout, const float* lse, int64_t B, int64_t S, int heads,
                        int kv_heads, int head_dim, uint16_t* dq, uint16_t* dk, uint16_t* dv,

@@ -37,6 +37,7 @@ EXPORTS = (
     "nf4s_grouped_workspace_bytes", "streamed_linear_fwd_grouped",
     "nf4s_lora_grouped_workspace_bytes", "lora_fwd_grouped", "lora_bwd_grouped",
     "nf4s_grouped_bwd_workspace_bytes", "streamed_linear_bwd_grouped", "streamed_linear_fwd_residual",
+    "nf4s_rope_pair",
     "nf4s_embed", "nf4s_rmsnorm_fwd", "nf4s_rmsnorm_bwd", "nf4s_rope", "nf4s_attention_fwd",
     "nf4s_attention_bwd", "nf4s_swiglu_fwd", "nf4s_swiglu_bwd", "nf4s_residual_add",
     "nf4s_to_bf16", "nf4s_cross_entropy", "nf4s_adamw", "nf4s_token_nll", "nf4s_dpo_loss",
@@ -112,6 +113,8 @@ _SIG = {
     "streamed_linear_fwd_grouped": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), ctypes.c_int, _P,
                                                    _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float,
                                                    _P, ctypes.c_size_t, _P]),
+    "nf4s_rope_pair": (ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int, _I64, _I64, ctypes.c_int,
+                                      ctypes.c_double, ctypes.c_int, _P]),
     "streamed_linear_fwd_residual": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P, _P,
                                                     ctypes.c_int, ctypes.c_float, _P, _P, _P,
                                                     ctypes.c_size_t, _P]),
@@ -135,7 +138,7 @@ _SIG = {
     "nf4s_rope": (ctypes.c_int, [_P, _I64, _I64, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                  ctypes.c_int, _P]),
     "nf4s_attention_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_int, ctypes.c_int,
-                                          ctypes.c_int, _P, _P, _P, _P]),
+                                          ctypes.c_int, _P, _P, _P, _P, _P]),
     "nf4s_attention_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int, _P, _P, _P, _P,
                                           ctypes.c_size_t, _P]),
@@ -326,12 +329,17 @@ def nf4s_rmsnorm_bwd(dys, x, w, rstd, T, H, accumulate, dh, stream=0, y=None, pa
     _check(lib().nf4s_rmsnorm_bwd(arr, len(dys), x, w, rstd, T, H, accumulate, dh, y, packed, stream))
 
 
+def nf4s_rope_pair(q, q_heads, k, k_heads, T, S, head_dim, theta, inverse, stream=0):
+    _check(lib().nf4s_rope_pair(q, q_heads, k, k_heads, T, S, head_dim, theta, inverse, stream))
+
+
 def nf4s_rope(x, T, S, heads, head_dim, theta, inverse, stream=0):
     _check(lib().nf4s_rope(x, T, S, heads, head_dim, theta, inverse, stream))
 
 
-def nf4s_attention_fwd(q, k, v, B, S, heads, kv_heads, head_dim, o, o_f32, lse, stream=0):
-    _check(lib().nf4s_attention_fwd(q, k, v, B, S, heads, kv_heads, head_dim, o, o_f32, lse, stream))
+def nf4s_attention_fwd(q, k, v, B, S, heads, kv_heads, head_dim, o, o_f32, lse, stream=0, packed=None):
+    _check(lib().nf4s_attention_fwd(q, k, v, B, S, heads, kv_heads, head_dim, o, o_f32, lse, packed,
+                                    stream))
 
 
 def nf4s_attention_bwd(q, k, v, o_f32, dout, lse, B, S, heads, kv_heads, head_dim, dq, dk, dv, ws,

@@ -787,6 +787,22 @@ int nf4s_rope(uint16_t* x, int64_t T, int64_t S, int heads, int head_dim, double
                   "rope launch");
 }
 
+int nf4s_rope_pair(uint16_t* q, int q_heads, uint16_t* k, int k_heads, int64_t T, int64_t S,
+                   int head_dim, double theta, int inverse, void* stream) {
+  int rc;
+  if ((rc = check_heads(q_heads, head_dim)) || (rc = check_heads(k_heads, head_dim))) return rc;
+  if (head_dim % 8) return fail(NF4S_ESHAPE, "head_dim=%d is not a multiple of 8", head_dim);
+  if (S <= 0 || T <= 0 || T % S) return fail(NF4S_ESHAPE, "rows=%lld must be a positive multiple of seq=%lld", (long long)T, (long long)S);
+  if ((rc = check_rows(T, (int64_t)q_heads * head_dim)) || (rc = check_rows(T, (int64_t)k_heads * head_dim)))
+    return rc;
+  if (!(theta > 1.0) || !std::isfinite(theta)) return fail(NF4S_EINVAL, "theta must be finite and > 1");
+  if (inverse != 0 && inverse != 1) return fail(NF4S_EINVAL, "inverse must be 0 or 1");
+  if ((rc = check_ptr(q, "q", 8)) || (rc = check_ptr(k, "k", 8))) return rc;
+  return launched(launch_rope_pair(q, q_heads, k, k_heads, T, S, head_dim, theta, inverse,
+                                   static_cast<hipStream_t>(stream)),
+                  "rope launch");
+}
+
 static int check_attention(int64_t B, int64_t S, int heads, int kv_heads, int head_dim) {
   int rc;
   if ((rc = check_heads(heads, head_dim))) return rc;
@@ -803,15 +819,16 @@ static int check_attention(int64_t B, int64_t S, int heads, int kv_heads, int he
 
 int nf4s_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
                        int64_t S, int heads, int kv_heads, int head_dim, uint16_t* o, float* o_f32,
-                       float* lse, void* stream) {
+                       float* lse, void* packed, void* stream) {
   int rc;
   if ((rc = check_attention(B, S, heads, kv_heads, head_dim))) return rc;
+  if (packed && (rc = check_packed_out(packed, B * S, (int64_t)heads * head_dim))) return rc;
   // the kernels move 16-byte fragments of q, k, v and store o / o_f32 in 8- and 16-byte pieces
   if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
       (rc = check_ptr(o, "o")) || (rc = check_ptr(lse, "lse", 4)))
     return rc;
   if (o_f32 && (rc = check_ptr(o_f32, "o_f32"))) return rc;
-  return launched(launch_attention_fwd(q, k, v, B, S, heads, kv_heads, head_dim, o, o_f32, lse,
+  return launched(launch_attention_fwd(q, k, v, B, S, heads, kv_heads, head_dim, o, o_f32, lse, packed,
                                        static_cast<hipStream_t>(stream)),
                   "attention_fwd launch");
 }

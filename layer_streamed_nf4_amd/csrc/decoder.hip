@@ -200,12 +200,23 @@ struct InvFreq {
   double f[128];
 };
 
-__global__ __launch_bounds__(256) void k_rope(uint16_t* __restrict__ x, int64_t T, int64_t S,
-                                              int heads, int d, InvFreq inv, int inverse) {
+// Two tensors per launch (queries and keys): threads past the first
+// tensor's n rotate the second (heads2 heads; none when x2 is null).
+__global__ __launch_bounds__(256) void k_rope(uint16_t* __restrict__ x1, int heads1,
+                                              uint16_t* __restrict__ x2, int heads2, int64_t T,
+                                              int64_t S, int d, InvFreq inv, int inverse) {
   const int half = d / 2, q4 = half / 4;
+  const int64_t n1 = T * heads1 * q4;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint16_t* x = x1;
+  int heads = heads1;
+  if (i >= n1) {
+    i -= n1;
+    x = x2;
+    heads = heads2;
+  }
   const int64_t n = T * heads * q4;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
+  if (x == nullptr || i >= n) return;
   const int j0 = 4 * (int)(i % q4);
   const int64_t th = i / q4;  // (row, head)
   const int64_t pos = (th / heads) % S;
@@ -402,7 +413,8 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_fwd(const uint16_t* __restr
                                                          const uint16_t* __restrict__ v, int64_t S,
                                                          int H, int Hkv, uint16_t* __restrict__ o,
                                                          float* __restrict__ o_f32,
-                                                         float* __restrict__ lse) {
+                                                         float* __restrict__ lse,
+                                                         uint8_t* __restrict__ packed) {
   constexpr int KS = D / 16, DT = D / 32, WS = RM_ELEMS(D) + TR_ELEMS(D);
   __shared__ __attribute__((aligned(16))) uint16_t smem[AW * WS];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, hf = lane >> 5, c = lane & 31;
@@ -518,7 +530,15 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_fwd(const uint16_t* __restr
     wv.y = pack_bf16x2(fo.z, fo.w);
     *reinterpret_cast<uint2*>(o + idx) = wv;
     if (o_f32 != nullptr) *reinterpret_cast<float4*>(o_f32 + idx) = fo;
+    // the o projection's input in fragment order: the two half-waves write
+    // the two 8-byte halves of a row's 16-byte chunk, the 32 rows of a query
+    // block 512 consecutive bytes
+    if (packed != nullptr)
+      *reinterpret_cast<uint2*>(packed + frag_offset(qrow, (int64_t)h * D + d0, (ldq + 63) / 64 * 4) +
+                                8 * hf) = wv;
   }
+  if (packed != nullptr && ldq % 64 != 0 && h == H - 1 && j == 0 && hf == 0)
+    frag_zero_tail(packed, qrow, ldq, (ldq + 63) / 64 * 4);
   if (j == 0 && hf == 0) lse[(b * H + h) * S + qpos] = mx + logf(ltot);
 }
 
@@ -1147,10 +1167,16 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float*
 
 hipError_t launch_rope(uint16_t* x, int64_t T, int64_t S, int heads, int d, double theta,
                        int inverse, hipStream_t s) {
+  return launch_rope_pair(x, heads, nullptr, 0, T, S, d, theta, inverse, s);
+}
+
+hipError_t launch_rope_pair(uint16_t* x1, int heads1, uint16_t* x2, int heads2, int64_t T, int64_t S,
+                            int d, double theta, int inverse, hipStream_t s) {
   InvFreq inv;
   for (int j = 0; j < 128; ++j) inv.f[j] = j < d / 2 ? pow(theta, -2.0 * j / d) : 0.0;
-  hipLaunchKernelGGL(k_rope, dim3(grid_of(T * heads * (d / 8))), dim3(256), 0, s, x, T, S, heads, d,
-                     inv, inverse);
+  const int64_t n = T * (heads1 + (x2 ? heads2 : 0)) * (d / 8);
+  hipLaunchKernelGGL(k_rope, dim3(grid_of(n)), dim3(256), 0, s, x1, heads1, x2, heads2, T, S, d, inv,
+                     inverse);
   return hipGetLastError();
 }
 
@@ -1164,9 +1190,10 @@ hipError_t launch_rope(uint16_t* x, int64_t T, int64_t S, int heads, int d, doub
 
 hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
                                 int64_t S, int H, int Hkv, int D, uint16_t* o, float* o_f32,
-                                float* lse, hipStream_t s) {
+                                float* lse, void* packed, hipStream_t s) {
   const unsigned grid = (unsigned)(B * H * ((S + AB - 1) / AB));
-#define CALL(DD) hipLaunchKernelGGL(k_attn_fwd<DD>, dim3(grid), dim3(64 * AW), 0, s, q, k, v, S, H, Hkv, o, o_f32, lse)
+  uint8_t* const pk = static_cast<uint8_t*>(packed);
+#define CALL(DD) hipLaunchKernelGGL(k_attn_fwd<DD>, dim3(grid), dim3(64 * AW), 0, s, q, k, v, S, H, Hkv, o, o_f32, lse, pk)
   NF4S_DISPATCH_D(D, CALL)
 #undef CALL
   return hipGetLastError();

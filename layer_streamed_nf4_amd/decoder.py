@@ -36,7 +36,7 @@ from . import (OP_ATTENTION_BWD, OP_CROSS_ENTROPY, OP_DENSE_BWD_PACKED, OP_DENSE
                nf4s_pack_activation, nf4s_packed_activation_bytes, nf4s_pool_acquire,
                nf4s_pool_create, nf4s_pool_destroy, nf4s_pool_prefetch, nf4s_pool_release,
                nf4s_pool_set_layer, nf4s_pool_stats, nf4s_rmsnorm_bwd,
-               nf4s_rmsnorm_fwd, nf4s_rope, nf4s_swiglu_bwd, nf4s_swiglu_fwd,
+               nf4s_rmsnorm_fwd, nf4s_rope_pair, nf4s_swiglu_bwd, nf4s_swiglu_fwd,
                nf4s_workspace_bytes, streamed_linear_bwd_packed, streamed_linear_fwd_packed,
                streamed_linear_fwd_grouped, grouped_workspace_bytes, grouped_bwd_workspace_bytes,
                streamed_linear_bwd_grouped, streamed_linear_fwd_residual)
@@ -374,11 +374,12 @@ class Decoder:
         nf4s_rmsnorm_fwd(hin.data_ptr(), self.norms["attn"][i].data_ptr(), M, H, c["eps"],
                          self.n1.data_ptr(), self.rstd1.data_ptr(), s, packed=self._produced(self.n1, H))
         self._fwd(base, i, ("q", "k", "v"), self.n1, (self.q, self.k, self.vv), a)
-        nf4s_rope(self.q.data_ptr(), M, self.S, c["heads"], c["head_dim"], c["rope_theta"], 0, s)
-        nf4s_rope(self.k.data_ptr(), M, self.S, c["kv_heads"], c["head_dim"], c["rope_theta"], 0, s)
+        nf4s_rope_pair(self.q.data_ptr(), c["heads"], self.k.data_ptr(), c["kv_heads"], M, self.S,
+                       c["head_dim"], c["rope_theta"], 0, s)
         nf4s_attention_fwd(self.q.data_ptr(), self.k.data_ptr(), self.vv.data_ptr(), self.B, self.S,
                            c["heads"], c["kv_heads"], c["head_dim"], self.o.data_ptr(),
-                           self.o32.data_ptr() if recompute or keep else None, self.lse.data_ptr(), s)
+                           self.o32.data_ptr() if recompute or keep else None, self.lse.data_ptr(), s,
+                           packed=self._produced(self.o, c["heads"] * c["head_dim"]))
         self._fwd(base, i, ("o",), self.o, (self.ao,), a, res=(hin, self.h_mid))
         nf4s_rmsnorm_fwd(self.h_mid.data_ptr(), self.norms["mlp"][i].data_ptr(), M, H, c["eps"],
                          self.n2.data_ptr(), self.rstd2.data_ptr(), s, packed=self._produced(self.n2, H))
@@ -418,8 +419,8 @@ class Decoder:
                            self.o32.data_ptr(), self.do.data_ptr(), self.lse.data_ptr(), self.B,
                            self.S, c["heads"], c["kv_heads"], c["head_dim"], self.dq.data_ptr(),
                            self.dk.data_ptr(), self.dv.data_ptr(), *self._ws(), s)
-        nf4s_rope(self.dq.data_ptr(), M, self.S, c["heads"], c["head_dim"], c["rope_theta"], 1, s)
-        nf4s_rope(self.dk.data_ptr(), M, self.S, c["kv_heads"], c["head_dim"], c["rope_theta"], 1, s)
+        nf4s_rope_pair(self.dq.data_ptr(), c["heads"], self.dk.data_ptr(), c["kv_heads"], M, self.S,
+                       c["head_dim"], c["rope_theta"], 1, s)
         dn = self._bwd(base, i, ("q", "k", "v"), self.n1, (self.dq, self.dk, self.dv), self.dnx)
         nf4s_rmsnorm_bwd([x.data_ptr() for x in dn], self.h[i].data_ptr(),
                          self.norms["attn"][i].data_ptr(), self.rstd1.data_ptr(), M, H, 1,

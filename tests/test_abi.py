@@ -424,3 +424,13 @@ def test_residual_forward_argument_errors():
     assert _err(f, FAKE, d, FAKE, 0, FAKE, None, None, 0, 0.0, FAKE, FAKE, None, 0) == L.ESHAPE
     o = L.nf4s_tensor_layout(4096, 4096, 0)
     assert _err(f, FAKE, o, FAKE, 512, FAKE, None, None, 0, 0.0, FAKE, FAKE, FAKE, 64) == L.EWORKSPACE
+
+
+def test_rope_pair_argument_errors():
+    f = L.nf4s_rope_pair
+    assert _err(f, FAKE, 4, FAKE, 2, 8, 4, 32, 1.0, 0) == L.EINVAL        # theta
+    assert _err(f, FAKE, 4, FAKE, 2, 8, 3, 32, 1e4, 0) == L.ESHAPE        # rows % seq
+    assert _err(f, FAKE, 4, FAKE, 0, 8, 4, 32, 1e4, 0) == L.ESHAPE        # heads
+    assert _err(f, FAKE, 4, FAKE + 2, 2, 8, 4, 32, 1e4, 0) == L.EALIGN
+    assert _err(f, FAKE, 4, None, 2, 8, 4, 32, 1e4, 0) == L.EINVAL
+    assert _err(f, FAKE, 4, FAKE, 2, 8, 4, 32, 1e4, 2) == L.EINVAL        # inverse

@@ -111,6 +111,23 @@ def test_rope_and_inverse(B, S, heads, d, theta):
     _check_bf16(host_u16(xd), ref_inv, abs_slack=1e-6, what="rope inverse")
 
 
+@pytest.mark.parametrize("S,hq,hk,d", [(70, 4, 2, 32), (512, 32, 8, 128), (7, 9, 3, 64)])
+@pytest.mark.parametrize("inverse", [0, 1])
+def test_rope_pair_equals_two_single_calls(S, hq, hk, d, inverse):
+    """Queries and keys in one launch: the bits of one nf4s_rope per tensor."""
+    require_gpu()
+    g = _rng(30 + d)
+    T = 2 * S
+    q, k = _bits(g.standard_normal((T, hq * d))), _bits(g.standard_normal((T, hk * d)))
+    q1, k1, q2, k2 = dev_bf16bits(q), dev_bf16bits(k), dev_bf16bits(q), dev_bf16bits(k)
+    s = stream()
+    L.nf4s_rope_pair(q1.data_ptr(), hq, k1.data_ptr(), hk, T, S, d, 10000.0, inverse, s)
+    L.nf4s_rope(q2.data_ptr(), T, S, hq, d, 10000.0, inverse, s)
+    L.nf4s_rope(k2.data_ptr(), T, S, hk, d, 10000.0, inverse, s)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(k1, k2)
+
+
 ATTN_CASES = [
     (2, 70, 4, 2, 32),     # ragged sequence over three 32-row blocks, groups of 2
     (1, 512, 9, 3, 64),    # SmolLM2-135M attention at S512
@@ -176,7 +193,7 @@ def test_swiglu_fwd_bwd(T, W):
     _check_bf16(host_u16(du), D.bf16(ru), abs_slack=1e-6, what="du")
 
 
-@pytest.mark.parametrize("T,W", [(37, 72), (300, 576), (512, 1536), (33, 4104)])
+@pytest.mark.parametrize("T,W", [(37, 72), (300, 576), (512, 1536), (33, 4104), (70, 96)])
 def test_producers_write_the_packed_layout(T, W):
     """RMSNorm, SwiGLU (both directions) and the fp32 -> bf16 rounding write
     their bf16 result a second time in MFMA fragment order: equal, byte for
@@ -224,6 +241,17 @@ def test_producers_write_the_packed_layout(T, W):
     pk = sentinel()
     L.nf4s_to_bf16(x.data_ptr(), T, W, y.data_ptr(), s, packed=pk.data_ptr())
     packed_rows_equal(y, pk)
+    # attention's output o [T, heads*d] with T = 1 sequence of T positions
+    for hd in (32, 64, 128):
+        if W % hd == 0 and W // hd <= 64:
+            nh = W // hd
+            qa, ka, va = (dev_bf16bits(_bits(g.standard_normal((T, W)))) for _ in range(3))
+            lse = torch.empty(nh * T, dtype=torch.float32, device="cuda")
+            pk = sentinel()
+            L.nf4s_attention_fwd(qa.data_ptr(), ka.data_ptr(), va.data_ptr(), 1, T, nh, nh, hd, y.data_ptr(),
+                                 None, lse.data_ptr(), s, packed=pk.data_ptr())
+            packed_rows_equal(y, pk)
+            break
     # the norm backward's bf16 copy of its result: the bits nf4s_to_bf16 gives
     # for that fp32 result, row-major and packed (accumulating into dh)
     dh = dev_f32(g.standard_normal((T, W)).astype(np.float32))

@@ -280,21 +280,6 @@ int streamed_linear_fwd_residual(const void* shard_dev, const nf4s_tensor_desc* 
                                  const void* x_packed, int64_t M, uint16_t* y, const float* lora_u,
                                  const float* lora_B, int r, float scale, const float* h_in,
                                  float* h_out, void* ws, size_t ws_bytes, void* stream);
-/*
- * The same, followed by the RMSNorm of h_out (the o projection and the MLP's
- * norm of a llama layer): norm_y, rstd (and norm_packed, nullable) as
- * nf4s_rmsnorm_fwd(h_out, norm_w, M, n_out, eps, ...) writes them, bit for
- * bit. With a split contraction one pass over the partials does the sum, the
- * residual and the norm; otherwise the residual and norm kernels follow the
- * GEMM. Errors: as streamed_linear_fwd_residual, and those of
- * nf4s_rmsnorm_fwd for the norm's arguments (n_out a multiple of 8).
- */
-int streamed_linear_fwd_residual_norm(const void* shard_dev, const nf4s_tensor_desc* d,
-                                      const void* x_packed, int64_t M, uint16_t* y,
-                                      const float* lora_u, const float* lora_B, int r, float scale,
-                                      const float* h_in, float* h_out, const float* norm_w, float eps,
-                                      uint16_t* norm_y, float* rstd, void* norm_packed, void* ws,
-                                      size_t ws_bytes, void* stream);
 int streamed_linear_fwd_grouped(const void* shard_dev, const nf4s_tensor_desc* descs, int n,
                                 const void* x_packed, int64_t M, uint16_t* const* ys,
                                 const float* const* lora_us, const float* const* lora_Bs, int r,

@@ -37,7 +37,7 @@ EXPORTS = (
     "nf4s_grouped_workspace_bytes", "streamed_linear_fwd_grouped",
     "nf4s_lora_grouped_workspace_bytes", "lora_fwd_grouped", "lora_bwd_grouped",
     "nf4s_grouped_bwd_workspace_bytes", "streamed_linear_bwd_grouped", "streamed_linear_fwd_residual",
-    "nf4s_rope_pair", "streamed_linear_fwd_residual_norm",
+    "nf4s_rope_pair",
     "nf4s_embed", "nf4s_rmsnorm_fwd", "nf4s_rmsnorm_bwd", "nf4s_rope", "nf4s_attention_fwd",
     "nf4s_attention_bwd", "nf4s_swiglu_fwd", "nf4s_swiglu_bwd", "nf4s_residual_add",
     "nf4s_to_bf16", "nf4s_cross_entropy", "nf4s_adamw", "nf4s_token_nll", "nf4s_dpo_loss",
@@ -115,10 +115,6 @@ _SIG = {
                                                    _P, ctypes.c_size_t, _P]),
     "nf4s_rope_pair": (ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int, _I64, _I64, ctypes.c_int,
                                       ctypes.c_double, ctypes.c_int, _P]),
-    "streamed_linear_fwd_residual_norm": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P,
-                                                         _P, ctypes.c_int, ctypes.c_float, _P, _P, _P,
-                                                         ctypes.c_float, _P, _P, _P, _P,
-                                                         ctypes.c_size_t, _P]),
     "streamed_linear_fwd_residual": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P, _P,
                                                     ctypes.c_int, ctypes.c_float, _P, _P, _P,
                                                     ctypes.c_size_t, _P]),
@@ -285,14 +281,6 @@ def streamed_linear_fwd_residual(shard, desc, x_packed, M, y, lora_u, lora_B, r,
     """y = the forward of desc on x_packed (bf16) and h_out = h_in + y (fp32)."""
     _check(lib().streamed_linear_fwd_residual(shard, ctypes.byref(desc), x_packed, M, y, lora_u, lora_B,
                                               r, scale, h_in, h_out, ws, ws_bytes, stream))
-
-
-def streamed_linear_fwd_residual_norm(shard, desc, x_packed, M, y, lora_u, lora_B, r, scale, h_in, h_out,
-                                      norm_w, eps, norm_y, rstd, ws, ws_bytes, stream=0, norm_packed=None):
-    """streamed_linear_fwd_residual, then the RMSNorm of h_out into norm_y / rstd (/ norm_packed)."""
-    _check(lib().streamed_linear_fwd_residual_norm(shard, ctypes.byref(desc), x_packed, M, y, lora_u,
-                                                   lora_B, r, scale, h_in, h_out, norm_w, eps, norm_y,
-                                                   rstd, norm_packed, ws, ws_bytes, stream))
 
 
 def grouped_bwd_workspace_bytes(n_outs, k_in, M):

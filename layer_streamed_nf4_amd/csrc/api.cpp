@@ -365,35 +365,6 @@ int streamed_linear_fwd_residual(const void* shard_dev, const nf4s_tensor_desc* 
   return e == hipSuccess ? NF4S_OK : hip_fail(e, "linear launch");
 }
 
-static int check_norm_width(int64_t H);
-static int check_packed_out(const void* packed, int64_t T, int64_t W);
-
-int streamed_linear_fwd_residual_norm(const void* shard_dev, const nf4s_tensor_desc* d,
-                                      const void* x_packed, int64_t M, uint16_t* y,
-                                      const float* lora_u, const float* lora_B, int r, float scale,
-                                      const float* h_in, float* h_out, const float* norm_w, float eps,
-                                      uint16_t* norm_y, float* rstd, void* norm_packed, void* ws,
-                                      size_t ws_bytes, void* stream) {
-  int rc;
-  GemmPlan p;
-  if ((rc = linear_checks(false, shard_dev, d, M, y, lora_u, lora_B, r, scale, &p))) return rc;
-  if ((rc = check_ptr(x_packed, "x_packed", 256))) return rc;
-  if ((rc = check_ptr(h_in, "h_in")) || (rc = check_ptr(h_out, "h_out"))) return rc;
-  if ((rc = check_norm_width(d->n_out))) return rc;
-  if ((rc = check_ptr(norm_w, "norm_w")) || (rc = check_ptr(norm_y, "norm_y")) ||
-      (rc = check_ptr(rstd, "rstd", 4)))
-    return rc;
-  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(NF4S_EINVAL, "eps must be finite and >= 0");
-  if (norm_packed && (rc = check_packed_out(norm_packed, M, d->n_out))) return rc;
-  if (p.part_bytes && (rc = check_ws(ws, ws_bytes, p.part_bytes))) return rc;
-  const NormOut nrm{norm_w, eps, norm_y, rstd, norm_packed};
-  hipError_t e = launch_linear_fwd_residual_norm(resolve(shard_dev, d), d->n_out, d->k_in,
-                                                 static_cast<const uint8_t*>(x_packed), M, y, lora_u,
-                                                 lora_B, lora_u ? r : 0, scale, h_in, h_out, nrm, ws,
-                                                 static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? NF4S_OK : hip_fail(e, "linear launch");
-}
-
 int streamed_linear_bwd_packed(const void* shard_dev, const nf4s_tensor_desc* d,
                                const void* dy_packed, int64_t M, uint16_t* dx,
                                const float* lora_du, const float* lora_A, int r, void* ws,

@@ -81,19 +81,6 @@ hipError_t launch_linear_fwd_residual(const QPtrs& q, int64_t n_out, int64_t k_i
                                       const uint8_t* x_packed, int64_t M, uint16_t* y,
                                       const float* lora_u, const float* lora_B, int r, float scale,
                                       const float* h_in, float* h_out, void* part_ws, hipStream_t s);
-// ... and then the RMSNorm of h_out (weight w, eps) into ny / rstd / packed
-struct NormOut {
-  const float* w;
-  float eps;
-  uint16_t* y;
-  float* rstd;
-  void* packed;
-};
-hipError_t launch_linear_fwd_residual_norm(const QPtrs& q, int64_t n_out, int64_t k_in,
-                                           const uint8_t* x_packed, int64_t M, uint16_t* y,
-                                           const float* lora_u, const float* lora_B, int r,
-                                           float scale, const float* h_in, float* h_out,
-                                           const NormOut& nrm, void* part_ws, hipStream_t s);
 // Forward of nseg (<= GEMM_MAX_SEG) NF4 linears reading the same packed
 // activation, in one launch (lora_us / lora_Bs entries may be null).
 hipError_t launch_linear_grouped_fwd(const QPtrs* q, int nseg, const int64_t* n_outs, int64_t k_in,
@@ -178,12 +165,6 @@ hipError_t launch_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t T, in
 hipError_t launch_swiglu_bwd(const uint16_t* ds, const uint16_t* g, const uint16_t* u, int64_t T,
                              int64_t W, uint16_t* dg, uint16_t* du, void* dg_packed,
                              void* du_packed, hipStream_t s);
-// split partials [splits, M, H] -> y, h_out = h_in + y, and the RMSNorm of
-// h_out (ny, rstd, packed nullable), in one pass (one workgroup per row)
-hipError_t launch_sum_residual_norm(const float* part, int splits, int64_t M, int64_t H,
-                                   const float* h_in, uint16_t* y, float* h_out, const float* w,
-                                   float eps, uint16_t* ny, float* rstd, void* packed,
-                                   hipStream_t s);
 hipError_t launch_residual_add(const float* h, const uint16_t* y, int64_t n, float* out,
                                hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* x, int64_t T, int64_t W, uint16_t* y, void* packed,

@@ -128,70 +128,6 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const float* __restrict__ x
   }
 }
 
-// One row per workgroup: the split sum of a projection's fp32 partials into
-// the residual stream, y = bf16(sum over splits in order), h_out = h_in + y,
-// followed by the RMSNorm of h_out (n = bf16(h_out * rstd * w), packed
-// optionally). Each thread takes the row's 8-wide chunks t, t + 256, ... as
-// k_rmsnorm_fwd does and adds the splits in the order k_split_sum does, so
-// every output has the bits of the three separate kernels.
-__global__ __launch_bounds__(256) void k_sum_residual_norm(const float* __restrict__ part, int splits,
-                                                           int64_t H, const float* __restrict__ h_in,
-                                                           uint16_t* __restrict__ y,
-                                                           float* __restrict__ h_out,
-                                                           const float* __restrict__ w, float eps,
-                                                           uint16_t* __restrict__ ny,
-                                                           float* __restrict__ rstd,
-                                                           uint8_t* __restrict__ packed) {
-  __shared__ float red[4];
-  const int64_t t = blockIdx.x;
-  const int64_t n = (int64_t)gridDim.x * H;  // elements of one split's partial
-  const int nc = (int)(H / 8);
-  float ss = 0.0f;
-  for (int c = threadIdx.x; c < nc; c += 256) {
-    const int64_t i = t * H + 8 * c;
-    float s[8], hv[8];
-    load8_f32(part + i, s);
-    for (int p = 1; p < splits; ++p) {
-      float v[8];
-      load8_f32(part + (int64_t)p * n + i, v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s[e] += v[e];
-    }
-    u32x4v o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(s[2 * q], s[2 * q + 1]);
-    *reinterpret_cast<u32x4v*>(y + i) = o;
-    load8_f32(h_in + i, hv);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      hv[2 * q] += __uint_as_float(o[q] << 16);
-      hv[2 * q + 1] += __uint_as_float(o[q] & 0xFFFF0000u);
-    }
-    store8_f32(h_out + i, hv);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss += hv[e] * hv[e];
-  }
-  ss = block_sum(ss, red);
-  const float r = 1.0f / sqrtf(ss / (float)H + eps);
-  if (threadIdx.x == 0) rstd[t] = r;
-  for (int c = threadIdx.x; c < nc; c += 256) {
-    float f[8], g[8];
-    load8_f32(h_out + t * H + 8 * c, f);
-    load8_f32(w + 8 * c, g);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = f[e] * r * g[e];
-    u32x4v o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
-    *reinterpret_cast<u32x4v*>(ny + t * H + 8 * c) = o;
-    if (packed) {
-      const int64_t kb = (H + 63) / 64 * 4;
-      *reinterpret_cast<u32x4v*>(packed + frag_offset(t, 8 * c, kb)) = o;
-      if (c == nc - 1) frag_zero_tail(packed, t, H, kb);
-    }
-  }
-}
-
 // dh (+)= rstd * g - x * rstd^3 * mean(g * x), g = w * (sum of the n bf16 inputs)
 struct DyPtrs {
   const uint16_t* p[3];
@@ -1308,15 +1244,6 @@ hipError_t launch_swiglu_bwd(const uint16_t* ds, const uint16_t* g, const uint16
                              void* du_packed, hipStream_t s) {
   hipLaunchKernelGGL(k_swiglu_bwd, ew_grid(T, W), dim3(256), 0, s, ds, g, u, T, W, dg, du,
                      static_cast<uint8_t*>(dg_packed), static_cast<uint8_t*>(du_packed));
-  return hipGetLastError();
-}
-
-hipError_t launch_sum_residual_norm(const float* part, int splits, int64_t M, int64_t H,
-                                   const float* h_in, uint16_t* y, float* h_out, const float* w,
-                                   float eps, uint16_t* ny, float* rstd, void* packed,
-                                   hipStream_t s) {
-  hipLaunchKernelGGL(k_sum_residual_norm, dim3((unsigned)M), dim3(256), 0, s, part, splits, H, h_in, y,
-                     h_out, w, eps, ny, rstd, static_cast<uint8_t*>(packed));
   return hipGetLastError();
 }
 

@@ -1270,7 +1270,7 @@ static hipError_t launch_gemm(bool backward, const QPtrs* q, int nseg, const uin
                               int64_t M, uint16_t* const* outs, const float* const* lora_ls,
                               const float* const* lora_rs, int r, float scale, void* part_ws,
                               hipStream_t s, const float* res_in = nullptr,
-                              float* res_out = nullptr, const NormOut* nrm = nullptr) {
+                              float* res_out = nullptr) {
   GemmArgs g = {};
   g.wd = wd;
   g.M = M;
@@ -1344,15 +1344,8 @@ static hipError_t launch_gemm(bool backward, const QPtrs* q, int nseg, const uin
 #undef NF4S_GEMM
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.splits == 1) {  // the residual (and norm) from the bf16 output, as kernels of their own
-    if (!res_out) return hipSuccess;
-    e = launch_residual_add(res_in, outs[0], M * n_outs[0], res_out, s);
-    if (e != hipSuccess || !nrm) return e;
-    return launch_rmsnorm_fwd(res_out, nrm->w, M, n_outs[0], nrm->eps, nrm->y, nrm->rstd, nrm->packed, s);
-  }
-  if (nrm)  // one pass over the partials: sum, residual and the norm
-    return launch_sum_residual_norm(sum.part[0], p.splits, M, n_outs[0], res_in, outs[0], res_out,
-                                    nrm->w, nrm->eps, nrm->y, nrm->rstd, nrm->packed, s);
+  if (p.splits == 1)  // the residual from the bf16 output, as a kernel of its own
+    return res_out ? launch_residual_add(res_in, outs[0], M * n_outs[0], res_out, s) : hipSuccess;
   const dim3 g2((unsigned)((max_n / 4 + 1 + 255) / 256), (unsigned)nseg);
   hipLaunchKernelGGL(k_split_sum, g2, dim3(256), 0, s, sum, p.splits);
   return hipGetLastError();
@@ -1372,15 +1365,6 @@ hipError_t launch_linear_fwd_residual(const QPtrs& q, int64_t n_out, int64_t k_i
                                       const float* h_in, float* h_out, void* part_ws, hipStream_t s) {
   return launch_gemm(false, &q, 1, nullptr, &n_out, k_in, x_packed, M, &y, &lora_u, &lora_B, r, scale,
                      part_ws, s, h_in, h_out);
-}
-
-hipError_t launch_linear_fwd_residual_norm(const QPtrs& q, int64_t n_out, int64_t k_in,
-                                           const uint8_t* x_packed, int64_t M, uint16_t* y,
-                                           const float* lora_u, const float* lora_B, int r,
-                                           float scale, const float* h_in, float* h_out,
-                                           const NormOut& nrm, void* part_ws, hipStream_t s) {
-  return launch_gemm(false, &q, 1, nullptr, &n_out, k_in, x_packed, M, &y, &lora_u, &lora_B, r, scale,
-                     part_ws, s, h_in, h_out, &nrm);
 }
 
 hipError_t launch_linear_grouped_fwd(const QPtrs* q, int nseg, const int64_t* n_outs, int64_t k_in,

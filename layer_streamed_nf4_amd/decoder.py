@@ -39,8 +39,7 @@ from . import (OP_ATTENTION_BWD, OP_CROSS_ENTROPY, OP_DENSE_BWD_PACKED, OP_DENSE
                nf4s_rmsnorm_fwd, nf4s_rope_pair, nf4s_swiglu_bwd, nf4s_swiglu_fwd,
                nf4s_workspace_bytes, streamed_linear_bwd_packed, streamed_linear_fwd_packed,
                streamed_linear_fwd_grouped, grouped_workspace_bytes, grouped_bwd_workspace_bytes,
-               streamed_linear_bwd_grouped, streamed_linear_fwd_residual,
-               streamed_linear_fwd_residual_norm)
+               streamed_linear_bwd_grouped, streamed_linear_fwd_residual)
 from .stack import ALIGN, PROJ, ShardSet, _round_up
 
 # projections that read the same input: q, k, v the normed h; gate, up the
@@ -245,7 +244,7 @@ class Decoder:
         self._packed_key = (a.data_ptr(), K)
         return self.packed.data_ptr()
 
-    def _fwd(self, base, i, ps, x, ys, adapters=True, res=None, norm=None):
+    def _fwd(self, base, i, ps, x, ys, adapters=True, res=None):
         """Forward of the projections ps, all reading x (q, k, v or gate, up,
         or a single one), as one GEMM launch writing ys; each launch the
         time_calls predicate accepts is one timed entry with n_out the sum."""
@@ -257,13 +256,7 @@ class Decoder:
         r = self.r if any(us) else 0
         scale = self.scale if any(us) else 0.0
         ev = self._tick("fwd", sum(self.sh.shapes[p][0] for p in ps), ki)
-        if res is not None and norm is not None:  # ... and the RMSNorm of h_out: (w, y, rstd, packed)
-            assert len(ps) == 1
-            streamed_linear_fwd_residual_norm(
-                base, self.sh.layout.descs[ps[0]], xp, self.M, ys[0].data_ptr(), us[0], Bs[0], r, scale,
-                res[0].data_ptr(), res[1].data_ptr(), norm[0].data_ptr(), self.cfg["eps"],
-                norm[1].data_ptr(), norm[2].data_ptr(), *self._ws(), self._s, norm_packed=norm[3])
-        elif res is not None:  # a single projection into the residual stream: res = (h_in, h_out)
+        if res is not None:  # a single projection into the residual stream: res = (h_in, h_out)
             assert len(ps) == 1
             streamed_linear_fwd_residual(base, self.sh.layout.descs[ps[0]], xp, self.M, ys[0].data_ptr(),
                                          us[0], Bs[0], r, scale, res[0].data_ptr(), res[1].data_ptr(),
@@ -387,8 +380,9 @@ class Decoder:
                            c["heads"], c["kv_heads"], c["head_dim"], self.o.data_ptr(),
                            self.o32.data_ptr() if recompute or keep else None, self.lse.data_ptr(), s,
                            packed=self._produced(self.o, c["heads"] * c["head_dim"]))
-        self._fwd(base, i, ("o",), self.o, (self.ao,), a, res=(hin, self.h_mid),
-                  norm=(self.norms["mlp"][i], self.n2, self.rstd2, self._produced(self.n2, H)))
+        self._fwd(base, i, ("o",), self.o, (self.ao,), a, res=(hin, self.h_mid))
+        nf4s_rmsnorm_fwd(self.h_mid.data_ptr(), self.norms["mlp"][i].data_ptr(), M, H, c["eps"],
+                         self.n2.data_ptr(), self.rstd2.data_ptr(), s, packed=self._produced(self.n2, H))
         self._fwd(base, i, ("gate", "up"), self.n2, (self.g, self.u_), a)
         if recompute:
             # h_{i+1} is stored and the backward reads no output of the down

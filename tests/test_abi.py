@@ -434,23 +434,3 @@ def test_rope_pair_argument_errors():
     assert _err(f, FAKE, 4, FAKE + 2, 2, 8, 4, 32, 1e4, 0) == L.EALIGN
     assert _err(f, FAKE, 4, None, 2, 8, 4, 32, 1e4, 0) == L.EINVAL
     assert _err(f, FAKE, 4, FAKE, 2, 8, 4, 32, 1e4, 2) == L.EINVAL        # inverse
-
-
-def test_residual_norm_forward_argument_errors():
-    d = L.nf4s_tensor_layout(64, 128, 0)
-    f = L.streamed_linear_fwd_residual_norm
-    # only error paths: every call below is refused before any launch
-    ok = [FAKE, d, FAKE, 16, FAKE, None, None, 0, 0.0, FAKE, FAKE, FAKE, 1e-5, FAKE, FAKE, None, 0]
-    def call(**kw):
-        a = list(ok)
-        for i, v in kw.items():
-            a[int(i[1:])] = v
-        return _err(f, *a)
-    assert call(a11=None) == L.EINVAL                    # norm weight
-    assert call(a13=FAKE + 2) == L.EALIGN                # norm output
-    assert call(a14=FAKE + 2) == L.EALIGN                # rstd (4-byte aligned)
-    assert call(a12=float("nan")) == L.EINVAL            # eps
-    assert call(a12=-1.0) == L.EINVAL
-    assert call(a9=None) == L.EINVAL                     # h_in
-    o = L.nf4s_tensor_layout(4096, 4096, 0)
-    assert call(a1=o, a3=512) == L.EWORKSPACE

@@ -595,49 +595,3 @@ def test_forward_into_residual_equals_forward_plus_residual_add(proj, n, k, M, l
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
     assert torch.equal(ref.view(torch.int32), out.view(torch.int32))
-
-
-@pytest.mark.parametrize("proj,n,k,M,lora", [
-    ("o", 4096, 4096, 512, True),     # split: one pass over the partials
-    ("o", 576, 576, 300, False),      # unsplit: residual and norm kernels follow
-    ("o", 72, 128, 37, True),         # a width with a ragged 64-block (packed tail zeros)
-])
-def test_forward_into_residual_and_norm_equals_the_separate_calls(proj, n, k, M, lora):
-    print(f"residual+norm fwd {proj} {n}x{k} M={M} lora={lora}", flush=True)
-    c = _setup(proj, n, k, M)
-    s = stream()
-    x = dev_bf16bits(c["x"])
-    xp = ws_tensor(L.nf4s_packed_activation_bytes(M, k))
-    L.nf4s_pack_activation(x.data_ptr(), M, k, xp.data_ptr(), xp.numel(), s)
-    A, B = dev_f32(c["a"]), dev_f32(c["b"])
-    u = torch.empty((M, R), dtype=torch.float32, device="cuda")
-    wsl = ws_tensor(L.nf4s_workspace_bytes(L.OP_LORA_FWD, M, n, k))
-    L.lora_fwd(x.data_ptr(), M, k, A.data_ptr(), R, u.data_ptr(), wsl.data_ptr(), wsl.numel(), s)
-    lu, lb, r, sc = (u.data_ptr(), B.data_ptr(), R, S) if lora else (None, None, 0, 0.0)
-    h = dev_f32(bits_to_f32(synth.activation((M, n), 3, 7)))
-    wn = dev_f32((1.0 + 0.05 * bits_to_f32(synth.activation((1, n), 3, 8))).reshape(-1))
-    ws = ws_tensor(L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, M, n, k))
-    sp = c["shard"].data_ptr()
-    nbytes = L.nf4s_packed_activation_bytes(M, n)
-    outs = []
-    for fused in (False, True):
-        y = torch.empty((M, n), dtype=torch.int16, device="cuda")
-        hout = torch.empty_like(h)
-        ny = torch.empty((M, n), dtype=torch.int16, device="cuda")
-        rstd = torch.empty(M, dtype=torch.float32, device="cuda")
-        pk = torch.full((nbytes,), 0x5A, dtype=torch.uint8, device="cuda")
-        if fused:
-            L.streamed_linear_fwd_residual_norm(sp, c["d"], xp.data_ptr(), M, y.data_ptr(), lu, lb, r, sc,
-                                                h.data_ptr(), hout.data_ptr(), wn.data_ptr(), 1e-5,
-                                                ny.data_ptr(), rstd.data_ptr(), ws.data_ptr(), ws.numel(),
-                                                s, norm_packed=pk.data_ptr())
-        else:
-            L.streamed_linear_fwd_packed(sp, c["d"], xp.data_ptr(), M, y.data_ptr(), lu, lb, r, sc,
-                                         ws.data_ptr(), ws.numel(), s)
-            L.nf4s_residual_add(h.data_ptr(), y.data_ptr(), M * n, hout.data_ptr(), s)
-            L.nf4s_rmsnorm_fwd(hout.data_ptr(), wn.data_ptr(), M, n, 1e-5, ny.data_ptr(), rstd.data_ptr(),
-                               s, packed=pk.data_ptr())
-        torch.cuda.synchronize()
-        outs.append((y, hout, ny, rstd, pk))
-    for a, b in zip(*outs):
-        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))

@@ -309,8 +309,8 @@ def sweep(args) -> None:
     for n = 2, 4, 8 slots. Per point: step times, copies and bytes per step,
     and the overlap efficiency (t_copy + t_compute - t_step) / min(t_copy,
     t_compute), where t_copy is the step's bytes at the same-session pinned
-    H2D rate and t_compute the resident step time (SURVEY-style crossover:
-    the copy hides once t_compute >= t_copy). One JSON line per point."""
+    H2D rate and t_compute the resident step time (the copy hides once
+    t_compute >= t_copy). One JSON line per point."""
     import torch
 
     import layer_streamed_nf4_amd as L
@@ -428,7 +428,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
-              "supported by this build (multi-GPU sharding is a design note only)", file=sys.stderr)
+              "supported (sharding across GPUs is described, not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -12,7 +12,7 @@ are packed N/2 + absmax N/64 + nested absmax N/4096 + a 4-byte offset, about
 256-entry nested table. Quantisation is deterministic across repeats and
 across a CPU round trip (section 2.3).
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   * flatten order: row-major W[N_out, K_in]; block b is elements [64b, 64b+64),
     nested block j is absmax blocks [256j, 256j+256); the last nested block may
     be partial;

@@ -595,3 +595,96 @@ def test_forward_into_residual_equals_forward_plus_residual_add(proj, n, k, M, l
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
     assert torch.equal(ref.view(torch.int32), out.view(torch.int32))
+
+
+@pytest.mark.parametrize("r", [8, 40, 64])
+@pytest.mark.parametrize("proj,n,k,M", [("q", 576, 576, 300), ("o", 4096, 4096, 512)])
+def test_lora_ranks_in_gemm_epilogues(proj, n, k, M, r):
+    """The GEMM epilogues add the adapter term in chunks of 16 rank columns:
+    ranks below, across and at the maximum of those chunks, forward and
+    backward, against the oracle (u and du from the adapter kernels)."""
+    print(f"lora rank {r} {proj} {n}x{k} M={M}", flush=True)
+    w = synth.weight(0, proj, n, k)
+    shard, d, _ = quantize_on_gpu(w)
+    wq = bits_to_f32(nf4.dequantize_bf16(nf4.quantize(w))).astype(np.float64)
+    a, b = synth.lora_pair(0, proj, n, k, r=r)
+    xb, dyb = synth.activation((M, k), 0, 0), synth.activation((M, n), 0, 1)
+    s = stream()
+    x, dy = dev_bf16bits(xb), dev_bf16bits(dyb)
+    A, B = dev_f32(a), dev_f32(b)
+    u = torch.empty((M, r), dtype=torch.float32, device="cuda")
+    du = torch.empty((M, r), dtype=torch.float32, device="cuda")
+    dA = torch.empty((r, k), dtype=torch.float32, device="cuda")
+    dB = torch.empty((n, r), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, n), dtype=torch.int16, device="cuda")
+    dx = torch.empty((M, k), dtype=torch.int16, device="cuda")
+    wsl = ws_tensor(max(L.nf4s_workspace_bytes(L.OP_LORA_FWD, M, n, k),
+                        L.nf4s_workspace_bytes(L.OP_LORA_BWD, M, n, k)))
+    wsf = ws_tensor(L.nf4s_workspace_bytes(L.OP_LINEAR_FWD, M, n, k))
+    wsb = ws_tensor(L.nf4s_workspace_bytes(L.OP_LINEAR_BWD, M, n, k))
+    L.lora_fwd(x.data_ptr(), M, k, A.data_ptr(), r, u.data_ptr(), wsl.data_ptr(), wsl.numel(), s)
+    L.streamed_linear_fwd(shard.data_ptr(), d, x.data_ptr(), M, y.data_ptr(), u.data_ptr(), B.data_ptr(),
+                          r, S, wsf.data_ptr(), wsf.numel(), s)
+    L.lora_bwd(x.data_ptr(), dy.data_ptr(), u.data_ptr(), M, k, n, B.data_ptr(), r, S, dA.data_ptr(),
+               dB.data_ptr(), du.data_ptr(), 0, wsl.data_ptr(), wsl.numel(), s)
+    L.streamed_linear_bwd(shard.data_ptr(), d, dy.data_ptr(), M, dx.data_ptr(), du.data_ptr(), A.data_ptr(),
+                          r, wsb.data_ptr(), wsb.numel(), s)
+    torch.cuda.synchronize()
+    xf, dyf = bits_to_f32(xb), bits_to_f32(dyb)
+    y_ref, u_ref = linear.forward(xf, wq, a, b, S)
+    g = linear.backward(xf, dyf, wq, a, b, S)
+    assert linear.rel_err(bits_to_f32(host_u16(y)), y_ref) <= TOL
+    assert linear.rel_err(bits_to_f32(host_u16(dx)), g["dx"]) <= TOL
+    assert linear.rel_err(u.cpu().numpy(), u_ref) <= 1e-5
+    for key, t in (("du", du), ("dA", dA), ("dB", dB)):
+        assert linear.rel_err(t.cpu().numpy(), g[key]) <= 1e-5, key
+    # the adapter term itself is resolved: a 1% error in it would exceed the bar
+    y_base, _ = linear.forward(xf, wq, None, None, 0.0)
+    assert np.max(np.abs(y_ref - y_base)) > 0.02 * np.max(np.abs(y_ref))
+
+
+def test_lora_rank_40_on_the_wide_forward_kernel():
+    """q, k, v at 8B widths and M = 2048 fill the chip unsplit: the 512-row
+    forward kernel's adapter epilogue at rank 40 (three 16-column chunks, the
+    last ragged), sampled outputs against the oracle."""
+    print("lora rank 40 wide forward", flush=True)
+    r, k, M = 40, 4096, 2048
+    ns, projs = (4096, 1024, 1024), ("q", "k", "v")
+    assert L.grouped_workspace_bytes(list(ns), k, M) == 0   # the unsplit 512-row plan
+    c = _group_setup(projs, ns, k, M, (), layer=2)
+    s = stream()
+    xb = c["x"]
+    x = dev_bf16bits(xb)
+    xp = ws_tensor(L.nf4s_packed_activation_bytes(M, k))
+    L.nf4s_pack_activation(x.data_ptr(), M, k, xp.data_ptr(), xp.numel(), s)
+    wsl = ws_tensor(L.nf4s_workspace_bytes(L.OP_LORA_FWD, M, 64, k))
+    ys, us, Bs, keep, pairs = [], [], [], [], []
+    for p, part in zip(projs, c["parts"]):
+        ys.append(torch.empty((M, part["n"]), dtype=torch.int16, device="cuda"))
+        if p in ("q", "v"):
+            a, b = synth.lora_pair(2, p, part["n"], k, r=r)
+            A, B = dev_f32(a), dev_f32(b)
+            u = torch.empty((M, r), dtype=torch.float32, device="cuda")
+            L.lora_fwd(x.data_ptr(), M, k, A.data_ptr(), r, u.data_ptr(), wsl.data_ptr(), wsl.numel(), s)
+            keep += [A, B, u]
+            us.append(u.data_ptr())
+            Bs.append(B.data_ptr())
+            pairs.append((a, b))
+        else:
+            us.append(None)
+            Bs.append(None)
+            pairs.append(None)
+    L.streamed_linear_fwd_grouped(c["shard"].data_ptr(), c["descs"], xp.data_ptr(), M,
+                                  [y.data_ptr() for y in ys], us, Bs, r, S, None, 0, s)
+    torch.cuda.synchronize()
+    xf = bits_to_f32(xb).astype(np.float64)
+    rng = np.random.Generator(np.random.PCG64(41))
+    for part, y, ab in zip(c["parts"], ys, pairs):
+        wq = bits_to_f32(nf4.dequantize_bf16(nf4.quantize(part["w"]))).astype(np.float64)
+        ms, js = rng.integers(0, M, 256), rng.integers(0, part["n"], 256)
+        ref = np.array([xf[m] @ wq[j] for m, j in zip(ms, js)])
+        if ab is not None:
+            a, b = ab[0].astype(np.float64), ab[1].astype(np.float64)
+            ref += np.array([S * (xf[m] @ a.T) @ b[j] for m, j in zip(ms, js)])
+        got = bits_to_f32(host_u16(y)).astype(np.float64)[ms, js]
+        assert linear.rel_err(got, ref) <= TOL

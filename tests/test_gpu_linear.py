@@ -441,7 +441,7 @@ def test_grouped_lora_matches_oracle(projs, ns, k, M, r):
         assert linear.rel_err(second[i]["dB"], 2 * ref["dB"]) <= 1e-5
 
 
-def _bwd_group_run(c, grouped, lora_on):
+def _bwd_group_run(c, grouped, lora_on, r_lora=R):
     """dx of a group from one streamed_linear_bwd_grouped call, or the list of
     single streamed_linear_bwd_packed outputs (same packed dy_j, du_j, A_j).
     du_j is a seeded fp32 stand-in [M, r]; dy_j are seeded bf16."""
@@ -463,7 +463,7 @@ def _bwd_group_run(c, grouped, lora_on):
             dus.append(None)
             As.append(None)
     sp = c["shard"].data_ptr()
-    r = R if any(dus) else 0
+    r = r_lora if any(dus) else 0
     if grouped:
         dx = torch.empty((M, k), dtype=torch.int16, device="cuda")
         ws = ws_tensor(L.grouped_bwd_workspace_bytes([p["n"] for p in c["parts"]], k, M))
@@ -475,19 +475,20 @@ def _bwd_group_run(c, grouped, lora_on):
     for d, dyp, du, A in zip(c["descs"], dyps, dus, As):
         dx = torch.empty((M, k), dtype=torch.int16, device="cuda")
         ws = ws_tensor(L.nf4s_workspace_bytes(L.OP_LINEAR_BWD_PACKED, M, d.n_out, k))
-        L.streamed_linear_bwd_packed(sp, d, dyp, M, dx.data_ptr(), du, A, R if du else 0, ws.data_ptr(),
-                                     ws.numel(), s)
+        L.streamed_linear_bwd_packed(sp, d, dyp, M, dx.data_ptr(), du, A, r_lora if du else 0,
+                                     ws.data_ptr(), ws.numel(), s)
         torch.cuda.synchronize()
         outs.append(host_u16(dx))
     return outs
 
 
-def _bwd_group_setup(projs, ns, k, M, layer=0, step=0):
+def _bwd_group_setup(projs, ns, k, M, layer=0, step=0, r=R):
     c = _group_setup(projs, ns, k, M, (), layer, step)
     for i, (p, part) in enumerate(zip(projs, c["parts"])):
         part["p"] = p
         part["dy"] = synth.activation((M, part["n"]), step, 1 + i)
-        part["du"] = synth.lora_pair(layer + 1, p, M, k)[1]  # seeded fp32 [M, r]
+        part["a"] = synth.lora_pair(layer, p, part["n"], k, r=r)[0]      # A [r, k]
+        part["du"] = synth.lora_pair(layer + 1, p, M, k, r=r)[1]        # seeded fp32 [M, r]
     return c
 
 
@@ -688,3 +689,23 @@ def test_lora_rank_40_on_the_wide_forward_kernel():
             ref += np.array([S * (xf[m] @ a.T) @ b[j] for m, j in zip(ms, js)])
         got = bits_to_f32(host_u16(y)).astype(np.float64)[ms, js]
         assert linear.rel_err(got, ref) <= TOL
+
+
+def test_grouped_backward_rank_40_on_two_adapters():
+    """Adapters on q and v at rank 40 (three 16-column chunks, the last
+    ragged) in one grouped backward with uneven per-weight splits."""
+    projs, ns, k, M, lora_on, r = ("q", "k", "v"), (576, 192, 192), 576, 300, ("q", "v"), 40
+    c = _bwd_group_setup(projs, ns, k, M, r=r)
+    got = bits_to_f32(_bwd_group_run(c, True, lora_on, r_lora=r)).astype(np.float64)
+    ref = np.zeros((M, k))
+    for p, part in zip(projs, c["parts"]):
+        wq = bits_to_f32(nf4.dequantize_bf16(nf4.quantize(part["w"]))).astype(np.float64)
+        ref += bits_to_f32(part["dy"]).astype(np.float64) @ wq
+        if p in lora_on:
+            ref += part["du"].astype(np.float64) @ part["a"].astype(np.float64)
+    assert linear.rel_err(got, ref) <= TOL
+    # a group of one at this rank: the single call's bits
+    c1 = _bwd_group_setup(("q",), (576,), k, M, r=r)
+    g1 = _bwd_group_run(c1, True, ("q",), r_lora=r)
+    (one,) = _bwd_group_run(c1, False, ("q",), r_lora=r)
+    assert np.array_equal(g1, one)

@@ -90,16 +90,8 @@ hipError_t launch_linear_grouped_fwd(const QPtrs* q, int nseg, const int64_t* n_
 
 // Backward of n (<= GEMM_MAX_SEG) NF4 linears that read the same input:
 // dx = sum_j (dy_j . W'_j + du_j . A_j), one contraction over the n weights
-// (every n_outs[j] a multiple of 64 when n > 1); dy_packed[j] is dy_j packed
-// (lora_dus / lora_As entries may be null).
-hipError_t launch_linear_grouped_bwd(const QPtrs* q, int n, const int64_t* n_outs, int64_t k_in,
-                                     const uint8_t* const* dy_packed, int64_t M, uint16_t* dx,
-                                     const float* const* lora_dus, const float* const* lora_As,
-                                     int r, void* part_ws, hipStream_t s);
-
-// Backward of n (<= GEMM_MAX_SEG) NF4 linears that read the same input:
-// dx = sum_j (dy_j . W'_j + du_j . A_j), rounded to bf16 once; dy_packed[j]
-// is dy_j packed (lora_dus / lora_As entries may be null).
+// (every n_outs[j] a multiple of 64 when n > 1) rounded to bf16 once;
+// dy_packed[j] is dy_j packed (lora_dus / lora_As entries may be null).
 struct BwdGroupPlan {
   int splits[GEMM_MAX_SEG];        // splits of each weight's contraction
   int64_t kc_chunk[GEMM_MAX_SEG];  // contraction rows per split

@@ -575,7 +575,9 @@ int nf4s_stream_wait_event(void* stream, void* event);
  *   nf4s_pool_create:   slots are caller-owned device buffers (256-B aligned,
  *                       slot_bytes each); n_slots in [2, 8]; copy and compute
  *                       are distinct streams.
- *   nf4s_pool_set_layer: register layer `layer`'s pinned host shard.
+ *   nf4s_pool_set_layer: register layer `layer`'s pinned host shard; a copy
+ *                       of an earlier registration still in a slot is
+ *                       dropped (ESLOT while a reader holds it).
  *   nf4s_pool_prefetch: start copying `layer` into a slot no reader holds
  *                       (no-op if resident or in flight). ESLOT if every
  *                       slot is held.

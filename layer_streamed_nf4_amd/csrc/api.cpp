@@ -1096,12 +1096,15 @@ int nf4s_pool_set_layer(nf4s_pool* p, int layer, const void* src, size_t bytes) 
     return fail(NF4S_ESLOT, "shard of %zu bytes does not fit a slot of %zu bytes", bytes, p->slot_bytes);
   int rc = check_pinned(src);
   if (rc) return rc;
+  // a re-registered layer is stale wherever it is resident; one that a reader
+  // holds cannot be replaced under it
+  const int i = pool_find(p, layer);
+  if (i >= 0 && p->slots[i].held)
+    return fail(NF4S_ESLOT, "layer %d is acquired; release it before registering it again", layer);
   if ((int)p->layers.size() <= layer) p->layers.resize(layer + 1);
   p->layers[layer].src = src;
   p->layers[layer].bytes = bytes;
-  // a re-registered layer is stale wherever it is resident
-  const int i = pool_find(p, layer);
-  if (i >= 0 && !p->slots[i].held) p->slots[i].layer = -1;
+  if (i >= 0) p->slots[i].layer = -1;
   return NF4S_OK;
 }
 

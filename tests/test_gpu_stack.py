@@ -133,6 +133,53 @@ def test_prefetch_copies_bytes_and_orders_events():
     L.nf4s_event_destroy(ready)
 
 
+def test_pool_slots_evict_and_reregister():
+    """Two slots, three layers: least recently used eviction, a held slot is
+    never a victim, and a layer registered again is copied afresh."""
+    require_gpu()
+    nbytes = 1024 * 1024
+    srcs = [torch.full((nbytes,), 11 * (i + 1), dtype=torch.uint8).pin_memory() for i in range(4)]
+    slots = [torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    cs = torch.cuda.Stream()
+    comp = torch.cuda.current_stream().cuda_stream
+    pool = L.nf4s_pool_create([t.data_ptr() for t in slots], nbytes, cs.cuda_stream, comp)
+    try:
+        for i in range(3):
+            L.nf4s_pool_set_layer(pool, i, srcs[i].data_ptr(), nbytes)
+
+        def read(layer):
+            ptr = L.nf4s_pool_acquire(pool, layer)
+            slot = next(t for t in slots if t.data_ptr() == ptr)
+            val = slot.cpu()
+            L.nf4s_pool_release(pool, layer)
+            return val
+
+        assert torch.equal(read(0), srcs[0]) and torch.equal(read(1), srcs[1])
+        assert L.nf4s_pool_stats(pool) == (2, 2 * nbytes)
+        assert torch.equal(read(0), srcs[0])                  # resident: no copy
+        assert L.nf4s_pool_stats(pool)[0] == 2
+        assert torch.equal(read(2), srcs[2])                  # evicts layer 1
+        assert torch.equal(read(0), srcs[0])
+        assert L.nf4s_pool_stats(pool)[0] == 3
+        # a held slot is no victim: with both held, a prefetch is refused
+        L.nf4s_pool_acquire(pool, 0)
+        L.nf4s_pool_acquire(pool, 2)
+        with pytest.raises(L.Nf4sError) as e:
+            L.nf4s_pool_prefetch(pool, 1)
+        assert e.value.code == L.ESLOT
+        with pytest.raises(L.Nf4sError) as e:               # held: not replaced
+            L.nf4s_pool_set_layer(pool, 0, srcs[3].data_ptr(), nbytes)
+        assert e.value.code == L.ESLOT
+        L.nf4s_pool_release(pool, 0)
+        L.nf4s_pool_release(pool, 2)
+        L.nf4s_pool_set_layer(pool, 0, srcs[3].data_ptr(), nbytes)
+        assert torch.equal(read(0), srcs[3])                  # copied afresh
+        assert L.nf4s_pool_stats(pool)[0] == 4
+    finally:
+        torch.cuda.synchronize()
+        L.nf4s_pool_destroy(pool)
+
+
 def test_pageable_source_is_refused():
     require_gpu()
     src = torch.zeros(4096, dtype=torch.uint8)           # pageable

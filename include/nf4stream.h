@@ -53,7 +53,7 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------ */
 #define NF4S_OK 0
 #define NF4S_EINVAL -1      /* null pointer, bad enum, non-finite scale, r out of range */
-#define NF4S_ESHAPE -2      /* K_in % 64 != 0, odd element count, M/N <= 0, size overflow */
+#define NF4S_ESHAPE -2      /* K_in % 64 != 0, odd element count, M/N <= 0, GEMM M > 2^23, size overflow */
 #define NF4S_EALIGN -3      /* pointer not aligned (16 B for tensors, 256 B for shards/slots) */
 #define NF4S_ETABLE -4      /* descriptor's table hash differs from the library's tables */
 #define NF4S_EKEY -5        /* method / block / nested block / double-quant flag mismatch */

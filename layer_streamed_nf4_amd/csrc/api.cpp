@@ -14,6 +14,10 @@ using namespace nf4s;
 
 namespace {
 
+// Rows of a GEMM operand: 256-row tiles keep the grid's y dimension far below
+// its limit of 65535.
+constexpr int64_t kMaxRows = 1ll << 23;
+
 thread_local std::string g_err;
 
 int fail(int code, const char* fmt, ...) {
@@ -164,7 +168,7 @@ uint64_t nf4s_table_hash(void) { return host_table_hash(); }
 int nf4s_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, size_t* bytes) {
   if (!bytes) return fail(NF4S_EINVAL, "bytes is NULL");
   if (op == NF4S_OP_ATTENTION_BWD || op == NF4S_OP_CROSS_ENTROPY) {
-    if (M <= 0 || M > (1ll << 24)) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
+    if (M <= 0 || M > kMaxRows) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
     if (op == NF4S_OP_CROSS_ENTROPY) {
       *bytes = cross_entropy_ws_bytes(M);
       return NF4S_OK;
@@ -187,7 +191,7 @@ int nf4s_workspace_bytes(int op, int64_t M, int64_t n_out, int64_t k_in, size_t*
     case NF4S_OP_LINEAR_BWD_PACKED:
     case NF4S_OP_DENSE_FWD_PACKED:
     case NF4S_OP_DENSE_BWD_PACKED: {
-      if (M <= 0) return fail(NF4S_ESHAPE, "M=%lld must be positive", (long long)M);
+      if (M <= 0 || M > kMaxRows) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
       const bool bwd = op == NF4S_OP_LINEAR_BWD || op == NF4S_OP_LINEAR_BWD_PACKED ||
                        op == NF4S_OP_DENSE_BWD_PACKED;
       const bool dense = op == NF4S_OP_DENSE_FWD_PACKED || op == NF4S_OP_DENSE_BWD_PACKED;
@@ -242,7 +246,7 @@ int nf4_dequant(const void* shard_dev, const nf4s_tensor_desc* d, uint16_t* w_bf
 
 // Packed activations are addressed with 32-bit offsets.
 static int check_packed_shape(int64_t M, int64_t K) {
-  if (M <= 0 || M > (1ll << 24)) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
+  if (M <= 0 || M > kMaxRows) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
   if (K <= 0 || K % 8) return fail(NF4S_ESHAPE, "K=%lld must be a positive multiple of 8", (long long)K);
   if (packed_activation_bytes(M, K) >= (1ull << 32))
     return fail(NF4S_ESHAPE, "packed activation of %lldx%lld exceeds 32-bit offsets", (long long)M,
@@ -256,7 +260,7 @@ static int linear_checks(bool bwd, const void* shard_dev, const nf4s_tensor_desc
                          float scale, GemmPlan* plan) {
   int rc;
   if ((rc = check_desc(d))) return rc;
-  if (M <= 0 || M > (1ll << 24)) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
+  if (M <= 0 || M > kMaxRows) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
   // the kernels address outputs and packed weights with 32-bit offsets
   const int64_t widest = d->n_out > d->k_in ? d->n_out : d->k_in;
   if (M * widest >= (1ll << 31) || d->n_out * d->k_in >= (1ll << 33))
@@ -454,7 +458,7 @@ static int check_bwd_group(int n, const int64_t* n_outs, int64_t k_in, int64_t M
   if (n < 1 || n > GEMM_MAX_SEG)
     return fail(NF4S_EINVAL, "group of %d weights (1..%d allowed)", n, GEMM_MAX_SEG);
   if (!n_outs) return fail(NF4S_EINVAL, "n_outs is NULL");
-  if (M <= 0 || M > (1ll << 24)) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
+  if (M <= 0 || M > kMaxRows) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
   int rc;
   for (int i = 0; i < n; ++i) {
     if ((rc = check_shape(n_outs[i], k_in))) return rc;
@@ -666,7 +670,7 @@ static int dense_common(bool bwd, const uint16_t* w, int64_t n_out, int64_t k_in
                         void* stream) {
   int rc;
   if ((rc = check_shape(n_out, k_in))) return rc;
-  if (M <= 0 || M > (1ll << 24)) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
+  if (M <= 0 || M > kMaxRows) return fail(NF4S_ESHAPE, "M=%lld out of range", (long long)M);
   const int64_t widest = n_out > k_in ? n_out : k_in;
   if (M * widest >= (1ll << 31)) return fail(NF4S_ESHAPE, "M x width exceeds 32-bit offsets");
   if ((rc = check_packed_shape(M, bwd ? n_out : k_in))) return rc;

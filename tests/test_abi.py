@@ -81,6 +81,12 @@ def test_workspace_queries_depend_on_shape_only():
     with pytest.raises(L.Nf4sError) as e:
         L.nf4s_workspace_bytes(99, 1, 64, 64)
     assert e.value.code == L.EINVAL
+    # GEMM rows: at most 2^23 (the tile grid's y dimension stays below 65535)
+    assert L.nf4s_workspace_bytes(L.OP_LINEAR_FWD, 1 << 23, 64, 64) >= 0
+    for op in (L.OP_LINEAR_FWD, L.OP_LINEAR_BWD):
+        with pytest.raises(L.Nf4sError) as e:
+            L.nf4s_workspace_bytes(op, (1 << 23) + 1, 64, 64)
+        assert e.value.code == L.ESHAPE
 
 
 FAKE = 1 << 40  # a 256-byte aligned address that is never dereferenced

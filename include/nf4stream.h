@@ -195,6 +195,7 @@ int streamed_linear_fwd(const void* shard_dev, const nf4s_tensor_desc* d, const 
                         int64_t M, uint16_t* y, const float* lora_u, const float* lora_B, int r,
                         float scale, void* ws, size_t ws_bytes, void* stream);
 
+
 /*
  * Backward (input gradient only) of the same linear, [G] s4.4 (frozen base:
  * dL/dx and no dL/dW) and [E] (dL/dx needs W again, hence the second read):
@@ -573,19 +574,38 @@ int nf4s_stream_wait_event(void* stream, void* event);
  * the NF4 layers above ~165 MiB). A layer still resident in a slot is not
  * copied again.
  *   nf4s_pool_create:   slots are caller-owned device buffers (256-B aligned,
- *                       slot_bytes each); n_slots in [2, 8]; copy and compute
- *                       are distinct streams.
+ *                       slot_bytes > 0 each, pairwise disjoint: EINVAL if two
+ *                       overlap); n_slots in [2, 8]; copy and compute are
+ *                       distinct streams.
  *   nf4s_pool_set_layer: register layer `layer`'s pinned host shard; a copy
  *                       of an earlier registration still in a slot is
  *                       dropped (ESLOT while a reader holds it).
- *   nf4s_pool_prefetch: start copying `layer` into a slot no reader holds
- *                       (no-op if resident or in flight). ESLOT if every
- *                       slot is held.
- *   nf4s_pool_acquire:  make `layer` resident (copying now if needed), make
- *                       the compute stream wait for it, return its slot.
+ *   nf4s_pool_prefetch: reserve `layer` for its next acquire: if it is
+ *                       resident or in flight it is only marked reserved;
+ *                       otherwise it is copied into a slot no reader holds
+ *                       and no earlier prefetch reserved (an empty slot
+ *                       first, else the least recently used one). When every
+ *                       slot no reader holds is reserved, nothing is copied
+ *                       (the acquire copies) and NF4S_OK is returned; ESLOT
+ *                       if every slot is held. A caller may thus prefetch up
+ *                       to n_slots - 1 layers ahead without evicting a layer
+ *                       it prefetched earlier.
+ *   nf4s_pool_acquire:  make `layer` resident (copying now if needed, into an
+ *                       empty, else unreserved, else reserved slot, least
+ *                       recently used first), make the compute stream wait
+ *                       for it, return its slot.
  *   nf4s_pool_release:  record the slot's free event on the compute stream
  *                       after the last kernel that reads it was enqueued.
  *   nf4s_pool_stats:    copies issued and bytes copied so far.
+ * prefetch, acquire and release return ESLOT for a layer index that was never
+ * registered (negative included).
+ *   nf4s_pool_set_debug: NF4S_POOL_POISON_ON_RELEASE makes every release also
+ *                       overwrite the slot with 0xFF bytes (NaN block scales)
+ *                       on the copy stream, ordered after the free event as a
+ *                       copy would be, and forget the layer it held; a kernel
+ *                       that read a slot after its release would then compute
+ *                       with NaN weights. For tests of the slot ordering; it
+ *                       adds one fill and, later, one copy per release.
  */
 typedef struct nf4s_pool nf4s_pool;
 int nf4s_pool_create(int n_slots, void* const* slots, size_t slot_bytes, void* copy_stream,
@@ -596,6 +616,8 @@ int nf4s_pool_prefetch(nf4s_pool* pool, int layer);
 int nf4s_pool_acquire(nf4s_pool* pool, int layer, void** slot_dev_out);
 int nf4s_pool_release(nf4s_pool* pool, int layer);
 int nf4s_pool_stats(const nf4s_pool* pool, uint64_t* copies, uint64_t* bytes);
+#define NF4S_POOL_POISON_ON_RELEASE 1
+int nf4s_pool_set_debug(nf4s_pool* pool, int flags);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,7 @@ EXPORTS = (
     "layer_prefetch", "nf4s_event_create", "nf4s_event_destroy", "nf4s_event_record",
     "nf4s_stream_wait_event", "nf4s_pool_create", "nf4s_pool_destroy", "nf4s_pool_set_layer",
     "nf4s_pool_prefetch", "nf4s_pool_acquire", "nf4s_pool_release", "nf4s_pool_stats",
-    "nf4s_packed_activation_bytes", "nf4s_pack_activation", "streamed_linear_fwd_packed",
+    "nf4s_pool_set_debug", "nf4s_packed_activation_bytes", "nf4s_pack_activation", "streamed_linear_fwd_packed",
     "streamed_linear_bwd_packed", "dense_linear_fwd_packed", "dense_linear_bwd_packed",
     "nf4s_grouped_workspace_bytes", "streamed_linear_fwd_grouped",
     "nf4s_lora_grouped_workspace_bytes", "lora_fwd_grouped", "lora_bwd_grouped",
@@ -102,6 +102,7 @@ _SIG = {
     "nf4s_pool_acquire": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_P)]),
     "nf4s_pool_release": (ctypes.c_int, [_P, ctypes.c_int]),
     "nf4s_pool_stats": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint64)]),
+    "nf4s_pool_set_debug": (ctypes.c_int, [_P, ctypes.c_int]),
     "nf4s_packed_activation_bytes": (ctypes.c_uint64, [_I64, _I64]),
     "nf4s_pack_activation": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_size_t, _P]),
     "streamed_linear_fwd_packed": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P,
@@ -471,6 +472,13 @@ def nf4s_pool_acquire(pool, layer) -> int:
 
 def nf4s_pool_release(pool, layer):
     _check(lib().nf4s_pool_release(pool, layer))
+
+
+POOL_POISON_ON_RELEASE = 1
+
+
+def nf4s_pool_set_debug(pool, flags):
+    _check(lib().nf4s_pool_set_debug(pool, flags))
 
 
 def nf4s_pool_stats(pool):

@@ -30,6 +30,20 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
+}  // namespace
+
+int nf4s::set_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+namespace {
+
 int hip_fail(hipError_t e, const char* what) {
   return fail(NF4S_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
@@ -1004,8 +1018,9 @@ struct nf4s_pool {
     hipEvent_t free = nullptr;   // recorded on the compute stream after the last reader
     int layer = -1;              // layer held (or being copied), -1 = none
     bool held = false;           // between acquire and release
+    bool reserved = false;       // prefetched (or asked for again) and not yet acquired
     bool free_recorded = false;  // a free event exists to wait on
-    uint64_t last_use = 0;
+    uint64_t last_use = 0;       // 0 = never, or emptied
   };
   struct Layer {
     const void* src = nullptr;
@@ -1014,6 +1029,7 @@ struct nf4s_pool {
   int n = 0;
   size_t slot_bytes = 0;
   hipStream_t copy = nullptr, compute = nullptr;
+  int debug = 0;  // NF4S_POOL_POISON_ON_RELEASE
   Slot slots[8];
   std::vector<Layer> layers;
   uint64_t tick = 0, copies = 0, bytes = 0;
@@ -1022,32 +1038,50 @@ struct nf4s_pool {
 namespace {
 
 int pool_find(const nf4s_pool* p, int layer) {
+  if (layer < 0) return -1;  // -1 marks an empty slot, never a layer
   for (int i = 0; i < p->n; ++i)
     if (p->slots[i].layer == layer) return i;
   return -1;
 }
 
-int pool_copy_into(nf4s_pool* p, int layer, int* slot_out) {
+int pool_check_layer(const nf4s_pool* p, int layer) {
   if (layer < 0 || layer >= (int)p->layers.size() || !p->layers[layer].src)
     return fail(NF4S_ESLOT, "layer %d was not registered", layer);
-  // victim: the least recently used slot that no reader holds
+  return NF4S_OK;
+}
+
+// The slot a copy may overwrite: one that no reader holds, preferring an
+// empty slot, then the least recently used slot that no earlier prefetch
+// reserved; a reserved slot only when take_reserved (an acquire that must
+// make room).
+int pool_victim(const nf4s_pool* p, bool take_reserved) {
   int v = -1;
-  for (int i = 0; i < p->n; ++i) {
-    const auto& s = p->slots[i];
-    if (s.held) continue;
-    if (v < 0 || s.last_use < p->slots[v].last_use) v = i;
+  for (int pass = 0; pass < (take_reserved ? 2 : 1) && v < 0; ++pass) {
+    for (int i = 0; i < p->n; ++i) {
+      const auto& s = p->slots[i];
+      if (s.held || (pass == 0 && s.reserved)) continue;
+      if (s.layer < 0) return i;
+      if (v < 0 || s.last_use < p->slots[v].last_use) v = i;
+    }
   }
-  if (v < 0) return fail(NF4S_ESLOT, "every slot is held; release one before prefetching");
+  return v;
+}
+
+int pool_copy_into(nf4s_pool* p, int layer, int v) {
   auto& s = p->slots[v];
   const auto& L = p->layers[layer];
   int rc = layer_prefetch(s.ptr, p->slot_bytes, L.src, L.bytes, p->copy,
                           s.free_recorded ? s.free : nullptr, s.ready);
-  if (rc) return rc;
+  if (rc) {
+    s.layer = -1;  // the copy was not enqueued; whatever the slot held is unknown
+    s.reserved = false;
+    s.last_use = 0;
+    return rc;
+  }
   s.layer = layer;
   s.last_use = ++p->tick;
   p->copies += 1;
   p->bytes += L.bytes;
-  *slot_out = v;
   return NF4S_OK;
 }
 
@@ -1059,12 +1093,21 @@ int nf4s_pool_create(int n_slots, void* const* slots, size_t slot_bytes, void* c
                      void* compute_stream, nf4s_pool** out) {
   if (!out || !slots) return fail(NF4S_EINVAL, "NULL argument");
   if (n_slots < 2 || n_slots > 8) return fail(NF4S_ESLOT, "pool size %d outside [2, 8]", n_slots);
+  if (slot_bytes == 0) return fail(NF4S_ESLOT, "slot_bytes is 0");
   if (copy_stream == compute_stream)
     return fail(NF4S_EINVAL, "copy and compute streams must differ (the copy overlaps compute)");
   for (int i = 0; i < n_slots; ++i) {
     int rc = check_ptr(slots[i], "slot", 256);
     if (rc) return rc;
   }
+  // two slots sharing memory would let a copy overwrite a layer another
+  // slot's reader still holds
+  for (int i = 0; i < n_slots; ++i)
+    for (int j = i + 1; j < n_slots; ++j) {
+      const uintptr_t a = (uintptr_t)slots[i], b = (uintptr_t)slots[j];
+      if (a < b + slot_bytes && b < a + slot_bytes)
+        return fail(NF4S_EINVAL, "slots %d and %d overlap (slot_bytes %zu)", i, j, slot_bytes);
+    }
   nf4s_pool* p = new nf4s_pool();
   p->n = n_slots;
   p->slot_bytes = slot_bytes;
@@ -1093,6 +1136,13 @@ int nf4s_pool_destroy(nf4s_pool* p) {
   return NF4S_OK;
 }
 
+int nf4s_pool_set_debug(nf4s_pool* p, int flags) {
+  if (!p) return fail(NF4S_EINVAL, "pool is NULL");
+  if (flags & ~NF4S_POOL_POISON_ON_RELEASE) return fail(NF4S_EINVAL, "unknown debug flags %d", flags);
+  p->debug = flags;
+  return NF4S_OK;
+}
+
 int nf4s_pool_set_layer(nf4s_pool* p, int layer, const void* src, size_t bytes) {
   if (!p || !src) return fail(NF4S_EINVAL, "NULL argument");
   if (layer < 0 || layer > (1 << 20)) return fail(NF4S_ESLOT, "layer index %d", layer);
@@ -1108,29 +1158,51 @@ int nf4s_pool_set_layer(nf4s_pool* p, int layer, const void* src, size_t bytes) 
   if ((int)p->layers.size() <= layer) p->layers.resize(layer + 1);
   p->layers[layer].src = src;
   p->layers[layer].bytes = bytes;
-  if (i >= 0) p->slots[i].layer = -1;
+  if (i >= 0) {
+    p->slots[i].layer = -1;
+    p->slots[i].reserved = false;
+    p->slots[i].last_use = 0;
+  }
   return NF4S_OK;
 }
 
 int nf4s_pool_prefetch(nf4s_pool* p, int layer) {
   if (!p) return fail(NF4S_EINVAL, "pool is NULL");
-  if (pool_find(p, layer) >= 0) return NF4S_OK;
-  int slot;
-  return pool_copy_into(p, layer, &slot);
+  int rc = pool_check_layer(p, layer);
+  if (rc) return rc;
+  const int i = pool_find(p, layer);
+  if (i >= 0) {  // resident or in flight: keep it for its next reader
+    if (!p->slots[i].held) p->slots[i].reserved = true;
+    return NF4S_OK;
+  }
+  const int v = pool_victim(p, false);
+  if (v < 0) {
+    for (int j = 0; j < p->n; ++j)
+      if (!p->slots[j].held) return NF4S_OK;  // every free slot is reserved: the acquire copies
+    return fail(NF4S_ESLOT, "every slot is held; release one before prefetching");
+  }
+  rc = pool_copy_into(p, layer, v);
+  if (rc) return rc;
+  p->slots[v].reserved = true;
+  return NF4S_OK;
 }
 
 int nf4s_pool_acquire(nf4s_pool* p, int layer, void** slot_dev_out) {
   if (!p || !slot_dev_out) return fail(NF4S_EINVAL, "NULL argument");
+  int rc = pool_check_layer(p, layer);
+  if (rc) return rc;
   int i = pool_find(p, layer);
+  if (i >= 0 && p->slots[i].held) return fail(NF4S_ESLOT, "layer %d is already acquired", layer);
   if (i < 0) {
-    int rc = pool_copy_into(p, layer, &i);
-    if (rc) return rc;
+    i = pool_victim(p, true);
+    if (i < 0) return fail(NF4S_ESLOT, "every slot is held; release one before acquiring layer %d", layer);
+    if ((rc = pool_copy_into(p, layer, i))) return rc;
   }
   auto& s = p->slots[i];
-  if (s.held) return fail(NF4S_ESLOT, "layer %d is already acquired", layer);
   hipError_t e = hipStreamWaitEvent(p->compute, s.ready, 0);
   if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   s.held = true;
+  s.reserved = false;
   s.last_use = ++p->tick;
   *slot_dev_out = s.ptr;
   return NF4S_OK;
@@ -1138,6 +1210,8 @@ int nf4s_pool_acquire(nf4s_pool* p, int layer, void** slot_dev_out) {
 
 int nf4s_pool_release(nf4s_pool* p, int layer) {
   if (!p) return fail(NF4S_EINVAL, "pool is NULL");
+  int rc = pool_check_layer(p, layer);
+  if (rc) return rc;
   const int i = pool_find(p, layer);
   if (i < 0 || !p->slots[i].held) return fail(NF4S_ESLOT, "layer %d is not acquired", layer);
   auto& s = p->slots[i];
@@ -1145,6 +1219,17 @@ int nf4s_pool_release(nf4s_pool* p, int layer) {
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   s.free_recorded = true;
   s.held = false;
+  if (p->debug & NF4S_POOL_POISON_ON_RELEASE) {
+    // Overwrite the slot with NaN bytes on the copy stream, ordered after the
+    // free event exactly as the next copy into the slot would be: a kernel
+    // that still read the slot after its release would see NaN weights.
+    s.layer = -1;
+    s.reserved = false;
+    s.last_use = 0;
+    if ((e = hipStreamWaitEvent(p->copy, s.free, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    if ((e = launch_fill_u32(s.ptr, p->slot_bytes, 0xFFFFFFFFu, p->copy)) != hipSuccess)
+      return hip_fail(e, "poison fill launch");
+  }
   return NF4S_OK;
 }
 

@@ -20,6 +20,9 @@ struct Mids8 {
   float m[255];
 };
 
+// Sets the calling thread's last-error message (nf4s_last_error) and returns code.
+int set_error(int code, const char* fmt, ...);
+
 // Host-side tables, computed once at first use (see tables.cpp).
 const Tables& host_tables();
 const Mids4& host_mids4();
@@ -70,6 +73,8 @@ hipError_t launch_dequant(const QPtrs& q, int64_t n_out, int64_t k_in, uint16_t*
                           hipStream_t s);
 
 hipError_t launch_pack(const uint16_t* a, int64_t M, int64_t K, uint8_t* packed, hipStream_t s);
+// Writes the 32-bit pattern v over `bytes` bytes at p (16-byte aligned).
+hipError_t launch_fill_u32(void* p, size_t bytes, uint32_t v, hipStream_t s);
 hipError_t launch_linear_packed(bool backward, const QPtrs& q, int64_t n_out, int64_t k_in,
                                 const uint8_t* a_packed, int64_t M, uint16_t* out,
                                 const float* lora_l, const float* lora_r, int r, float scale,

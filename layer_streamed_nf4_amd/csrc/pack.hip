@@ -58,7 +58,29 @@ __global__ __launch_bounds__(256) void k_frag_pack(const uint16_t* __restrict__ 
   }
 }
 
+// Writes the 32-bit pattern v (little-endian, repeated) over `bytes` bytes at p
+// (16-byte aligned): 16-byte stores for the bulk, byte stores for a ragged
+// tail (the slot pool's poison mode).
+__global__ __launch_bounds__(256) void k_fill_u32(uint8_t* __restrict__ p, int64_t bytes, uint32_t v) {
+  const int64_t n = bytes / 16;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int64_t i = t; i < n; i += stride) reinterpret_cast<u32x4*>(p)[i] = u32x4{v, v, v, v};
+  if (t == 0)
+    for (int64_t b = n * 16; b < bytes; ++b) p[b] = (uint8_t)(v >> (8 * (b % 4)));
+}
+
 }  // namespace
+
+hipError_t launch_fill_u32(void* p, size_t bytes, uint32_t v, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  const int64_t words = (int64_t)(bytes / 16);
+  int64_t blocks = (words + 255) / 256;
+  blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<uint8_t*>(p),
+                     (int64_t)bytes, v);
+  return hipGetLastError();
+}
 
 size_t packed_activation_bytes(int64_t M, int64_t K) {
   return (size_t)((M + PACK_ROWS - 1) / PACK_ROWS * PACK_ROWS) *

@@ -34,13 +34,13 @@ from . import (OP_ATTENTION_BWD, OP_CROSS_ENTROPY, OP_DENSE_BWD_PACKED, OP_DENSE
                nf4s_attention_bwd, nf4s_attention_fwd, nf4s_cross_entropy, nf4s_dpo_loss,
                nf4s_embed, nf4s_logit_grad, nf4s_token_nll,
                nf4s_pack_activation, nf4s_packed_activation_bytes, nf4s_pool_acquire,
-               nf4s_pool_create, nf4s_pool_destroy, nf4s_pool_prefetch, nf4s_pool_release,
-               nf4s_pool_set_layer, nf4s_pool_stats, nf4s_rmsnorm_bwd,
+               nf4s_pool_create, nf4s_pool_destroy, nf4s_pool_release, nf4s_pool_set_debug,
+               nf4s_pool_set_layer, POOL_POISON_ON_RELEASE, nf4s_pool_stats, nf4s_rmsnorm_bwd,
                nf4s_rmsnorm_fwd, nf4s_rope_pair, nf4s_swiglu_bwd, nf4s_swiglu_fwd,
                nf4s_workspace_bytes, streamed_linear_bwd_packed, streamed_linear_fwd_packed,
                streamed_linear_fwd_grouped, grouped_workspace_bytes, grouped_bwd_workspace_bytes,
                streamed_linear_bwd_grouped, streamed_linear_fwd_residual)
-from .stack import ALIGN, PROJ, ShardSet, _round_up
+from .stack import ALIGN, PROJ, ShardSet, _prefetch_ahead, _round_up
 
 # projections that read the same input: q, k, v the normed h; gate, up the
 # normed h_mid; o and down each their own
@@ -64,7 +64,7 @@ class Decoder:
 
     def __init__(self, cfg, shards: ShardSet, embed, lm_head, norms, lora, batch, seq,
                  targets=("q", "v"), r=16, alpha=32, n_slots=2, mode="streamed", lr=1e-4,
-                 betas=(0.9, 0.999), adam_eps=1e-8, weight_decay=0.0, time_calls=None):
+                 betas=(0.9, 0.999), adam_eps=1e-8, weight_decay=0.0, time_calls=None, poison=False):
         """time_calls: optional predicate (direction, n_out, k_in) -> bool; the
         streamed linear forward calls it accepts are bracketed by timing
         events on the compute stream, collected in self.timed as
@@ -202,6 +202,8 @@ class Decoder:
                                          self.copy.cuda_stream, self.compute.cuda_stream)
             for i, hst in enumerate(shards.host):
                 nf4s_pool_set_layer(self.pool, i, hst.data_ptr(), nb)
+            if poison:  # every released slot is overwritten with NaN block scales
+                nf4s_pool_set_debug(self.pool, POOL_POISON_ON_RELEASE)
         else:
             self.resident = shards.to_device()
 
@@ -441,14 +443,15 @@ class Decoder:
         dense_linear_fwd_packed(self.lm_head.data_ptr(), V, H, self._pack(self.hn, H), M,
                                 self.logits.data_ptr(), *self._ws(), s)
 
-    def _forward_sweep(self, adapters, nxt_last=None):
-        """Layers 0..L-1 from h_0 (the last one prefetching nxt_last). With
+    def _forward_sweep(self, adapters, then=()):
+        """Layers 0..L-1 from h_0; `then` is the order in which layers are read
+        after this sweep (what the pool prefetches beyond its end). With
         the adapters on, the last layer's body stays in the buffers for the
         backward, which then skips its recompute (same kernels, same inputs:
         the same bits)."""
         L = self.L
         for i in range(L):
-            base = self._acquire(i, nxt=i + 1 if i + 1 < L else nxt_last)
+            base = self._acquire(i, list(range(i + 1, L)) + list(then))
             keep = adapters and i == L - 1
             self._layer_fwd(i, base, recompute=False, adapters=adapters, keep=keep)
             self._release(i)
@@ -467,7 +470,7 @@ class Decoder:
                          self.rstd_f.data_ptr(), M, H, 0, self.dh.data_ptr(), s, y=self.dd.data_ptr(),
                          packed=self.packed_c.data_ptr())
         for i in range(L - 1, -1, -1):
-            base = self._acquire(i, nxt=i - 1 if i > 0 else None)
+            base = self._acquire(i, range(i - 1, -1, -1))
             if not (i == L - 1 and self._kept_last):
                 self._layer_fwd(i, base, recompute=True)
             self._layer_bwd(i, base)
@@ -483,7 +486,7 @@ class Decoder:
         self.compute.wait_stream(torch.cuda.current_stream())
         s = self._s
         nf4s_embed(self.embed.data_ptr(), V, H, ids.data_ptr(), M, self.h[0].data_ptr(), s)
-        self._forward_sweep(adapters=True)
+        self._forward_sweep(adapters=True, then=range(self.L - 1, -1, -1))
         self._head_fwd(self.h[self.L])
         nf4s_cross_entropy(self.logits.data_ptr(), targets.data_ptr(), M, V, self.loss.data_ptr(),
                            self.dlogits.data_ptr(), *self._ws(), s)
@@ -513,15 +516,15 @@ class Decoder:
         s = self._s
         nf4s_embed(self.embed.data_ptr(), V, H, ids.data_ptr(), M, self.h[0].data_ptr(), s)
         if schedule == "separate":
-            # the last reference layer prefetches the policy's first
-            self._forward_sweep(adapters=False, nxt_last=0)
+            # the reference sweep prefetches the policy's first layers
+            self._forward_sweep(adapters=False, then=range(L))
             self._head_fwd(self.h[L])
             nf4s_token_nll(self.logits.data_ptr(), targets.data_ptr(), M, V, self.nll_ref.data_ptr(), s)
-            self._forward_sweep(adapters=True)
+            self._forward_sweep(adapters=True, then=range(L - 1, -1, -1))
         else:
             href = self.href
             for i in range(L):
-                base = self._acquire(i, nxt=i + 1 if i + 1 < L else None)
+                base = self._acquire(i, list(range(i + 1, L)) + list(range(L - 1, -1, -1)))
                 self._layer_fwd(i, base, recompute=False, adapters=False,
                                 hin=self.h[0] if i == 0 else href[i % 2], hout=href[(i + 1) % 2])
                 self._layer_fwd(i, base, recompute=False, keep=i == L - 1)
@@ -566,12 +569,13 @@ class Decoder:
         self.forward_backward(ids, targets)
         self.optimizer_step()
 
-    def _acquire(self, i, nxt):
+    def _acquire(self, i, ahead):
+        """Layer i's slot; then prefetch the next n - 1 distinct layers of
+        `ahead` (the rest of the step's reading order)."""
         if self.pool is None:
             return self.resident[i].data_ptr()
         base = nf4s_pool_acquire(self.pool, i)
-        if nxt is not None:
-            nf4s_pool_prefetch(self.pool, nxt)
+        _prefetch_ahead(self.pool, i, ahead, len(self.slots) - 1)
         return base
 
     def _release(self, i):

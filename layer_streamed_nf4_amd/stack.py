@@ -24,6 +24,7 @@ from . import (DTYPE_F32, OP_LINEAR_BWD_PACKED, OP_LINEAR_FWD_PACKED, OP_LORA_BW
                OP_QUANTIZE, lora_bwd, lora_fwd, nf4_quantize_shard, nf4s_pack_activation,
                nf4s_packed_activation_bytes, nf4s_pool_acquire, nf4s_pool_create,
                nf4s_pool_destroy, nf4s_pool_prefetch, nf4s_pool_release, nf4s_pool_set_layer,
+               nf4s_pool_set_debug, POOL_POISON_ON_RELEASE,
                nf4s_pool_stats, nf4s_tensor_layout, nf4s_workspace_bytes,
                streamed_linear_bwd_packed, streamed_linear_fwd_packed)
 
@@ -112,6 +113,22 @@ class ShardSet:
         return self.device
 
 
+def _prefetch_ahead(pool, cur, ahead, depth):
+    """Prefetch the first `depth` distinct layers of `ahead` other than cur, in
+    order ("Fine-Tune 8B Models on 4GB VRAM: Soup's Layer Streaming", "The
+    Principle of Layer Streaming": the next layer is fetched on the side
+    stream while the current one computes; with n slots, n - 1 can be in
+    flight or waiting). The pool never evicts a prefetched layer for a later
+    prefetch, so the nearest layers keep their slots."""
+    seen = []
+    for j in ahead:
+        if len(seen) >= depth:
+            break
+        if j != cur and j not in seen:
+            seen.append(j)
+            nf4s_pool_prefetch(pool, j)
+
+
 class LinearStack:
     """Runs the linear-stack step streamed (slot pool) or resident.
 
@@ -121,10 +138,12 @@ class LinearStack:
     """
 
     def __init__(self, shards: ShardSet, M, targets, lora, r=16, alpha=32, n_slots=2,
-                 mode="streamed", keep_outputs=True, time_calls=None):
+                 mode="streamed", keep_outputs=True, time_calls=None, poison=False):
         """time_calls: optional predicate (direction, n_out, k_in) -> bool; the
         linear calls it accepts are bracketed by timing events on the compute
-        stream and collected in self.timed as (direction, n_out, k_in, start, end)."""
+        stream and collected in self.timed as (direction, n_out, k_in, start, end).
+        poison: the pool overwrites every released slot with NaN block scales
+        (ordered after its last reader), so a read after release would show."""
         assert mode in ("streamed", "resident")
         self.sh = shards
         self.M = M
@@ -164,6 +183,8 @@ class LinearStack:
                                          self.copy.cuda_stream, self.compute.cuda_stream)
             for i, h in enumerate(shards.host):
                 nf4s_pool_set_layer(self.pool, i, h.data_ptr(), nb)
+            if poison:
+                nf4s_pool_set_debug(self.pool, POOL_POISON_ON_RELEASE)
         else:
             self.resident = shards.to_device()
         self.y = {}
@@ -288,31 +309,39 @@ class LinearStack:
         rkey = (lambda i: ("r", i)) if self.keep else (lambda i: ("f", 0))
         refkey = (lambda i: ("ref", i)) if self.keep else (lambda i: ("ref", 0))
         self.compute.wait_stream(torch.cuda.current_stream())
+        fwd, bwd = list(range(L)), list(range(L - 1, -1, -1))
+        # the order in which the step reads the layers: the pool prefetches
+        # along it (the last reference layer prefetches the policy's first)
+        order = (fwd if reference == "separate" else []) + fwd + bwd
+        t = 0
         if reference == "separate":
-            for i in range(L):
-                # the last reference layer prefetches the policy's first
-                base = self._acquire(i, nxt=i + 1 if i + 1 < L else 0)
+            for i in fwd:
+                base = self._acquire(i, order[t + 1:])
                 self._layer_fwd(i, base, inputs, refkey, adapters=False)
                 self._release(i)
-        for i in range(L):
-            base = self._acquire(i, nxt=i + 1 if i + 1 < L else None)
+                t += 1
+        for i in fwd:
+            base = self._acquire(i, order[t + 1:])
             if reference == "fused":
                 self._layer_fwd(i, base, inputs, refkey, adapters=False)
             self._layer_fwd(i, base, inputs, fkey)
             self._release(i)
-        for i in range(L - 1, -1, -1):
-            base = self._acquire(i, nxt=i - 1 if i > 0 else None)
+            t += 1
+        for i in bwd:
+            base = self._acquire(i, order[t + 1:])
             self._layer_fwd(i, base, inputs, rkey)      # recompute
             self._layer_bwd(i, base, inputs, grads)
             self._release(i)
+            t += 1
         torch.cuda.current_stream().wait_stream(self.compute)
 
-    def _acquire(self, i, nxt):
+    def _acquire(self, i, ahead):
+        """Layer i's slot; then prefetch the next n - 1 distinct layers of
+        `ahead` (the rest of the step's reading order)."""
         if self.pool is None:
             return self.resident[i].data_ptr()
         base = nf4s_pool_acquire(self.pool, i)
-        if nxt is not None:
-            nf4s_pool_prefetch(self.pool, nxt)
+        _prefetch_ahead(self.pool, i, ahead, len(self.slots) - 1)
         return base
 
     def _release(self, i):

@@ -184,6 +184,15 @@ def test_prefetch_and_pool_argument_errors():
     with pytest.raises(L.Nf4sError) as e:
         L.nf4s_pool_create([FAKE, FAKE], 1024, 1, 1)         # copy stream == compute stream
     assert e.value.code == L.EINVAL
+    with pytest.raises(L.Nf4sError) as e:
+        L.nf4s_pool_create([FAKE, FAKE + 4096], 0, 1, 2)     # empty slots
+    assert e.value.code == L.ESLOT
+    # slots that share memory would let a copy overwrite a layer another
+    # slot's reader still holds
+    for slots in ([FAKE, FAKE], [FAKE, FAKE + 256], [FAKE + 4096, FAKE + 8192, FAKE + 4352]):
+        with pytest.raises(L.Nf4sError) as e:
+            L.nf4s_pool_create(slots, 1024, 1, 2)
+        assert e.value.code == L.EINVAL, slots
 
 
 def test_packed_activation_bytes():

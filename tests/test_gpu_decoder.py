@@ -652,7 +652,7 @@ def _run_pref(w, shards, mode, schedule, pairs, prompt, n_slots=2, lora=None):
     return out
 
 
-def _check_dpo_against_oracle(w, got, pairs, prompt, beta=0.1):
+def _check_dpo_against_oracle(w, got, pairs, prompt, beta=0.1, fixed_rel=None):
     """The DPO loss compares two nearly equal models (policy = reference plus
     the adapters), so it amplifies the one-unit bf16 flips that both sides
     are entitled to; it is checked through the well-conditioned quantities:
@@ -661,7 +661,11 @@ def _check_dpo_against_oracle(w, got, pairs, prompt, beta=0.1):
     those errors imply (|dL/d delta| <= 1, delta = beta times a signed sum of
     a pair's four log-probabilities, so |dL| <= beta / pairs * sum |d log p|,
     plus fp32 slack), the policy logits and the adapter gradients (2e-2 of
-    the largest, as the plain step)."""
+    the largest, as the plain step). The loss is also held to a bar fixed by
+    the oracle alone: the largest move the 1e-4 log-probability bar allows,
+    beta / pairs * 1e-4 * sum |log p| (plus fp32 slack), and, where the
+    sequences are short enough for the loss to be well conditioned
+    (fixed_rel), to fixed_rel of its value."""
     P = _oracle_params(w)
     cfg = _oracle_cfg(w)
     ids, tg, mask = _pref(w, pairs, prompt)
@@ -674,9 +678,13 @@ def _check_dpo_against_oracle(w, got, pairs, prompt, beta=0.1):
     assert np.all(np.abs(g_lp - o_lp) <= 1e-4 * np.abs(o_lp)), (g_lp, o_lp)
     assert np.all(np.abs(g_lr - o_lr) <= 1e-4 * np.abs(o_lr)), (g_lr, o_lr)
     bound = beta / pairs * float(np.sum(np.abs(g_lp - o_lp) + np.abs(g_lr - o_lr))) + 1e-5 * abs(loss)
+    fixed = beta / pairs * 1e-4 * float(np.sum(np.abs(o_lp) + np.abs(o_lr))) + 1e-5 * abs(loss)
     gloss = float(got["loss"][0])
-    print(f"dpo oracle loss {loss:.6f} gpu {gloss:.6f} bound {bound:.2e}", flush=True)
+    print(f"dpo oracle loss {loss:.6f} gpu {gloss:.6f} bound {bound:.2e} fixed bar {fixed:.2e}", flush=True)
     assert abs(gloss - loss) <= bound, (gloss, loss, bound)
+    assert abs(gloss - loss) <= fixed, (gloss, loss, fixed)
+    if fixed_rel is not None:
+        assert abs(gloss - loss) <= fixed_rel * abs(loss), (gloss, loss, fixed_rel)
     gl = _vals(got["logits"]).reshape(logits.shape)
     assert np.max(np.abs(gl - logits)) / np.max(np.abs(logits)) <= 2e-2
     for key, (dA, dB) in g["lora"].items():
@@ -691,7 +699,7 @@ def test_tiny_dpo_step_matches_oracle():
     require_gpu()
     w = _world("tiny", 4, 70, targets=PROJ)
     got = _run_pref(w, _shards(w), "resident", "separate", pairs=2, prompt=20)
-    _check_dpo_against_oracle(w, got, pairs=2, prompt=20)
+    _check_dpo_against_oracle(w, got, pairs=2, prompt=20, fixed_rel=5e-3)
 
 
 @pytest.fixture(scope="module")

@@ -110,3 +110,22 @@ def test_flipped_nibble_is_detected():
     out = torch.empty((576, 576), dtype=torch.int16, device="cuda")
     L.nf4_dequant(h.to("cuda").data_ptr(), d, out.data_ptr(), stream())
     assert not np.array_equal(host_u16(out), nf4.dequantize_bf16(ref))
+
+
+def test_threshold_ties_bit_exact():
+    """Weights on, one ulp above and one ulp below every NF4 threshold; absmax
+    values whose centred form lands exactly on thresholds of the 256-level
+    table; and absmax values whose mean needs the exact sum (a plain fp64
+    running sum rounds the offset the other way): the device sharder gives the
+    oracle's bytes in every case, and the offset of the last is 1 + 2^-23."""
+    from tests.nf4_cases import nested_ties, nf4_ties, offset_needs_exact_sum
+    for w in (nf4_ties(), nested_ties()[0], offset_needs_exact_sum()):
+        shard, d, status = quantize_on_gpu(w)
+        assert status == 0
+        ref = _compare(w, shard, d)
+        out = torch.empty(w.shape, dtype=torch.int16, device="cuda")
+        L.nf4_dequant(shard.data_ptr(), d, out.data_ptr(), stream())
+        assert np.array_equal(host_u16(out), nf4.dequantize_bf16(ref))
+    _, _, _, offset = sections(quantize_on_gpu(offset_needs_exact_sum())[0],
+                               L.nf4s_tensor_layout(64, 256))
+    assert offset == np.float32(1 + 2.0 ** -23)

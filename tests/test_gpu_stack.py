@@ -9,6 +9,10 @@ layers, on the 135M model (30 layers, hidden 576, B1 S512, LoRA r16 on q/v).
 Stand-in here: the 30 layers' seven projections at those shapes with seeded
 weights and seeded activations/upstream gradients per layer.
 """
+import os
+import subprocess
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -17,7 +21,10 @@ import layer_streamed_nf4_amd as L
 import synth
 from layer_streamed_nf4_amd.stack import PROJ, LinearStack, ShardSet
 from oracle import linear, nf4, stack as ostack
+from tests import stack32b
 from tests.gpu_helpers import bits_to_f32, dev_bf16bits, dev_f32, host_u16, require_gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 pytestmark = pytest.mark.gpu
 
@@ -180,6 +187,115 @@ def test_pool_slots_evict_and_reregister():
         L.nf4s_pool_destroy(pool)
 
 
+def test_pool_refuses_unregistered_layers_and_keeps_reservations():
+    """Layer indices that were never registered (-1 included: it also marks an
+    empty slot) are ESLOT for prefetch, acquire and release, also after a
+    re-registration emptied a slot. A prefetch never evicts a layer an earlier
+    prefetch reserved; an empty slot is filled before a resident layer is
+    evicted; an acquire may take a reserved slot when nothing else is left."""
+    require_gpu()
+    nbytes = 256 * 1024
+    srcs = [torch.full((nbytes,), 7 * (i + 1), dtype=torch.uint8).pin_memory() for i in range(6)]
+    slots = [torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for _ in range(3)]
+    cs = torch.cuda.Stream()
+    comp = torch.cuda.current_stream().cuda_stream
+    pool = L.nf4s_pool_create([t.data_ptr() for t in slots], nbytes, cs.cuda_stream, comp)
+    try:
+        for i in range(5):
+            L.nf4s_pool_set_layer(pool, i, srcs[i].data_ptr(), nbytes)
+        for bad in (-1, 5, 100):
+            for call in (lambda: L.nf4s_pool_prefetch(pool, bad), lambda: L.nf4s_pool_acquire(pool, bad),
+                         lambda: L.nf4s_pool_release(pool, bad)):
+                with pytest.raises(L.Nf4sError) as e:
+                    call()
+                assert e.value.code == L.ESLOT, bad
+
+        def held_value(layer):
+            ptr = L.nf4s_pool_acquire(pool, layer)
+            return next(t for t in slots if t.data_ptr() == ptr).cpu()
+
+        assert torch.equal(held_value(0), srcs[0])
+        L.nf4s_pool_prefetch(pool, 1)
+        L.nf4s_pool_prefetch(pool, 2)                         # pool: 0 held, 1 and 2 reserved
+        assert L.nf4s_pool_stats(pool)[0] == 3
+        L.nf4s_pool_prefetch(pool, 3)                         # no slot to take: nothing copied
+        assert L.nf4s_pool_stats(pool)[0] == 3
+        L.nf4s_pool_release(pool, 0)
+        L.nf4s_pool_prefetch(pool, 3)                         # evicts 0, not a reserved layer
+        assert L.nf4s_pool_stats(pool)[0] == 4
+        for j in (1, 2, 3):
+            assert torch.equal(held_value(j), srcs[j])
+            L.nf4s_pool_release(pool, j)
+        assert L.nf4s_pool_stats(pool)[0] == 4                # all three were resident
+        # re-registering layer 2 empties its slot; the next copy goes there
+        L.nf4s_pool_set_layer(pool, 2, srcs[5].data_ptr(), nbytes)
+        with pytest.raises(L.Nf4sError) as e:
+            L.nf4s_pool_acquire(pool, -1)
+        assert e.value.code == L.ESLOT
+        assert torch.equal(held_value(4), srcs[4])
+        L.nf4s_pool_release(pool, 4)
+        assert torch.equal(held_value(1), srcs[1])            # 1 survived: the empty slot took 4
+        assert torch.equal(held_value(3), srcs[3])
+        assert L.nf4s_pool_stats(pool)[0] == 5
+        # 1 and 3 held, the third slot holds 4: an acquire takes it even when
+        # it is reserved
+        L.nf4s_pool_prefetch(pool, 4)
+        assert torch.equal(held_value(2), srcs[5])
+        assert L.nf4s_pool_stats(pool)[0] == 6
+        for j in (1, 3, 2):
+            L.nf4s_pool_release(pool, j)
+    finally:
+        torch.cuda.synchronize()
+        L.nf4s_pool_destroy(pool)
+
+
+def test_poisoned_release_is_never_read():
+    """With the pool's poison mode on, every released slot is overwritten with
+    NaN block scales on the copy stream, ordered after its free event exactly
+    as the next copy would be. The streamed step still equals the resident one
+    bit for bit (no kernel reads a slot after its release) and every layer is
+    copied twice (a poisoned slot holds no layer)."""
+    require_gpu()
+    nbytes = 4096
+    src = torch.full((nbytes,), 3, dtype=torch.uint8).pin_memory()
+    slots = [torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    cs = torch.cuda.Stream()
+    comp = torch.cuda.current_stream().cuda_stream
+    pool = L.nf4s_pool_create([t.data_ptr() for t in slots], nbytes, cs.cuda_stream, comp)
+    try:
+        L.nf4s_pool_set_debug(pool, L.POOL_POISON_ON_RELEASE)
+        with pytest.raises(L.Nf4sError) as e:
+            L.nf4s_pool_set_debug(pool, 2)
+        assert e.value.code == L.EINVAL
+        L.nf4s_pool_set_layer(pool, 0, src.data_ptr(), nbytes)
+        ptr = L.nf4s_pool_acquire(pool, 0)
+        slot = next(t for t in slots if t.data_ptr() == ptr)
+        assert torch.equal(slot.cpu(), src)
+        L.nf4s_pool_release(pool, 0)
+        torch.cuda.synchronize()
+        assert bool((slot.cpu() == 255).all())
+        assert L.nf4s_pool_acquire(pool, 0) is not None and L.nf4s_pool_stats(pool)[0] == 2
+        L.nf4s_pool_release(pool, 0)
+    finally:
+        torch.cuda.synchronize()
+        L.nf4s_pool_destroy(pool)
+
+
+@pytest.mark.parametrize("n_slots", [2, 3])
+def test_streamed_with_poisoned_releases_equals_resident(world, resident, n_slots):
+    st = LinearStack(world["shards"], M, TARGETS, world["lora"], n_slots=n_slots, mode="streamed",
+                     poison=True)
+    st.step(lambda i, p: world["xd"][i, p], lambda i, p: world["dyd"][i, p])
+    torch.cuda.synchronize()
+    got = {("y",) + k: t.cpu().numpy().copy() for k, t in st.y.items()}
+    got.update({("dx",) + k: t.cpu().numpy().copy() for k, t in st.dx.items()})
+    got.update({("g",) + k: t.cpu().numpy().copy() for k, t in st.grads.items()})
+    copies, _ = st.stats()
+    st.close()
+    _same(got, resident)
+    assert copies == 2 * N_LAYERS
+
+
 def test_pageable_source_is_refused():
     require_gpu()
     src = torch.zeros(4096, dtype=torch.uint8)           # pageable
@@ -250,44 +366,36 @@ def test_32b_layers_preference_streamed_equals_resident():
     streamed through a 2-slot pool give the resident results bit for bit,
     gradients included, in a preference step -- the size at which the pages'
     streamed gradients went silently wrong (gate walkthrough section 2.5,
-    "Fine-Tune 8B Models on 4GB VRAM", "Boundary Conditions List")."""
+    "Fine-Tune 8B Models on 4GB VRAM", "Boundary Conditions List"). Also with
+    every released slot poisoned (NaN block scales written after its free
+    event): no kernel reads a slot after its release."""
     require_gpu()
-    shapes = synth.SHAPES["32b"]
-    n_layers, m = 3, 64
-    g = torch.Generator(device="cuda")
-
-    def weight_fn(i, p):
-        g.manual_seed(synth.weight_seed(i, p))
-        return torch.randn(shapes[p], generator=g, device="cuda") * 0.02
-
-    shards = ShardSet(shapes, n_layers, weight_fn)
-    assert shards.layout.nbytes > 165 * 2**20
-    lora = []
-    for i in range(n_layers):
-        d = {}
-        for p in TARGETS:
-            n, k = shapes[p]
-            g.manual_seed(10_000 + 10 * i + PROJ.index(p))
-            d[p] = (torch.randn((16, k), generator=g, device="cuda") * 0.01,
-                    torch.randn((n, 16), generator=g, device="cuda") * 0.01)
-        lora.append(d)
-    g.manual_seed(77)
-    xs = {p: torch.randn((m, shapes[p][1]), generator=g, device="cuda").to(torch.bfloat16) for p in PROJ}
-    dys = {p: torch.randn((m, shapes[p][0]), generator=g, device="cuda").to(torch.bfloat16) for p in PROJ}
-
-    def run(mode):
-        st = LinearStack(shards, m, TARGETS, lora, n_slots=2, mode=mode)
-        st.step(lambda i, p: xs[p], lambda i, p: dys[p], reference="separate")
-        torch.cuda.synchronize()
-        out = {("y",) + k: t.cpu().numpy().copy() for k, t in st.y.items()}
-        out.update({("dx",) + k: t.cpu().numpy().copy() for k, t in st.dx.items()})
-        out.update({("g",) + k: t.cpu().numpy().copy() for k, t in st.grads.items()})
-        st.close()
-        return out
-
-    a, b = run("streamed"), run("resident")
+    world32 = stack32b.setup()
+    assert world32["shards"].layout.nbytes > 165 * 2**20
+    a, b = stack32b.run(world32, "streamed"), stack32b.run(world32, "resident")
     _same(a, b)
-    for i in range(n_layers):
+    c = stack32b.run(world32, "streamed", poison=True)
+    _same(c, b)
+    for i in range(stack32b.N_LAYERS):
         for p in TARGETS:
             assert np.count_nonzero(a[("g", i, p, "dA")]) > 0
             assert np.count_nonzero(a[("g", i, p, "dB")]) > 0
+
+
+def test_32b_layers_serialized_equals_async(tmp_path):
+    """The same streamed 32B-class preference step in a child process with
+    every kernel and copy serialised (AMD_SERIALIZE_KERNEL=3,
+    AMD_SERIALIZE_COPY=3: no overlap of copy and compute at all) gives the
+    asynchronous run's bits: the overlap changes no value."""
+    require_gpu()
+    out = str(tmp_path / "serial.npz")
+    env = dict(os.environ, AMD_SERIALIZE_KERNEL="3", AMD_SERIALIZE_COPY="3")
+    print("serialised child process", flush=True)
+    r = subprocess.run([sys.executable, "-m", "tests.stack32b", out], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    serial = dict(np.load(out))
+    got = stack32b.run(stack32b.setup(), "streamed")
+    assert set(serial) == {stack32b.key_str(k) for k in got}
+    for k, v in got.items():
+        assert np.array_equal(v.view(np.uint8), serial[stack32b.key_str(k)].view(np.uint8)), k

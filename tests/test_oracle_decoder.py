@@ -292,3 +292,28 @@ def test_dpo_finite_differences(share_prompt):
             arr[idx] = old
             fd = (lp_ - lm_) / (2 * eps)
             assert abs(fd - grad[idx]) <= 1e-8 + 1e-4 * abs(fd), (l, p, idx, fd, grad[idx])
+
+
+def test_slot_aliasing_shows_in_gradients_only():
+    """The pages' slot-aliasing bug ("Fine-Tune 8B Models on 4GB VRAM: Soup's
+    Layer Streaming", failure records: forward exact, gradients silently wrong)
+    planted in the oracle: with two slots, a copy that lands in a slot before
+    its last reader finished hands layer l's backward the weights of layer
+    l - 2 (the layer the backward sweep prefetches into that slot). The
+    forward never sees it, so logits and loss are unchanged; every adapter
+    gradient at or below the first aliased layer moves far beyond the bars
+    the streamed == resident (0.0) and oracle (2e-2) comparisons use."""
+    cfg = _cfg(layers=4)
+    P = _params(cfg)
+    ids, tg = _batch(cfg, B=2, S=12)
+    loss, logits, cache = D.forward(P, ids, tg, cfg)
+    good = D.backward(P, cache, cfg)
+    W_alias = [P.W[l] if l < 2 else P.W[l - 2] for l in range(cfg.layers)]
+    bad = D.backward(D.Params(**{**P.__dict__, "W": W_alias}), cache, cfg)
+    loss2, logits2, _ = D.forward(P, ids, tg, cfg)
+    assert loss2 == loss and np.array_equal(logits2, logits)
+    for (l, p), (dA, dB) in good["lora"].items():
+        bA, bB = bad["lora"][(l, p)]
+        e = max(np.max(np.abs(bA - dA)) / np.max(np.abs(dA)), np.max(np.abs(bB - dB)) / np.max(np.abs(dB)))
+        if l < 3:   # layers 3 and 2 read the wrong weights; the error flows down
+            assert e > 5e-2, (l, p, e)

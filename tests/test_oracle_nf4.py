@@ -217,3 +217,52 @@ def test_payload_formula_matches_page_totals(golden):
     assert round(s8 + emb, 2) == g["shard_set_8b_gb"]["value"]
     params8 = sum(a * b for a, b in synth.SHAPES["8b"].values())
     assert round(per8 / params8, 3) == g["bytes_per_param_approx"]["value"]
+
+
+def test_nf4_ties_at_every_threshold():
+    """Weights that divide exactly onto each NF4 threshold (power-of-two
+    absmax) take the lower code; one ulp above takes the upper code, one ulp
+    below the lower; the exact-rational brute force agrees away from the
+    thresholds."""
+    from tests.nf4_cases import nf4_ties
+    w = nf4_ties()
+    q = nf4.quantize(w)
+    codes = q.codes.reshape(-1, 64)
+    for b in range(codes.shape[0]):
+        kind = b % 4
+        got = codes[b, 1:16].tolist()
+        if kind in (0, 2):        # on the threshold, or one ulp below: the lower code
+            assert got == list(range(15)), (b, got)
+        elif kind == 1:           # one ulp above: the upper code
+            assert got == list(range(1, 16)), (b, got)
+        else:                     # negated thresholds: mirror of the lower code rule
+            assert got == [int(np.searchsorted(tables.midpoints(tables.nf4_table()), -m, "left"))
+                           for m in tables.midpoints(tables.nf4_table())]
+        assert codes[b, 16:31].tolist() == list(range(14, -1, -1))
+
+
+def test_nested_ties_take_the_lower_code():
+    from tests.nf4_cases import nested_ties
+    w, hit = nested_ties()
+    assert len(hit) >= 16
+    q = nf4.quantize(w)
+    assert q.offset == np.float32(1.0) and q.nested.tolist() == [1.0]
+    mids = tables.midpoints(tables.dynamic_table()).astype(np.float64)
+    c = (q.absmax.astype(np.float64) - 1.0)
+    for b, cv in enumerate(c):
+        on = np.nonzero(mids == cv)[0]
+        if on.size:               # exactly on threshold i: code i (the lower level)
+            assert q.q8[b] == on[0], (b, cv)
+    assert sum(np.any(mids == cv) for cv in c) >= 2 * min(len(hit), 127)
+
+
+def test_offset_needs_the_exact_sum():
+    from tests.nf4_cases import offset_needs_exact_sum
+    w = offset_needs_exact_sum()
+    q = nf4.quantize(w)
+    assert q.offset == np.float32(1 + 2.0 ** -23)
+    # a plain running fp64 sum would give the tie, which rounds to 1.0
+    run = 0.0
+    for a in q.absmax.astype(np.float64):
+        run += a
+    assert np.float32(run / 256) == np.float32(1.0)

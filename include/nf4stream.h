@@ -195,6 +195,22 @@ int streamed_linear_fwd(const void* shard_dev, const nf4s_tensor_desc* d, const 
                         int64_t M, uint16_t* y, const float* lora_u, const float* lora_B, int r,
                         float scale, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * streamed_linear_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The same kernels and results, bit for
+ * bit; their scratch (packed x and split partials) lives in a library-owned
+ * device array of NF4S_NOALLOC_SCRATCH_BYTES per GPU, held until the process
+ * ends. Arguments and errors as streamed_linear_fwd, plus EWORKSPACE when
+ * nf4s_workspace_bytes(NF4S_OP_LINEAR_FWD, M, n_out, k_in) exceeds that size
+ * (checked before anything is enqueued; e.g. every 8B projection up to
+ * M = 2048 fits). Allocates nothing. All calls on one GPU share the array:
+ * calls that overlap on one GPU (two streams, two host threads) race.
+ */
+#define NF4S_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int streamed_linear_fwd_noalloc(const void* shard_dev, const nf4s_tensor_desc* d, const uint16_t* x,
+                                int64_t M, uint16_t* y, const float* lora_u, const float* lora_B,
+                                int r, float scale, void* stream);
 
 /*
  * Backward (input gradient only) of the same linear, [G] s4.4 (frozen base:

@@ -32,7 +32,7 @@ EXPORTS = (
     "layer_prefetch", "nf4s_event_create", "nf4s_event_destroy", "nf4s_event_record",
     "nf4s_stream_wait_event", "nf4s_pool_create", "nf4s_pool_destroy", "nf4s_pool_set_layer",
     "nf4s_pool_prefetch", "nf4s_pool_acquire", "nf4s_pool_release", "nf4s_pool_stats",
-    "nf4s_pool_set_debug", "nf4s_packed_activation_bytes", "nf4s_pack_activation", "streamed_linear_fwd_packed",
+    "nf4s_pool_set_debug", "streamed_linear_fwd_noalloc", "nf4s_packed_activation_bytes", "nf4s_pack_activation", "streamed_linear_fwd_packed",
     "streamed_linear_bwd_packed", "dense_linear_fwd_packed", "dense_linear_bwd_packed",
     "nf4s_grouped_workspace_bytes", "streamed_linear_fwd_grouped",
     "nf4s_lora_grouped_workspace_bytes", "lora_fwd_grouped", "lora_bwd_grouped",
@@ -86,6 +86,8 @@ _SIG = {
                                            ctypes.c_int, ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "streamed_linear_bwd": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P, _P,
                                            ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "streamed_linear_fwd_noalloc": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P, _P,
+                                                   ctypes.c_int, ctypes.c_float, _P]),
     "lora_fwd": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, _P, _P, ctypes.c_size_t, _P]),
     "lora_bwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _P, ctypes.c_int, ctypes.c_float,
                                 _P, _P, _P, ctypes.c_int, _P, ctypes.c_size_t, _P]),
@@ -221,6 +223,14 @@ def nf4_dequant(shard, desc, w_bf16, stream=0):
 def streamed_linear_fwd(shard, desc, x, M, y, lora_u, lora_B, r, scale, ws, ws_bytes, stream=0):
     _check(lib().streamed_linear_fwd(shard, ctypes.byref(desc), x, M, y, lora_u, lora_B, r, scale,
                                      ws, ws_bytes, stream))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def streamed_linear_fwd_noalloc(shard, desc, x, M, y, lora_u, lora_B, r, scale, stream=0):
+    _check(lib().streamed_linear_fwd_noalloc(shard, ctypes.byref(desc), x, M, y, lora_u, lora_B, r,
+                                             scale, stream))
 
 
 def streamed_linear_bwd(shard, desc, dy, M, dx, lora_du, lora_A, r, ws, ws_bytes, stream=0):

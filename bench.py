@@ -68,6 +68,25 @@ def flops_per_token(model: str, lm_head: bool, reference: bool = False) -> int:
     return f
 
 
+def executed_flops_per_token(model: str, decoder: bool, reference: bool = False) -> int:
+    """The frozen-linear and lm_head FLOPs the step actually executes (same
+    counting rules as flops_per_token). The decoder's recompute skips the down
+    product (its output h_{i+1} is stored and the backward reads nothing else
+    of it) and the whole last layer (its body is kept from the forward); the
+    linear stack recomputes every projection of every layer."""
+    if not decoder:
+        return flops_per_token(model, False, reference)
+    sh = synth.SHAPES[model]
+    n_layers = synth.N_LAYERS[model]
+    p_lin = sum(a * b for a, b in sh.values())
+    p_down = sh["down"][0] * sh["down"][1]
+    v, h = LM_HEAD[model]
+    f = 2 * p_lin * n_layers + 2 * (p_lin - p_down) * (n_layers - 1) + 2 * p_lin * n_layers + 4 * v * h
+    if reference:
+        f += 2 * p_lin * n_layers + 2 * v * h
+    return f
+
+
 def flop_shares(model: str) -> dict:
     sh = synth.SHAPES[model]
     tot = sum(a * b for a, b in sh.values())
@@ -116,7 +135,9 @@ def profile_gemm(spec: str, reps: int) -> None:
     """Run one fused GEMM shape `fwd:N:K:M` or `bwd:N:K:M` (resident weight)
     `reps` times, then a 64 MiB device copy whose FETCH/WRITE counters give the
     scale of the memory counters. `fwd:N1+N2:K:M` runs the grouped forward of
-    weights of N1 and N2 outputs reading one input. Used under rocprofv3."""
+    weights of N1 and N2 outputs reading one input; `bwd:N1+N2:K:M` the
+    grouped backward (one contraction over both weights, each with its own dy).
+    Used under rocprofv3."""
     import torch
     import layer_streamed_nf4_amd as L
     direction, ns, k, M = spec.split(":")
@@ -139,20 +160,29 @@ def profile_gemm(spec: str, reps: int) -> None:
                              wq.data_ptr(), wq.numel(), s)
     bwd = direction == "bwd"
     n = ns[0]
-    a = torch.randn((M, n if bwd else k), generator=g, device=dev).to(torch.bfloat16)
     outs = [torch.empty((M, k if bwd else n_), dtype=torch.bfloat16, device=dev) for n_ in ns]
     if len(ns) > 1:
-        assert not bwd, "grouped launches are forward only"
-        ws_bytes = L.grouped_workspace_bytes(ns, k, M)
+        ws_bytes = (L.grouped_bwd_workspace_bytes(ns, k, M) if bwd
+                    else L.grouped_workspace_bytes(ns, k, M))
     else:
         op = L.OP_LINEAR_BWD_PACKED if bwd else L.OP_LINEAR_FWD_PACKED
         ws_bytes = L.nf4s_workspace_bytes(op, M, n, k)
     ws = torch.zeros(max(256, ws_bytes), dtype=torch.uint8, device=dev)
-    K = n if bwd else k
-    ap = torch.empty(L.nf4s_packed_activation_bytes(M, K), dtype=torch.uint8, device=dev)
-    L.nf4s_pack_activation(a.data_ptr(), M, K, ap.data_ptr(), ap.numel(), s)
+    # one packed input per weight of a grouped backward (its own dy), else one
+    aps = []
+    for n_ in (ns if bwd else ns[:1]):
+        K = n_ if bwd else k
+        a = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+        ap = torch.empty(L.nf4s_packed_activation_bytes(M, K), dtype=torch.uint8, device=dev)
+        L.nf4s_pack_activation(a.data_ptr(), M, K, ap.data_ptr(), ap.numel(), s)
+        aps.append(ap)
+    ap = aps[0]
     for _ in range(reps):
-        if bwd:
+        if bwd and len(ns) > 1:
+            L.streamed_linear_bwd_grouped(shard.data_ptr(), descs, [x.data_ptr() for x in aps], M,
+                                          outs[0].data_ptr(), [None] * len(ns), [None] * len(ns), 0,
+                                          ws.data_ptr(), ws.numel(), s)
+        elif bwd:
             L.streamed_linear_bwd_packed(shard.data_ptr(), descs[0], ap.data_ptr(), M,
                                          outs[0].data_ptr(), None, None, 0, ws.data_ptr(),
                                          ws.numel(), s)
@@ -173,6 +203,17 @@ def profile_gemm(spec: str, reps: int) -> None:
     print(f"profiled {spec} x{reps}; gemm source {gemm_source_hash()}", flush=True)
 
 
+def _cpu_threads() -> int:
+    """Threads for the oracle's BLAS: the CPUs this process may run on, capped
+    by OMP_NUM_THREADS where the environment sets the machine's share."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
+    except ValueError:
+        pass
+    return max(1, n)
+
+
 def _cpu_baseline(model: str, M: int, targets) -> dict:
     """The oracle, as it stands, on one full layer of the step (dequantise the
     seven tensors, then forward and backward of the seven projections with the
@@ -181,11 +222,7 @@ def _cpu_baseline(model: str, M: int, targets) -> dict:
     import numpy as np
 
     from oracle import nf4 as onf4, stack as ostack
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+    cores = _cpu_threads()
     sh = synth.SHAPES[model]
     q = {p: onf4.quantize(synth.weight(0, p, *sh[p])) for p in ostack.PROJ}
     lora = {p: synth.lora_pair(0, p, *sh[p]) for p in targets}
@@ -219,11 +256,7 @@ def _cpu_baseline_decoder(model: str, batch: int, seq: int, targets, preference=
     import numpy as np
 
     from oracle import decoder as odec, nf4 as onf4
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+    cores = _cpu_threads()
     c = dict(synth.DECODER[model])
     c.pop("tied")
     n_layers = c["layers"]
@@ -273,6 +306,34 @@ def _cpu_baseline_decoder(model: str, batch: int, seq: int, targets, preference=
                       f"step = head + {n_layers} x layer = {t_step:.1f} s"}
 
 
+def _time_sharder(L, torch, sh) -> dict:
+    """nf4_quantize_shard on one gate-shaped tensor (the largest of the layer),
+    HIP events over 5 calls after one warm-up. Algorithmic bytes: the fp32
+    weight read once (4 B/param) and the payload written (0.516 B/param);
+    HBM-bound, offline (gate walkthrough, section 2.1)."""
+    n, k = sh["gate"]
+    dev = "cuda"
+    s = torch.cuda.current_stream().cuda_stream
+    w = torch.randn((n, k), device=dev) * 0.02
+    d = L.nf4s_tensor_layout(n, k)
+    out = torch.empty(d.end, dtype=torch.uint8, device=dev)
+    ws = torch.empty(L.nf4s_workspace_bytes(L.OP_QUANTIZE, 0, n, k), dtype=torch.uint8, device=dev)
+    call = lambda: L.nf4_quantize_shard(w.data_ptr(), L.DTYPE_F32, n, k, out.data_ptr(), d, None,  # noqa: E731
+                                        ws.data_ptr(), ws.numel(), s)
+    call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / 5 * 1e3
+    nbytes = 4 * n * k + L.nf4_shard_bytes(n, k)
+    return {"tensor": f"{n}x{k} fp32", "us": round(us, 1), "bytes": nbytes,
+            "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 3)}
+
+
 def _cpu_model() -> str | None:
     try:
         for line in open("/proc/cpuinfo"):
@@ -310,7 +371,8 @@ def sweep(args) -> None:
     and the overlap efficiency (t_copy + t_compute - t_step) / min(t_copy,
     t_compute), where t_copy is the step's bytes at the same-session pinned
     H2D rate and t_compute the resident step time (the copy hides once
-    t_compute >= t_copy). One JSON line per point."""
+    t_compute >= t_copy). Batch 4 also runs with n = 3..8 slots. One JSON
+    line per point."""
     import torch
 
     import layer_streamed_nf4_amd as L
@@ -394,7 +456,7 @@ def sweep(args) -> None:
 
     for batch in (1, 2, 4, 8, 16):
         point(batch, 2, ("q", "v"))
-    for slots in (4, 8):
+    for slots in (3, 4, 5, 6, 7, 8):
         point(4, slots, ("q", "v"))
     point(4, 4, PROJ)  # the pages' config 4: B4, LoRA on all seven projections, n = 4
 
@@ -630,12 +692,14 @@ def main():
     cs.synchronize()
     h2d_peak = 5 * (256 << 20) / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del host, devb
+    sharder = _time_sharder(L, torch, sh)
 
     tokens = M
     f_tok = flops_per_token(model, lm_head=use_decoder, reference=reference is not None)
     f_lin = flops_per_token(model, lm_head=False, reference=reference is not None)
     value = tokens / dt_s
     step_tflops = f_tok * tokens / dt_s / 1e12
+    f_exec = executed_flops_per_token(model, use_decoder, reference is not None)
     dom_ms = [d for (_, _, d) in durs]
     dom_flops = [2 * M * n * k for (n, k, _) in durs]
     roofline = None
@@ -690,16 +754,22 @@ def main():
         "step_tflops": round(step_tflops, 2),
         "step_frac_of_mfma_peak": round(step_tflops / PEAK_BF16_TFLOPS, 4),
         "flop_per_token": f_tok,
+        "executed_flop_per_token": f_exec,
+        "executed_tflops": round(f_exec * tokens / dt_s / 1e12, 2),
         "lora_flop_per_token": lora_flops_per_token(model, targets),
         "resident": None if dt_r is None else {
             "tok_s": round(tokens / dt_r, 1), "ms_per_step": round(dt_r * 1e3, 3),
             "tflops": round(f_tok * tokens / dt_r / 1e12, 2),
+            "executed_tflops": round(f_exec * tokens / dt_r / 1e12, 2),
             "frac_of_mfma_peak": round(f_tok * tokens / dt_r / 1e12 / PEAK_BF16_TFLOPS, 4),
             "streamed_over_resident_time": round(dt_s / dt_r, 3)},
         "h2d": {"bytes_per_step": int(h2d_bytes), "copies_per_step": copies,
                 "effective_gbs": round(h2d_bytes / dt_s / 1e9, 2),
                 "pinned_peak_gbs_same_session": round(h2d_peak, 2),
                 "host_link_theoretical_gbs": HOST_LINK_GBS,
+                # the step's bytes at the same-session pinned rate over the step time:
+                # the share of the step the host link alone needs
+                "host_link_frac": round(h2d_bytes / (h2d_peak * 1e9) / dt_s, 4),
                 # (t_copy + t_compute - t_step) / min(t_copy, t_compute), with t_copy the
                 # step's bytes at the same-session pinned rate, t_compute the resident step
                 "overlap_efficiency": None if dt_r is None else round(
@@ -709,6 +779,7 @@ def main():
                    "sclk_mhz_after_timed_region": gpu_state["sclk_mhz"],
                    "junction_temperature_c_after_timed_region": gpu_state["temperature_c"]},
         "roofline": roofline,
+        "sharder": sharder,
         "hipblaslt_bf16_same_shape_tflops": round(blas_tflops, 1),
         "context": "pages (NVIDIA, full model incl. attention/lm_head/optimizer): 119.6 tok/s at "
                    "3.32 GB on an RTX 3050 Laptop 4 GB, 113 tok/s on an H100 -- context only",
@@ -722,8 +793,10 @@ def main():
             "flop_per_token": f_lin, "copies_per_step": lin_copies}
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = (_cpu_baseline_decoder(model, batch, seq, targets, reference)
-                               if use_decoder else _cpu_baseline(model, M, targets))
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=_cpu_threads()):
+            out["cpu_baseline"] = (_cpu_baseline_decoder(model, batch, seq, targets, reference)
+                                   if use_decoder else _cpu_baseline(model, M, targets))
     print(json.dumps(out), flush=True)
 
 

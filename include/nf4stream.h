@@ -303,6 +303,36 @@ int streamed_linear_fwd_grouped(const void* shard_dev, const nf4s_tensor_desc* d
                                 float scale, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The gate and up projections of a llama MLP ([G] s2.1: the unmodified layer
+ * body around the streamed linears, SwiGLU between them) as one launch whose
+ * epilogue applies the activation:
+ *   out = bf16( silu(g) * u ),  g = bf16(x.W'_gate^T + s.u_g.B_g^T),
+ *                               u = bf16(x.W'_up^T + s.u_u.B_u^T),
+ * silu(g) * u = g / (1 + e^-g) * u in fp32 -- the same bits as
+ * streamed_linear_fwd_grouped on (gate, up) followed by nf4s_swiglu_fwd, with
+ * half the output bytes and no g, u tensors.
+ *   d_gate, d_up: descriptors of the shard, both width x k_in, width a
+ *              multiple of 64;
+ *   x_packed:  nf4s_pack_activation of bf16 x [M, k_in];
+ *   out:       nullable bf16 [M, width]; out_packed: nullable, the same
+ *              values in fragment order (nf4s_packed_activation_bytes(M,
+ *              width) bytes, 256-B aligned; rows past M are not written),
+ *              the input of the down projection; at least one is given;
+ *   lora_us, lora_Bs: nullable host arrays of 2 device pointers (gate, up),
+ *              as for streamed_linear_fwd_grouped.
+ * Only shapes whose launch needs no split of the contraction are supported
+ * (nf4s_swiglu_fused_supported returns 1; e.g. 8B widths at M >= 512); others
+ * are refused with ESHAPE. No workspace. Errors: EINVAL, ESHAPE, EALIGN,
+ * ETABLE, EKEY, EWORKSPACE (out_packed too small).
+ */
+int nf4s_swiglu_fused_supported(int64_t M, int64_t width, int64_t k_in);
+int streamed_linear_fwd_swiglu(const void* shard_dev, const nf4s_tensor_desc* d_gate,
+                               const nf4s_tensor_desc* d_up, const void* x_packed, int64_t M,
+                               uint16_t* out, void* out_packed, size_t out_packed_bytes,
+                               const float* const* lora_us, const float* const* lora_Bs, int r,
+                               float scale, void* stream);
+
+/*
  * Grouped backward ([G] s2.1 and s4.4: the input gradient of the layer's
  * normed input is the sum over the projections that read it, q, k and v, or
  * gate and up): for n in [1, 3] weights sharing k_in,

@@ -32,7 +32,8 @@ EXPORTS = (
     "layer_prefetch", "nf4s_event_create", "nf4s_event_destroy", "nf4s_event_record",
     "nf4s_stream_wait_event", "nf4s_pool_create", "nf4s_pool_destroy", "nf4s_pool_set_layer",
     "nf4s_pool_prefetch", "nf4s_pool_acquire", "nf4s_pool_release", "nf4s_pool_stats",
-    "nf4s_pool_set_debug", "streamed_linear_fwd_noalloc", "nf4s_packed_activation_bytes", "nf4s_pack_activation", "streamed_linear_fwd_packed",
+    "nf4s_pool_set_debug", "streamed_linear_fwd_noalloc", "nf4s_swiglu_fused_supported",
+    "streamed_linear_fwd_swiglu", "nf4s_packed_activation_bytes", "nf4s_pack_activation", "streamed_linear_fwd_packed",
     "streamed_linear_bwd_packed", "dense_linear_fwd_packed", "dense_linear_bwd_packed",
     "nf4s_grouped_workspace_bytes", "streamed_linear_fwd_grouped",
     "nf4s_lora_grouped_workspace_bytes", "lora_fwd_grouped", "lora_bwd_grouped",
@@ -86,6 +87,10 @@ _SIG = {
                                            ctypes.c_int, ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "streamed_linear_bwd": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P, _P,
                                            ctypes.c_int, _P, ctypes.c_size_t, _P]),
+    "nf4s_swiglu_fused_supported": (ctypes.c_int, [_I64, _I64, _I64]),
+    "streamed_linear_fwd_swiglu": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), ctypes.POINTER(TensorDesc),
+                                                  _P, _I64, _P, _P, ctypes.c_size_t, _P, _P, ctypes.c_int,
+                                                  ctypes.c_float, _P]),
     "streamed_linear_fwd_noalloc": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P, _P,
                                                    ctypes.c_int, ctypes.c_float, _P]),
     "lora_fwd": (ctypes.c_int, [_P, _I64, _I64, _P, ctypes.c_int, _P, _P, ctypes.c_size_t, _P]),
@@ -285,6 +290,18 @@ def streamed_linear_fwd_grouped(shard, descs, x_packed, M, ys, lora_us, lora_Bs,
     _check(lib().streamed_linear_fwd_grouped(shard, darr, n, x_packed, M, _ptr_array(ys),
                                              _ptr_array(lora_us), _ptr_array(lora_Bs), r, scale, ws,
                                              ws_bytes, stream))
+
+
+def nf4s_swiglu_fused_supported(M, width, k_in) -> bool:
+    return bool(lib().nf4s_swiglu_fused_supported(M, width, k_in))
+
+
+def streamed_linear_fwd_swiglu(shard, d_gate, d_up, x_packed, M, out, out_packed, out_packed_bytes,
+                               lora_us, lora_Bs, r, scale, stream=0):
+    """out (and/or out_packed) = bf16(silu(g) * u) of the gate and up projections."""
+    _check(lib().streamed_linear_fwd_swiglu(shard, ctypes.byref(d_gate), ctypes.byref(d_up), x_packed, M,
+                                            out, out_packed, out_packed_bytes, _ptr_array(lora_us),
+                                            _ptr_array(lora_Bs), r, scale, stream))
 
 
 def streamed_linear_fwd_residual(shard, desc, x_packed, M, y, lora_u, lora_B, r, scale, h_in, h_out, ws,

@@ -468,6 +468,63 @@ int streamed_linear_fwd_grouped(const void* shard_dev, const nf4s_tensor_desc* d
   return e == hipSuccess ? NF4S_OK : hip_fail(e, "grouped linear launch");
 }
 
+int nf4s_swiglu_fused_supported(int64_t M, int64_t width, int64_t k_in) {
+  if (M <= 0 || M > kMaxRows || width <= 0 || k_in <= 0 || width % 64 || k_in % 64) return 0;
+  return swiglu_fused_ok(M, width, k_in) ? 1 : 0;
+}
+
+int streamed_linear_fwd_swiglu(const void* shard_dev, const nf4s_tensor_desc* d_gate,
+                               const nf4s_tensor_desc* d_up, const void* x_packed, int64_t M,
+                               uint16_t* out, void* out_packed, size_t out_packed_bytes,
+                               const float* const* lora_us, const float* const* lora_Bs, int r,
+                               float scale, void* stream) {
+  int rc;
+  if ((rc = check_desc(d_gate)) || (rc = check_desc(d_up))) return rc;
+  if (d_gate->n_out != d_up->n_out || d_gate->k_in != d_up->k_in)
+    return fail(NF4S_ESHAPE, "gate %lldx%lld and up %lldx%lld differ", (long long)d_gate->n_out,
+                (long long)d_gate->k_in, (long long)d_up->n_out, (long long)d_up->k_in);
+  const int64_t width = d_gate->n_out, k_in = d_gate->k_in;
+  const int64_t n_outs[2] = {width, width};
+  if ((rc = check_group(2, n_outs, k_in, M))) return rc;
+  if (width % 64)
+    return fail(NF4S_ESHAPE, "width %lld is not a multiple of 64 (whole 64-column tiles)", (long long)width);
+  if (!swiglu_fused_ok(M, width, k_in))
+    return fail(NF4S_ESHAPE,
+                "M=%lld, width %lld, k_in %lld needs a split contraction; the fused SwiGLU launch has "
+                "none (use streamed_linear_fwd_grouped and nf4s_swiglu_fwd)",
+                (long long)M, (long long)width, (long long)k_in);
+  if (!out && !out_packed) return fail(NF4S_EINVAL, "out and out_packed are both NULL");
+  if (out && (rc = check_ptr(out, "out"))) return rc;
+  if (out_packed) {
+    if ((rc = check_ptr(out_packed, "out_packed", 256))) return rc;
+    const size_t need = packed_activation_bytes(M, width);
+    if (out_packed_bytes < need)
+      return fail(NF4S_EWORKSPACE, "out_packed of %zu bytes needed, %zu given", need, out_packed_bytes);
+  }
+  bool any_lora = false;
+  for (int i = 0; i < 2; ++i) {
+    const float* u = lora_us ? lora_us[i] : nullptr;
+    const float* B = lora_Bs ? lora_Bs[i] : nullptr;
+    if ((u == nullptr) != (B == nullptr))
+      return fail(NF4S_EINVAL, "LoRA operands of weight %d must be given together", i);
+    if (u) {
+      any_lora = true;
+      if ((rc = check_ptr(u, "lora_us[i]", 4)) || (rc = check_ptr(B, "lora_Bs[i]", 4))) return rc;
+    }
+  }
+  if (any_lora) {
+    if ((rc = check_rank(r))) return rc;
+    if (!std::isfinite(scale)) return fail(NF4S_EINVAL, "scale is not finite");
+  }
+  if ((rc = check_ptr(shard_dev, "shard_dev", 256))) return rc;
+  if ((rc = check_ptr(x_packed, "x_packed", 256))) return rc;
+  const QPtrs q[2] = {resolve(shard_dev, d_gate), resolve(shard_dev, d_up)};
+  hipError_t e = launch_linear_swiglu_fwd(q, width, k_in, static_cast<const uint8_t*>(x_packed), M, out,
+                                          static_cast<uint8_t*>(out_packed), lora_us, lora_Bs,
+                                          any_lora ? r : 0, scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4S_OK : hip_fail(e, "swiglu linear launch");
+}
+
 static int check_bwd_group(int n, const int64_t* n_outs, int64_t k_in, int64_t M) {
   if (n < 1 || n > GEMM_MAX_SEG)
     return fail(NF4S_EINVAL, "group of %d weights (1..%d allowed)", n, GEMM_MAX_SEG);

@@ -88,6 +88,15 @@ hipError_t launch_linear_fwd_residual(const QPtrs& q, int64_t n_out, int64_t k_i
                                       const float* h_in, float* h_out, void* part_ws, hipStream_t s);
 // Forward of nseg (<= GEMM_MAX_SEG) NF4 linears reading the same packed
 // activation, in one launch (lora_us / lora_Bs entries may be null).
+// gate + up forward with the SwiGLU epilogue: out = bf16(silu(g) * u) for
+// g, u the two weights' bf16 outputs (q[0] gate, q[1] up, both width x k_in);
+// out and out_packed (fragment order) nullable. swiglu_fused_ok: the launch
+// needs no split of the contraction (the only case it supports).
+bool swiglu_fused_ok(int64_t M, int64_t width, int64_t k_in);
+hipError_t launch_linear_swiglu_fwd(const QPtrs* q, int64_t width, int64_t k_in, const uint8_t* x_packed,
+                                    int64_t M, uint16_t* out, uint8_t* out_packed,
+                                    const float* const* lora_us, const float* const* lora_Bs, int r,
+                                    float scale, hipStream_t s);
 hipError_t launch_linear_grouped_fwd(const QPtrs* q, int nseg, const int64_t* n_outs, int64_t k_in,
                                      const uint8_t* x_packed, int64_t M, uint16_t* const* ys,
                                      const float* const* lora_us, const float* const* lora_Bs,

@@ -897,7 +897,7 @@ __global__ __launch_bounds__(256) void k_swiglu_fwd(const uint16_t* __restrict__
     load8_bf16(g + e.m * W + e.c, gv);
     load8_bf16(u + e.m * W + e.c, uv);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = gv[i] / (1.0f + __expf(-gv[i])) * uv[i];
+    for (int i = 0; i < 8; ++i) o[i] = swiglu_val(gv[i], uv[i]);
   }
   ew_store(e, T, W, out, packed, stage, o);
 }

@@ -18,6 +18,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// SwiGLU of one element: silu(g) * u = g / (1 + e^-g) * u in fp32 (the
+// decoder's MLP activation), the quotient as g times the hardware reciprocal
+// (v_rcp_f32, within 1 ulp) -- one definition for the elementwise kernel and
+// the GEMM epilogue that fuses it, so both give the same bits.
+__device__ __forceinline__ float swiglu_val(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // Block scale: a' = fp32(fp32(C8[q8] * nested) + offset), two separate
 // roundings (never a fused multiply-add).
 __device__ __forceinline__ float decode_scale(float c8v, float nested, float offset) {

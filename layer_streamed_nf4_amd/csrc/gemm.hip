@@ -48,7 +48,7 @@
 // 16 KB of decoded stores, against 1024 MFMA cycles per SIMD.
 // LDS rows are padded to 144 B so the 16-byte fragment reads of 8 consecutive
 // lanes cover all 32 banks; in the backward orientation the 16-byte chunks of
-// a column are XOR-swizzled by the column's 8-group so the transposing stores
+// a column are XOR-swizzled by the column's 16-group so the transposing stores
 // of a row of lanes spread over the banks. When the output has too few tiles
 // to occupy the chip, the contraction is split; each split writes fp32
 // partials and a second kernel sums them in split order (deterministic, no
@@ -119,6 +119,8 @@ struct GemmArgs {
   float scale;
   int nseg;             // weights in the launch (1 unless a grouped forward)
   GemmSeg seg[GEMM_MAX_SEG];
+  uint8_t* out_packed;  // SwiGLU epilogue: its output again in fragment order (nullable)
+  int xcd_pairs;        // backward: deal the tiles of a (row tile, split) pair to shared XCDs
 };
 
 // A contraction step covers [k0, k0 + 64). The packed activation is zero past
@@ -207,8 +209,20 @@ __device__ __forceinline__ void load_b(const GemmArgs& g, const WLanes<false>& L
   rb.nest = g.nested[blk >> 8];
 }
 
-// Backward: producer thread pt owns weight rows k0 + 4*(pt/16) + i (i < 4) and
-// output columns n0 + 8*(pt%16) + j (j < 8): four packed words. The 128
+// Backward patch of producer thread pt: output-column group m (columns
+// 8m .. 8m+7 of the tile) and contraction group kg (rows 4kg .. 4kg+3 of the
+// step). Lane bit 0 is kg's bit 0, lane bits 1-3 are m's bits 1-3, lane bit 4
+// is m's bit 0, lane bit 5 is kg's bit 1 and the wave gives kg's bits 2-3, so
+// every 16 consecutive lanes hold 8 column groups of distinct m/2, each at
+// both halves of a 16-byte LDS chunk: with the XOR by col/16 below, the
+// 8-byte stores of any 16 (or 32) consecutive lanes hit distinct banks. For a
+// fixed row the lanes still cover 16 consecutive column groups (64
+// contiguous bytes of packed codes).
+__device__ __forceinline__ int bwd_m(int pt) { return (((pt >> 1) & 7) << 1) | ((pt >> 4) & 1); }
+__device__ __forceinline__ int bwd_kg(int pt) { return (pt & 1) | (((pt >> 5) & 1) << 1) | ((pt >> 6) << 2); }
+
+// Backward: producer thread pt owns weight rows k0 + 4*bwd_kg(pt) + i (i < 4)
+// and output columns n0 + 8*bwd_m(pt) + j (j < 8): four packed words. The 128
 // block scales of a step (64 rows x 2 column blocks of 64) are loaded and
 // decoded once, by producer threads 0..127 (row pt/2, column block pt%2),
 // and shared through LDS; a scale is 0 for a row past the contraction or a
@@ -233,12 +247,12 @@ struct BRegs<true> {
 __device__ __forceinline__ WLanes<true> w_lanes(const GemmArgs& g, int64_t n0, int pt,
                                                 WLanes<true>*) {
   WLanes<true> L;
-  int64_t col = n0 + 8 * (pt & 15);
+  int64_t col = n0 + 8 * bwd_m(pt);
   L.cvalid = col < g.k_in;
   col = L.cvalid ? col : g.k_in - 8;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t row = 4 * (pt >> 4) + i;  // relative to the step's start
+    const int64_t row = 4 * bwd_kg(pt) + i;  // relative to the step's start
     L.woff[i] = (uint32_t)((row * g.k_in + col) / 2);
   }
   L.col = (uint32_t)col;
@@ -258,7 +272,7 @@ __device__ __forceinline__ void load_b(const GemmArgs& g, const WLanes<true>& L,
   } else {  // the last step of a contraction that is not a multiple of 64
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t row = s.k0 + 4 * (pt >> 4) + i;
+      const int64_t row = s.k0 + 4 * bwd_kg(pt) + i;
       const int64_t e = (row < g.Kc ? row : g.Kc - 1) * g.k_in + L.col;  // code index
       rb.w[i] = *reinterpret_cast<const uint32_t*>(g.packed + e / 2);
     }
@@ -339,9 +353,15 @@ __device__ __forceinline__ void finish_stage(uint16_t* Bs, const BRegs<false>& r
 }
 
 // Backward LDS layout: stage[col][k] with the 16-byte chunk k/8 of column col
-// stored at chunk (k/8) ^ ((col/8) % 8).
+// stored at chunk (k/8) ^ ((col/16) % 8). A 144-byte row puts column col's
+// chunk c on 16-byte bank group (9 col + c) mod 16 of the 64 banks, so the
+// fragment reads (16 consecutive columns, one chunk: the XOR term constant)
+// cover all 16 groups; and the decode's 8-byte stores of a half-wave (columns
+// 8m + c for m = 0..15, two halves of one chunk) see m/2 through the XOR, so
+// the even m and the odd m each take 8 different chunks: 32 different 8-byte
+// slots. (The XOR by col/8 used before mapped m and m + 8 to one slot.)
 __device__ __forceinline__ int bwd_swizzle_off(int col, int k) {
-  return ((((k >> 3) ^ (col >> 3)) & 7) << 3) | (k & 7);
+  return ((((k >> 3) ^ (col >> 4)) & 7) << 3) | (k & 7);
 }
 
 // Also decodes and publishes the thread's block scale (scale loaders), for
@@ -365,8 +385,8 @@ __device__ __forceinline__ void prep_reads(const BRegs<true>& rb, const PairTab&
 // here, in the bf16 pairing.
 __device__ __forceinline__ void finish_stage(uint16_t* Bs, const BRegs<true>&, const Prep<1>& pp,
                                              const float* sc, int pt) {
-  const int r0 = 4 * (pt >> 4);
-  const float4 a4 = *reinterpret_cast<const float4*>(sc + ((pt & 15) >> 3) * 64 + r0);
+  const int r0 = 4 * bwd_kg(pt);
+  const float4 a4 = *reinterpret_cast<const float4*>(sc + (bwd_m(pt) >> 3) * 64 + r0);
   const float a[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -376,7 +396,7 @@ __device__ __forceinline__ void finish_stage(uint16_t* Bs, const BRegs<true>&, c
       v0[i] = __fmul_rn(pp.v[q * 4 + i].x, a[i]);
       v1[i] = __fmul_rn(pp.v[q * 4 + i].y, a[i]);
     }
-    const int cb = 8 * (pt & 15) + 2 * q;
+    const int cb = 8 * bwd_m(pt) + 2 * q;
     uint2 p0, p1;
     p0.x = pack_bf16x2(v0[0], v0[1]);
     p0.y = pack_bf16x2(v0[2], v0[3]);
@@ -437,7 +457,7 @@ __device__ __forceinline__ void finish_dense(uint16_t* Bs, const DRegs& rb, int 
 __device__ __forceinline__ DLanes<true> d_lanes(const GemmArgs& g, int64_t n0, int pt,
                                                 DLanes<true>*) {
   DLanes<true> L;
-  const int64_t col = n0 + 8 * (pt & 15);
+  const int64_t col = n0 + 8 * bwd_m(pt);
   L.cvalid = col < g.k_in;
   L.col = L.cvalid ? col : g.k_in - 8;
   return L;
@@ -447,7 +467,7 @@ __device__ __forceinline__ void load_d(const GemmArgs& g, const DLanes<true>& L,
                                        DRegs& rb) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t row = s.k0 + 4 * (pt >> 4) + i;
+    const int64_t row = s.k0 + 4 * bwd_kg(pt) + i;
     const bool ok = L.cvalid && row < g.Kc;
     const u32x4 v = *reinterpret_cast<const u32x4*>(g.wd + (ok ? row : 0) * g.k_in + L.col);
     rb.w[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
@@ -457,11 +477,11 @@ __device__ __forceinline__ void load_d(const GemmArgs& g, const DLanes<true>& L,
 // Word q of row i holds columns 2q (low half) and 2q+1 (high half); column c
 // of the patch goes to LDS as its four contraction values r0..r0+3.
 __device__ __forceinline__ void finish_dense(uint16_t* Bs, const DRegs& rb, int pt, DLanes<true>*) {
-  const int r0 = 4 * (pt >> 4);
+  const int r0 = 4 * bwd_kg(pt);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const uint32_t w0 = rb.w[0][q], w1 = rb.w[1][q], w2 = rb.w[2][q], w3 = rb.w[3][q];
-    const int cb = 8 * (pt & 15) + 2 * q;
+    const int cb = 8 * bwd_m(pt) + 2 * q;
     uint2 p0, p1;
     p0.x = (w0 & 0xFFFFu) | (w1 << 16);
     p0.y = (w2 & 0xFFFFu) | (w3 << 16);
@@ -504,11 +524,37 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
   // lm_head grid spans many waves, so there ids are mapped to put all row
   // tiles of a column tile on one XCD at the same time (ids ct%8 + 8*rt in a
   // block of 8*R ids) and each weight tile leaves HBM once.
+  // The NF4 backward reads a different activation block per (row tile,
+  // split) pair -- the dy rows of the tile over the split's share of the
+  // contraction, e.g. 3.7 MB at the grouped gate+up backward -- and every
+  // column tile of the pair reads all of it. Dealt in launch order, each XCD
+  // would hold tiles of every pair and fetch all their blocks (8 x 29 MB);
+  // instead the ids are mapped so that a pair's column tiles share XCDs: with
+  // P pairs dividing or divided by 8, id 8 s + x (x the XCD) is pair
+  // x / G + 8 (s / C') and column tile (s % C') G + x % G, G = max(1, 8 / P)
+  // XCDs per pair, C' = C / G tiles per XCD (used when G divides C). The
+  // host asks for it when the blocks together exceed two L2s: where they fit
+  // the launch order is faster (measured: 6% slower q+k+v backward at M =
+  // 512 with the mapping, 4-6% faster gate+up backward).
   const int C = (int)gridDim.x, R = (int)gridDim.y;
   const int id = (int)blockIdx.x + C * (int)blockIdx.y;
   const int full = C / 8 * 8;
-  int ct, rt;
-  if (!DENSE) {
+  int ct, rt, zz = (int)blockIdx.z;
+  if (!DENSE && BWD && ga.xcd_pairs) {
+    const int P = R * (int)gridDim.z;
+    const int G = P >= 8 ? 1 : 8 / P;
+    const int flat = id + C * R * (int)blockIdx.z;
+    if ((P % 8 == 0 || 8 % P == 0) && C % G == 0) {
+      const int x = flat % 8, sl = flat / 8, cg = C / G;
+      const int pair = x / G + 8 * (sl / cg);
+      ct = (sl % cg) * G + x % G;
+      rt = pair % R;
+      zz = pair / R;
+    } else {
+      ct = (int)blockIdx.x;
+      rt = (int)blockIdx.y;
+    }
+  } else if (!DENSE) {
     ct = (int)blockIdx.x;
     rt = (int)blockIdx.y;
   } else if (id < full * R) {
@@ -525,7 +571,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
   int sgi = 0;
 #pragma unroll
   for (int q = 1; q < GEMM_MAX_SEG; ++q)
-    if (q < ga.nseg && (BWD ? (int)blockIdx.z >= ga.seg[q].z0 : ct >= ga.seg[q].tile0)) sgi = q;
+    if (q < ga.nseg && (BWD ? zz >= ga.seg[q].z0 : ct >= ga.seg[q].tile0)) sgi = q;
   GemmArgs g = ga;
   g.packed = ga.seg[sgi].packed;
   g.q8 = ga.seg[sgi].q8;
@@ -555,7 +601,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm(GemmArgs ga, Tables tab) {
 
   const int64_t n0 = (int64_t)(ct - ga.seg[sgi].tile0) * BN;
   const int64_t m0 = (int64_t)rt * BM;
-  const int zpart = blockIdx.z;                         // the partial this workgroup writes
+  const int zpart = zz;                                 // the partial this workgroup writes
   const int split = zpart - (BWD ? ga.seg[sgi].z0 : 0);  // its split of the weight's contraction
   const int64_t kb = split * g.kc_chunk;
   const int64_t ke = (kb + g.kc_chunk < g.Kc) ? kb + g.kc_chunk : g.Kc;
@@ -900,18 +946,28 @@ struct FSlot {
   float nest;  // nested scale of that block
 };
 
+// SWIGLU: the launch holds the gate (weight 0) and up (weight 1) projections of
+// one MLP; column tile ct covers gate rows and up rows 64 ct .. 64 ct + 63
+// (waves 0-1 decode the gate rows into tile columns 0-63, waves 2-3 the up
+// rows into columns 64-127), and the epilogue writes silu(g) * u of the two
+// bf16-rounded results instead of g and u.
+template <bool SWIGLU>
 __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables tab) {
   const int ct = (int)blockIdx.x;
   int sgi = 0;
+  if constexpr (SWIGLU) {
+    sgi = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 7);  // the weight this wave decodes
+  } else {
 #pragma unroll
-  for (int q = 1; q < GEMM_MAX_SEG; ++q)
-    if (q < ga.nseg && ct >= ga.seg[q].tile0) sgi = q;
+    for (int q = 1; q < GEMM_MAX_SEG; ++q)
+      if (q < ga.nseg && ct >= ga.seg[q].tile0) sgi = q;
+  }
   const uint8_t* const packed = ga.seg[sgi].packed;
   const uint8_t* const q8 = ga.seg[sgi].q8;
   const float* const nested = ga.seg[sgi].nested;
   const float off = ga.seg[sgi].offset[0];
   const int64_t n_out = ga.seg[sgi].n_out;
-  const int64_t n0 = (int64_t)(ct - ga.seg[sgi].tile0) * BN;
+  const int64_t n0 = SWIGLU ? (int64_t)ct * (BN / 2) : (int64_t)(ct - ga.seg[sgi].tile0) * BN;
   const int64_t m0 = (int64_t)blockIdx.y * FBM;
   const int split = blockIdx.z;
   const int64_t M = ga.M, k_in = ga.k_in;
@@ -950,9 +1006,10 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables ta
     return (int)(((kb + (int64_t)kc * BK) / 16) * FRAG_BYTES);
   };
 
-  // weights: thread t owns row n0 + t/2 (clamped; scale forced to 0 past
-  // n_out) and the contraction half t%2 of every step
-  int64_t wrow = n0 + (t >> 1);
+  // weights: thread t owns row n0 + t/2 (SWIGLU: n0 + (t/2) % 64 of its
+  // wave's weight; clamped, scale forced to 0 past n_out) and the contraction
+  // half t%2 of every step
+  int64_t wrow = n0 + (SWIGLU ? ((t >> 1) & (BN / 2 - 1)) : (t >> 1));
   const bool valid = wrow < n_out;
   wrow = valid ? wrow : n_out - 1;
   const __amdgpu_buffer_rsrc_t wr =
@@ -1090,10 +1147,15 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables ta
   if (s < nk) step(s, s % FNST, A0, sa);
 
   // LoRA term on the matrix cores, in chunks of 16 over the rank (split 0):
-  // + u[m, :] . (s * B[n, :])
-  if (ga.seg[sgi].lora_l != nullptr && split == 0) {
-    const float* const lu = ga.seg[sgi].lora_l;
-    const float* const lb = ga.seg[sgi].lora_r;
+  // + u[m, :] . (s * B[n, :]); SWIGLU: gate's adapter on column tiles 0-1,
+  // up's on 2-3
+  for (int lw = 0; lw < (SWIGLU ? 2 : 1); ++lw) {
+    const int ls = SWIGLU ? lw : sgi;
+    if (ga.seg[ls].lora_l == nullptr || split != 0) continue;
+    const float* const lu = ga.seg[ls].lora_l;
+    const float* const lb = ga.seg[ls].lora_r;
+    const int64_t ln_out = ga.seg[ls].n_out;
+    const int64_t ln0 = SWIGLU ? (int64_t)ct * (BN / 2) : n0;
     for (int r0 = 0; r0 < ga.r; r0 += 16) {
       bf16x8_t fa[4], fb[4];
 #pragma unroll
@@ -1109,12 +1171,14 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables ta
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int64_t col = n0 + j * 32 + lrow;
+        // SWIGLU: tile column j*32 + lrow is column (j%2)*32 + lrow of weight j/2
+        const int64_t col = ln0 + (SWIGLU ? (j & 1) : j) * 32 + lrow;
+        const bool mine = !SWIGLU || (j >> 1) == lw;
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int rr = r0 + lk + e;
-          v[e] = (col < n_out && rr < ga.r) ? ga.scale * lb[col * ga.r + rr] : 0.0f;
+          v[e] = (mine && col < ln_out && rr < ga.r) ? ga.scale * lb[col * ga.r + rr] : 0.0f;
         }
         fb[j] = f32x8_to_bf16(v);
       }
@@ -1122,7 +1186,8 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables ta
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+          if (!SWIGLU || (j >> 1) == lw)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
   }
 
@@ -1132,6 +1197,59 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables ta
   // register r of lane l holds output row l%32 and column 8*(r/4) + 4*(l/32)
   // + r%4 of its 32x32 tile: registers 4q..4q+3 are four adjacent columns,
   // one 8-byte LDS store.
+  if constexpr (SWIGLU) {
+    // tile columns c and 64 + c are gate and up column n0 + c (accumulator
+    // tiles j and j + 2): round both to bf16 as the unfused launch stores
+    // them, then silu(g) * u as the elementwise kernel computes it; the 512 x
+    // 64 result leaves row-major and, when asked, in fragment order
+    constexpr int OS = BN / 2 + 8;  // bf16 per LDS row, all 512 rows at once
+    uint16_t* const ot = reinterpret_cast<uint16_t*>(smem);
+    auto bf = [](float x) { return __uint_as_float(pack_bf16x2(x, 0.0f) << 16); };
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = wave * 128 + i * 32 + lrow;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float sv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sv[e] = swiglu_val(bf(acc[i][j][4 * q + e]), bf(acc[i][j + 2][4 * q + e]));
+          uint2 v;
+          v.x = pack_bf16x2(sv[0], sv[1]);
+          v.y = pack_bf16x2(sv[2], sv[3]);
+          *reinterpret_cast<uint2*>(ot + row * OS + j * 32 + 8 * q + 4 * (lane >> 5)) = v;
+        }
+      }
+    __syncthreads();
+    uint16_t* const out = ga.seg[0].out;
+    const int64_t width = ga.seg[0].n_out;
+#pragma unroll
+    for (int it = 0; it < FBM * (BN / 2) / 8 / FTHREADS; ++it) {
+      const int q = it * FTHREADS + t;
+      const int row = q / (BN / 16), c8 = q % (BN / 16);
+      const int64_t grow = m0 + row, gcol = n0 + 8 * c8;
+      if (out && grow < M && gcol < width)
+        *reinterpret_cast<u32x4*>(out + grow * width + gcol) = *reinterpret_cast<const u32x4*>(ot + row * OS + 8 * c8);
+    }
+    if (ga.out_packed) {
+      // fragment (32-row block b, 16-wide block s) of the tile: lane l holds
+      // row 32 b + l%32, columns 16 s + 8 (l/32) .. + 8
+      const int64_t kbw = (width + 63) / 64 * 4;
+#pragma unroll
+      for (int it = 0; it < FBM * (BN / 2) / 8 / FTHREADS; ++it) {
+        const int q = it * FTHREADS + t;
+        const int f = q >> 6, l = q & 63;
+        const int row = 32 * (f >> 2) + (l & 31), col = 16 * (f & 3) + 8 * (l >> 5);
+        const int64_t grow = m0 + row, gcol = n0 + col;
+        if (grow < M && gcol < width)
+          *reinterpret_cast<u32x4*>(ga.out_packed + frag_offset(grow, gcol, kbw)) =
+              *reinterpret_cast<const u32x4*>(ot + row * OS + col);
+      }
+    }
+    return;
+  }
   constexpr int OS = BN + 8;  // bf16 per LDS row; 256 rows (two waves) per pass
   uint16_t* const ot = reinterpret_cast<uint16_t*>(smem);
   uint16_t* const out = ga.seg[sgi].out;
@@ -1219,6 +1337,10 @@ __global__ __launch_bounds__(256) void k_split_sum(SumSegs sg, int splits) {
 
 
 static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// A backward's activation blocks are kept on shared XCDs (k_gemm's tile
+// mapping) when all of them together exceed two 4 MB L2s.
+constexpr int64_t kXcdPairBytes = 8ll << 20;
 
 static GemmPlan plan_tiles(int64_t M, const int64_t* n_cols, int nseg, int64_t k_contract, int bm) {
   GemmPlan p;
@@ -1325,11 +1447,12 @@ static hipError_t launch_gemm(bool backward, const QPtrs* q, int nseg, const uin
   }
   const dim3 grid((unsigned)tile0, (unsigned)((M + p.bm - 1) / p.bm), (unsigned)p.splits);
   const bool split = p.splits > 1;
+  g.xcd_pairs = backward && wd == nullptr && 2 * M * g.Kc > kXcdPairBytes;
   const Tables& tab = host_tables();
   // forward NF4 without a split: k_gemm_fwd; everything else: k_gemm
 #define NF4S_GEMM(B_, S_, D_) hipLaunchKernelGGL((k_gemm<B_, S_, D_>), grid, dim3(THREADS), 0, s, g, tab)
   if (fwd_nf4 && p.bm == FBM) {
-    hipLaunchKernelGGL(k_gemm_fwd, grid, dim3(FTHREADS), 0, s, g, tab);
+    hipLaunchKernelGGL(k_gemm_fwd<false>, grid, dim3(FTHREADS), 0, s, g, tab);
   } else if (wd == nullptr) {
     if (backward && split) NF4S_GEMM(true, true, false);
     else if (backward) NF4S_GEMM(true, false, false);
@@ -1373,6 +1496,48 @@ hipError_t launch_linear_grouped_fwd(const QPtrs* q, int nseg, const int64_t* n_
                                      int r, float scale, void* part_ws, hipStream_t s) {
   return launch_gemm(false, q, nseg, nullptr, n_outs, k_in, x_packed, M, ys, lora_us, lora_Bs, r,
                      scale, part_ws, s);
+}
+
+// The gate + up forward with the SwiGLU epilogue runs on k_gemm_fwd<true>,
+// which has no split path: it is planned only where the grid of 512-row
+// tiles of 64 gate and 64 up columns needs no split by plan_tiles' rule.
+bool swiglu_fused_ok(int64_t M, int64_t width, int64_t k_in) {
+  const int64_t tiles = ((M + FBM - 1) / FBM) * ((width + BN / 2 - 1) / (BN / 2));
+  const int64_t nk = (k_in + BK - 1) / BK;
+  return tiles >= 192 || nk / 2 < 8;
+}
+
+hipError_t launch_linear_swiglu_fwd(const QPtrs* q, int64_t width, int64_t k_in, const uint8_t* x_packed,
+                                    int64_t M, uint16_t* out, uint8_t* out_packed,
+                                    const float* const* lora_us, const float* const* lora_Bs, int r,
+                                    float scale, hipStream_t s) {
+  GemmArgs g = {};
+  g.M = M;
+  g.k_in = k_in;
+  g.Kc = k_in;
+  g.Nc = width;
+  g.n_out = width;
+  g.afrag = x_packed;
+  g.kblocks = (k_in + BK - 1) / BK * (BK / 16);
+  g.kc_chunk = (k_in + BK - 1) / BK * BK;
+  g.r = r;
+  g.scale = scale;
+  g.nseg = 2;
+  g.out_packed = out_packed;
+  for (int i = 0; i < 2; ++i) {
+    GemmSeg& sg = g.seg[i];
+    sg.packed = q[i].packed;
+    sg.q8 = q[i].q8;
+    sg.nested = q[i].nested;
+    sg.offset = q[i].offset;
+    sg.out = out;
+    sg.lora_l = lora_us ? lora_us[i] : nullptr;
+    sg.lora_r = lora_Bs ? lora_Bs[i] : nullptr;
+    sg.n_out = width;
+  }
+  const dim3 grid((unsigned)((width + BN / 2 - 1) / (BN / 2)), (unsigned)((M + FBM - 1) / FBM), 1u);
+  hipLaunchKernelGGL(k_gemm_fwd<true>, grid, dim3(FTHREADS), 0, s, g, host_tables());
+  return hipGetLastError();
 }
 
 // Splits of a grouped backward: split j's contraction into S_j chunks of c
@@ -1442,6 +1607,9 @@ hipError_t launch_linear_grouped_bwd(const QPtrs* q, int n, const int64_t* n_out
     z0 += bp.splits[j];
   }
   const dim3 grid((unsigned)((k_in + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)bp.total);
+  int64_t a_bytes = 0;
+  for (int j = 0; j < n; ++j) a_bytes += 2 * M * n_outs[j];
+  g.xcd_pairs = a_bytes > kXcdPairBytes;
   const Tables& tab = host_tables();
   if (bp.total > 1) hipLaunchKernelGGL((k_gemm<true, true, false>), grid, dim3(THREADS), 0, s, g, tab);
   else hipLaunchKernelGGL((k_gemm<true, false, false>), grid, dim3(THREADS), 0, s, g, tab);

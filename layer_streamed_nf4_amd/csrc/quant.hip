@@ -6,8 +6,9 @@
 // absmax per 256 blocks and one offset; section 2.3: the result is byte-for-byte
 // deterministic. Three passes, all with fixed reduction orders:
 //   1. per 64-block absmax, NF4 codes, nibble packing (16 lanes per block);
-//   2. the offset = mean of the absmax, summed exactly (double-double, one
-//      workgroup, fixed tree) then divided once in fp64 and rounded to fp32;
+//   2. the offset = mean of the absmax, summed exactly (double-double, fixed
+//      chunks over many workgroups then a fixed tree over their partials)
+//      then divided once in fp64 and rounded to fp32;
 //   3. per 256-block nested absmax of (absmax - offset) and the 8-bit codes.
 #include "common.h"
 #include "device.h"
@@ -92,19 +93,24 @@ __device__ __forceinline__ void dd_add(double& hi, double& lo, double xhi, doubl
   lo = e - (hi - s);
 }
 
-constexpr int kSumThreads = 1024;
+// The offset sum in two fixed-order passes: workgroup g adds the contiguous
+// chunk [g*chunk, (g+1)*chunk) of the absmax (each thread a strided subset,
+// then a fixed tree over the workgroup), and one workgroup adds the partials
+// in a fixed tree and divides once. The partition is a function of nb only,
+// so the result is the same on every run; every addition is double-double.
+constexpr int kPartThreads = 256;
+constexpr int kFinalThreads = 1024;
+constexpr int64_t kChunk = 4096;          // absmax values per first-pass workgroup
+constexpr int kMaxParts = kFinalThreads;  // first-pass workgroups at most
 
-__global__ __launch_bounds__(kSumThreads) void k_offset(const float* __restrict__ absmax,
-                                                        int64_t nb, float* __restrict__ offset) {
-  __shared__ double s_hi[kSumThreads];
-  __shared__ double s_lo[kSumThreads];
-  const int t = threadIdx.x;
-  double hi = 0.0, lo = 0.0;
-  for (int64_t i = t; i < nb; i += kSumThreads) dd_add(hi, lo, (double)absmax[i], 0.0);
-  s_hi[t] = hi;
-  s_lo[t] = lo;
-  __syncthreads();
-  for (int half = kSumThreads / 2; half >= 1; half >>= 1) {
+int64_t offset_parts(int64_t nb) {
+  int64_t g = (nb + kChunk - 1) / kChunk;
+  return g < 1 ? 1 : (g > kMaxParts ? kMaxParts : g);
+}
+
+template <int T>
+__device__ __forceinline__ void dd_tree(double* s_hi, double* s_lo, int t) {
+  for (int half = T / 2; half >= 1; half >>= 1) {
     if (t < half) {
       double h = s_hi[t], l = s_lo[t];
       dd_add(h, l, s_hi[t + half], s_lo[t + half]);
@@ -113,6 +119,36 @@ __global__ __launch_bounds__(kSumThreads) void k_offset(const float* __restrict_
     }
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(kPartThreads) void k_offset_part(const float* __restrict__ absmax,
+                                                               int64_t nb, int64_t chunk,
+                                                               double2* __restrict__ part) {
+  __shared__ double s_hi[kPartThreads];
+  __shared__ double s_lo[kPartThreads];
+  const int t = threadIdx.x;
+  const int64_t b0 = (int64_t)blockIdx.x * chunk;
+  const int64_t b1 = b0 + chunk < nb ? b0 + chunk : nb;
+  double hi = 0.0, lo = 0.0;
+  for (int64_t i = b0 + t; i < b1; i += kPartThreads) dd_add(hi, lo, (double)absmax[i], 0.0);
+  s_hi[t] = hi;
+  s_lo[t] = lo;
+  __syncthreads();
+  dd_tree<kPartThreads>(s_hi, s_lo, t);
+  if (t == 0) part[blockIdx.x] = make_double2(s_hi[0], s_lo[0]);
+}
+
+__global__ __launch_bounds__(kFinalThreads) void k_offset_final(const double2* __restrict__ part,
+                                                                 int parts, int64_t nb,
+                                                                 float* __restrict__ offset) {
+  __shared__ double s_hi[kFinalThreads];
+  __shared__ double s_lo[kFinalThreads];
+  const int t = threadIdx.x;
+  const double2 v = t < parts ? part[t] : make_double2(0.0, 0.0);
+  s_hi[t] = v.x;
+  s_lo[t] = v.y;
+  __syncthreads();
+  dd_tree<kFinalThreads>(s_hi, s_lo, t);
   if (t == 0) {
     const double sum = s_hi[0] + s_lo[0];  // one rounding of the exact sum
     offset[0] = (float)(sum / (double)nb);
@@ -164,9 +200,12 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t* __restrict__ pa
 
 }  // namespace
 
+// absmax fp32 [nb], then the offset pass's double-double partials
+static size_t absmax_bytes(int64_t nb) { return ((size_t)nb * sizeof(float) + 255) / 256 * 256; }
+
 size_t quantize_ws_bytes(int64_t n_out, int64_t k_in) {
   const int64_t nb = n_out * k_in / 64;
-  return (size_t)nb * sizeof(float);
+  return absmax_bytes(nb) + (size_t)offset_parts(nb) * sizeof(double2);
 }
 
 hipError_t launch_quantize(const void* w, int dtype, int64_t n_out, int64_t k_in, uint8_t* packed,
@@ -184,7 +223,14 @@ hipError_t launch_quantize(const void* w, int dtype, int64_t n_out, int64_t k_in
                        absmax, status, host_mids4());
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_offset, dim3(1), dim3(kSumThreads), 0, s, absmax, nb, offset);
+  const int64_t parts = offset_parts(nb);
+  const int64_t chunk = (nb + parts - 1) / parts;
+  double2* part = reinterpret_cast<double2*>(static_cast<uint8_t*>(ws) + absmax_bytes(nb));
+  hipLaunchKernelGGL(k_offset_part, dim3((unsigned)parts), dim3(kPartThreads), 0, s, absmax, nb, chunk,
+                     part);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_offset_final, dim3(1), dim3(kFinalThreads), 0, s, part, (int)parts, nb, offset);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nn = (nb + 255) / 256;

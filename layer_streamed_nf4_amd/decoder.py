@@ -39,7 +39,8 @@ from . import (OP_ATTENTION_BWD, OP_CROSS_ENTROPY, OP_DENSE_BWD_PACKED, OP_DENSE
                nf4s_rmsnorm_fwd, nf4s_rope_pair, nf4s_swiglu_bwd, nf4s_swiglu_fwd,
                nf4s_workspace_bytes, streamed_linear_bwd_packed, streamed_linear_fwd_packed,
                streamed_linear_fwd_grouped, grouped_workspace_bytes, grouped_bwd_workspace_bytes,
-               streamed_linear_bwd_grouped, streamed_linear_fwd_residual)
+               streamed_linear_bwd_grouped, streamed_linear_fwd_residual, streamed_linear_fwd_swiglu,
+               nf4s_swiglu_fused_supported)
 from .stack import ALIGN, PROJ, ShardSet, _prefetch_ahead, _round_up
 
 # projections that read the same input: q, k, v the normed h; gate, up the
@@ -171,6 +172,9 @@ class Decoder:
         # the backward of q, k, v (and of gate, up) as one contraction when
         # every member would split its contraction alone (small M): one
         # launch and one sum instead of one of each per projection
+        # the first forward's gate + up with SwiGLU fused into the launch's
+        # epilogue, where its shapes allow (same bits, half the output)
+        self._fuse_swiglu = nf4s_swiglu_fused_supported(M, I, H) and I % 64 == 0
         self._group_bwd = {}
         for grp in (("q", "k", "v"), ("gate", "up")):
             n_outs, ki = [shapes[p][0] for p in grp], shapes[grp[0]][1]
@@ -270,6 +274,22 @@ class Decoder:
             streamed_linear_fwd_grouped(base, [self.sh.layout.descs[p] for p in ps], xp, self.M,
                                         [y.data_ptr() for y in ys], us, Bs, r, scale, *self._ws(),
                                         self._s)
+        self._tock(ev)
+
+    def _fwd_swiglu(self, base, i, adapters):
+        """gate and up of layer i with the SwiGLU epilogue: self.sw row-major
+        and, in the second packed buffer (the first holds n2, which the launch
+        reads), in fragment order for the down projection."""
+        H, I = self.H, self.I
+        xp = self._pack(self.n2, H)
+        tg = self._lora_u(i, ("gate", "up"), self.n2, adapters)
+        us = [self.u[p].data_ptr() if p in tg else None for p in ("gate", "up")]
+        Bs = [self.lora[(i, p)][1].data_ptr() if p in tg else None for p in ("gate", "up")]
+        r, scale = (self.r, self.scale) if tg else (0, 0.0)
+        ev = self._tick("fwd", 2 * I, H)
+        streamed_linear_fwd_swiglu(base, self.sh.layout.descs["gate"], self.sh.layout.descs["up"], xp,
+                                   self.M, self.sw.data_ptr(), self._produced(self.sw, I, second=True),
+                                   self.packed_b.numel(), us, Bs, r, scale, self._s)
         self._tock(ev)
 
     def _lora_u(self, i, ps, x, adapters=True):
@@ -385,7 +405,11 @@ class Decoder:
         self._fwd(base, i, ("o",), self.o, (self.ao,), a, res=(hin, self.h_mid))
         nf4s_rmsnorm_fwd(self.h_mid.data_ptr(), self.norms["mlp"][i].data_ptr(), M, H, c["eps"],
                          self.n2.data_ptr(), self.rstd2.data_ptr(), s, packed=self._produced(self.n2, H))
-        self._fwd(base, i, ("gate", "up"), self.n2, (self.g, self.u_), a)
+        fuse = self._fuse_swiglu and not recompute and not keep
+        if fuse:
+            self._fwd_swiglu(base, i, a)
+        else:
+            self._fwd(base, i, ("gate", "up"), self.n2, (self.g, self.u_), a)
         if recompute:
             # h_{i+1} is stored and the backward reads no output of the down
             # projection: only its adapter's u is recomputed, from the SwiGLU
@@ -394,8 +418,9 @@ class Decoder:
                 nf4s_swiglu_fwd(self.g.data_ptr(), self.u_.data_ptr(), M, self.I, self.sw.data_ptr(), s)
                 self._lora_u(i, ("down",), self.sw, a)
         else:
-            nf4s_swiglu_fwd(self.g.data_ptr(), self.u_.data_ptr(), M, self.I, self.sw.data_ptr(), s,
-                            packed=self._produced(self.sw, self.I))
+            if not fuse:
+                nf4s_swiglu_fwd(self.g.data_ptr(), self.u_.data_ptr(), M, self.I, self.sw.data_ptr(), s,
+                                packed=self._produced(self.sw, self.I))
             self._fwd(base, i, ("down",), self.sw, (self.dn,), a, res=(self.h_mid, hout))
 
     def _layer_bwd(self, i, base):

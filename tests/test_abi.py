@@ -77,7 +77,10 @@ def test_workspace_queries_depend_on_shape_only():
     a = L.nf4s_workspace_bytes(L.OP_LINEAR_FWD, 512, 4096, 4096)
     b = L.nf4s_workspace_bytes(L.OP_LINEAR_FWD, 512, 4096, 4096)
     assert a == b and a % 4 == 0
-    assert L.nf4s_workspace_bytes(L.OP_QUANTIZE, 0, 576, 576) == 5184 * 4
+    # the absmax (5184 fp32, padded to 256 B) and one double-double partial
+    # of the offset sum per 4096 absmax values
+    assert L.nf4s_workspace_bytes(L.OP_QUANTIZE, 0, 576, 576) == 20736 + 2 * 16
+    assert L.nf4s_workspace_bytes(L.OP_QUANTIZE, 0, 14336, 4096) == 917504 * 4 + 224 * 16
     with pytest.raises(L.Nf4sError) as e:
         L.nf4s_workspace_bytes(99, 1, 64, 64)
     assert e.value.code == L.EINVAL
@@ -449,3 +452,26 @@ def test_rope_pair_argument_errors():
     assert _err(f, FAKE, 4, FAKE + 2, 2, 8, 4, 32, 1e4, 0) == L.EALIGN
     assert _err(f, FAKE, 4, None, 2, 8, 4, 32, 1e4, 0) == L.EINVAL
     assert _err(f, FAKE, 4, FAKE, 2, 8, 4, 32, 1e4, 2) == L.EINVAL        # inverse
+
+
+def test_fused_swiglu_refuses_split_shapes_and_bad_arguments():
+    # q-sized weights at M = 512: 64 tiles of 512 rows, the contraction would be split
+    assert not L.nf4s_swiglu_fused_supported(512, 4096, 4096)
+    assert L.nf4s_swiglu_fused_supported(512, 14336, 4096)
+    assert not L.nf4s_swiglu_fused_supported(512, 14336 + 8, 4096)   # not whole 64-column tiles
+    d0 = L.nf4s_tensor_layout(4096, 4096)
+    d1 = L.nf4s_tensor_layout(4096, 4096, d0.end)
+    with pytest.raises(L.Nf4sError) as e:
+        L.streamed_linear_fwd_swiglu(FAKE, d0, d1, FAKE, 512, FAKE, None, 0, None, None, 0, 0.0)
+    assert e.value.code == L.ESHAPE
+    g0 = L.nf4s_tensor_layout(14336, 4096)
+    g1 = L.nf4s_tensor_layout(14336, 4096, g0.end)
+    with pytest.raises(L.Nf4sError) as e:                               # no output at all
+        L.streamed_linear_fwd_swiglu(FAKE, g0, g1, FAKE, 512, None, None, 0, None, None, 0, 0.0)
+    assert e.value.code == L.EINVAL
+    with pytest.raises(L.Nf4sError) as e:                               # packed output too small
+        L.streamed_linear_fwd_swiglu(FAKE, g0, g1, FAKE, 512, None, FAKE, 1024, None, None, 0, 0.0)
+    assert e.value.code == L.EWORKSPACE
+    with pytest.raises(L.Nf4sError) as e:                               # gate and up differ
+        L.streamed_linear_fwd_swiglu(FAKE, g0, d1, FAKE, 512, FAKE, None, 0, None, None, 0, 0.0)
+    assert e.value.code == L.ESHAPE

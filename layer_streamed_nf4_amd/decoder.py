@@ -65,7 +65,8 @@ class Decoder:
 
     def __init__(self, cfg, shards: ShardSet, embed, lm_head, norms, lora, batch, seq,
                  targets=("q", "v"), r=16, alpha=32, n_slots=2, mode="streamed", lr=1e-4,
-                 betas=(0.9, 0.999), adam_eps=1e-8, weight_decay=0.0, time_calls=None, poison=False):
+                 betas=(0.9, 0.999), adam_eps=1e-8, weight_decay=0.0, time_calls=None, poison=False,
+                 trace=False):
         """time_calls: optional predicate (direction, n_out, k_in) -> bool; the
         streamed linear forward calls it accepts are bracketed by timing
         events on the compute stream, collected in self.timed as
@@ -73,6 +74,9 @@ class Decoder:
         (q, k, v; gate, up) is one entry whose n_out is the group's total."""
         assert mode in ("streamed", "resident")
         self.time_calls = time_calls
+        # trace=True: after each backward, trace[i] holds dL/dh_i (fp32 [M,
+        # hidden]) for i = 0..L, copied on the compute stream (for tests)
+        self.trace = {} if trace else None
         self.timed = []
         self._kept_last = False  # the last layer's body is still in the buffers
         dev = "cuda"
@@ -498,9 +502,15 @@ class Decoder:
             base = self._acquire(i, range(i - 1, -1, -1))
             if not (i == L - 1 and self._kept_last):
                 self._layer_fwd(i, base, recompute=True)
+            if self.trace is not None:  # dL/dh_{i+1}, the gradient layer i starts from
+                with torch.cuda.stream(self.compute):
+                    self.trace[i + 1] = self.dh.clone()
             self._layer_bwd(i, base)
             self._release(i)
         self._kept_last = False
+        if self.trace is not None:
+            with torch.cuda.stream(self.compute):
+                self.trace[0] = self.dh.clone()
 
     def forward_backward(self, ids, targets):
         """Queue the forward and backward sweeps for token ids / next-token

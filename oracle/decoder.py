@@ -206,34 +206,41 @@ def _lin_bwd(x, dy, P: Params, l, p, cfg, grads):
     return dx
 
 
+def layer_forward(P: Params, l, h, B, S, cfg: Config, cos, sin, exact=False, adapters=True):
+    """Layer l of the decoder from its input residual h [B*S, H]: returns
+    (h_out, cache of the layer's activations)."""
+    T = B * S
+    grp = cfg.heads // cfg.kv_heads
+    c = {"h_in": h}
+    n1, c["rstd1"] = rmsnorm(h, P.w_attn[l], cfg.eps)
+    n1 = _r(n1, exact)
+    q = _r(_lin(n1, P, l, "q", cfg, adapters), exact).reshape(B, S, cfg.heads, cfg.head_dim)
+    k = _r(_lin(n1, P, l, "k", cfg, adapters), exact).reshape(B, S, cfg.kv_heads, cfg.head_dim)
+    v = _r(_lin(n1, P, l, "v", cfg, adapters), exact).reshape(B, S, cfg.kv_heads, cfg.head_dim)
+    qr, kr = _r(rope(q, cos, sin), exact), _r(rope(k, cos, sin), exact)
+    o, Pm = attention(qr, kr, v, grp)
+    o = _r(o, exact).reshape(T, -1)
+    h = h + _r(_lin(o, P, l, "o", cfg, adapters), exact)
+    c.update(n1=n1, qr=qr, kr=kr, v=v, P=Pm, o=o, h_mid=h)
+    n2, c["rstd2"] = rmsnorm(h, P.w_mlp[l], cfg.eps)
+    n2 = _r(n2, exact)
+    g = _r(_lin(n2, P, l, "gate", cfg, adapters), exact)
+    u = _r(_lin(n2, P, l, "up", cfg, adapters), exact)
+    sw = _r(silu(g) * u, exact)
+    h = h + _r(_lin(sw, P, l, "down", cfg, adapters), exact)
+    c.update(n2=n2, g=g, u=u, sw=sw)
+    return h, c
+
+
 def forward(P: Params, ids, targets, cfg: Config, exact=False, adapters=True):
     """Returns (loss, logits [B*S, V], cache). adapters=False evaluates the
     frozen base alone (the reference model of a preference step)."""
     B, S = ids.shape
-    T = B * S
     cos, sin = rope_tables(S, cfg.head_dim, cfg.rope_theta)
-    grp = cfg.heads // cfg.kv_heads
     h = P.embed[ids.reshape(-1)].astype(np.float64)
     cache = {"layers": []}
     for l in range(cfg.layers):
-        c = {"h_in": h}
-        n1, c["rstd1"] = rmsnorm(h, P.w_attn[l], cfg.eps)
-        n1 = _r(n1, exact)
-        q = _r(_lin(n1, P, l, "q", cfg, adapters), exact).reshape(B, S, cfg.heads, cfg.head_dim)
-        k = _r(_lin(n1, P, l, "k", cfg, adapters), exact).reshape(B, S, cfg.kv_heads, cfg.head_dim)
-        v = _r(_lin(n1, P, l, "v", cfg, adapters), exact).reshape(B, S, cfg.kv_heads, cfg.head_dim)
-        qr, kr = _r(rope(q, cos, sin), exact), _r(rope(k, cos, sin), exact)
-        o, Pm = attention(qr, kr, v, grp)
-        o = _r(o, exact).reshape(T, -1)
-        h = h + _r(_lin(o, P, l, "o", cfg, adapters), exact)
-        c.update(n1=n1, qr=qr, kr=kr, v=v, P=Pm, o=o, h_mid=h)
-        n2, c["rstd2"] = rmsnorm(h, P.w_mlp[l], cfg.eps)
-        n2 = _r(n2, exact)
-        g = _r(_lin(n2, P, l, "gate", cfg, adapters), exact)
-        u = _r(_lin(n2, P, l, "up", cfg, adapters), exact)
-        sw = _r(silu(g) * u, exact)
-        h = h + _r(_lin(sw, P, l, "down", cfg, adapters), exact)
-        c.update(n2=n2, g=g, u=u, sw=sw)
+        h, c = layer_forward(P, l, h, B, S, cfg, cos, sin, exact, adapters)
         cache["layers"].append(c)
     hn, rstd_f = rmsnorm(h, P.w_final, cfg.eps)
     hn = _r(hn, exact)
@@ -247,34 +254,41 @@ def backward(P: Params, cache, cfg: Config, exact=False):
     """Gradients of the mean cross-entropy: {(layer, proj): (dA, dB)} for the
     adapters and dh0 = dL/d(embedding rows) [B*S, H]."""
     B, S = cache["shape"]
-    T = B * S
-    grp = cfg.heads // cfg.kv_heads
     cos, sin = cache["cos"], cache["sin"]
     grads = {}
     dl = _r(cache["dlogits"], exact)
     dhn = _r(dl @ P.lm_head, exact)
     dh = rmsnorm_bwd(dhn, cache["h_final"], P.w_final, cache["rstd_f"])
     for l in range(cfg.layers - 1, -1, -1):
-        c = cache["layers"][l]
-        dd = _r(dh, exact)
-        dsw = _r(_lin_bwd(c["sw"], dd, P, l, "down", cfg, grads), exact)
-        dg, du = swiglu_bwd(dsw, c["g"], c["u"])
-        dg, du = _r(dg, exact), _r(du, exact)
-        dn2 = (_r(_lin_bwd(c["n2"], dg, P, l, "gate", cfg, grads), exact)
-               + _r(_lin_bwd(c["n2"], du, P, l, "up", cfg, grads), exact))
-        dh = dh + rmsnorm_bwd(dn2, c["h_mid"], P.w_mlp[l], c["rstd2"])
-        dao = _r(dh, exact)
-        do = _r(_lin_bwd(c["o"], dao, P, l, "o", cfg, grads), exact)
-        do = do.reshape(B, S, cfg.heads, cfg.head_dim)
-        dqr, dkr, dv = attention_bwd(do, c["qr"], c["kr"], c["v"], c["P"], grp)
-        dq = _r(rope(_r(dqr, exact), cos, sin, inverse=True), exact).reshape(T, -1)
-        dk = _r(rope(_r(dkr, exact), cos, sin, inverse=True), exact).reshape(T, -1)
-        dv = _r(dv, exact).reshape(T, -1)
-        dn1 = (_r(_lin_bwd(c["n1"], dq, P, l, "q", cfg, grads), exact)
-               + _r(_lin_bwd(c["n1"], dk, P, l, "k", cfg, grads), exact)
-               + _r(_lin_bwd(c["n1"], dv, P, l, "v", cfg, grads), exact))
-        dh = dh + rmsnorm_bwd(dn1, c["h_in"], P.w_attn[l], c["rstd1"])
+        dh = layer_backward(P, l, cache["layers"][l], dh, B, S, cfg, cos, sin, grads, exact)
     return {"lora": grads, "dh0": dh}
+
+
+def layer_backward(P: Params, l, c, dh, B, S, cfg: Config, cos, sin, grads, exact=False):
+    """Backward of layer l from dL/dh_out (fp64 [B*S, H]) and the layer's
+    cached activations: returns dL/dh_in and adds the layer's adapter
+    gradients to grads."""
+    T = B * S
+    grp = cfg.heads // cfg.kv_heads
+    dd = _r(dh, exact)
+    dsw = _r(_lin_bwd(c["sw"], dd, P, l, "down", cfg, grads), exact)
+    dg, du = swiglu_bwd(dsw, c["g"], c["u"])
+    dg, du = _r(dg, exact), _r(du, exact)
+    dn2 = (_r(_lin_bwd(c["n2"], dg, P, l, "gate", cfg, grads), exact)
+           + _r(_lin_bwd(c["n2"], du, P, l, "up", cfg, grads), exact))
+    dh = dh + rmsnorm_bwd(dn2, c["h_mid"], P.w_mlp[l], c["rstd2"])
+    dao = _r(dh, exact)
+    do = _r(_lin_bwd(c["o"], dao, P, l, "o", cfg, grads), exact)
+    do = do.reshape(B, S, cfg.heads, cfg.head_dim)
+    dqr, dkr, dv = attention_bwd(do, c["qr"], c["kr"], c["v"], c["P"], grp)
+    dq = _r(rope(_r(dqr, exact), cos, sin, inverse=True), exact).reshape(T, -1)
+    dk = _r(rope(_r(dkr, exact), cos, sin, inverse=True), exact).reshape(T, -1)
+    dv = _r(dv, exact).reshape(T, -1)
+    dn1 = (_r(_lin_bwd(c["n1"], dq, P, l, "q", cfg, grads), exact)
+           + _r(_lin_bwd(c["n1"], dk, P, l, "k", cfg, grads), exact)
+           + _r(_lin_bwd(c["n1"], dv, P, l, "v", cfg, grads), exact))
+    dh = dh + rmsnorm_bwd(dn1, c["h_in"], P.w_attn[l], c["rstd1"])
+    return dh
 
 
 # ---- preference step -------------------------------------------------------------

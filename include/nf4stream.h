@@ -284,6 +284,20 @@ int nf4s_grouped_workspace_bytes(int n, const int64_t* n_outs, int64_t k_in, int
                                  size_t* bytes);
 
 /*
+ * The launch plan of streamed_linear_fwd_grouped (swiglu = 0; n = 1 is the
+ * plan of streamed_linear_fwd_packed) or of streamed_linear_fwd_swiglu
+ * (swiglu = 1, n = 2 equal widths) for these shapes: the output tile
+ * (*tile_rows x *tile_cols; 512 x 128 is the one-wave-per-SIMD forward
+ * kernel, 256 x 128 the general one; for the SwiGLU launch the columns count
+ * gate and up together) and the split of the contraction (1 = none).
+ * Host-only, depends on the shapes alone. Errors: EINVAL (NULL outputs, n
+ * out of range, SwiGLU widths differ), ESHAPE (sizes; a SwiGLU launch that
+ * would need a split).
+ */
+int nf4s_linear_fwd_plan(int n, const int64_t* n_outs, int64_t k_in, int64_t M, int swiglu,
+                         int* tile_rows, int* tile_cols, int* splits);
+
+/*
  * Forward into the residual stream (the o and down projections of a llama
  * layer, [G] s2.1): y as streamed_linear_fwd_packed writes it, and
  *   h_out = h_in + y        fp32 [M, n_out], y's bf16 values added in fp32

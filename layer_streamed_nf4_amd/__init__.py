@@ -35,7 +35,7 @@ EXPORTS = (
     "nf4s_pool_set_debug", "streamed_linear_fwd_noalloc", "nf4s_swiglu_fused_supported",
     "streamed_linear_fwd_swiglu", "nf4s_packed_activation_bytes", "nf4s_pack_activation", "streamed_linear_fwd_packed",
     "streamed_linear_bwd_packed", "dense_linear_fwd_packed", "dense_linear_bwd_packed",
-    "nf4s_grouped_workspace_bytes", "streamed_linear_fwd_grouped",
+    "nf4s_grouped_workspace_bytes", "streamed_linear_fwd_grouped", "nf4s_linear_fwd_plan",
     "nf4s_lora_grouped_workspace_bytes", "lora_fwd_grouped", "lora_bwd_grouped",
     "nf4s_grouped_bwd_workspace_bytes", "streamed_linear_bwd_grouped", "streamed_linear_fwd_residual",
     "nf4s_rope_pair",
@@ -118,6 +118,7 @@ _SIG = {
     "streamed_linear_bwd_packed": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P,
                                                   _P, ctypes.c_int, _P, ctypes.c_size_t, _P]),
     "nf4s_grouped_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _P]),
+    "nf4s_linear_fwd_plan": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, ctypes.c_int, _P, _P, _P]),
     "streamed_linear_fwd_grouped": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), ctypes.c_int, _P,
                                                    _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float,
                                                    _P, ctypes.c_size_t, _P]),
@@ -270,6 +271,15 @@ def grouped_workspace_bytes(n_outs, k_in, M):
     _check(lib().nf4s_grouped_workspace_bytes(len(n_outs), ctypes.cast(arr, ctypes.c_void_p), k_in, M,
                                               ctypes.byref(out)))
     return out.value
+
+
+def linear_fwd_plan(n_outs, k_in, M, swiglu=False):
+    """(tile rows, tile columns, splits) of the forward launch for these shapes."""
+    arr = (ctypes.c_int64 * len(n_outs))(*n_outs)
+    v = [ctypes.c_int() for _ in range(3)]
+    _check(lib().nf4s_linear_fwd_plan(len(n_outs), ctypes.cast(arr, ctypes.c_void_p), k_in, M, int(swiglu),
+                                      *(ctypes.byref(x) for x in v)))
+    return tuple(x.value for x in v)
 
 
 def _ptr_array(ptrs):

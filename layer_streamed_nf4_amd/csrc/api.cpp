@@ -468,6 +468,27 @@ int streamed_linear_fwd_grouped(const void* shard_dev, const nf4s_tensor_desc* d
   return e == hipSuccess ? NF4S_OK : hip_fail(e, "grouped linear launch");
 }
 
+int nf4s_linear_fwd_plan(int n, const int64_t* n_outs, int64_t k_in, int64_t M, int swiglu,
+                         int* tile_rows, int* tile_cols, int* splits) {
+  if (!tile_rows || !tile_cols || !splits) return fail(NF4S_EINVAL, "plan outputs must be given");
+  int rc;
+  if ((rc = check_group(n, n_outs, k_in, M))) return rc;
+  if (swiglu) {
+    if (n != 2 || n_outs[0] != n_outs[1])
+      return fail(NF4S_EINVAL, "the SwiGLU launch takes gate and up of one width");
+    if (!swiglu_tiles(M, n_outs[0], k_in, tile_rows, tile_cols))
+      return fail(NF4S_ESHAPE, "no unsplit SwiGLU launch for M=%lld width=%lld k_in=%lld", (long long)M,
+                  (long long)n_outs[0], (long long)k_in);
+    *splits = 1;
+    return NF4S_OK;
+  }
+  const GemmPlan p = plan_gemm_grouped(M, n_outs, n, k_in, true);
+  *tile_rows = p.bm;
+  *tile_cols = p.bn;
+  *splits = p.splits;
+  return NF4S_OK;
+}
+
 int nf4s_swiglu_fused_supported(int64_t M, int64_t width, int64_t k_in) {
   if (M <= 0 || M > kMaxRows || width <= 0 || k_in <= 0 || width % 64 || k_in % 64) return 0;
   return swiglu_fused_ok(M, width, k_in) ? 1 : 0;

@@ -93,6 +93,8 @@ hipError_t launch_linear_fwd_residual(const QPtrs& q, int64_t n_out, int64_t k_i
 // out and out_packed (fragment order) nullable. swiglu_fused_ok: the launch
 // needs no split of the contraction (the only case it supports).
 bool swiglu_fused_ok(int64_t M, int64_t width, int64_t k_in);
+// The fused launch's tile (rows, gate + up columns); false where unsupported.
+bool swiglu_tiles(int64_t M, int64_t width, int64_t k_in, int* bm, int* bn);
 hipError_t launch_linear_swiglu_fwd(const QPtrs* q, int64_t width, int64_t k_in, const uint8_t* x_packed,
                                     int64_t M, uint16_t* out, uint8_t* out_packed,
                                     const float* const* lora_us, const float* const* lora_Bs, int r,

@@ -1507,6 +1507,12 @@ bool swiglu_fused_ok(int64_t M, int64_t width, int64_t k_in) {
   return tiles >= 192 || nk / 2 < 8;
 }
 
+bool swiglu_tiles(int64_t M, int64_t width, int64_t k_in, int* bm, int* bn) {
+  *bm = FBM;
+  *bn = BN;
+  return swiglu_fused_ok(M, width, k_in);
+}
+
 hipError_t launch_linear_swiglu_fwd(const QPtrs* q, int64_t width, int64_t k_in, const uint8_t* x_packed,
                                     int64_t M, uint16_t* out, uint8_t* out_packed,
                                     const float* const* lora_us, const float* const* lora_Bs, int r,

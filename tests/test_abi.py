@@ -322,6 +322,25 @@ def test_grouped_forward_workspace():
     assert _err(L.grouped_workspace_bytes, [64, 64], 64, 0) == L.ESHAPE
 
 
+def test_forward_plans():
+    """Which forward kernel a shape runs on: 512 x 128 tiles where they fill
+    the chip unsplit (gate + up of the 8B layer at 512 rows: 224 tiles), else
+    256 x 128 tiles, split while the grid is short of the CUs."""
+    g8, k8 = [14336, 14336], 4096
+    assert L.linear_fwd_plan(g8, k8, 512) == (512, 128, 1)
+    assert L.linear_fwd_plan(g8, k8, 2048) == (512, 128, 1)
+    assert L.linear_fwd_plan(g8, k8, 512, swiglu=True) == (512, 128, 1)
+    assert L.linear_fwd_plan([14336], k8, 512) == (256, 128, 1)      # 112 tiles of 512 would split
+    assert L.linear_fwd_plan([4096, 1024, 1024], k8, 512) == (256, 128, 2)
+    assert L.linear_fwd_plan([4096, 1024, 1024], k8, 2048) == (512, 128, 1)
+    assert L.linear_fwd_plan([4096], 14336, 512) == (256, 128, 4)
+    assert L.linear_fwd_plan([576, 200, 136], 576, 700) == (512, 128, 1)  # 9 steps: never split
+    assert _err(L.linear_fwd_plan, [14336, 1024], k8, 512, True) == L.EINVAL
+    assert _err(L.linear_fwd_plan, [4096, 4096], k8, 512, True) == L.ESHAPE   # would split
+    assert _err(L.linear_fwd_plan, [64] * 4, 64, 16) == L.EINVAL
+    assert _err(L.linear_fwd_plan, [64, 60], 64, 16) == L.ESHAPE
+
+
 def test_grouped_forward_argument_errors():
     d = [L.nf4s_tensor_layout(64, 128, 0)]
     d.append(L.nf4s_tensor_layout(32, 128, d[0].end))

@@ -326,6 +326,9 @@ def test_grouped_forward_bit_identical_when_split_matches(projs, ns, k, M, lora_
     the single calls run on different kernels."""
     splits_single = [L.nf4s_workspace_bytes(L.OP_LINEAR_FWD_PACKED, M, n, k) for n in ns]
     assert splits_single == [0] * len(ns) and L.grouped_workspace_bytes(list(ns), k, M) == 0
+    if ns == (14336, 14336) and M == 512:   # the two kernels named above
+        assert L.linear_fwd_plan(list(ns), k, M) == (512, 128, 1)
+        assert L.linear_fwd_plan([ns[0]], k, M) == (256, 128, 1)
     c = _group_setup(projs, ns, k, M, lora_on)
     g, single = _group_run(c, True), _group_run(c, False)
     for a, b in zip(g, single):

@@ -511,9 +511,13 @@ int nf4s_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float* x, const
 int nf4s_rope(uint16_t* x, int64_t T, int64_t S, int heads, int head_dim, double theta, int inverse,
               void* stream);
 /* The same on queries q [T, q_heads*head_dim] and keys k [T, k_heads*head_dim]
- * in one launch (each element as nf4s_rope rotates it). */
+ * in one launch (each element as nf4s_rope rotates it). q_packed / k_packed
+ * (nullable, 256-B aligned, nf4s_packed_activation_bytes(T, heads*head_dim)
+ * bytes): the rotated tensors also as nf4s_pack_activation lays them out, for
+ * the GEMMs that read them next (the backward's dq and dk). */
 int nf4s_rope_pair(uint16_t* q, int q_heads, uint16_t* k, int k_heads, int64_t T, int64_t S,
-                   int head_dim, double theta, int inverse, void* stream);
+                   int head_dim, double theta, int inverse, void* q_packed, void* k_packed,
+                   void* stream);
 
 /*
  * Causal softmax attention with grouped KV heads (head h reads KV head

@@ -123,7 +123,7 @@ _SIG = {
                                                    _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float,
                                                    _P, ctypes.c_size_t, _P]),
     "nf4s_rope_pair": (ctypes.c_int, [_P, ctypes.c_int, _P, ctypes.c_int, _I64, _I64, ctypes.c_int,
-                                      ctypes.c_double, ctypes.c_int, _P]),
+                                      ctypes.c_double, ctypes.c_int, _P, _P, _P]),
     "streamed_linear_fwd_residual": (ctypes.c_int, [_P, ctypes.POINTER(TensorDesc), _P, _I64, _P, _P, _P,
                                                     ctypes.c_int, ctypes.c_float, _P, _P, _P,
                                                     ctypes.c_size_t, _P]),
@@ -367,8 +367,10 @@ def nf4s_rmsnorm_bwd(dys, x, w, rstd, T, H, accumulate, dh, stream=0, y=None, pa
     _check(lib().nf4s_rmsnorm_bwd(arr, len(dys), x, w, rstd, T, H, accumulate, dh, y, packed, stream))
 
 
-def nf4s_rope_pair(q, q_heads, k, k_heads, T, S, head_dim, theta, inverse, stream=0):
-    _check(lib().nf4s_rope_pair(q, q_heads, k, k_heads, T, S, head_dim, theta, inverse, stream))
+def nf4s_rope_pair(q, q_heads, k, k_heads, T, S, head_dim, theta, inverse, stream=0, q_packed=None,
+                   k_packed=None):
+    _check(lib().nf4s_rope_pair(q, q_heads, k, k_heads, T, S, head_dim, theta, inverse, q_packed, k_packed,
+                                stream))
 
 
 def nf4s_rope(x, T, S, heads, head_dim, theta, inverse, stream=0):

@@ -884,7 +884,8 @@ int nf4s_rope(uint16_t* x, int64_t T, int64_t S, int heads, int head_dim, double
 }
 
 int nf4s_rope_pair(uint16_t* q, int q_heads, uint16_t* k, int k_heads, int64_t T, int64_t S,
-                   int head_dim, double theta, int inverse, void* stream) {
+                   int head_dim, double theta, int inverse, void* q_packed, void* k_packed,
+                   void* stream) {
   int rc;
   if ((rc = check_heads(q_heads, head_dim)) || (rc = check_heads(k_heads, head_dim))) return rc;
   if (head_dim % 8) return fail(NF4S_ESHAPE, "head_dim=%d is not a multiple of 8", head_dim);
@@ -894,8 +895,10 @@ int nf4s_rope_pair(uint16_t* q, int q_heads, uint16_t* k, int k_heads, int64_t T
   if (!(theta > 1.0) || !std::isfinite(theta)) return fail(NF4S_EINVAL, "theta must be finite and > 1");
   if (inverse != 0 && inverse != 1) return fail(NF4S_EINVAL, "inverse must be 0 or 1");
   if ((rc = check_ptr(q, "q", 8)) || (rc = check_ptr(k, "k", 8))) return rc;
-  return launched(launch_rope_pair(q, q_heads, k, k_heads, T, S, head_dim, theta, inverse,
-                                   static_cast<hipStream_t>(stream)),
+  if (q_packed && (rc = check_ptr(q_packed, "q_packed", 256))) return rc;
+  if (k_packed && (rc = check_ptr(k_packed, "k_packed", 256))) return rc;
+  return launched(launch_rope_pair(q, q_heads, k, k_heads, T, S, head_dim, theta, inverse, q_packed,
+                                   k_packed, static_cast<hipStream_t>(stream)),
                   "rope launch");
 }
 

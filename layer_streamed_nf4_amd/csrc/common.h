@@ -156,9 +156,10 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float*
                               uint16_t* y, void* packed, hipStream_t s);
 hipError_t launch_rope(uint16_t* x, int64_t T, int64_t S, int heads, int d, double theta,
                        int inverse, hipStream_t s);
-// x1 and x2 (heads1 / heads2 heads, x2 nullable) in one launch
+// x1 and x2 (heads1 / heads2 heads, x2 nullable) in one launch; p1 / p2
+// (nullable): the results also in MFMA fragment order
 hipError_t launch_rope_pair(uint16_t* x1, int heads1, uint16_t* x2, int heads2, int64_t T, int64_t S,
-                            int d, double theta, int inverse, hipStream_t s);
+                            int d, double theta, int inverse, void* p1, void* p2, hipStream_t s);
 // packed (nullable): o also in fragment order (width H*D), as the producers above
 hipError_t launch_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
                                 int64_t S, int H, int Hkv, int D, uint16_t* o, float* o_f32,

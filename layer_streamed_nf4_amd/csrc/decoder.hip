@@ -195,54 +195,70 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(DyPtrs dys, int n_dy, const
 
 // In-place rotary embedding of bf16 x[T, heads * d]; row t is position t % S.
 // inv[j] = theta^(-2j/d) (computed on the host in fp64); the angle and its
-// sine and cosine are fp64, the rotation fp32. One thread per 4 pairs.
+// sine and cosine are fp64, the rotation fp32.
 struct InvFreq {
   double f[128];
 };
 
-// Two tensors per launch (queries and keys): threads past the first
-// tensor's n rotate the second (heads2 heads; none when x2 is null).
-__global__ __launch_bounds__(256) void k_rope(uint16_t* __restrict__ x1, int heads1,
-                                              uint16_t* __restrict__ x2, int heads2, int64_t T,
-                                              int64_t S, int d, InvFreq inv, int inverse) {
+// One workgroup per row t and both tensors (queries and keys; none second
+// when x2 is null): the d/2 cosines and sines of position t % S are computed
+// once into LDS (fp64, rounded to fp32), then every head is rotated, four
+// pairs per thread and item. p1 / p2 (nullable): the rotated rows also in
+// MFMA fragment order (K = heads * d), as the GEMMs that read them next take
+// them (k_frag_pack's layout, the columns past K up to a multiple of 64 zero).
+__global__ __launch_bounds__(256) void k_rope_rows(uint16_t* __restrict__ x1, int heads1,
+                                                   uint8_t* __restrict__ p1, uint16_t* __restrict__ x2,
+                                                   int heads2, uint8_t* __restrict__ p2, int64_t S, int d,
+                                                   InvFreq inv, int inverse) {
+  __shared__ float2 cs[128];
+  const int64_t t = blockIdx.x;
   const int half = d / 2, q4 = half / 4;
-  const int64_t n1 = T * heads1 * q4;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  uint16_t* x = x1;
-  int heads = heads1;
-  if (i >= n1) {
-    i -= n1;
-    x = x2;
-    heads = heads2;
-  }
-  const int64_t n = T * heads * q4;
-  if (x == nullptr || i >= n) return;
-  const int j0 = 4 * (int)(i % q4);
-  const int64_t th = i / q4;  // (row, head)
-  const int64_t pos = (th / heads) % S;
-  uint16_t* v = x + th * d;
-  const uint2 a = *reinterpret_cast<const uint2*>(v + j0);
-  const uint2 b = *reinterpret_cast<const uint2*>(v + j0 + half);
-  const uint32_t aw[2] = {a.x, a.y}, bw[2] = {b.x, b.y};
-  float o1[4], o2[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
+  const int64_t pos = t % S;
+  for (int j = threadIdx.x; j < half; j += 256) {
     double sd, cd;
-    sincos((double)pos * inv.f[j0 + e], &sd, &cd);
-    const float c = (float)cd, sn = inverse ? -(float)sd : (float)sd;
-    const uint32_t wa = aw[e >> 1], wb = bw[e >> 1];
-    const float x1 = __uint_as_float((e & 1) ? (wa & 0xFFFF0000u) : (wa << 16));
-    const float x2 = __uint_as_float((e & 1) ? (wb & 0xFFFF0000u) : (wb << 16));
-    o1[e] = x1 * c - x2 * sn;
-    o2[e] = x2 * c + x1 * sn;
+    sincos((double)pos * inv.f[j], &sd, &cd);
+    cs[j] = make_float2((float)cd, inverse ? -(float)sd : (float)sd);
   }
-  uint2 ra, rb;
-  ra.x = pack_bf16x2(o1[0], o1[1]);
-  ra.y = pack_bf16x2(o1[2], o1[3]);
-  rb.x = pack_bf16x2(o2[0], o2[1]);
-  rb.y = pack_bf16x2(o2[2], o2[3]);
-  *reinterpret_cast<uint2*>(v + j0) = ra;
-  *reinterpret_cast<uint2*>(v + j0 + half) = rb;
+  __syncthreads();
+  const int n1 = heads1 * q4, n = n1 + (x2 ? heads2 * q4 : 0);
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const bool second = i >= n1;
+    const int ii = second ? i - n1 : i;
+    uint16_t* const x = second ? x2 : x1;
+    uint8_t* const p = second ? p2 : p1;
+    const int heads = second ? heads2 : heads1;
+    const int h = ii / q4, j0 = 4 * (ii % q4);
+    const int64_t K = (int64_t)heads * d;
+    uint16_t* const v = x + t * K + (int64_t)h * d;
+    const uint2 a = *reinterpret_cast<const uint2*>(v + j0);
+    const uint2 b = *reinterpret_cast<const uint2*>(v + j0 + half);
+    const uint32_t aw[2] = {a.x, a.y}, bw[2] = {b.x, b.y};
+    float o1[4], o2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float c = cs[j0 + e].x, sn = cs[j0 + e].y;
+      const uint32_t wa = aw[e >> 1], wb = bw[e >> 1];
+      const float x1v = __uint_as_float((e & 1) ? (wa & 0xFFFF0000u) : (wa << 16));
+      const float x2v = __uint_as_float((e & 1) ? (wb & 0xFFFF0000u) : (wb << 16));
+      o1[e] = x1v * c - x2v * sn;
+      o2[e] = x2v * c + x1v * sn;
+    }
+    uint2 ra, rb;
+    ra.x = pack_bf16x2(o1[0], o1[1]);
+    ra.y = pack_bf16x2(o1[2], o1[3]);
+    rb.x = pack_bf16x2(o2[0], o2[1]);
+    rb.y = pack_bf16x2(o2[2], o2[3]);
+    *reinterpret_cast<uint2*>(v + j0) = ra;
+    *reinterpret_cast<uint2*>(v + j0 + half) = rb;
+    if (p) {
+      // four consecutive columns are one half of a fragment's 16-byte slot
+      const int64_t kb = (K + 63) / 64 * 4;
+      const int64_t c1 = (int64_t)h * d + j0, c2 = c1 + half;
+      *reinterpret_cast<uint2*>(p + frag_offset(t, c1 & ~7ll, kb) + (c1 & 7) * 2) = ra;
+      *reinterpret_cast<uint2*>(p + frag_offset(t, c2 & ~7ll, kb) + (c2 & 7) * 2) = rb;
+      if (h == heads - 1 && j0 == 0) frag_zero_tail(p, t, K, kb);
+    }
+  }
 }
 
 // ---- attention on the matrix cores -------------------------------------------
@@ -1167,16 +1183,15 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float*
 
 hipError_t launch_rope(uint16_t* x, int64_t T, int64_t S, int heads, int d, double theta,
                        int inverse, hipStream_t s) {
-  return launch_rope_pair(x, heads, nullptr, 0, T, S, d, theta, inverse, s);
+  return launch_rope_pair(x, heads, nullptr, 0, T, S, d, theta, inverse, nullptr, nullptr, s);
 }
 
 hipError_t launch_rope_pair(uint16_t* x1, int heads1, uint16_t* x2, int heads2, int64_t T, int64_t S,
-                            int d, double theta, int inverse, hipStream_t s) {
+                            int d, double theta, int inverse, void* p1, void* p2, hipStream_t s) {
   InvFreq inv;
   for (int j = 0; j < 128; ++j) inv.f[j] = j < d / 2 ? pow(theta, -2.0 * j / d) : 0.0;
-  const int64_t n = T * (heads1 + (x2 ? heads2 : 0)) * (d / 8);
-  hipLaunchKernelGGL(k_rope, dim3(grid_of(n)), dim3(256), 0, s, x1, heads1, x2, heads2, T, S, d, inv,
-                     inverse);
+  hipLaunchKernelGGL(k_rope_rows, dim3((unsigned)T), dim3(256), 0, s, x1, heads1, static_cast<uint8_t*>(p1),
+                     x2, heads2, static_cast<uint8_t*>(p2), S, d, inv, inverse);
   return hipGetLastError();
 }
 

@@ -450,8 +450,11 @@ class Decoder:
                            self.o32.data_ptr(), self.do.data_ptr(), self.lse.data_ptr(), self.B,
                            self.S, c["heads"], c["kv_heads"], c["head_dim"], self.dq.data_ptr(),
                            self.dk.data_ptr(), self.dv.data_ptr(), *self._ws(), s)
+        # the inverse rotation also leaves dq and dk packed for the q / k backward
         nf4s_rope_pair(self.dq.data_ptr(), c["heads"], self.dk.data_ptr(), c["kv_heads"], M, self.S,
-                       c["head_dim"], c["rope_theta"], 1, s)
+                       c["head_dim"], c["rope_theta"], 1, s,
+                       q_packed=self._produced(self.dq, c["heads"] * c["head_dim"]),
+                       k_packed=self._produced(self.dk, c["kv_heads"] * c["head_dim"], second=True))
         dn = self._bwd(base, i, ("q", "k", "v"), self.n1, (self.dq, self.dk, self.dv), self.dnx)
         nf4s_rmsnorm_bwd([x.data_ptr() for x in dn], self.h[i].data_ptr(),
                          self.norms["attn"][i].data_ptr(), self.rstd1.data_ptr(), M, H, 1,

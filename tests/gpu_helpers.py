@@ -64,3 +64,15 @@ def sections(shard: torch.Tensor, d):
 
 def stream():
     return torch.cuda.current_stream().cuda_stream
+
+
+def packed_rows_below(pk, M, K):
+    """The bytes of a fragment-order buffer that hold rows < M."""
+    Mp, Kp = -(-M // 256) * 256, -(-K // 64) * 64
+    KB = Kp // 16
+    idx = np.arange(Mp * Kp * 2 // 16)            # 16-byte chunks
+    lane = idx % 64
+    frag = idx // 64
+    row = 32 * (frag // KB) + lane % 32
+    keep = np.repeat(row < M, 16)
+    return pk[keep]

@@ -471,6 +471,8 @@ def test_rope_pair_argument_errors():
     assert _err(f, FAKE, 4, FAKE + 2, 2, 8, 4, 32, 1e4, 0) == L.EALIGN
     assert _err(f, FAKE, 4, None, 2, 8, 4, 32, 1e4, 0) == L.EINVAL
     assert _err(f, FAKE, 4, FAKE, 2, 8, 4, 32, 1e4, 2) == L.EINVAL        # inverse
+    assert _err(f, FAKE, 4, FAKE, 2, 8, 4, 32, 1e4, 0, 0, FAKE + 64) == L.EALIGN   # packed copy
+    assert _err(f, FAKE, 4, FAKE, 2, 8, 4, 32, 1e4, 0, 0, None, FAKE + 8) == L.EALIGN
 
 
 def test_fused_swiglu_refuses_split_shapes_and_bad_arguments():

@@ -28,7 +28,8 @@ from layer_streamed_nf4_amd.decoder import Decoder
 from layer_streamed_nf4_amd.stack import PROJ, ShardSet
 from oracle import decoder as D
 from oracle import nf4
-from tests.gpu_helpers import bits_to_f32, dev_bf16bits, dev_f32, host_u16, require_gpu, stream, ws_tensor
+from tests.gpu_helpers import (bits_to_f32, dev_bf16bits, dev_f32, host_u16, packed_rows_below, require_gpu,
+                               stream, ws_tensor)
 
 pytestmark = pytest.mark.gpu
 
@@ -111,21 +112,34 @@ def test_rope_and_inverse(B, S, heads, d, theta):
     _check_bf16(host_u16(xd), ref_inv, abs_slack=1e-6, what="rope inverse")
 
 
-@pytest.mark.parametrize("S,hq,hk,d", [(70, 4, 2, 32), (512, 32, 8, 128), (7, 9, 3, 64)])
+@pytest.mark.parametrize("S,hq,hk,d", [(70, 4, 2, 32), (512, 32, 8, 128), (7, 9, 3, 64), (9, 5, 3, 24)])
 @pytest.mark.parametrize("inverse", [0, 1])
 def test_rope_pair_equals_two_single_calls(S, hq, hk, d, inverse):
-    """Queries and keys in one launch: the bits of one nf4s_rope per tensor."""
+    """Queries and keys in one launch: the bits of one nf4s_rope per tensor,
+    and the packed copies the bytes nf4s_pack_activation makes of the results
+    (rows below T; with d = 24 the widths 120 and 72 end inside a 64-column
+    step, whose tail must read zero)."""
     require_gpu()
+    print(f"rope pair S={S} heads {hq}/{hk} d={d} inverse={inverse}", flush=True)
     g = _rng(30 + d)
     T = 2 * S
     q, k = _bits(g.standard_normal((T, hq * d))), _bits(g.standard_normal((T, hk * d)))
     q1, k1, q2, k2 = dev_bf16bits(q), dev_bf16bits(k), dev_bf16bits(q), dev_bf16bits(k)
+    nq, nk = L.nf4s_packed_activation_bytes(T, hq * d), L.nf4s_packed_activation_bytes(T, hk * d)
+    pq, pk = (torch.full((n,), 0x7F, dtype=torch.uint8, device="cuda") for n in (nq, nk))
+    rq, rk = (torch.full((n,), 0x7F, dtype=torch.uint8, device="cuda") for n in (nq, nk))
     s = stream()
-    L.nf4s_rope_pair(q1.data_ptr(), hq, k1.data_ptr(), hk, T, S, d, 10000.0, inverse, s)
+    L.nf4s_rope_pair(q1.data_ptr(), hq, k1.data_ptr(), hk, T, S, d, 10000.0, inverse, s,
+                     q_packed=pq.data_ptr(), k_packed=pk.data_ptr())
     L.nf4s_rope(q2.data_ptr(), T, S, hq, d, 10000.0, inverse, s)
     L.nf4s_rope(k2.data_ptr(), T, S, hk, d, 10000.0, inverse, s)
+    L.nf4s_pack_activation(q2.data_ptr(), T, hq * d, rq.data_ptr(), nq, s)
+    L.nf4s_pack_activation(k2.data_ptr(), T, hk * d, rk.data_ptr(), nk, s)
     torch.cuda.synchronize()
     assert torch.equal(q1, q2) and torch.equal(k1, k2)
+    for got, ref, K in ((pq, rq, hq * d), (pk, rk, hk * d)):
+        assert np.array_equal(packed_rows_below(got.cpu().numpy(), T, K),
+                              packed_rows_below(ref.cpu().numpy(), T, K))
 
 
 ATTN_CASES = [

@@ -14,7 +14,8 @@ import torch
 import layer_streamed_nf4_amd as L
 import synth
 from oracle import decoder as D, linear, nf4
-from tests.gpu_helpers import bits_to_f32, dev_bf16bits, dev_f32, host_u16, require_gpu, stream, ws_tensor
+from tests.gpu_helpers import (bits_to_f32, dev_bf16bits, dev_f32, host_u16, packed_rows_below, require_gpu,
+                               stream, ws_tensor)
 
 pytestmark = pytest.mark.gpu
 R, S = 16, 2.0
@@ -79,18 +80,6 @@ def _run(width, k, M, layer, lora):
                 ref_pk=ref_pk.cpu().numpy(), g=host_u16(g), u=host_u16(u_), pairs=pairs)
 
 
-def _packed_rows_below(pk, M, K):
-    """The bytes of a fragment-order buffer that hold rows < M."""
-    Mp, Kp = -(-M // 256) * 256, -(-K // 64) * 64
-    KB = Kp // 16
-    idx = np.arange(Mp * Kp * 2 // 16)            # 16-byte chunks
-    lane = idx % 64
-    frag = idx // 64
-    row = 32 * (frag // KB) + lane % 32
-    keep = np.repeat(row < M, 16)
-    return pk[keep]
-
-
 @pytest.mark.parametrize("M,lora,layer", [(512, (), 1), (512, ("gate", "up"), 2), (700, ("up",), 3),
                                           (2048, ("gate", "up"), 4)])
 def test_fused_swiglu_equals_grouped_then_swiglu(M, lora, layer):
@@ -99,8 +88,8 @@ def test_fused_swiglu_equals_grouped_then_swiglu(M, lora, layer):
     assert L.nf4s_swiglu_fused_supported(M, width, k)
     got = _run(width, k, M, layer, lora)
     assert np.array_equal(got["out"], got["ref"])
-    a = _packed_rows_below(got["out_pk"], M, width)
-    b = _packed_rows_below(got["ref_pk"], M, width)
+    a = packed_rows_below(got["out_pk"], M, width)
+    b = packed_rows_below(got["ref_pk"], M, width)
     assert np.array_equal(a, b)
     if M == 700:
         # against the oracle: silu(g) * u of its own fp64 products, bf16-rounded where the path rounds

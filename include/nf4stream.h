@@ -533,8 +533,11 @@ int nf4s_rope_pair(uint16_t* q, int q_heads, uint16_t* k, int k_heads, int64_t T
  * bytes (rowsum and per-head fp32 partials of dk, dv, summed per group in
  * head order). The products run on the matrix cores with P and dS split into
  * bf16 high + low parts (about 16 significant bits), fp32 accumulation.
- * head_dim in {32, 64, 128}; heads % kv_heads == 0; every tensor argument
- * except lse 16-byte aligned. Errors: EINVAL, ESHAPE, EALIGN, EWORKSPACE.
+ * dv_packed (nullable, 256-B aligned, nf4s_packed_activation_bytes(B*S,
+ * kv_heads*d) bytes): dv also as nf4s_pack_activation lays it out, for the v
+ * projection's backward. head_dim in {32, 64, 128}; heads % kv_heads == 0;
+ * every tensor argument except lse 16-byte aligned. Errors: EINVAL, ESHAPE,
+ * EALIGN, EWORKSPACE.
  */
 int nf4s_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
                        int64_t S, int heads, int kv_heads, int head_dim, uint16_t* o, float* o_f32,
@@ -542,7 +545,7 @@ int nf4s_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
 int nf4s_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* o_f32,
                        const uint16_t* dout, const float* lse, int64_t B, int64_t S, int heads,
                        int kv_heads, int head_dim, uint16_t* dq, uint16_t* dk, uint16_t* dv,
-                       void* ws, size_t ws_bytes, void* stream);
+                       void* dv_packed, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * SwiGLU: out = bf16(silu(g) * u), silu(z) = z / (1 + e^-z); backward from ds:

@@ -149,7 +149,7 @@ _SIG = {
     "nf4s_attention_fwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, _P, _P, _P, _P, _P]),
     "nf4s_attention_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_int,
-                                          ctypes.c_int, ctypes.c_int, _P, _P, _P, _P,
+                                          ctypes.c_int, ctypes.c_int, _P, _P, _P, _P, _P,
                                           ctypes.c_size_t, _P]),
     "nf4s_swiglu_fwd": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
     "nf4s_swiglu_bwd": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P]),
@@ -383,9 +383,9 @@ def nf4s_attention_fwd(q, k, v, B, S, heads, kv_heads, head_dim, o, o_f32, lse, 
 
 
 def nf4s_attention_bwd(q, k, v, o_f32, dout, lse, B, S, heads, kv_heads, head_dim, dq, dk, dv, ws,
-                       ws_bytes, stream=0):
+                       ws_bytes, stream=0, dv_packed=None):
     _check(lib().nf4s_attention_bwd(q, k, v, o_f32, dout, lse, B, S, heads, kv_heads, head_dim, dq,
-                                    dk, dv, ws, ws_bytes, stream))
+                                    dk, dv, dv_packed, ws, ws_bytes, stream))
 
 
 def nf4s_swiglu_fwd(g, u, T, width, out, stream=0, packed=None):

@@ -895,8 +895,9 @@ int nf4s_rope_pair(uint16_t* q, int q_heads, uint16_t* k, int k_heads, int64_t T
   if (!(theta > 1.0) || !std::isfinite(theta)) return fail(NF4S_EINVAL, "theta must be finite and > 1");
   if (inverse != 0 && inverse != 1) return fail(NF4S_EINVAL, "inverse must be 0 or 1");
   if ((rc = check_ptr(q, "q", 8)) || (rc = check_ptr(k, "k", 8))) return rc;
-  if (q_packed && (rc = check_ptr(q_packed, "q_packed", 256))) return rc;
-  if (k_packed && (rc = check_ptr(k_packed, "k_packed", 256))) return rc;
+  if ((rc = check_packed_out(q_packed, T, (int64_t)q_heads * head_dim)) ||
+      (rc = check_packed_out(k_packed, T, (int64_t)k_heads * head_dim)))
+    return rc;
   return launched(launch_rope_pair(q, q_heads, k, k_heads, T, S, head_dim, theta, inverse, q_packed,
                                    k_packed, static_cast<hipStream_t>(stream)),
                   "rope launch");
@@ -935,17 +936,17 @@ int nf4s_attention_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
 int nf4s_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* o_f32,
                        const uint16_t* dout, const float* lse, int64_t B, int64_t S, int heads,
                        int kv_heads, int head_dim, uint16_t* dq, uint16_t* dk, uint16_t* dv,
-                       void* ws, size_t ws_bytes, void* stream) {
+                       void* dv_packed, void* ws, size_t ws_bytes, void* stream) {
   int rc;
   if ((rc = check_attention(B, S, heads, kv_heads, head_dim))) return rc;
   if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k, "k")) || (rc = check_ptr(v, "v")) ||
       (rc = check_ptr(o_f32, "o_f32")) || (rc = check_ptr(dout, "dout")) ||
       (rc = check_ptr(lse, "lse", 4)) || (rc = check_ptr(dq, "dq")) || (rc = check_ptr(dk, "dk")) ||
-      (rc = check_ptr(dv, "dv")))
+      (rc = check_ptr(dv, "dv")) || (rc = check_packed_out(dv_packed, B * S, (int64_t)kv_heads * head_dim)))
     return rc;
   if ((rc = check_ws(ws, ws_bytes, attention_bwd_ws_bytes(B, S, heads, head_dim)))) return rc;
   return launched(launch_attention_bwd(q, k, v, o_f32, dout, lse, B, S, heads, kv_heads, head_dim, dq,
-                                       dk, dv, ws, static_cast<hipStream_t>(stream)),
+                                       dk, dv, dv_packed, ws, static_cast<hipStream_t>(stream)),
                   "attention_bwd launch");
 }
 

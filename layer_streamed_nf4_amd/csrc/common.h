@@ -168,7 +168,7 @@ size_t attention_bwd_ws_bytes(int64_t B, int64_t S, int H, int D);
 hipError_t launch_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const float* o_f32, const uint16_t* dout, const float* lse,
                                 int64_t B, int64_t S, int H, int Hkv, int D, uint16_t* dq,
-                                uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s);
+                                uint16_t* dk, uint16_t* dv, void* dv_packed, void* ws, hipStream_t s);
 hipError_t launch_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t T, int64_t W,
                              uint16_t* out, void* packed, hipStream_t s);
 hipError_t launch_swiglu_bwd(const uint16_t* ds, const uint16_t* g, const uint16_t* u, int64_t T,

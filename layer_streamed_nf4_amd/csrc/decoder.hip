@@ -818,12 +818,15 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restr
 }
 
 // dk[row, g, :] = bf16(sum over the heads of group g, in head order, of the
-// per-head partials); one thread per (row, kv head, 4 dims).
+// per-head partials); one thread per (row, kv head, 4 dims). dv_packed
+// (nullable): dv also in MFMA fragment order (K = Hkv * D), as k_frag_pack
+// lays it out, for the v projection's backward.
 __global__ __launch_bounds__(256) void k_attn_group_sum(const float* __restrict__ pk,
                                                         const float* __restrict__ pv, int64_t T,
                                                         int H, int Hkv, int D,
                                                         uint16_t* __restrict__ dk,
-                                                        uint16_t* __restrict__ dv) {
+                                                        uint16_t* __restrict__ dv,
+                                                        uint8_t* __restrict__ dv_packed) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t n4 = T * Hkv * (D / 4);
   if (i >= n4) return;
@@ -848,6 +851,13 @@ __global__ __launch_bounds__(256) void k_attn_group_sum(const float* __restrict_
   wv.y = pack_bf16x2(sv.z, sv.w);
   *reinterpret_cast<uint2*>(dk + out) = wk;
   *reinterpret_cast<uint2*>(dv + out) = wv;
+  if (dv_packed) {
+    // four consecutive columns are one half of a fragment's 16-byte slot
+    const int64_t K = (int64_t)Hkv * D, kb = (K + 63) / 64 * 4;
+    const int64_t c = (int64_t)g * D + 4 * d4;
+    *reinterpret_cast<uint2*>(dv_packed + frag_offset(row, c & ~7ll, kb) + (c & 7) * 2) = wv;
+    if (g == Hkv - 1 && d4 == 0) frag_zero_tail(dv_packed, row, K, kb);
+  }
 }
 
 // ---- elementwise ------------------------------------------------------------
@@ -1226,7 +1236,7 @@ size_t attention_bwd_ws_bytes(int64_t B, int64_t S, int H, int D) {
 hipError_t launch_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const float* o_f32, const uint16_t* dout, const float* lse,
                                 int64_t B, int64_t S, int H, int Hkv, int D, uint16_t* dq,
-                                uint16_t* dk, uint16_t* dv, void* ws, hipStream_t s) {
+                                uint16_t* dk, uint16_t* dv, void* dv_packed, void* ws, hipStream_t s) {
   const size_t rows = (size_t)(B * S);
   uint8_t* w = static_cast<uint8_t*>(ws);
   float* dsum = reinterpret_cast<float*>(w);
@@ -1242,7 +1252,7 @@ hipError_t launch_attention_bwd(const uint16_t* q, const uint16_t* k, const uint
 #undef CALL
   const int64_t n4 = (int64_t)rows * Hkv * (D / 4);
   hipLaunchKernelGGL(k_attn_group_sum, dim3(grid_of(n4)), dim3(256), 0, s, pk, pv, (int64_t)rows, H,
-                     Hkv, D, dk, dv);
+                     Hkv, D, dk, dv, static_cast<uint8_t*>(dv_packed));
   return hipGetLastError();
 }
 #undef NF4S_DISPATCH_D

@@ -201,6 +201,7 @@ class Decoder:
         self.packed_c = torch.empty(_round_up(pk_layer), dtype=torch.uint8, device=dev)
         self._packed_key = None
         self._packed_key_b = None
+        self._packed_key_c = None
 
         self.pool = None
         if mode == "streamed":
@@ -239,15 +240,21 @@ class Decoder:
         key = (a.data_ptr(), K)
         if key == self._packed_key_b:
             return self.packed_b.data_ptr()
+        if key == self._packed_key_c:
+            return self.packed_c.data_ptr()
         if key != self._packed_key:
             nf4s_pack_activation(a.data_ptr(), self.M, K, self.packed.data_ptr(), self.packed.numel(),
                                  self._s)
             self._packed_key = key
         return self.packed.data_ptr()
 
-    def _produced(self, a, K, second=False):
+    def _produced(self, a, K, second=False, third=False):
         """Mark a (bf16 [M, K]) as written packed by its producer into the main
-        (or second) buffer; returns that buffer's pointer for the producer."""
+        (or second, or third) buffer; returns that buffer's pointer for the
+        producer."""
+        if third:
+            self._packed_key_c = (a.data_ptr(), K)
+            return self.packed_c.data_ptr()
         if second:
             self._packed_key_b = (a.data_ptr(), K)
             return self.packed_b.data_ptr()
@@ -322,12 +329,12 @@ class Decoder:
     def _pack_group(self, dys, nos):
         """Packed pointers of the dys, one buffer each: those their producer
         wrote packed, the others packed now into the buffers left free."""
-        bufs = [(self.packed, "_packed_key"), (self.packed_b, "_packed_key_b"), (self.packed_c, None)]
+        bufs = [(self.packed, "_packed_key"), (self.packed_b, "_packed_key_b"), (self.packed_c, "_packed_key_c")]
         keys = [(dy.data_ptr(), no) for dy, no in zip(dys, nos)]
         out, used = [None] * len(dys), set()
         for j, key in enumerate(keys):
             for bi, (buf, attr) in enumerate(bufs):
-                if bi not in used and attr is not None and getattr(self, attr) == key:
+                if bi not in used and getattr(self, attr) == key:
                     out[j] = buf.data_ptr()
                     used.add(bi)
                     break
@@ -337,8 +344,7 @@ class Decoder:
                 buf, attr = bufs[bi]
                 nf4s_pack_activation(dys[j].data_ptr(), self.M, nos[j], buf.data_ptr(), buf.numel(),
                                      self._s)
-                if attr is not None:
-                    setattr(self, attr, key)
+                setattr(self, attr, key)
                 used.add(bi)
                 out[j] = buf.data_ptr()
         return out
@@ -393,7 +399,7 @@ class Decoder:
         hin/hout default to the checkpoints h_i, h_{i+1}."""
         c, s, M = self.cfg, self._s, self.M
         H = self.H
-        self._packed_key = self._packed_key_b = None
+        self._packed_key = self._packed_key_b = self._packed_key_c = None
         hin = self.h[i] if hin is None else hin
         hout = self.h[i + 1] if hout is None else hout
         a = adapters
@@ -432,7 +438,7 @@ class Decoder:
         packed_c) and dL/dh_i on exit (likewise, for i > 0); the layer's body
         was just recomputed (with the fp32 attention output kept)."""
         c, s, M, H = self.cfg, self._s, self.M, self.H
-        self._packed_key = self._packed_key_b = None
+        self._packed_key = self._packed_key_b = self._packed_key_c = None
         self._bwd(base, i, ("down",), self.sw, (self.dd,), (self.dsw,),
                   dy_packed=self.packed_c.data_ptr())
         nf4s_swiglu_bwd(self.dsw.data_ptr(), self.g.data_ptr(), self.u_.data_ptr(), M, self.I,
@@ -449,13 +455,15 @@ class Decoder:
         nf4s_attention_bwd(self.q.data_ptr(), self.k.data_ptr(), self.vv.data_ptr(),
                            self.o32.data_ptr(), self.do.data_ptr(), self.lse.data_ptr(), self.B,
                            self.S, c["heads"], c["kv_heads"], c["head_dim"], self.dq.data_ptr(),
-                           self.dk.data_ptr(), self.dv.data_ptr(), *self._ws(), s)
+                           self.dk.data_ptr(), self.dv.data_ptr(), *self._ws(), s,
+                           dv_packed=self._produced(self.dv, c["kv_heads"] * c["head_dim"], third=True))
         # the inverse rotation also leaves dq and dk packed for the q / k backward
         nf4s_rope_pair(self.dq.data_ptr(), c["heads"], self.dk.data_ptr(), c["kv_heads"], M, self.S,
                        c["head_dim"], c["rope_theta"], 1, s,
                        q_packed=self._produced(self.dq, c["heads"] * c["head_dim"]),
                        k_packed=self._produced(self.dk, c["kv_heads"] * c["head_dim"], second=True))
         dn = self._bwd(base, i, ("q", "k", "v"), self.n1, (self.dq, self.dk, self.dv), self.dnx)
+        self._packed_key_c = None  # packed_c now receives dL/dh_i for the next layer's down projection
         nf4s_rmsnorm_bwd([x.data_ptr() for x in dn], self.h[i].data_ptr(),
                          self.norms["attn"][i].data_ptr(), self.rstd1.data_ptr(), M, H, 1,
                          self.dh.data_ptr(), s, y=self.dd.data_ptr() if i > 0 else None,
@@ -469,7 +477,7 @@ class Decoder:
     def _head_fwd(self, h_last):
         """Final norm and the resident lm_head: self.logits from h_L."""
         c, M, H, V, s = self.cfg, self.M, self.H, self.V, self._s
-        self._packed_key = self._packed_key_b = None
+        self._packed_key = self._packed_key_b = self._packed_key_c = None
         nf4s_rmsnorm_fwd(h_last.data_ptr(), self.norms["final"].data_ptr(), M, H, c["eps"],
                          self.hn.data_ptr(), self.rstd_f.data_ptr(), s, packed=self._produced(self.hn, H))
         dense_linear_fwd_packed(self.lm_head.data_ptr(), V, H, self._pack(self.hn, H), M,
@@ -493,7 +501,7 @@ class Decoder:
         """From self.dlogits: lm_head and final norm backward, then the
         backward sweep that recomputes each layer and differentiates it."""
         M, H, V, s, L = self.M, self.H, self.V, self._s, self.L
-        self._packed_key = self._packed_key_b = None
+        self._packed_key = self._packed_key_b = self._packed_key_c = None
         dense_linear_bwd_packed(self.lm_head.data_ptr(), V, H, self._pack(self.dlogits, V), M,
                                 self.dhn.data_ptr(), *self._ws(), s)
         # (every norm backward of the sweep also leaves dh as bf16 dd, packed

@@ -266,6 +266,8 @@ def test_decoder_argument_errors():
     assert _err(L.nf4s_attention_fwd, FAKE, FAKE, FAKE, 1, 4, 4, 2, 16, FAKE, None, FAKE) == L.ESHAPE
     assert _err(L.nf4s_attention_bwd, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 4, 2, 32, FAKE, FAKE,
                 FAKE, None, 0) == L.EWORKSPACE
+    assert _err(L.nf4s_attention_bwd, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 4, 2, 32, FAKE, FAKE,
+                FAKE, FAKE, 1 << 30, 0, FAKE + 16) == L.EALIGN                  # packed dv
     assert _err(L.nf4s_rmsnorm_bwd, [], FAKE, FAKE, FAKE, 4, 8, 0, FAKE) == L.EINVAL
     assert _err(L.nf4s_rmsnorm_bwd, [FAKE] * 4, FAKE, FAKE, FAKE, 4, 8, 0, FAKE) == L.EINVAL
     assert _err(L.nf4s_rmsnorm_bwd, [FAKE], FAKE, FAKE, FAKE, 4, 8, 2, FAKE) == L.EINVAL

@@ -167,10 +167,17 @@ def test_attention_fwd_bwd(B, S, H, Hkv, d):
     dk = torch.empty_like(kd)
     dv = torch.empty_like(vd)
     ws = ws_tensor(L.nf4s_workspace_bytes(L.OP_ATTENTION_BWD, B * S, H, d))
+    nv = L.nf4s_packed_activation_bytes(B * S, Hkv * d)
+    dvp, dvr = (torch.full((nv,), 0x7F, dtype=torch.uint8, device="cuda") for _ in range(2))
     L.nf4s_attention_bwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o32.data_ptr(), dod.data_ptr(),
                          lse.data_ptr(), B, S, H, Hkv, d, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                         ws.data_ptr(), ws.numel(), stream())
+                         ws.data_ptr(), ws.numel(), stream(), dv_packed=dvp.data_ptr())
+    # the packed copy of dv: the bytes nf4s_pack_activation makes of it (rows below B*S;
+    # kv_heads*d = 32 ends inside a 64-column step, whose tail must read zero)
+    L.nf4s_pack_activation(dv.data_ptr(), B * S, Hkv * d, dvr.data_ptr(), nv, stream())
     torch.cuda.synchronize()
+    assert np.array_equal(packed_rows_below(dvp.cpu().numpy(), B * S, Hkv * d),
+                          packed_rows_below(dvr.cpu().numpy(), B * S, Hkv * d))
     q4, k4, v4, do4 = (_vals(a).reshape(B, S, -1, d) for a in (q, k, v, do))
     ref_o, P = D.attention(q4, k4, v4, H // Hkv)
     _check_f32(o32.cpu().numpy().reshape(ref_o.shape), ref_o, what="o32")

@@ -660,12 +660,20 @@ int nf4s_stream_wait_event(void* stream, void* event);
  *   nf4s_pool_acquire:  make `layer` resident (copying now if needed, into an
  *                       empty, else unreserved, else reserved slot, least
  *                       recently used first), make the compute stream wait
- *                       for it, return its slot.
+ *                       for it, return its slot. It may block the calling
+ *                       thread until that slot's copy is enqueued (below).
  *   nf4s_pool_release:  record the slot's free event on the compute stream
  *                       after the last kernel that reads it was enqueued.
  *   nf4s_pool_stats:    copies issued and bytes copied so far.
  * prefetch, acquire and release return ESLOT for a layer index that was never
  * registered (negative included).
+ * Copies are enqueued on the copy stream by a host thread the pool owns, in
+ * the order they were asked for, each once the free event it follows has
+ * completed on the device (so the copy stream never waits on a pending
+ * event, which costs tens of microseconds per copy); the host sources must
+ * stay valid until then. A failure of that thread is returned by the next
+ * prefetch, acquire or release. nf4s_pool_destroy lets it enqueue what was
+ * asked, then stops it.
  *   nf4s_pool_set_debug: NF4S_POOL_POISON_ON_RELEASE makes every release also
  *                       overwrite the slot with 0xFF bytes (NaN block scales)
  *                       on the copy stream, ordered after the free event as a

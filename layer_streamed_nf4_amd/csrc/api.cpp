@@ -4,8 +4,12 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <condition_variable>
 #include <cstring>
+#include <deque>
+#include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "common.h"
@@ -1093,6 +1097,15 @@ int nf4s_stream_wait_event(void* stream, void* event) {
 
 // ---- slot pool -----------------------------------------------------------
 
+// The pool's copies are enqueued on the copy stream by a host thread of its
+// own (the issuer), each only once the free event it must follow has
+// completed, so the copy stream never holds a wait on a pending event: the
+// runtime resolves such a wait tens of microseconds after the event
+// completes, a gap before every layer copy of a copy-bound sweep (measured
+// on MI355X: a median 68 us between back-to-back 112.5 MB copies). The
+// issuer takes requests in order; an acquire waits on the host until the
+// copy (and ready event) of its slot is enqueued, then makes the compute
+// stream wait for the ready event as before.
 struct nf4s_pool {
   struct Slot {
     void* ptr = nullptr;
@@ -1103,18 +1116,35 @@ struct nf4s_pool {
     bool reserved = false;       // prefetched (or asked for again) and not yet acquired
     bool free_recorded = false;  // a free event exists to wait on
     uint64_t last_use = 0;       // 0 = never, or emptied
+    uint64_t asked = 0;          // copies and fills requested of the issuer for this slot
+    uint64_t issued = 0;         // of those, the ones it has enqueued (under mu)
   };
   struct Layer {
     const void* src = nullptr;
     size_t bytes = 0;
   };
+  struct Job {
+    bool fill = false;  // poison fill instead of a copy
+    int slot = 0;
+    uint64_t seq = 0;   // the slot's request number
+    const void* src = nullptr;
+    size_t bytes = 0;
+    bool wait_free = false;
+  };
   int n = 0;
   size_t slot_bytes = 0;
   hipStream_t copy = nullptr, compute = nullptr;
+  int device = 0;
   int debug = 0;  // NF4S_POOL_POISON_ON_RELEASE
   Slot slots[8];
   std::vector<Layer> layers;
   uint64_t tick = 0, copies = 0, bytes = 0;
+  std::mutex mu;
+  std::condition_variable cv;  // a job queued, or a job enqueued on the copy stream
+  std::deque<Job> jobs;
+  bool stop = false;
+  hipError_t issue_error = hipSuccess;  // the first failure of the issuer
+  std::thread issuer;
 };
 
 namespace {
@@ -1149,17 +1179,73 @@ int pool_victim(const nf4s_pool* p, bool take_reserved) {
   return v;
 }
 
+// The issuer: wait for the slot's free event on the host, then enqueue the
+// copy and record the ready event (or enqueue the poison fill); requests in
+// the order they were made. Stops once asked to and every request is done.
+void pool_issue_loop(nf4s_pool* p) {
+  (void)hipSetDevice(p->device);
+  for (;;) {
+    nf4s_pool::Job j;
+    {
+      std::unique_lock<std::mutex> lk(p->mu);
+      p->cv.wait(lk, [p] { return p->stop || !p->jobs.empty(); });
+      if (p->jobs.empty()) return;
+      j = p->jobs.front();
+      p->jobs.pop_front();
+    }
+    auto& s = p->slots[j.slot];
+    hipError_t e = j.wait_free ? hipEventSynchronize(s.free) : hipSuccess;
+    if (e == hipSuccess) {
+      if (j.fill) {
+        e = launch_fill_u32(s.ptr, p->slot_bytes, 0xFFFFFFFFu, p->copy);
+      } else {
+        e = hipMemcpyAsync(s.ptr, j.src, j.bytes, hipMemcpyHostToDevice, p->copy);
+        if (e == hipSuccess) e = hipEventRecord(s.ready, p->copy);
+      }
+    }
+    {
+      std::lock_guard<std::mutex> lk(p->mu);
+      if (e != hipSuccess && p->issue_error == hipSuccess) p->issue_error = e;
+      s.issued = j.seq;
+    }
+    p->cv.notify_all();
+  }
+}
+
+void pool_request(nf4s_pool* p, nf4s_pool::Job j) {
+  auto& s = p->slots[j.slot];
+  j.seq = ++s.asked;
+  j.wait_free = s.free_recorded;
+  {
+    std::lock_guard<std::mutex> lk(p->mu);
+    p->jobs.push_back(j);
+  }
+  p->cv.notify_all();
+}
+
+// Block until every request for slot v is enqueued on the copy stream;
+// the issuer's first failure, if any.
+int pool_wait_issued(nf4s_pool* p, int v) {
+  auto& s = p->slots[v];
+  std::unique_lock<std::mutex> lk(p->mu);
+  p->cv.wait(lk, [&] { return s.issued == s.asked; });
+  if (p->issue_error != hipSuccess) return hip_fail(p->issue_error, "slot copy (pool issuer)");
+  return NF4S_OK;
+}
+
+int pool_issue_status(nf4s_pool* p) {
+  std::lock_guard<std::mutex> lk(p->mu);
+  return p->issue_error == hipSuccess ? NF4S_OK : hip_fail(p->issue_error, "slot copy (pool issuer)");
+}
+
 int pool_copy_into(nf4s_pool* p, int layer, int v) {
   auto& s = p->slots[v];
   const auto& L = p->layers[layer];
-  int rc = layer_prefetch(s.ptr, p->slot_bytes, L.src, L.bytes, p->copy,
-                          s.free_recorded ? s.free : nullptr, s.ready);
-  if (rc) {
-    s.layer = -1;  // the copy was not enqueued; whatever the slot held is unknown
-    s.reserved = false;
-    s.last_use = 0;
-    return rc;
-  }
+  nf4s_pool::Job j;
+  j.slot = v;
+  j.src = L.src;
+  j.bytes = L.bytes;
+  pool_request(p, j);
   s.layer = layer;
   s.last_use = ++p->tick;
   p->copies += 1;
@@ -1195,6 +1281,11 @@ int nf4s_pool_create(int n_slots, void* const* slots, size_t slot_bytes, void* c
   p->slot_bytes = slot_bytes;
   p->copy = static_cast<hipStream_t>(copy_stream);
   p->compute = static_cast<hipStream_t>(compute_stream);
+  hipError_t e0 = hipGetDevice(&p->device);
+  if (e0 != hipSuccess) {
+    delete p;
+    return hip_fail(e0, "hipGetDevice");
+  }
   for (int i = 0; i < n_slots; ++i) {
     p->slots[i].ptr = slots[i];
     hipError_t e1 = hipEventCreateWithFlags(&p->slots[i].ready, hipEventDisableTiming);
@@ -1204,12 +1295,21 @@ int nf4s_pool_create(int n_slots, void* const* slots, size_t slot_bytes, void* c
       return hip_fail(e1 != hipSuccess ? e1 : e2, "hipEventCreateWithFlags");
     }
   }
+  p->issuer = std::thread(pool_issue_loop, p);
   *out = p;
   return NF4S_OK;
 }
 
 int nf4s_pool_destroy(nf4s_pool* p) {
   if (!p) return NF4S_OK;
+  if (p->issuer.joinable()) {  // let the issuer enqueue what was asked, then stop it
+    {
+      std::lock_guard<std::mutex> lk(p->mu);
+      p->stop = true;
+    }
+    p->cv.notify_all();
+    p->issuer.join();
+  }
   for (int i = 0; i < p->n; ++i) {
     if (p->slots[i].ready) (void)hipEventDestroy(p->slots[i].ready);
     if (p->slots[i].free) (void)hipEventDestroy(p->slots[i].free);
@@ -1251,7 +1351,7 @@ int nf4s_pool_set_layer(nf4s_pool* p, int layer, const void* src, size_t bytes) 
 int nf4s_pool_prefetch(nf4s_pool* p, int layer) {
   if (!p) return fail(NF4S_EINVAL, "pool is NULL");
   int rc = pool_check_layer(p, layer);
-  if (rc) return rc;
+  if (rc || (rc = pool_issue_status(p))) return rc;
   const int i = pool_find(p, layer);
   if (i >= 0) {  // resident or in flight: keep it for its next reader
     if (!p->slots[i].held) p->slots[i].reserved = true;
@@ -1280,6 +1380,7 @@ int nf4s_pool_acquire(nf4s_pool* p, int layer, void** slot_dev_out) {
     if (i < 0) return fail(NF4S_ESLOT, "every slot is held; release one before acquiring layer %d", layer);
     if ((rc = pool_copy_into(p, layer, i))) return rc;
   }
+  if ((rc = pool_wait_issued(p, i))) return rc;
   auto& s = p->slots[i];
   hipError_t e = hipStreamWaitEvent(p->compute, s.ready, 0);
   if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
@@ -1302,17 +1403,18 @@ int nf4s_pool_release(nf4s_pool* p, int layer) {
   s.free_recorded = true;
   s.held = false;
   if (p->debug & NF4S_POOL_POISON_ON_RELEASE) {
-    // Overwrite the slot with NaN bytes on the copy stream, ordered after the
+    // Overwrite the slot with NaN bytes on the copy stream, issued after the
     // free event exactly as the next copy into the slot would be: a kernel
     // that still read the slot after its release would see NaN weights.
     s.layer = -1;
     s.reserved = false;
     s.last_use = 0;
-    if ((e = hipStreamWaitEvent(p->copy, s.free, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-    if ((e = launch_fill_u32(s.ptr, p->slot_bytes, 0xFFFFFFFFu, p->copy)) != hipSuccess)
-      return hip_fail(e, "poison fill launch");
+    nf4s_pool::Job j;
+    j.fill = true;
+    j.slot = i;
+    pool_request(p, j);
   }
-  return NF4S_OK;
+  return pool_issue_status(p);
 }
 
 int nf4s_pool_stats(const nf4s_pool* p, uint64_t* copies, uint64_t* bytes) {

@@ -192,7 +192,6 @@ hipError_t rowdot(bool trans_f, int n, const uint16_t* const* X, int64_t M, cons
 }
 
 constexpr int COL_WAVES = 16;
-constexpr int CUNR = 2;  // 16-row slices whose loads are issued together
 
 struct ColsSeg {
   const uint16_t* G;  // [M, N]
@@ -207,12 +206,23 @@ struct ColsArgs {
 // out(r0 + j, c) (+)= scale * sum_m L[m, r0 + j] * G[m, c] for one 32-column
 // tile of c; out is [r, N] (dA) or, with TRANS_OUT, [N, r] (dB).
 // MFMA view: C[rho, c] = sum_m L'[rho, m] G[m, c]. The waves take consecutive
-// stretches of M; loads of CUNR 16-row slices are issued before their MFMAs.
-// blockIdx.z = adapter.
+// stretches of M in 16-row slices. The contraction runs over M, which is G's
+// row index, while each lane of the B operand needs 8 consecutive rows of
+// one column: a wave reads its 16 x 32 slice of G with one 16-byte load per
+// lane (a row's 8 consecutive columns) and the 16 x 16 slice of L with four
+// 4-byte loads per lane, writes both into LDS of its own (G transposed), and
+// reads the operands back -- lanes of one wave, whose LDS accesses complete
+// in issue order, so no workgroup barrier is needed. blockIdx.z = adapter.
+constexpr int CT_STRIDE = 24;  // bf16 per transposed row (16 rows + 8 pad: 16-B reads, 2-way writes)
+constexpr int CL_STRIDE = 17;  // fp32 per staged L row
+constexpr int COL_WAVE_LDS = 32 * CT_STRIDE * 2 + 16 * CL_STRIDE * 4;  // bytes per wave
+constexpr int COL_SMEM = (COL_WAVES * COL_WAVE_LDS > COL_WAVES * 64 * 8 * 4) ? COL_WAVES * COL_WAVE_LDS
+                                                                              : COL_WAVES * 64 * 8 * 4;
+
 template <bool TRANS_OUT>
 __global__ __launch_bounds__(COL_WAVES * 64) void k_lora_cols(ColsArgs ca, int64_t M, int r,
                                                               float scale, int accumulate) {
-  __shared__ float s_part[COL_WAVES][64][8];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[COL_SMEM];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int64_t c0 = (int64_t)blockIdx.x * 32;
@@ -223,50 +233,49 @@ __global__ __launch_bounds__(COL_WAVES * 64) void k_lora_cols(ColsArgs ca, int64
   const uint16_t* __restrict__ G = sg.G;
   const float* __restrict__ Lm = sg.L;
   float* __restrict__ out = sg.out;
-  const int rho = lane & 31;
+  uint16_t* const Ts = reinterpret_cast<uint16_t*>(smem + wave * COL_WAVE_LDS);  // [32 c][CT_STRIDE]
+  float* const Ls = reinterpret_cast<float*>(smem + wave * COL_WAVE_LDS + 32 * CT_STRIDE * 2);  // [16 m][CL_STRIDE]
+  // loads: lane l takes slice row l / 4, columns 8 (l % 4) .. +8 of G and
+  // ranks 4 (l % 4) .. +4 of L
+  const int lrow = lane >> 2, lq = lane & 3;
+  const int64_t gc = c0 + 8 * lq;  // N % 8 == 0: the 8 columns are all in or all out
+  // operands: lane l is MFMA row / column l % 32, contraction half l / 32
+  const int rho = lane & 31, hf = lane >> 5;
   const bool lo = rho >= 16;
-  const int j = r0 + (rho & 15);
-  const int jc = j < r ? j : r - 1;
-  const int ms = (lane >> 5) * 8;
-  const int64_t c = c0 + rho;
-  const int64_t cc = c < N ? c : N - 1;  // columns past N are never stored
-  const int64_t per = ((M + COL_WAVES * 16 - 1) / (COL_WAVES * 16)) * 16;
-  const int64_t mb = wave * per;
+  const int per = (int)(((M + COL_WAVES * 16 - 1) / (COL_WAVES * 16)) * 16);
+  const int64_t mb = (int64_t)wave * per;
   const int64_t me = (mb + per < M) ? mb + per : M;
   f32x16_t acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-  // 32-bit element offsets from uniform bases (M * N < 2^31, checked on the host)
-  const uint32_t uN = (uint32_t)N;
-  const uint32_t ur = (uint32_t)r;
-  for (int64_t m1 = mb; m1 < me; m1 += 16 * CUNR) {
-    float f[CUNR][8];
-    uint32_t gq[CUNR][8];
+  for (int64_t m1 = mb; m1 < me; m1 += 16) {
+    const int64_t m = m1 + lrow;
+    const bool okm = m < me;
+    uint4 gv = make_uint4(0u, 0u, 0u, 0u);
+    if (okm && gc < N) gv = *reinterpret_cast<const uint4*>(G + m * N + gc);
+    float lv[4];
 #pragma unroll
-    for (int u = 0; u < CUNR; ++u) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int64_t m = m1 + 16 * u + ms + e;
-        const bool ok = m < me;
-        const uint32_t mcl = (uint32_t)(ok ? m : me - 1);
-        const float fv = Lm[mcl * ur + (uint32_t)jc];
-        const uint32_t gv = G[mcl * uN + (uint32_t)cc];
-        f[u][e] = (ok && j < r) ? fv : 0.0f;
-        gq[u][e] = ok ? gv : 0u;
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int jj = r0 + 4 * lq + q;
+      lv[q] = (okm && jj < r) ? Lm[m * r + jj] : 0.0f;
     }
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
-    for (int u = 0; u < CUNR; ++u) {
-      const bf16x8_t fa = frag_from_f32(f[u], lo);
-      uint4 gv;
-      gv.x = gq[u][0] | (gq[u][1] << 16);
-      gv.y = gq[u][2] | (gq[u][3] << 16);
-      gv.z = gq[u][4] | (gq[u][5] << 16);
-      gv.w = gq[u][6] | (gq[u][7] << 16);
-      const bf16x8_t fb = __builtin_bit_cast(bf16x8_t, gv);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc, 0, 0, 0);
-    }
+    for (int e = 0; e < 8; ++e)
+      Ts[(8 * lq + e) * CT_STRIDE + lrow] = (uint16_t)((e & 1) ? (gw[e >> 1] >> 16) : (gw[e >> 1] & 0xFFFFu));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Ls[lrow * CL_STRIDE + 4 * lq + q] = lv[q];
+    __builtin_amdgcn_wave_barrier();
+    const uint4 bv = *reinterpret_cast<const uint4*>(Ts + rho * CT_STRIDE + 8 * hf);
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = Ls[(8 * hf + e) * CL_STRIDE + (rho & 15)];
+    __builtin_amdgcn_wave_barrier();
+    const bf16x8_t fa = frag_from_f32(f, lo);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
   }
+  __syncthreads();  // every wave is done with its staging area before the partials reuse it
+  float (*s_part)[64][8] = reinterpret_cast<float (*)[64][8]>(smem);
 #pragma unroll
   for (int i = 0; i < 8; ++i) s_part[wave][lane][i] = acc[i] + acc[i + 8];
   __syncthreads();
@@ -274,12 +283,12 @@ __global__ __launch_bounds__(COL_WAVES * 64) void k_lora_cols(ColsArgs ca, int64
     const int64_t co = c0 + (lane & 31);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float s = s_part[0][lane][i];
-      for (int w = 1; w < COL_WAVES; ++w) s += s_part[w][lane][i];
+      float sacc = s_part[0][lane][i];
+      for (int w = 1; w < COL_WAVES; ++w) sacc += s_part[w][lane][i];
       const int jj = r0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
       if (co < N && jj < r) {
         float* o = TRANS_OUT ? out + co * r + jj : out + (int64_t)jj * N + co;
-        const float v = scale * s;
+        const float v = scale * sacc;
         *o = accumulate ? *o + v : v;
       }
     }

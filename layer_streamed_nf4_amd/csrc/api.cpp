@@ -1183,7 +1183,11 @@ int pool_victim(const nf4s_pool* p, bool take_reserved) {
 // copy and record the ready event (or enqueue the poison fill); requests in
 // the order they were made. Stops once asked to and every request is done.
 void pool_issue_loop(nf4s_pool* p) {
-  (void)hipSetDevice(p->device);
+  const hipError_t dev_e = hipSetDevice(p->device);  // the device is per thread
+  if (dev_e != hipSuccess) {
+    std::lock_guard<std::mutex> lk(p->mu);
+    p->issue_error = dev_e;
+  }
   for (;;) {
     nf4s_pool::Job j;
     {
@@ -1194,7 +1198,8 @@ void pool_issue_loop(nf4s_pool* p) {
       p->jobs.pop_front();
     }
     auto& s = p->slots[j.slot];
-    hipError_t e = j.wait_free ? hipEventSynchronize(s.free) : hipSuccess;
+    hipError_t e = dev_e;  // after a failure every request is still marked issued, never enqueued
+    if (e == hipSuccess && j.wait_free) e = hipEventSynchronize(s.free);
     if (e == hipSuccess) {
       if (j.fill) {
         e = launch_fill_u32(s.ptr, p->slot_bytes, 0xFFFFFFFFu, p->copy);

@@ -249,6 +249,61 @@ def test_pool_refuses_unregistered_layers_and_keeps_reservations():
         L.nf4s_pool_destroy(pool)
 
 
+def test_pool_copy_waits_for_the_release_on_the_device():
+    """A copy into a released slot is issued only once the compute stream has
+    passed the release: a reader queued behind ≈ms of compute before the
+    release still sees the old layer, and the next acquire sees the new one."""
+    require_gpu()
+    nbytes = 8 << 20
+    srcs = [torch.full((nbytes,), 5 * (i + 1), dtype=torch.uint8).pin_memory() for i in range(3)]
+    slots = [torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    cs = torch.cuda.Stream()
+    comp = torch.cuda.current_stream()
+    pool = L.nf4s_pool_create([t.data_ptr() for t in slots], nbytes, cs.cuda_stream, comp.cuda_stream)
+    a = torch.randn((4096, 4096), device="cuda", dtype=torch.bfloat16)
+    try:
+        for i in range(3):
+            L.nf4s_pool_set_layer(pool, i, srcs[i].data_ptr(), nbytes)
+        ptr0 = L.nf4s_pool_acquire(pool, 0)
+        slot0 = next(t for t in slots if t.data_ptr() == ptr0)
+        for _ in range(20):                                  # keep the compute stream busy
+            a = (a @ a) * (1.0 / 64)
+        seen = slot0.clone()                                 # queued behind the matmuls
+        L.nf4s_pool_release(pool, 0)
+        ptr1 = L.nf4s_pool_acquire(pool, 1)                  # the other slot
+        L.nf4s_pool_release(pool, 1)
+        L.nf4s_pool_prefetch(pool, 2)                        # evicts layer 0 (least recently used)
+        ptr2 = L.nf4s_pool_acquire(pool, 2)
+        assert ptr2 == ptr0 and ptr1 != ptr0
+        after = slot0.clone()
+        L.nf4s_pool_release(pool, 2)
+        torch.cuda.synchronize()
+        assert torch.equal(seen.cpu(), srcs[0])
+        assert torch.equal(after.cpu(), srcs[2])
+    finally:
+        torch.cuda.synchronize()
+        L.nf4s_pool_destroy(pool)
+
+
+def test_pool_destroy_issues_pending_copies():
+    """Copies asked for and never acquired are still enqueued before the pool
+    is destroyed (its issuer drains its requests, then stops)."""
+    require_gpu()
+    nbytes = 4 << 20
+    srcs = [torch.full((nbytes,), 3 * (i + 1), dtype=torch.uint8).pin_memory() for i in range(2)]
+    slots = [torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    cs = torch.cuda.Stream()
+    pool = L.nf4s_pool_create([t.data_ptr() for t in slots], nbytes, cs.cuda_stream,
+                              torch.cuda.current_stream().cuda_stream)
+    for i in range(2):
+        L.nf4s_pool_set_layer(pool, i, srcs[i].data_ptr(), nbytes)
+        L.nf4s_pool_prefetch(pool, i)
+    L.nf4s_pool_destroy(pool)
+    cs.synchronize()
+    got = sorted(int(t[0].item()) for t in slots)
+    assert got == [3, 6] and all(torch.equal(t.cpu(), srcs[(int(t[0].item()) // 3) - 1]) for t in slots)
+
+
 def test_poisoned_release_is_never_read():
     """With the pool's poison mode on, every released slot is overwritten with
     NaN block scales on the copy stream, ordered after its free event exactly

@@ -562,7 +562,7 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_fwd(const uint16_t* __restr
 // the partial dQ summed in wave order); also writes Dsum = dO . O (fp32) of
 // its queries for the key-side kernel.
 template <int D>
-__global__ __launch_bounds__(64 * AW, 1) void k_attn_dq(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * AW, 2) void k_attn_dq(const uint16_t* __restrict__ q,
                                                         const uint16_t* __restrict__ k,
                                                         const uint16_t* __restrict__ v,
                                                         const float* __restrict__ o_f32,
@@ -570,12 +570,11 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dq(const uint16_t* __restri
                                                         const float* __restrict__ lse, int64_t S,
                                                         int H, int Hkv, float* __restrict__ dsum,
                                                         uint16_t* __restrict__ dq) {
-  constexpr int KS = D / 16, DT = D / 32, WS = 2 * RM_ELEMS(D) + TR_ELEMS(D);
+  constexpr int KS = D / 16, DT = D / 32, WS = RM_ELEMS(D) + TR_ELEMS(D);
   __shared__ __attribute__((aligned(16))) uint16_t smem[AW * WS];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, hf = lane >> 5, c = lane & 31;
   uint16_t* const Ks = smem + wave * WS;
-  uint16_t* const Vs = Ks + RM_ELEMS(D);
-  uint16_t* const Kt = Vs + RM_ELEMS(D);
+  uint16_t* const Kt = Ks + RM_ELEMS(D);
   const int64_t nqb = (S + AB - 1) / AB;
   const int64_t b = blockIdx.x / (H * nqb);
   const int h = (int)((blockIdx.x / nqb) % H);
@@ -610,23 +609,23 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dq(const uint16_t* __restri
   for (int j = 0; j < DT; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
-  BlockRegs<D> rk, rv;
-  if (wave <= qb) {
-    load_block<D>(k, ldk, (int64_t)g * D, b * S, wave * AB, S, lane, rk);
-    load_block<D>(v, ldk, (int64_t)g * D, b * S, wave * AB, S, lane, rv);
-  }
+  // Two workgroups share a CU: the key block goes through LDS (row-major and
+  // transposed) without a register prefetch, and the value rows, which only
+  // ever serve as A operands of their own lane, come straight from memory.
   for (int64_t kb = wave; kb <= qb; kb += AW) {
-    store_block<D>(rk, Ks, Kt, lane);
-    store_block<D>(rv, Vs, nullptr, lane);
-    if (kb + AW <= qb) {
-      load_block<D>(k, ldk, (int64_t)g * D, b * S, (kb + AW) * AB, S, lane, rk);
-      load_block<D>(v, ldk, (int64_t)g * D, b * S, (kb + AW) * AB, S, lane, rv);
+    {
+      BlockRegs<D> rk;
+      load_block<D>(k, ldk, (int64_t)g * D, b * S, kb * AB, S, lane, rk);
+      store_block<D>(rk, Ks, Kt, lane);
     }
+    const int64_t key = kb * AB + c;
+    bf16x8_t vf[KS];
+    row_frags<D>(v + (b * S + (key < S ? key : S - 1)) * ldk + (int64_t)g * D, hf, vf);
     f32x16_t st = zero16(), dp = zero16();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       st = mfma32(frag_rm<D>(Ks, c, hf, kk), qf[kk], st);
-      dp = mfma32(frag_rm<D>(Vs, c, hf, kk), df[kk], dp);
+      dp = mfma32(vf[kk], df[kk], dp);
     }
     float ds[16];
 #pragma unroll
@@ -654,6 +653,7 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dq(const uint16_t* __restri
   }
   __syncthreads();
   float* part = reinterpret_cast<float*>(smem);  // [AW][64][DT * 16]
+  static_assert(AW * 64 * DT * 16 * 4 <= AW * WS * 2, "partial staging fits the LDS");
   park<DT * 16>(part, wave, lane, &acc[0][0]);
   __syncthreads();
   if (wave >= DT || qpos >= S) return;

@@ -80,18 +80,21 @@ def _run(width, k, M, layer, lora):
                 ref_pk=ref_pk.cpu().numpy(), g=host_u16(g), u=host_u16(u_), pairs=pairs)
 
 
-@pytest.mark.parametrize("M,lora,layer", [(512, (), 1), (512, ("gate", "up"), 2), (700, ("up",), 3),
-                                          (2048, ("gate", "up"), 4)])
-def test_fused_swiglu_equals_grouped_then_swiglu(M, lora, layer):
-    width, k = synth.SHAPES["8b"]["gate"]
-    print(f"fused swiglu M={M} lora={lora}", flush=True)
+@pytest.mark.parametrize("M,lora,layer,shape", [(512, (), 1, "8b"), (512, ("gate", "up"), 2, "8b"),
+                                                (700, ("up",), 3, "8b"), (2048, ("gate", "up"), 4, "8b"),
+                                                # 135M widths: 24 tiles of 64 + 64 columns for 512
+                                                # rows, a contraction of 9 steps (never split)
+                                                (300, ("gate",), 5, "135m"), (512, ("up",), 6, "135m")])
+def test_fused_swiglu_equals_grouped_then_swiglu(M, lora, layer, shape):
+    width, k = synth.SHAPES[shape]["gate"]
+    print(f"fused swiglu {shape} M={M} lora={lora}", flush=True)
     assert L.nf4s_swiglu_fused_supported(M, width, k)
     got = _run(width, k, M, layer, lora)
     assert np.array_equal(got["out"], got["ref"])
     a = packed_rows_below(got["out_pk"], M, width)
     b = packed_rows_below(got["ref_pk"], M, width)
     assert np.array_equal(a, b)
-    if M == 700:
+    if M in (700, 300):
         # against the oracle: silu(g) * u of its own fp64 products, bf16-rounded where the path rounds
         x = bits_to_f32(got["x"]).astype(np.float64)
         gu = {}

@@ -277,8 +277,9 @@ __global__ __launch_bounds__(256) void k_rope_rows(uint16_t* __restrict__ x1, in
 // The probabilities (and dS) feed the next product without moving: its
 // contraction index is taken in the order the score registers hold it --
 // step kk, lane half hf, slot e <-> position 16kk + 8(e/4) + 4hf + e%4 of the
-// 32-block -- and the other operand is read from a transposed LDS tile in
-// that same order (two 8-byte reads of four consecutive positions). P and dS
+// 32-block -- and the other operand is read in that same order from the
+// row-major LDS tile of its block, transposed by the LDS transpose read (two
+// reads of four consecutive positions; no transposed copy). P and dS
 // enter the matrix cores as a bf16 high part plus a bf16 low part (about 16
 // significant bits), K, Q, V and dO are bf16 already, and accumulation is
 // fp32, so the attention arithmetic keeps fp32-level accuracy.
@@ -346,33 +347,18 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ src, int
   }
 }
 
-// The block into LDS: row-major `rm` (row stride D + 8) and/or transposed
-// `tr` (tr[d * 36 + row]); 16-byte row-major stores, 8-byte transposed stores
-// of four consecutive rows.
-template <int D>
-__device__ __forceinline__ void store_block(const BlockRegs<D>& br, uint16_t* rm, uint16_t* tr,
-                                            int lane) {
-  constexpr int RS = D + 8, TS = 36, CH = D / 8;
+// The block into LDS, row-major with row stride RS: 16-byte stores.
+template <int D, int RS = D + 8>
+__device__ __forceinline__ void store_block(const BlockRegs<D>& br, uint16_t* rm, int lane) {
+  constexpr int CH = D / 8;
 #pragma unroll
   for (int x = 0; x < BlockRegs<D>::PER_LANE; ++x) {
     const int it = lane + 64 * x;
     if (it < BlockRegs<D>::ITEMS) {
       const int rg = it / CH, ch = it % CH;
-      if (rm != nullptr) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<u32x4_t*>(rm + (4 * rg + i) * RS + 8 * ch) = br.v[x][i];
-      }
-      if (tr != nullptr) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int sh = (e & 1) * 16;
-          uint2 w;
-          w.x = ((br.v[x][0][e >> 1] >> sh) & 0xFFFFu) | (((br.v[x][1][e >> 1] >> sh) & 0xFFFFu) << 16);
-          w.y = ((br.v[x][2][e >> 1] >> sh) & 0xFFFFu) | (((br.v[x][3][e >> 1] >> sh) & 0xFFFFu) << 16);
-          *reinterpret_cast<uint2*>(tr + (8 * ch + e) * TS + 4 * rg) = w;
-        }
-      }
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4_t*>(rm + (4 * rg + i) * RS + 8 * ch) = br.v[x][i];
     }
   }
 }
@@ -384,17 +370,31 @@ __device__ __forceinline__ bf16x8_t frag_rm(const uint16_t* rm, int c, int hf, i
   return *reinterpret_cast<const bf16x8_t*>(rm + c * (D + 8) + 16 * kk + 8 * hf);
 }
 
-// A operand from a transposed LDS tile: row d, contraction positions in the
-// score-register order of step kk.
-__device__ __forceinline__ bf16x8_t frag_tr(const uint16_t* tr, int d, int hf, int kk) {
-  const uint16_t* p = tr + d * 36 + 16 * kk + 4 * hf;
-  const uint2 lo = *reinterpret_cast<const uint2*>(p);
-  const uint2 hi = *reinterpret_cast<const uint2*>(p + 8);
+// A operand of the transposed products (row d = col0 + l%32, contraction
+// positions in the score-register order of step kk), read straight from a
+// row-major LDS tile (row = position, RS bf16 per row) with the LDS transpose
+// read ds_read_b64_tr_b16: within each group of 16 lanes, lane s gives the
+// address of 4 consecutive columns 4(s%4) .. of row s/4 and receives column s
+// of those 4 rows (element e from the lane that addressed row e). Lane l
+// thus gets column col0 + l%32 at positions 16kk + 4(l/32) + 0..3 and, from a
+// second read, + 8 .. + 11. RS = D + 16 puts 8 consecutive rows on disjoint
+// 8-bank spans (conflict-free); tiles that are also read row by row keep
+// D + 8, which is conflict-free for those reads.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+template <int RS>
+__device__ __forceinline__ bf16x8_t frag_trr(const uint16_t* rm, int col0, int lane, int kk) {
+  const int grp = lane >> 4, s = lane & 15;
+  const int row = 16 * kk + 4 * (grp >> 1) + (s >> 2);
+  const int col = col0 + 16 * (grp & 1) + 4 * (s & 3);
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(rm + row * RS + col));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(rm + (row + 8) * RS + col));
   u32x4_t u;
-  u[0] = lo.x;
-  u[1] = lo.y;
-  u[2] = hi.x;
-  u[3] = hi.y;
+  u[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  u[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  u[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  u[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
   return __builtin_bit_cast(bf16x8_t, u);
 }
 
@@ -412,7 +412,7 @@ __device__ __forceinline__ void row_frags(const uint16_t* __restrict__ rowp, int
 // are combined through LDS in wave order at the end.
 constexpr int AW = 4;
 constexpr int RM_ELEMS(int D) { return AB * (D + 8); }
-constexpr int TR_ELEMS(int D) { return D * 36; }
+constexpr int RV_ELEMS(int D) { return AB * (D + 16); }  // a tile read only transposed
 
 // Per-lane partial results of the AW waves go through LDS lane-major:
 // part[((w * 64 + lane) * NV) + i].
@@ -431,11 +431,12 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_fwd(const uint16_t* __restr
                                                          float* __restrict__ o_f32,
                                                          float* __restrict__ lse,
                                                          uint8_t* __restrict__ packed) {
-  constexpr int KS = D / 16, DT = D / 32, WS = RM_ELEMS(D) + TR_ELEMS(D);
-  __shared__ __attribute__((aligned(16))) uint16_t smem[AW * WS];
+  constexpr int KS = D / 16, DT = D / 32, WS = RM_ELEMS(D) + RV_ELEMS(D);
+  constexpr int STAGE = AW * 64 * (DT * 16 + 2) * 2;  // the waves' partial results (bf16 units)
+  __shared__ __attribute__((aligned(16))) uint16_t smem[AW * WS > STAGE ? AW * WS : STAGE];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, hf = lane >> 5, c = lane & 31;
   uint16_t* const Ks = smem + wave * WS;
-  uint16_t* const Vt = Ks + RM_ELEMS(D);
+  uint16_t* const Vs = Ks + RM_ELEMS(D);
   const int64_t nqb = (S + AB - 1) / AB;
   const int64_t b = blockIdx.x / (H * nqb);
   const int h = (int)((blockIdx.x / nqb) % H);
@@ -459,8 +460,8 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_fwd(const uint16_t* __restr
     load_block<D>(v, ldk, (int64_t)g * D, b * S, wave * AB, S, lane, rv);
   }
   for (int64_t kb = wave; kb <= qb; kb += AW) {
-    store_block<D>(rk, Ks, nullptr, lane);
-    store_block<D>(rv, nullptr, Vt, lane);
+    store_block<D>(rk, Ks, lane);
+    store_block<D, D + 16>(rv, Vs, lane);
     if (kb + AW <= qb) {
       load_block<D>(k, ldk, (int64_t)g * D, b * S, (kb + AW) * AB, S, lane, rk);
       load_block<D>(v, ldk, (int64_t)g * D, b * S, (kb + AW) * AB, S, lane, rv);
@@ -496,7 +497,7 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_fwd(const uint16_t* __restr
         f32x16_t a;
 #pragma unroll
         for (int r = 0; r < 16; ++r) a[r] = kk == 0 ? acc[j][r] * corr : acc[j][r];
-        const bf16x8_t va = frag_tr(Vt, 32 * j + c, hf, kk);
+        const bf16x8_t va = frag_trr<D + 16>(Vs, 32 * j, lane, kk);
         a = mfma32(va, ph, a);
         a = mfma32(va, pl, a);
 #pragma unroll
@@ -570,11 +571,11 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_dq(const uint16_t* __restri
                                                         const float* __restrict__ lse, int64_t S,
                                                         int H, int Hkv, float* __restrict__ dsum,
                                                         uint16_t* __restrict__ dq) {
-  constexpr int KS = D / 16, DT = D / 32, WS = RM_ELEMS(D) + TR_ELEMS(D);
-  __shared__ __attribute__((aligned(16))) uint16_t smem[AW * WS];
+  constexpr int KS = D / 16, DT = D / 32, WS = RM_ELEMS(D);
+  constexpr int STAGE = AW * 64 * DT * 16 * 2;  // the waves' partial dQ (bf16 units)
+  __shared__ __attribute__((aligned(16))) uint16_t smem[AW * WS > STAGE ? AW * WS : STAGE];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, hf = lane >> 5, c = lane & 31;
   uint16_t* const Ks = smem + wave * WS;
-  uint16_t* const Kt = Ks + RM_ELEMS(D);
   const int64_t nqb = (S + AB - 1) / AB;
   const int64_t b = blockIdx.x / (H * nqb);
   const int h = (int)((blockIdx.x / nqb) % H);
@@ -609,14 +610,15 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_dq(const uint16_t* __restri
   for (int j = 0; j < DT; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
-  // Two workgroups share a CU: the key block goes through LDS (row-major and
-  // transposed) without a register prefetch, and the value rows, which only
-  // ever serve as A operands of their own lane, come straight from memory.
+  // Two workgroups share a CU: the key block goes through LDS (row-major; the
+  // dQ product reads it transposed) without a register prefetch, and the
+  // value rows, which only ever serve as A operands of their own lane, come
+  // straight from memory.
   for (int64_t kb = wave; kb <= qb; kb += AW) {
     {
       BlockRegs<D> rk;
       load_block<D>(k, ldk, (int64_t)g * D, b * S, kb * AB, S, lane, rk);
-      store_block<D>(rk, Ks, Kt, lane);
+      store_block<D>(rk, Ks, lane);
     }
     const int64_t key = kb * AB + c;
     bf16x8_t vf[KS];
@@ -643,7 +645,7 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_dq(const uint16_t* __restri
         f32x16_t a;
 #pragma unroll
         for (int r = 0; r < 16; ++r) a[r] = acc[j][r];
-        const bf16x8_t ka = frag_tr(Kt, 32 * j + c, hf, kk);
+        const bf16x8_t ka = frag_trr<D + 8>(Ks, 32 * j, lane, kk);
         a = mfma32(ka, sh, a);
         a = mfma32(ka, sl, a);
 #pragma unroll
@@ -653,7 +655,7 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_dq(const uint16_t* __restri
   }
   __syncthreads();
   float* part = reinterpret_cast<float*>(smem);  // [AW][64][DT * 16]
-  static_assert(AW * 64 * DT * 16 * 4 <= AW * WS * 2, "partial staging fits the LDS");
+  static_assert(AW * 64 * DT * 16 * 4 <= sizeof(smem), "partial staging fits the LDS");
   park<DT * 16>(part, wave, lane, &acc[0][0]);
   __syncthreads();
   if (wave >= DT || qpos >= S) return;
@@ -689,14 +691,13 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restr
                                                          int H, int Hkv, float* __restrict__ pk,
                                                          float* __restrict__ pv) {
   constexpr int KS = D / 16, DT = D / 32;
-  constexpr int WS = 2 * RM_ELEMS(D) + 2 * TR_ELEMS(D) + 4 * AB;  // + lse and Dsum (fp32) of the block
-  __shared__ __attribute__((aligned(16))) uint16_t smem[AW * WS];
+  constexpr int WS = 2 * RM_ELEMS(D) + 4 * AB;  // + lse and Dsum (fp32) of the block
+  constexpr int STAGE = AW * 64 * 2 * DT * 16 * 2;  // the waves' partial dK, dV (bf16 units)
+  __shared__ __attribute__((aligned(16))) uint16_t smem[AW * WS > STAGE ? AW * WS : STAGE];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, hf = lane >> 5, c = lane & 31;
   uint16_t* const Qs = smem + wave * WS;
   uint16_t* const Os = Qs + RM_ELEMS(D);
-  uint16_t* const Qt = Os + RM_ELEMS(D);
-  uint16_t* const Ot = Qt + TR_ELEMS(D);
-  float* const Ls = reinterpret_cast<float*>(Ot + TR_ELEMS(D));
+  float* const Ls = reinterpret_cast<float*>(Os + RM_ELEMS(D));
   float* const Dl = Ls + AB;
   const int64_t nkb = (S + AB - 1) / AB;
   const int64_t b = blockIdx.x / (H * nkb);
@@ -725,8 +726,8 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restr
     load_block<D>(dout, ldq, (int64_t)h * D, b * S, q0 * AB, S, lane, ro);
   }
   for (int64_t qb = q0; qb < nkb; qb += AW) {
-    store_block<D>(rq, Qs, Qt, lane);
-    store_block<D>(ro, Os, Ot, lane);
+    store_block<D>(rq, Qs, lane);
+    store_block<D>(ro, Os, lane);
     if (lane < AB) {
       const int64_t qp = qb * AB + lane;
       const int64_t qc = qp < S ? qp : S - 1;
@@ -765,10 +766,10 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restr
           a[r] = adv[j][r];
           bq[r] = adk[j][r];
         }
-        const bf16x8_t oa = frag_tr(Ot, 32 * j + c, hf, kk);
+        const bf16x8_t oa = frag_trr<D + 8>(Os, 32 * j, lane, kk);
         a = mfma32(oa, ph, a);
         a = mfma32(oa, pl, a);
-        const bf16x8_t qa = frag_tr(Qt, 32 * j + c, hf, kk);
+        const bf16x8_t qa = frag_trr<D + 8>(Qs, 32 * j, lane, kk);
         bq = mfma32(qa, sh, bq);
         bq = mfma32(qa, sl, bq);
 #pragma unroll

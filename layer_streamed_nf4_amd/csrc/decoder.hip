@@ -327,24 +327,63 @@ struct BlockRegs {
   u32x4_t v[PER_LANE][4];
 };
 
+// The rows of one sequence of a [rows, ld] bf16 matrix, columns c0 .. c0 + D,
+// read through a buffer resource with 32-bit byte offsets (a sequence of the
+// attention calls holds fewer than 2^30 bytes); rows past the sequence are
+// clamped to its last one. `lrow`, `lcol`: the lane's offsets inside a block
+// (row 4(it / (D/8)), column 8(it % (D/8))), the same for every block.
 template <int D>
-__device__ __forceinline__ void load_block(const uint16_t* __restrict__ src, int64_t ld, int64_t c0,
-                                           int64_t base_row, int64_t r0, int64_t S, int lane,
-                                           BlockRegs<D>& br) {
+struct SeqRows {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t ld2;   // bytes per row
+  uint32_t last;  // byte offset of the sequence's last row
+  uint32_t lrow[BlockRegs<D>::PER_LANE], lcol[BlockRegs<D>::PER_LANE];
+};
+
+template <int D>
+__device__ __forceinline__ SeqRows<D> seq_rows(const uint16_t* __restrict__ src, int64_t ld, int64_t c0,
+                                               int64_t base_row, int64_t S, int lane) {
   constexpr int CH = D / 8;
+  SeqRows<D> sr;
+  sr.rs = __builtin_amdgcn_make_buffer_rsrc((void*)(src + base_row * ld + c0), (short)0, (int)0xFFFFFFFFu,
+                                            0x00020000);
+  sr.ld2 = (uint32_t)ld * 2u;
+  sr.last = (uint32_t)(S - 1) * sr.ld2;
 #pragma unroll
   for (int x = 0; x < BlockRegs<D>::PER_LANE; ++x) {
     const int it = lane + 64 * x;
-    if (it < BlockRegs<D>::ITEMS) {
-      const int rg = it / CH, ch = it % CH;
+    sr.lrow[x] = (uint32_t)(4 * (it / CH)) * sr.ld2;
+    sr.lcol[x] = (uint32_t)(16 * (it % CH));
+  }
+  return sr;
+}
+
+// Rows r0 .. r0 + 31 of the sequence into the registers of one wave.
+template <int D>
+__device__ __forceinline__ void load_block(const SeqRows<D>& sr, int r0, BlockRegs<D>& br, int lane) {
+  const uint32_t base = (uint32_t)r0 * sr.ld2;
+#pragma unroll
+  for (int x = 0; x < BlockRegs<D>::PER_LANE; ++x) {
+    if (lane + 64 * x < BlockRegs<D>::ITEMS) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t rr = r0 + 4 * rg + i;
-        const int64_t row = base_row + (rr < S ? rr : S - 1);
-        br.v[x][i] = *reinterpret_cast<const u32x4_t*>(src + row * ld + c0 + 8 * ch);
+        const uint32_t ro = base + sr.lrow[x] + (uint32_t)i * sr.ld2;
+        const uint32_t off = (ro < sr.last ? ro : sr.last) + sr.lcol[x];
+        br.v[x][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sr.rs, off, 0, 0));
       }
     }
   }
+}
+
+// Row `row` (clamped to the sequence) as the lane's operand fragments, the
+// 16-wide steps of the head dimension (half hf of each).
+template <int D>
+__device__ __forceinline__ void row_frags(const SeqRows<D>& sr, int row, int hf, bf16x8_t* f) {
+  const uint32_t ro = (uint32_t)row * sr.ld2;
+  const uint32_t off = (ro < sr.last ? ro : sr.last) + 16u * (uint32_t)hf;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    f[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(sr.rs, off + 32u * kk, 0, 0));
 }
 
 // The block into LDS, row-major with row stride RS: 16-byte stores.
@@ -447,7 +486,7 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_fwd(const uint16_t* __restr
   const int64_t qrow = b * S + (qpos < S ? qpos : S - 1);
   const float scale = 1.0f / sqrtf((float)D);
   bf16x8_t qf[KS];
-  row_frags<D>(q + qrow * ldq + (int64_t)h * D, hf, qf);
+  row_frags<D>(seq_rows<D>(q, ldq, (int64_t)h * D, b * S, S, lane), (int)qpos, hf, qf);
   float acc[DT][16];
 #pragma unroll
   for (int j = 0; j < DT; ++j)
@@ -455,26 +494,37 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_fwd(const uint16_t* __restr
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
   float m = -INFINITY, lsum = 0.0f;
   BlockRegs<D> rk, rv;
+  const SeqRows<D> sk = seq_rows<D>(k, ldk, (int64_t)g * D, b * S, S, lane);
+  const SeqRows<D> sv = seq_rows<D>(v, ldk, (int64_t)g * D, b * S, S, lane);
+  const int qp = (int)qpos, S32 = (int)S;
   if (wave <= qb) {
-    load_block<D>(k, ldk, (int64_t)g * D, b * S, wave * AB, S, lane, rk);
-    load_block<D>(v, ldk, (int64_t)g * D, b * S, wave * AB, S, lane, rv);
+    load_block<D>(sk, wave * AB, rk, lane);
+    load_block<D>(sv, wave * AB, rv, lane);
   }
-  for (int64_t kb = wave; kb <= qb; kb += AW) {
+  for (int kb = wave; kb <= (int)qb; kb += AW) {
     store_block<D>(rk, Ks, lane);
     store_block<D, D + 16>(rv, Vs, lane);
     if (kb + AW <= qb) {
-      load_block<D>(k, ldk, (int64_t)g * D, b * S, (kb + AW) * AB, S, lane, rk);
-      load_block<D>(v, ldk, (int64_t)g * D, b * S, (kb + AW) * AB, S, lane, rv);
+      load_block<D>(sk, (kb + AW) * AB, rk, lane);
+      load_block<D>(sv, (kb + AW) * AB, rv, lane);
     }
     f32x16_t st = zero16();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) st = mfma32(frag_rm<D>(Ks, c, hf, kk), qf[kk], st);
     float mt = -INFINITY;
+    if (kb < qb && (kb + 1) * AB <= S32) {  // every key of the block precedes every query
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t key = kb * AB + crow(r, hf);
-      st[r] = (key <= qpos && key < S) ? st[r] * scale : -INFINITY;
-      mt = fmaxf(mt, st[r]);
+      for (int r = 0; r < 16; ++r) {
+        st[r] *= scale;
+        mt = fmaxf(mt, st[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * AB + crow(r, hf);
+        st[r] = (key <= qp && key < S32) ? st[r] * scale : -INFINITY;
+        mt = fmaxf(mt, st[r]);
+      }
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float mn = fmaxf(m, mt);  // finite: key kb*32 <= qpos and < S
@@ -586,8 +636,8 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_dq(const uint16_t* __restri
   const int64_t qrow = b * S + (qpos < S ? qpos : S - 1);
   const float scale = 1.0f / sqrtf((float)D);
   bf16x8_t qf[KS], df[KS];
-  row_frags<D>(q + qrow * ldq + (int64_t)h * D, hf, qf);
-  row_frags<D>(dout + qrow * ldq + (int64_t)h * D, hf, df);
+  row_frags<D>(seq_rows<D>(q, ldq, (int64_t)h * D, b * S, S, lane), (int)qpos, hf, qf);
+  row_frags<D>(seq_rows<D>(dout, ldq, (int64_t)h * D, b * S, S, lane), (int)qpos, hf, df);
   // Dsum over the lane's half of the head dimension, then both halves
   float di = 0.0f;
   {
@@ -614,15 +664,17 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_dq(const uint16_t* __restri
   // dQ product reads it transposed) without a register prefetch, and the
   // value rows, which only ever serve as A operands of their own lane, come
   // straight from memory.
-  for (int64_t kb = wave; kb <= qb; kb += AW) {
+  const SeqRows<D> sk = seq_rows<D>(k, ldk, (int64_t)g * D, b * S, S, lane);
+  const SeqRows<D> sv = seq_rows<D>(v, ldk, (int64_t)g * D, b * S, S, lane);
+  const int qp = (int)qpos, S32 = (int)S;
+  for (int kb = wave; kb <= (int)qb; kb += AW) {
     {
       BlockRegs<D> rk;
-      load_block<D>(k, ldk, (int64_t)g * D, b * S, kb * AB, S, lane, rk);
+      load_block<D>(sk, kb * AB, rk, lane);
       store_block<D>(rk, Ks, lane);
     }
-    const int64_t key = kb * AB + c;
     bf16x8_t vf[KS];
-    row_frags<D>(v + (b * S + (key < S ? key : S - 1)) * ldk + (int64_t)g * D, hf, vf);
+    row_frags<D>(sv, kb * AB + c, hf, vf);
     f32x16_t st = zero16(), dp = zero16();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -630,11 +682,16 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_dq(const uint16_t* __restri
       dp = mfma32(vf[kk], df[kk], dp);
     }
     float ds[16];
+    if (kb < qb && (kb + 1) * AB <= S32) {  // every key of the block precedes every query
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t key = kb * AB + crow(r, hf);
-      const float pr = (key <= qpos && key < S) ? __expf(st[r] * scale - L) : 0.0f;
-      ds[r] = pr * (dp[r] - di) * scale;
+      for (int r = 0; r < 16; ++r) ds[r] = __expf(st[r] * scale - L) * (dp[r] - di) * scale;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * AB + crow(r, hf);
+        const float pr = (key <= qp && key < S32) ? __expf(st[r] * scale - L) : 0.0f;
+        ds[r] = pr * (dp[r] - di) * scale;
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -709,8 +766,8 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restr
   const int64_t krow = b * S + (kpos < S ? kpos : S - 1);
   const float scale = 1.0f / sqrtf((float)D);
   bf16x8_t kf[KS], vf[KS];
-  row_frags<D>(k + krow * ldk + (int64_t)g * D, hf, kf);
-  row_frags<D>(v + krow * ldk + (int64_t)g * D, hf, vf);
+  row_frags<D>(seq_rows<D>(k, ldk, (int64_t)g * D, b * S, S, lane), (int)kpos, hf, kf);
+  row_frags<D>(seq_rows<D>(v, ldk, (int64_t)g * D, b * S, S, lane), (int)kpos, hf, vf);
   float adk[DT][16], adv[DT][16];
 #pragma unroll
   for (int j = 0; j < DT; ++j)
@@ -720,23 +777,25 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restr
       adv[j][r] = 0.0f;
     }
   BlockRegs<D> rq, ro;
-  const int64_t q0 = kb + wave;
+  const SeqRows<D> sq = seq_rows<D>(q, ldq, (int64_t)h * D, b * S, S, lane);
+  const SeqRows<D> so = seq_rows<D>(dout, ldq, (int64_t)h * D, b * S, S, lane);
+  const int kp = (int)kpos, S32 = (int)S;
+  const int q0 = (int)kb + wave;
   if (q0 < nkb) {
-    load_block<D>(q, ldq, (int64_t)h * D, b * S, q0 * AB, S, lane, rq);
-    load_block<D>(dout, ldq, (int64_t)h * D, b * S, q0 * AB, S, lane, ro);
+    load_block<D>(sq, q0 * AB, rq, lane);
+    load_block<D>(so, q0 * AB, ro, lane);
   }
-  for (int64_t qb = q0; qb < nkb; qb += AW) {
+  for (int qb = q0; qb < (int)nkb; qb += AW) {
     store_block<D>(rq, Qs, lane);
     store_block<D>(ro, Os, lane);
     if (lane < AB) {
-      const int64_t qp = qb * AB + lane;
-      const int64_t qc = qp < S ? qp : S - 1;
+      const int qc = qb * AB + lane < S32 ? qb * AB + lane : S32 - 1;
       Ls[lane] = lse[(b * H + h) * S + qc];
       Dl[lane] = dsum[(b * S + qc) * H + h];
     }
     if (qb + AW < nkb) {
-      load_block<D>(q, ldq, (int64_t)h * D, b * S, (qb + AW) * AB, S, lane, rq);
-      load_block<D>(dout, ldq, (int64_t)h * D, b * S, (qb + AW) * AB, S, lane, ro);
+      load_block<D>(sq, (qb + AW) * AB, rq, lane);
+      load_block<D>(so, (qb + AW) * AB, ro, lane);
     }
     f32x16_t st = zero16(), dp = zero16();
 #pragma unroll
@@ -745,13 +804,21 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restr
       dp = mfma32(frag_rm<D>(Os, c, hf, kk), vf[kk], dp);
     }
     float p[16], ds[16];
+    if (qb > (int)kb && (qb + 1) * AB <= S32) {  // every query of the block follows every key
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qr = crow(r, hf);
-      const int64_t qp = qb * AB + qr;
-      const bool ok = kpos <= qp && qp < S;
-      p[r] = ok ? __expf(st[r] * scale - Ls[qr]) : 0.0f;
-      ds[r] = p[r] * (dp[r] - Dl[qr]) * scale;
+      for (int r = 0; r < 16; ++r) {
+        const int qr = crow(r, hf);
+        p[r] = __expf(st[r] * scale - Ls[qr]);
+        ds[r] = p[r] * (dp[r] - Dl[qr]) * scale;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = crow(r, hf);
+        const int qp = qb * AB + qr;
+        p[r] = (kp <= qp && qp < S32) ? __expf(st[r] * scale - Ls[qr]) : 0.0f;
+        ds[r] = p[r] * (dp[r] - Dl[qr]) * scale;
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {

@@ -330,46 +330,68 @@ struct BlockRegs {
 // The rows of one sequence of a [rows, ld] bf16 matrix, columns c0 .. c0 + D,
 // read through a buffer resource with 32-bit byte offsets (a sequence of the
 // attention calls holds fewer than 2^30 bytes); rows past the sequence are
-// clamped to its last one. `lrow`, `lcol`: the lane's offsets inside a block
-// (row 4(it / (D/8)), column 8(it % (D/8))), the same for every block.
+// clamped to its last one.
 template <int D>
 struct SeqRows {
   __amdgpu_buffer_rsrc_t rs;
   uint32_t ld2;   // bytes per row
   uint32_t last;  // byte offset of the sequence's last row
-  uint32_t lrow[BlockRegs<D>::PER_LANE], lcol[BlockRegs<D>::PER_LANE];
 };
 
 template <int D>
 __device__ __forceinline__ SeqRows<D> seq_rows(const uint16_t* __restrict__ src, int64_t ld, int64_t c0,
-                                               int64_t base_row, int64_t S, int lane) {
-  constexpr int CH = D / 8;
+                                               int64_t base_row, int64_t S) {
   SeqRows<D> sr;
   sr.rs = __builtin_amdgcn_make_buffer_rsrc((void*)(src + base_row * ld + c0), (short)0, (int)0xFFFFFFFFu,
                                             0x00020000);
   sr.ld2 = (uint32_t)ld * 2u;
   sr.last = (uint32_t)(S - 1) * sr.ld2;
-#pragma unroll
-  for (int x = 0; x < BlockRegs<D>::PER_LANE; ++x) {
-    const int it = lane + 64 * x;
-    sr.lrow[x] = (uint32_t)(4 * (it / CH)) * sr.ld2;
-    sr.lcol[x] = (uint32_t)(16 * (it % CH));
-  }
   return sr;
 }
 
-// Rows r0 .. r0 + 31 of the sequence into the registers of one wave.
+// A lane's byte offsets inside a block of rows of ld2 bytes: load (x, i) is
+// row 4(it / (D/8)) + i, column 8(it % (D/8)) of item it = lane + 64 x; the
+// same for every block and for every matrix of that row length.
 template <int D>
-__device__ __forceinline__ void load_block(const SeqRows<D>& sr, int r0, BlockRegs<D>& br, int lane) {
+struct BlockLanes {
+  uint32_t off[BlockRegs<D>::PER_LANE][4];
+  uint32_t col[BlockRegs<D>::PER_LANE];
+};
+
+template <int D>
+__device__ __forceinline__ BlockLanes<D> block_lanes(uint32_t ld2, int lane) {
+  constexpr int CH = D / 8;
+  BlockLanes<D> bl;
+#pragma unroll
+  for (int x = 0; x < BlockRegs<D>::PER_LANE; ++x) {
+    const int it = lane + 64 * x;
+    bl.col[x] = (uint32_t)(16 * (it % CH));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bl.off[x][i] = (uint32_t)(4 * (it / CH) + i) * ld2 + bl.col[x];
+  }
+  return bl;
+}
+
+// Rows r0 .. r0 + 31 of the sequence into the registers of one wave: the
+// block's byte offset as the scalar offset of every load, except for a block
+// that runs past the sequence, whose rows are clamped one by one.
+template <int D>
+__device__ __forceinline__ void load_block(const SeqRows<D>& sr, const BlockLanes<D>& bl, int r0, int S,
+                                           BlockRegs<D>& br, int lane) {
   const uint32_t base = (uint32_t)r0 * sr.ld2;
+  const bool whole = r0 + AB <= S;
 #pragma unroll
   for (int x = 0; x < BlockRegs<D>::PER_LANE; ++x) {
     if (lane + 64 * x < BlockRegs<D>::ITEMS) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t ro = base + sr.lrow[x] + (uint32_t)i * sr.ld2;
-        const uint32_t off = (ro < sr.last ? ro : sr.last) + sr.lcol[x];
-        br.v[x][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sr.rs, off, 0, 0));
+        if (whole) {
+          br.v[x][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sr.rs, bl.off[x][i], (int)base, 0));
+        } else {
+          const uint32_t ro = base + bl.off[x][i] - bl.col[x];
+          const uint32_t off = (ro < sr.last ? ro : sr.last) + bl.col[x];
+          br.v[x][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sr.rs, off, 0, 0));
+        }
       }
     }
   }
@@ -477,16 +499,18 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_fwd(const uint16_t* __restr
   uint16_t* const Ks = smem + wave * WS;
   uint16_t* const Vs = Ks + RM_ELEMS(D);
   const int64_t nqb = (S + AB - 1) / AB;
-  const int64_t b = blockIdx.x / (H * nqb);
-  const int h = (int)((blockIdx.x / nqb) % H);
-  const int64_t qb = blockIdx.x % nqb;
+  // the longest causal ranges (the last query blocks) are dispatched first
+  const int64_t nbh = gridDim.x / nqb;  // sequences x heads
+  const int64_t qb = nqb - 1 - blockIdx.x / nbh;
+  const int64_t b = (blockIdx.x % nbh) / H;
+  const int h = (int)(blockIdx.x % nbh % H);
   const int g = h / (H / Hkv);
   const int64_t ldq = (int64_t)H * D, ldk = (int64_t)Hkv * D;
   const int64_t qpos = qb * AB + c;
   const int64_t qrow = b * S + (qpos < S ? qpos : S - 1);
   const float scale = 1.0f / sqrtf((float)D);
   bf16x8_t qf[KS];
-  row_frags<D>(seq_rows<D>(q, ldq, (int64_t)h * D, b * S, S, lane), (int)qpos, hf, qf);
+  row_frags<D>(seq_rows<D>(q, ldq, (int64_t)h * D, b * S, S), (int)qpos, hf, qf);
   float acc[DT][16];
 #pragma unroll
   for (int j = 0; j < DT; ++j)
@@ -494,19 +518,20 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_fwd(const uint16_t* __restr
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
   float m = -INFINITY, lsum = 0.0f;
   BlockRegs<D> rk, rv;
-  const SeqRows<D> sk = seq_rows<D>(k, ldk, (int64_t)g * D, b * S, S, lane);
-  const SeqRows<D> sv = seq_rows<D>(v, ldk, (int64_t)g * D, b * S, S, lane);
+  const SeqRows<D> sk = seq_rows<D>(k, ldk, (int64_t)g * D, b * S, S);
+  const SeqRows<D> sv = seq_rows<D>(v, ldk, (int64_t)g * D, b * S, S);
+  const BlockLanes<D> bl = block_lanes<D>(sk.ld2, lane);
   const int qp = (int)qpos, S32 = (int)S;
   if (wave <= qb) {
-    load_block<D>(sk, wave * AB, rk, lane);
-    load_block<D>(sv, wave * AB, rv, lane);
+    load_block<D>(sk, bl, wave * AB, S32, rk, lane);
+    load_block<D>(sv, bl, wave * AB, S32, rv, lane);
   }
   for (int kb = wave; kb <= (int)qb; kb += AW) {
     store_block<D>(rk, Ks, lane);
     store_block<D, D + 16>(rv, Vs, lane);
     if (kb + AW <= qb) {
-      load_block<D>(sk, (kb + AW) * AB, rk, lane);
-      load_block<D>(sv, (kb + AW) * AB, rv, lane);
+      load_block<D>(sk, bl, (kb + AW) * AB, S32, rk, lane);
+      load_block<D>(sv, bl, (kb + AW) * AB, S32, rv, lane);
     }
     f32x16_t st = zero16();
 #pragma unroll
@@ -627,17 +652,19 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_dq(const uint16_t* __restri
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, hf = lane >> 5, c = lane & 31;
   uint16_t* const Ks = smem + wave * WS;
   const int64_t nqb = (S + AB - 1) / AB;
-  const int64_t b = blockIdx.x / (H * nqb);
-  const int h = (int)((blockIdx.x / nqb) % H);
-  const int64_t qb = blockIdx.x % nqb;
+  // the longest causal ranges (the last query blocks) are dispatched first
+  const int64_t nbh = gridDim.x / nqb;  // sequences x heads
+  const int64_t qb = nqb - 1 - blockIdx.x / nbh;
+  const int64_t b = (blockIdx.x % nbh) / H;
+  const int h = (int)(blockIdx.x % nbh % H);
   const int g = h / (H / Hkv);
   const int64_t ldq = (int64_t)H * D, ldk = (int64_t)Hkv * D;
   const int64_t qpos = qb * AB + c;
   const int64_t qrow = b * S + (qpos < S ? qpos : S - 1);
   const float scale = 1.0f / sqrtf((float)D);
   bf16x8_t qf[KS], df[KS];
-  row_frags<D>(seq_rows<D>(q, ldq, (int64_t)h * D, b * S, S, lane), (int)qpos, hf, qf);
-  row_frags<D>(seq_rows<D>(dout, ldq, (int64_t)h * D, b * S, S, lane), (int)qpos, hf, df);
+  row_frags<D>(seq_rows<D>(q, ldq, (int64_t)h * D, b * S, S), (int)qpos, hf, qf);
+  row_frags<D>(seq_rows<D>(dout, ldq, (int64_t)h * D, b * S, S), (int)qpos, hf, df);
   // Dsum over the lane's half of the head dimension, then both halves
   float di = 0.0f;
   {
@@ -664,13 +691,14 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_dq(const uint16_t* __restri
   // dQ product reads it transposed) without a register prefetch, and the
   // value rows, which only ever serve as A operands of their own lane, come
   // straight from memory.
-  const SeqRows<D> sk = seq_rows<D>(k, ldk, (int64_t)g * D, b * S, S, lane);
-  const SeqRows<D> sv = seq_rows<D>(v, ldk, (int64_t)g * D, b * S, S, lane);
+  const SeqRows<D> sk = seq_rows<D>(k, ldk, (int64_t)g * D, b * S, S);
+  const SeqRows<D> sv = seq_rows<D>(v, ldk, (int64_t)g * D, b * S, S);
+  const BlockLanes<D> bl = block_lanes<D>(sk.ld2, lane);
   const int qp = (int)qpos, S32 = (int)S;
   for (int kb = wave; kb <= (int)qb; kb += AW) {
     {
       BlockRegs<D> rk;
-      load_block<D>(sk, kb * AB, rk, lane);
+      load_block<D>(sk, bl, kb * AB, S32, rk, lane);
       store_block<D>(rk, Ks, lane);
     }
     bf16x8_t vf[KS];
@@ -757,17 +785,19 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restr
   float* const Ls = reinterpret_cast<float*>(Os + RM_ELEMS(D));
   float* const Dl = Ls + AB;
   const int64_t nkb = (S + AB - 1) / AB;
-  const int64_t b = blockIdx.x / (H * nkb);
-  const int h = (int)((blockIdx.x / nkb) % H);
-  const int64_t kb = blockIdx.x % nkb;
+  // the longest causal ranges (the first key blocks) are dispatched first
+  const int64_t nbh = gridDim.x / nkb;  // sequences x heads
+  const int64_t kb = blockIdx.x / nbh;
+  const int64_t b = (blockIdx.x % nbh) / H;
+  const int h = (int)(blockIdx.x % nbh % H);
   const int g = h / (H / Hkv);
   const int64_t ldq = (int64_t)H * D, ldk = (int64_t)Hkv * D;
   const int64_t kpos = kb * AB + c;
   const int64_t krow = b * S + (kpos < S ? kpos : S - 1);
   const float scale = 1.0f / sqrtf((float)D);
   bf16x8_t kf[KS], vf[KS];
-  row_frags<D>(seq_rows<D>(k, ldk, (int64_t)g * D, b * S, S, lane), (int)kpos, hf, kf);
-  row_frags<D>(seq_rows<D>(v, ldk, (int64_t)g * D, b * S, S, lane), (int)kpos, hf, vf);
+  row_frags<D>(seq_rows<D>(k, ldk, (int64_t)g * D, b * S, S), (int)kpos, hf, kf);
+  row_frags<D>(seq_rows<D>(v, ldk, (int64_t)g * D, b * S, S), (int)kpos, hf, vf);
   float adk[DT][16], adv[DT][16];
 #pragma unroll
   for (int j = 0; j < DT; ++j)
@@ -777,13 +807,14 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restr
       adv[j][r] = 0.0f;
     }
   BlockRegs<D> rq, ro;
-  const SeqRows<D> sq = seq_rows<D>(q, ldq, (int64_t)h * D, b * S, S, lane);
-  const SeqRows<D> so = seq_rows<D>(dout, ldq, (int64_t)h * D, b * S, S, lane);
+  const SeqRows<D> sq = seq_rows<D>(q, ldq, (int64_t)h * D, b * S, S);
+  const SeqRows<D> so = seq_rows<D>(dout, ldq, (int64_t)h * D, b * S, S);
+  const BlockLanes<D> bl = block_lanes<D>(sq.ld2, lane);
   const int kp = (int)kpos, S32 = (int)S;
   const int q0 = (int)kb + wave;
   if (q0 < nkb) {
-    load_block<D>(sq, q0 * AB, rq, lane);
-    load_block<D>(so, q0 * AB, ro, lane);
+    load_block<D>(sq, bl, q0 * AB, S32, rq, lane);
+    load_block<D>(so, bl, q0 * AB, S32, ro, lane);
   }
   for (int qb = q0; qb < (int)nkb; qb += AW) {
     store_block<D>(rq, Qs, lane);
@@ -794,8 +825,8 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restr
       Dl[lane] = dsum[(b * S + qc) * H + h];
     }
     if (qb + AW < nkb) {
-      load_block<D>(sq, (qb + AW) * AB, rq, lane);
-      load_block<D>(so, (qb + AW) * AB, ro, lane);
+      load_block<D>(sq, bl, (qb + AW) * AB, S32, rq, lane);
+      load_block<D>(so, bl, (qb + AW) * AB, S32, ro, lane);
     }
     f32x16_t st = zero16(), dp = zero16();
 #pragma unroll

@@ -495,7 +495,8 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_fwd(const uint16_t* __restr
   constexpr int KS = D / 16, DT = D / 32, WS = RM_ELEMS(D) + RV_ELEMS(D);
   constexpr int STAGE = AW * 64 * (DT * 16 + 2) * 2;  // the waves' partial results (bf16 units)
   __shared__ __attribute__((aligned(16))) uint16_t smem[AW * WS > STAGE ? AW * WS : STAGE];
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, hf = lane >> 5, c = lane & 31;
+  const int t = threadIdx.x, lane = t & 63, hf = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: the walk over blocks is scalar
   uint16_t* const Ks = smem + wave * WS;
   uint16_t* const Vs = Ks + RM_ELEMS(D);
   const int64_t nqb = (S + AB - 1) / AB;
@@ -649,7 +650,8 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_dq(const uint16_t* __restri
   constexpr int KS = D / 16, DT = D / 32, WS = RM_ELEMS(D);
   constexpr int STAGE = AW * 64 * DT * 16 * 2;  // the waves' partial dQ (bf16 units)
   __shared__ __attribute__((aligned(16))) uint16_t smem[AW * WS > STAGE ? AW * WS : STAGE];
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, hf = lane >> 5, c = lane & 31;
+  const int t = threadIdx.x, lane = t & 63, hf = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: the walk over blocks is scalar
   uint16_t* const Ks = smem + wave * WS;
   const int64_t nqb = (S + AB - 1) / AB;
   // the longest causal ranges (the last query blocks) are dispatched first
@@ -779,7 +781,8 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restr
   constexpr int WS = 2 * RM_ELEMS(D) + 4 * AB;  // + lse and Dsum (fp32) of the block
   constexpr int STAGE = AW * 64 * 2 * DT * 16 * 2;  // the waves' partial dK, dV (bf16 units)
   __shared__ __attribute__((aligned(16))) uint16_t smem[AW * WS > STAGE ? AW * WS : STAGE];
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, hf = lane >> 5, c = lane & 31;
+  const int t = threadIdx.x, lane = t & 63, hf = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: the walk over blocks is scalar
   uint16_t* const Qs = smem + wave * WS;
   uint16_t* const Os = Qs + RM_ELEMS(D);
   float* const Ls = reinterpret_cast<float*>(Os + RM_ELEMS(D));

@@ -397,12 +397,22 @@ __device__ __forceinline__ void load_block(const SeqRows<D>& sr, const BlockLane
   }
 }
 
+// Zero that the compiler cannot see through: added to the offset of a load
+// inside a loop, it keeps the compiler from hoisting a loop-invariant load
+// (and then spilling its registers) where the loop re-reads on purpose.
+__device__ __forceinline__ uint32_t opaque_zero() {
+  uint32_t z;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+  return z;
+}
+
 // Row `row` (clamped to the sequence) as the lane's operand fragments, the
 // 16-wide steps of the head dimension (half hf of each).
 template <int D>
-__device__ __forceinline__ void row_frags(const SeqRows<D>& sr, int row, int hf, bf16x8_t* f) {
+__device__ __forceinline__ void row_frags(const SeqRows<D>& sr, int row, int hf, bf16x8_t* f,
+                                          uint32_t extra = 0) {
   const uint32_t ro = (uint32_t)row * sr.ld2;
-  const uint32_t off = (ro < sr.last ? ro : sr.last) + 16u * (uint32_t)hf;
+  const uint32_t off = (ro < sr.last ? ro : sr.last) + 16u * (uint32_t)hf + extra;
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
     f[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(sr.rs, off + 32u * kk, 0, 0));
@@ -767,9 +777,14 @@ __global__ __launch_bounds__(64 * AW, 2) void k_attn_dq(const uint16_t* __restri
 
 // dK, dV of a 32-key block for one query head (the query blocks split over AW
 // waves and summed in wave order; fp32 partials per head, the heads of a KV
-// group summed afterwards in head order).
+// group summed afterwards in head order). Two workgroups share a CU (at most
+// 256 registers and 80 KB of LDS each): each query and dO block goes through
+// LDS without a register prefetch, and the key and value rows, operands of
+// their own lane only, are read from memory for every block (they stay in
+// L2); the waves' dK partials and then their dV partials are
+// combined through the same 64 KB of LDS.
 template <int D>
-__global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * AW, 2) void k_attn_dkv(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
                                                          const uint16_t* __restrict__ dout,
@@ -779,7 +794,7 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restr
                                                          float* __restrict__ pv) {
   constexpr int KS = D / 16, DT = D / 32;
   constexpr int WS = 2 * RM_ELEMS(D) + 4 * AB;  // + lse and Dsum (fp32) of the block
-  constexpr int STAGE = AW * 64 * 2 * DT * 16 * 2;  // the waves' partial dK, dV (bf16 units)
+  constexpr int STAGE = AW * 64 * DT * 16 * 2;  // the waves' partial dK or dV (bf16 units)
   __shared__ __attribute__((aligned(16))) uint16_t smem[AW * WS > STAGE ? AW * WS : STAGE];
   const int t = threadIdx.x, lane = t & 63, hf = lane >> 5, c = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: the walk over blocks is scalar
@@ -798,9 +813,8 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restr
   const int64_t kpos = kb * AB + c;
   const int64_t krow = b * S + (kpos < S ? kpos : S - 1);
   const float scale = 1.0f / sqrtf((float)D);
-  bf16x8_t kf[KS], vf[KS];
-  row_frags<D>(seq_rows<D>(k, ldk, (int64_t)g * D, b * S, S), (int)kpos, hf, kf);
-  row_frags<D>(seq_rows<D>(v, ldk, (int64_t)g * D, b * S, S), (int)kpos, hf, vf);
+  const SeqRows<D> sk = seq_rows<D>(k, ldk, (int64_t)g * D, b * S, S);
+  const SeqRows<D> sv = seq_rows<D>(v, ldk, (int64_t)g * D, b * S, S);
   float adk[DT][16], adv[DT][16];
 #pragma unroll
   for (int j = 0; j < DT; ++j)
@@ -809,33 +823,35 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restr
       adk[j][r] = 0.0f;
       adv[j][r] = 0.0f;
     }
-  BlockRegs<D> rq, ro;
   const SeqRows<D> sq = seq_rows<D>(q, ldq, (int64_t)h * D, b * S, S);
   const SeqRows<D> so = seq_rows<D>(dout, ldq, (int64_t)h * D, b * S, S);
   const BlockLanes<D> bl = block_lanes<D>(sq.ld2, lane);
   const int kp = (int)kpos, S32 = (int)S;
-  const int q0 = (int)kb + wave;
-  if (q0 < nkb) {
-    load_block<D>(sq, bl, q0 * AB, S32, rq, lane);
-    load_block<D>(so, bl, q0 * AB, S32, ro, lane);
-  }
-  for (int qb = q0; qb < (int)nkb; qb += AW) {
-    store_block<D>(rq, Qs, lane);
-    store_block<D>(ro, Os, lane);
+  for (int qb = (int)kb + wave; qb < (int)nkb; qb += AW) {
+    {
+      BlockRegs<D> rb;
+      load_block<D>(sq, bl, qb * AB, S32, rb, lane);
+      store_block<D>(rb, Qs, lane);
+      load_block<D>(so, bl, qb * AB, S32, rb, lane);
+      store_block<D>(rb, Os, lane);
+    }
     if (lane < AB) {
       const int qc = qb * AB + lane < S32 ? qb * AB + lane : S32 - 1;
       Ls[lane] = lse[(b * H + h) * S + qc];
       Dl[lane] = dsum[(b * S + qc) * H + h];
     }
-    if (qb + AW < nkb) {
-      load_block<D>(sq, bl, (qb + AW) * AB, S32, rq, lane);
-      load_block<D>(so, bl, (qb + AW) * AB, S32, ro, lane);
-    }
     f32x16_t st = zero16(), dp = zero16();
+    {
+      bf16x8_t kf[KS];
+      row_frags<D>(sk, kp, hf, kf, opaque_zero());
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      st = mfma32(frag_rm<D>(Qs, c, hf, kk), kf[kk], st);
-      dp = mfma32(frag_rm<D>(Os, c, hf, kk), vf[kk], dp);
+      for (int kk = 0; kk < KS; ++kk) st = mfma32(frag_rm<D>(Qs, c, hf, kk), kf[kk], st);
+    }
+    {
+      bf16x8_t vf[KS];
+      row_frags<D>(sv, kp, hf, vf, opaque_zero());
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) dp = mfma32(frag_rm<D>(Os, c, hf, kk), vf[kk], dp);
     }
     float p[16], ds[16];
     if (qb > (int)kb && (qb + 1) * AB <= S32) {  // every query of the block follows every key
@@ -881,41 +897,32 @@ __global__ __launch_bounds__(64 * AW, 1) void k_attn_dkv(const uint16_t* __restr
       }
     }
   }
-  __syncthreads();
-  float* part = reinterpret_cast<float*>(smem);  // [AW][64][2 * DT * 16]
-  {
-    float both[2 * DT * 16];
-#pragma unroll
-    for (int j = 0; j < DT; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        both[j * 16 + r] = adk[j][r];
-        both[DT * 16 + j * 16 + r] = adv[j][r];
-      }
-    park<2 * DT * 16>(part, wave, lane, both);
-  }
-  __syncthreads();
-  if (wave >= DT || kpos >= S) return;
-  const int j = wave;
+  // combine the waves: dK first, then dV through the same LDS
+  float* part = reinterpret_cast<float*>(smem);  // [AW][64][DT * 16]
+  static_assert(AW * 64 * DT * 16 * 4 <= sizeof(smem), "partial staging fits the LDS");
   const int64_t prow = (krow * H + h) * D;
 #pragma unroll
-  for (int rq2 = 0; rq2 < 4; ++rq2) {
-    float sk[4], sv[4];
+  for (int pass = 0; pass < 2; ++pass) {
+    __syncthreads();
+    park<DT * 16>(part, wave, lane, pass == 0 ? &adk[0][0] : &adv[0][0]);
+    __syncthreads();
+    if (wave < DT && kpos < S) {
+      const int j = wave;
+      float* const dst = pass == 0 ? pk : pv;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float a = 0.0f, bsum = 0.0f;
+      for (int rq2 = 0; rq2 < 4; ++rq2) {
+        float sm[4];
 #pragma unroll
-      for (int w = 0; w < AW; ++w) {
-        const float* pw = part + (w * 64 + lane) * 2 * DT * 16;
-        a += pw[j * 16 + 4 * rq2 + e];
-        bsum += pw[DT * 16 + j * 16 + 4 * rq2 + e];
+        for (int e = 0; e < 4; ++e) {
+          float a = 0.0f;
+#pragma unroll
+          for (int w = 0; w < AW; ++w) a += part[(w * 64 + lane) * DT * 16 + j * 16 + 4 * rq2 + e];
+          sm[e] = a;
+        }
+        const int d0 = 32 * j + 8 * rq2 + 4 * hf;
+        *reinterpret_cast<float4*>(dst + prow + d0) = make_float4(sm[0], sm[1], sm[2], sm[3]);
       }
-      sk[e] = a;
-      sv[e] = bsum;
     }
-    const int d0 = 32 * j + 8 * rq2 + 4 * hf;
-    *reinterpret_cast<float4*>(pk + prow + d0) = make_float4(sk[0], sk[1], sk[2], sk[3]);
-    *reinterpret_cast<float4*>(pv + prow + d0) = make_float4(sv[0], sv[1], sv[2], sv[3]);
   }
 }
 

@@ -128,6 +128,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const float* __restrict__ x
   }
 }
 
+// chunks of 8 of the row a thread of the norm backward keeps in registers
+// between its two passes (rows up to 8192 wide are read once)
+constexpr int RC = 4;
+
 // dh (+)= rstd * g - x * rstd^3 * mean(g * x), g = w * (sum of the n bf16 inputs)
 struct DyPtrs {
   const uint16_t* p[3];
@@ -144,7 +148,9 @@ __device__ __forceinline__ void dy_sum8(const DyPtrs& dys, int n_dy, int64_t off
 }
 
 // y, packed (nullable): the resulting dh row also as bf16, row-major and in
-// MFMA fragment order (the next GEMM's input), as k_f32_to_bf16 writes them
+// MFMA fragment order (the next GEMM's input), as k_f32_to_bf16 writes them.
+// The first RC chunks of the summed dy and of x stay in registers for the
+// second pass.
 __global__ __launch_bounds__(256) void k_rmsnorm_bwd(DyPtrs dys, int n_dy, const float* __restrict__ x,
                                                      const float* __restrict__ w,
                                                      const float* __restrict__ rstd, int64_t H,
@@ -156,8 +162,20 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(DyPtrs dys, int n_dy, const
   const float* xr = x + t * H;
   const float r = rstd[t];
   const int nc = (int)(H / 8);
-  float acc = 0.0f;
-  for (int c = threadIdx.x; c < nc; c += 256) {
+  float acc = 0.0f, dyc[RC][8], xc[RC][8];
+#pragma unroll
+  for (int i = 0; i < RC; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nc) {
+      float g[8];
+      dy_sum8(dys, n_dy, t * H + 8 * c, dyc[i]);
+      load8_f32(xr + 8 * c, xc[i]);
+      load8_f32(w + 8 * c, g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += dyc[i][e] * g[e] * xc[i][e];
+    }
+  }
+  for (int c = threadIdx.x + 256 * RC; c < nc; c += 256) {
     float dy[8], f[8], g[8];
     dy_sum8(dys, n_dy, t * H + 8 * c, dy);
     load8_f32(xr + 8 * c, f);
@@ -167,10 +185,8 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(DyPtrs dys, int n_dy, const
   }
   acc = block_sum(acc, red);
   const float cc = r * r * r * acc / (float)H;
-  for (int c = threadIdx.x; c < nc; c += 256) {
-    float dy[8], f[8], g[8], o[8];
-    dy_sum8(dys, n_dy, t * H + 8 * c, dy);
-    load8_f32(xr + 8 * c, f);
+  auto emit = [&](int c, const float* dy, const float* f) {
+    float g[8], o[8];
     load8_f32(w + 8 * c, g);
     if (accumulate) load8_f32(dh + t * H + 8 * c, o);
 #pragma unroll
@@ -190,6 +206,17 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(DyPtrs dys, int n_dy, const
         if (c == nc - 1) frag_zero_tail(packed, t, H, kb);
       }
     }
+  };
+#pragma unroll
+  for (int i = 0; i < RC; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nc) emit(c, dyc[i], xc[i]);
+  }
+  for (int c = threadIdx.x + 256 * RC; c < nc; c += 256) {
+    float dy[8], f[8];
+    dy_sum8(dys, n_dy, t * H + 8 * c, dy);
+    load8_f32(xr + 8 * c, f);
+    emit(c, dy, f);
   }
 }
 

@@ -147,6 +147,8 @@ ATTN_CASES = [
     (1, 512, 9, 3, 64),    # SmolLM2-135M attention at S512
     (1, 130, 8, 2, 128),   # Llama-8B head size, groups of 4, ragged
     (3, 1, 2, 1, 32),      # a single position
+    (2, 160, 8, 8, 128),   # no grouping, two sequences of whole 32-row blocks
+    (1, 1000, 4, 1, 64),   # one KV head for four query heads, 32 blocks (8 per wave), ragged
 ]
 
 

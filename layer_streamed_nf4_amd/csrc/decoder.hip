@@ -406,21 +406,23 @@ template <int D>
 __device__ __forceinline__ void load_block(const SeqRows<D>& sr, const BlockLanes<D>& bl, int r0, int S,
                                            BlockRegs<D>& br, int lane) {
   const uint32_t base = (uint32_t)r0 * sr.ld2;
-  const bool whole = r0 + AB <= S;
+  if (r0 + AB <= S) {  // uniform
 #pragma unroll
-  for (int x = 0; x < BlockRegs<D>::PER_LANE; ++x) {
-    if (lane + 64 * x < BlockRegs<D>::ITEMS) {
+    for (int x = 0; x < BlockRegs<D>::PER_LANE; ++x)
+      if (lane + 64 * x < BlockRegs<D>::ITEMS)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (whole) {
+        for (int i = 0; i < 4; ++i)
           br.v[x][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sr.rs, bl.off[x][i], (int)base, 0));
-        } else {
+  } else {
+#pragma unroll
+    for (int x = 0; x < BlockRegs<D>::PER_LANE; ++x)
+      if (lane + 64 * x < BlockRegs<D>::ITEMS)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
           const uint32_t ro = base + bl.off[x][i] - bl.col[x];
           const uint32_t off = (ro < sr.last ? ro : sr.last) + bl.col[x];
           br.v[x][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sr.rs, off, 0, 0));
         }
-      }
-    }
   }
 }
 

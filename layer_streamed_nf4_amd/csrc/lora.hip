@@ -81,7 +81,7 @@ struct RowsArgs {
 template <bool TRANS_F>
 __global__ __launch_bounds__(ROW_WAVES * 64) void k_lora_rows(RowsArgs ra, int64_t M, int r, int rch) {
   __shared__ float s_part[ROW_WAVES][64][8];
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   const int lane = threadIdx.x & 63;
   const int64_t m0 = (int64_t)blockIdx.x * 32;
   const int ks = blockIdx.y;
@@ -223,7 +223,7 @@ template <bool TRANS_OUT>
 __global__ __launch_bounds__(COL_WAVES * 64) void k_lora_cols(ColsArgs ca, int64_t M, int r,
                                                               float scale, int accumulate) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[COL_SMEM];
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   const int lane = threadIdx.x & 63;
   const int64_t c0 = (int64_t)blockIdx.x * 32;
   const int r0 = blockIdx.y * RCH;

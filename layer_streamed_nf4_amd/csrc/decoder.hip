@@ -345,8 +345,10 @@ __device__ __forceinline__ int crow(int r, int hf) { return 8 * (r >> 2) + 4 * h
 // A 32-row block of a [rows, ld] bf16 matrix (rows r0 .. r0 + 31 of one
 // sequence, clamped to it; columns c0 .. c0 + D) in the registers of one wave:
 // item it = lane + 64 x covers rows 4(it / (D/8)) .. +4 and columns 8(it % (D/8))
-// .. +8, as four 16-byte loads. Loading a block one step ahead of its use
-// hides the memory latency behind the current block's products.
+// .. +8, as four 16-byte loads. The forward loads each block one step ahead
+// of its use, hiding the memory latency behind the current block's products;
+// the backward kernels load just before use and leave the latency to the
+// second workgroup on their CU.
 template <int D>
 struct BlockRegs {
   static constexpr int ITEMS = 8 * (D / 8);           // 4-row x 8-column items per block

@@ -71,17 +71,18 @@ def flops_per_token(model: str, lm_head: bool, reference: bool = False) -> int:
 def executed_flops_per_token(model: str, decoder: bool, reference: bool = False) -> int:
     """The frozen-linear and lm_head FLOPs the step actually executes (same
     counting rules as flops_per_token). The decoder's recompute skips the down
-    product (its output h_{i+1} is stored and the backward reads nothing else
-    of it) and the whole last layer (its body is kept from the forward); the
-    linear stack recomputes every projection of every layer."""
+    and o products (their outputs h_{i+1} and the mid-layer residual are kept
+    from the forward and the backward reads nothing else of them) and the
+    whole last layer (its body is kept from the forward); the linear stack
+    recomputes every projection of every layer."""
     if not decoder:
         return flops_per_token(model, False, reference)
     sh = synth.SHAPES[model]
     n_layers = synth.N_LAYERS[model]
     p_lin = sum(a * b for a, b in sh.values())
-    p_down = sh["down"][0] * sh["down"][1]
+    p_skip = sh["down"][0] * sh["down"][1] + sh["o"][0] * sh["o"][1]
     v, h = LM_HEAD[model]
-    f = 2 * p_lin * n_layers + 2 * (p_lin - p_down) * (n_layers - 1) + 2 * p_lin * n_layers + 4 * v * h
+    f = 2 * p_lin * n_layers + 2 * (p_lin - p_skip) * (n_layers - 1) + 2 * p_lin * n_layers + 4 * v * h
     if reference:
         f += 2 * p_lin * n_layers + 2 * v * h
     return f

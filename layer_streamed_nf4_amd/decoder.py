@@ -135,13 +135,17 @@ class Decoder:
         def bf(*shape):
             return torch.empty(shape, dtype=BF16, device=dev)
 
-        # residual stream checkpoints h_0 .. h_L (the layer inputs)
+        # residual stream checkpoints h_0 .. h_L (the layer inputs), and each
+        # layer's mid-layer residual h + o(attention), the one output of the o
+        # projection the backward reads: kept from the forward, so that the
+        # recompute skips that product
         self.h = [f32(M, H) for _ in range(self.L + 1)]
+        self.h_mids = [f32(M, H) for _ in range(self.L)]
         # one layer's recomputable body
         self.n1, self.rstd1 = bf(M, H), f32(M)
         self.q, self.k, self.vv = bf(M, self.qd), bf(M, self.kvd), bf(M, self.kvd)
         self.o, self.o32, self.lse = bf(M, self.qd), f32(M, self.qd), f32(batch, nh, seq)
-        self.ao, self.h_mid = bf(M, H), f32(M, H)
+        self.ao, self.h_mid = bf(M, H), f32(M, H)  # h_mid: the reference model's (adapters off)
         self.n2, self.rstd2 = bf(M, H), f32(M)
         self.g, self.u_, self.sw, self.dn = bf(M, I), bf(M, I), bf(M, I), bf(M, H)
         # head
@@ -391,15 +395,21 @@ class Decoder:
     # -- one layer ---------------------------------------------------------------------
     def _layer_fwd(self, i, base, recompute, adapters=True, hin=None, hout=None, keep=False):
         """Layer i's body from h_i. The recompute keeps the fp32 attention
-        output for the backward and skips h_{i+1}, which is already stored
-        (and with it the down projection's product, which nothing else reads);
-        keep=True keeps it in a first forward too (the last layer, whose
-        backward follows the head with the body buffers intact).
-        adapters=False runs the frozen base alone (the reference model);
-        hin/hout default to the checkpoints h_i, h_{i+1}."""
+        output for the backward and skips h_{i+1} and the mid-layer residual
+        h_mid, which are already stored (and with them the down and o
+        projections' products, which nothing else reads; only their adapters'
+        u are recomputed); keep=True keeps the fp32 attention output in a
+        first forward too (the last layer, whose backward follows the head
+        with the body buffers intact).
+        adapters=False runs the frozen base alone (the reference model, whose
+        h_mid goes to a scratch buffer); hin/hout default to the checkpoints
+        h_i, h_{i+1}."""
         c, s, M = self.cfg, self._s, self.M
         H = self.H
         self._packed_key = self._packed_key_b = self._packed_key_c = None
+        own = adapters and hin is None  # the policy's own sweep: h_mid is a checkpoint
+        h_mid = self.h_mids[i] if own else self.h_mid
+        assert own or not recompute
         hin = self.h[i] if hin is None else hin
         hout = self.h[i + 1] if hout is None else hout
         a = adapters
@@ -412,8 +422,11 @@ class Decoder:
                            c["heads"], c["kv_heads"], c["head_dim"], self.o.data_ptr(),
                            self.o32.data_ptr() if recompute or keep else None, self.lse.data_ptr(), s,
                            packed=self._produced(self.o, c["heads"] * c["head_dim"]))
-        self._fwd(base, i, ("o",), self.o, (self.ao,), a, res=(hin, self.h_mid))
-        nf4s_rmsnorm_fwd(self.h_mid.data_ptr(), self.norms["mlp"][i].data_ptr(), M, H, c["eps"],
+        if recompute:
+            self._lora_u(i, ("o",), self.o, a)
+        else:
+            self._fwd(base, i, ("o",), self.o, (self.ao,), a, res=(hin, h_mid))
+        nf4s_rmsnorm_fwd(h_mid.data_ptr(), self.norms["mlp"][i].data_ptr(), M, H, c["eps"],
                          self.n2.data_ptr(), self.rstd2.data_ptr(), s, packed=self._produced(self.n2, H))
         fuse = self._fuse_swiglu and not recompute and not keep
         if fuse:
@@ -431,7 +444,7 @@ class Decoder:
             if not fuse:
                 nf4s_swiglu_fwd(self.g.data_ptr(), self.u_.data_ptr(), M, self.I, self.sw.data_ptr(), s,
                                 packed=self._produced(self.sw, self.I))
-            self._fwd(base, i, ("down",), self.sw, (self.dn,), a, res=(self.h_mid, hout))
+            self._fwd(base, i, ("down",), self.sw, (self.dn,), a, res=(h_mid, hout))
 
     def _layer_bwd(self, i, base):
         """dh holds dL/dh_{i+1} on entry (and dd its bf16 form, packed in
@@ -448,7 +461,7 @@ class Decoder:
         dn = self._bwd(base, i, ("gate", "up"), self.n2, (self.dg, self.du_), self.dnx[:2])
         self._packed_key_b = None
         # the norm's backward also leaves dh as the o projection's bf16 input
-        nf4s_rmsnorm_bwd([x.data_ptr() for x in dn], self.h_mid.data_ptr(),
+        nf4s_rmsnorm_bwd([x.data_ptr() for x in dn], self.h_mids[i].data_ptr(),
                          self.norms["mlp"][i].data_ptr(), self.rstd2.data_ptr(), M, H, 1,
                          self.dh.data_ptr(), s, y=self.dd.data_ptr(), packed=self._produced(self.dd, H))
         self._bwd(base, i, ("o",), self.o, (self.dd,), (self.do,))

@@ -109,6 +109,8 @@ hipError_t launch_linear_grouped_fwd(const QPtrs* q, int nseg, const int64_t* n_
 // (every n_outs[j] a multiple of 64 when n > 1) rounded to bf16 once;
 // dy_packed[j] is dy_j packed (lora_dus / lora_As entries may be null).
 struct BwdGroupPlan {
+  int bm;                          // tile rows: 256 (k_gemm) or 512 (k_gemm_bwd512)
+  int cmax;                        // contraction steps of the longest split
   int splits[GEMM_MAX_SEG];        // splits of each weight's contraction
   int64_t kc_chunk[GEMM_MAX_SEG];  // contraction rows per split
   int total;                       // all splits (partials when > 1)

@@ -1284,6 +1284,360 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables ta
   }
 }
 
+// ---- backward kernel: one wave per SIMD -----------------------------------
+// k_gemm_fwd's construction for the backward orientation, dx = dy . W': 256
+// threads = 4 waves, one per SIMD, each owning 128 output rows x 128 columns
+// (4x4 MFMA tiles, 256 fp32 accumulators); the workgroup tile is 512 rows x
+// 128 columns (columns = k_in), the contraction (n_out) in steps of 64 rows
+// of W. The decode is k_gemm's backward producer, done by all 256 threads
+// (thread t = producer thread pt of k_gemm): a 4x8 patch of codes per thread
+// and step, paired along the contraction as it is packed, stored transposed
+// into the XOR-swizzled LDS layout; the 128 block scales of a stage are
+// decoded twice over (threads t and t+128 alike) and published through a
+// two-slot LDS ring. Stage X:
+//  * step X-5: its scale codes are fetched; step X-3: its block scale is
+//    decoded and published (the barrier that ends the step makes it visible);
+//  * step X-4: its patch codes are fetched; step X-2: the pair lookups run
+//    through sub-step 0 and the products, bf16 pairs and 8-byte LDS stores
+//    every other MFMA of sub-step 1, so no lookup lives across a step;
+//  * three LDS stages, one barrier per step;
+//  * the per-element contraction order is k_gemm's: same bits for the same
+//    split of the contraction.
+// With 512-row tiles the grid has half k_gemm's tiles, so where that needs
+// more splits the fp32 partials double; the plan takes this kernel only
+// for groups of two or more weights (always split: every weight has its own
+// splits) where the grid still fills the chip with long splits.
+__global__ __launch_bounds__(FTHREADS, 1) void k_gemm_bwd512(GemmArgs ga, Tables tab) {
+  // tile order as k_gemm's backward: the column tiles of one (row tile,
+  // split) pair share XCDs when the host asks for it
+  const int C = (int)gridDim.x, R = (int)gridDim.y;
+  const int id = (int)blockIdx.x + C * (int)blockIdx.y;
+  int ct = (int)blockIdx.x, rt = (int)blockIdx.y, zz = (int)blockIdx.z;
+  if (ga.xcd_pairs) {
+    const int P = R * (int)gridDim.z;
+    const int G = P >= 8 ? 1 : 8 / P;
+    const int flat = id + C * R * (int)blockIdx.z;
+    if ((P % 8 == 0 || 8 % P == 0) && C % G == 0) {
+      const int x = flat % 8, sl = flat / 8, cg = C / G;
+      const int pair = x / G + 8 * (sl / cg);
+      ct = (sl % cg) * G + x % G;
+      rt = pair % R;
+      zz = pair / R;
+    }
+  }
+  int sgi = 0;
+#pragma unroll
+  for (int q = 1; q < GEMM_MAX_SEG; ++q)
+    if (q < ga.nseg && zz >= ga.seg[q].z0) sgi = q;
+  const GemmSeg& sg = ga.seg[sgi];
+  const int64_t M = ga.M, k_in = ga.k_in, Nc = ga.Nc, Kc = sg.n_out;
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[F_SMEM_BYTES + 2 * SCALE_FLOATS * 4];
+  uint16_t* const Bs0 = reinterpret_cast<uint16_t*>(smem);
+  float2* const s_pair_all = reinterpret_cast<float2*>(smem + FNST * STAGE_ELEMS * 2);
+  float* const s_c8 = reinterpret_cast<float*>(smem + FNST * STAGE_ELEMS * 2 + 256 * PAIR_COPIES * 8);
+  float* const s_scale = reinterpret_cast<float*>(smem + F_SMEM_BYTES);  // [2][SCALE_FLOATS]
+  const int t = threadIdx.x;
+  fill_tables(s_pair_all, s_c8, tab, t);
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
+  const int lrow = lane & 31;
+  const int lk = (lane >> 5) * 8;
+  auto stage = [&](int st) { return Bs0 + st * STAGE_ELEMS; };
+
+  const int64_t n0 = (int64_t)ct * BN;
+  const int64_t m0 = (int64_t)rt * FBM;
+  const int zpart = zz;
+  const int split = zpart - sg.z0;
+  const int64_t kb = split * sg.kc_chunk;
+  const int64_t ke = (kb + sg.kc_chunk < Kc) ? kb + sg.kc_chunk : Kc;
+  const int nk = (int)((ke - kb + BK - 1) / BK);
+
+  // activation (dy) fragments, as in k_gemm_fwd
+  const __amdgpu_buffer_rsrc_t ar =
+      __builtin_amdgcn_make_buffer_rsrc((void*)sg.afrag, (short)0, (int)0xFFFFFFFFu, 0x00020000);
+  const int64_t nblk = (M + PACK_ROWS - 1) / PACK_ROWS * (PACK_ROWS / 32);
+  uint32_t aoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int64_t b = (m0 + wave * 128 + i * 32) / 32;
+    b = b < nblk ? b : nblk - 1;
+    aoff[i] = (uint32_t)(b * sg.kblocks * FRAG_BYTES + lane * 16);
+  }
+  auto a_soff = [&](int k) {
+    const int kc = k < nk ? k : nk - 1;
+    return (int)(((kb + (int64_t)kc * BK) / 16) * FRAG_BYTES);
+  };
+
+  // weights (k_gemm's backward producer map, pt = t): rows 4 kg + i of a
+  // step, columns n0 + mcol .. + 8 (clamped inside k_in; the block scale of
+  // a column block past k_in is 0). Every contraction length here is a
+  // multiple of 64 (the plan's condition), so every step is whole and every
+  // code offset is the thread's own offset plus a wave-uniform row offset.
+  // Every thread loads the block scale of row (pt/2)%64, column block pt%2:
+  // threads pt and pt+128 load and publish the same one, which keeps the
+  // loop free of branches.
+  const int pt = t;
+  const int kg = bwd_kg(pt), mcol = 8 * bwd_m(pt), r0p = 4 * kg;
+  const uint32_t kin2 = (uint32_t)(k_in / 2), kblk = (uint32_t)(k_in / 64);
+  int64_t col = n0 + mcol;
+  col = col < k_in ? col : k_in - 8;
+  const int64_t bcol = n0 + 64 * (pt & 1);
+  const bool scol = bcol < k_in;
+  const uint32_t sblk = (uint32_t)((scol ? bcol : 0) / 64);
+  const int srow = (pt >> 1) & 63;
+  const uint32_t woff0 = (uint32_t)r0p * kin2 + (uint32_t)(col / 2);  // the thread's part
+  const uint32_t sbase = (uint32_t)srow * kblk + sblk;
+  const __amdgpu_buffer_rsrc_t wr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)sg.packed, (short)0, (int)0xFFFFFFFFu, 0x00020000);
+  const __amdgpu_buffer_rsrc_t qr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)sg.q8, (short)0, (int)0xFFFFFFFFu, 0x00020000);
+  const __amdgpu_buffer_rsrc_t nr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)sg.nested, (short)0, (int)0xFFFFFFFFu, 0x00020000);
+  const float off = sg.offset[0];
+  // a stage's codes: four packed words (the patch), and the scale code and
+  // nested scale of the thread's block scale, fetched at different times
+  struct WCodes {
+    uint32_t w[4];
+  };
+  struct QCodes {
+    uint32_t q;
+    float nest;
+  };
+  auto load_w = [&](int k, WCodes& c) {
+    const int kc = k < nk ? k : nk - 1;
+    const uint32_t k0 = (uint32_t)(kb + kc * BK);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      c.w[i] = __builtin_amdgcn_raw_buffer_load_b32(wr, woff0, (int)((k0 + i) * kin2), 0);
+  };
+  auto load_q = [&](int k, QCodes& c) {
+    const int kc = k < nk ? k : nk - 1;
+    const uint32_t blk = sbase + (uint32_t)(kb + kc * BK) * kblk;
+    c.q = __builtin_amdgcn_raw_buffer_load_b8(qr, blk, 0, 0);
+    c.nest = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(nr, (blk >> 8) * 4, 0, 0));
+  };
+  const PairTab ptab{reinterpret_cast<const uint8_t*>(s_pair_all), (uint32_t)(t & (PAIR_COPIES - 1)) * 8u};
+  float2 pv[16];  // pair lookups of the stage being decoded: [byte q * 4 + row i]
+  float cq = 0.0f;
+  float4 a4;      // the block scales of the thread's four rows
+  // the block scale of stage x into ring slot x%2: scale code lookup, then
+  // the decode and store
+  auto scale_code = [&](const QCodes& c) { cq = s_c8[c.q]; };
+  auto scale_put = [&](const QCodes& c, int x) {
+    s_scale[(x & 1) * SCALE_FLOATS + (pt & 1) * 64 + srow] = scol ? decode_scale(cq, c.nest, off) : 0.0f;
+  };
+  // decoding stage x into LDS stage st: pair lookups, the four block scales
+  // (published one step earlier), then half h (byte q = h/2, column 2q + h%2
+  // of the patch) -- four products, two bf16 pairs along the contraction,
+  // one 8-byte store (k_gemm's backward decode, in pieces)
+  auto lookup = [&](const WCodes& c, int u) { pv[u] = pair_of(ptab, c.w[u & 3], u >> 2); };
+  auto fin_scales = [&](int x) {
+    a4 = *reinterpret_cast<const float4*>(s_scale + (x & 1) * SCALE_FLOATS + (bwd_m(pt) >> 3) * 64 + r0p);
+  };
+  // column mcol + c of the patch lands at wbase + c * LDS_STRIDE: the
+  // swizzle bwd_swizzle_off(mcol + c, r0p) is the same for c < 8, since
+  // mcol is a multiple of 8
+  const int wbase = mcol * LDS_STRIDE + bwd_swizzle_off(mcol, r0p);
+  auto fin_half = [&](int st, int h) {
+    const int q = h >> 1, hi = h & 1;
+    const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __fmul_rn(hi ? pv[q * 4 + i].y : pv[q * 4 + i].x, a[i]);
+    uint2 p;
+    p.x = pack_bf16x2(v[0], v[1]);
+    p.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(stage(st) + wbase + (2 * q + hi) * LDS_STRIDE) = p;
+  };
+  auto decode_all = [&](const WCodes& c, int x, int st) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) lookup(c, u);
+    fin_scales(x);
+#pragma unroll
+    for (int h = 0; h < 8; ++h) fin_half(st, h);
+  };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // stage X: scale codes fetched in step X-5, block scale published in step
+  // X-3, patch codes fetched in step X-4, looked up and decoded into LDS in
+  // step X-2 -- the pair lookups never live across a step
+  WCodes w0, w1;  // patch codes of even and odd stages
+  QCodes q0, q1;  // scale codes of even and odd stages
+  u32x4 A0[4][4], A1[4][4];
+  auto issue_a = [&](u32x4 (&A)[4][4], int k) {
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        A[i][gg] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[i], a_soff(k) + gg * FRAG_BYTES, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+  // prologue: stages 0 and 1 decoded, the scale of stage 2 published, the
+  // patch codes of stages 2 and 3 and the scale codes of 3 and 4 in flight
+  load_w(0, w0);
+  load_q(0, q0);
+  load_w(1, w1);
+  load_q(1, q1);
+  issue_a(A0, 0);
+  issue_a(A1, 1);
+  __syncthreads();  // tables in LDS
+  scale_code(q0);
+  scale_put(q0, 0);
+  scale_code(q1);
+  scale_put(q1, 1);
+  load_q(2, q0);
+  load_q(3, q1);
+  __syncthreads();  // scales of stages 0 and 1 published
+  decode_all(w0, 0, 0);
+  decode_all(w1, 1, 1);
+  load_w(2, w0);
+  load_w(3, w1);
+  __syncthreads();  // every thread is past the scales of stages 0 and 1
+  scale_code(q0);
+  scale_put(q0, 2);
+  load_q(4, q0);
+  __syncthreads();  // stages 0 and 1 in LDS, the scale of stage 2 published
+  // b_frag<true>(bs, lane, j, kk) with its swizzle split into a lane part
+  // and a constant: for column 32 j + l%32 and contraction 16 kk + 8 (l/32)
+  // the swizzled offset is 16 (kk ^ j) + 8 ((l/32) ^ (l/16 % 2))
+  const int fbase = (lane & 31) * LDS_STRIDE + 8 * (((lane >> 5) ^ (lane >> 4)) & 1);
+  auto bfrag = [&](int st, int j, int kk) {
+    return *reinterpret_cast<const bf16x8_t*>(stage(st) + fbase + 32 * j * LDS_STRIDE + 16 * (kk ^ j));
+  };
+  bf16x8_t fb0[4], fb1[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fb0[j] = bfrag(0, j, 0);
+
+  // step s: multiply LDS stage st = s % FNST (activation set A); decode
+  // stage s+2 (patch codes wc) into LDS stage (s+2) % FNST; publish the
+  // scale of stage s+3 (scale codes qc); fetch the patch codes of stage s+4
+  // into wc and the scale codes of stage s+5 into qc
+  auto step = [&](int s, int st, u32x4 (&A)[4][4], WCodes& wc, QCodes& qc) __attribute__((always_inline)) {
+    const int s1 = st + 1 < FNST ? st + 1 : st + 1 - FNST;
+    const int s2 = st + 2 < FNST ? st + 2 : st + 2 - FNST;
+    const int a2 = a_soff(s + 2);
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      bf16x8_t(&fc)[4] = (gg & 1) ? fb1 : fb0;
+      bf16x8_t(&fn)[4] = (gg & 1) ? fb0 : fb1;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const int i = m >> 2, j = m & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc[j], __builtin_bit_cast(bf16x8_t, A[i][gg]),
+                                                            acc[i][j], 0, 0, 0);
+        if (m < 4) fn[m] = (gg < 3) ? bfrag(st, m, gg + 1) : bfrag(s1, m, 0);
+        if (j == 3) A[i][gg] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[i], a2 + gg * FRAG_BYTES, 0);
+        // stage s+2: lookups through sub-step 0, scales, then a half-column
+        // every other MFMA of sub-step 1
+        if (gg == 0) lookup(wc, m);
+        if (gg == 0 && m == 15) fin_scales(s + 2);
+        if (gg == 1 && (m & 1)) fin_half(s2, m >> 1);
+        // stage s+3's block scale; then the codes of s+4 and s+5
+        if (gg == 2 && m == 0) scale_code(qc);
+        if (gg == 2 && m == 4) scale_put(qc, s + 3);
+        if (gg == 3 && m == 8) {
+          load_w(s + 4, wc);
+          load_q(s + 5, qc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // stage s+2 is in set (s+2)%2 = s%2 of the patch codes, stage s+3 in set
+  // (s+3)%2 = (s+1)%2 of the scale codes
+  int s = 0;
+  for (; s + 5 < nk; s += 6) {
+    step(s, 0, A0, w0, q1);
+    step(s + 1, 1, A1, w1, q0);
+    step(s + 2, 2, A0, w0, q1);
+    step(s + 3, 0, A1, w1, q0);
+    step(s + 4, 1, A0, w0, q1);
+    step(s + 5, 2, A1, w1, q0);
+  }
+  for (; s + 1 < nk; s += 2) {
+    step(s, s % FNST, A0, w0, q1);
+    step(s + 1, (s + 1) % FNST, A1, w1, q0);
+  }
+  if (s < nk) step(s, s % FNST, A0, w0, q1);
+
+  // LoRA term (split 0): + du[m, :] . A[:, n], in chunks of 16 over the rank
+  if (sg.lora_l != nullptr && split == 0) {
+    for (int r0 = 0; r0 < ga.r; r0 += 16) {
+      bf16x8_t fa[4], fbl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = m0 + wave * 128 + i * 32 + lrow;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int rr = r0 + lk + e;
+          v[e] = (row < M && rr < ga.r) ? sg.lora_l[row * ga.r + rr] : 0.0f;
+        }
+        fa[i] = f32x8_to_bf16(v);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = n0 + j * 32 + lrow;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int rr = r0 + lk + e;
+          v[e] = (col < Nc && rr < ga.r) ? sg.lora_r[(int64_t)rr * k_in + col] : 0.0f;
+        }
+        fbl[j] = f32x8_to_bf16(v);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fbl[j], fa[i], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // the fp32 partial of this split through LDS, 128 rows (one wave) per pass
+  {
+    constexpr int OS = BN + 4;
+    float* const ot = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int ph = 0; ph < 4; ++ph) {
+      if (wave == ph) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = i * 32 + lrow;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<float4*>(ot + row * OS + j * 32 + 8 * q + 4 * (lane >> 5)) =
+                  make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < 128 * BN / 4 / FTHREADS; ++it) {
+        const int q = it * FTHREADS + t;
+        const int row = q / (BN / 4), c4 = q % (BN / 4);
+        const int64_t grow = m0 + 128 * ph + row, gcol = n0 + 4 * c4;
+        if (grow < M && gcol < Nc)
+          *reinterpret_cast<u32x4*>(sg.part + ((int64_t)zpart * M + grow) * Nc + gcol) =
+              *reinterpret_cast<const u32x4*>(ot + row * OS + 4 * c4);
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // Sum of the split partials in split order, rounded once to bf16; blockIdx.y
 // selects the weight of a grouped launch. With res_out, also the residual
 // stream res_out = res_in + bf16 result in fp32 (what k_residual_add computes
@@ -1549,38 +1903,59 @@ hipError_t launch_linear_swiglu_fwd(const QPtrs* q, int64_t width, int64_t k_in,
 // Splits of a grouped backward: split j's contraction into S_j chunks of c
 // steps, the smallest c for which the grid still fits one wave of 256
 // workgroups (so the slowest workgroup runs as few steps as possible), never
-// below 8 steps; a group of one plans as the single call.
-BwdGroupPlan plan_bwd_grouped(int64_t M, const int64_t* n_outs, int n, int64_t k_in) {
+// below 8 steps; a group of one plans as the single call. Planned for
+// k_gemm's 256-row tiles and for k_gemm_bwd512's 512-row tiles; the latter
+// is taken where its splits keep at least 32 steps (its per-step cost is
+// about 1.6 times k_gemm's for twice the rows, and its partials are twice as
+// many, which long splits amortise).
+static BwdGroupPlan plan_bwd_tiles(int64_t M, const int64_t* n_outs, int n, int64_t k_in, int bm) {
   BwdGroupPlan bp = {};
-  if (n == 1) {
-    const GemmPlan p = plan_gemm(M, k_in, n_outs[0], false);
-    bp.splits[0] = p.splits;
-    bp.kc_chunk[0] = p.kc_chunk;
-    bp.total = p.splits;
-  } else {
-    const int64_t tiles = ((M + BM - 1) / BM) * ((k_in + BN - 1) / BN);
-    int64_t steps[GEMM_MAX_SEG], cmax = 0;
-    for (int j = 0; j < n; ++j) {
-      steps[j] = (n_outs[j] + BK - 1) / BK;
-      cmax = steps[j] > cmax ? steps[j] : cmax;
-    }
-    int64_t best = cmax;
-    for (int64_t c = cmax; c >= 8; --c) {
-      int64_t sz = 0;
-      for (int j = 0; j < n; ++j) sz += (steps[j] + c - 1) / c;
-      if (tiles * sz > 256) break;
-      best = c;
-    }
-    bp.total = 0;
-    for (int j = 0; j < n; ++j) {
-      const int64_t c = best < steps[j] ? best : steps[j];
-      bp.splits[j] = (int)((steps[j] + c - 1) / c);
-      bp.kc_chunk[j] = c * BK;
-      bp.total += bp.splits[j];
-    }
+  bp.bm = bm;
+  const int64_t tiles = ((M + bm - 1) / bm) * ((k_in + BN - 1) / BN);
+  int64_t steps[GEMM_MAX_SEG], cmax = 0;
+  for (int j = 0; j < n; ++j) {
+    steps[j] = (n_outs[j] + BK - 1) / BK;
+    cmax = steps[j] > cmax ? steps[j] : cmax;
+  }
+  int64_t best = cmax;
+  for (int64_t c = cmax; c >= 8; --c) {
+    int64_t sz = 0;
+    for (int j = 0; j < n; ++j) sz += (steps[j] + c - 1) / c;
+    if (tiles * sz > 256) break;
+    best = c;
+  }
+  bp.total = 0;
+  bp.cmax = 0;
+  for (int j = 0; j < n; ++j) {
+    const int64_t c = best < steps[j] ? best : steps[j];
+    bp.splits[j] = (int)((steps[j] + c - 1) / c);
+    bp.kc_chunk[j] = c * BK;
+    bp.total += bp.splits[j];
+    bp.cmax = c > bp.cmax ? (int)c : bp.cmax;
   }
   bp.part_bytes = bp.total > 1 ? round256((size_t)bp.total * (size_t)M * (size_t)k_in * sizeof(float)) : 0;
   return bp;
+}
+
+BwdGroupPlan plan_bwd_grouped(int64_t M, const int64_t* n_outs, int n, int64_t k_in) {
+  if (n == 1) {
+    BwdGroupPlan bp = {};
+    const GemmPlan p = plan_gemm(M, k_in, n_outs[0], false);
+    bp.bm = BM;
+    bp.splits[0] = p.splits;
+    bp.kc_chunk[0] = p.kc_chunk;
+    bp.total = p.splits;
+    bp.cmax = (int)(p.kc_chunk / BK);
+    bp.part_bytes = bp.total > 1 ? round256((size_t)bp.total * (size_t)M * (size_t)k_in * sizeof(float)) : 0;
+    return bp;
+  }
+  // k_gemm_bwd512 addresses a weight's codes with 32-bit offsets and takes
+  // whole 64-row contraction steps only
+  bool fits = true;
+  for (int j = 0; j < n; ++j) fits = fits && n_outs[j] * (k_in / 2) < ((int64_t)1 << 31) && n_outs[j] % BK == 0;
+  const BwdGroupPlan wide = plan_bwd_tiles(M, n_outs, n, k_in, FBM);
+  if (fits && wide.cmax >= 32) return wide;
+  return plan_bwd_tiles(M, n_outs, n, k_in, BM);
 }
 
 hipError_t launch_linear_grouped_bwd(const QPtrs* q, int n, const int64_t* n_outs, int64_t k_in,
@@ -1612,13 +1987,18 @@ hipError_t launch_linear_grouped_bwd(const QPtrs* q, int n, const int64_t* n_out
     sg.kc_chunk = bp.kc_chunk[j];
     z0 += bp.splits[j];
   }
-  const dim3 grid((unsigned)((k_in + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)bp.total);
+  const dim3 grid((unsigned)((k_in + BN - 1) / BN), (unsigned)((M + bp.bm - 1) / bp.bm), (unsigned)bp.total);
   int64_t a_bytes = 0;
   for (int j = 0; j < n; ++j) a_bytes += 2 * M * n_outs[j];
   g.xcd_pairs = a_bytes > kXcdPairBytes;
   const Tables& tab = host_tables();
-  if (bp.total > 1) hipLaunchKernelGGL((k_gemm<true, true, false>), grid, dim3(THREADS), 0, s, g, tab);
-  else hipLaunchKernelGGL((k_gemm<true, false, false>), grid, dim3(THREADS), 0, s, g, tab);
+  if (bp.bm == FBM) {
+    hipLaunchKernelGGL(k_gemm_bwd512, grid, dim3(FTHREADS), 0, s, g, tab);
+  } else if (bp.total > 1) {
+    hipLaunchKernelGGL((k_gemm<true, true, false>), grid, dim3(THREADS), 0, s, g, tab);
+  } else {
+    hipLaunchKernelGGL((k_gemm<true, false, false>), grid, dim3(THREADS), 0, s, g, tab);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || bp.total == 1) return e;
   SumSegs sum = {};

@@ -415,8 +415,11 @@ def test_grouped_backward_workspace():
     # in two splits, k and v one each: 256 workgroups of at most 32 steps,
     # four fp32 partials of 512 x 4096
     assert L.grouped_bwd_workspace_bytes([4096, 1024, 1024], 4096, 512) == 4 * 512 * 4096 * 4
-    # gate and up: 224 steps each, two splits each
-    assert L.grouped_bwd_workspace_bytes([14336, 14336], 4096, 512) == 4 * 512 * 4096 * 4
+    # gate and up: 224 steps each on 32 tiles of 512 x 128, four splits of
+    # 56 steps each: eight partials
+    assert L.grouped_bwd_workspace_bytes([14336, 14336], 4096, 512) == 8 * 512 * 4096 * 4
+    # at M = 2048: 128 tiles of 512 x 128, one split each
+    assert L.grouped_bwd_workspace_bytes([14336, 14336], 4096, 2048) == 2 * 2048 * 4096 * 4
     # a group of one plans like the single call
     for n, k, M in ((4096, 4096, 512), (40, 64, 100), (14336, 4096, 2048)):
         assert L.grouped_bwd_workspace_bytes([n], k, M) == \

@@ -536,16 +536,20 @@ def test_grouped_backward_of_one_is_the_single_call(projs, ns, k, M, lora_on):
     assert np.array_equal(g, one)
 
 
-@pytest.mark.parametrize("projs,ns,lora_on", [
-    (("q", "k", "v"), (4096, 1024, 1024), ("q", "v")),
-    (("gate", "up"), (14336, 14336), ()),
+@pytest.mark.parametrize("projs,ns,lora_on,M", [
+    (("q", "k", "v"), (4096, 1024, 1024), ("q", "v"), 512),
+    (("gate", "up"), (14336, 14336), (), 512),
+    # gate+up at these widths take 512-row tiles: one partial tile, and a
+    # full one followed by a ragged one, with both adapters on
+    (("gate", "up"), (14336, 14336), ("gate", "up"), 300),
+    (("gate", "up"), (14336, 14336), ("gate", "up"), 700),
 ])
-def test_grouped_backward_8b_sampled(projs, ns, lora_on):
-    """8B widths at M = 512, as the decoder step launches them: 512 sampled
-    outputs recomputed by the oracle one by one, and the whole result within
-    bf16 rounding of the sum of the single calls."""
-    print(f"grouped bwd 8b {projs}", flush=True)
-    k, M = 4096, 512
+def test_grouped_backward_8b_sampled(projs, ns, lora_on, M):
+    """8B widths at M = 512, as the decoder step launches them (and ragged M):
+    512 sampled outputs recomputed by the oracle one by one, and the whole
+    result within bf16 rounding of the sum of the single calls."""
+    print(f"grouped bwd 8b {projs} M={M} lora={lora_on}", flush=True)
+    k = 4096
     c = _bwd_group_setup(projs, ns, k, M, layer=3)
     got = _bwd_group_run(c, True, lora_on)
     singles = _bwd_group_run(c, False, lora_on)

@@ -1658,17 +1658,27 @@ __global__ __launch_bounds__(256) void k_split_sum(SumSegs sg, int splits) {
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (i >= n) return;
   if (i + 4 <= n) {
+    // every load issued ahead of the adds, which keep split order
+    const bool res = sg.res_out[sgi] != nullptr;
+    float4 h = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (res) h = *reinterpret_cast<const float4*>(sg.res_in[sgi] + i);
     float4 s = *reinterpret_cast<const float4*>(part + i);
-    for (int p = 1; p < splits; ++p) {
-      const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)p * n + i);
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    for (int p = 1; p < splits; p += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (p + q < splits) v[q] = *reinterpret_cast<const float4*>(part + (int64_t)(p + q) * n + i);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (p + q < splits) {
+          s.x += v[q].x; s.y += v[q].y; s.z += v[q].z; s.w += v[q].w;
+        }
     }
     uint2 o;
     o.x = pack_bf16x2(s.x, s.y);
     o.y = pack_bf16x2(s.z, s.w);
     *reinterpret_cast<uint2*>(out + i) = o;
-    if (sg.res_out[sgi]) {
-      const float4 h = *reinterpret_cast<const float4*>(sg.res_in[sgi] + i);
+    if (res) {
       float4 r;
       r.x = h.x + __uint_as_float(o.x << 16);
       r.y = h.y + __uint_as_float(o.x & 0xFFFF0000u);

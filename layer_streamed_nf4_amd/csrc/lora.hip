@@ -152,8 +152,18 @@ __global__ __launch_bounds__(256) void k_rows_sum(RowsArgs ra, int64_t n, float 
   const RowsSeg& sg = ra.seg[blockIdx.y];
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
+  // the partials in chunk order; loads issued eight at a time ahead of
+  // their adds, which keep that order
   float s = sg.part[i];
-  for (int p = 1; p < sg.nks; ++p) s += sg.part[(int64_t)p * n + i];
+  for (int p = 1; p < sg.nks; p += 8) {
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (p + q < sg.nks) v[q] = sg.part[(int64_t)(p + q) * n + i];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (p + q < sg.nks) s += v[q];
+  }
   sg.out[i] = scale * s;
 }
 

@@ -93,46 +93,39 @@ __global__ __launch_bounds__(256) void k_embed(const uint16_t* __restrict__ E, i
 // y = bf16(x * rstd * w), rstd = 1/sqrt(mean(x^2) + eps); one workgroup per
 // row, 8 elements (16- and 32-byte accesses) per thread and step.
 // packed (nullable): y also in MFMA fragment order (K = H), for the GEMMs
-// One wave per row, four consecutive rows per workgroup: the four rows'
-// 16-byte pieces of a fragment-order chunk are adjacent (lanes m%32 of one
-// fragment), so the packed copy leaves one XCD in whole 64-byte segments.
-// The first RF chunks of 8 a lane reads stay in registers for the second
-// pass (rows up to 4096 wide are read once).
-constexpr int RF = 8;
+// One workgroup per row. Workgroups are dealt to the 8 XCDs round-robin by
+// id; xcd_row gives each XCD a contiguous range of rows, so that rows that
+// share the 64-byte segments of a fragment-order copy (4 consecutive rows)
+// are written through one L2. Launch xcd_rows(T) workgroups.
+__device__ __forceinline__ int64_t xcd_row(int64_t b, int64_t T) {
+  const int64_t rpx = (T + 7) / 8;
+  return (b % 8) * rpx + b / 8;
+}
+inline unsigned xcd_rows(int64_t T) { return (unsigned)(8 * ((T + 7) / 8)); }
+
 __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const float* __restrict__ x,
-                                                     const float* __restrict__ w, int64_t T, int64_t H,
+                                                     const float* __restrict__ w, int64_t H,
                                                      float eps, uint16_t* __restrict__ y,
                                                      float* __restrict__ rstd,
-                                                     uint8_t* __restrict__ packed) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // whole waves; no workgroup barrier follows
+                                                     uint8_t* __restrict__ packed, int64_t T) {
+  __shared__ float red[4];
+  const int64_t t = xcd_row(blockIdx.x, T);
+  if (t >= T) return;  // uniform per workgroup
   const float* xr = x + t * H;
   const int nc = (int)(H / 8);
-  float keep[RF][8];
   float ss = 0.0f;
-#pragma unroll
-  for (int j = 0; j < RF; ++j) {
-    const int c = lane + 64 * j;
-    if (c < nc) {
-      load8_f32(xr + 8 * c, keep[j]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += keep[j][e] * keep[j][e];
-    }
-  }
-  for (int c = lane + 64 * RF; c < nc; c += 64) {
+  for (int c = threadIdx.x; c < nc; c += 256) {
     float f[8];
     load8_f32(xr + 8 * c, f);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += f[e] * f[e];
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  ss = block_sum(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)H + eps);
-  if (lane == 0) rstd[t] = r;
-  const int64_t kb = (H + 63) / 64 * 4;
-  auto out = [&](int c, float* f) {
-    float g[8];
+  if (threadIdx.x == 0) rstd[t] = r;
+  for (int c = threadIdx.x; c < nc; c += 256) {
+    float f[8], g[8];
+    load8_f32(xr + 8 * c, f);
     load8_f32(w + 8 * c, g);
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] = f[e] * r * g[e];
@@ -140,19 +133,12 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const float* __restrict__ x
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
     *reinterpret_cast<u32x4v*>(y + t * H + 8 * c) = o;
-    if (packed) *reinterpret_cast<u32x4v*>(packed + frag_offset(t, 8 * c, kb)) = o;
-  };
-#pragma unroll
-  for (int j = 0; j < RF; ++j) {
-    const int c = lane + 64 * j;
-    if (c < nc) out(c, keep[j]);
+    if (packed) {
+      const int64_t kb = (H + 63) / 64 * 4;
+      *reinterpret_cast<u32x4v*>(packed + frag_offset(t, 8 * c, kb)) = o;
+      if (c == nc - 1) frag_zero_tail(packed, t, H, kb);
+    }
   }
-  for (int c = lane + 64 * RF; c < nc; c += 64) {
-    float f[8];
-    load8_f32(xr + 8 * c, f);
-    out(c, f);
-  }
-  if (packed && lane == 0) frag_zero_tail(packed, t, H, kb);
 }
 
 // chunks of 8 of the row a thread of the norm backward keeps in registers
@@ -183,9 +169,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(DyPtrs dys, int n_dy, const
                                                      const float* __restrict__ rstd, int64_t H,
                                                      int accumulate, float* __restrict__ dh,
                                                      uint16_t* __restrict__ y,
-                                                     uint8_t* __restrict__ packed) {
+                                                     uint8_t* __restrict__ packed, int64_t T) {
   __shared__ float red[4];
-  const int64_t t = blockIdx.x;
+  const int64_t t = xcd_row(blockIdx.x, T);
+  if (t >= T) return;  // uniform per workgroup
   const float* xr = x + t * H;
   const float r = rstd[t];
   const int nc = (int)(H / 8);
@@ -260,30 +247,28 @@ struct InvFreq {
 // pairs per thread and item. p1 / p2 (nullable): the rotated rows also in
 // MFMA fragment order (K = heads * d), as the GEMMs that read them next take
 // them (k_frag_pack's layout, the columns past K up to a multiple of 64 zero).
-// Four consecutive rows per workgroup (their 16-byte fragment slots are
-// adjacent, so the packed copies leave one XCD in whole segments), four
-// waves per row. A lane rotates G consecutive columns of each half of a head:
-// G = 8 where the half is a multiple of 8 and the rows are 16-byte aligned
-// (one fragment slot per store), else G = 4.
+// One workgroup per row, rows dealt to XCDs by xcd_row. A thread rotates G
+// consecutive columns of each half of a head: G = 8 where the half is a
+// multiple of 8 and the rows are 16-byte aligned (one fragment slot per
+// packed store), else G = 4.
 template <int G>
-__global__ __launch_bounds__(1024) void k_rope_rows(uint16_t* __restrict__ x1, int heads1,
+__global__ __launch_bounds__(256) void k_rope_rows(uint16_t* __restrict__ x1, int heads1,
                                                    uint8_t* __restrict__ p1, uint16_t* __restrict__ x2,
                                                    int heads2, uint8_t* __restrict__ p2, int64_t T,
                                                    int64_t S, int d, InvFreq inv, int inverse) {
   using V = typename std::conditional<G == 8, u32x4v, uint2>::type;
-  __shared__ float2 cs[4][128];
-  const int wv = (threadIdx.x >> 6) & 3, part = threadIdx.x >> 8, lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + wv;
+  __shared__ float2 cs[128];
+  const int64_t t = xcd_row(blockIdx.x, T);
+  if (t >= T) return;  // uniform per workgroup
   const int half = d / 2, qg = half / G;
-  for (int j = 64 * part + lane; j < half; j += 256) {
+  for (int j = threadIdx.x; j < half; j += 256) {
     double sd, cd;
     sincos((double)(t % S) * inv.f[j], &sd, &cd);
-    cs[wv][j] = make_float2((float)cd, inverse ? -(float)sd : (float)sd);
+    cs[j] = make_float2((float)cd, inverse ? -(float)sd : (float)sd);
   }
   __syncthreads();
-  if (t >= T) return;
   const int n1 = heads1 * qg, n = n1 + (x2 ? heads2 * qg : 0);
-  for (int i = 64 * part + lane; i < n; i += 256) {
+  for (int i = threadIdx.x; i < n; i += 256) {
     const bool second = i >= n1;
     const int ii = second ? i - n1 : i;
     uint16_t* const x = second ? x2 : x1;
@@ -299,7 +284,7 @@ __global__ __launch_bounds__(1024) void k_rope_rows(uint16_t* __restrict__ x1, i
     float o1[G], o2[G];
 #pragma unroll
     for (int e = 0; e < G; ++e) {
-      const float c = cs[wv][j0 + e].x, sn = cs[wv][j0 + e].y;
+      const float c = cs[j0 + e].x, sn = cs[j0 + e].y;
       const uint32_t wa = aw[e >> 1], wb = bw[e >> 1];
       const float x1v = __uint_as_float((e & 1) ? (wa & 0xFFFF0000u) : (wa << 16));
       const float x2v = __uint_as_float((e & 1) ? (wb & 0xFFFF0000u) : (wb << 16));
@@ -323,7 +308,7 @@ __global__ __launch_bounds__(1024) void k_rope_rows(uint16_t* __restrict__ x1, i
       *reinterpret_cast<V*>(p + frag_offset(t, c2 & ~7ll, kb) + (c2 & 7) * 2) = rb;
     }
   }
-  if (lane == 0 && part == 0) {
+  if (threadIdx.x == 0) {
     if (p1) frag_zero_tail(p1, t, (int64_t)heads1 * d, ((int64_t)heads1 * d + 63) / 64 * 4);
     if (x2 && p2) frag_zero_tail(p2, t, (int64_t)heads2 * d, ((int64_t)heads2 * d + 63) / 64 * 4);
   }
@@ -1358,8 +1343,8 @@ hipError_t launch_embed(const uint16_t* E, int64_t V, const int64_t* ids, int64_
 
 hipError_t launch_rmsnorm_fwd(const float* x, const float* w, int64_t T, int64_t H, float eps,
                               uint16_t* y, float* rstd, void* packed, hipStream_t s) {
-  hipLaunchKernelGGL(k_rmsnorm_fwd, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, w, T, H, eps, y,
-                     rstd, static_cast<uint8_t*>(packed));
+  hipLaunchKernelGGL(k_rmsnorm_fwd, dim3(xcd_rows(T)), dim3(256), 0, s, x, w, H, eps, y, rstd,
+                     static_cast<uint8_t*>(packed), T);
   return hipGetLastError();
 }
 
@@ -1367,8 +1352,8 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* const* dys, int n_dy, const float*
                               const float* rstd, int64_t T, int64_t H, int accumulate, float* dh,
                               uint16_t* y, void* packed, hipStream_t s) {
   DyPtrs d{{dys[0], n_dy > 1 ? dys[1] : nullptr, n_dy > 2 ? dys[2] : nullptr}};
-  hipLaunchKernelGGL(k_rmsnorm_bwd, dim3((unsigned)T), dim3(256), 0, s, d, n_dy, x, w, rstd, H,
-                     accumulate, dh, y, static_cast<uint8_t*>(packed));
+  hipLaunchKernelGGL(k_rmsnorm_bwd, dim3(xcd_rows(T)), dim3(256), 0, s, d, n_dy, x, w, rstd, H,
+                     accumulate, dh, y, static_cast<uint8_t*>(packed), T);
   return hipGetLastError();
 }
 
@@ -1384,10 +1369,10 @@ hipError_t launch_rope_pair(uint16_t* x1, int heads1, uint16_t* x2, int heads2, 
   const bool wide = (d / 2) % 8 == 0 && reinterpret_cast<uintptr_t>(x1) % 16 == 0 &&
                     reinterpret_cast<uintptr_t>(x2) % 16 == 0;
   if (wide)
-    hipLaunchKernelGGL(k_rope_rows<8>, dim3((unsigned)((T + 3) / 4)), dim3(1024), 0, s, x1, heads1,
+    hipLaunchKernelGGL(k_rope_rows<8>, dim3(xcd_rows(T)), dim3(256), 0, s, x1, heads1,
                        static_cast<uint8_t*>(p1), x2, heads2, static_cast<uint8_t*>(p2), T, S, d, inv, inverse);
   else
-    hipLaunchKernelGGL(k_rope_rows<4>, dim3((unsigned)((T + 3) / 4)), dim3(1024), 0, s, x1, heads1,
+    hipLaunchKernelGGL(k_rope_rows<4>, dim3(xcd_rows(T)), dim3(256), 0, s, x1, heads1,
                        static_cast<uint8_t*>(p1), x2, heads2, static_cast<uint8_t*>(p2), T, S, d, inv, inverse);
   return hipGetLastError();
 }

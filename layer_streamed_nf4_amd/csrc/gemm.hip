@@ -1304,9 +1304,11 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_fwd(GemmArgs ga, Tables ta
 //  * the per-element contraction order is k_gemm's: same bits for the same
 //    split of the contraction.
 // With 512-row tiles the grid has half k_gemm's tiles, so where that needs
-// more splits the fp32 partials double; the plan takes this kernel only
-// for groups of two or more weights (always split: every weight has its own
-// splits) where the grid still fills the chip with long splits.
+// more splits the fp32 partials double; the plan takes this kernel for groups
+// of two or more weights (always split: every weight has its own splits)
+// where the grid still fills the chip with long splits, and for a single
+// weight where its grid needs no split at all (SPLIT = false: bf16 output).
+template <bool SPLIT>
 __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_bwd512(GemmArgs ga, Tables tab) {
   // tile order as k_gemm's backward: the column tiles of one (row tile,
   // split) pair share XCDs when the host asks for it
@@ -1605,8 +1607,40 @@ __global__ __launch_bounds__(FTHREADS, 1) void k_gemm_bwd512(GemmArgs ga, Tables
     }
   }
 
-  // the fp32 partial of this split through LDS, 128 rows (one wave) per pass
-  {
+  // output through LDS: bf16, 256 rows (two waves) per pass, or the fp32
+  // partial of this split, 128 rows (one wave) per pass
+  if constexpr (!SPLIT) {
+    constexpr int OS = BN + 8;
+    uint16_t* const ot = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll
+    for (int ph = 0; ph < 2; ++ph) {
+      if ((wave >> 1) == ph) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int row = (wave & 1) * 128 + i * 32 + lrow;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              uint2 v;
+              v.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+              v.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+              *reinterpret_cast<uint2*>(ot + row * OS + j * 32 + 8 * q + 4 * (lane >> 5)) = v;
+            }
+          }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < 256 * BN / 8 / FTHREADS; ++it) {
+        const int q = it * FTHREADS + t;
+        const int row = q / (BN / 8), c8 = q % (BN / 8);
+        const int64_t grow = m0 + 256 * ph + row, gcol = n0 + 8 * c8;
+        if (grow < M && gcol < Nc)
+          *reinterpret_cast<u32x4*>(sg.out + grow * Nc + gcol) = *reinterpret_cast<const u32x4*>(ot + row * OS + 8 * c8);
+      }
+      __syncthreads();
+    }
+  } else {
     constexpr int OS = BN + 4;
     float* const ot = reinterpret_cast<float*>(smem);
 #pragma unroll
@@ -1748,6 +1782,14 @@ GemmPlan plan_gemm(int64_t M, int64_t n_cols, int64_t k_contract, bool fwd_nf4) 
   return plan_gemm_grouped(M, &n_cols, 1, k_contract, fwd_nf4);
 }
 
+// A single NF4 backward runs on k_gemm_bwd512 (no split) where its 512-row
+// grid needs no split of the contraction by plan_tiles' rule; k_gemm's
+// 256-row grid then needs none either, so the workspace is the same.
+static bool bwd512_unsplit(int64_t M, int64_t n_out, int64_t k_in) {
+  if (n_out % BK != 0 || n_out * (k_in / 2) >= ((int64_t)1 << 31)) return false;
+  return plan_tiles(M, &k_in, 1, n_out, FBM).splits == 1;
+}
+
 // Launches the GEMM (and the split sum when the contraction is split) for
 // C[M, Nc] = A . B with the weight given either as NF4 tensors (q: nseg of
 // them, forward only when nseg > 1) or as a dense bf16 matrix (wd).
@@ -1809,14 +1851,19 @@ static hipError_t launch_gemm(bool backward, const QPtrs* q, int nseg, const uin
     sum.res_out[i] = res_out;
     max_n = n > max_n ? n : max_n;
   }
-  const dim3 grid((unsigned)tile0, (unsigned)((M + p.bm - 1) / p.bm), (unsigned)p.splits);
   const bool split = p.splits > 1;
+  // a single NF4 backward whose 512-row grid needs no split: k_gemm_bwd512
+  const bool bwd_wide = backward && wd == nullptr && nseg == 1 && bwd512_unsplit(M, n_outs[0], k_in);
+  const int bm = bwd_wide ? FBM : p.bm;
+  const dim3 grid((unsigned)tile0, (unsigned)((M + bm - 1) / bm), (unsigned)p.splits);
   g.xcd_pairs = backward && wd == nullptr && 2 * M * g.Kc > kXcdPairBytes;
   const Tables& tab = host_tables();
   // forward NF4 without a split: k_gemm_fwd; everything else: k_gemm
 #define NF4S_GEMM(B_, S_, D_) hipLaunchKernelGGL((k_gemm<B_, S_, D_>), grid, dim3(THREADS), 0, s, g, tab)
   if (fwd_nf4 && p.bm == FBM) {
     hipLaunchKernelGGL(k_gemm_fwd<false>, grid, dim3(FTHREADS), 0, s, g, tab);
+  } else if (bwd_wide) {
+    hipLaunchKernelGGL(k_gemm_bwd512<false>, grid, dim3(FTHREADS), 0, s, g, tab);
   } else if (wd == nullptr) {
     if (backward && split) NF4S_GEMM(true, true, false);
     else if (backward) NF4S_GEMM(true, false, false);
@@ -1951,7 +1998,7 @@ BwdGroupPlan plan_bwd_grouped(int64_t M, const int64_t* n_outs, int n, int64_t k
   if (n == 1) {
     BwdGroupPlan bp = {};
     const GemmPlan p = plan_gemm(M, k_in, n_outs[0], false);
-    bp.bm = BM;
+    bp.bm = bwd512_unsplit(M, n_outs[0], k_in) ? FBM : BM;
     bp.splits[0] = p.splits;
     bp.kc_chunk[0] = p.kc_chunk;
     bp.total = p.splits;
@@ -2003,7 +2050,8 @@ hipError_t launch_linear_grouped_bwd(const QPtrs* q, int n, const int64_t* n_out
   g.xcd_pairs = a_bytes > kXcdPairBytes;
   const Tables& tab = host_tables();
   if (bp.bm == FBM) {
-    hipLaunchKernelGGL(k_gemm_bwd512, grid, dim3(FTHREADS), 0, s, g, tab);
+    if (bp.total > 1) hipLaunchKernelGGL(k_gemm_bwd512<true>, grid, dim3(FTHREADS), 0, s, g, tab);
+    else hipLaunchKernelGGL(k_gemm_bwd512<false>, grid, dim3(FTHREADS), 0, s, g, tab);
   } else if (bp.total > 1) {
     hipLaunchKernelGGL((k_gemm<true, true, false>), grid, dim3(THREADS), 0, s, g, tab);
   } else {

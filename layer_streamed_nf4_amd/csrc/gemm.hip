@@ -1783,11 +1783,12 @@ GemmPlan plan_gemm(int64_t M, int64_t n_cols, int64_t k_contract, bool fwd_nf4) 
 }
 
 // A single NF4 backward runs on k_gemm_bwd512 (no split) where its 512-row
-// grid needs no split of the contraction by plan_tiles' rule; k_gemm's
-// 256-row grid then needs none either, so the workspace is the same.
+// grid alone fills the chip (plan_tiles' 192 tiles), so that it needs no split
+// of the contraction; k_gemm's 256-row grid then needs none either, so the
+// workspace is the same. Smaller grids keep k_gemm's twice as many tiles.
 static bool bwd512_unsplit(int64_t M, int64_t n_out, int64_t k_in) {
   if (n_out % BK != 0 || n_out * (k_in / 2) >= ((int64_t)1 << 31)) return false;
-  return plan_tiles(M, &k_in, 1, n_out, FBM).splits == 1;
+  return ((M + FBM - 1) / FBM) * ((k_in + BN - 1) / BN) >= 192;
 }
 
 // Launches the GEMM (and the split sum when the contraction is split) for

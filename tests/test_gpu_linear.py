@@ -503,9 +503,11 @@ BWD_GROUPS = [
     (("gate", "up"), (256, 64), 64, 513, ("up",)),
     # a group of one may have any n_out % 8 == 0 (a ragged last step)
     (("o",), (40,), 64, 100, ("o",)),
-    # one weight whose 512-row grid needs no split (224 tiles): the 512-row
-    # backward kernel with its bf16 output, a ragged second row tile
+    # one weight whose 512-row grid fills the chip unsplit (224 tiles): the
+    # 512-row backward kernel with its bf16 output, a ragged second row tile
     (("down",), (1024,), 14336, 600, ("down",)),
+    # the same kernel with a ragged last column tile (12352 = 96.5 x 128)
+    (("down",), (256,), 12352, 600, ("down",)),
 ]
 
 
@@ -531,6 +533,7 @@ def test_grouped_backward_matches_oracle(projs, ns, k, M, lora_on):
     (("gate",), (14336,), 4096, 512, ()),
     (("v",), (1024,), 4096, 512, ("v",)),
     (("down",), (1024,), 14336, 600, ("down",)),
+    (("down",), (256,), 12352, 600, ()),
 ])
 def test_grouped_backward_of_one_is_the_single_call(projs, ns, k, M, lora_on):
     """A group of one plans and contracts exactly as streamed_linear_bwd_packed."""

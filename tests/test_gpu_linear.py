@@ -705,6 +705,22 @@ def test_lora_rank_40_on_the_wide_forward_kernel():
         assert linear.rel_err(got, ref) <= TOL
 
 
+def test_backward_512_row_tiles_rank_40():
+    """The 512-row backward kernel (a single weight whose 194 tiles fill the
+    chip unsplit; ragged last row and column tiles) with an adapter of rank
+    40: its adapter term runs in three 16-column chunks, the last ragged."""
+    k, M, r = 12352, 600, 40
+    c = _bwd_group_setup(("down",), (256,), k, M, r=r)
+    got = _bwd_group_run(c, True, ("down",), r_lora=r)
+    (one,) = _bwd_group_run(c, False, ("down",), r_lora=r)
+    assert np.array_equal(got, one)
+    part = c["parts"][0]
+    wq = bits_to_f32(nf4.dequantize_bf16(nf4.quantize(part["w"]))).astype(np.float64)
+    ref = bits_to_f32(part["dy"]).astype(np.float64) @ wq
+    ref += part["du"].astype(np.float64) @ part["a"].astype(np.float64)
+    assert linear.rel_err(bits_to_f32(got).astype(np.float64), ref) <= TOL
+
+
 def test_grouped_backward_rank_40_on_two_adapters():
     """Adapters on q and v at rank 40 (three 16-column chunks, the last
     ragged) in one grouped backward with uneven per-weight splits."""

@@ -19,6 +19,15 @@ struct Mids4 {
 struct Mids8 {
   float m[255];
 };
+// The NF4 code search of the quantiser (quant.hip): bucket b of v / m, of
+// width 1/128 from -1, counts code[b] thresholds below it; b_mid[i] is the fp64
+// midpoint between threshold i and the next fp32 above it (b_mid[15] = +inf).
+// ok: every threshold lies at least 1/64 of a bucket width from a bucket edge.
+struct Buckets4 {
+  double b_mid[16];
+  uint8_t code[260];
+  int ok;
+};
 
 // Sets the calling thread's last-error message (nf4s_last_error) and returns code.
 int set_error(int code, const char* fmt, ...);
@@ -27,6 +36,7 @@ int set_error(int code, const char* fmt, ...);
 const Tables& host_tables();
 const Mids4& host_mids4();
 const Mids8& host_mids8();
+const Buckets4& host_buckets4();
 uint64_t host_table_hash();
 
 // Pointers into one quantised tensor (resolved from shard base + descriptor).

@@ -76,6 +76,7 @@ struct State {
   Tables t;
   Mids4 m4;
   Mids8 m8;
+  Buckets4 b4;
   uint64_t hash;
 };
 
@@ -88,6 +89,22 @@ const State& state() {
     // decision thresholds between consecutive levels, in fp32
     for (int i = 0; i < 15; ++i) s.m4.m[i] = (s.t.c4[i] + s.t.c4[i + 1]) * 0.5f;
     for (int i = 0; i < 255; ++i) s.m8.m[i] = (s.t.c8[i] + s.t.c8[i + 1]) * 0.5f;
+    // the quantiser's bucket table (exact: t and the next fp32 sum in fp64)
+    s.b4.ok = 1;
+    for (int i = 0; i < 15; ++i) {
+      const float t = s.m4.m[i];
+      s.b4.b_mid[i] = ((double)t + (double)std::nextafter(t, INFINITY)) * 0.5;
+      const double pos = ((double)t + 1.0) * 128.0;
+      const double f = pos - std::floor(pos);
+      if (f < 1.0 / 64 || f > 1.0 - 1.0 / 64) s.b4.ok = 0;
+    }
+    s.b4.b_mid[15] = INFINITY;
+    for (int b = 0; b < 260; ++b) {
+      const double lo = b / 128.0 - 1.0;
+      int c = 0;
+      for (int i = 0; i < 15; ++i) c += (double)s.m4.m[i] < lo;
+      s.b4.code[b] = (uint8_t)c;
+    }
     // FNV-1a 64 over the little-endian fp32 bytes, NF4 table then nested table
     uint64_t h = 0xCBF29CE484222325ull;
     auto eat = [&h](const float* p, int n) {
@@ -109,6 +126,7 @@ const State& state() {
 const Tables& host_tables() { return state().t; }
 const Mids4& host_mids4() { return state().m4; }
 const Mids8& host_mids8() { return state().m8; }
+const Buckets4& host_buckets4() { return state().b4; }
 uint64_t host_table_hash() { return state().hash; }
 
 }  // namespace nf4s

@@ -78,9 +78,9 @@ def test_workspace_queries_depend_on_shape_only():
     b = L.nf4s_workspace_bytes(L.OP_LINEAR_FWD, 512, 4096, 4096)
     assert a == b and a % 4 == 0
     # the absmax (5184 fp32, padded to 256 B) and one double-double partial
-    # of the offset sum per 4096 absmax values
-    assert L.nf4s_workspace_bytes(L.OP_QUANTIZE, 0, 576, 576) == 20736 + 2 * 16
-    assert L.nf4s_workspace_bytes(L.OP_QUANTIZE, 0, 14336, 4096) == 917504 * 4 + 224 * 16
+    # of the offset sum per 64 absmax values (81 of them; 14336 at 8B gate)
+    assert L.nf4s_workspace_bytes(L.OP_QUANTIZE, 0, 576, 576) == 20736 + 81 * 16
+    assert L.nf4s_workspace_bytes(L.OP_QUANTIZE, 0, 14336, 4096) == 917504 * 4 + 14336 * 16
     with pytest.raises(L.Nf4sError) as e:
         L.nf4s_workspace_bytes(99, 1, 64, 64)
     assert e.value.code == L.EINVAL

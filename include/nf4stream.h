@@ -551,7 +551,9 @@ int nf4s_attention_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
  * SwiGLU: out = bf16(silu(g) * u), silu(z) = z / (1 + e^-z); backward from ds:
  * dg = bf16(ds * u * s * (1 + g * (1 - s))), du = bf16(ds * g * s), s the
  * logistic of g. All bf16 [T, width], width a multiple of 8, 16-byte aligned;
- * packed outputs as above (out; dg and du). Errors: EINVAL, ESHAPE, EALIGN.
+ * packed outputs as above (out; dg and du). dg (du) may be NULL when
+ * dg_packed (du_packed) is given: only the packed form is then written.
+ * Errors: EINVAL, ESHAPE, EALIGN.
  */
 int nf4s_swiglu_fwd(const uint16_t* g, const uint16_t* u, int64_t T, int64_t width, uint16_t* out,
                     void* packed, void* stream);

@@ -971,9 +971,11 @@ int nf4s_swiglu_bwd(const uint16_t* ds, const uint16_t* g, const uint16_t* u, in
   int rc;
   if ((rc = check_rows(T, width)) || (rc = check_norm_width(width))) return rc;
   if ((rc = check_ptr(ds, "ds")) || (rc = check_ptr(g, "g")) || (rc = check_ptr(u, "u")) ||
-      (rc = check_ptr(dg, "dg")) || (rc = check_ptr(du, "du")) ||
       (rc = check_packed_out(dg_packed, T, width)) || (rc = check_packed_out(du_packed, T, width)))
     return rc;
+  // a row-major result may be left out when its packed form is written
+  if ((dg || !dg_packed) && (rc = check_ptr(dg, "dg"))) return rc;
+  if ((du || !du_packed) && (rc = check_ptr(du, "du"))) return rc;
   return launched(launch_swiglu_bwd(ds, g, u, T, width, dg, du, dg_packed, du_packed,
                                     static_cast<hipStream_t>(stream)),
                   "swiglu_bwd launch");

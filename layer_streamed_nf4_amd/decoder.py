@@ -454,8 +454,11 @@ class Decoder:
         self._packed_key = self._packed_key_b = self._packed_key_c = None
         self._bwd(base, i, ("down",), self.sw, (self.dd,), (self.dsw,),
                   dy_packed=self.packed_c.data_ptr())
+        # the row-major dg, du feed only the gate/up adapters' gradients; the
+        # GEMM reads the packed copies
+        rows = "gate" in self.targets or "up" in self.targets
         nf4s_swiglu_bwd(self.dsw.data_ptr(), self.g.data_ptr(), self.u_.data_ptr(), M, self.I,
-                        self.dg.data_ptr(), self.du_.data_ptr(), s,
+                        self.dg.data_ptr() if rows else None, self.du_.data_ptr() if rows else None, s,
                         dg_packed=self._produced(self.dg, self.I),
                         du_packed=self._produced(self.du_, self.I, second=True))
         dn = self._bwd(base, i, ("gate", "up"), self.n2, (self.dg, self.du_), self.dnx[:2])

@@ -286,6 +286,9 @@ def test_decoder_argument_errors():
     assert _err(L.nf4s_swiglu_fwd, FAKE, FAKE, 4, 16, FAKE, 0, FAKE + 16) == L.EALIGN  # packed 256-B
     assert _err(L.nf4s_swiglu_bwd, FAKE, FAKE, FAKE, 4, 16, FAKE, FAKE + 8) == L.EALIGN
     assert _err(L.nf4s_swiglu_bwd, FAKE, FAKE, FAKE, 4, 16, FAKE, FAKE, 0, None, FAKE + 64) == L.EALIGN
+    # a row-major result may be NULL only when its packed form is asked for
+    assert _err(L.nf4s_swiglu_bwd, FAKE, FAKE, FAKE, 4, 16, None, FAKE) == L.EINVAL
+    assert _err(L.nf4s_swiglu_bwd, FAKE, FAKE, FAKE, 4, 16, FAKE, None, 0, FAKE, None) == L.EINVAL
     assert _err(L.nf4s_rmsnorm_fwd, FAKE, FAKE, 4, 16, 1e-5, FAKE, FAKE, 0, FAKE + 32) == L.EALIGN
     assert _err(L.nf4s_residual_add, FAKE, FAKE, 16, None) == L.EINVAL
     assert _err(L.nf4s_to_bf16, FAKE + 2, 2, 8, FAKE) == L.EALIGN

@@ -261,6 +261,11 @@ def test_producers_write_the_packed_layout(T, W):
                       s, dg_packed=pg.data_ptr(), du_packed=pu.data_ptr())
     packed_rows_equal(dgo, pg)
     packed_rows_equal(duo, pu)
+    # packed forms only (the decoder's call when gate and up carry no adapter)
+    pg2, pu2 = sentinel(), sentinel()
+    L.nf4s_swiglu_bwd(db.data_ptr(), gb.data_ptr(), ub.data_ptr(), T, W, None, None, s,
+                      dg_packed=pg2.data_ptr(), du_packed=pu2.data_ptr())
+    assert torch.equal(pg2, pg) and torch.equal(pu2, pu)
     pk = sentinel()
     L.nf4s_to_bf16(x.data_ptr(), T, W, y.data_ptr(), s, packed=pk.data_ptr())
     packed_rows_equal(y, pk)
